@@ -1,0 +1,223 @@
+"""Pins of the oracle's NF4 + double quantization ("QLoRA 原理精讲", sections 2.1-2.2)."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from qlora_linear_layers_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bf16_block(rng, nblocks, std=0.02):
+    return oracle.bf16_bits_to_f32(synth.to_bf16_bits(rng.standard_normal(nblocks * 64).astype(np.float32) * std))
+
+
+# ---------------------------------------------------------------- NF4 encode
+
+def test_encode_brute_force_fraction():
+    """Exact-rational nearest codeword over all 16, ties to the lower index."""
+    rng = np.random.default_rng(0)
+    w = _bf16_block(rng, 6)
+    w[64:128] *= 1e-30                     # tiny magnitudes
+    w[128:192] = np.round(w[128:192] * 1e3) / 1e3
+    w = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits(w))
+    c1 = oracle.block_absmax(w)
+    got = oracle.nf4_encode(w, c1)
+    q = [Fraction(float(v)) for v in oracle.nf4_codebook()]
+    for i, wi in enumerate(w):
+        c = Fraction(float(c1[i // 64]))
+        if c == 0:
+            assert got[i] == 7
+            continue
+        n = Fraction(float(wi)) / c
+        d = [abs(n - qi) for qi in q]
+        assert got[i] == d.index(min(d)), (i, wi)
+
+
+def test_fp32_division_equals_exact_ratio_for_all_bf16_pairs():
+    """For every bf16 pair (w, c1) with |w| <= c1, the code from fl32(w/c1) equals the
+    code from the exact ratio: the fp32 rounding never crosses a midpoint."""
+    mids = oracle.nf4_midpoints()
+    sig = np.arange(1, 256, dtype=np.float64)            # all bf16 significands (normal + subnormal)
+    for qs in range(1, 256):
+        for dexp in range(0, 10):
+            w = sig * 2.0 ** -dexp                       # exponent-shifted numerators
+            w = w[w <= qs]
+            for sign in (1.0, -1.0):
+                ws, cs = sign * w * 2.0 ** -20, float(qs) * 2.0 ** -20
+                n32 = (ws.astype(np.float32) / np.float32(cs)).astype(np.float64)
+                code_fl = (n32[:, None] > mids).sum(1)
+                # exact: w/c > m  <=>  w > c*m, and c*m is exact in fp64 (8 x 26 bits)
+                code_ex = (ws[:, None] > cs * mids[None, :]).sum(1)
+                assert np.array_equal(code_fl, code_ex), (qs, dexp, sign)
+
+
+def test_zero_block_and_absmax_element():
+    w = np.zeros(128, np.float32)
+    w[64 + 5] = -0.5
+    w[64 + 9] = 0.25
+    c1 = oracle.block_absmax(w)
+    codes = oracle.nf4_encode(w, c1)
+    assert np.all(codes[:64] == 7)
+    assert codes[64 + 5] == 0 and codes[64 + 9] == 12      # 0.5 -> between q12 and q13 midpoint
+    rng = np.random.default_rng(1)
+    w = _bf16_block(rng, 50)
+    codes = oracle.nf4_encode(w, oracle.block_absmax(w)).reshape(-1, 64)
+    arg = np.abs(w.reshape(-1, 64)).argmax(1)
+    picked = codes[np.arange(50), arg]
+    assert np.all((picked == 0) | (picked == 15))
+
+
+def test_pack_nibble_order_and_roundtrip():
+    codes = np.array([0xA, 0x3, 0x0, 0xF, 0x7, 0x7], np.uint8)
+    assert list(oracle.pack_codes(codes)) == [0xA3, 0x0F, 0x77]
+    rng = np.random.default_rng(2)
+    c = rng.integers(0, 16, 4096).astype(np.uint8)
+    assert np.array_equal(oracle.unpack_codes(oracle.pack_codes(c)), c)
+    for i in range(16):                        # one-hot position lands in the right nibble
+        one = np.zeros(16, np.uint8)
+        one[i] = 9
+        p = oracle.pack_codes(one)
+        assert p[i // 2] == (0x90 if i % 2 == 0 else 0x09) and p.sum() == p[i // 2]
+
+
+# ---------------------------------------------------------------- FP8 E4M3FN
+
+def test_e4m3_values_match_torch_decode():
+    vals = oracle.e4m3fn_values()
+    assert vals.size == 127 and np.all(np.diff(vals) > 0) and vals[-1] == 448.0
+    ref = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(vals, ref)
+
+
+def test_e4m3_encode_matches_torch_off_ties():
+    rng = np.random.default_rng(3)
+    y = np.concatenate([rng.uniform(0, 448, 100_000), np.exp(rng.uniform(-14, 6.1, 100_000))])
+    y = np.minimum(y, 448).astype(np.float32)
+    vals = oracle.e4m3fn_values()
+    mids = (vals[:-1] + vals[1:]) / 2
+    y = y[~np.isin(y.astype(np.float64), mids)]
+    got = oracle.e4m3fn_encode(y)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_ties_go_to_lower_code():
+    vals = oracle.e4m3fn_values()
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (vals[:-1] + vals[1:]) / 2)   # exact in fp32
+    assert np.array_equal(oracle.e4m3fn_encode(mids), np.arange(126, dtype=np.uint8))
+    assert oracle.e4m3fn_encode(np.float32(448.0))[0] == 0x7E
+    assert oracle.e4m3fn_encode(np.float32(0.0))[0] == 0
+    assert oracle.e4m3fn_encode(np.float32(2.0 ** -10))[0] == 0           # tie 0 / 2^-9 -> 0
+    assert oracle.e4m3fn_encode(np.float32(3 * 2.0 ** -10))[0] == 1       # tie 2^-9 / 2^-8 -> 1
+
+
+def test_double_quantize_groups():
+    rng = np.random.default_rng(4)
+    c1 = np.abs(rng.standard_normal(256 * 3 + 17)).astype(np.float32) * 0.05
+    c1[256:512] = 0                                   # an all-zero group
+    f, s = oracle.double_quantize(c1)
+    assert s.size == 4 and s[1] == 0 and np.all(f[256:512] == 0)
+    for g in (0, 2, 3):
+        grp = c1[g * 256:(g + 1) * 256]
+        assert s[g] == np.float32(grp.max()) / np.float32(448)
+        assert f[g * 256 + grp.argmax()] == 0x7E      # the group max maps to the top code
+    # reconstruction is within half an E4M3 step (relative 1/16) of each constant (normal range)
+    c1p = oracle.double_dequantize_scales(f, s)
+    ok = c1 >= s.repeat(256)[:c1.size] * 2.0 ** -6
+    assert np.all(np.abs(c1p[ok] - c1[ok]) <= c1[ok] / 16 + 1e-12)
+
+
+def test_double_quantize_idempotent():
+    rng = np.random.default_rng(5)
+    c1 = np.abs(rng.standard_normal(256 * 8)).astype(np.float32)
+    f, s = oracle.double_quantize(c1)
+    c1p = oracle.double_dequantize_scales(f, s)
+    f2, s2 = oracle.double_quantize(c1p)
+    assert np.array_equal(f, f2)
+
+
+# ---------------------------------------------------------------- full quantize / dequantize
+
+def test_quantize_dequantize_roundtrip_idempotent():
+    """quantize(dequantize(codes)) reproduces the codes (Gaussian and outlier weights)."""
+    for cfg, outl in ((1, False), (5, True)):
+        rng = synth.rng_for(cfg, 0, 0, synth.ROLE_W)
+        w = (synth.outlier_weight_bf16(rng, (64, 4096)) if outl
+             else synth.normal_bf16(rng, (64, 4096), 0.02))
+        packed, f, s = oracle.quantize_nf4_dq(w)
+        wd = oracle.dequantize_nf4_dq(packed, f, s, w.size)
+        packed2, _, _ = oracle.quantize_nf4_dq(wd)
+        assert np.array_equal(packed, packed2)
+
+
+def test_dequant_zero_code_and_error_bound():
+    rng = synth.rng_for(1, 0, 0, synth.ROLE_W)
+    w_bits = synth.normal_bf16(rng, (32, 4096), 0.02)
+    packed, f, s = oracle.quantize_nf4_dq(w_bits)
+    wd = oracle.bf16_bits_to_f32(oracle.dequantize_nf4_dq(packed, f, s)).astype(np.float64)
+    codes = oracle.unpack_codes(packed)
+    assert np.all(wd[codes == 7] == 0) and not np.any(np.signbit(wd[codes == 7]))
+    w = oracle.bf16_bits_to_f32(w_bits).astype(np.float64).reshape(-1)
+    c1 = np.repeat(oracle.block_absmax(w.astype(np.float32)).astype(np.float64), 64)
+    c1p = np.repeat(oracle.double_dequantize_scales(f, s).astype(np.float64), 64)
+    gap = np.diff(oracle.nf4_codebook().astype(np.float64)).max() / 2      # 0.1519
+    bound = gap * c1 + np.abs(c1 - c1p) + np.abs(wd) * 2.0 ** -8
+    assert np.all(np.abs(wd - w) <= bound)
+    rel_rms = np.sqrt(np.mean((wd - w) ** 2) / np.mean(w ** 2))
+    assert 0.05 < rel_rms < 0.15
+
+
+def test_dequantize_rows_matches_full():
+    rng = synth.rng_for(1, 0, 1, synth.ROLE_W)
+    N, K = 24, 11008 // 2
+    K -= K % 64
+    w = synth.normal_bf16(rng, (N, K), 0.02)
+    packed, f, s = oracle.quantize_nf4_dq(w)
+    full = oracle.dequantize_nf4_dq(packed, f, s).reshape(N, K)
+    rows = [0, 3, 17, 23, 3]
+    assert np.array_equal(oracle.dequantize_rows(packed, f, s, N, K, rows), full[rows])
+
+
+def test_partial_last_group():
+    rng = np.random.default_rng(6)
+    w = synth.to_bf16_bits(rng.standard_normal(64 * 300).astype(np.float32))
+    packed, f, s = oracle.quantize_nf4_dq(w)
+    assert packed.size == 64 * 150 and f.size == 300 and s.size == 2
+
+
+# ---------------------------------------------------------------- storage arithmetic
+
+def _golden():
+    with open(os.path.join(GOLDEN, "memory_arithmetic.json")) as fh:
+        return {e["id"]: e for e in json.load(fh)["entries"]}
+
+
+def test_storage_closed_form_and_pages_figures():
+    g = _golden()
+    n = 64 * 256 * 1000
+    bits = 8 * oracle.storage_bytes(n) / n
+    assert bits == 4 + 8 / 64 + 32 / (64 * 256) == 4.126953125
+    P = 70e9
+    assert 32 / 64 == g["fp32_scale_overhead_bits"]["value"]
+    assert abs(P * 0.5 / 8 / 1e9 - g["fp32_scale_overhead_70b_gb"]["value"]) <= g["fp32_scale_overhead_70b_gb"]["tol"]
+    dq = bits - 4
+    assert abs(dq - g["dq_overhead_bits"]["value"]) <= g["dq_overhead_bits"]["tol"]
+    assert abs(P * (0.5 - dq) / 8 / 1e9 - g["dq_saving_70b_gb"]["value"]) <= g["dq_saving_70b_gb"]["tol"]
+    assert P * 2 / 1e9 == g["bf16_70b_weights_gb"]["value"]
+    assert P * 4 / 8 / 1e9 == g["nf4_70b_weights_gb"]["value"]
+    assert 1 - 4 / 16 == g["weight_memory_saving_frac"]["value"]
+
+
+def test_70b_stream_packed_total():
+    per_layer = sum(oracle.storage_bytes(l.N * l.K) for l in synth.LLAMA70B)
+    params = sum(l.N * l.K for l in synth.LLAMA70B) * 80
+    assert params == 68_451_041_280
+    assert per_layer * 80 == 35_311_779_840
