@@ -1,0 +1,163 @@
+/*
+ * qlora.h - C ABI of the MI355X (gfx950) QLoRA frozen-base linear layer.
+ *
+ * The layer keeps a frozen weight W [N, K] in 4-bit NormalFloat (NF4) with
+ * double quantization, and adds a trainable low-rank bf16 adapter (A [K, r],
+ * B [r, N]) on top of it.  Sources (page titles and the part of each page):
+ *   - "QLoRA 原理精讲" (1.2.3), section 2.1: NF4 codebook from N(0,1) quantiles,
+ *     per-block absmax (64 weights) and nearest-codeword lookup;
+ *     section 2.2 and its storage figure: the fp32 block constants are
+ *     quantized again to FP8, 256 per fp32 super-scale; storage is the 4-bit
+ *     codes + FP8 constants + fp32 super-scales; dequantization runs in
+ *     reverse order (super-scale, then constant, then weight).
+ *   - "从LoRA到QLoRA：量化技术如何改变预训练模型的微调方式", section 2.3 (NF4 on
+ *     [-1, 1]) and section 3.1 (storage type NF4, compute type bf16;
+ *     gradients reach the LoRA adapters through the frozen base).
+ *   - Volcengine article on LoRA / Q-LoRA / PortLLM, section 3.4: the QLoRA
+ *     linear layer (its equation was lost in extraction; the reading used here
+ *     is Y = X W'^T + s (X A) B with s = alpha / r).
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense row-major DEVICE pointers owned by the caller.  bf16
+ *     values are passed as uint16_t bit patterns.  Every pointer must be 16-byte
+ *     aligned.  The library never allocates or frees device memory and keeps
+ *     no per-call state; the only global state is its immutable codebook.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     on it and the call returns before it completes; a device fault surfaces
+ *     at the caller's next synchronisation.
+ *   - Every call validates its arguments on the host BEFORE launching anything:
+ *     on a non-zero status nothing has been launched and no output was touched.
+ *     Functions never throw across the ABI.
+ *   - Blocks are 64 consecutive elements of the flattened weight, groups are 256
+ *     consecutive blocks (the last group may be partial).  Both are fixed.
+ *   - Inputs must be finite; the result for non-finite inputs is unspecified.
+ *   - Storage of a quantized W with numel = N*K elements:
+ *       codes       uint8 [numel/2]          two 4-bit codes per byte, even element in the high nibble
+ *       absmax_fp8  uint8 [numel/64]         FP8 E4M3FN code of each block's absmax (scaled by the group super-scale)
+ *       superscale  float [ceil(numel/16384)] one fp32 super-scale per group of 256 blocks
+ */
+#ifndef QLORA_MI355X_H
+#define QLORA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum {
+    QLORA_OK = 0,
+    QLORA_ERR_NULL = 1,       /* a required pointer is NULL                                  */
+    QLORA_ERR_SHAPE = 2,      /* a size is out of range (numel % 64, K % 64, T < 1, r, ...)   */
+    QLORA_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned                            */
+    QLORA_ERR_VALUE = 4,      /* a scalar argument is not finite                             */
+    QLORA_ERR_WORKSPACE = 5,  /* workspace is NULL or smaller than qlora_workspace_bytes()   */
+    QLORA_ERR_DEVICE = 6      /* the HIP runtime reported an error (launch, device query)    */
+} qlora_status;
+
+#define QLORA_BLOCK 64
+#define QLORA_GROUP 256
+#define QLORA_MAX_RANK 256
+
+/*
+ * nf4_build_codebook - the 16 NF4 codewords, ascending (index = 4-bit code).
+ *   Source: "QLoRA 原理精讲" section 2.1 and "从LoRA到QLoRA" section 2.3: N(0,1)
+ *   quantiles at evenly spaced probabilities, normalised to [-1, 1].  Reading
+ *   of the lost formula: 8 positive codewords Phi^-1(1/2 + j(d-1/2)/8)/z
+ *   (j = 1..8), 7 negative ones -Phi^-1(1/2 + j(d-1/2)/7)/z (j = 1..7) and an
+ *   exact 0, with d = ((1-1/30) + (1-1/32))/2 and z = Phi^-1(d); computed in
+ *   fp64 and rounded once to fp32, so out[0] = -1, out[7] = +0, out[15] = +1.
+ *   codebook_out: HOST pointer to 16 floats, written.  Pure host code, no GPU.
+ *   Errors: QLORA_ERR_NULL.
+ */
+int nf4_build_codebook(float codebook_out[16]);
+
+/*
+ * nf4_quantize_dq - blockwise NF4 quantization with double quantization.
+ *   Source: "QLoRA 原理精讲" sections 2.1-2.2.  Per block of 64: c1 = max|w|,
+ *   n = fl32(w / c1), code = nearest codeword (exact ties to the lower code;
+ *   an all-zero block gives code 7).  Per group of 256 blocks:
+ *   s2 = fl32(max c1 / 448); each c1 becomes the E4M3FN code nearest to
+ *   min(fl32(c1 / s2), 448), exact ties to the lower code (s2 = 0 -> codes 0).
+ *   w          [numel] bf16 (device), read.
+ *   numel      number of elements, > 0 and a multiple of 64.
+ *   codes      [numel/2] uint8 (device), written.
+ *   absmax_fp8 [numel/64] uint8 (device), written.
+ *   superscale [ceil(numel/16384)] float (device), written.
+ *   Errors: NULL, SHAPE, ALIGN, DEVICE.
+ */
+int nf4_quantize_dq(const uint16_t* w, int64_t numel,
+                    uint8_t* codes, uint8_t* absmax_fp8, float* superscale,
+                    void* stream);
+
+/*
+ * nf4_dequantize_dq - double dequantization back to bf16.
+ *   Source: "QLoRA 原理精讲" section 2.2 (reverse order).  For block b of group g:
+ *   c1' = fl32(e4m3(absmax_fp8[b]) * superscale[g]);
+ *   w'  = RNE_bf16(fl32(q[code] * c1')).
+ *   codes, absmax_fp8, superscale: the storage triple (device), read.
+ *   numel  > 0, multiple of 64.   w_out [numel] bf16 (device), written.
+ *   Errors: NULL, SHAPE, ALIGN, DEVICE.
+ */
+int nf4_dequantize_dq(const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale,
+                      int64_t numel, uint16_t* w_out, void* stream);
+
+/*
+ * qlora_workspace_bytes - device workspace (bytes) that qlora_linear_fwd and
+ *   qlora_linear_bwd_input need for these sizes (the larger of the two).
+ *   Returns 0 for sizes the entry points would reject.
+ */
+size_t qlora_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r);
+
+/*
+ * qlora_linear_fwd - fused forward of one QLoRA linear layer.
+ *   Source: Volcengine article section 3.4 (equation lost; reading above) and
+ *   "从LoRA到QLoRA" section 3.1 (dequantize to bf16 on the fly).
+ *     Y = X W'^T + scaling * (X A) B,   fp32 accumulation, bf16 output.
+ *   W' is the double-dequantized bf16 weight (same values nf4_dequantize_dq
+ *   writes); it is never materialised in HBM.
+ *   x [T, K] bf16; codes/absmax_fp8/superscale: W [N, K] quantized as above;
+ *   lora_a [K, r] bf16, lora_b [r, N] bf16 (both NULL iff r == 0);
+ *   y [T, N] bf16, written.  T >= 1, K and N multiples of 64, r = 0 or a
+ *   multiple of 8 up to 256.
+ *   workspace: device scratch of at least qlora_workspace_bytes(T, K, N, r)
+ *   bytes (may be NULL if that is 0); its contents on entry do not matter.
+ *   Errors: NULL, SHAPE, ALIGN, VALUE (non-finite scaling), WORKSPACE, DEVICE.
+ */
+int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N,
+                     const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale,
+                     const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling,
+                     uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qlora_linear_bwd_input - backward of the layer through the frozen base.
+ *   Source: "从LoRA到QLoRA" sections 1.3 and 3.1 (gradients flow through the
+ *   frozen 4-bit base into the adapters; only the adapters get weight
+ *   gradients); "QLoRA 原理精讲" section 3 (adapters stay bf16).
+ *     dX = dY W' + scaling * (dY B^T) A^T
+ *     dA = scaling * X^T (dY B^T)        (only if d_lora_a != NULL)
+ *     dB = scaling * (X A)^T dY          (only if d_lora_b != NULL)
+ *   fp32 accumulation, bf16 outputs.
+ *   dy [T, N] bf16; W as in qlora_linear_fwd; dx [T, K] bf16, written;
+ *   x [T, K] bf16, required iff d_lora_a or d_lora_b is non-NULL;
+ *   d_lora_a [K, r] and d_lora_b [r, N] bf16, written when non-NULL
+ *   (must be NULL when r == 0).
+ *   Errors: NULL, SHAPE, ALIGN, VALUE, WORKSPACE, DEVICE.
+ */
+int qlora_linear_bwd_input(const uint16_t* dy, int64_t T, int64_t K, int64_t N,
+                           const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale,
+                           const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling,
+                           uint16_t* dx, const uint16_t* x,
+                           uint16_t* d_lora_a, uint16_t* d_lora_b,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* qlora_status_string - static, NUL-terminated description of a status code. */
+const char* qlora_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_MI355X_H */

@@ -51,15 +51,22 @@ def block_absmax(w_f32):
 
 
 def nf4_encode(w_f32, absmax):
-    """4-bit code per element, as in the per-block pseudocode: normalise, nearest codeword."""
+    """4-bit code per element, as in the per-block pseudocode: normalise, nearest codeword.
+
+    code = number of midpoints strictly below n = fl32(w / c1) (``searchsorted``
+    with side='left' counts exactly those), so an exact tie keeps the lower code.
+    """
     w = np.asarray(w_f32, dtype=np.float32).reshape(-1, BLOCK)
     c1 = np.asarray(absmax, dtype=np.float32).reshape(-1, 1)
     mids = nf4_midpoints()
     codes = np.full(w.shape, ZERO_CODE, dtype=np.uint8)
-    nz = c1[:, 0] > 0
-    if np.any(nz):
-        n = w[nz] / c1[nz]                          # fp32 division, correctly rounded
-        codes[nz] = (n.astype(np.float64)[..., None] > mids).sum(axis=-1).astype(np.uint8)
+    step = 1 << 18                                   # blocks per chunk (memory bound only)
+    for s in range(0, w.shape[0], step):
+        wc, cc = w[s:s + step], c1[s:s + step]
+        nz = cc[:, 0] > 0
+        if np.any(nz):
+            n = wc[nz] / cc[nz]                      # fp32 division, correctly rounded
+            codes[s:s + step][nz] = np.searchsorted(mids, n.astype(np.float64), side="left").astype(np.uint8)
     return codes.reshape(-1)
 
 

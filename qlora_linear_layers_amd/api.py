@@ -1,0 +1,179 @@
+"""Thin Python binding over the C ABI of ``libqlora_mi355x.so`` (``include/qlora.h``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels.  torch provides device memory (tensors) and the current stream.  The
+names match the C entry points.  A missing library raises ``RuntimeError``;
+there is no fallback.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora_mi355x.so")
+
+_c_p = ctypes.c_void_p
+_c_i64 = ctypes.c_int64
+_SIGS = {
+    "nf4_build_codebook": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
+    "nf4_quantize_dq": (ctypes.c_int, [_c_p, _c_i64, _c_p, _c_p, _c_p, _c_p]),
+    "nf4_dequantize_dq": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_p, _c_p]),
+    "qlora_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64]),
+    "qlora_linear_fwd": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                                        ctypes.c_float, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "qlora_linear_bwd_input": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                                              ctypes.c_float, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+EXPORTS = tuple(_SIGS)
+
+_lib = None
+
+
+class QLoraError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: status {status} ({lib().qlora_status_string(status).decode()})")
+        self.status = status
+
+
+def lib():
+    """Load the in-tree HIP library (built by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise QLoraError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class NF4Weight:
+    """Storage triple of a quantized [N, K] weight (device tensors)."""
+    codes: torch.Tensor       # uint8 [N*K/2]
+    absmax_fp8: torch.Tensor  # uint8 [N*K/64]
+    superscale: torch.Tensor  # float32 [ceil(N*K/16384)]
+    N: int
+    K: int
+
+    @property
+    def numel(self):
+        return self.N * self.K
+
+    def nbytes(self):
+        return self.codes.numel() + self.absmax_fp8.numel() + 4 * self.superscale.numel()
+
+
+def nf4_build_codebook():
+    out = (ctypes.c_float * 16)()
+    _check("nf4_build_codebook", lib().nf4_build_codebook(out))
+    return torch.tensor(list(out), dtype=torch.float32)
+
+
+def nf4_quantize_dq(w):
+    """bf16 weight [N, K] (or flat) on the GPU -> NF4Weight."""
+    _dev(w, torch.bfloat16, "w")
+    numel = w.numel()
+    N, K = (w.shape[0], w.shape[1]) if w.dim() == 2 else (1, numel)
+    codes = torch.empty(numel // 2, dtype=torch.uint8, device=w.device)
+    fp8 = torch.empty(max(numel // 64, 1), dtype=torch.uint8, device=w.device)
+    sup = torch.empty(max(-(-numel // 16384), 1), dtype=torch.float32, device=w.device)
+    _check("nf4_quantize_dq", lib().nf4_quantize_dq(_ptr(w), numel, _ptr(codes), _ptr(fp8), _ptr(sup), _stream()))
+    return NF4Weight(codes, fp8, sup, N, K)
+
+
+def nf4_quantize_dq_into(w, qw):
+    """Quantize into an existing NF4Weight (no allocation)."""
+    _dev(w, torch.bfloat16, "w")
+    _check("nf4_quantize_dq", lib().nf4_quantize_dq(_ptr(w), w.numel(), _ptr(qw.codes), _ptr(qw.absmax_fp8),
+                                                     _ptr(qw.superscale), _stream()))
+
+
+def nf4_dequantize_dq(qw, out=None):
+    """NF4Weight -> bf16 [N, K] on the GPU."""
+    if out is None:
+        out = torch.empty((qw.N, qw.K), dtype=torch.bfloat16, device=qw.codes.device)
+    _dev(out, torch.bfloat16, "out")
+    _check("nf4_dequantize_dq", lib().nf4_dequantize_dq(_ptr(qw.codes), _ptr(qw.absmax_fp8), _ptr(qw.superscale),
+                                                         qw.numel, _ptr(out), _stream()))
+    return out
+
+
+def qlora_workspace_bytes(T, K, N, r):
+    return int(lib().qlora_workspace_bytes(T, K, N, r))
+
+
+def workspace_for(T, K, N, r, device):
+    n = qlora_workspace_bytes(T, K, N, r)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def qlora_linear_fwd(x, qw, lora_a=None, lora_b=None, scaling=1.0, workspace=None, out=None):
+    """Y = X W'^T + scaling (X A) B; x [T, K] bf16 -> y [T, N] bf16."""
+    _dev(x, torch.bfloat16, "x")
+    _dev(lora_a, torch.bfloat16, "lora_a")
+    _dev(lora_b, torch.bfloat16, "lora_b")
+    T, K = x.shape
+    r = 0 if lora_a is None else lora_a.shape[1]
+    if out is None:
+        out = torch.empty((T, qw.N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = workspace_for(T, K, qw.N, r, x.device)
+    _check("qlora_linear_fwd", lib().qlora_linear_fwd(
+        _ptr(x), T, K, qw.N, _ptr(qw.codes), _ptr(qw.absmax_fp8), _ptr(qw.superscale), _ptr(lora_a), _ptr(lora_b),
+        r, float(scaling), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def qlora_linear_bwd_input(dy, qw, lora_a=None, lora_b=None, scaling=1.0, x=None, lora_grads=False,
+                           workspace=None, dx=None, d_lora_a=None, d_lora_b=None):
+    """dX (and dA, dB when lora_grads) for upstream gradient dy [T, N] bf16."""
+    _dev(dy, torch.bfloat16, "dy")
+    _dev(x, torch.bfloat16, "x")
+    T, N = dy.shape
+    K = qw.K
+    r = 0 if lora_a is None else lora_a.shape[1]
+    if dx is None:
+        dx = torch.empty((T, K), dtype=torch.bfloat16, device=dy.device)
+    if lora_grads:
+        if d_lora_a is None:
+            d_lora_a = torch.empty((K, r), dtype=torch.bfloat16, device=dy.device)
+        if d_lora_b is None:
+            d_lora_b = torch.empty((r, N), dtype=torch.bfloat16, device=dy.device)
+    if workspace is None:
+        workspace = workspace_for(T, K, N, r, dy.device)
+    _check("qlora_linear_bwd_input", lib().qlora_linear_bwd_input(
+        _ptr(dy), T, K, N, _ptr(qw.codes), _ptr(qw.absmax_fp8), _ptr(qw.superscale), _ptr(lora_a), _ptr(lora_b),
+        r, float(scaling), _ptr(dx), _ptr(x), _ptr(d_lora_a) if lora_grads else None,
+        _ptr(d_lora_b) if lora_grads else None, _ptr(workspace), workspace.numel(), _stream()))
+    return (dx, d_lora_a, d_lora_b) if lora_grads else (dx, None, None)

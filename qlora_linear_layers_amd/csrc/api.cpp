@@ -1,0 +1,138 @@
+// extern "C" entry points declared in include/qlora.h: host-side validation,
+// workspace carving and kernel sequencing.  No device memory is allocated
+// here; every buffer comes from the caller.
+#include <cmath>
+
+#include "qlora.h"
+#include "common.hpp"
+#include "plan.hpp"
+
+namespace ql {
+hipError_t launch_lora_down_x(const uint16_t* x, const uint16_t* lora_a, float scaling, const LoraPlan& pl,
+                              uint8_t* ws, hipStream_t s);
+hipError_t launch_lora_down_dy(const uint16_t* dy, const uint16_t* lora_b, float scaling, const LoraPlan& pl,
+                               uint8_t* ws, hipStream_t s);
+hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* fp8, const float* sup,
+                      const uint16_t* lora_b, const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s);
+hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* fp8, const float* sup,
+                     const uint16_t* lora_a, const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s);
+hipError_t launch_lora_grads(const uint16_t* x, const uint16_t* dy, const LoraPlan& pl, uint8_t* ws,
+                             uint16_t* d_lora_a, uint16_t* d_lora_b, hipStream_t s);
+}  // namespace ql
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int dev(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_DEVICE; }
+
+// Shape rules shared by the linear entry points.
+int check_linear_shape(int64_t T, int64_t K, int64_t N, int64_t r) {
+    if (T < 1 || K < 64 || N < 64 || K % 64 || N % 64) return QLORA_ERR_SHAPE;
+    if (r < 0 || r > QLORA_MAX_RANK || (r > 0 && r % 8)) return QLORA_ERR_SHAPE;
+    if (T > (int64_t(1) << 31) / 256 || K > (int64_t(1) << 30) || N > (int64_t(1) << 30)) return QLORA_ERR_SHAPE;
+    if (N * K > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
+    return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qlora_status_string(int status) {
+    switch (status) {
+        case QLORA_OK: return "ok";
+        case QLORA_ERR_NULL: return "a required pointer is NULL";
+        case QLORA_ERR_SHAPE: return "a size is out of range";
+        case QLORA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case QLORA_ERR_VALUE: return "a scalar argument is not finite";
+        case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
+        case QLORA_ERR_DEVICE: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int nf4_build_codebook(float codebook_out[16]) {
+    if (!codebook_out) return QLORA_ERR_NULL;
+    const ql::Codebook& cb = ql::host_codebook();
+    for (int i = 0; i < 16; ++i) codebook_out[i] = cb.q[i];
+    return QLORA_OK;
+}
+
+int nf4_quantize_dq(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* absmax_fp8, float* superscale,
+                    void* stream) {
+    if (!w || !codes || !absmax_fp8 || !superscale) return QLORA_ERR_NULL;
+    if (numel <= 0 || numel % 64 || numel > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(codes) || !aligned16(absmax_fp8) || !aligned16(superscale))
+        return QLORA_ERR_ALIGN;
+    return dev(ql::launch_quantize(w, numel, codes, absmax_fp8, superscale, static_cast<hipStream_t>(stream)));
+}
+
+int nf4_dequantize_dq(const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale, int64_t numel,
+                      uint16_t* w_out, void* stream) {
+    if (!codes || !absmax_fp8 || !superscale || !w_out) return QLORA_ERR_NULL;
+    if (numel <= 0 || numel % 64 || numel > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
+    if (!aligned16(w_out) || !aligned16(codes) || !aligned16(absmax_fp8) || !aligned16(superscale))
+        return QLORA_ERR_ALIGN;
+    return dev(ql::launch_dequantize(codes, absmax_fp8, superscale, numel, w_out, static_cast<hipStream_t>(stream)));
+}
+
+size_t qlora_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r) {
+    if (check_linear_shape(T, K, N, r) != QLORA_OK) return 0;
+    return ql::LoraPlan(T, K, N, r).bwd_grad_bytes;
+}
+
+int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* codes,
+                     const uint8_t* absmax_fp8, const float* superscale, const uint16_t* lora_a,
+                     const uint16_t* lora_b, int64_t r, float scaling, uint16_t* y, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    if (!x || !codes || !absmax_fp8 || !superscale || !y) return QLORA_ERR_NULL;
+    if (r > 0 && (!lora_a || !lora_b)) return QLORA_ERR_NULL;
+    if (int st = check_linear_shape(T, K, N, r)) return st;
+    if (r == 0 && (lora_a || lora_b)) return QLORA_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(absmax_fp8) || !aligned16(superscale) || !aligned16(y) ||
+        (lora_a && !aligned16(lora_a)) || (lora_b && !aligned16(lora_b)) || (workspace && !aligned16(workspace)))
+        return QLORA_ERR_ALIGN;
+    if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
+    const ql::LoraPlan pl(T, K, N, r);
+    if (pl.fwd_bytes && (!workspace || workspace_bytes < pl.fwd_bytes)) return QLORA_ERR_WORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    if (r > 0)
+        if (int st = dev(ql::launch_lora_down_x(x, lora_a, scaling, pl, ws, s))) return st;
+    return dev(ql::launch_fwd(x, codes, absmax_fp8, superscale, lora_b, pl, ws, y, s));
+}
+
+int qlora_linear_bwd_input(const uint16_t* dy, int64_t T, int64_t K, int64_t N, const uint8_t* codes,
+                           const uint8_t* absmax_fp8, const float* superscale, const uint16_t* lora_a,
+                           const uint16_t* lora_b, int64_t r, float scaling, uint16_t* dx, const uint16_t* x,
+                           uint16_t* d_lora_a, uint16_t* d_lora_b, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    if (!dy || !codes || !absmax_fp8 || !superscale || !dx) return QLORA_ERR_NULL;
+    if (r > 0 && (!lora_a || !lora_b)) return QLORA_ERR_NULL;
+    const bool grads = d_lora_a || d_lora_b;
+    if (grads && !x) return QLORA_ERR_NULL;
+    if (int st = check_linear_shape(T, K, N, r)) return st;
+    if (r == 0 && (lora_a || lora_b || grads)) return QLORA_ERR_SHAPE;
+    const void* ptrs[] = {dy, codes, absmax_fp8, superscale, dx, x, lora_a, lora_b, d_lora_a, d_lora_b, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
+    if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
+    const ql::LoraPlan pl(T, K, N, r);
+    const size_t need = grads ? pl.bwd_grad_bytes : pl.bwd_bytes;
+    if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    if (r > 0)
+        if (int st = dev(ql::launch_lora_down_dy(dy, lora_b, scaling, pl, ws, s))) return st;
+    if (int st = dev(ql::launch_dx(dy, codes, absmax_fp8, superscale, lora_a, pl, ws, dx, s))) return st;
+    if (grads) {
+        if (int st = dev(ql::launch_lora_down_x(x, lora_a, scaling, pl, ws, s))) return st;
+        if (int st = dev(ql::launch_lora_grads(x, dy, pl, ws, d_lora_a, d_lora_b, s))) return st;
+    }
+    return QLORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Shared device helpers and host-side launch declarations for the gfx950
+// QLoRA library.  Everything here is written for CDNA4 (wave64, MFMA, 160 KB
+// LDS); there is no other target.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define QL_DEV __device__ __forceinline__
+
+namespace ql {
+
+constexpr int kBlock = 64;    // weights per NF4 block
+constexpr int kGroup = 256;   // blocks per fp32 super-scale
+
+// The 16 NF4 codewords (fp32, ascending; index = code).  Passed to kernels by
+// value as a kernel argument and copied to LDS at kernel start.
+struct Codebook {
+    float q[16];
+};
+
+// Encoder lookup over n in [-1, 1]: cell = trunc(16 n + 16) in [0, 32]; the
+// code is base[cell] + (n > thr[cell]).  Each cell of width 1/16 holds at most
+// one decision midpoint (neighbouring midpoints are >= 0.08 apart), whose
+// round-down fp32 value is thr[cell] (cells without one carry thr = 2).
+struct EncodeTable {
+    float thr[34];
+    uint32_t base[34];
+};
+
+// Host: the library's codebook and encoder table (computed once, thread-safe).
+const Codebook& host_codebook();
+const EncodeTable& host_encode_table();
+
+// ------------------------------------------------------------------ bf16
+
+QL_DEV float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+QL_DEV float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even of two fp32 values into one packed dword: `a` in the
+// low half (lower address), `b` in the high half (v_cvt_pk_bf16_f32).
+QL_DEV uint32_t pack_bf16x2(float a, float b) {
+    f32x2_t v = {a, b};
+    bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// ------------------------------------------------------------------ FP8 E4M3FN
+
+// Exact value of a non-negative E4M3FN code (0x00..0x7E): bias 7, 3 fraction
+// bits, subnormal spacing 2^-9.
+QL_DEV float e4m3_decode(uint32_t code) {
+    const uint32_t e = (code >> 3) & 0xF, m = code & 7;
+    const float sub = (float)m * 0.001953125f;                   // m * 2^-9, exact
+    const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return e ? nrm : sub;
+}
+
+// Nearest E4M3FN code to y in [0, 448]; an exact tie goes to the lower code.
+QL_DEV uint32_t e4m3_encode_tie_low(float y) {
+    if (y < 0.015625f) {                                         // below 2^-6: fixed spacing 2^-9
+        const float s = y * 512.0f;                              // exact
+        const float f = floorf(s);
+        return (uint32_t)f + ((s - f) > 0.5f ? 1u : 0u);         // 8 -> code 0x08 = 2^-6
+    }
+    const uint32_t b = __float_as_uint(y);
+    const uint32_t code = ((((b >> 23) & 0xFF) - 120u) << 3) | ((b >> 20) & 7u);
+    return code + ((b & 0xFFFFFu) > 0x80000u ? 1u : 0u);        // strictly above half -> up
+}
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* fp8,
+                           float* superscale, hipStream_t s);
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* fp8, const float* superscale,
+                             int64_t numel, uint16_t* out, hipStream_t s);
+
+}  // namespace ql

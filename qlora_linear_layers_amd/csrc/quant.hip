@@ -1,0 +1,176 @@
+// NF4 quantization with double quantization, and double dequantization, for
+// gfx950.  Both kernels are HBM-bound streams; they are written for 128-bit
+// coalesced loads and stores and keep the codebook / encoder table in LDS.
+//
+// Method: "QLoRA 原理精讲" section 2.1 (absmax per block of 64, nearest of the 16
+// NF4 codewords) and section 2.2 with its storage figure (the block constants
+// quantized to FP8 in groups of 256 under one fp32 super-scale; dequantization
+// in reverse order).
+#include "common.hpp"
+
+namespace ql {
+
+// -------------------------------------------------------------------- quantize
+//
+// One workgroup (4 wave64) per group of 256 blocks = 16384 bf16 (32 KB).  Thread
+// t handles 16-byte chunk j*256 + t for j = 0..7, so the eight lanes of each
+// 8-lane cluster hold one 64-element block; block absmax is an integer max of
+// |bf16| bit patterns (order-preserving for non-negative values) across the
+// cluster.  Encoding avoids a division: n = w * rcp(c1) has a relative error
+// below 2^-22, while no ratio of two bf16 values lies closer than 2^-19.4
+// (relative) to a decision midpoint, so comparing n with the round-down fp32
+// midpoint gives the same code as the exact ratio.  Blocks whose c1 is outside
+// [2^-64, 2^64] (where rcp could over/underflow) take correctly rounded
+// division instead, which is the definition itself.
+__global__ __launch_bounds__(256) void k_quantize_dq(const uint16_t* __restrict__ w, int64_t nblocks,
+                                                     uint8_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ fp8,
+                                                     float* __restrict__ superscale, EncodeTable tab) {
+    __shared__ uint2 s_tab[34];
+    __shared__ float s_c1[kGroup];
+    __shared__ float s_wmax[4];
+
+    const int tid = threadIdx.x;
+    const int64_t blk0 = (int64_t)blockIdx.x * kGroup;
+    const int nb = (int)((nblocks - blk0) < kGroup ? (nblocks - blk0) : kGroup);
+    if (tid < 34) s_tab[tid] = make_uint2(__float_as_uint(tab.thr[tid]), tab.base[tid]);
+
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w + blk0 * kBlock);
+    u32x4_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int chunk = j * 256 + tid;
+        v[j] = (chunk >> 3) < nb ? __builtin_nontemporal_load(src + chunk) : u32x4_t{0, 0, 0, 0};
+    }
+    __syncthreads();
+
+    uint32_t* dst = reinterpret_cast<uint32_t*>(codes + blk0 * (kBlock / 2));
+    float gmax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int chunk = j * 256 + tid;
+        const int lb = chunk >> 3;
+        const uint32_t d[4] = {v[j][0], v[j][1], v[j][2], v[j][3]};
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m = max(m, max(d[k] & 0x7FFFu, (d[k] >> 16) & 0x7FFFu));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+        const float c1 = __uint_as_float(m << 16);
+        const float r = c1 > 0.0f ? __builtin_amdgcn_rcpf(c1) : 0.0f;
+        const bool exact = c1 != 0.0f && (c1 < 0x1p-64f || c1 > 0x1p64f);
+
+        float n[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = (e & 1) ? bf16hi(d[e >> 1]) : bf16lo(d[e >> 1]);
+            n[e] = __fmul_rn(x, r);
+        }
+        if (__any(exact)) {
+            if (exact) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = (e & 1) ? bf16hi(d[e >> 1]) : bf16lo(d[e >> 1]);
+                    n[e] = __fdiv_rn(x, c1);
+                }
+            }
+        }
+        uint32_t out = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            int cell = (int)fmaf(n[e], 16.0f, 16.0f);
+            cell = min(max(cell, 0), 32);
+            const uint2 t = s_tab[cell];
+            const uint32_t code = t.y + (n[e] > __uint_as_float(t.x) ? 1u : 0u);
+            out |= code << ((e >> 1) * 8 + ((e & 1) ? 0 : 4));   // even element -> high nibble
+        }
+        if (lb < nb) {
+            dst[chunk] = out;
+            if ((tid & 7) == 0) s_c1[lb] = c1;
+        }
+        gmax = fmaxf(gmax, c1);
+    }
+
+    // Second level: group max -> fp32 super-scale, then one FP8 code per block.
+    gmax = fmaxf(gmax, __shfl_xor(gmax, 8));
+    gmax = fmaxf(gmax, __shfl_xor(gmax, 16));
+    gmax = fmaxf(gmax, __shfl_xor(gmax, 32));
+    if ((tid & 63) == 0) s_wmax[tid >> 6] = gmax;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
+    const float s2 = __fdiv_rn(amax, 448.0f);
+    if (tid == 0) superscale[blockIdx.x] = s2;
+    if (tid < nb) {
+        uint32_t code = 0;
+        if (s2 > 0.0f) code = e4m3_encode_tie_low(fminf(__fdiv_rn(s_c1[tid], s2), 448.0f));
+        fp8[blk0 + tid] = (uint8_t)code;
+    }
+}
+
+hipError_t launch_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* fp8,
+                           float* superscale, hipStream_t s) {
+    const int64_t nblocks = numel / kBlock;
+    const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
+    hipLaunchKernelGGL(k_quantize_dq, dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes, fp8,
+                       superscale, host_encode_table());
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ dequantize
+//
+// Each thread expands two 16-byte chunks of codes (32 codes each, half a
+// block) into 2 x 64 bytes of bf16: c1' = fl32(e4m3(f) * s2) once per chunk,
+// then w' = RNE_bf16(fl32(q[code] * c1')) per element, with the codebook in LDS.
+constexpr int kDeqChunksPerThread = 2;
+
+__global__ __launch_bounds__(256) void k_dequantize_dq(const uint8_t* __restrict__ codes,
+                                                       const uint8_t* __restrict__ fp8,
+                                                       const float* __restrict__ superscale,
+                                                       int64_t nchunks, uint16_t* __restrict__ out,
+                                                       Codebook cb) {
+    __shared__ float s_q[16];
+    if (threadIdx.x < 16) s_q[threadIdx.x] = cb.q[threadIdx.x];
+
+    const int64_t c0 = (int64_t)blockIdx.x * (256 * kDeqChunksPerThread) + threadIdx.x;
+    u32x4_t cv[kDeqChunksPerThread];
+    float scale[kDeqChunksPerThread];
+#pragma unroll
+    for (int u = 0; u < kDeqChunksPerThread; ++u) {
+        const int64_t c = c0 + u * 256;
+        if (c < nchunks) {
+            cv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(codes) + c);
+            const int64_t blk = c >> 1;
+            scale[u] = __fmul_rn(e4m3_decode(fp8[blk]), superscale[blk >> 8]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kDeqChunksPerThread; ++u) {
+        const int64_t c = c0 + u * 256;
+        if (c >= nchunks) continue;
+        const uint32_t d[4] = {cv[u][0], cv[u][1], cv[u][2], cv[u][3]};
+        u32x4_t* o = reinterpret_cast<u32x4_t*>(out + c * 32);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t r[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t byte = (d[k] >> (8 * b)) & 0xFFu;
+                r[b] = pack_bf16x2(__fmul_rn(s_q[byte >> 4], scale[u]), __fmul_rn(s_q[byte & 15u], scale[u]));
+            }
+            __builtin_nontemporal_store(u32x4_t{r[0], r[1], r[2], r[3]}, o + k);
+        }
+    }
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* fp8, const float* superscale,
+                             int64_t numel, uint16_t* out, hipStream_t s) {
+    const int64_t nchunks = numel / 32;
+    const int64_t per_wg = 256 * kDeqChunksPerThread;
+    hipLaunchKernelGGL(k_dequantize_dq, dim3((unsigned)((nchunks + per_wg - 1) / per_wg)), dim3(256), 0, s,
+                       codes, fp8, superscale, nchunks, out, host_codebook());
+    return hipGetLastError();
+}
+
+}  // namespace ql

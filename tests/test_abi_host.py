@@ -1,0 +1,119 @@
+"""The C ABI library on the host: it loads, exports every symbol the header
+declares, its own codebook (an independent inverse-normal) equals the
+oracle's bit for bit, and argument validation rejects bad calls before any
+launch (these calls never reach the GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from qlora_linear_layers_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+OK, NULL, SHAPE, ALIGN, VALUE, WORKSPACE = 0, 1, 2, 3, 4, 5
+FAKE = 1 << 20           # a 16-byte aligned non-NULL address; never dereferenced on these paths
+MIS = FAKE + 8           # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(api.LIB_PATH):
+        pytest.skip("library not built")
+    return api.lib()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_match_header(L):
+    names = _declared()
+    assert set(names) == set(api.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_codebook_bit_exact(L):
+    got = api.nf4_build_codebook().numpy()
+    assert np.array_equal(got.view(np.uint32), oracle.nf4_codebook().view(np.uint32))
+    assert L.nf4_build_codebook(None) == NULL
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert L.qlora_status_string(s)
+    assert L.qlora_status_string(99) == b"unknown status"
+
+
+def test_quantize_validation(L):
+    q = L.nf4_quantize_dq
+    assert q(None, 64, FAKE, FAKE, FAKE, None) == NULL
+    assert q(FAKE, 63, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(FAKE, 0, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(FAKE, -64, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(MIS, 64, FAKE, FAKE, FAKE, None) == ALIGN
+    assert q(FAKE, 64, FAKE, MIS, FAKE, None) == ALIGN
+    d = L.nf4_dequantize_dq
+    assert d(FAKE, FAKE, None, 64, FAKE, None) == NULL
+    assert d(FAKE, FAKE, FAKE, 100, FAKE, None) == SHAPE
+    assert d(FAKE, FAKE, FAKE, 64, MIS, None) == ALIGN
+
+
+def _fwd(L, **kw):
+    a = dict(x=FAKE, T=16, K=256, N=256, codes=FAKE, f8=FAKE, sup=FAKE, la=FAKE, lb=FAKE, r=16, s=1.0,
+             y=FAKE, ws=FAKE, wsb=1 << 40, st=None)
+    a.update(kw)
+    return L.qlora_linear_fwd(a["x"], a["T"], a["K"], a["N"], a["codes"], a["f8"], a["sup"], a["la"], a["lb"],
+                              a["r"], a["s"], a["y"], a["ws"], a["wsb"], a["st"])
+
+
+def test_fwd_validation(L):
+    assert _fwd(L, x=None) == NULL
+    assert _fwd(L, la=None) == NULL
+    assert _fwd(L, T=0) == SHAPE
+    assert _fwd(L, K=100) == SHAPE
+    assert _fwd(L, N=32) == SHAPE
+    assert _fwd(L, r=12) == SHAPE
+    assert _fwd(L, r=264) == SHAPE
+    assert _fwd(L, r=0) == SHAPE            # adapters given with r = 0
+    assert _fwd(L, y=MIS) == ALIGN
+    assert _fwd(L, s=math.inf) == VALUE
+    assert _fwd(L, s=math.nan) == VALUE
+    assert _fwd(L, ws=None) == WORKSPACE
+    assert _fwd(L, wsb=16) == WORKSPACE
+
+
+def _bwd(L, **kw):
+    a = dict(dy=FAKE, T=16, K=256, N=256, codes=FAKE, f8=FAKE, sup=FAKE, la=FAKE, lb=FAKE, r=16, s=1.0,
+             dx=FAKE, x=FAKE, da=FAKE, db=FAKE, ws=FAKE, wsb=1 << 40, st=None)
+    a.update(kw)
+    return L.qlora_linear_bwd_input(a["dy"], a["T"], a["K"], a["N"], a["codes"], a["f8"], a["sup"], a["la"],
+                                    a["lb"], a["r"], a["s"], a["dx"], a["x"], a["da"], a["db"], a["ws"], a["wsb"],
+                                    a["st"])
+
+
+def test_bwd_validation(L):
+    assert _bwd(L, dy=None) == NULL
+    assert _bwd(L, x=None) == NULL            # grads requested without X
+    assert _bwd(L, lb=None) == NULL
+    assert _bwd(L, T=-1) == SHAPE
+    assert _bwd(L, r=0, la=None, lb=None) == SHAPE   # grads requested with r = 0
+    assert _bwd(L, da=MIS) == ALIGN
+    assert _bwd(L, s=math.inf) == VALUE
+    assert _bwd(L, wsb=0) == WORKSPACE
+
+
+def test_workspace_bytes(L):
+    assert L.qlora_workspace_bytes(16, 4096, 4096, 0) == 0
+    assert L.qlora_workspace_bytes(16, 100, 4096, 16) == 0
+    a = L.qlora_workspace_bytes(4096, 4096, 11008, 64)
+    b = L.qlora_workspace_bytes(4096, 4096, 11008, 16)
+    assert a > 0 and b > 0 and a % 256 == 0

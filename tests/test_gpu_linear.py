@@ -1,0 +1,134 @@
+"""GPU parity of the fused forward and the backward (dX, dA, dB) against the
+fp64 oracle rounded once to bf16: max relative error <= 1e-2 (with an rms
+floor) and mean absolute error <= 1e-3 rms."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from qlora_linear_layers_amd import api, synth
+from helpers import assert_gemm_close, bits_of, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(cfg, lin, T, r, seed_layer=0):
+    d = synth.layer_inputs(cfg, seed_layer, 0, lin, T, r, with_dy=True)
+    return d
+
+
+def _run_full(name, lin, T, r, s, cfg=9, zero_w=False, check_bwd=True):
+    say(f"[linear] {name}: T={T} N={lin.N} K={lin.K} r={r} s={s}")
+    d = _inputs(cfg, lin, T, r)
+    w = np.zeros_like(d["w"]) if zero_w else d["w"]
+    qw = api.nf4_quantize_dq(to_dev(w, (lin.N, lin.K)))
+    rc, rf, rs = oracle.quantize_nf4_dq(w)
+    wd = oracle.dequantize_nf4_dq(rc, rf, rs).reshape(lin.N, lin.K)
+    x = to_dev(d["x"], (T, lin.K))
+    a = to_dev(d["a"], (lin.K, r)) if r else None
+    b = to_dev(d["b"], (r, lin.N)) if r else None
+    y = api.qlora_linear_fwd(x, qw, a, b, s)
+    torch.cuda.synchronize()
+    ref = oracle.linear_fwd(d["x"], wd, d.get("a") if r else None, d.get("b") if r else None, s)
+    assert_gemm_close(bits_of(y), ref, f"{name} Y")
+    if not check_bwd:
+        return
+    dy = to_dev(d["dy"], (T, lin.N))
+    dx, da, db = api.qlora_linear_bwd_input(dy, qw, a, b, s, x=x if r else None, lora_grads=bool(r))
+    torch.cuda.synchronize()
+    rdx, rda, rdb = oracle.linear_bwd(d["dy"], d["x"], wd, d.get("a") if r else None, d.get("b") if r else None, s)
+    assert_gemm_close(bits_of(dx), rdx, f"{name} dX")
+    if r:
+        assert_gemm_close(bits_of(da), rda, f"{name} dA")
+        assert_gemm_close(bits_of(db), rdb, f"{name} dB")
+
+
+def test_small_ragged_tiles():
+    _run_full("ragged", synth.Linear("t", 448, 320), T=300, r=16, s=1.0)
+
+
+def test_multi_tile_rank64():
+    _run_full("multi-tile", synth.Linear("t", 768, 1024), T=520, r=64, s=0.25)
+
+
+def test_no_lora():
+    _run_full("r=0", synth.Linear("t", 512, 256), T=64, r=0, s=0.0)
+
+
+def test_zero_weight_lora_only():
+    _run_full("zero W", synth.Linear("t", 256, 512), T=128, r=32, s=2.0, zero_w=True)
+
+
+def test_single_token_and_small_T():
+    for T in (1, 4, 8, 16):
+        _run_full(f"T={T}", synth.Linear("t", 384, 512), T=T, r=16, s=0.5)
+
+
+def test_single_layer_config():
+    lin = synth.Linear("w", 4096, 4096)
+    _run_full("4096x4096 T=16 r=16", lin, T=16, r=16, s=1.0, cfg=1)
+
+
+def test_one_hot_rows_give_columns():
+    """X = one-hot rows, r = 0: Y must reproduce rows of W' exactly (layout and transposition)."""
+    lin = synth.Linear("t", 320, 256)
+    d = _inputs(9, lin, 0, 0)
+    qw = api.nf4_quantize_dq(to_dev(d["w"], (lin.N, lin.K)))
+    wd = bits_of(api.nf4_dequantize_dq(qw))
+    x = torch.zeros((lin.K, lin.K), dtype=torch.bfloat16, device="cuda")
+    x.fill_diagonal_(1.0)
+    y = api.qlora_linear_fwd(x, qw)
+    assert np.array_equal(bits_of(y), wd.T.copy())
+    dy = torch.zeros((lin.N, lin.N), dtype=torch.bfloat16, device="cuda")
+    dy.fill_diagonal_(1.0)
+    dx, _, _ = api.qlora_linear_bwd_input(dy, qw)
+    assert np.array_equal(bits_of(dx), wd)
+
+
+def _sampled(cfg, lin, T, r, s, nsamp=192):
+    say(f"[linear sampled] config {cfg} {lin.name}: T={T} N={lin.N} K={lin.K} r={r}")
+    d = _inputs(cfg, lin, T, r)
+    qw = api.nf4_quantize_dq(to_dev(d["w"], (lin.N, lin.K)))
+    rc, rf, rs = oracle.quantize_nf4_dq(d["w"])
+    x, a, b = to_dev(d["x"], (T, lin.K)), to_dev(d["a"], (lin.K, r)), to_dev(d["b"], (r, lin.N))
+    dy = to_dev(d["dy"], (T, lin.N))
+    y = bits_of(api.qlora_linear_fwd(x, qw, a, b, s))
+    dx, da, db = api.qlora_linear_bwd_input(dy, qw, a, b, s, x=x, lora_grads=True)
+    dx, da, db = bits_of(dx), bits_of(da), bits_of(db)
+    rng = np.random.default_rng(cfg * 100 + lin.N)
+    t = rng.integers(0, T, nsamp)
+    n = rng.integers(0, lin.N, nsamp)
+    k = rng.integers(0, lin.K, nsamp)
+    wrows = oracle.dequantize_rows(rc, rf, rs, lin.N, lin.K, n)
+    ref = oracle.linear_fwd_at(d["x"], wrows, d["a"], d["b"], s, t, n)
+    assert_gemm_close(y[t, n], ref, "Y samples")
+    wfull_cols = oracle.dequantize_nf4_dq(rc, rf, rs).reshape(lin.N, lin.K)[:, k].T
+    ref = oracle.linear_bwd_dx_at(d["dy"], wfull_cols, d["a"], d["b"], s, t, k)
+    assert_gemm_close(dx[t, k], ref, "dX samples")
+    rda, rdb = oracle.lora_grads(d["x"], d["dy"], d["a"], d["b"], s)
+    assert_gemm_close(da, rda, "dA (full)")
+    assert_gemm_close(db, rdb, "dB (full)")
+
+
+@pytest.mark.parametrize("idx", [0, 4, 6])
+def test_train_7b_shapes_sampled(idx):
+    _sampled(3, synth.LLAMA7B[idx], 4096, 64, 16.0 / 64)
+
+
+@pytest.mark.parametrize("idx", [0, 6])
+def test_65b_shapes_sampled(idx):
+    _sampled(4, synth.LLAMA65B[idx], 2048, 64, 16.0 / 64)
+
+
+def test_determinism():
+    lin = synth.Linear("t", 512, 768)
+    d = _inputs(9, lin, 300, 16)
+    qw = api.nf4_quantize_dq(to_dev(d["w"], (lin.N, lin.K)))
+    x, a, b = to_dev(d["x"], (300, lin.K)), to_dev(d["a"], (lin.K, 16)), to_dev(d["b"], (16, lin.N))
+    dy = to_dev(d["dy"], (300, lin.N))
+    r1 = [bits_of(v) for v in (api.qlora_linear_fwd(x, qw, a, b, 0.5),) + api.qlora_linear_bwd_input(
+        dy, qw, a, b, 0.5, x=x, lora_grads=True)]
+    r2 = [bits_of(v) for v in (api.qlora_linear_fwd(x, qw, a, b, 0.5),) + api.qlora_linear_bwd_input(
+        dy, qw, a, b, 0.5, x=x, lora_grads=True)]
+    for u, v in zip(r1, r2):
+        assert np.array_equal(u, v)

@@ -1,0 +1,122 @@
+"""GPU parity of NF4 + double quantization and double dequantization against
+the oracle: bit-exact codes, FP8 codes, super-scales and bf16 values."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from qlora_linear_layers_amd import api, synth
+from helpers import bits_of, say, to_dev, to_dev_f32, to_dev_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_quant(w_bits, shape):
+    qw = api.nf4_quantize_dq(to_dev(w_bits, shape))
+    torch.cuda.synchronize()
+    return qw, qw.codes.cpu().numpy(), qw.absmax_fp8.cpu().numpy(), qw.superscale.cpu().numpy()
+
+
+def _check_full(w_bits, shape, name):
+    say(f"[quant] {name} shape={shape}")
+    qw, c, f, s = _gpu_quant(w_bits, shape)
+    rc, rf, rs = oracle.quantize_nf4_dq(w_bits)
+    assert np.array_equal(c, rc), f"{name}: packed codes differ at {np.flatnonzero(c != rc)[:8]}"
+    assert np.array_equal(f, rf), f"{name}: FP8 codes differ at {np.flatnonzero(f != rf)[:8]}"
+    assert np.array_equal(s.view(np.uint32), rs.view(np.uint32)), f"{name}: super-scales differ"
+    say(f"[dequant] {name}")
+    wd = bits_of(api.nf4_dequantize_dq(qw)).reshape(-1)
+    rd = oracle.dequantize_nf4_dq(rc, rf, rs)
+    assert np.array_equal(wd, rd), f"{name}: dequantized bf16 differ at {np.flatnonzero(wd != rd)[:8]}"
+    return qw
+
+
+def test_single_layer_4096():
+    w = synth.layer_inputs(1, 0, 0, synth.Linear("w", 4096, 4096), 0, 0)["w"]
+    _check_full(w, (4096, 4096), "4096x4096 N(0,0.02)")
+
+
+def test_ragged_partial_group():
+    rng = np.random.default_rng(11)
+    w = synth.to_bf16_bits(rng.standard_normal(64 * 300).astype(np.float32))
+    _check_full(w, (300, 64), "300 blocks (partial group)")
+    w = synth.to_bf16_bits(rng.standard_normal(64).astype(np.float32))
+    _check_full(w, (1, 64), "single block")
+
+
+def test_edge_magnitudes_and_zero_blocks():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((600, 64)).astype(np.float32)
+    x[0:3] = 0.0                                          # all-zero blocks
+    x[256:512] = 0.0                                      # an all-zero group
+    x[3] *= 1e-38                                         # subnormal-range fp32 -> bf16 subnormals
+    x[4] *= 2.0 ** -100                                   # c1 below 2^-64: exact-division path
+    x[5] *= 1e30                                          # c1 above 2^64
+    x[6] = 0.0
+    x[6, 17] = -3.0                                       # one non-zero element
+    x[7] *= 2.0 ** -133 / np.abs(x[7]).max() * 3          # a few subnormal bf16 steps
+    w = synth.to_bf16_bits(x)
+    _check_full(w, x.shape, "edge magnitudes")
+
+
+def test_fp8_exact_ties():
+    """Groups whose super-scale is exact (amax = 1.75 * 2^e) and whose block
+    constants sit exactly on E4M3 midpoints: ties must go to the lower code."""
+    vals = oracle.e4m3fn_values()
+    mids = (vals[:-1] + vals[1:]) / 2
+    mids = mids[(mids > 2.0 ** -9) & (mids < 448)]
+    rng = np.random.default_rng(13)
+    nblk = 512
+    x = (rng.uniform(-1, 1, (nblk, 64)) * 1e-3).astype(np.float32)
+    for g in range(2):
+        e = -6 - 3 * g
+        s2 = 1.75 * 2.0 ** e / 448                         # exact power of two
+        for b in range(256):
+            blk = g * 256 + b
+            c1 = 1.75 * 2.0 ** e if b == 0 else float(mids[(b * 7 + g) % mids.size]) * s2
+            x[blk] = np.clip(x[blk], -c1 * 0.9, c1 * 0.9)
+            x[blk, b % 64] = c1 if b % 2 else -c1
+    w = synth.to_bf16_bits(x)
+    c1 = oracle.block_absmax(oracle.bf16_bits_to_f32(w))
+    f, s = oracle.double_quantize(c1)
+    y = c1 / np.repeat(s, 256)
+    n_ties = int(np.isin(y.astype(np.float64), mids).sum())
+    say(f"  crafted ties: {n_ties}")
+    assert n_ties > 300
+    _check_full(w, x.shape, "FP8 ties")
+
+
+def test_llama_shapes_sampled_groups():
+    """Full 7B / 65B / 70B-shaped tensors quantized on the GPU; the oracle checks
+    64 random groups of each (groups are independent) and dequantizes them."""
+    cases = [(2, synth.LLAMA7B[4], False), (2, synth.LLAMA7B[6], False), (4, synth.LLAMA65B[4], False),
+             (5, synth.LLAMA70B[1], True), (5, synth.LLAMA70B[6], True)]
+    rng = np.random.default_rng(14)
+    for cfg, lin, outl in cases:
+        say(f"[quant sampled] config {cfg} {lin.name} {lin.N}x{lin.K} outliers={outl}")
+        w = synth.layer_inputs(cfg, 0, 4, lin, 0, 0, outliers=outl)["w"]
+        qw, c, f, s = _gpu_quant(w, (lin.N, lin.K))
+        wd = bits_of(api.nf4_dequantize_dq(qw)).reshape(-1)
+        ngroups = s.size
+        for g in rng.choice(ngroups, size=min(64, ngroups), replace=False):
+            e0, e1 = g * 16384, min((g + 1) * 16384, w.size)
+            rc, rf, rs = oracle.quantize_nf4_dq(w.reshape(-1)[e0:e1])
+            assert np.array_equal(c[e0 // 2:e1 // 2], rc), (lin.name, g)
+            assert np.array_equal(f[e0 // 64:e1 // 64], rf), (lin.name, g)
+            assert s[g].view(np.uint32) == rs[0].view(np.uint32), (lin.name, g)
+            assert np.array_equal(wd[e0:e1], oracle.dequantize_nf4_dq(rc, rf, rs)), (lin.name, g)
+
+
+def test_dequantize_oracle_storage_and_determinism():
+    """Dequantize storage produced by the oracle (not by the GPU quantizer), and
+    check that two GPU quantizations of the same weight are bitwise identical."""
+    w = synth.layer_inputs(3, 0, 1, synth.Linear("x", 1024, 4096), 0, 0)["w"]
+    rc, rf, rs = oracle.quantize_nf4_dq(w)
+    say("[dequant] oracle-made storage 1024x4096")
+    qw = api.NF4Weight(to_dev_u8(rc), to_dev_u8(rf), to_dev_f32(rs), 1024, 4096)
+    assert np.array_equal(bits_of(api.nf4_dequantize_dq(qw)).reshape(-1), oracle.dequantize_nf4_dq(rc, rf, rs))
+    say("[quant] determinism")
+    a = _gpu_quant(w, (1024, 4096))
+    b = _gpu_quant(w, (1024, 4096))
+    for u, v in zip(a[1:], b[1:]):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
