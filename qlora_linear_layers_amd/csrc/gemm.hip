@@ -48,16 +48,22 @@ struct PlainRows {
     int64_t nrows;       // valid rows (global)
     int64_t red_len;     // valid reduction length (multiple of 8)
     int64_t row0;
+    // Reduction tiles kt >= split_kt read src2 at tile kt - split_kt (the
+    // second half of a concatenated reduction, e.g. the lo part of hi/lo).
+    const uint16_t* src2 = nullptr;
+    int split_kt = 1 << 30;
     u32x4_t reg[kChunks];
 
     QL_DEV void load(int kt) {
+        const uint16_t* base = kt < split_kt ? src : src2;
+        const int ktl = kt < split_kt ? kt : kt - split_kt;
 #pragma unroll
         for (int i = 0; i < kChunks; ++i) {
             const int c = threadIdx.x + i * kThreads;
             const int64_t gr = row0 + (c >> 3);
-            const int64_t k = (int64_t)kt * 64 + (c & 7) * 8;
+            const int64_t k = (int64_t)ktl * 64 + (c & 7) * 8;
             if (gr < nrows && k < red_len)
-                reg[i] = *reinterpret_cast<const u32x4_t*>(src + gr * ld + k);
+                reg[i] = *reinterpret_cast<const u32x4_t*>(base + gr * ld + k);
             else
                 reg[i] = u32x4_t{0, 0, 0, 0};
         }
@@ -173,31 +179,34 @@ struct NF4Cols {
 
 // bf16 source laid out [red][cols]; the tile rows are columns col0 .. col0+ROWS-1
 // and the reduction runs down the source rows.  The reduction index space can
-// be the concatenation of two sources (rows < red_split from src1, the rest
-// from src2), which is how hi/lo bf16 pairs enter one accumulation.
+// be the concatenation of two sources: index i < red_split reads row i of
+// src1, red_split <= i < 2 red_split reads row i - red_split of src2 (this is
+// how hi/lo bf16 pairs enter one accumulation); rows at or beyond red_valid
+// within a half read as zero.
 template <int ROWS>
 struct TransRows {
     static constexpr int kCC = ROWS / 8;                       // 8-column chunks
     static constexpr int kUnits = 32 * kCC / kThreads;         // row-pair x chunk units per thread
     const uint16_t* src1;
     const uint16_t* src2;
-    int64_t ld, ncols, red_split, red_len, col0;
+    int64_t ld, ncols, red_split, red_valid, col0;
     u32x4_t ra[kUnits], rb[kUnits];
 
-    QL_DEV const uint16_t* rowp(int64_t r) const {
-        return r < red_split ? src1 + r * ld : src2 + (r - red_split) * ld;
+    QL_DEV u32x4_t row_chunk(int64_t i, int64_t c) const {
+        const bool second = i >= red_split;
+        const int64_t li = second ? i - red_split : i;
+        if (i >= 2 * red_split || li >= red_valid || c >= ncols) return u32x4_t{0, 0, 0, 0};
+        return *reinterpret_cast<const u32x4_t*>((second ? src2 : src1) + li * ld + c);
     }
     QL_DEV void load(int kt) {
 #pragma unroll
         for (int u = 0; u < kUnits; ++u) {
             const int unit = threadIdx.x + u * kThreads;
             const int pair = unit / kCC, cc = unit % kCC;
-            const int64_t r = (int64_t)kt * 64 + 2 * pair;
+            const int64_t i = (int64_t)kt * 64 + 2 * pair;
             const int64_t c = col0 + cc * 8;
-            const bool okc = c < ncols;
-            ra[u] = (okc && r < red_len) ? *reinterpret_cast<const u32x4_t*>(rowp(r) + c) : u32x4_t{0, 0, 0, 0};
-            rb[u] = (okc && r + 1 < red_len) ? *reinterpret_cast<const u32x4_t*>(rowp(r + 1) + c)
-                                             : u32x4_t{0, 0, 0, 0};
+            ra[u] = row_chunk(i, c);
+            rb[u] = row_chunk(i + 1, c);
         }
     }
     QL_DEV void store(uint8_t* lds, const float*) {
@@ -348,7 +357,8 @@ struct FwdArgs {
     const uint8_t* fp8;
     const float* sup;
     const uint16_t* lora_b;   // [r][N]
-    const uint16_t* ps;       // [T][r_pad] bf16 = s X A (hi part)
+    const uint16_t* ps_hi;    // [T][r_pad] bf16: s X A = hi + lo
+    const uint16_t* ps_lo;
     uint16_t* y;
     int64_t T, K, N, r, r_pad;
 };
@@ -371,9 +381,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
         mainloop<TA, TB>(pa, pb, 0, (int)(p.K / 64), acc, smem, q);
     }
     if (p.r > 0) {
-        TransRows<TA> pa{p.lora_b, p.lora_b, p.N, p.N, p.r, p.r, n0};
-        PlainRows<TB> pb{p.ps, p.r_pad, p.T, p.r_pad, t0};
-        mainloop<TA, TB>(pa, pb, 0, (int)(p.r_pad / 64), acc, smem, q);
+        // reduction over [hi | lo] of s X A against B stacked twice
+        TransRows<TA> pa{p.lora_b, p.lora_b, p.N, p.N, p.r_pad, p.r, n0};
+        PlainRows<TB> pb{p.ps_hi, p.r_pad, p.T, p.r_pad, t0, p.ps_lo, (int)(p.r_pad / 64)};
+        mainloop<TA, TB>(pa, pb, 0, (int)(2 * p.r_pad / 64), acc, smem, q);
     }
     store_out<TA, TB, true>(acc, p.y, p.N, n0, t0, p.N, p.T);
 }
@@ -384,7 +395,8 @@ struct DxArgs {
     const uint8_t* fp8;
     const float* sup;
     const uint16_t* lora_a;   // [K][r]
-    const uint16_t* gs;       // [T][r_pad] bf16 = s dY B^T (hi part)
+    const uint16_t* gs_hi;    // [T][r_pad] bf16: s dY B^T = hi + lo
+    const uint16_t* gs_lo;
     uint16_t* dx;
     int64_t T, K, N, r, r_pad;
 };
@@ -407,9 +419,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
         mainloop<TA, TB>(pa, pb, 0, (int)(p.N / 64), acc, smem, q);
     }
     if (p.r > 0) {
-        PlainRows<TA> pa{p.lora_a, p.r, p.K, p.r, k0};
-        PlainRows<TB> pb{p.gs, p.r_pad, p.T, p.r_pad, t0};
-        mainloop<TA, TB>(pa, pb, 0, (int)(p.r_pad / 64), acc, smem, q);
+        const int half = (int)(p.r_pad / 64);
+        PlainRows<TA> pa{p.lora_a, p.r, p.K, p.r, k0, p.lora_a, half};
+        PlainRows<TB> pb{p.gs_hi, p.r_pad, p.T, p.r_pad, t0, p.gs_lo, half};
+        mainloop<TA, TB>(pa, pb, 0, 2 * half, acc, smem, q);
     }
     store_out<TA, TB, true>(acc, p.dx, p.K, k0, t0, p.K, p.T);
 }
@@ -458,14 +471,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_small(SmallArgs p) {
         a_len = p.r_pad; b_len = p.T;
     } else if constexpr (KIND == kDA) {
         // dA[k][j] = sum over 2T of X[t][k] (G_hi | G_lo)[t][j]: a = j, b = k.  s0 = G_hi, s1 = G_lo, s2 = X.
-        TransRows<TA> pa{p.s0, p.s1, p.r_pad, p.r_pad, p.T, 2 * p.T, a0};
-        TransRows<TB> pb{p.s2, p.s2, p.K, p.K, p.T, 2 * p.T, b0};
+        TransRows<TA> pa{p.s0, p.s1, p.r_pad, p.r_pad, p.T, p.T, a0};
+        TransRows<TB> pb{p.s2, p.s2, p.K, p.K, p.T, p.T, b0};
         mainloop<TA, TB>(pa, pb, kt0, kt1, acc, smem, nullptr);
         a_len = p.r_pad; b_len = p.K;
     } else {
         // dB[j][n] = sum over 2T of (P_hi | P_lo)[t][j] dY[t][n]: a = n, b = j.  s0 = P_hi, s1 = P_lo, s2 = dY.
-        TransRows<TA> pa{p.s2, p.s2, p.N, p.N, p.T, 2 * p.T, a0};
-        TransRows<TB> pb{p.s0, p.s1, p.r_pad, p.r_pad, p.T, 2 * p.T, b0};
+        TransRows<TA> pa{p.s2, p.s2, p.N, p.N, p.T, p.T, a0};
+        TransRows<TB> pb{p.s0, p.s1, p.r_pad, p.r_pad, p.T, p.T, b0};
         mainloop<TA, TB>(pa, pb, kt0, kt1, acc, smem, nullptr);
         a_len = p.N; b_len = p.r_pad;
     }
@@ -550,7 +563,8 @@ hipError_t launch_lora_down_dy(const uint16_t* dy, const uint16_t* lora_b, float
 
 hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* fp8, const float* sup,
                       const uint16_t* lora_b, const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s) {
-    FwdArgs a{x, codes, fp8, sup, lora_b, reinterpret_cast<const uint16_t*>(ws + pl.off_ps_hi), y,
+    FwdArgs a{x, codes, fp8, sup, lora_b, reinterpret_cast<const uint16_t*>(ws + pl.off_ps_hi),
+              reinterpret_cast<const uint16_t*>(ws + pl.off_ps_lo), y,
               pl.T, pl.K, pl.N, pl.r, pl.r_pad};
     const size_t lds = smem_bytes<256, 256>();
     hipError_t e = set_smem(k_fwd, lds);
@@ -562,7 +576,8 @@ hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* fp
 
 hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* fp8, const float* sup,
                      const uint16_t* lora_a, const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s) {
-    DxArgs a{dy, codes, fp8, sup, lora_a, reinterpret_cast<const uint16_t*>(ws + pl.off_gs_hi), dx,
+    DxArgs a{dy, codes, fp8, sup, lora_a, reinterpret_cast<const uint16_t*>(ws + pl.off_gs_hi),
+             reinterpret_cast<const uint16_t*>(ws + pl.off_gs_lo), dx,
              pl.T, pl.K, pl.N, pl.r, pl.r_pad};
     const size_t lds = smem_bytes<256, 256>();
     hipError_t e = set_smem(k_dx, lds);
