@@ -1,0 +1,208 @@
+#!/usr/bin/env python
+"""Benchmark of the QLoRA frozen-base linear layer hot path on one MI355X.
+
+Workload (one "step"): the seven linears of a LLaMA-7B-shaped transformer
+layer (q/k/v/o 4096x4096, gate/up 11008x4096, down 4096x11008) at training
+shape T = 8 x 512 = 4096 tokens, LoRA rank 64, alpha 16 (s = 0.25).  For each
+linear the step runs the whole path: NF4 + double quantization of the bf16
+weight, double dequantization back to bf16, the fused forward
+Y = X W'^T + s (X A) B, and the backward dX = dY W' + s (dY B^T) A^T with the
+LoRA gradients dA, dB.  Inputs are seeded synthetic tensors (W ~ N(0, 0.02),
+X, dY ~ N(0, 1), A, B ~ N(0, 0.01)), resident in HBM before timing starts.
+
+Output: one JSON line.  `value` is the step's attainment of the MI355X
+roofline: the sum over all phases of their roofline time (algorithmic bytes at
+8 TB/s for quantize / dequantize, algorithmic flops at 2.5 PFLOP/s bf16 dense
+for the GEMM phases) divided by the measured step time.  Per-phase durations
+come from HIP events recorded on the stream the kernels run on.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s
+MFMA_BF16_PEAK = 2.5e15    # flop/s, dense
+
+
+def storage_bytes(numel):
+    return numel // 2 + numel // 64 + 4 * (-(-numel // 16384))
+
+
+def phase_work(lin, T, r):
+    """Algorithmic bytes (HBM phases) and flops (GEMM phases) of one linear."""
+    N, K = lin.N, lin.K
+    nk = N * K
+    st = storage_bytes(nk)
+    return {
+        "quantize": ("hbm", 2 * nk + st),
+        "dequantize": ("hbm", st + 2 * nk),
+        "forward": ("mfma", 2 * T * N * K + 2 * T * K * r + 2 * T * r * N),
+        # dX (base + LoRA), dY B^T, X A recompute, dA, dB
+        "backward": ("mfma", 2 * T * N * K + 2 * T * N * r + 2 * T * r * K + 2 * T * K * r + 2 * T * K * r
+                     + 2 * T * r * N),
+    }
+
+
+def roofline_seconds(kind, amount):
+    return amount / (HBM_PEAK if kind == "hbm" else MFMA_BF16_PEAK)
+
+
+def cpu_baseline(layers, T, r, s, t_sample):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    from qlora_linear_layers_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    roof = 0.0
+    t0 = time.perf_counter()
+    for li, lin in enumerate(layers):
+        d = synth.layer_inputs(3, 0, li, lin, T, r, with_dy=True)
+        x, dy = d["x"][:t_sample], d["dy"][:t_sample]
+        rc, rf, rs = oracle.quantize_nf4_dq(d["w"])
+        wd = oracle.dequantize_nf4_dq(rc, rf, rs).reshape(lin.N, lin.K)
+        oracle.linear_fwd(x, wd, d["a"], d["b"], s)
+        oracle.linear_bwd(dy, x, wd, d["a"], d["b"], s)
+        for name, (kind, amt) in phase_work(lin, t_sample, r).items():
+            roof += roofline_seconds(kind, amt)
+    dt = time.perf_counter() - t0
+    # generation of the synthetic inputs is inside dt; it is small next to the oracle
+    return {"value": 100.0 * roof / dt, "unit": "% of MI355X roofline", "cores": int(threads), "kind": "oracle",
+            "sample": f"all 7 linears: full quantize + dequantize, forward and backward on {t_sample} of {T} tokens",
+            "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path is single-GPU by design); --gpus {args.gpus} is not "
+              f"supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from qlora_linear_layers_amd import api, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    api.lib()
+    cfg = synth.TRAIN_7B
+    layers, T, r, s = cfg["layers"], cfg["T"], cfg["r"], cfg["scaling"]
+
+    def dev(bits, shape):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).reshape(shape).cuda()
+
+    bufs = []
+    ws_bytes = max(api.qlora_workspace_bytes(T, l.K, l.N, r) for l in layers)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    for li, lin in enumerate(layers):
+        d = synth.layer_inputs(3, 0, li, lin, T, r, with_dy=True)
+        b = dict(lin=lin, w=dev(d["w"], (lin.N, lin.K)), x=dev(d["x"], (T, lin.K)), dy=dev(d["dy"], (T, lin.N)),
+                 a=dev(d["a"], (lin.K, r)), b=dev(d["b"], (r, lin.N)))
+        b["qw"] = api.nf4_quantize_dq(b["w"])
+        b["wd"] = torch.empty((lin.N, lin.K), dtype=torch.bfloat16, device="cuda")
+        b["y"] = torch.empty((T, lin.N), dtype=torch.bfloat16, device="cuda")
+        b["dx"] = torch.empty((T, lin.K), dtype=torch.bfloat16, device="cuda")
+        b["da"] = torch.empty((lin.K, r), dtype=torch.bfloat16, device="cuda")
+        b["db"] = torch.empty((r, lin.N), dtype=torch.bfloat16, device="cuda")
+        bufs.append(b)
+    torch.cuda.synchronize()
+
+    phases = ("quantize", "dequantize", "forward", "backward")
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for li, b in enumerate(bufs):
+            ev = events[li] if events is not None else None
+            if ev: ev[0].record(stream)
+            api.nf4_quantize_dq_into(b["w"], b["qw"])
+            if ev: ev[1].record(stream)
+            api.nf4_dequantize_dq(b["qw"], out=b["wd"])
+            if ev: ev[2].record(stream)
+            api.qlora_linear_fwd(b["x"], b["qw"], b["a"], b["b"], s, workspace=ws, out=b["y"])
+            if ev: ev[3].record(stream)
+            api.qlora_linear_bwd_input(b["dy"], b["qw"], b["a"], b["b"], s, x=b["x"], lora_grads=True,
+                                       workspace=ws, dx=b["dx"], d_lora_a=b["da"], d_lora_b=b["db"])
+            if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    all_events = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in bufs] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(all_events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+
+    # per-phase, per-linear average durations (ms) from the events
+    dur = {p: np.zeros(len(bufs)) for p in phases}
+    for k in range(args.steps):
+        for li in range(len(bufs)):
+            ev = all_events[k][li]
+            for pi, p in enumerate(phases):
+                dur[p][li] += ev[pi].elapsed_time(ev[pi + 1]) / args.steps
+
+    comp = {}
+    roof_step = 0.0
+    for p in phases:
+        kind = None
+        amt = 0
+        for b in bufs:
+            kind, a = phase_work(b["lin"], T, r)[p]
+            amt += a
+        secs = dur[p].sum() / 1e3
+        rs = roofline_seconds(kind, amt)
+        roof_step += rs
+        if kind == "hbm":
+            comp[p] = {"GB/s": round(amt / secs / 1e9, 1), "frac_of_hbm_peak": round(rs / secs, 4),
+                       "ms": round(1e3 * secs, 4)}
+        else:
+            comp[p] = {"TFLOP/s": round(amt / secs / 1e12, 1), "frac_of_mfma_peak": round(rs / secs, 4),
+                       "ms": round(1e3 * secs, 4)}
+
+    # roofline of the dominant unit: the fused forward call, per linear shape
+    fwd_flops = sum(phase_work(b["lin"], T, r)["forward"][1] for b in bufs)
+    fwd_secs = dur["forward"].sum() / 1e3
+    achieved = fwd_flops / fwd_secs / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                "frac": round(achieved / 2500.0, 4), "traffic": None,
+                "kernel": "qlora_linear_fwd (fused NF4-dequant MFMA GEMM + LoRA down-projection)",
+                "per_linear_ms": {b["lin"].name: round(float(dur["forward"][i]), 4) for i, b in enumerate(bufs)}}
+
+    out = {
+        "metric": "QLoRA linear fwd TFLOP/s + NF4 quant/dequant GB/s, as % of MI355X roofline",
+        "value": round(100.0 * roof_step / (wall / args.steps), 3),
+        "unit": "% of MI355X roofline",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "LLaMA-7B-shaped layer, 7 linears (q/k/v/o 4096x4096, gate/up 11008x4096, "
+                               "down 4096x11008), T=4096 tokens, LoRA r=64 alpha=16; step = quantize + dequantize "
+                               "+ forward + backward (dX, dA, dB) of every linear",
+                   "global_batch": 8, "seq_len": 512, "parallelism": "none (1 GPU)"},
+        "components": comp,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(layers, T, r, s, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
