@@ -31,6 +31,14 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
+// LDS pointers carry address space 3 explicitly so that every tile access is a
+// ds_read / ds_write (a generic pointer would fall back to flat instructions).
+typedef __attribute__((address_space(3))) uint8_t lds8_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+typedef __attribute__((address_space(3))) float lds_f32_t;
+
 // LDS tile of [rows][64] bf16: 128 bytes per row in 16-byte chunks, the chunk
 // index XOR-swizzled with bits of the row so that the 32-row fragment reads
 // (fixed chunk) and every producer's writes spread over all banks.
@@ -38,141 +46,178 @@ QL_DEV uint32_t lds_off(int row, int chunk) {
     return (uint32_t)row * 128u + ((uint32_t)(chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
 }
 
-// ------------------------------------------------------------------ producers
+// ------------------------------------------------------------------ loads
 
-template <int ROWS>
-struct PlainRows {
-    static constexpr int kChunks = ROWS * 8 / kThreads;     // 16-byte chunks per thread
-    const uint16_t* src;
-    int64_t ld;          // elements between consecutive rows
-    int64_t nrows;       // valid rows (global)
-    int64_t red_len;     // valid reduction length (multiple of 8)
-    int64_t row0;
-    // Reduction tiles kt >= split_kt read src2 at tile kt - split_kt (the
-    // second half of a concatenated reduction, e.g. the lo part of hi/lo).
-    const uint16_t* src2 = nullptr;
-    int split_kt = 1 << 30;
-    u32x4_t reg[kChunks];
+// Raw buffer loads: a per-thread 32-bit byte offset (constant over the k loop)
+// plus a scalar per-tile offset, no 64-bit address arithmetic per load.  A
+// thread whose row lies outside the operand gets an offset past the buffer's
+// end, for which the hardware returns zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;
 
-    QL_DEV void load(int kt) {
-        const uint16_t* base = kt < split_kt ? src : src2;
-        const int ktl = kt < split_kt ? kt : kt - split_kt;
-#pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const int c = threadIdx.x + i * kThreads;
-            const int64_t gr = row0 + (c >> 3);
-            const int64_t k = (int64_t)ktl * 64 + (c & 7) * 8;
-            if (gr < nrows && k < red_len)
-                reg[i] = *reinterpret_cast<const u32x4_t*>(base + gr * ld + k);
-            else
-                reg[i] = u32x4_t{0, 0, 0, 0};
-        }
-    }
-    QL_DEV void store(uint8_t* lds, const float*) {
-#pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const int c = threadIdx.x + i * kThreads;
-            *reinterpret_cast<u32x4_t*>(lds + lds_off(c >> 3, c & 7)) = reg[i];
-        }
-    }
-};
+QL_DEV rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+QL_DEV u32x4_t bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+QL_DEV uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+QL_DEV uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
 
-// Dequantize 8 codes of one packed dword (element 2i in the high nibble of
-// byte i) with block scale c1': w' = RNE_bf16(fl32(q[code] * c1')), packed in
-// element order.
-QL_DEV u32x4_t dequant8(uint32_t d, float c1p, const float* q) {
+// ------------------------------------------------------------------ NF4 decode
+
+// Byte-pair codebook: entry e holds (q[e >> 4], q[e & 15]) as two floats, i.e.
+// the codewords of the even (high nibble) and odd (low nibble) element of a
+// packed byte.  Built once per workgroup in LDS (2 KB); one 8-byte LDS read
+// decodes two elements.
+constexpr uint32_t kPairTableBytes = 256 * 8;
+typedef __attribute__((address_space(3))) f32x2_t lds_f32x2_t;
+
+QL_DEV void build_pair_table(lds8_t* tbl, const Codebook& cb) {
+    const int t = threadIdx.x;
+    const f32x2_t v = {cb.q[t >> 4], cb.q[t & 15]};
+    *reinterpret_cast<lds_f32x2_t*>(tbl + t * 8) = v;
+}
+
+// Byte b of dword d, times 8 (its pair-table offset).
+QL_DEV uint32_t byte_x8(uint32_t d, int b) { return b == 0 ? ((d << 3) & 0x7F8u) : ((d >> (8 * b - 3)) & 0x7F8u); }
+
+// Two elements of byte b: fl32(q * c1') each (the bf16 rounding happens at the pack).
+QL_DEV f32x2_t deq_pair(uint32_t d, int b, float c1p, const lds8_t* tbl) {
+    const f32x2_t qq = *reinterpret_cast<const lds_f32x2_t*>(tbl + byte_x8(d, b));
+    return f32x2_t{__fmul_rn(qq[0], c1p), __fmul_rn(qq[1], c1p)};
+}
+
+// Eight elements of one packed dword (element 2b in the high nibble of byte b)
+// as bf16 in element order: w' = RNE_bf16(fl32(q[code] * c1')).
+QL_DEV u32x4_t deq_dword(uint32_t d, float c1p, const lds8_t* tbl) {
     u32x4_t o;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        const uint32_t byte = (d >> (8 * b)) & 0xFFu;
-        o[b] = pack_bf16x2(__fmul_rn(q[byte >> 4], c1p), __fmul_rn(q[byte & 15u], c1p));
+        const f32x2_t v = deq_pair(d, b, c1p, tbl);
+        o[b] = pack_bf16x2(v[0], v[1]);
     }
     return o;
 }
 
-// W [N, K] rows n0 .. n0+255 for reduction tile kt: thread t owns row n0 + t and
-// its NF4 block kt (64 codes = 32 bytes, one FP8 constant, one super-scale).
-struct NF4Rows {
-    const uint8_t* codes;
-    const uint8_t* fp8;
-    const float* sup;
-    int64_t K, N, row0;
-    u32x4_t c0, c1;
-    uint32_t f8;
-    float s2;
+// Block scale c1' = fl32(e4m3(f) * s2).
+QL_DEV float block_scale(uint32_t f8, float s2) { return __fmul_rn(e4m3_decode(f8), s2); }
 
-    QL_DEV void load(int kt) {
-        const int64_t n = row0 + threadIdx.x;
-        if (n < N) {
-            const uint8_t* p = codes + n * (K / 2) + (int64_t)kt * 32;
-            c0 = *reinterpret_cast<const u32x4_t*>(p);
-            c1 = *reinterpret_cast<const u32x4_t*>(p + 16);
-            const int64_t b = n * (K / 64) + kt;
-            f8 = fp8[b];
-            s2 = sup[b >> 8];
-        } else {
-            c0 = c1 = u32x4_t{0, 0, 0, 0};
-            f8 = 0;
-            s2 = 0.0f;
+// ------------------------------------------------------------------ LDS tile producers
+
+// bf16 rows contiguous along the reduction (X, dY, ...), via buffer loads.
+// Reduction tiles kt >= split_kt read src2 at tile kt - split_kt (the second
+// half of a concatenated reduction, e.g. the lo part of a hi/lo pair).  With
+// kCheckK, chunks at or beyond red_len within a tile read as zero (needed when
+// the reduction length is not a multiple of 64).
+template <int ROWS, bool kCheckK = false>
+struct PlainRows {
+    static constexpr int kChunks = ROWS * 8 / kThreads;     // 16-byte chunks per thread
+    const uint16_t* src1;
+    const uint16_t* src2;
+    int64_t bytes;
+    int split_kt;
+    int64_t red_len;
+    uint32_t voff[kChunks];
+    u32x4_t reg[kChunks];
+
+    QL_DEV void init(const uint16_t* s1, const uint16_t* s2, int64_t ld, int64_t nrows, int64_t row0, int64_t rl,
+                     int split) {
+        src1 = s1;
+        src2 = s2 ? s2 : s1;
+        bytes = nrows * ld * 2;
+        split_kt = split;
+        red_len = rl;
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            const int64_t row = row0 + (c >> 3);
+            voff[i] = row < nrows ? (uint32_t)((row * ld + (c & 7) * 8) * 2) : kOOB;
         }
     }
-    QL_DEV void store(uint8_t* lds, const float* q) {
-        const float c1p = __fmul_rn(e4m3_decode(f8), s2);
-        const int row = threadIdx.x;
+    QL_DEV void load(int kt) {
+        const bool first = kt < split_kt;
+        const int ktl = first ? kt : kt - split_kt;
+        const rsrc_t rs = make_rsrc(first ? src1 : src2, bytes);
 #pragma unroll
-        for (int ch = 0; ch < 8; ++ch) {
-            const uint32_t d = ch < 4 ? c0[ch] : c1[ch - 4];
-            *reinterpret_cast<u32x4_t*>(lds + lds_off(row, ch)) = dequant8(d, c1p, q);
+        for (int i = 0; i < kChunks; ++i) {
+            u32x4_t v = bload16(rs, voff[i], (uint32_t)ktl * 128u);
+            if constexpr (kCheckK) {
+                const int c = threadIdx.x + i * kThreads;
+                v = ((int64_t)ktl * 64 + (c & 7) * 8 < red_len) ? v : u32x4_t{0, 0, 0, 0};
+            }
+            reg[i] = v;
+        }
+    }
+    QL_DEV void store(lds8_t* lds, const lds8_t*) {
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            *reinterpret_cast<lds_u32x4_t*>(lds + lds_off(c >> 3, c & 7)) = reg[i];
         }
     }
 };
 
 // W read transposed for dX: tile rows are k (256 of them), the reduction runs
 // over n (64 per tile).  Thread t owns k = k0 + (t % 32) * 8 .. +7 and
-// n = kt*64 + (t / 32) * 8 .. +7: eight 4-byte code words, eight scales.
+// n = kt*64 + (t / 32) * 8 .. +7: eight 4-byte code words and eight block
+// scales.  Two elements of one code byte are neighbours in k; the bf16 pack
+// pairs neighbours in n, which writes the transposed tile directly.
 struct NF4Cols {
     const uint8_t* codes;
     const uint8_t* fp8;
     const float* sup;
-    int64_t K, N, col0;
+    int64_t K, N;
+    uint32_t cvo, fvo, blk0;       // per-thread offsets at kt = 0 (row n = ng*8)
+    bool ok;
     uint32_t cw[8], f8[8];
     float s2[8];
 
-    QL_DEV void load(int kt) {
+    QL_DEV void init(const uint8_t* c, const uint8_t* f, const float* su, int64_t K_, int64_t N_, int64_t col0) {
+        codes = c; fp8 = f; sup = su; K = K_; N = N_;
         const int64_t k = col0 + (threadIdx.x & 31) * 8;
-        const int64_t n0 = (int64_t)kt * 64 + (threadIdx.x >> 5) * 8;
+        const int64_t n = (threadIdx.x >> 5) * 8;
+        ok = k < K;
+        cvo = ok ? (uint32_t)(n * (K / 2) + k / 2) : kOOB;
+        fvo = ok ? (uint32_t)(n * (K / 64) + k / 64) : kOOB;
+        blk0 = (uint32_t)(n * (K / 64) + (ok ? k / 64 : 0));
+    }
+    QL_DEV void load(int kt) {
+        const rsrc_t rc = make_rsrc(codes, N * K / 2);
+        const rsrc_t rf = make_rsrc(fp8, N * K / 64);
+        const rsrc_t rs = make_rsrc(sup, ceil_div(N * K / 64, 256) * 4);
+        const uint32_t soc = (uint32_t)(kt * 64 * (K / 2)), sof = (uint32_t)(kt * 64 * (K / 64));
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int64_t n = n0 + i;
-            if (k < K) {
-                cw[i] = *reinterpret_cast<const uint32_t*>(codes + n * (K / 2) + k / 2);
-                const int64_t b = n * (K / 64) + k / 64;
-                f8[i] = fp8[b];
-                s2[i] = sup[b >> 8];
-            } else {
-                cw[i] = 0;
-                f8[i] = 0;
-                s2[i] = 0.0f;
-            }
+            cw[i] = bload4(rc, cvo + i * (uint32_t)(K / 2), soc);
+            f8[i] = bload1(rf, fvo + i * (uint32_t)(K / 64), sof);
+            const uint32_t blk = blk0 + sof + i * (uint32_t)(K / 64);
+            s2[i] = __uint_as_float(bload4(rs, ok ? (blk >> 8) * 4u : kOOB, 0));
         }
     }
-    QL_DEV void store(uint8_t* lds, const float* q) {
-        float c1p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c1p[i] = __fmul_rn(e4m3_decode(f8[i]), s2[i]);
+    QL_DEV void store(lds8_t* lds, const lds8_t* tbl) {
         const int kc = threadIdx.x & 31, ng = threadIdx.x >> 5;
+        float v[8][8];                                   // [row i][k]
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float c1p = block_scale(f8[i], s2[i]);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const f32x2_t e = deq_pair(cw[i], b, c1p, tbl);
+                v[i][2 * b] = e[0];
+                v[i][2 * b + 1] = e[1];
+            }
+        }
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            // element kk of each row: byte kk/2, high nibble when kk is even
-            const int sh = (kk >> 1) * 8 + ((kk & 1) ? 0 : 4);
             u32x4_t o;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const float v0 = __fmul_rn(q[(cw[2 * p] >> sh) & 15u], c1p[2 * p]);
-                const float v1 = __fmul_rn(q[(cw[2 * p + 1] >> sh) & 15u], c1p[2 * p + 1]);
-                o[p] = pack_bf16x2(v0, v1);
-            }
-            *reinterpret_cast<u32x4_t*>(lds + lds_off(kc * 8 + kk, ng)) = o;
+            for (int p = 0; p < 4; ++p) o[p] = pack_bf16x2(v[2 * p][kk], v[2 * p + 1][kk]);
+            *reinterpret_cast<lds_u32x4_t*>(lds + lds_off(kc * 8 + kk, ng)) = o;
         }
     }
 };
@@ -182,7 +227,7 @@ struct NF4Cols {
 // be the concatenation of two sources: index i < red_split reads row i of
 // src1, red_split <= i < 2 red_split reads row i - red_split of src2 (this is
 // how hi/lo bf16 pairs enter one accumulation); rows at or beyond red_valid
-// within a half read as zero.
+// within a half read as zero.  Two source rows are paired into dwords.
 template <int ROWS>
 struct TransRows {
     static constexpr int kCC = ROWS / 8;                       // 8-column chunks
@@ -192,11 +237,16 @@ struct TransRows {
     int64_t ld, ncols, red_split, red_valid, col0;
     u32x4_t ra[kUnits], rb[kUnits];
 
+    QL_DEV void init(const uint16_t* s1, const uint16_t* s2, int64_t ld_, int64_t nc, int64_t rs, int64_t rv,
+                     int64_t c0) {
+        src1 = s1; src2 = s2; ld = ld_; ncols = nc; red_split = rs; red_valid = rv; col0 = c0;
+    }
     QL_DEV u32x4_t row_chunk(int64_t i, int64_t c) const {
         const bool second = i >= red_split;
         const int64_t li = second ? i - red_split : i;
-        if (i >= 2 * red_split || li >= red_valid || c >= ncols) return u32x4_t{0, 0, 0, 0};
-        return *reinterpret_cast<const u32x4_t*>((second ? src2 : src1) + li * ld + c);
+        const bool ok = i < 2 * red_split && li < red_valid && c < ncols;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>((second ? src2 : src1) + (ok ? li * ld + c : 0));
+        return ok ? v : u32x4_t{0, 0, 0, 0};
     }
     QL_DEV void load(int kt) {
 #pragma unroll
@@ -209,7 +259,7 @@ struct TransRows {
             rb[u] = row_chunk(i + 1, c);
         }
     }
-    QL_DEV void store(uint8_t* lds, const float*) {
+    QL_DEV void store(lds8_t* lds, const lds8_t*) {
 #pragma unroll
         for (int u = 0; u < kUnits; ++u) {
             const int unit = threadIdx.x + u * kThreads;
@@ -218,7 +268,7 @@ struct TransRows {
             for (int i = 0; i < 8; ++i) {
                 const uint32_t lo = (ra[u][i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
                 const uint32_t hi = (rb[u][i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-                *reinterpret_cast<uint32_t*>(lds + lds_off(cc * 8 + i, pair >> 2) + (pair & 3) * 4) = lo | (hi << 16);
+                *reinterpret_cast<lds_u32_t*>(lds + lds_off(cc * 8 + i, pair >> 2) + (pair & 3) * 4) = lo | (hi << 16);
             }
         }
     }
@@ -240,8 +290,14 @@ struct Acc {
     }
 };
 
+QL_DEV bf16x8_t lds_frag(const lds8_t* base, int row, int chunk) {
+    return *reinterpret_cast<const lds_bf16x8_t*>(base + lds_off(row, chunk));
+}
+
+// Four 16-deep MFMA steps over one 64-wide LDS tile pair, waves arranged 2 x 2
+// (wave (wa, wb) owns rows wa*TA/2.. of A and wb*TB/2.. of B).
 template <int TA, int TB>
-QL_DEV void mma_tile(const uint8_t* lA, const uint8_t* lB, Acc<TA, TB>& acc) {
+QL_DEV void mma_tile(const lds8_t* lA, const lds8_t* lB, Acc<TA, TB>& acc) {
     constexpr int MA = TA / 64, MB = TB / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wa = wave >> 1, wb = wave & 1;
@@ -250,11 +306,9 @@ QL_DEV void mma_tile(const uint8_t* lA, const uint8_t* lB, Acc<TA, TB>& acc) {
     for (int s = 0; s < 4; ++s) {
         bf16x8_t a[MA], b[MB];
 #pragma unroll
-        for (int i = 0; i < MA; ++i)
-            a[i] = *reinterpret_cast<const bf16x8_t*>(lA + lds_off(wa * (TA / 2) + i * 32 + r, 2 * s + h));
+        for (int i = 0; i < MA; ++i) a[i] = lds_frag(lA, wa * (TA / 2) + i * 32 + r, 2 * s + h);
 #pragma unroll
-        for (int j = 0; j < MB; ++j)
-            b[j] = *reinterpret_cast<const bf16x8_t*>(lB + lds_off(wb * (TB / 2) + j * 32 + r, 2 * s + h));
+        for (int j = 0; j < MB; ++j) b[j] = lds_frag(lB, wb * (TB / 2) + j * 32 + r, 2 * s + h);
 #pragma unroll
         for (int i = 0; i < MA; ++i)
 #pragma unroll
@@ -265,38 +319,49 @@ QL_DEV void mma_tile(const uint8_t* lA, const uint8_t* lB, Acc<TA, TB>& acc) {
 
 // Double-buffered main loop over reduction tiles [kt0, kt1).  Global loads for
 // tile kt+1 are issued before the MFMAs of tile kt and written to the other
-// LDS buffer after them; one barrier per tile.
+// LDS buffer after them; one barrier per tile.  The body has no branches (the
+// last iteration reloads its own tile into the idle buffer), so the compiler
+// can interleave the producers' VALU work with the MFMAs.
 template <int TA, int TB, class PA, class PB>
-QL_DEV void mainloop(PA& pa, PB& pb, int kt0, int kt1, Acc<TA, TB>& acc, uint8_t* smem, const float* q) {
+QL_DEV void mainloop(PA& pa, PB& pb, int kt0, int kt1, Acc<TA, TB>& acc, lds8_t* smem, const lds8_t* tbl) {
     if (kt0 >= kt1) return;
-    uint8_t* lA[2] = {smem, smem + TA * 128};
-    uint8_t* lB[2] = {smem + 2 * TA * 128, smem + 2 * TA * 128 + TB * 128};
+    lds8_t* const lA0 = smem;
+    lds8_t* const lB0 = smem + 2 * TA * 128;
     pa.load(kt0);
     pb.load(kt0);
-    pa.store(lA[0], q);
-    pb.store(lB[0], q);
+    pa.store(lA0, tbl);
+    pb.store(lB0, tbl);
     __syncthreads();
     for (int kt = kt0; kt < kt1; ++kt) {
         const int cur = (kt - kt0) & 1;
-        const bool more = kt + 1 < kt1;
-        if (more) {
-            pa.load(kt + 1);
-            pb.load(kt + 1);
-        }
-        mma_tile<TA, TB>(lA[cur], lB[cur], acc);
-        if (more) {
-            pa.store(lA[cur ^ 1], q);
-            pb.store(lB[cur ^ 1], q);
-        }
+        const int nxt = kt + 1 < kt1 ? kt + 1 : kt;
+        pa.load(nxt);
+        pb.load(nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_tile<TA, TB>(lA0 + cur * (TA * 128), lB0 + cur * (TB * 128), acc);
+        pa.store(lA0 + (cur ^ 1) * (TA * 128), tbl);
+        pb.store(lB0 + (cur ^ 1) * (TB * 128), tbl);
         __syncthreads();
     }
 }
 
 template <int TA, int TB>
-constexpr size_t smem_bytes() { return (size_t)2 * (TA + TB) * 128 + 64; }
+constexpr size_t smem_bytes() { return (size_t)2 * (TA + TB) * 128 + kPairTableBytes; }
 
-// Output C[a][b] to out[b][a] (a contiguous): each lane holds four consecutive
-// a for one b per MFMA row group.  bf16 (8-byte stores) or fp32 (16-byte).
+// Output C[a][b] to out[b][a] (a contiguous) for the 2 x 2 wave layout: each
+// lane holds four consecutive a for one b per MFMA row group.  bf16 (8-byte
+// stores) or fp32 (16-byte).
+template <bool kBF16>
+QL_DEV void store4(const f32x16_t& v, int g, void* out, int64_t ldo, int64_t a, int64_t b) {
+    if constexpr (kBF16) {
+        const u32x2_t o = {pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3])};
+        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + b * ldo + a) = o;
+    } else {
+        const f32x4_t o = {v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+        *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + b * ldo + a) = o;
+    }
+}
+
 template <int TA, int TB, bool kBF16>
 QL_DEV void store_out(const Acc<TA, TB>& acc, void* out, int64_t ldo, int64_t a0, int64_t b0, int64_t a_len,
                       int64_t b_len) {
@@ -313,24 +378,9 @@ QL_DEV void store_out(const Acc<TA, TB>& acc, void* out, int64_t ldo, int64_t a0
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int64_t a = a0 + wa * (TA / 2) + i * 32 + g * 8 + h * 4;
-                if (a >= a_len) continue;
-                const f32x16_t& v = acc.v[i][j];
-                if constexpr (kBF16) {
-                    u32x2_t o = {pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3])};
-                    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + b * ldo + a) = o;
-                } else {
-                    f32x4_t o = {v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
-                    *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + b * ldo + a) = o;
-                }
+                if (a < a_len) store4<kBF16>(acc.v[i][j], g, out, ldo, a, b);
             }
         }
-}
-
-QL_DEV float* codebook_to_lds(uint8_t* smem, size_t off, const Codebook& cb) {
-    float* q = reinterpret_cast<float*>(smem + off);
-    if (threadIdx.x < 16) q[threadIdx.x] = cb.q[threadIdx.x];
-    __syncthreads();
-    return q;
 }
 
 // Map a linear workgroup id to an (a-tile, b-tile) pair.  Workgroups are
@@ -349,7 +399,7 @@ QL_DEV void tile_of(int pid, int ga, int gb, int& ta, int& tb) {
     tb = band * kBand + within % bw;
 }
 
-// ------------------------------------------------------------------ kernels
+// ------------------------------------------------------------------ forward
 
 struct FwdArgs {
     const uint16_t* x;
@@ -363,31 +413,276 @@ struct FwdArgs {
     int64_t T, K, N, r, r_pad;
 };
 
-// Y = X W'^T (+ (s X A) B): a = n over W rows, b = t over tokens.
+// Byte-pair codebook replicated 32 times so that the 32 lanes one LDS cycle
+// serves (64 banks x 4 bytes) always read distinct banks: entry e of copy c
+// sits at e*256 + c*8, and lane l uses copy (l & 31).  With that stride the
+// lookup address is (byte << 8) | (copy * 8), one byte permute of the packed
+// codes.
+constexpr uint32_t kWideTableBytes = 256 * 256;
+
+QL_DEV void build_wide_pair_table(lds8_t* tbl, const Codebook& cb) {
+    for (int i = threadIdx.x; i < 256 * 32; i += kThreads) {
+        const int e = i >> 5;
+        const f32x2_t v = {cb.q[e >> 4], cb.q[e & 15]};
+        *reinterpret_cast<lds_f32x2_t*>(tbl + e * 256 + (i & 31) * 8) = v;
+    }
+}
+
+// Eight elements of one packed dword as bf16 (see deq_dword), with the lane's
+// own table copy; lane8 = (lane & 31) * 8 sits in the low byte of the address.
+QL_DEV u32x4_t deq_dword_wide(uint32_t d, float c1p, const lds8_t* tbl, uint32_t lane8) {
+    u32x4_t o;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        // bytes of the address: [0] = lane8, [1] = byte b of d, [2], [3] = 0
+        const uint32_t off = __builtin_amdgcn_perm(d, lane8, 0x0C0C0000u | ((4u + b) << 8));
+        const f32x2_t qq = *reinterpret_cast<const lds_f32x2_t*>(tbl + off);
+        o[b] = pack_bf16x2(__fmul_rn(qq[0], c1p), __fmul_rn(qq[1], c1p));
+    }
+    return o;
+}
+
+// Y = X W'^T (+ (s X A) B), tile 256 (n) x 256 (t), waves stacked along n.
+//
+// Wave w owns W rows n0 + 64w .. +63 (two 32-row MFMA A-fragments) against all
+// 256 tokens (eight B-fragments).  Its W rows are private to it, so they are
+// dequantized straight into A-operand registers: per 64-wide k tile a lane
+// loads 16 code bytes of one row (32 k values), one FP8 constant and one
+// super-scale.  The k order inside a tile is permuted consistently on both
+// operands (MFMA step s, lane half h, slot j <-> k = 32h + 8s + j), which makes
+// each lane's codes contiguous.
+//
+// Pipeline.  Global loads run two k tiles ahead (X and W codes into
+// registers, alternating register sets by tile parity); X is written to the
+// idle LDS buffer one tile ahead; inside a tile, the LDS reads of step s+1
+// (eight X fragments, eight codebook lookups) are issued before the sixteen
+// MFMAs of step s, and step s+1's A fragments are finished while those MFMAs
+// run.  One barrier per tile.
+struct FwdPipe {
+    static constexpr int TT = 256;
+    static constexpr uint32_t kTile = TT * 128;   // one [256][64] bf16 LDS tile
+    rsrc_t rc, rf, rs, rx;
+    uint32_t cvo[2], fvo[2], blk[2], xvo[8];
+    bool wok[2];
+    uint32_t lane8;
+    int KT;
+    // global-load register sets, indexed by tile parity
+    u32x4_t xr[2][8];
+    u32x4_t wc[2][2];
+    uint32_t wf[2][2];
+    float ws[2][2];
+
+    QL_DEV void load_w(int kt, int par) {
+        kt = kt < KT ? kt : KT - 1;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            wc[par][i] = bload16(rc, cvo[i], (uint32_t)kt * 32u);
+            wf[par][i] = bload1(rf, fvo[i], (uint32_t)kt);
+            ws[par][i] = __uint_as_float(bload4(rs, wok[i] ? ((blk[i] + kt) >> 8) * 4u : kOOB, 0));
+        }
+    }
+    QL_DEV void load_x(int kt, int par) {
+        kt = kt < KT ? kt : KT - 1;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) xr[par][c] = bload16(rx, xvo[c], (uint32_t)kt * 128u);
+    }
+    QL_DEV void store_x(int par, lds8_t* lx) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int ch = threadIdx.x + c * kThreads;
+            *reinterpret_cast<lds_u32x4_t*>(lx + lds_off(ch >> 3, ch & 7)) = xr[par][c];
+        }
+    }
+};
+
+// LDS reads of one MFMA step: eight X fragments and the eight codebook pairs
+// of the two A fragments (codes dword s of each W row).
+struct StepIn {
+    bf16x8_t x[8];
+    f32x2_t q[2][4];
+};
+
+QL_DEV void step_reads(StepIn& in, const lds8_t* xb, int s, const u32x4_t (&wc)[2], const lds8_t* tbl,
+                       uint32_t lane8, int r, int h) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t off = __builtin_amdgcn_perm(wc[i][s], lane8, 0x0C0C0000u | ((4u + b) << 8));
+            in.q[i][b] = *reinterpret_cast<const lds_f32x2_t*>(tbl + off);
+        }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) in.x[j] = lds_frag(xb, 32 * j + r, 4 * h + s);
+}
+
+QL_DEV void step_frags(bf16x8_t (&a)[2], const StepIn& in, const float (&c1p)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        u32x4_t o;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            o[b] = pack_bf16x2(__fmul_rn(in.q[i][b][0], c1p[i]), __fmul_rn(in.q[i][b][1], c1p[i]));
+        a[i] = __builtin_bit_cast(bf16x8_t, o);
+    }
+}
+
+QL_DEV void step_mfma(f32x16_t (&acc)[2][8], const bf16x8_t (&a)[2], const StepIn& in) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], in.x[j], acc[0][j], 0, 0, 0);
+        acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], in.x[j], acc[1][j], 0, 0, 0);
+    }
+}
+
+// One k tile.  On entry `in0`/`a0` hold step 0 of tile kt (reads done, A
+// fragments built); on exit they hold step 0 of tile kt+1.
+template <int P>
+QL_DEV void fwd_tile(FwdPipe& pp, int kt, f32x16_t (&acc)[2][8], lds8_t* lX, const lds8_t* tbl, int r, int h,
+                     StepIn& in0, bf16x8_t (&a0)[2]) {
+    constexpr int Q = P ^ 1;
+    pp.load_x(kt + 2, P);                     // X set P held tile kt, already in LDS
+    __builtin_amdgcn_sched_barrier(0);
+    const lds8_t* xb = lX + P * FwdPipe::kTile;
+    const float c1p[2] = {block_scale(pp.wf[P][0], pp.ws[P][0]), block_scale(pp.wf[P][1], pp.ws[P][1])};
+    StepIn in1;
+    bf16x8_t a1[2];
+    // steps 0..3 with the next step's reads issued ahead of the MFMAs
+    step_reads(in1, xb, 1, pp.wc[P], tbl, pp.lane8, r, h);
+    step_mfma(acc, a0, in0);
+    step_frags(a1, in1, c1p);
+    step_reads(in0, xb, 2, pp.wc[P], tbl, pp.lane8, r, h);
+    step_mfma(acc, a1, in1);
+    step_frags(a0, in0, c1p);
+    step_reads(in1, xb, 3, pp.wc[P], tbl, pp.lane8, r, h);
+    __builtin_amdgcn_sched_barrier(0);
+    pp.load_w(kt + 2, P);                     // last read of tile kt's codes is above
+    step_mfma(acc, a0, in0);
+    step_frags(a1, in1, c1p);
+    step_mfma(acc, a1, in1);
+    // tile kt+1: X to the other buffer, then its step 0
+    pp.store_x(Q, lX + Q * FwdPipe::kTile);
+    __syncthreads();
+    const float n1p[2] = {block_scale(pp.wf[Q][0], pp.ws[Q][0]), block_scale(pp.wf[Q][1], pp.ws[Q][1])};
+    step_reads(in0, lX + Q * FwdPipe::kTile, 0, pp.wc[Q], tbl, pp.lane8, r, h);
+    step_frags(a0, in0, n1p);
+}
+
 __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    constexpr int TA = 256, TB = 256;
-    const float* q = codebook_to_lds(smem, smem_bytes<TA, TB>() - 64, cb);
-    const int ga = (int)ceil_div(p.N, TA), gb = (int)ceil_div(p.T, TB);
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    lds8_t* smem = (lds8_t*)(smem_raw);
+    constexpr int TT = FwdPipe::TT;
+    constexpr uint32_t kTile = FwdPipe::kTile;
+    lds8_t* const lX = smem;                  // 2 tiles (the LoRA phase reuses them)
+    lds8_t* const lL = smem + kTile;
+    lds8_t* const tbl = smem + 2 * kTile;     // wide pair table
+    build_wide_pair_table(tbl, cb);
+
+    const int ga = (int)ceil_div(p.N, 256), gb = (int)ceil_div(p.T, TT);
     int ta, tb;
     tile_of(blockIdx.x, ga, gb, ta, tb);
-    const int64_t n0 = (int64_t)ta * TA, t0 = (int64_t)tb * TB;
+    const int64_t n0 = (int64_t)ta * 256, t0 = (int64_t)tb * TT;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = lane & 31, h = lane >> 5;
 
-    Acc<TA, TB> acc;
-    acc.zero();
+    FwdPipe pp;
+    pp.rc = make_rsrc(p.codes, p.N * p.K / 2);
+    pp.rf = make_rsrc(p.fp8, p.N * p.K / 64);
+    pp.rs = make_rsrc(p.sup, ceil_div(p.N * p.K / 64, 256) * 4);
+    pp.rx = make_rsrc(p.x, p.T * p.K * 2);
+    pp.KT = (int)(p.K / 64);
+    pp.lane8 = (uint32_t)(lane & 31) * 8u;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t n = n0 + 64 * w + 32 * i + r;
+        pp.wok[i] = n < p.N;
+        pp.cvo[i] = pp.wok[i] ? (uint32_t)(n * (p.K / 2) + 16 * h) : kOOB;
+        pp.fvo[i] = pp.wok[i] ? (uint32_t)(n * (p.K / 64)) : kOOB;
+        pp.blk[i] = pp.wok[i] ? (uint32_t)(n * (p.K / 64)) : 0u;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int ch = threadIdx.x + c * kThreads;
+        const int64_t t = t0 + (ch >> 3);
+        pp.xvo[c] = t < p.T ? (uint32_t)((t * p.K + (ch & 7) * 8) * 2) : kOOB;
+    }
+
+    f32x16_t acc[2][8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // prologue: tiles 0 and 1 in flight; tile 0's X in LDS and its step 0 ready
+    pp.load_w(0, 0);
+    pp.load_x(0, 0);
+    pp.load_w(1, 1);
+    pp.load_x(1, 1);
+    pp.store_x(0, lX);
+    __syncthreads();                          // pair table and X tile 0 visible
+    StepIn in0;
+    bf16x8_t a0[2];
     {
-        NF4Rows pa{p.codes, p.fp8, p.sup, p.K, p.N, n0};
-        PlainRows<TB> pb{p.x, p.K, p.T, p.K, t0};
-        mainloop<TA, TB>(pa, pb, 0, (int)(p.K / 64), acc, smem, q);
+        const float c1p[2] = {block_scale(pp.wf[0][0], pp.ws[0][0]), block_scale(pp.wf[0][1], pp.ws[0][1])};
+        step_reads(in0, lX, 0, pp.wc[0], tbl, pp.lane8, r, h);
+        step_frags(a0, in0, c1p);
     }
+    const int KT = pp.KT;
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+        fwd_tile<0>(pp, kt, acc, lX, tbl, r, h, in0, a0);
+        fwd_tile<1>(pp, kt + 1, acc, lX, tbl, r, h, in0, a0);
+    }
+    if (kt < KT) fwd_tile<0>(pp, kt, acc, lX, tbl, r, h, in0, a0);
+
     if (p.r > 0) {
-        // reduction over [hi | lo] of s X A against B stacked twice
-        TransRows<TA> pa{p.lora_b, p.lora_b, p.N, p.N, p.r_pad, p.r, n0};
-        PlainRows<TB> pb{p.ps_hi, p.r_pad, p.T, p.r_pad, t0, p.ps_lo, (int)(p.r_pad / 64)};
-        mainloop<TA, TB>(pa, pb, 0, (int)(2 * p.r_pad / 64), acc, smem, q);
+        // reduction over [hi | lo] of s X A (tokens) against B^T stacked twice (rows n)
+        TransRows<256> pl;
+        pl.init(p.lora_b, p.lora_b, p.N, p.N, p.r_pad, p.r, n0);
+        PlainRows<TT> ps;
+        ps.init(p.ps_hi, p.ps_lo, p.r_pad, p.T, t0, p.r_pad, (int)(p.r_pad / 64));
+        const int LT = (int)(2 * p.r_pad / 64);
+        for (int lt = 0; lt < LT; ++lt) {
+            pl.load(lt);
+            ps.load(lt);
+            __syncthreads();                  // previous readers of both buffers are done
+            pl.store(lL, tbl);
+            ps.store(lX, tbl);
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8_t a0 = lds_frag(lL, 64 * w + r, 4 * h + s);
+                const bf16x8_t a1 = lds_frag(lL, 64 * w + 32 + r, 4 * h + s);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const bf16x8_t b = lds_frag(lX, 32 * j + r, 4 * h + s);
+                    acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0][j], 0, 0, 0);
+                    acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1][j], 0, 0, 0);
+                }
+            }
+            __syncthreads();
+        }
     }
-    store_out<TA, TB, true>(acc, p.y, p.N, n0, t0, p.N, p.T);
+
+    // C[n][t] -> Y[t][n]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t t = t0 + 32 * j + r;
+            if (t >= p.T) continue;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t n = n0 + 64 * w + 32 * i + 8 * g + 4 * h;
+                if (n < p.N) store4<true>(acc[i][j], g, p.y, p.N, n, t);
+            }
+        }
 }
+
+constexpr size_t kFwdSmem = 2 * 256 * 128 + kWideTableBytes;
+
+// ------------------------------------------------------------------ dX
 
 struct DxArgs {
     const uint16_t* dy;
@@ -401,31 +696,40 @@ struct DxArgs {
     int64_t T, K, N, r, r_pad;
 };
 
-// dX = dY W' (+ (s dY B^T) A^T): a = k over W columns, b = t.
+// dX = dY W' (+ (s dY B^T) A^T): a = k over W columns, b = t, waves 2 x 2.
 __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
-    extern __shared__ __align__(16) uint8_t smem[];
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    lds8_t* smem = (lds8_t*)(smem_raw);
     constexpr int TA = 256, TB = 256;
-    const float* q = codebook_to_lds(smem, smem_bytes<TA, TB>() - 64, cb);
+    lds8_t* const tbl = smem + 2 * (TA + TB) * 128;
+    build_pair_table(tbl, cb);
     const int ga = (int)ceil_div(p.K, TA), gb = (int)ceil_div(p.T, TB);
     int ta, tb;
     tile_of(blockIdx.x, ga, gb, ta, tb);
     const int64_t k0 = (int64_t)ta * TA, t0 = (int64_t)tb * TB;
+    __syncthreads();
 
     Acc<TA, TB> acc;
     acc.zero();
     {
-        NF4Cols pa{p.codes, p.fp8, p.sup, p.K, p.N, k0};
-        PlainRows<TB> pb{p.dy, p.N, p.T, p.N, t0};
-        mainloop<TA, TB>(pa, pb, 0, (int)(p.N / 64), acc, smem, q);
+        NF4Cols pa;
+        pa.init(p.codes, p.fp8, p.sup, p.K, p.N, k0);
+        PlainRows<TB> pb;
+        pb.init(p.dy, nullptr, p.N, p.T, t0, p.N, 1 << 30);
+        mainloop<TA, TB>(pa, pb, 0, (int)(p.N / 64), acc, smem, tbl);
     }
     if (p.r > 0) {
         const int half = (int)(p.r_pad / 64);
-        PlainRows<TA> pa{p.lora_a, p.r, p.K, p.r, k0, p.lora_a, half};
-        PlainRows<TB> pb{p.gs_hi, p.r_pad, p.T, p.r_pad, t0, p.gs_lo, half};
-        mainloop<TA, TB>(pa, pb, 0, 2 * half, acc, smem, q);
+        PlainRows<TA, true> pa;
+        pa.init(p.lora_a, p.lora_a, p.r, p.K, k0, p.r, half);
+        PlainRows<TB> pb;
+        pb.init(p.gs_hi, p.gs_lo, p.r_pad, p.T, t0, p.r_pad, half);
+        mainloop<TA, TB>(pa, pb, 0, 2 * half, acc, smem, tbl);
     }
     store_out<TA, TB, true>(acc, p.dx, p.K, k0, t0, p.K, p.T);
 }
+
+// ------------------------------------------------------------------ small LoRA products
 
 // Small LoRA products with split reduction; fp32 partials out[split][b][a].
 enum SmallKind { kXA = 0, kG = 1, kDA = 2, kDB = 3 };
@@ -441,7 +745,8 @@ struct SmallArgs {
 
 template <int KIND>
 __global__ __launch_bounds__(kThreads, 1) void k_small(SmallArgs p) {
-    extern __shared__ __align__(16) uint8_t smem[];
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    lds8_t* smem = (lds8_t*)(smem_raw);
     constexpr int TA = (KIND == kDB) ? 256 : 64;
     constexpr int TB = (KIND == kDB) ? 64 : 256;
     const int split = blockIdx.y;
@@ -459,26 +764,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_small(SmallArgs p) {
 
     if constexpr (KIND == kXA) {
         // P[t][j] = sum_k X[t][k] A[k][j]: a = j (A transposed), b = t.  s0 = A, s1 = X.
-        TransRows<TA> pa{p.s0, p.s0, p.r, p.r, p.K, p.K, a0};
-        PlainRows<TB> pb{p.s1, p.K, p.T, p.K, b0};
+        TransRows<TA> pa;
+        pa.init(p.s0, p.s0, p.r, p.r, p.K, p.K, a0);
+        PlainRows<TB> pb;
+        pb.init(p.s1, nullptr, p.K, p.T, b0, p.K, 1 << 30);
         mainloop<TA, TB>(pa, pb, kt0, kt1, acc, smem, nullptr);
         a_len = p.r_pad; b_len = p.T;
     } else if constexpr (KIND == kG) {
         // G[t][j] = sum_n dY[t][n] B[j][n]: a = j, b = t.  s0 = B, s1 = dY.
-        PlainRows<TA> pa{p.s0, p.N, p.r, p.N, a0};
-        PlainRows<TB> pb{p.s1, p.N, p.T, p.N, b0};
+        PlainRows<TA> pa;
+        pa.init(p.s0, nullptr, p.N, p.r, a0, p.N, 1 << 30);
+        PlainRows<TB> pb;
+        pb.init(p.s1, nullptr, p.N, p.T, b0, p.N, 1 << 30);
         mainloop<TA, TB>(pa, pb, kt0, kt1, acc, smem, nullptr);
         a_len = p.r_pad; b_len = p.T;
     } else if constexpr (KIND == kDA) {
         // dA[k][j] = sum over 2T of X[t][k] (G_hi | G_lo)[t][j]: a = j, b = k.  s0 = G_hi, s1 = G_lo, s2 = X.
-        TransRows<TA> pa{p.s0, p.s1, p.r_pad, p.r_pad, p.T, p.T, a0};
-        TransRows<TB> pb{p.s2, p.s2, p.K, p.K, p.T, p.T, b0};
+        TransRows<TA> pa;
+        pa.init(p.s0, p.s1, p.r_pad, p.r_pad, p.T, p.T, a0);
+        TransRows<TB> pb;
+        pb.init(p.s2, p.s2, p.K, p.K, p.T, p.T, b0);
         mainloop<TA, TB>(pa, pb, kt0, kt1, acc, smem, nullptr);
         a_len = p.r_pad; b_len = p.K;
     } else {
         // dB[j][n] = sum over 2T of (P_hi | P_lo)[t][j] dY[t][n]: a = n, b = j.  s0 = P_hi, s1 = P_lo, s2 = dY.
-        TransRows<TA> pa{p.s2, p.s2, p.N, p.N, p.T, p.T, a0};
-        TransRows<TB> pb{p.s0, p.s1, p.r_pad, p.r_pad, p.T, p.T, b0};
+        TransRows<TA> pa;
+        pa.init(p.s2, p.s2, p.N, p.N, p.T, p.T, a0);
+        TransRows<TB> pb;
+        pb.init(p.s0, p.s1, p.r_pad, p.r_pad, p.T, p.T, b0);
         mainloop<TA, TB>(pa, pb, kt0, kt1, acc, smem, nullptr);
         a_len = p.N; b_len = p.r_pad;
     }
@@ -566,7 +879,7 @@ hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* fp
     FwdArgs a{x, codes, fp8, sup, lora_b, reinterpret_cast<const uint16_t*>(ws + pl.off_ps_hi),
               reinterpret_cast<const uint16_t*>(ws + pl.off_ps_lo), y,
               pl.T, pl.K, pl.N, pl.r, pl.r_pad};
-    const size_t lds = smem_bytes<256, 256>();
+    const size_t lds = kFwdSmem;
     hipError_t e = set_smem(k_fwd, lds);
     if (e != hipSuccess) return e;
     const int64_t tiles = ceil_div(pl.N, 256) * ceil_div(pl.T, 256);

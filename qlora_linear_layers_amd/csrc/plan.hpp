@@ -17,12 +17,14 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Number of reduction splits for a small GEMM with `tiles` output tiles and
-// `ktiles` 64-wide reduction tiles: enough workgroups to cover the chip,
-// at least two reduction tiles per split.
-inline int plan_splits(int64_t tiles, int64_t ktiles) {
-    int64_t s = ceil_div(512, tiles > 0 ? tiles : 1);
-    const int64_t cap = ktiles / 2 > 1 ? ktiles / 2 : 1;
+// `ktiles` 64-wide reduction tiles: about one workgroup per compute unit
+// (256), at least four reduction tiles per split, and fp32 partials kept
+// under `part_cap` elements so that the finalize pass stays cheap.
+inline int plan_splits(int64_t tiles, int64_t ktiles, int64_t part_elems, int64_t part_cap = 4 << 20) {
+    int64_t s = ceil_div(256, tiles > 0 ? tiles : 1);
+    const int64_t cap = ktiles / 4 > 1 ? ktiles / 4 : 1;
     if (s > cap) s = cap;
+    while (s > 1 && s * part_elems > part_cap) --s;
     if (s > 64) s = 64;
     return (int)(s < 1 ? 1 : s);
 }
@@ -47,10 +49,10 @@ struct LoraPlan {
     LoraPlan(int64_t T_, int64_t K_, int64_t N_, int64_t r_) : T(T_), K(K_), N(N_), r(r_) {
         r_pad = r > 0 ? ceil_div(r, kTileSmall) * kTileSmall : 0;
         const int64_t ttiles = ceil_div(T, kTileA);
-        s_xa = plan_splits(ttiles * (r_pad / kTileSmall), K / kBK);
-        s_g = plan_splits(ttiles * (r_pad / kTileSmall), N / kBK);
-        s_da = plan_splits(ceil_div(K, kTileA) * (r_pad / kTileSmall), ceil_div(2 * T, kBK));
-        s_db = plan_splits(ceil_div(N, kTileA) * (r_pad / kTileSmall), ceil_div(2 * T, kBK));
+        s_xa = plan_splits(ttiles * (r_pad / kTileSmall), K / kBK, T * r_pad);
+        s_g = plan_splits(ttiles * (r_pad / kTileSmall), N / kBK, T * r_pad);
+        s_da = plan_splits(ceil_div(K, kTileA) * (r_pad / kTileSmall), ceil_div(2 * T, kBK), K * r_pad);
+        s_db = plan_splits(ceil_div(N, kTileA) * (r_pad / kTileSmall), ceil_div(2 * T, kBK), N * r_pad);
         const size_t tr4 = (size_t)T * r_pad * 4, tr2 = (size_t)T * r_pad * 2;
         size_t o = 0;
         if (r == 0) {

@@ -119,57 +119,58 @@ hipError_t launch_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uin
 
 // ------------------------------------------------------------------ dequantize
 //
-// Each thread expands two 16-byte chunks of codes (32 codes each, half a
-// block) into 2 x 64 bytes of bf16: c1' = fl32(e4m3(f) * s2) once per chunk,
-// then w' = RNE_bf16(fl32(q[code] * c1')) per element, with the codebook in LDS.
-constexpr int kDeqChunksPerThread = 2;
+// Lane-contiguous streaming: each thread expands 4 packed bytes (8 codes) into
+// one 16-byte bf16 store, so every wave-wide load and store instruction covers
+// one contiguous span (256 B of codes in, 1 KB of bf16 out).  A thread handles
+// kDeqUnits such units, 256 units apart, to keep several loads in flight.
+// c1' = fl32(e4m3(f) * s2) per unit; w' = RNE_bf16(fl32(q[code] * c1')) per
+// element with the codebook in LDS (16 floats: every lookup hits one of 16
+// distinct banks, so lookups never conflict).
+constexpr int kDeqUnits = 4;
 
-__global__ __launch_bounds__(256) void k_dequantize_dq(const uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(256) void k_dequantize_dq(const uint32_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ fp8,
                                                        const float* __restrict__ superscale,
-                                                       int64_t nchunks, uint16_t* __restrict__ out,
-                                                       Codebook cb) {
+                                                       int64_t nunits, u32x4_t* __restrict__ out, Codebook cb) {
     __shared__ float s_q[16];
     if (threadIdx.x < 16) s_q[threadIdx.x] = cb.q[threadIdx.x];
 
-    const int64_t c0 = (int64_t)blockIdx.x * (256 * kDeqChunksPerThread) + threadIdx.x;
-    u32x4_t cv[kDeqChunksPerThread];
-    float scale[kDeqChunksPerThread];
+    const int64_t u0 = (int64_t)blockIdx.x * (256 * kDeqUnits) + threadIdx.x;
+    uint32_t cv[kDeqUnits];
+    uint32_t f8[kDeqUnits];
+    float s2[kDeqUnits];
 #pragma unroll
-    for (int u = 0; u < kDeqChunksPerThread; ++u) {
-        const int64_t c = c0 + u * 256;
-        if (c < nchunks) {
-            cv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(codes) + c);
-            const int64_t blk = c >> 1;
-            scale[u] = __fmul_rn(e4m3_decode(fp8[blk]), superscale[blk >> 8]);
-        }
+    for (int u = 0; u < kDeqUnits; ++u) {
+        const int64_t i = u0 + u * 256;
+        const int64_t ii = i < nunits ? i : 0;
+        cv[u] = __builtin_nontemporal_load(codes + ii);
+        const int64_t blk = ii >> 3;                      // 8 units of 8 codes per block
+        f8[u] = fp8[blk];
+        s2[u] = superscale[blk >> 8];
     }
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kDeqChunksPerThread; ++u) {
-        const int64_t c = c0 + u * 256;
-        if (c >= nchunks) continue;
-        const uint32_t d[4] = {cv[u][0], cv[u][1], cv[u][2], cv[u][3]};
-        u32x4_t* o = reinterpret_cast<u32x4_t*>(out + c * 32);
+    for (int u = 0; u < kDeqUnits; ++u) {
+        const int64_t i = u0 + u * 256;
+        if (i >= nunits) continue;
+        const float c1p = __fmul_rn(e4m3_decode(f8[u]), s2[u]);
+        u32x4_t o;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            uint32_t r[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const uint32_t byte = (d[k] >> (8 * b)) & 0xFFu;
-                r[b] = pack_bf16x2(__fmul_rn(s_q[byte >> 4], scale[u]), __fmul_rn(s_q[byte & 15u], scale[u]));
-            }
-            __builtin_nontemporal_store(u32x4_t{r[0], r[1], r[2], r[3]}, o + k);
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t byte = (cv[u] >> (8 * b)) & 0xFFu;
+            o[b] = pack_bf16x2(__fmul_rn(s_q[byte >> 4], c1p), __fmul_rn(s_q[byte & 15u], c1p));
         }
+        __builtin_nontemporal_store(o, out + i);
     }
 }
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* fp8, const float* superscale,
                              int64_t numel, uint16_t* out, hipStream_t s) {
-    const int64_t nchunks = numel / 32;
-    const int64_t per_wg = 256 * kDeqChunksPerThread;
-    hipLaunchKernelGGL(k_dequantize_dq, dim3((unsigned)((nchunks + per_wg - 1) / per_wg)), dim3(256), 0, s,
-                       codes, fp8, superscale, nchunks, out, host_codebook());
+    const int64_t nunits = numel / 8;
+    const int64_t per_wg = 256 * kDeqUnits;
+    hipLaunchKernelGGL(k_dequantize_dq, dim3((unsigned)((nunits + per_wg - 1) / per_wg)), dim3(256), 0, s,
+                       reinterpret_cast<const uint32_t*>(codes), fp8, superscale, nunits,
+                       reinterpret_cast<u32x4_t*>(out), host_codebook());
     return hipGetLastError();
 }
 
