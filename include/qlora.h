@@ -121,7 +121,8 @@ size_t qlora_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r);
  *   x [T, K] bf16; codes/absmax_fp8/superscale: W [N, K] quantized as above;
  *   lora_a [K, r] bf16, lora_b [r, N] bf16 (both NULL iff r == 0);
  *   y [T, N] bf16, written.  T >= 1, K and N multiples of 64, r = 0 or a
- *   multiple of 8 up to 256.
+ *   multiple of 8 up to 256.  Size limits (32-bit operand addressing):
+ *   K, N <= 2^20, T <= 2^22, T*K <= 2^30, T*N <= 2^30, N*K < 2^32.
  *   workspace: device scratch of at least qlora_workspace_bytes(T, K, N, r)
  *   bytes (may be NULL if that is 0); its contents on entry do not matter.
  *   Errors: NULL, SHAPE, ALIGN, VALUE (non-finite scaling), WORKSPACE, DEVICE.
@@ -143,7 +144,8 @@ int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N,
  *   dy [T, N] bf16; W as in qlora_linear_fwd; dx [T, K] bf16, written;
  *   x [T, K] bf16, required iff d_lora_a or d_lora_b is non-NULL;
  *   d_lora_a [K, r] and d_lora_b [r, N] bf16, written when non-NULL
- *   (must be NULL when r == 0).
+ *   (must be NULL when r == 0).  Sizes as for qlora_linear_fwd.  The
+ *   workspace is needed even when r == 0 (block scales are staged there).
  *   Errors: NULL, SHAPE, ALIGN, VALUE, WORKSPACE, DEVICE.
  */
 int qlora_linear_bwd_input(const uint16_t* dy, int64_t T, int64_t K, int64_t N,

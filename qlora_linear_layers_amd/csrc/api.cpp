@@ -26,12 +26,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int dev(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_DEVICE; }
 
-// Shape rules shared by the linear entry points.
+// Shape rules shared by the linear entry points.  The GEMM kernels address
+// each operand with 32-bit buffer offsets, so every operand stays below 2 GiB.
 int check_linear_shape(int64_t T, int64_t K, int64_t N, int64_t r) {
     if (T < 1 || K < 64 || N < 64 || K % 64 || N % 64) return QLORA_ERR_SHAPE;
     if (r < 0 || r > QLORA_MAX_RANK || (r > 0 && r % 8)) return QLORA_ERR_SHAPE;
-    if (T > (int64_t(1) << 31) / 256 || K > (int64_t(1) << 30) || N > (int64_t(1) << 30)) return QLORA_ERR_SHAPE;
-    if (N * K > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
+    if (T > (int64_t(1) << 22) || K > (int64_t(1) << 20) || N > (int64_t(1) << 20)) return QLORA_ERR_SHAPE;
+    if (T * K > (int64_t(1) << 30) || T * N > (int64_t(1) << 30) || N * K >= (int64_t(1) << 32))
+        return QLORA_ERR_SHAPE;
     return QLORA_OK;
 }
 
@@ -120,7 +122,7 @@ int qlora_linear_bwd_input(const uint16_t* dy, int64_t T, int64_t K, int64_t N, 
         if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
     if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
     const ql::LoraPlan pl(T, K, N, r);
-    const size_t need = grads ? pl.bwd_grad_bytes : pl.bwd_bytes;
+    const size_t need = grads ? pl.bwd_grad_bytes : pl.bwd_bytes;   // > 0: the scale pre-pass needs room
     if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -692,42 +692,251 @@ struct DxArgs {
     const uint16_t* lora_a;   // [K][r]
     const uint16_t* gs_hi;    // [T][r_pad] bf16: s dY B^T = hi + lo
     const uint16_t* gs_lo;
+    const float* sclt;        // [K/64][N] block scales c1'
     uint16_t* dx;
     int64_t T, K, N, r, r_pad;
 };
 
-// dX = dY W' (+ (s dY B^T) A^T): a = k over W columns, b = t, waves 2 x 2.
+// Block scales c1' = fl32(e4m3(f) * s2) of W [N, K], written transposed as
+// [K/64][N] so that eight consecutive rows of one block column are contiguous.
+__global__ __launch_bounds__(256) void k_scales_t(const uint8_t* __restrict__ fp8, const float* __restrict__ sup,
+                                                  int64_t N, int64_t KB, float* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;     // over N x KB, n fastest
+    if (i >= N * KB) return;
+    const int64_t kb = i / N, n = i % N;
+    const int64_t b = n * KB + kb;
+    out[i] = block_scale(fp8[b], sup[b >> 8]);
+}
+
+// dX = dY W' (+ (s dY B^T) A^T): tile 256 (k) x 256 (t), reduction over n in
+// tiles of 64, waves 2 x 2 (wave (wa, wb) owns k rows wa*128.. and t rows
+// wb*128..; four A and four B fragments per MFMA step, both from LDS).
+//
+// The W tile is written to LDS already transposed ([k][n]): each thread owns
+// an 8 (n) x 8 (k) patch, i.e. one code dword of each of 8 rows; the two
+// elements of one code byte are neighbours in k, and the bf16 pack pairs
+// neighbours in n.  The codebook lookups use a 16-copy byte-pair table
+// (entry e of copy c at e*128 + c*8, lane l uses copy l & 15).
+//
+// Pipeline (per reduction tile kt): global loads of tile kt+2 (dY rows and W
+// codes + scales) into the register set freed by tile kt; the sixteen MFMAs
+// of each step of tile kt run from LDS buffer kt&1 with the next step's
+// fragment reads issued ahead; interleaved with them, tile kt+1 is staged into
+// the other LDS buffer (dY copied, W dequantized and transposed); one barrier.
+constexpr uint32_t kNarrowTableBytes = 256 * 128;
+
+QL_DEV void build_pair_table16(lds8_t* tbl, const Codebook& cb) {
+    for (int i = threadIdx.x; i < 256 * 16; i += kThreads) {
+        const int e = i >> 4;
+        const f32x2_t v = {cb.q[e >> 4], cb.q[e & 15]};
+        *reinterpret_cast<lds_f32x2_t*>(tbl + e * 128 + (i & 15) * 8) = v;
+    }
+}
+
+struct DxPipe {
+    static constexpr uint32_t kTile = 256 * 128;
+    rsrc_t rc, rs, rd;
+    uint32_t cvo, svo, dvo[8];
+    uint32_t lane8;
+    int64_t K, N;
+    int NT;
+    u32x4_t dr[8];                 // dY rows of the next tile (one tile ahead)
+    uint32_t cw[2][8];             // W codes, two tiles ahead
+    u32x4_t sc[2][2];              // eight block scales (rows n..n+7), two tiles ahead
+
+    QL_DEV void load_w(int kt, int par) {
+        kt = kt < NT ? kt : NT - 1;
+        const uint32_t soc = (uint32_t)(kt * 64 * (K / 2));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cw[par][i] = bload4(rc, cvo + i * (uint32_t)(K / 2), soc);
+        sc[par][0] = bload16(rs, svo, (uint32_t)kt * 256u);
+        sc[par][1] = bload16(rs, svo + 16, (uint32_t)kt * 256u);
+    }
+    QL_DEV void load_dy(int kt) {
+        kt = kt < NT ? kt : NT - 1;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dr[c] = bload16(rd, dvo[c], (uint32_t)kt * 128u);
+    }
+    QL_DEV void store_dy(lds8_t* l) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int ch = threadIdx.x + c * kThreads;
+            *reinterpret_cast<lds_u32x4_t*>(l + lds_off(ch >> 3, ch & 7)) = dr[c];
+        }
+    }
+    // rows 4q .. 4q+3 of the thread's 8 x 8 patch, written transposed: for each
+    // k, the dwords of row pairs (4q, 4q+1) and (4q+2, 4q+3) as one 8-byte store
+    QL_DEV void dequant_half(int par, int q, const lds8_t* tbl, lds8_t* l) {
+        float v[4][8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q + e;
+            const float c1p = __uint_as_float(sc[par][i >> 2][i & 3]);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t off = (__builtin_amdgcn_ubfe(cw[par][i], 8 * b, 8) << 7) | lane8;
+                const f32x2_t qq = *reinterpret_cast<const lds_f32x2_t*>(tbl + off);
+                v[e][2 * b] = __fmul_rn(qq[0], c1p);
+                v[e][2 * b + 1] = __fmul_rn(qq[1], c1p);
+            }
+        }
+        const int kc = threadIdx.x & 31, ng = threadIdx.x >> 5;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const u32x2_t o = {pack_bf16x2(v[0][kk], v[1][kk]), pack_bf16x2(v[2][kk], v[3][kk])};
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(l + lds_off(kc * 8 + kk, ng) + 8 * q) = o;
+        }
+    }
+};
+
+struct DxFrags {
+    bf16x8_t a[4], b[4];
+};
+
+QL_DEV void dx_reads(DxFrags& f, const lds8_t* lw, const lds8_t* ld, int s, int wa, int wb, int r, int h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = lds_frag(lw, wa * 128 + i * 32 + r, 2 * s + h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[j] = lds_frag(ld, wb * 128 + j * 32 + r, 2 * s + h);
+}
+
+QL_DEV void dx_mfma(f32x16_t (&acc)[4][4], const DxFrags& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+template <int P>
+QL_DEV void dx_tile(DxPipe& pp, int kt, f32x16_t (&acc)[4][4], lds8_t* lW, lds8_t* lD, const lds8_t* tbl,
+                    int wa, int wb, int r, int h, DxFrags& f0) {
+    constexpr int Q = P ^ 1;
+    pp.load_w(kt + 2, P);                     // set P held tile kt, staged during the previous tile
+    pp.load_dy(kt + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const lds8_t* cw = lW + P * DxPipe::kTile;
+    const lds8_t* cd = lD + P * DxPipe::kTile;
+    lds8_t* nw = lW + Q * DxPipe::kTile;
+    lds8_t* nd = lD + Q * DxPipe::kTile;
+    DxFrags f1;
+    dx_reads(f1, cw, cd, 1, wa, wb, r, h);
+    dx_mfma(acc, f0);
+    pp.dequant_half(Q, 0, tbl, nw);
+    dx_reads(f0, cw, cd, 2, wa, wb, r, h);
+    dx_mfma(acc, f1);
+    pp.dequant_half(Q, 1, tbl, nw);
+    dx_reads(f1, cw, cd, 3, wa, wb, r, h);
+    dx_mfma(acc, f0);
+    dx_mfma(acc, f1);
+    pp.store_dy(nd);
+    __syncthreads();
+    dx_reads(f0, nw, nd, 0, wa, wb, r, h);
+}
+
 __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     lds8_t* smem = (lds8_t*)(smem_raw);
-    constexpr int TA = 256, TB = 256;
-    lds8_t* const tbl = smem + 2 * (TA + TB) * 128;
-    build_pair_table(tbl, cb);
-    const int ga = (int)ceil_div(p.K, TA), gb = (int)ceil_div(p.T, TB);
+    constexpr uint32_t kTile = DxPipe::kTile;
+    lds8_t* const lW = smem;                  // 2 tiles [256 k][64 n]
+    lds8_t* const lD = smem + 2 * kTile;      // 2 tiles [256 t][64 n]
+    lds8_t* const tbl = smem + 4 * kTile;     // 16-copy pair table
+    build_pair_table16(tbl, cb);
+    const int ga = (int)ceil_div(p.K, 256), gb = (int)ceil_div(p.T, 256);
     int ta, tb;
     tile_of(blockIdx.x, ga, gb, ta, tb);
-    const int64_t k0 = (int64_t)ta * TA, t0 = (int64_t)tb * TB;
-    __syncthreads();
+    const int64_t k0 = (int64_t)ta * 256, t0 = (int64_t)tb * 256;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wa = wave >> 1, wb = wave & 1;
+    const int r = lane & 31, h = lane >> 5;
 
-    Acc<TA, TB> acc;
-    acc.zero();
+    DxPipe pp;
+    pp.K = p.K;
+    pp.N = p.N;
+    pp.NT = (int)(p.N / 64);
+    pp.rc = make_rsrc(p.codes, p.N * p.K / 2);
+    pp.rs = make_rsrc(p.sclt, (p.K / 64) * p.N * 4);
+    pp.rd = make_rsrc(p.dy, p.T * p.N * 2);
+    pp.lane8 = (uint32_t)(lane & 15) * 8u;
     {
-        NF4Cols pa;
-        pa.init(p.codes, p.fp8, p.sup, p.K, p.N, k0);
-        PlainRows<TB> pb;
-        pb.init(p.dy, nullptr, p.N, p.T, t0, p.N, 1 << 30);
-        mainloop<TA, TB>(pa, pb, 0, (int)(p.N / 64), acc, smem, tbl);
+        const int64_t k = k0 + (threadIdx.x & 31) * 8;
+        const int64_t n = (threadIdx.x >> 5) * 8;
+        const bool ok = k < p.K;
+        pp.cvo = ok ? (uint32_t)(n * (p.K / 2) + k / 2) : kOOB;
+        pp.svo = ok ? (uint32_t)(((k / 64) * p.N + n) * 4) : kOOB;
     }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int ch = threadIdx.x + c * kThreads;
+        const int64_t t = t0 + (ch >> 3);
+        pp.dvo[c] = t < p.T ? (uint32_t)((t * p.N + (ch & 7) * 8) * 2) : kOOB;
+    }
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // prologue: W tiles 0 and 1 in flight; tile 0 staged and its step-0 fragments read
+    pp.load_w(0, 0);
+    pp.load_w(1, 1);
+    pp.load_dy(0);
+    __syncthreads();                          // pair table visible
+    pp.dequant_half(0, 0, tbl, lW);
+    pp.dequant_half(0, 1, tbl, lW);
+    pp.store_dy(lD);
+    __syncthreads();
+    DxFrags f0;
+    dx_reads(f0, lW, lD, 0, wa, wb, r, h);
+    const int NT = pp.NT;
+    int kt = 0;
+    for (; kt + 1 < NT; kt += 2) {
+        dx_tile<0>(pp, kt, acc, lW, lD, tbl, wa, wb, r, h, f0);
+        dx_tile<1>(pp, kt + 1, acc, lW, lD, tbl, wa, wb, r, h, f0);
+    }
+    if (kt < NT) dx_tile<0>(pp, kt, acc, lW, lD, tbl, wa, wb, r, h, f0);
+
     if (p.r > 0) {
+        // LoRA term (s dY B^T) A^T: reduction over [hi | lo] of s dY B^T against A stacked twice
         const int half = (int)(p.r_pad / 64);
-        PlainRows<TA, true> pa;
+        PlainRows<256, true> pa;
         pa.init(p.lora_a, p.lora_a, p.r, p.K, k0, p.r, half);
-        PlainRows<TB> pb;
+        PlainRows<256> pb;
         pb.init(p.gs_hi, p.gs_lo, p.r_pad, p.T, t0, p.r_pad, half);
-        mainloop<TA, TB>(pa, pb, 0, 2 * half, acc, smem, tbl);
+        for (int lt = 0; lt < 2 * half; ++lt) {
+            pa.load(lt);
+            pb.load(lt);
+            __syncthreads();
+            pa.store(lW, tbl);
+            pb.store(lD, tbl);
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                DxFrags f;
+                dx_reads(f, lW, lD, s, wa, wb, r, h);
+                dx_mfma(acc, f);
+            }
+        }
     }
-    store_out<TA, TB, true>(acc, p.dx, p.K, k0, t0, p.K, p.T);
+    // C[k][t] -> dX[t][k]
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t t = t0 + wb * 128 + j * 32 + r;
+            if (t >= p.T) continue;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t k = k0 + wa * 128 + i * 32 + g * 8 + h * 4;
+                if (k < p.K) store4<true>(acc[i][j], g, p.dx, p.K, k, t);
+            }
+        }
 }
+
+constexpr size_t kDxSmem = 4 * 256 * 128 + kNarrowTableBytes;
 
 // ------------------------------------------------------------------ small LoRA products
 
@@ -889,10 +1098,16 @@ hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* fp
 
 hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* fp8, const float* sup,
                      const uint16_t* lora_a, const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s) {
+    float* sclt = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + pl.off_scl);
+    const int64_t nsc = (pl.K / 64) * pl.N;
+    hipLaunchKernelGGL(k_scales_t, dim3((unsigned)ceil_div(nsc, 256)), dim3(256), 0, s, fp8, sup, pl.N, pl.K / 64,
+                       sclt);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
     DxArgs a{dy, codes, fp8, sup, lora_a, reinterpret_cast<const uint16_t*>(ws + pl.off_gs_hi),
-             reinterpret_cast<const uint16_t*>(ws + pl.off_gs_lo), dx,
+             reinterpret_cast<const uint16_t*>(ws + pl.off_gs_lo), sclt, dx,
              pl.T, pl.K, pl.N, pl.r, pl.r_pad};
-    const size_t lds = smem_bytes<256, 256>();
+    const size_t lds = kDxSmem;
     hipError_t e = set_smem(k_dx, lds);
     if (e != hipSuccess) return e;
     const int64_t tiles = ceil_div(pl.K, 256) * ceil_div(pl.T, 256);

@@ -44,6 +44,7 @@ struct LoraPlan {
     size_t off_pxa, off_ps_hi, off_ps_lo;     // fp32 partials [s_xa][T][r_pad], bf16 [T][r_pad] x 2
     size_t off_pg, off_gs_hi, off_gs_lo;      // fp32 partials [s_g][T][r_pad], bf16 [T][r_pad] x 2
     size_t off_pda, off_pdb;                  // fp32 partials [s_da][K][r_pad], [s_db][r_pad][N]
+    size_t off_scl;                           // fp32 block scales c1', transposed [K/64][N] (backward)
     size_t fwd_bytes, bwd_bytes, bwd_grad_bytes;
 
     LoraPlan(int64_t T_, int64_t K_, int64_t N_, int64_t r_) : T(T_), K(K_), N(N_), r(r_) {
@@ -54,12 +55,16 @@ struct LoraPlan {
         s_da = plan_splits(ceil_div(K, kTileA) * (r_pad / kTileSmall), ceil_div(2 * T, kBK), K * r_pad);
         s_db = plan_splits(ceil_div(N, kTileA) * (r_pad / kTileSmall), ceil_div(2 * T, kBK), N * r_pad);
         const size_t tr4 = (size_t)T * r_pad * 4, tr2 = (size_t)T * r_pad * 2;
+        const size_t scl = align256((size_t)(K / 64) * N * 4);
         size_t o = 0;
         if (r == 0) {
             off_pxa = off_ps_hi = off_ps_lo = off_pg = off_gs_hi = off_gs_lo = off_pda = off_pdb = 0;
-            fwd_bytes = bwd_bytes = bwd_grad_bytes = 0;
+            off_scl = 0;
+            fwd_bytes = 0;
+            bwd_bytes = bwd_grad_bytes = scl;
             return;
         }
+        off_scl = o;   o = align256(o + scl);
         off_pxa = o;   o = align256(o + tr4 * s_xa);
         off_ps_hi = o; o = align256(o + tr2);
         off_ps_lo = o; o = align256(o + tr2);

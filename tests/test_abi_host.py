@@ -83,6 +83,7 @@ def test_fwd_validation(L):
     assert _fwd(L, N=32) == SHAPE
     assert _fwd(L, r=12) == SHAPE
     assert _fwd(L, r=264) == SHAPE
+    assert _fwd(L, T=1 << 20, K=2048) == SHAPE      # T*K above 2^30
     assert _fwd(L, r=0) == SHAPE            # adapters given with r = 0
     assert _fwd(L, y=MIS) == ALIGN
     assert _fwd(L, s=math.inf) == VALUE
@@ -112,7 +113,8 @@ def test_bwd_validation(L):
 
 
 def test_workspace_bytes(L):
-    assert L.qlora_workspace_bytes(16, 4096, 4096, 0) == 0
+    assert L.qlora_workspace_bytes(16, 4096, 4096, 0) == (4096 // 64) * 4096 * 4   # backward block scales
+    assert L.qlora_workspace_bytes(1 << 23, 4096, 4096, 16) == 0                     # T too large
     assert L.qlora_workspace_bytes(16, 100, 4096, 16) == 0
     a = L.qlora_workspace_bytes(4096, 4096, 11008, 64)
     b = L.qlora_workspace_bytes(4096, 4096, 11008, 16)
