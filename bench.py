@@ -52,6 +52,45 @@ def roofline_seconds(kind, amount):
     return amount / (HBM_PEAK if kind == "hbm" else MFMA_BF16_PEAK)
 
 
+def decode_bytes(lin, T, r):
+    """Algorithmic bytes of one decode-size forward: the packed weight, X, Y and the adapters."""
+    return storage_bytes(lin.N * lin.K) + 2 * T * lin.K + 2 * T * lin.N + 2 * r * (lin.K + lin.N)
+
+
+def measure_decode(api, torch, layers, qws, r, s, tokens=(1, 4, 8), copies=6, reps=10):
+    """Decode-size forward over the seven linears, rotating `copies` copies of the
+    quantized weights (about 100 MB each) so that the 256 MB last-level cache
+    cannot serve repeats.  Returns {T: (seconds per layer set, bytes per layer set)}."""
+    import numpy as np
+    sets = [[api.NF4Weight(q.codes.clone(), q.absmax_fp8.clone(), q.superscale.clone(), q.N, q.K) for q in qws]
+            for _ in range(copies)]
+    out = {}
+    for T in tokens:
+        g = torch.Generator(device="cuda").manual_seed(T)
+        xs = [torch.randn((T, l.K), generator=g, device="cuda").to(torch.bfloat16) for l in layers]
+        a = [torch.randn((l.K, r), generator=g, device="cuda").mul_(0.01).to(torch.bfloat16) for l in layers]
+        b = [torch.randn((r, l.N), generator=g, device="cuda").mul_(0.01).to(torch.bfloat16) for l in layers]
+        ys = [torch.empty((T, l.N), dtype=torch.bfloat16, device="cuda") for l in layers]
+        ws = torch.empty(max(api.qlora_workspace_bytes(T, l.K, l.N, r) for l in layers), dtype=torch.uint8,
+                         device="cuda")
+
+        def one(c):
+            for i, l in enumerate(layers):
+                api.qlora_linear_fwd(xs[i], sets[c][i], a[i], b[i], s, workspace=ws, out=ys[i])
+        for c in range(copies):
+            one(c)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for k in range(reps):
+            one(k % copies)
+        ev[1].record()
+        torch.cuda.synchronize()
+        secs = ev[0].elapsed_time(ev[1]) / 1e3 / reps
+        out[T] = (secs, sum(decode_bytes(l, T, r) for l in layers))
+    return out
+
+
 def cpu_baseline(layers, T, r, s, t_sample):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -199,6 +238,12 @@ def main():
         "components": comp,
         "roofline": roofline,
     }
+    dec = measure_decode(api, torch, layers, [b["qw"] for b in bufs], r, s)
+    for Td, (secs, nbytes) in dec.items():
+        comp[f"decode_T{Td}"] = {"GB/s": round(nbytes / secs / 1e9, 1),
+                                 "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
+                                 "us_per_layer_set": round(1e6 * secs, 2),
+                                 "note": "7 linears, fused dequant + VALU GEMV incl. LoRA; weights rotated over 6 copies"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, T, r, s, args.cpu_tokens)
     print(json.dumps(out), flush=True)

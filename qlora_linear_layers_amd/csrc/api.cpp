@@ -81,7 +81,13 @@ int nf4_dequantize_dq(const uint8_t* codes, const uint8_t* absmax_fp8, const flo
 
 size_t qlora_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r) {
     if (check_linear_shape(T, K, N, r) != QLORA_OK) return 0;
-    return ql::LoraPlan(T, K, N, r).bwd_grad_bytes;
+    const ql::LoraPlan pl(T, K, N, r);
+    size_t n = pl.bwd_grad_bytes;
+    if (T <= ql::kGemvMaxT) {
+        const size_t g = ql::gemv_workspace(T, K, N, pl.r_pad);
+        if (g > n) n = g;
+    }
+    return n;
 }
 
 int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* codes,
@@ -97,10 +103,13 @@ int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N, const u
         return QLORA_ERR_ALIGN;
     if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
     const ql::LoraPlan pl(T, K, N, r);
-    if (pl.fwd_bytes && (!workspace || workspace_bytes < pl.fwd_bytes)) return QLORA_ERR_WORKSPACE;
+    const size_t need = T <= ql::kGemvMaxT ? ql::gemv_workspace(T, K, N, pl.r_pad) : pl.fwd_bytes;
+    if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
+    if (T <= ql::kGemvMaxT)      // decode sizes: VALU GEMV, no MFMA
+        return dev(ql::launch_gemv(x, codes, absmax_fp8, superscale, lora_a, lora_b, scaling, pl, ws, y, s));
     if (r > 0)
         if (int st = dev(ql::launch_lora_down_x(x, lora_a, scaling, pl, ws, s))) return st;
     return dev(ql::launch_fwd(x, codes, absmax_fp8, superscale, lora_b, pl, ws, y, s));

@@ -74,11 +74,23 @@ QL_DEV uint32_t e4m3_encode_tie_low(float y) {
     return code + ((b & 0xFFFFFu) > 0x80000u ? 1u : 0u);        // strictly above half -> up
 }
 
+// Block scale c1' = fl32(e4m3(f) * s2) (first step of the reverse-order
+// dequantization).
+QL_DEV float block_scale(uint32_t f8, float s2) { return __fmul_rn(e4m3_decode(f8), s2); }
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* fp8,
                            float* superscale, hipStream_t s);
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* fp8, const float* superscale,
                              int64_t numel, uint16_t* out, hipStream_t s);
+
+// Forward calls with at most this many tokens take the VALU GEMV path.
+constexpr int64_t kGemvMaxT = 16;
+struct LoraPlan;
+size_t gemv_workspace(int64_t T, int64_t K, int64_t N, int64_t r_pad);
+hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, const uint8_t* fp8, const float* sup,
+                       const uint16_t* lora_a, const uint16_t* lora_b, float scaling, const LoraPlan& pl,
+                       uint8_t* ws, uint16_t* y, hipStream_t s);
 
 }  // namespace ql

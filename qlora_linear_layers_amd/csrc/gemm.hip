@@ -104,8 +104,6 @@ QL_DEV u32x4_t deq_dword(uint32_t d, float c1p, const lds8_t* tbl) {
     return o;
 }
 
-// Block scale c1' = fl32(e4m3(f) * s2).
-QL_DEV float block_scale(uint32_t f8, float s2) { return __fmul_rn(e4m3_decode(f8), s2); }
 
 // ------------------------------------------------------------------ LDS tile producers
 

@@ -132,3 +132,21 @@ def test_determinism():
         dy, qw, a, b, 0.5, x=x, lora_grads=True)]
     for u, v in zip(r1, r2):
         assert np.array_equal(u, v)
+
+
+@pytest.mark.parametrize("idx", [0, 4, 6])
+def test_decode_7b_shapes_full(idx):
+    """Decode-size forward (VALU GEMV path) on the 7B layer shapes, r = 64, s = 0.25,
+    T = 1, 4, 8: every output against the oracle."""
+    lin = synth.LLAMA7B[idx]
+    d = synth.layer_inputs(2, 0, idx, lin, 8, 64)
+    qw = api.nf4_quantize_dq(to_dev(d["w"], (lin.N, lin.K)))
+    rc, rf, rs = oracle.quantize_nf4_dq(d["w"])
+    wd = oracle.dequantize_nf4_dq(rc, rf, rs).reshape(lin.N, lin.K)
+    a, b = to_dev(d["a"], (lin.K, 64)), to_dev(d["b"], (64, lin.N))
+    for T in (1, 4, 8):
+        say(f"[decode] {lin.name} {lin.N}x{lin.K} T={T}")
+        x = to_dev(d["x"][:T], (T, lin.K))
+        y = api.qlora_linear_fwd(x, qw, a, b, 0.25)
+        ref = oracle.linear_fwd(d["x"][:T], wd, d["a"], d["b"], 0.25)
+        assert_gemm_close(bits_of(y), ref, f"decode {lin.name} T={T}")
