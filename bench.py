@@ -27,6 +27,48 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # bytes/s
 MFMA_BF16_PEAK = 2.5e15    # flop/s, dense
+GEMM_SOURCE = os.path.join(ROOT, "qlora_linear_layers_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fwd_llama7b_T4096_traffic.txt")
+COPY_BYTES = 256 << 20     # calibration copy for the HBM byte counters
+
+
+def source_hash():
+    import hashlib
+    with open(GEMM_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per k_fwd launch from the committed counter summary, if it was taken
+    on the current GEMM source (otherwise None)."""
+    try:
+        kv = dict(l.strip().split("=", 1) for l in open(TRAFFIC_FILE) if "=" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("gemm_source_sha256_16") != source_hash():
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def measure_roofline_kernel(api, torch, layers, bufs, reps):
+    """k_fwd alone: the forward with r = 0 is exactly one launch of the fused
+    NF4-dequant MFMA GEMM.  Returns (flops per launch, seconds per launch)."""
+    ys = [torch.empty((b["x"].shape[0], b["lin"].N), dtype=torch.bfloat16, device="cuda") for b in bufs]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps * len(bufs))]
+    for i, b in enumerate(bufs):
+        api.qlora_linear_fwd(b["x"], b["qw"], out=ys[i])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    for k in range(reps):
+        for i, b in enumerate(bufs):
+            e = ev[k * len(bufs) + i]
+            e[0].record(stream)
+            api.qlora_linear_fwd(b["x"], b["qw"], out=ys[i])
+            e[1].record(stream)
+    torch.cuda.synchronize()
+    secs = sum(e[0].elapsed_time(e[1]) for e in ev) / 1e3 / len(ev)
+    flops = sum(2 * b["x"].shape[0] * b["lin"].N * b["lin"].K for b in bufs) / len(bufs)
+    return flops, secs
 
 
 def storage_bytes(numel):
@@ -126,6 +168,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="only the calibration copy and the k_fwd launches (for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path is single-GPU by design); --gpus {args.gpus} is not "
@@ -160,6 +204,17 @@ def main():
         b["db"] = torch.empty((r, lin.N), dtype=torch.bfloat16, device="cuda")
         bufs.append(b)
     torch.cuda.synchronize()
+
+    if args.roofline_only:
+        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        c = torch.empty_like(a)
+        for _ in range(3):
+            c.copy_(a)
+        flops, secs = measure_roofline_kernel(api, torch, layers, bufs, args.steps)
+        print(json.dumps({"roofline_kernel": "k_fwd", "tflops": flops / secs / 1e12, "us_per_launch": secs * 1e6,
+                          "copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES,
+                          "gemm_source_sha256_16": source_hash()}), flush=True)
+        return
 
     phases = ("quantize", "dequantize", "forward", "backward")
     stream = torch.cuda.current_stream()
@@ -216,14 +271,17 @@ def main():
             comp[p] = {"TFLOP/s": round(amt / secs / 1e12, 1), "frac_of_mfma_peak": round(rs / secs, 4),
                        "ms": round(1e3 * secs, 4)}
 
-    # roofline of the dominant unit: the fused forward call, per linear shape
-    fwd_flops = sum(phase_work(b["lin"], T, r)["forward"][1] for b in bufs)
-    fwd_secs = dur["forward"].sum() / 1e3
-    achieved = fwd_flops / fwd_secs / 1e12
+    # roofline of the dominant kernel: k_fwd, timed alone (r = 0 forward = one launch)
+    rf_flops, rf_secs = measure_roofline_kernel(api, torch, layers, bufs, max(args.steps // 2, 3))
+    achieved = rf_flops / rf_secs / 1e12
+    traffic = stored_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": 2500.0, "unit": "TFLOP/s",
-                "frac": round(achieved / 2500.0, 4), "traffic": None,
-                "kernel": "qlora_linear_fwd (fused NF4-dequant MFMA GEMM + LoRA down-projection)",
-                "per_linear_ms": {b["lin"].name: round(float(dur["forward"][i]), 4) for i, b in enumerate(bufs)}}
+                "frac": round(achieved / 2500.0, 4),
+                "traffic": None if traffic is None else round(traffic),
+                "kernel": "k_fwd: fused NF4 double-dequant + MFMA bf16 GEMM, 7B layer shapes at T=4096 "
+                          "(per-launch average over the 7 linears)",
+                "us_per_launch": round(1e6 * rf_secs, 2),
+                "flops_per_launch": rf_flops}
 
     out = {
         "metric": "QLoRA linear fwd TFLOP/s + NF4 quant/dequant GB/s, as % of MI355X roofline",
