@@ -7,19 +7,20 @@
 // with W' the double-dequantized bf16 weight ("QLoRA 原理精讲" section 2.2:
 // super-scale, then block constant, then weight) that is never written to HBM.
 //
-// Structure.  Every product here is C[a][b] = sum_k Pa(a, k) * Pb(b, k) with
-// both operands staged in LDS as [rows][64] bf16 tiles (reduction contiguous),
-// consumed by v_mfma_f32_32x32x16_bf16 from four wave64s arranged 2 x 2.
-// What differs between the products is only how a tile is produced:
-//   PlainRows  - bf16 rows already contiguous along the reduction (X, dY, ...)
-//   NF4Rows    - W rows: 64 codes + one block scale per row -> bf16 in LDS
-//   NF4Cols    - W read transposed for dX: an 8 x 8 code patch per thread,
-//                dequantized and paired across rows by the bf16 pack itself
-//   TransRows  - bf16 stored with the reduction as the row index (A, B, X, dY
-//                in the LoRA products): pairs of rows packed into dwords
-// and how C leaves the kernel (bf16 rows of the output, or fp32 split-K
-// partials reduced in a fixed order by a finalize kernel, so results are
-// deterministic).
+// Structure.  Every product is a sum over 64-wide reduction tiles of
+// v_mfma_f32_32x32x16_bf16 steps, with both operands fed as 8 consecutive
+// reduction elements per lane:
+//   k_fwd   - W rows dequantized straight into A-operand registers, X through
+//             swizzled LDS (reduction over k is contiguous in both);
+//   k_dx    - W dequantized and transposed into LDS ([k][n] tiles), dY through
+//             LDS (reduction over n);
+//   k_small - the rank-r LoRA products, with operands staged by PlainRows (bf16
+//             rows contiguous along the reduction) or TransRows (bf16 stored
+//             with the reduction as the row index: row pairs packed into dwords).
+// NF4 codes are decoded with byte-pair tables in LDS: one 8-byte read returns
+// the two fp32 codewords of a packed byte.  Outputs leave as bf16 rows, or as
+// fp32 split-reduction partials that k_finalize sums in a fixed order, so
+// every result is deterministic.
 #include "common.hpp"
 #include "plan.hpp"
 
@@ -38,6 +39,18 @@ typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 typedef __attribute__((address_space(3))) float lds_f32_t;
+typedef __attribute__((address_space(3))) f32x2_t lds_f32x2_t;
+
+// LDS byte address of a pointer, and a pointer from an LDS byte address.  The
+// codebook tables are aligned to their own size (64 KB / 32 KB) inside LDS, so
+// a lookup address is the table's address OR-ed with the entry offset, built
+// by one permute or shift-or with no add (dynamic LDS starts at address 0 in
+// these kernels, which declare no static LDS).
+QL_DEV uint32_t lds_addr(const lds8_t* p) { return (uint32_t)(uintptr_t)p; }
+template <class T>
+QL_DEV const __attribute__((address_space(3))) T* lds_at(uint32_t a) {
+    return reinterpret_cast<const __attribute__((address_space(3))) T*>((uintptr_t)a);
+}
 
 // LDS tile of [rows][64] bf16: 128 bytes per row in 16-byte chunks, the chunk
 // index XOR-swizzled with bits of the row so that the 32-row fragment reads
@@ -67,43 +80,6 @@ QL_DEV uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
 QL_DEV uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
 }
-
-// ------------------------------------------------------------------ NF4 decode
-
-// Byte-pair codebook: entry e holds (q[e >> 4], q[e & 15]) as two floats, i.e.
-// the codewords of the even (high nibble) and odd (low nibble) element of a
-// packed byte.  Built once per workgroup in LDS (2 KB); one 8-byte LDS read
-// decodes two elements.
-constexpr uint32_t kPairTableBytes = 256 * 8;
-typedef __attribute__((address_space(3))) f32x2_t lds_f32x2_t;
-
-QL_DEV void build_pair_table(lds8_t* tbl, const Codebook& cb) {
-    const int t = threadIdx.x;
-    const f32x2_t v = {cb.q[t >> 4], cb.q[t & 15]};
-    *reinterpret_cast<lds_f32x2_t*>(tbl + t * 8) = v;
-}
-
-// Byte b of dword d, times 8 (its pair-table offset).
-QL_DEV uint32_t byte_x8(uint32_t d, int b) { return b == 0 ? ((d << 3) & 0x7F8u) : ((d >> (8 * b - 3)) & 0x7F8u); }
-
-// Two elements of byte b: fl32(q * c1') each (the bf16 rounding happens at the pack).
-QL_DEV f32x2_t deq_pair(uint32_t d, int b, float c1p, const lds8_t* tbl) {
-    const f32x2_t qq = *reinterpret_cast<const lds_f32x2_t*>(tbl + byte_x8(d, b));
-    return f32x2_t{__fmul_rn(qq[0], c1p), __fmul_rn(qq[1], c1p)};
-}
-
-// Eight elements of one packed dword (element 2b in the high nibble of byte b)
-// as bf16 in element order: w' = RNE_bf16(fl32(q[code] * c1')).
-QL_DEV u32x4_t deq_dword(uint32_t d, float c1p, const lds8_t* tbl) {
-    u32x4_t o;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const f32x2_t v = deq_pair(d, b, c1p, tbl);
-        o[b] = pack_bf16x2(v[0], v[1]);
-    }
-    return o;
-}
-
 
 // ------------------------------------------------------------------ LDS tile producers
 
@@ -156,66 +132,6 @@ struct PlainRows {
         for (int i = 0; i < kChunks; ++i) {
             const int c = threadIdx.x + i * kThreads;
             *reinterpret_cast<lds_u32x4_t*>(lds + lds_off(c >> 3, c & 7)) = reg[i];
-        }
-    }
-};
-
-// W read transposed for dX: tile rows are k (256 of them), the reduction runs
-// over n (64 per tile).  Thread t owns k = k0 + (t % 32) * 8 .. +7 and
-// n = kt*64 + (t / 32) * 8 .. +7: eight 4-byte code words and eight block
-// scales.  Two elements of one code byte are neighbours in k; the bf16 pack
-// pairs neighbours in n, which writes the transposed tile directly.
-struct NF4Cols {
-    const uint8_t* codes;
-    const uint8_t* fp8;
-    const float* sup;
-    int64_t K, N;
-    uint32_t cvo, fvo, blk0;       // per-thread offsets at kt = 0 (row n = ng*8)
-    bool ok;
-    uint32_t cw[8], f8[8];
-    float s2[8];
-
-    QL_DEV void init(const uint8_t* c, const uint8_t* f, const float* su, int64_t K_, int64_t N_, int64_t col0) {
-        codes = c; fp8 = f; sup = su; K = K_; N = N_;
-        const int64_t k = col0 + (threadIdx.x & 31) * 8;
-        const int64_t n = (threadIdx.x >> 5) * 8;
-        ok = k < K;
-        cvo = ok ? (uint32_t)(n * (K / 2) + k / 2) : kOOB;
-        fvo = ok ? (uint32_t)(n * (K / 64) + k / 64) : kOOB;
-        blk0 = (uint32_t)(n * (K / 64) + (ok ? k / 64 : 0));
-    }
-    QL_DEV void load(int kt) {
-        const rsrc_t rc = make_rsrc(codes, N * K / 2);
-        const rsrc_t rf = make_rsrc(fp8, N * K / 64);
-        const rsrc_t rs = make_rsrc(sup, ceil_div(N * K / 64, 256) * 4);
-        const uint32_t soc = (uint32_t)(kt * 64 * (K / 2)), sof = (uint32_t)(kt * 64 * (K / 64));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            cw[i] = bload4(rc, cvo + i * (uint32_t)(K / 2), soc);
-            f8[i] = bload1(rf, fvo + i * (uint32_t)(K / 64), sof);
-            const uint32_t blk = blk0 + sof + i * (uint32_t)(K / 64);
-            s2[i] = __uint_as_float(bload4(rs, ok ? (blk >> 8) * 4u : kOOB, 0));
-        }
-    }
-    QL_DEV void store(lds8_t* lds, const lds8_t* tbl) {
-        const int kc = threadIdx.x & 31, ng = threadIdx.x >> 5;
-        float v[8][8];                                   // [row i][k]
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float c1p = block_scale(f8[i], s2[i]);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const f32x2_t e = deq_pair(cw[i], b, c1p, tbl);
-                v[i][2 * b] = e[0];
-                v[i][2 * b + 1] = e[1];
-            }
-        }
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            u32x4_t o;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) o[p] = pack_bf16x2(v[2 * p][kk], v[2 * p + 1][kk]);
-            *reinterpret_cast<lds_u32x4_t*>(lds + lds_off(kc * 8 + kk, ng)) = o;
         }
     }
 };
@@ -344,7 +260,7 @@ QL_DEV void mainloop(PA& pa, PB& pb, int kt0, int kt1, Acc<TA, TB>& acc, lds8_t*
 }
 
 template <int TA, int TB>
-constexpr size_t smem_bytes() { return (size_t)2 * (TA + TB) * 128 + kPairTableBytes; }
+constexpr size_t smem_bytes() { return (size_t)2 * (TA + TB) * 128; }
 
 // Output C[a][b] to out[b][a] (a contiguous) for the 2 x 2 wave layout: each
 // lane holds four consecutive a for one b per MFMA row group.  bf16 (8-byte
@@ -426,20 +342,6 @@ QL_DEV void build_wide_pair_table(lds8_t* tbl, const Codebook& cb) {
     }
 }
 
-// Eight elements of one packed dword as bf16 (see deq_dword), with the lane's
-// own table copy; lane8 = (lane & 31) * 8 sits in the low byte of the address.
-QL_DEV u32x4_t deq_dword_wide(uint32_t d, float c1p, const lds8_t* tbl, uint32_t lane8) {
-    u32x4_t o;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        // bytes of the address: [0] = lane8, [1] = byte b of d, [2], [3] = 0
-        const uint32_t off = __builtin_amdgcn_perm(d, lane8, 0x0C0C0000u | ((4u + b) << 8));
-        const f32x2_t qq = *reinterpret_cast<const lds_f32x2_t*>(tbl + off);
-        o[b] = pack_bf16x2(__fmul_rn(qq[0], c1p), __fmul_rn(qq[1], c1p));
-    }
-    return o;
-}
-
 // Y = X W'^T (+ (s X A) B), tile 256 (n) x 256 (t), waves stacked along n.
 //
 // Wave w owns W rows n0 + 64w .. +63 (two 32-row MFMA A-fragments) against all
@@ -452,10 +354,8 @@ QL_DEV u32x4_t deq_dword_wide(uint32_t d, float c1p, const lds8_t* tbl, uint32_t
 //
 // Pipeline.  Global loads run two k tiles ahead (X and W codes into
 // registers, alternating register sets by tile parity); X is written to the
-// idle LDS buffer one tile ahead; inside a tile, the LDS reads of step s+1
-// (eight X fragments, eight codebook lookups) are issued before the sixteen
-// MFMAs of step s, and step s+1's A fragments are finished while those MFMAs
-// run.  One barrier per tile.
+// idle LDS buffer one tile ahead, in the middle of the last step of a tile;
+// one barrier per tile.  Within the tile, see fwd_tile.
 struct FwdPipe {
     static constexpr int TT = 256;
     static constexpr uint32_t kTile = TT * 128;   // one [256][64] bf16 LDS tile
@@ -493,76 +393,119 @@ struct FwdPipe {
     }
 };
 
-// LDS reads of one MFMA step: eight X fragments and the eight codebook pairs
-// of the two A fragments (codes dword s of each W row).
-struct StepIn {
-    bf16x8_t x[8];
-    f32x2_t q[2][4];
-};
+// Pieces of one MFMA step s (16 k): eight X fragments from LDS, the eight
+// codebook pairs of the two A fragments (codes dword s of each W row), the
+// A fragments themselves, and the sixteen MFMAs.
+typedef bf16x8_t XFr[8];
+typedef f32x2_t QPr[2][4];
+typedef bf16x8_t AFr[2];
 
-QL_DEV void step_reads(StepIn& in, const lds8_t* xb, int s, const u32x4_t (&wc)[2], const lds8_t* tbl,
-                       uint32_t lane8, int r, int h) {
+QL_DEV void read_x(XFr& x, const lds8_t* xb, int s, int r, int h) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = lds_frag(xb, 32 * j + r, 4 * h + s);
+}
+
+QL_DEV void read_q(QPr& q, const u32x4_t (&wc)[2], int s, uint32_t lane8) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const uint32_t off = __builtin_amdgcn_perm(wc[i][s], lane8, 0x0C0C0000u | ((4u + b) << 8));
-            in.q[i][b] = *reinterpret_cast<const lds_f32x2_t*>(tbl + off);
+            // address bytes: [0] lane copy, [1] code byte b, [2..3] from the table base
+            const uint32_t addr = __builtin_amdgcn_perm(wc[i][s], lane8, 0x03020000u | ((4u + b) << 8));
+            q[i][b] = *lds_at<f32x2_t>(addr);
         }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) in.x[j] = lds_frag(xb, 32 * j + r, 4 * h + s);
 }
 
-QL_DEV void step_frags(bf16x8_t (&a)[2], const StepIn& in, const float (&c1p)[2]) {
+QL_DEV void make_a(AFr& a, const QPr& q, const float (&c1p)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         u32x4_t o;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-            o[b] = pack_bf16x2(__fmul_rn(in.q[i][b][0], c1p[i]), __fmul_rn(in.q[i][b][1], c1p[i]));
+        for (int b = 0; b < 4; ++b) o[b] = pack_bf16x2(__fmul_rn(q[i][b][0], c1p[i]), __fmul_rn(q[i][b][1], c1p[i]));
         a[i] = __builtin_bit_cast(bf16x8_t, o);
     }
 }
 
-QL_DEV void step_mfma(f32x16_t (&acc)[2][8], const bf16x8_t (&a)[2], const StepIn& in) {
+QL_DEV void mfma16(f32x16_t (&acc)[2][8], const AFr& a, const XFr& x) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], in.x[j], acc[0][j], 0, 0, 0);
-        acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], in.x[j], acc[1][j], 0, 0, 0);
+        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], x[j], acc[0][j], 0, 0, 0);
+        acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], x[j], acc[1][j], 0, 0, 0);
     }
 }
 
-// One k tile.  On entry `in0`/`a0` hold step 0 of tile kt (reads done, A
-// fragments built); on exit they hold step 0 of tile kt+1.
+// Scheduling hint for one step: each MFMA followed by one LDS read and two
+// VALU instructions, so the reads and the dequantization of later steps issue
+// in the shadow of the 32-cycle MFMAs instead of in front of them.
+template <int kMfma, int kReads, int kValu>
+QL_DEV void interleave() {
+#pragma unroll
+    for (int j = 0; j < kMfma; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+        if (j < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        if (j < kValu) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);    // VALU
+    }
+}
+
+// One k tile (parity P: LDS buffer and register sets).  Software pipeline over
+// the steps: while the MFMAs of step s run, the X fragments of step s+1 and
+// the codebook pairs of step s+2 are read, and the A fragments of step s+1
+// are built from pairs read during step s-1.  On entry xa / aa hold step 0 of
+// tile kt and qa the pairs of step 1; on exit the same for tile kt+1.
 template <int P>
-QL_DEV void fwd_tile(FwdPipe& pp, int kt, f32x16_t (&acc)[2][8], lds8_t* lX, const lds8_t* tbl, int r, int h,
-                     StepIn& in0, bf16x8_t (&a0)[2]) {
+QL_DEV void fwd_tile(FwdPipe& pp, int kt, f32x16_t (&acc)[2][8], lds8_t* lX, int r, int h, XFr& xa, AFr& aa,
+                     QPr& qa, float (&c1p)[2]) {
     constexpr int Q = P ^ 1;
-    pp.load_x(kt + 2, P);                     // X set P held tile kt, already in LDS
-    __builtin_amdgcn_sched_barrier(0);
     const lds8_t* xb = lX + P * FwdPipe::kTile;
-    const float c1p[2] = {block_scale(pp.wf[P][0], pp.ws[P][0]), block_scale(pp.wf[P][1], pp.ws[P][1])};
-    StepIn in1;
-    bf16x8_t a1[2];
-    // steps 0..3 with the next step's reads issued ahead of the MFMAs
-    step_reads(in1, xb, 1, pp.wc[P], tbl, pp.lane8, r, h);
-    step_mfma(acc, a0, in0);
-    step_frags(a1, in1, c1p);
-    step_reads(in0, xb, 2, pp.wc[P], tbl, pp.lane8, r, h);
-    step_mfma(acc, a1, in1);
-    step_frags(a0, in0, c1p);
-    step_reads(in1, xb, 3, pp.wc[P], tbl, pp.lane8, r, h);
+    XFr xb_;
+    AFr ab;
+    QPr qb;
+    pp.load_x(kt + 2, P);                     // staging set P held tile kt, stored during tile kt-1
     __builtin_amdgcn_sched_barrier(0);
-    pp.load_w(kt + 2, P);                     // last read of tile kt's codes is above
-    step_mfma(acc, a0, in0);
-    step_frags(a1, in1, c1p);
-    step_mfma(acc, a1, in1);
-    // tile kt+1: X to the other buffer, then its step 0
-    pp.store_x(Q, lX + Q * FwdPipe::kTile);
-    __syncthreads();
+    // step 0
+    read_x(xb_, xb, 1, r, h);
+    read_q(qb, pp.wc[P], 2, pp.lane8);
+    make_a(ab, qa, c1p);
+    mfma16(acc, aa, xa);
+    interleave<16, 16, 16>();
+    __builtin_amdgcn_sched_barrier(0);
+    // step 1
+    read_x(xa, xb, 2, r, h);
+    read_q(qa, pp.wc[P], 3, pp.lane8);
+    make_a(aa, qb, c1p);
+    mfma16(acc, ab, xb_);
+    interleave<16, 16, 16>();
+    __builtin_amdgcn_sched_barrier(0);
+    // step 2: the pairs of the next tile's step 0 come from code set Q
+    read_x(xb_, xb, 3, r, h);
+    read_q(qb, pp.wc[Q], 0, pp.lane8);
+    make_a(ab, qa, c1p);
+    mfma16(acc, aa, xa);
+    interleave<16, 16, 16>();
+    __builtin_amdgcn_sched_barrier(0);
+    pp.load_w(kt + 2, P);                     // code set P is no longer read
     const float n1p[2] = {block_scale(pp.wf[Q][0], pp.ws[Q][0]), block_scale(pp.wf[Q][1], pp.ws[Q][1])};
-    step_reads(in0, lX + Q * FwdPipe::kTile, 0, pp.wc[Q], tbl, pp.lane8, r, h);
-    step_frags(a0, in0, n1p);
+    // step 3: the first half of its MFMAs cover the X store and the barrier
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[0], xb_[j], acc[0][j], 0, 0, 0);
+        acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[1], xb_[j], acc[1][j], 0, 0, 0);
+    }
+    pp.store_x(Q, lX + Q * FwdPipe::kTile);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    read_x(xa, lX + Q * FwdPipe::kTile, 0, r, h);
+    read_q(qa, pp.wc[Q], 1, pp.lane8);
+    make_a(aa, qb, n1p);
+#pragma unroll
+    for (int j = 4; j < 8; ++j) {
+        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[0], xb_[j], acc[0][j], 0, 0, 0);
+        acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[1], xb_[j], acc[1][j], 0, 0, 0);
+    }
+    interleave<8, 8, 8>();
+    __builtin_amdgcn_sched_barrier(0);
+    c1p[0] = n1p[0];
+    c1p[1] = n1p[1];
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
@@ -588,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
     pp.rs = make_rsrc(p.sup, ceil_div(p.N * p.K / 64, 256) * 4);
     pp.rx = make_rsrc(p.x, p.T * p.K * 2);
     pp.KT = (int)(p.K / 64);
-    pp.lane8 = (uint32_t)(lane & 31) * 8u;
+    pp.lane8 = lds_addr(tbl) + (uint32_t)(lane & 31) * 8u;   // table is 64 KB aligned
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int64_t n = n0 + 64 * w + 32 * i + r;
@@ -619,20 +562,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
     pp.load_x(1, 1);
     pp.store_x(0, lX);
     __syncthreads();                          // pair table and X tile 0 visible
-    StepIn in0;
-    bf16x8_t a0[2];
+    XFr xa;
+    AFr aa;
+    QPr qa;
+    float c1p[2] = {block_scale(pp.wf[0][0], pp.ws[0][0]), block_scale(pp.wf[0][1], pp.ws[0][1])};
     {
-        const float c1p[2] = {block_scale(pp.wf[0][0], pp.ws[0][0]), block_scale(pp.wf[0][1], pp.ws[0][1])};
-        step_reads(in0, lX, 0, pp.wc[0], tbl, pp.lane8, r, h);
-        step_frags(a0, in0, c1p);
+        QPr q0;
+        read_q(q0, pp.wc[0], 0, pp.lane8);
+        make_a(aa, q0, c1p);
+        read_q(qa, pp.wc[0], 1, pp.lane8);
+        read_x(xa, lX, 0, r, h);
     }
     const int KT = pp.KT;
     int kt = 0;
     for (; kt + 1 < KT; kt += 2) {
-        fwd_tile<0>(pp, kt, acc, lX, tbl, r, h, in0, a0);
-        fwd_tile<1>(pp, kt + 1, acc, lX, tbl, r, h, in0, a0);
+        fwd_tile<0>(pp, kt, acc, lX, r, h, xa, aa, qa, c1p);
+        fwd_tile<1>(pp, kt + 1, acc, lX, r, h, xa, aa, qa, c1p);
     }
-    if (kt < KT) fwd_tile<0>(pp, kt, acc, lX, tbl, r, h, in0, a0);
+    if (kt < KT) fwd_tile<0>(pp, kt, acc, lX, r, h, xa, aa, qa, c1p);
 
     if (p.r > 0) {
         // reduction over [hi | lo] of s X A (tokens) against B^T stacked twice (rows n)
@@ -764,7 +711,7 @@ struct DxPipe {
     }
     // rows 4q .. 4q+3 of the thread's 8 x 8 patch, written transposed: for each
     // k, the dwords of row pairs (4q, 4q+1) and (4q+2, 4q+3) as one 8-byte store
-    QL_DEV void dequant_half(int par, int q, const lds8_t* tbl, lds8_t* l) {
+    QL_DEV void dequant_half(int par, int q, lds8_t* l) {
         float v[4][8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -772,8 +719,8 @@ struct DxPipe {
             const float c1p = __uint_as_float(sc[par][i >> 2][i & 3]);
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const uint32_t off = (__builtin_amdgcn_ubfe(cw[par][i], 8 * b, 8) << 7) | lane8;
-                const f32x2_t qq = *reinterpret_cast<const lds_f32x2_t*>(tbl + off);
+                const uint32_t addr = (__builtin_amdgcn_ubfe(cw[par][i], 8 * b, 8) << 7) | lane8;
+                const f32x2_t qq = *lds_at<f32x2_t>(addr);
                 v[e][2 * b] = __fmul_rn(qq[0], c1p);
                 v[e][2 * b + 1] = __fmul_rn(qq[1], c1p);
             }
@@ -820,10 +767,10 @@ QL_DEV void dx_tile(DxPipe& pp, int kt, f32x16_t (&acc)[4][4], lds8_t* lW, lds8_
     DxFrags f1;
     dx_reads(f1, cw, cd, 1, wa, wb, r, h);
     dx_mfma(acc, f0);
-    pp.dequant_half(Q, 0, tbl, nw);
+    pp.dequant_half(Q, 0, nw);
     dx_reads(f0, cw, cd, 2, wa, wb, r, h);
     dx_mfma(acc, f1);
-    pp.dequant_half(Q, 1, tbl, nw);
+    pp.dequant_half(Q, 1, nw);
     dx_reads(f1, cw, cd, 3, wa, wb, r, h);
     dx_mfma(acc, f0);
     dx_mfma(acc, f1);
@@ -855,7 +802,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
     pp.rc = make_rsrc(p.codes, p.N * p.K / 2);
     pp.rs = make_rsrc(p.sclt, (p.K / 64) * p.N * 4);
     pp.rd = make_rsrc(p.dy, p.T * p.N * 2);
-    pp.lane8 = (uint32_t)(lane & 15) * 8u;
+    pp.lane8 = lds_addr(tbl) + (uint32_t)(lane & 15) * 8u;   // table is 32 KB aligned
     {
         const int64_t k = k0 + (threadIdx.x & 31) * 8;
         const int64_t n = (threadIdx.x >> 5) * 8;
@@ -883,8 +830,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
     pp.load_w(1, 1);
     pp.load_dy(0);
     __syncthreads();                          // pair table visible
-    pp.dequant_half(0, 0, tbl, lW);
-    pp.dequant_half(0, 1, tbl, lW);
+    pp.dequant_half(0, 0, lW);
+    pp.dequant_half(0, 1, lW);
     pp.store_dy(lD);
     __syncthreads();
     DxFrags f0;
