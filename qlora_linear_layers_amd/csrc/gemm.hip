@@ -434,16 +434,18 @@ QL_DEV void mfma16(f32x16_t (&acc)[2][8], const AFr& a, const XFr& x) {
     }
 }
 
-// Scheduling hint for one step: each MFMA followed by one LDS read and two
-// VALU instructions, so the reads and the dequantization of later steps issue
-// in the shadow of the 32-cycle MFMAs instead of in front of them.
-template <int kMfma, int kReads, int kValu>
+// Scheduling hint for one step: each MFMA followed by one LDS read, two VALU
+// instructions and (for the first kWrites) one LDS write, so the reads and
+// the dequantization of later steps issue in the shadow of the 32-cycle MFMAs
+// instead of in front of them.
+template <int kMfma, int kReads, int kValu, int kWrites = 0, int kValuPer = 2>
 QL_DEV void interleave() {
 #pragma unroll
     for (int j = 0; j < kMfma; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
         if (j < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-        if (j < kValu) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);    // VALU
+        if (j < kValu) __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);   // VALU
+        if (j < kWrites) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
     }
 }
 
@@ -658,16 +660,25 @@ __global__ __launch_bounds__(256) void k_scales_t(const uint8_t* __restrict__ fp
 // wb*128..; four A and four B fragments per MFMA step, both from LDS).
 //
 // The W tile is written to LDS already transposed ([k][n]): each thread owns
-// an 8 (n) x 8 (k) patch, i.e. one code dword of each of 8 rows; the two
-// elements of one code byte are neighbours in k, and the bf16 pack pairs
-// neighbours in n.  The codebook lookups use a 16-copy byte-pair table
-// (entry e of copy c at e*128 + c*8, lane l uses copy l & 15).
+// an 8 (n) x 8 (k) patch, i.e. one code dword of each of 8 rows.  The patch
+// is done in quarters of two k columns (code byte j of every row); for each
+// k the eight n values form one whole 16-byte chunk of the [k][n] tile.  W
+// tile rows are stored permuted (bit 0 of the row flipped when bit 6 is set),
+// which makes those 16-byte writes bank-conflict-free: the 16 lanes of a
+// write phase hold k groups 0..15, so their rows cover both parities and all
+// eight swizzled chunk positions.  The 32-row fragment reads only see a
+// permutation inside their 32 rows and stay conflict-free.  The codebook
+// lookups use a 16-copy byte-pair table (entry e of copy c at e*128 + c*8,
+// lane l uses copy l & 15).
 //
-// Pipeline (per reduction tile kt): global loads of tile kt+2 (dY rows and W
-// codes + scales) into the register set freed by tile kt; the sixteen MFMAs
-// of each step of tile kt run from LDS buffer kt&1 with the next step's
-// fragment reads issued ahead; interleaved with them, tile kt+1 is staged into
-// the other LDS buffer (dY copied, W dequantized and transposed); one barrier.
+// Pipeline (per reduction tile kt, LDS buffers and register sets by parity):
+// step j of tile kt runs its sixteen MFMAs while it reads the fragments of
+// step j+1, looks up the codebook pairs of quarter j+1 of tile kt+1's W patch
+// and dequantizes quarter j into the idle W buffer.  Step 3 is split around
+// the barrier: half its MFMAs, the last quarter and tile kt+1's dY rows
+// written, barrier, then the fragments of tile kt+1's step 0 and the lookups
+// of quarter 0 of tile kt+2 are read during the other half.  W codes and
+// block scales are loaded about a tile and a half ahead, dY one tile ahead.
 constexpr uint32_t kNarrowTableBytes = 256 * 128;
 
 QL_DEV void build_pair_table16(lds8_t* tbl, const Codebook& cb) {
@@ -678,6 +689,11 @@ QL_DEV void build_pair_table16(lds8_t* tbl, const Codebook& cb) {
     }
 }
 
+// LDS offset inside a W^T tile: rows permuted as described above.
+QL_DEV uint32_t lds_off_w(int row, int chunk) { return lds_off(row ^ ((row >> 6) & 1), chunk); }
+
+typedef f32x2_t DqPairs[8];   // codebook pairs of one quarter patch: code byte j of rows 0..7
+
 struct DxPipe {
     static constexpr uint32_t kTile = 256 * 128;
     rsrc_t rc, rs, rd;
@@ -685,9 +701,9 @@ struct DxPipe {
     uint32_t lane8;
     int64_t K, N;
     int NT;
-    u32x4_t dr[8];                 // dY rows of the next tile (one tile ahead)
-    uint32_t cw[2][8];             // W codes, two tiles ahead
-    u32x4_t sc[2][2];              // eight block scales (rows n..n+7), two tiles ahead
+    u32x4_t dr[8];                 // dY rows of the next tile to store
+    uint32_t cw[2][8];             // W codes of the tiles being staged, by parity
+    u32x4_t sc[2][2];              // their eight block scales (rows n..n+7)
 
     QL_DEV void load_w(int kt, int par) {
         kt = kt < NT ? kt : NT - 1;
@@ -709,27 +725,31 @@ struct DxPipe {
             *reinterpret_cast<lds_u32x4_t*>(l + lds_off(ch >> 3, ch & 7)) = dr[c];
         }
     }
-    // rows 4q .. 4q+3 of the thread's 8 x 8 patch, written transposed: for each
-    // k, the dwords of row pairs (4q, 4q+1) and (4q+2, 4q+3) as one 8-byte store
-    QL_DEV void dequant_half(int par, int q, lds8_t* l) {
-        float v[4][8];
+    // codebook pairs of code byte j of the eight code dwords of set par
+    QL_DEV void lookup(DqPairs& qv, int par, int j) const {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 4 * q + e;
-            const float c1p = __uint_as_float(sc[par][i >> 2][i & 3]);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const uint32_t addr = (__builtin_amdgcn_ubfe(cw[par][i], 8 * b, 8) << 7) | lane8;
-                const f32x2_t qq = *lds_at<f32x2_t>(addr);
-                v[e][2 * b] = __fmul_rn(qq[0], c1p);
-                v[e][2 * b + 1] = __fmul_rn(qq[1], c1p);
-            }
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t addr = (__builtin_amdgcn_ubfe(cw[par][i], 8 * j, 8) << 7) | lane8;
+            qv[i] = *lds_at<f32x2_t>(addr);
         }
+    }
+    // k columns 2j, 2j+1 of the patch: w' = RNE_bf16(fl32(q * c1')), eight n
+    // values per column packed into one 16-byte chunk
+    QL_DEV void finish(const DqPairs& qv, int par, int j, lds8_t* l) const {
         const int kc = threadIdx.x & 31, ng = threadIdx.x >> 5;
+        float v[8][2];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            const u32x2_t o = {pack_bf16x2(v[0][kk], v[1][kk]), pack_bf16x2(v[2][kk], v[3][kk])};
-            *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(l + lds_off(kc * 8 + kk, ng) + 8 * q) = o;
+        for (int i = 0; i < 8; ++i) {
+            const float c1p = __uint_as_float(sc[par][i >> 2][i & 3]);
+            v[i][0] = __fmul_rn(qv[i][0], c1p);
+            v[i][1] = __fmul_rn(qv[i][1], c1p);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            u32x4_t o;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) o[p] = pack_bf16x2(v[2 * p][c], v[2 * p + 1][c]);
+            *reinterpret_cast<lds_u32x4_t*>(l + lds_off_w(kc * 8 + 2 * j + c, ng)) = o;
         }
     }
 };
@@ -738,9 +758,13 @@ struct DxFrags {
     bf16x8_t a[4], b[4];
 };
 
+template <bool kMapW>
 QL_DEV void dx_reads(DxFrags& f, const lds8_t* lw, const lds8_t* ld, int s, int wa, int wb, int r, int h) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = lds_frag(lw, wa * 128 + i * 32 + r, 2 * s + h);
+    for (int i = 0; i < 4; ++i) {
+        const int row = wa * 128 + i * 32 + r;
+        f.a[i] = *reinterpret_cast<const lds_bf16x8_t*>(lw + (kMapW ? lds_off_w(row, 2 * s + h) : lds_off(row, 2 * s + h)));
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) f.b[j] = lds_frag(ld, wb * 128 + j * 32 + r, 2 * s + h);
 }
@@ -753,37 +777,68 @@ QL_DEV void dx_mfma(f32x16_t (&acc)[4][4], const DxFrags& f) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
+// MFMAs of output rows i in [i0, i1) only (used to split a step around the barrier)
+template <int i0, int i1>
+QL_DEV void dx_mfma_rows(f32x16_t (&acc)[4][4], const DxFrags& f) {
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
 template <int P>
-QL_DEV void dx_tile(DxPipe& pp, int kt, f32x16_t (&acc)[4][4], lds8_t* lW, lds8_t* lD, const lds8_t* tbl,
-                    int wa, int wb, int r, int h, DxFrags& f0) {
+QL_DEV void dx_tile(DxPipe& pp, int kt, f32x16_t (&acc)[4][4], lds8_t* lW, lds8_t* lD, int wa, int wb, int r,
+                    int h, DxFrags& f0, DqPairs& qa) {
     constexpr int Q = P ^ 1;
-    pp.load_w(kt + 2, P);                     // set P held tile kt, staged during the previous tile
-    pp.load_dy(kt + 1);
-    __builtin_amdgcn_sched_barrier(0);
     const lds8_t* cw = lW + P * DxPipe::kTile;
     const lds8_t* cd = lD + P * DxPipe::kTile;
     lds8_t* nw = lW + Q * DxPipe::kTile;
     lds8_t* nd = lD + Q * DxPipe::kTile;
     DxFrags f1;
-    dx_reads(f1, cw, cd, 1, wa, wb, r, h);
+    DqPairs qb;
+    // step 0
+    dx_reads<true>(f1, cw, cd, 1, wa, wb, r, h);
+    pp.lookup(qb, Q, 1);
+    pp.finish(qa, Q, 0, nw);
     dx_mfma(acc, f0);
-    pp.dequant_half(Q, 0, nw);
-    dx_reads(f0, cw, cd, 2, wa, wb, r, h);
+    interleave<16, 16, 16>();
+    __builtin_amdgcn_sched_barrier(0);
+    // step 1
+    dx_reads<true>(f0, cw, cd, 2, wa, wb, r, h);
+    pp.lookup(qa, Q, 2);
+    pp.finish(qb, Q, 1, nw);
     dx_mfma(acc, f1);
-    pp.dequant_half(Q, 1, nw);
-    dx_reads(f1, cw, cd, 3, wa, wb, r, h);
+    interleave<16, 16, 16>();
+    __builtin_amdgcn_sched_barrier(0);
+    // step 2
+    dx_reads<true>(f1, cw, cd, 3, wa, wb, r, h);
+    pp.lookup(qb, Q, 3);
+    pp.finish(qa, Q, 2, nw);
     dx_mfma(acc, f0);
-    dx_mfma(acc, f1);
+    interleave<16, 16, 16>();
+    __builtin_amdgcn_sched_barrier(0);
+    // step 3
+    dx_mfma_rows<0, 2>(acc, f1);
+    pp.finish(qb, Q, 3, nw);
     pp.store_dy(nd);
+    interleave<8, 0, 8, 8, 4>();
+    __builtin_amdgcn_sched_barrier(0);
+    pp.load_dy(kt + 2);                       // dY registers are free again
     __syncthreads();
-    dx_reads(f0, nw, nd, 0, wa, wb, r, h);
+    dx_reads<true>(f0, nw, nd, 0, wa, wb, r, h);
+    pp.lookup(qa, P, 0);                      // tile kt+2's codes (set P, loaded during tile kt-1)
+    dx_mfma_rows<2, 4>(acc, f1);
+    interleave<8, 16, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    pp.load_w(kt + 3, Q);                     // set Q (tile kt+1) is no longer read
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     lds8_t* smem = (lds8_t*)(smem_raw);
     constexpr uint32_t kTile = DxPipe::kTile;
-    lds8_t* const lW = smem;                  // 2 tiles [256 k][64 n]
+    lds8_t* const lW = smem;                  // 2 tiles [256 k][64 n] (rows permuted)
     lds8_t* const lD = smem + 2 * kTile;      // 2 tiles [256 t][64 n]
     lds8_t* const tbl = smem + 4 * kTile;     // 16-copy pair table
     build_pair_table16(tbl, cb);
@@ -825,24 +880,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // prologue: W tiles 0 and 1 in flight; tile 0 staged and its step-0 fragments read
+    // prologue: tile 0 staged in LDS buffer 0; tile 1's codes and dY rows and
+    // tile 2's codes in registers; tile 0's step-0 fragments and the pairs of
+    // quarter 0 of tile 1 read
     pp.load_w(0, 0);
     pp.load_w(1, 1);
     pp.load_dy(0);
     __syncthreads();                          // pair table visible
-    pp.dequant_half(0, 0, lW);
-    pp.dequant_half(0, 1, lW);
+    DqPairs qa;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        pp.lookup(qa, 0, j);
+        pp.finish(qa, 0, j, lW);
+    }
     pp.store_dy(lD);
+    pp.load_dy(1);
+    pp.load_w(2, 0);
+    pp.lookup(qa, 1, 0);
     __syncthreads();
     DxFrags f0;
-    dx_reads(f0, lW, lD, 0, wa, wb, r, h);
+    dx_reads<true>(f0, lW, lD, 0, wa, wb, r, h);
     const int NT = pp.NT;
     int kt = 0;
     for (; kt + 1 < NT; kt += 2) {
-        dx_tile<0>(pp, kt, acc, lW, lD, tbl, wa, wb, r, h, f0);
-        dx_tile<1>(pp, kt + 1, acc, lW, lD, tbl, wa, wb, r, h, f0);
+        dx_tile<0>(pp, kt, acc, lW, lD, wa, wb, r, h, f0, qa);
+        dx_tile<1>(pp, kt + 1, acc, lW, lD, wa, wb, r, h, f0, qa);
     }
-    if (kt < NT) dx_tile<0>(pp, kt, acc, lW, lD, tbl, wa, wb, r, h, f0);
+    if (kt < NT) dx_tile<0>(pp, kt, acc, lW, lD, wa, wb, r, h, f0, qa);
 
     if (p.r > 0) {
         // LoRA term (s dY B^T) A^T: reduction over [hi | lo] of s dY B^T against A stacked twice
@@ -861,7 +925,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 DxFrags f;
-                dx_reads(f, lW, lD, s, wa, wb, r, h);
+                dx_reads<false>(f, lW, lD, s, wa, wb, r, h);
                 dx_mfma(acc, f);
             }
         }
