@@ -8,10 +8,11 @@
 #include "plan.hpp"
 
 namespace ql {
-hipError_t launch_lora_down_x(const uint16_t* x, const uint16_t* lora_a, float scaling, const LoraPlan& pl,
-                              uint8_t* ws, hipStream_t s);
+hipError_t launch_transpose_a(const uint16_t* lora_a, const LoraPlan& pl, uint8_t* ws, hipStream_t s);
+hipError_t launch_lora_down_x(const uint16_t* x, float scaling, const LoraPlan& pl, uint8_t* ws, bool transposed,
+                              hipStream_t s);
 hipError_t launch_lora_down_dy(const uint16_t* dy, const uint16_t* lora_b, float scaling, const LoraPlan& pl,
-                               uint8_t* ws, hipStream_t s);
+                               uint8_t* ws, bool transposed, hipStream_t s);
 hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* fp8, const float* sup,
                       const uint16_t* lora_b, const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s);
 hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* fp8, const float* sup,
@@ -110,8 +111,10 @@ int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N, const u
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (T <= ql::kGemvMaxT)      // decode sizes: VALU GEMV, no MFMA
         return dev(ql::launch_gemv(x, codes, absmax_fp8, superscale, lora_a, lora_b, scaling, pl, ws, y, s));
-    if (r > 0)
-        if (int st = dev(ql::launch_lora_down_x(x, lora_a, scaling, pl, ws, s))) return st;
+    if (r > 0) {
+        if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
+        if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, false, s))) return st;
+    }
     return dev(ql::launch_fwd(x, codes, absmax_fp8, superscale, lora_b, pl, ws, y, s));
 }
 
@@ -136,11 +139,14 @@ int qlora_linear_bwd_input(const uint16_t* dy, int64_t T, int64_t K, int64_t N, 
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    if (r > 0)
-        if (int st = dev(ql::launch_lora_down_dy(dy, lora_b, scaling, pl, ws, s))) return st;
+    if (r > 0) {
+        if (grads)
+            if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
+        if (int st = dev(ql::launch_lora_down_dy(dy, lora_b, scaling, pl, ws, grads, s))) return st;
+    }
     if (int st = dev(ql::launch_dx(dy, codes, absmax_fp8, superscale, lora_a, pl, ws, dx, s))) return st;
     if (grads) {
-        if (int st = dev(ql::launch_lora_down_x(x, lora_a, scaling, pl, ws, s))) return st;
+        if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, true, s))) return st;
         if (int st = dev(ql::launch_lora_grads(x, dy, pl, ws, d_lora_a, d_lora_b, s))) return st;
     }
     return QLORA_OK;

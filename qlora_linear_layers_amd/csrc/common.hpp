@@ -42,6 +42,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Round-to-nearest-even of two fp32 values into one packed dword: `a` in the
 // low half (lower address), `b` in the high half (v_cvt_pk_bf16_f32).
@@ -77,6 +79,55 @@ QL_DEV uint32_t e4m3_encode_tie_low(float y) {
 // Block scale c1' = fl32(e4m3(f) * s2) (first step of the reverse-order
 // dequantization).
 QL_DEV float block_scale(uint32_t f8, float s2) { return __fmul_rn(e4m3_decode(f8), s2); }
+
+// ------------------------------------------------------------------ LDS and buffer access
+
+// LDS pointers carry address space 3 explicitly so that every tile access is a
+// ds_read / ds_write (a generic pointer would fall back to flat instructions).
+typedef __attribute__((address_space(3))) uint8_t lds8_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+typedef __attribute__((address_space(3))) float lds_f32_t;
+typedef __attribute__((address_space(3))) f32x2_t lds_f32x2_t;
+
+// LDS byte address of a pointer, and a pointer from an LDS byte address.  The
+// codebook tables are aligned to their own size (64 KB / 32 KB) inside LDS, so
+// a lookup address is the table's address OR-ed with the entry offset, built
+// by one permute or shift-or with no add (dynamic LDS starts at address 0 in
+// these kernels, which declare no static LDS).
+QL_DEV uint32_t lds_addr(const lds8_t* p) { return (uint32_t)(uintptr_t)p; }
+template <class T>
+QL_DEV const __attribute__((address_space(3))) T* lds_at(uint32_t a) {
+    return reinterpret_cast<const __attribute__((address_space(3))) T*>((uintptr_t)a);
+}
+
+// LDS tile of [rows][64] bf16: 128 bytes per row in 16-byte chunks, the chunk
+// index XOR-swizzled with bits of the row so that fragment reads (16 or 32
+// consecutive rows at a fixed chunk) and row-wise writes spread over all banks.
+QL_DEV uint32_t lds_off(int row, int chunk) {
+    return (uint32_t)row * 128u + ((uint32_t)(chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
+// Raw buffer loads: a per-thread 32-bit byte offset (constant over the k loop)
+// plus a scalar per-tile offset, no 64-bit address arithmetic per load.  A
+// thread whose row lies outside the operand gets an offset past the buffer's
+// end, for which the hardware returns zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;
+
+QL_DEV rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+QL_DEV u32x4_t bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+QL_DEV uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+QL_DEV uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
 
 // ------------------------------------------------------------------ launchers
 

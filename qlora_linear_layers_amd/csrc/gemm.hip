@@ -7,79 +7,26 @@
 // with W' the double-dequantized bf16 weight ("QLoRA 原理精讲" section 2.2:
 // super-scale, then block constant, then weight) that is never written to HBM.
 //
-// Structure.  Every product is a sum over 64-wide reduction tiles of
+// Structure.  Both products are sums over 64-wide reduction tiles of
 // v_mfma_f32_32x32x16_bf16 steps, with both operands fed as 8 consecutive
 // reduction elements per lane:
-//   k_fwd   - W rows dequantized straight into A-operand registers, X through
-//             swizzled LDS (reduction over k is contiguous in both);
-//   k_dx    - W dequantized and transposed into LDS ([k][n] tiles), dY through
-//             LDS (reduction over n);
-//   k_small - the rank-r LoRA products, with operands staged by PlainRows (bf16
-//             rows contiguous along the reduction) or TransRows (bf16 stored
-//             with the reduction as the row index: row pairs packed into dwords).
+//   k_fwd - W rows dequantized straight into A-operand registers, X through
+//           swizzled LDS (reduction over k is contiguous in both);
+//   k_dx  - W dequantized and transposed into LDS ([k][n] tiles), dY through
+//           LDS (reduction over n).
 // NF4 codes are decoded with byte-pair tables in LDS: one 8-byte read returns
-// the two fp32 codewords of a packed byte.  Outputs leave as bf16 rows, or as
-// fp32 split-reduction partials that k_finalize sums in a fixed order, so
-// every result is deterministic.
+// the two fp32 codewords of a packed byte.  The LoRA up-projection (rank r) is
+// a short extra reduction at the end of each tile, from operands staged by
+// PlainRows (bf16 rows contiguous along the reduction) or TransRows (bf16
+// stored with the reduction as the row index).  Outputs leave as bf16 rows.
 #include "common.hpp"
 #include "plan.hpp"
 
 namespace ql {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-
-// LDS pointers carry address space 3 explicitly so that every tile access is a
-// ds_read / ds_write (a generic pointer would fall back to flat instructions).
-typedef __attribute__((address_space(3))) uint8_t lds8_t;
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
-typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
-typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
-typedef __attribute__((address_space(3))) float lds_f32_t;
-typedef __attribute__((address_space(3))) f32x2_t lds_f32x2_t;
-
-// LDS byte address of a pointer, and a pointer from an LDS byte address.  The
-// codebook tables are aligned to their own size (64 KB / 32 KB) inside LDS, so
-// a lookup address is the table's address OR-ed with the entry offset, built
-// by one permute or shift-or with no add (dynamic LDS starts at address 0 in
-// these kernels, which declare no static LDS).
-QL_DEV uint32_t lds_addr(const lds8_t* p) { return (uint32_t)(uintptr_t)p; }
-template <class T>
-QL_DEV const __attribute__((address_space(3))) T* lds_at(uint32_t a) {
-    return reinterpret_cast<const __attribute__((address_space(3))) T*>((uintptr_t)a);
-}
-
-// LDS tile of [rows][64] bf16: 128 bytes per row in 16-byte chunks, the chunk
-// index XOR-swizzled with bits of the row so that the 32-row fragment reads
-// (fixed chunk) and every producer's writes spread over all banks.
-QL_DEV uint32_t lds_off(int row, int chunk) {
-    return (uint32_t)row * 128u + ((uint32_t)(chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
-
-// ------------------------------------------------------------------ loads
-
-// Raw buffer loads: a per-thread 32-bit byte offset (constant over the k loop)
-// plus a scalar per-tile offset, no 64-bit address arithmetic per load.  A
-// thread whose row lies outside the operand gets an offset past the buffer's
-// end, for which the hardware returns zeros.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr uint32_t kOOB = 0x80000000u;
-
-QL_DEV rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-QL_DEV u32x4_t bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-QL_DEV uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-}
-QL_DEV uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
-    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
-}
 
 // ------------------------------------------------------------------ LDS tile producers
 
@@ -190,111 +137,15 @@ struct TransRows {
 
 // ------------------------------------------------------------------ MFMA core
 
-template <int TA, int TB>
-struct Acc {
-    static constexpr int MA = TA / 64, MB = TB / 64;   // 32x32 MFMA tiles per wave and dimension
-    f32x16_t v[MA][MB];
-    QL_DEV void zero() {
-#pragma unroll
-        for (int i = 0; i < MA; ++i)
-#pragma unroll
-            for (int j = 0; j < MB; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) v[i][j][e] = 0.0f;
-    }
-};
-
 QL_DEV bf16x8_t lds_frag(const lds8_t* base, int row, int chunk) {
     return *reinterpret_cast<const lds_bf16x8_t*>(base + lds_off(row, chunk));
 }
 
-// Four 16-deep MFMA steps over one 64-wide LDS tile pair, waves arranged 2 x 2
-// (wave (wa, wb) owns rows wa*TA/2.. of A and wb*TB/2.. of B).
-template <int TA, int TB>
-QL_DEV void mma_tile(const lds8_t* lA, const lds8_t* lB, Acc<TA, TB>& acc) {
-    constexpr int MA = TA / 64, MB = TB / 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wa = wave >> 1, wb = wave & 1;
-    const int r = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        bf16x8_t a[MA], b[MB];
-#pragma unroll
-        for (int i = 0; i < MA; ++i) a[i] = lds_frag(lA, wa * (TA / 2) + i * 32 + r, 2 * s + h);
-#pragma unroll
-        for (int j = 0; j < MB; ++j) b[j] = lds_frag(lB, wb * (TB / 2) + j * 32 + r, 2 * s + h);
-#pragma unroll
-        for (int i = 0; i < MA; ++i)
-#pragma unroll
-            for (int j = 0; j < MB; ++j)
-                acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.v[i][j], 0, 0, 0);
-    }
-}
-
-// Double-buffered main loop over reduction tiles [kt0, kt1).  Global loads for
-// tile kt+1 are issued before the MFMAs of tile kt and written to the other
-// LDS buffer after them; one barrier per tile.  The body has no branches (the
-// last iteration reloads its own tile into the idle buffer), so the compiler
-// can interleave the producers' VALU work with the MFMAs.
-template <int TA, int TB, class PA, class PB>
-QL_DEV void mainloop(PA& pa, PB& pb, int kt0, int kt1, Acc<TA, TB>& acc, lds8_t* smem, const lds8_t* tbl) {
-    if (kt0 >= kt1) return;
-    lds8_t* const lA0 = smem;
-    lds8_t* const lB0 = smem + 2 * TA * 128;
-    pa.load(kt0);
-    pb.load(kt0);
-    pa.store(lA0, tbl);
-    pb.store(lB0, tbl);
-    __syncthreads();
-    for (int kt = kt0; kt < kt1; ++kt) {
-        const int cur = (kt - kt0) & 1;
-        const int nxt = kt + 1 < kt1 ? kt + 1 : kt;
-        pa.load(nxt);
-        pb.load(nxt);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_tile<TA, TB>(lA0 + cur * (TA * 128), lB0 + cur * (TB * 128), acc);
-        pa.store(lA0 + (cur ^ 1) * (TA * 128), tbl);
-        pb.store(lB0 + (cur ^ 1) * (TB * 128), tbl);
-        __syncthreads();
-    }
-}
-
-template <int TA, int TB>
-constexpr size_t smem_bytes() { return (size_t)2 * (TA + TB) * 128; }
-
-// Output C[a][b] to out[b][a] (a contiguous) for the 2 x 2 wave layout: each
-// lane holds four consecutive a for one b per MFMA row group.  bf16 (8-byte
-// stores) or fp32 (16-byte).
-template <bool kBF16>
-QL_DEV void store4(const f32x16_t& v, int g, void* out, int64_t ldo, int64_t a, int64_t b) {
-    if constexpr (kBF16) {
-        const u32x2_t o = {pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3])};
-        *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + b * ldo + a) = o;
-    } else {
-        const f32x4_t o = {v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
-        *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + b * ldo + a) = o;
-    }
-}
-
-template <int TA, int TB, bool kBF16>
-QL_DEV void store_out(const Acc<TA, TB>& acc, void* out, int64_t ldo, int64_t a0, int64_t b0, int64_t a_len,
-                      int64_t b_len) {
-    constexpr int MA = TA / 64, MB = TB / 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wa = wave >> 1, wb = wave & 1;
-    const int r = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < MA; ++i)
-#pragma unroll
-        for (int j = 0; j < MB; ++j) {
-            const int64_t b = b0 + wb * (TB / 2) + j * 32 + r;
-            if (b >= b_len) continue;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t a = a0 + wa * (TA / 2) + i * 32 + g * 8 + h * 4;
-                if (a < a_len) store4<kBF16>(acc.v[i][j], g, out, ldo, a, b);
-            }
-        }
+// C[a][b] to out[b][a] (a contiguous), bf16: four consecutive a of one b per
+// MFMA row group g of a 32 x 32 accumulator, as one 8-byte store.
+QL_DEV void store4_bf16(const f32x16_t& v, int g, uint16_t* out, int64_t ldo, int64_t a, int64_t b) {
+    const u32x2_t o = {pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3])};
+    *reinterpret_cast<u32x2_t*>(out + b * ldo + a) = o;
 }
 
 // Map a linear workgroup id to an (a-tile, b-tile) pair.  Workgroups are
@@ -622,7 +473,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int64_t n = n0 + 64 * w + 32 * i + 8 * g + 4 * h;
-                if (n < p.N) store4<true>(acc[i][j], g, p.y, p.N, n, t);
+                if (n < p.N) store4_bf16(acc[i][j], g, p.y, p.N, n, t);
             }
         }
 }
@@ -940,104 +791,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int64_t k = k0 + wa * 128 + i * 32 + g * 8 + h * 4;
-                if (k < p.K) store4<true>(acc[i][j], g, p.dx, p.K, k, t);
+                if (k < p.K) store4_bf16(acc[i][j], g, p.dx, p.K, k, t);
             }
         }
 }
 
 constexpr size_t kDxSmem = 4 * 256 * 128 + kNarrowTableBytes;
-
-// ------------------------------------------------------------------ small LoRA products
-
-// Small LoRA products with split reduction; fp32 partials out[split][b][a].
-enum SmallKind { kXA = 0, kG = 1, kDA = 2, kDB = 3 };
-
-struct SmallArgs {
-    const uint16_t* s0;   // see the instantiations below
-    const uint16_t* s1;
-    const uint16_t* s2;
-    float* part;
-    int64_t T, K, N, r, r_pad;
-    int ktiles, splits;
-};
-
-template <int KIND>
-__global__ __launch_bounds__(kThreads, 1) void k_small(SmallArgs p) {
-    extern __shared__ __align__(16) uint8_t smem_raw[];
-    lds8_t* smem = (lds8_t*)(smem_raw);
-    constexpr int TA = (KIND == kDB) ? 256 : 64;
-    constexpr int TB = (KIND == kDB) ? 64 : 256;
-    const int split = blockIdx.y;
-    const int per = (p.ktiles + p.splits - 1) / p.splits;
-    const int kt0 = split * per;
-    const int kt1 = (kt0 + per) < p.ktiles ? (kt0 + per) : p.ktiles;
-    Acc<TA, TB> acc;
-    acc.zero();
-    int64_t a_len, b_len;
-    int ga;
-    if constexpr (KIND == kXA || KIND == kG || KIND == kDA) ga = (int)(p.r_pad / 64);
-    else ga = (int)ceil_div(p.N, TA);
-    const int ta = blockIdx.x % ga, tb = blockIdx.x / ga;
-    const int64_t a0 = (int64_t)ta * TA, b0 = (int64_t)tb * TB;
-
-    if constexpr (KIND == kXA) {
-        // P[t][j] = sum_k X[t][k] A[k][j]: a = j (A transposed), b = t.  s0 = A, s1 = X.
-        TransRows<TA> pa;
-        pa.init(p.s0, p.s0, p.r, p.r, p.K, p.K, a0);
-        PlainRows<TB> pb;
-        pb.init(p.s1, nullptr, p.K, p.T, b0, p.K, 1 << 30);
-        mainloop<TA, TB>(pa, pb, kt0, kt1, acc, smem, nullptr);
-        a_len = p.r_pad; b_len = p.T;
-    } else if constexpr (KIND == kG) {
-        // G[t][j] = sum_n dY[t][n] B[j][n]: a = j, b = t.  s0 = B, s1 = dY.
-        PlainRows<TA> pa;
-        pa.init(p.s0, nullptr, p.N, p.r, a0, p.N, 1 << 30);
-        PlainRows<TB> pb;
-        pb.init(p.s1, nullptr, p.N, p.T, b0, p.N, 1 << 30);
-        mainloop<TA, TB>(pa, pb, kt0, kt1, acc, smem, nullptr);
-        a_len = p.r_pad; b_len = p.T;
-    } else if constexpr (KIND == kDA) {
-        // dA[k][j] = sum over 2T of X[t][k] (G_hi | G_lo)[t][j]: a = j, b = k.  s0 = G_hi, s1 = G_lo, s2 = X.
-        TransRows<TA> pa;
-        pa.init(p.s0, p.s1, p.r_pad, p.r_pad, p.T, p.T, a0);
-        TransRows<TB> pb;
-        pb.init(p.s2, p.s2, p.K, p.K, p.T, p.T, b0);
-        mainloop<TA, TB>(pa, pb, kt0, kt1, acc, smem, nullptr);
-        a_len = p.r_pad; b_len = p.K;
-    } else {
-        // dB[j][n] = sum over 2T of (P_hi | P_lo)[t][j] dY[t][n]: a = n, b = j.  s0 = P_hi, s1 = P_lo, s2 = dY.
-        TransRows<TA> pa;
-        pa.init(p.s2, p.s2, p.N, p.N, p.T, p.T, a0);
-        TransRows<TB> pb;
-        pb.init(p.s0, p.s1, p.r_pad, p.r_pad, p.T, p.T, b0);
-        mainloop<TA, TB>(pa, pb, kt0, kt1, acc, smem, nullptr);
-        a_len = p.N; b_len = p.r_pad;
-    }
-    float* out = p.part + (int64_t)split * a_len * b_len;
-    store_out<TA, TB, false>(acc, out, a_len, a0, b0, a_len, b_len);
-}
-
-// Sum split partials [S][rows][cols] in split order; v = scale * sum.
-// mode 0: bf16 hi = RNE(v), lo = RNE(v - hi) into two [rows][cols] arrays.
-// mode 1: bf16 RNE(v) into out [rows][out_cols] for cols < out_cols.
-__global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ part, int splits, int64_t sstride,
-                                                  int64_t rows, int64_t cols, float scale, int mode,
-                                                  uint16_t* __restrict__ hi, uint16_t* __restrict__ lo,
-                                                  int64_t out_cols) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= rows * cols) return;
-    float acc = 0.0f;
-    for (int s = 0; s < splits; ++s) acc += part[(int64_t)s * sstride + i];
-    const float v = acc * scale;
-    const uint32_t hb = pack_bf16x2(v, 0.0f) & 0xFFFFu;
-    if (mode == 0) {
-        hi[i] = (uint16_t)hb;
-        lo[i] = (uint16_t)(pack_bf16x2(v - bf16lo(hb), 0.0f) & 0xFFFFu);
-    } else {
-        const int64_t rr = i / cols, cc = i % cols;
-        if (cc < out_cols) hi[rr * out_cols + cc] = (uint16_t)hb;
-    }
-}
 
 // ------------------------------------------------------------------ launchers
 
@@ -1048,49 +807,7 @@ hipError_t set_smem(F* f, size_t bytes) {
                                (int)bytes);
 }
 
-hipError_t finalize(const float* part, int splits, int64_t sstride, int64_t rows, int64_t cols, float scale,
-                    int mode, uint16_t* hi, uint16_t* lo, int64_t out_cols, hipStream_t s) {
-    const int64_t n = rows * cols;
-    hipLaunchKernelGGL(k_finalize, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, part, splits, sstride, rows,
-                       cols, scale, mode, hi, lo, out_cols);
-    return hipGetLastError();
-}
-
-template <int KIND>
-hipError_t small(const SmallArgs& a, int64_t tiles, hipStream_t s) {
-    constexpr int TA = (KIND == kDB) ? 256 : 64;
-    constexpr int TB = (KIND == kDB) ? 64 : 256;
-    const size_t lds = smem_bytes<TA, TB>();
-    hipError_t e = set_smem(k_small<KIND>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_small<KIND>, dim3((unsigned)tiles, (unsigned)a.splits), dim3(kThreads), lds, s, a);
-    return hipGetLastError();
-}
 }  // namespace
-
-// s X A -> ws (hi/lo bf16 [T][r_pad])
-hipError_t launch_lora_down_x(const uint16_t* x, const uint16_t* lora_a, float scaling, const LoraPlan& pl,
-                              uint8_t* ws, hipStream_t s) {
-    SmallArgs a{lora_a, x, nullptr, reinterpret_cast<float*>(ws + pl.off_pxa), pl.T, pl.K, pl.N, pl.r, pl.r_pad,
-                (int)(pl.K / 64), pl.s_xa};
-    const int64_t tiles = (pl.r_pad / 64) * ceil_div(pl.T, 256);
-    hipError_t e = small<kXA>(a, tiles, s);
-    if (e != hipSuccess) return e;
-    return finalize(a.part, pl.s_xa, pl.T * pl.r_pad, pl.T, pl.r_pad, scaling, 0, reinterpret_cast<uint16_t*>(ws + pl.off_ps_hi),
-                    reinterpret_cast<uint16_t*>(ws + pl.off_ps_lo), pl.r_pad, s);
-}
-
-// s dY B^T -> ws (hi/lo bf16 [T][r_pad])
-hipError_t launch_lora_down_dy(const uint16_t* dy, const uint16_t* lora_b, float scaling, const LoraPlan& pl,
-                               uint8_t* ws, hipStream_t s) {
-    SmallArgs a{lora_b, dy, nullptr, reinterpret_cast<float*>(ws + pl.off_pg), pl.T, pl.K, pl.N, pl.r, pl.r_pad,
-                (int)(pl.N / 64), pl.s_g};
-    const int64_t tiles = (pl.r_pad / 64) * ceil_div(pl.T, 256);
-    hipError_t e = small<kG>(a, tiles, s);
-    if (e != hipSuccess) return e;
-    return finalize(a.part, pl.s_g, pl.T * pl.r_pad, pl.T, pl.r_pad, scaling, 0, reinterpret_cast<uint16_t*>(ws + pl.off_gs_hi),
-                    reinterpret_cast<uint16_t*>(ws + pl.off_gs_lo), pl.r_pad, s);
-}
 
 hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* fp8, const float* sup,
                       const uint16_t* lora_b, const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s) {
@@ -1122,32 +839,6 @@ hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* fp
     const int64_t tiles = ceil_div(pl.K, 256) * ceil_div(pl.T, 256);
     hipLaunchKernelGGL(k_dx, dim3((unsigned)tiles), dim3(kThreads), lds, s, a, host_codebook());
     return hipGetLastError();
-}
-
-// dA and dB from the hi/lo intermediates already in ws.
-hipError_t launch_lora_grads(const uint16_t* x, const uint16_t* dy, const LoraPlan& pl, uint8_t* ws,
-                             uint16_t* d_lora_a, uint16_t* d_lora_b, hipStream_t s) {
-    const int ktiles = (int)ceil_div(2 * pl.T, 64);
-    if (d_lora_a) {
-        SmallArgs a{reinterpret_cast<const uint16_t*>(ws + pl.off_gs_hi),
-                    reinterpret_cast<const uint16_t*>(ws + pl.off_gs_lo), x,
-                    reinterpret_cast<float*>(ws + pl.off_pda), pl.T, pl.K, pl.N, pl.r, pl.r_pad, ktiles, pl.s_da};
-        hipError_t e = small<kDA>(a, (pl.r_pad / 64) * ceil_div(pl.K, 256), s);
-        if (e != hipSuccess) return e;
-        e = finalize(a.part, pl.s_da, pl.K * pl.r_pad, pl.K, pl.r_pad, 1.0f, 1, d_lora_a, nullptr, pl.r, s);
-        if (e != hipSuccess) return e;
-    }
-    if (d_lora_b) {
-        SmallArgs a{reinterpret_cast<const uint16_t*>(ws + pl.off_ps_hi),
-                    reinterpret_cast<const uint16_t*>(ws + pl.off_ps_lo), dy,
-                    reinterpret_cast<float*>(ws + pl.off_pdb), pl.T, pl.K, pl.N, pl.r, pl.r_pad, ktiles, pl.s_db};
-        hipError_t e = small<kDB>(a, ceil_div(pl.N, 256) * (pl.r_pad / 64), s);
-        if (e != hipSuccess) return e;
-        // partials are [S][r_pad][N]; output rows j < r
-        e = finalize(a.part, pl.s_db, pl.r_pad * pl.N, pl.r, pl.N, 1.0f, 1, d_lora_b, nullptr, pl.N, s);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
 }
 
 }  // namespace ql

@@ -189,26 +189,30 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs p, Codebook cb) {
     for (int i = 0; i < R; ++i)
 #pragma unroll
         for (int t = 0; t < TT; ++t) acc[i][t] = 0.0f;
-    u32x4_t xv[TT][2];
-    const int xo = (wave * 1024 + lane * 16) * 2;
+    // A round narrower than the four wave chunks (KR = 2048) leaves waves 2, 3
+    // without k: they read no X (their chunk lies outside the staged rows).
+    if (wave * 1024 < KR) {
+        u32x4_t xv[TT][2];
+        const int xo = (wave * 1024 + lane * 16) * 2;
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
-        xv[t][0] = *reinterpret_cast<const g_lds_u32x4_t*>(xs + t * (KR * 2) + xo);
-        xv[t][1] = *reinterpret_cast<const g_lds_u32x4_t*>(xs + t * (KR * 2) + xo + 16);
-    }
+        for (int t = 0; t < TT; ++t) {
+            xv[t][0] = *reinterpret_cast<const g_lds_u32x4_t*>(xs + t * (KR * 2) + xo);
+            xv[t][1] = *reinterpret_cast<const g_lds_u32x4_t*>(xs + t * (KR * 2) + xo + 16);
+        }
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-        const float c1p = block_scale(f8[i], s2[i]);
+        for (int i = 0; i < R; ++i) {
+            const float c1p = block_scale(f8[i], s2[i]);
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
+            for (int d = 0; d < 2; ++d) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const uint32_t byte = __builtin_amdgcn_ubfe(cw[i][d], 8 * b, 8);
-                const f32x2_t qq = *reinterpret_cast<const g_lds_f32x2_t*>(tbl + byte * 8);
-                const uint32_t wp = pack_bf16x2(__fmul_rn(qq[0], c1p), __fmul_rn(qq[1], c1p));
-                const int e = d * 4 + b;
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t byte = __builtin_amdgcn_ubfe(cw[i][d], 8 * b, 8);
+                    const f32x2_t qq = *reinterpret_cast<const g_lds_f32x2_t*>(tbl + byte * 8);
+                    const uint32_t wp = pack_bf16x2(__fmul_rn(qq[0], c1p), __fmul_rn(qq[1], c1p));
+                    const int e = d * 4 + b;
 #pragma unroll
-                for (int t = 0; t < TT; ++t) acc[i][t] = dot2(wp, xv[t][e >> 2][e & 3], acc[i][t]);
+                    for (int t = 0; t < TT; ++t) acc[i][t] = dot2(wp, xv[t][e >> 2][e & 3], acc[i][t]);
+                }
             }
         }
     }
