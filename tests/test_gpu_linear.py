@@ -51,6 +51,23 @@ def test_multi_tile_rank64():
     _run_full("multi-tile", synth.Linear("t", 768, 1024), T=520, r=64, s=0.25)
 
 
+@pytest.mark.parametrize("r", [72, 136, 256])
+def test_ranks_above_64(r):
+    """Padded ranks (r_pad = 128, 192, 256): the wide down-projection variants,
+    several 64-rank groups in the adapter gradients, zero rank padding."""
+    _run_full(f"r={r}", synth.Linear("t", 384, 448), T=100, r=r, s=0.75)
+
+
+def test_short_token_tile():
+    """T below one 64-row tile with the reduction split 7 ways (K = 448): ragged
+    tokens in the split partials and in the transposed intermediates."""
+    _run_full("T=40", synth.Linear("t", 320, 448), T=40, r=8, s=1.5)
+
+
+def test_decode_rank_256():
+    _run_full("decode r=256", synth.Linear("t", 256, 320), T=5, r=256, s=0.25, check_bwd=False)
+
+
 def test_no_lora():
     _run_full("r=0", synth.Linear("t", 512, 256), T=64, r=0, s=0.0)
 
