@@ -359,16 +359,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad(GradArgs a) {
         for (int jt = 0; jt < 4; ++jt)
             *reinterpret_cast<f32x4_t*>(red + (((w * 8 + i) * 4 + jt) * 64 + l) * 4) = acc[i][jt];
     __syncthreads();
+    // thread: one (operand i, rank tile jt, lane) slot, the four waves' float4s
+    // added in wave order; the float4 holds rows c = 8 (4 (lane / 16) + v) + i
     float* out = a.part + (int64_t)split * a.C * a.r_pad;
-    for (int e = threadIdx.x; e < 128 * 64; e += kThreads) {
-        const int cl = e >> 6, jl = e & 63;                        // column c = cb*128 + cl, j = j0 + jl
-        const int row = cl >> 3, i = cl & 7;                       // MFMA row (0..15) and operand i
-        const int ll = (row >> 2) * 16 + (jl & 15), v = row & 3, jt = jl >> 4;
-        float sum = 0.0f;
+    const f32x4_t* red4 = reinterpret_cast<const f32x4_t*>(red);
+    for (int e = threadIdx.x; e < 8 * 4 * 64; e += kThreads) {
+        const int ll = e & 63, jt = (e >> 6) & 3, i = e >> 8;
+        f32x4_t s4 = red4[(i * 4 + jt) * 64 + ll];
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) sum += red[(((ww * 8 + i) * 4 + jt) * 64 + ll) * 4 + v];
-        const int64_t c = (int64_t)cb * 128 + cl;
-        if (c < a.C) out[c * a.r_pad + j0 + jl] = sum;
+        for (int ww = 1; ww < 4; ++ww) s4 += red4[((ww * 8 + i) * 4 + jt) * 64 + ll];
+        const int64_t j = j0 + jt * 16 + (ll & 15);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t c = (int64_t)cb * 128 + 8 * (4 * (ll >> 4) + v) + i;
+            if (c < a.C) out[c * a.r_pad + j] = s4[v];
+        }
     }
 }
 
