@@ -54,9 +54,11 @@ __global__ __launch_bounds__(256) void k_quantize_dq(const uint16_t* __restrict_
         uint32_t m = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) m = max(m, max(d[k] & 0x7FFFu, (d[k] >> 16) & 0x7FFFu));
-        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-        m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-        m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+        // max over the 8-lane cluster with DPP lane swaps (quad_perm [1,0,3,2],
+        // [2,3,0,1], then row_half_mirror pairs each quad with the other)
+        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));
+        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));
+        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, false));
         const float c1 = __uint_as_float(m << 16);
         const float r = c1 > 0.0f ? __builtin_amdgcn_rcpf(c1) : 0.0f;
         const bool exact = c1 != 0.0f && (c1 < 0x1p-64f || c1 > 0x1p64f);
