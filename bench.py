@@ -230,7 +230,8 @@ def main():
             api.qlora_linear_fwd(b["x"], b["qw"], b["a"], b["b"], s, workspace=ws, out=b["y"])
             if ev: ev[3].record(stream)
             api.qlora_linear_bwd_input(b["dy"], b["qw"], b["a"], b["b"], s, x=b["x"], lora_grads=True,
-                                       workspace=ws, dx=b["dx"], d_lora_a=b["da"], d_lora_b=b["db"])
+                                       workspace=ws, dx=b["dx"], d_lora_a=b["da"], d_lora_b=b["db"],
+                                       reuse_forward=True)
             if ev: ev[4].record(stream)
 
     for _ in range(args.warmup):
@@ -291,7 +292,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "LLaMA-7B-shaped layer, 7 linears (q/k/v/o 4096x4096, gate/up 11008x4096, "
                                "down 4096x11008), T=4096 tokens, LoRA r=64 alpha=16; step = quantize + dequantize "
-                               "+ forward + backward (dX, dA, dB) of every linear",
+                               "+ forward + backward (dX, dA, dB; s X A kept from the forward) of every linear",
                    "global_batch": 8, "seq_len": 512, "parallelism": "none (1 GPU)"},
         "components": comp,
         "roofline": roofline,

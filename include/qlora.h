@@ -104,6 +104,9 @@ int nf4_quantize_dq(const uint16_t* w, int64_t numel,
 int nf4_dequantize_dq(const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale,
                       int64_t numel, uint16_t* w_out, void* stream);
 
+/* qlora_linear_bwd_input flag: reuse the forward's s X A (see below). */
+#define QLORA_BWD_REUSE_FORWARD 1u
+
 /*
  * qlora_workspace_bytes - device workspace (bytes) that qlora_linear_fwd and
  *   qlora_linear_bwd_input need for these sizes (the larger of the two).
@@ -146,14 +149,20 @@ int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N,
  *   d_lora_a [K, r] and d_lora_b [r, N] bf16, written when non-NULL
  *   (must be NULL when r == 0).  Sizes as for qlora_linear_fwd.  The
  *   workspace is needed even when r == 0 (block scales are staged there).
- *   Errors: NULL, SHAPE, ALIGN, VALUE, WORKSPACE, DEVICE.
+ *   flags: 0, or QLORA_BWD_REUSE_FORWARD when `workspace` still holds what a
+ *   qlora_linear_fwd with the same x, lora_a, scaling and sizes left there
+ *   (nothing else used it since): s X A is then taken from it instead of
+ *   being recomputed for dB.  Ignored for T <= 16 (that forward keeps
+ *   nothing).  With a stale workspace the flag gives wrong dB.
+ *   Errors: NULL, SHAPE, ALIGN, VALUE (non-finite scaling, unknown flag),
+ *   WORKSPACE, DEVICE.
  */
 int qlora_linear_bwd_input(const uint16_t* dy, int64_t T, int64_t K, int64_t N,
                            const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale,
                            const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling,
                            uint16_t* dx, const uint16_t* x,
                            uint16_t* d_lora_a, uint16_t* d_lora_b,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           void* workspace, size_t workspace_bytes, unsigned flags, void* stream);
 
 /* qlora_status_string - static, NUL-terminated description of a status code. */
 const char* qlora_status_string(int status);

@@ -24,10 +24,13 @@ _SIGS = {
     "qlora_linear_fwd": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                         ctypes.c_float, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "qlora_linear_bwd_input": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
-                                              ctypes.c_float, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+                                              ctypes.c_float, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t,
+                                              ctypes.c_uint, _c_p]),
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 EXPORTS = tuple(_SIGS)
+
+REUSE_FORWARD = 1   # QLORA_BWD_REUSE_FORWARD
 
 _lib = None
 
@@ -156,8 +159,12 @@ def qlora_linear_fwd(x, qw, lora_a=None, lora_b=None, scaling=1.0, workspace=Non
 
 
 def qlora_linear_bwd_input(dy, qw, lora_a=None, lora_b=None, scaling=1.0, x=None, lora_grads=False,
-                           workspace=None, dx=None, d_lora_a=None, d_lora_b=None):
-    """dX (and dA, dB when lora_grads) for upstream gradient dy [T, N] bf16."""
+                           workspace=None, dx=None, d_lora_a=None, d_lora_b=None, reuse_forward=False):
+    """dX (and dA, dB when lora_grads) for upstream gradient dy [T, N] bf16.  With
+    reuse_forward, `workspace` must be the one the forward of the same x, A, scaling
+    just used (s X A is taken from it)."""
+    if reuse_forward and workspace is None:
+        raise ValueError("reuse_forward needs the forward's workspace")
     _dev(dy, torch.bfloat16, "dy")
     _dev(x, torch.bfloat16, "x")
     T, N = dy.shape
@@ -175,5 +182,6 @@ def qlora_linear_bwd_input(dy, qw, lora_a=None, lora_b=None, scaling=1.0, x=None
     _check("qlora_linear_bwd_input", lib().qlora_linear_bwd_input(
         _ptr(dy), T, K, N, _ptr(qw.codes), _ptr(qw.absmax_fp8), _ptr(qw.superscale), _ptr(lora_a), _ptr(lora_b),
         r, float(scaling), _ptr(dx), _ptr(x), _ptr(d_lora_a) if lora_grads else None,
-        _ptr(d_lora_b) if lora_grads else None, _ptr(workspace), workspace.numel(), _stream()))
+        _ptr(d_lora_b) if lora_grads else None, _ptr(workspace), workspace.numel(),
+        REUSE_FORWARD if reuse_forward else 0, _stream()))
     return (dx, d_lora_a, d_lora_b) if lora_grads else (dx, None, None)

@@ -113,7 +113,9 @@ int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N, const u
         return dev(ql::launch_gemv(x, codes, absmax_fp8, superscale, lora_a, lora_b, scaling, pl, ws, y, s));
     if (r > 0) {
         if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
-        if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, false, s))) return st;
+        // s X A in both layouts: the transposed copy lets a backward with
+        // QLORA_BWD_REUSE_FORWARD take the adapter gradients without recomputing it
+        if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, true, s))) return st;
     }
     return dev(ql::launch_fwd(x, codes, absmax_fp8, superscale, lora_b, pl, ws, y, s));
 }
@@ -122,7 +124,7 @@ int qlora_linear_bwd_input(const uint16_t* dy, int64_t T, int64_t K, int64_t N, 
                            const uint8_t* absmax_fp8, const float* superscale, const uint16_t* lora_a,
                            const uint16_t* lora_b, int64_t r, float scaling, uint16_t* dx, const uint16_t* x,
                            uint16_t* d_lora_a, uint16_t* d_lora_b, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           unsigned flags, void* stream) {
     if (!dy || !codes || !absmax_fp8 || !superscale || !dx) return QLORA_ERR_NULL;
     if (r > 0 && (!lora_a || !lora_b)) return QLORA_ERR_NULL;
     const bool grads = d_lora_a || d_lora_b;
@@ -133,20 +135,23 @@ int qlora_linear_bwd_input(const uint16_t* dy, int64_t T, int64_t K, int64_t N, 
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
     if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
+    if (flags & ~(unsigned)QLORA_BWD_REUSE_FORWARD) return QLORA_ERR_VALUE;
     const ql::LoraPlan pl(T, K, N, r);
     const size_t need = grads ? pl.bwd_grad_bytes : pl.bwd_bytes;   // > 0: the scale pre-pass needs room
+    // s X A from the forward's workspace (only the MFMA forward, T > 16, leaves it there)
+    const bool reuse = (flags & QLORA_BWD_REUSE_FORWARD) && T > ql::kGemvMaxT;
     if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    if (r > 0) {
-        if (grads)
-            if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
+    if (r > 0)
         if (int st = dev(ql::launch_lora_down_dy(dy, lora_b, scaling, pl, ws, grads, s))) return st;
-    }
     if (int st = dev(ql::launch_dx(dy, codes, absmax_fp8, superscale, lora_a, pl, ws, dx, s))) return st;
     if (grads) {
-        if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, true, s))) return st;
+        if (!reuse) {
+            if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
+            if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, true, s))) return st;
+        }
         if (int st = dev(ql::launch_lora_grads(x, dy, pl, ws, d_lora_a, d_lora_b, s))) return st;
     }
     return QLORA_OK;

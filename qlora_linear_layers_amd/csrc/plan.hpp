@@ -77,21 +77,24 @@ struct LoraPlan {
         }
         const size_t tr2 = (size_t)T * r_pad * 2, rt2 = (size_t)r_pad * ld_t * 2;
         size_t o = 0;
+        // forward: A^T, s X A (both layouts, kept for the backward), split partials
         off_at = o;     o = align256(o + (size_t)r_pad * ld_at * 2);
         off_ps_hi = o;  o = align256(o + tr2);
         off_ps_lo = o;  o = align256(o + tr2);
+        off_pst_hi = o; o = align256(o + rt2);
+        off_pst_lo = o; o = align256(o + rt2);
         off_dpart = o;
         {
             const int sd = s_down_x > s_down_dy ? s_down_x : s_down_dy;
             o = align256(o + (sd > 1 ? (size_t)sd * T * r_pad * 4 : 0));
         }
         fwd_bytes = o;
+        // backward (dX): s dY B^T, block scales
         off_gs_hi = o;  o = align256(o + tr2);
         off_gs_lo = o;  o = align256(o + tr2);
         off_scl = o;    o = align256(o + scl);
         bwd_bytes = o;
-        off_pst_hi = o; o = align256(o + rt2);
-        off_pst_lo = o; o = align256(o + rt2);
+        // adapter gradients
         off_gst_hi = o; o = align256(o + rt2);
         off_gst_lo = o; o = align256(o + rt2);
         off_pda = o;    o = align256(o + (size_t)s_da * K * r_pad * 4);

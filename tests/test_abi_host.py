@@ -94,11 +94,11 @@ def test_fwd_validation(L):
 
 def _bwd(L, **kw):
     a = dict(dy=FAKE, T=16, K=256, N=256, codes=FAKE, f8=FAKE, sup=FAKE, la=FAKE, lb=FAKE, r=16, s=1.0,
-             dx=FAKE, x=FAKE, da=FAKE, db=FAKE, ws=FAKE, wsb=1 << 40, st=None)
+             dx=FAKE, x=FAKE, da=FAKE, db=FAKE, ws=FAKE, wsb=1 << 40, flags=0, st=None)
     a.update(kw)
     return L.qlora_linear_bwd_input(a["dy"], a["T"], a["K"], a["N"], a["codes"], a["f8"], a["sup"], a["la"],
                                     a["lb"], a["r"], a["s"], a["dx"], a["x"], a["da"], a["db"], a["ws"], a["wsb"],
-                                    a["st"])
+                                    a["flags"], a["st"])
 
 
 def test_bwd_validation(L):
@@ -109,6 +109,7 @@ def test_bwd_validation(L):
     assert _bwd(L, r=0, la=None, lb=None) == SHAPE   # grads requested with r = 0
     assert _bwd(L, da=MIS) == ALIGN
     assert _bwd(L, s=math.inf) == VALUE
+    assert _bwd(L, flags=2) == VALUE          # unknown flag bit
     assert _bwd(L, wsb=0) == WORKSPACE
 
 

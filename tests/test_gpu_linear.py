@@ -151,6 +151,24 @@ def test_determinism():
         assert np.array_equal(u, v)
 
 
+def test_backward_reuses_forward_state():
+    """QLORA_BWD_REUSE_FORWARD: the backward takes s X A from the forward's
+    workspace; dX, dA and dB are bit-identical to the backward that recomputes it."""
+    lin = synth.Linear("t", 640, 448)
+    T, r, s = 333, 24, 0.5
+    d = _inputs(9, lin, T, r)
+    qw = api.nf4_quantize_dq(to_dev(d["w"], (lin.N, lin.K)))
+    x, a, b = to_dev(d["x"], (T, lin.K)), to_dev(d["a"], (lin.K, r)), to_dev(d["b"], (r, lin.N))
+    dy = to_dev(d["dy"], (T, lin.N))
+    ref = [bits_of(v) for v in api.qlora_linear_bwd_input(dy, qw, a, b, s, x=x, lora_grads=True)]
+    ws = api.workspace_for(T, lin.K, lin.N, r, x.device)
+    api.qlora_linear_fwd(x, qw, a, b, s, workspace=ws)
+    got = [bits_of(v) for v in api.qlora_linear_bwd_input(dy, qw, a, b, s, x=x, lora_grads=True, workspace=ws,
+                                                             reuse_forward=True)]
+    for name, u, v in zip(("dX", "dA", "dB"), got, ref):
+        assert np.array_equal(u, v), name
+
+
 @pytest.mark.parametrize("idx", [0, 4, 6])
 def test_decode_7b_shapes_full(idx):
     """Decode-size forward (VALU GEMV path) on the 7B layer shapes, r = 64, s = 0.25,
