@@ -125,6 +125,9 @@ QL_DEV u32x4_t bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
 QL_DEV uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
+QL_DEV uint32_t bload2(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+}
 QL_DEV uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
 }

@@ -9,14 +9,16 @@
 // the Volcengine article section 3.4, read as above).  s X A arrives as the
 // bf16 hi/lo pair the LoRA down-projection writes.
 //
-// Mapping: a workgroup of four wave64s owns 16 consecutive rows of W (four
-// per wave).  The reduction over K runs in slices of 1024: the slice of X
-// (T x 1024 bf16) is staged in LDS once per workgroup, each lane takes 16
-// consecutive k of the slice (8 code bytes per row, one block scale per row),
+// Mapping: a workgroup of four wave64s owns R consecutive rows of W (R = 16,
+// 8 or 4 as T grows) and one round of the reduction (4096 k, or 2048 at
+// T > 8).  The round of X (T x round bf16) is staged in LDS once; each lane
+// takes 16 consecutive k (8 code bytes per row, one block scale per row),
 // dequantizes them once and multiplies them with all T tokens using
-// v_dot2_f32_bf16 (two products per instruction, fp32 accumulation).  At the
-// end the LoRA up-projection is added lane-parallel over the rank and a
-// butterfly reduction over the wave gives each (row, token) sum.
+// v_dot2_f32_bf16 (two products per instruction, fp32 accumulation).  The 64
+// lanes of a wave are summed with DPP row swaps and four lane reads, the four
+// waves in LDS.  The LoRA down projection runs as extra workgroups of the
+// same launch over 256-wide slices; a second small kernel adds all partial
+// sums in a fixed order and applies the LoRA up projection.
 #include "common.hpp"
 #include "plan.hpp"
 
@@ -28,13 +30,22 @@ typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint8_t g_lds8_t;
 typedef __attribute__((address_space(3))) u32x4_t g_lds_u32x4_t;
 typedef __attribute__((address_space(3))) f32x2_t g_lds_f32x2_t;
-typedef __amdgpu_buffer_rsrc_t g_rsrc_t;
-constexpr uint32_t kGOOB = 0x80000000u;
 
-__device__ __forceinline__ g_rsrc_t g_rsrc(const void* base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+
+// Sum over the 64 lanes of a wave, returned in every lane (deterministic
+// order): DPP swaps give every lane its 16-lane row's sum (quad_perm
+// [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror), then the four row sums
+// are read out and added.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+    return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
 }
-
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, a), __builtin_bit_cast(bf16x2v_t, b), c,
@@ -65,7 +76,7 @@ constexpr int gemv_rows() { return TT <= 4 ? 16 : (TT <= 8 ? 8 : 4); }
 // k per workgroup (one LDS-staged round of X; four 1024-wide wave chunks)
 template <int TT>
 constexpr int gemv_round() { return TT <= 8 ? 4096 : 2048; }
-constexpr int kLoraSlice = 256;   // k per LoRA down-projection workgroup
+constexpr int kLoraSlice = 256;   // k per LoRA down-projection workgroup (one 64-k chunk per wave)
 
 // Launch 1.  Blocks [0, gemv_blocks) are GEMV blocks: rows [n0, n0 + R) over
 // the k round ks; the round of X (T x 4096 bf16) is staged in LDS once and
@@ -88,13 +99,14 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs p, Codebook cb) {
 
     if ((int)blockIdx.x >= p.gemv_blocks) {
         // ---- LoRA down-projection partials: lpart[kl][t][j] = sum_{k in slice} X[t][k] A[k][j]
-        // X[0:TT][slice] is staged in LDS; lane j of wave g loads its 64 A values
-        // (rows k0 + 64g .. +63) in one burst, then reads X as LDS broadcasts.
+        // X[0:TT][slice] is staged in LDS; wave g takes its quarter of the slice
+        // in chunks of 64: lane j loads its 64 A values of a chunk in one burst
+        // and reads X as LDS broadcasts.
         const int lb = (int)blockIdx.x - p.gemv_blocks;
         const int jc = lb % (int)(p.r_pad / 64), kl = lb / (int)(p.r_pad / 64);
         const int64_t j = (int64_t)jc * 64 + lane;
         const int64_t k0 = (int64_t)kl * kLoraSlice;
-        g_lds8_t* xl = base;                                           // [TT][256] bf16
+        g_lds8_t* xl = base;                                           // [TT][kLoraSlice] bf16
         for (int ch = threadIdx.x; ch < TT * (kLoraSlice / 8); ch += 256) {
             const int t = ch / (kLoraSlice / 8);
             const int64_t kk = k0 + (ch % (kLoraSlice / 8)) * 8;
@@ -102,27 +114,34 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs p, Codebook cb) {
             if (t < p.T && kk < p.K) v = *reinterpret_cast<const u32x4_t*>(p.x + t * p.K + kk);
             *reinterpret_cast<g_lds_u32x4_t*>(xl + (t * kLoraSlice + (ch % (kLoraSlice / 8)) * 8) * 2) = v;
         }
-        float av[64];
-#pragma unroll
-        for (int i = 0; i < 64; ++i) {
-            const int64_t k = k0 + 64 * wave + i;
-            av[i] = (j < p.r && k < p.K) ? bf16lo(p.lora_a[k * p.r + j]) : 0.0f;
-        }
         __syncthreads();
         float acc[TT];
 #pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            float v = 0.0f;
+        for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+        // A[k][j] by buffer loads: ranks j >= r get an offset past the end, and
+        // so do rows k >= K (their offset is at least K r 2 bytes), both read 0
+        const rsrc_t ra = make_rsrc(p.lora_a, p.K * p.r * 2);
+        for (int sub = 0; sub < kLoraSlice / 256; ++sub) {
+            const int kw = (kLoraSlice / 4) * wave + 64 * sub;         // chunk start inside the slice
+            const uint32_t vo = j < p.r ? (uint32_t)(((k0 + kw) * p.r + j) * 2) : kOOB;
+            const uint32_t row = (uint32_t)(p.r * 2);
+            float av[64];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const u32x4_t xv = *reinterpret_cast<const g_lds_u32x4_t*>(xl + (t * kLoraSlice + 64 * wave + 8 * c) * 2);
+            for (int i = 0; i < 64; ++i) av[i] = bf16lo(bload2(ra, vo + i * row, 0));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v = fmaf(bf16lo(xv[e]), av[8 * c + 2 * e], v);
-                    v = fmaf(bf16hi(xv[e]), av[8 * c + 2 * e + 1], v);
+            for (int t = 0; t < TT; ++t) {
+                float v = acc[t];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const u32x4_t xv = *reinterpret_cast<const g_lds_u32x4_t*>(xl + (t * kLoraSlice + kw + 8 * c) * 2);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v = fmaf(bf16lo(xv[e]), av[8 * c + 2 * e], v);
+                        v = fmaf(bf16hi(xv[e]), av[8 * c + 2 * e + 1], v);
+                    }
                 }
+                acc[t] = v;
             }
-            acc[t] = v;
         }
         __syncthreads();
         g_lds_f32_t* red = (g_lds_f32_t*)base;                         // [4][TT][64]
@@ -151,10 +170,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs p, Codebook cb) {
     const int rb = (int)blockIdx.x % nb, ks = (int)blockIdx.x / nb;
     const int64_t n0 = (int64_t)rb * R;
     const int64_t kr0 = (int64_t)ks * KR;
-    const g_rsrc_t rc = g_rsrc(p.codes, p.N * p.K / 2);
-    const g_rsrc_t rf = g_rsrc(p.fp8, p.N * p.K / 64);
-    const g_rsrc_t rs = g_rsrc(p.sup, ceil_div(p.N * p.K / 64, 256) * 4);
-    const g_rsrc_t rx = g_rsrc(p.x, p.T * p.K * 2);
+    const rsrc_t rc = make_rsrc(p.codes, p.N * p.K / 2);
+    const rsrc_t rf = make_rsrc(p.fp8, p.N * p.K / 64);
+    const rsrc_t rs = make_rsrc(p.sup, ceil_div(p.N * p.K / 64, 256) * 4);
+    const rsrc_t rx = make_rsrc(p.x, p.T * p.K * 2);
 
     // this wave's loads first: codes, FP8 constants and super-scales of R rows
     const int64_t k = kr0 + wave * 1024 + lane * 16;
@@ -168,9 +187,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs p, Codebook cb) {
         const bool ok = kok && n < p.N;
         const int64_t blk = n * (p.K / 64) + k / 64;
         cw[i] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
-                                                rc, ok ? (uint32_t)(n * (p.K / 2) + k / 2) : kGOOB, 0, 0));
-        f8[i] = __builtin_amdgcn_raw_buffer_load_b8(rf, ok ? (uint32_t)blk : kGOOB, 0, 0);
-        s2[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, ok ? (uint32_t)(blk >> 8) * 4u : kGOOB, 0, 0));
+                                                rc, ok ? (uint32_t)(n * (p.K / 2) + k / 2) : kOOB, 0, 0));
+        f8[i] = __builtin_amdgcn_raw_buffer_load_b8(rf, ok ? (uint32_t)blk : kOOB, 0, 0);
+        s2[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, ok ? (uint32_t)(blk >> 8) * 4u : kOOB, 0, 0));
     }
     // stage X[0:TT][kr0 : kr0 + KR] (zeros past T and K)
 #pragma unroll
@@ -178,7 +197,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs p, Codebook cb) {
         const int ch = threadIdx.x + c * 256;
         const int t = ch / (KR / 8);
         const int64_t kk = kr0 + (ch % (KR / 8)) * 8;
-        const uint32_t vo = (t < p.T && kk < p.K) ? (uint32_t)((t * p.K + kk) * 2) : kGOOB;
+        const uint32_t vo = (t < p.T && kk < p.K) ? (uint32_t)((t * p.K + kk) * 2) : kOOB;
         const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, vo, 0, 0));
         *reinterpret_cast<g_lds_u32x4_t*>(xs + (int64_t)t * (KR * 2) + (ch % (KR / 8)) * 16) = v;
     }
@@ -216,16 +235,14 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs p, Codebook cb) {
             }
         }
     }
-    // wave butterfly, then the four waves meet in LDS (reusing the X area)
+    // wave sums, then the four waves meet in LDS (reusing the X area)
     __syncthreads();
     g_lds_f32_t* red = (g_lds_f32_t*)xs;                               // [4][R][TT]
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
-            float v = acc[i][t];
-#pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+            const float v = wave_sum(acc[i][t]);
             if (lane == 0) red[(wave * R + i) * TT + t] = v;
         }
     __syncthreads();
@@ -240,58 +257,132 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs p, Codebook cb) {
     }
 }
 
-// Launch 2.  s X A from its slice partials (fixed order, loads issued in
-// batches of 8), then Y[t][n] = sum_ks part[ks][t][n] + sum_j (s X A)[t][j] B[j][n]
-// rounded to bf16.  Thread n loads its column of B 64 ranks at a time before
-// using it.
+// Launch 2.  Y[t][n] = sum_ks part[ks][t][n] + sum_j (s X A)[t][j] B[j][n],
+// rounded to bf16.  A workgroup owns 64 columns n (one per lane); wave w takes
+// ranks [w r_pad/4, (w+1) r_pad/4) of B and the base partials of the tokens
+// t = w mod 4, and issues those loads first.  Meanwhile the whole workgroup
+// rebuilds s X A from its slice partials: thread (e, g) adds slices
+// g, g + G, g + 2G, ... of the float4 entry e, all loads independent, and the
+// G group sums are added in g order.  The four wave sums of each output are
+// added in wave order, so the result does not depend on timing.
+constexpr int kFinCols = 64;
+template <int RP>
 __global__ __launch_bounds__(256) void k_gemv_finalize(GemvArgs p) {
-    __shared__ float ps[16 * 256];                                     // [T][r] (T <= 16, r <= 256)
-    for (int64_t i = threadIdx.x; i < p.T * p.r; i += 256) {
-        const int64_t t = i / p.r, j = i % p.r;
-        const float* src = p.lpart + t * p.r_pad + j;
-        const int64_t stride = p.T * p.r_pad;
-        float v = 0.0f;
-        int kl = 0;
-        for (; kl + 8 <= p.KL; kl += 8) {
-            float b[8];
+    constexpr int RQ = 16 * RP;                                        // ranks of B per wave
+    __shared__ __align__(16) float pr[4 * 256];                        // group sums [G][W] float4
+    __shared__ __align__(16) float ps[16 * 256];                       // s X A [T][r_pad]
+    __shared__ __align__(16) float red[4 * 16 * kFinCols];             // wave sums [4][T][64]
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t n = (int64_t)blockIdx.x * kFinCols + lane;
+    const bool nok = n < p.N;
+
+    // B column n over this wave's ranks, and the first 8 base partials of its tokens
+    uint32_t bv[RQ > 0 ? RQ : 1];
+    if constexpr (RP > 0) {
+        const rsrc_t rb = make_rsrc(p.lora_b, p.r * p.N * 2);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) b[u] = src[(kl + u) * stride];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v += b[u];
+        for (int u = 0; u < RQ; ++u) {
+            const int64_t j = (int64_t)wave * RQ + u;
+            bv[u] = bload2(rb, (nok && j < p.r) ? (uint32_t)((j * p.N + n) * 2) : kOOB, 0);
         }
-        for (; kl < p.KL; ++kl) v += src[kl * stride];
-        ps[i] = v * p.scaling;
+    }
+    const rsrc_t rp = make_rsrc(p.part, (int64_t)p.KS * p.T * p.N * 4);
+    const uint32_t n4 = (uint32_t)n * 4u;
+    auto part_at = [&](int ks, int t) -> uint32_t {
+        const uint32_t row = (uint32_t)(((int64_t)ks * p.T + t) * p.N * 4);   // wave-uniform
+        return (nok && t < p.T && ks < p.KS) ? row + n4 : kOOB;
+    };
+    uint32_t pv[8][4];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[c][i] = bload4(rp, part_at(c, wave + 4 * i), 0);
+
+    if constexpr (RP > 0) {
+        const int E4 = (int)(p.T * p.r_pad / 4);                       // float4 entries of s X A
+        const int W = E4 < 256 ? E4 : 256;
+        const int G = 256 / W;                                         // slice groups
+        const int eb = (int)threadIdx.x % W, g = (int)threadIdx.x / W;
+        const rsrc_t rl = make_rsrc(p.lpart, (int64_t)p.KL * p.T * p.r_pad * 4);
+        const uint32_t slice = (uint32_t)(p.T * p.r_pad * 4);
+        for (int e = eb; e < E4; e += W) {
+            f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int kb = g; kb < p.KL; kb += 16 * G) {
+                u32x4_t v[16];
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    const int kl = kb + c * G;
+                    v[c] = bload16(rl, kl < p.KL ? kl * slice + (uint32_t)e * 16u : kOOB, 0);
+                }
+#pragma unroll
+                for (int c = 0; c < 16; ++c) a += __builtin_bit_cast(f32x4_t, v[c]);
+            }
+            if (G == 1) {
+                *reinterpret_cast<f32x4_t*>(ps + 4 * e) = a * p.scaling;
+            } else if (g < G) {
+                *reinterpret_cast<f32x4_t*>(pr + 4 * (g * W + e)) = a;
+            }
+        }
+        if (G > 1) {
+            __syncthreads();
+            if ((int)threadIdx.x < E4) {
+                f32x4_t a = *reinterpret_cast<const f32x4_t*>(pr + 4 * threadIdx.x);
+                for (int gg = 1; gg < G; ++gg)
+                    a += *reinterpret_cast<const f32x4_t*>(pr + 4 * (gg * W + threadIdx.x));
+                *reinterpret_cast<f32x4_t*>(ps + 4 * threadIdx.x) = a * p.scaling;
+            }
+        }
+        __syncthreads();
+    }
+
+    // base partials of this wave's tokens, in ks order
+    float yb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float v = __uint_as_float(pv[0][i]);
+#pragma unroll
+        for (int c = 1; c < 8; ++c) v += __uint_as_float(pv[c][i]);
+        yb[i] = v;
+    }
+    for (int ks0 = 8; ks0 < p.KS; ks0 += 8) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pv[c][i] = bload4(rp, part_at(ks0 + c, wave + 4 * i), 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) yb[i] += __uint_as_float(pv[c][i]);
+    }
+
+    // this wave's share of every output column: base partials (own tokens) + its ranks of B
+    const int T = (int)p.T;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        if (t < T) {
+            float v = (t & 3) == wave ? yb[t >> 2] : 0.0f;
+            if constexpr (RP > 0) {
+#pragma unroll
+                for (int q = 0; q < RQ / 4; ++q) {
+                    const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(ps + t * p.r_pad + wave * RQ + 4 * q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v = fmaf(sv[e], bf16lo(bv[4 * q + e]), v);
+                }
+            }
+            red[(wave * 16 + t) * kFinCols + lane] = v;
+        }
     }
     __syncthreads();
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (n >= p.N) return;
-    float y[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) y[t] = 0.0f;
-    for (int ks = 0; ks < p.KS; ++ks) {
-        float v[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) v[t] = t < p.T ? p.part[((int64_t)ks * p.T + t) * p.N + n] : 0.0f;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) y[t] += v[t];
-    }
-    for (int64_t j0 = 0; j0 < p.r; j0 += 64) {
-        float bv[64];
-#pragma unroll
-        for (int u = 0; u < 64; ++u) bv[u] = (j0 + u < p.r) ? bf16lo(p.lora_b[(j0 + u) * p.N + n]) : 0.0f;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            if (t >= p.T) continue;
-            float v = y[t];
-#pragma unroll
-            for (int u = 0; u < 64; ++u)
-                if (j0 + u < p.r) v = fmaf(ps[t * p.r + j0 + u], bv[u], v);
-            y[t] = v;
+    for (int i = threadIdx.x; i < T * kFinCols; i += 256) {
+        const int t = i / kFinCols, l = i % kFinCols;
+        const int64_t nn = (int64_t)blockIdx.x * kFinCols + l;
+        if (nn < p.N) {
+            const float v = red[(0 * 16 + t) * kFinCols + l] + red[(1 * 16 + t) * kFinCols + l] +
+                            red[(2 * 16 + t) * kFinCols + l] + red[(3 * 16 + t) * kFinCols + l];
+            p.y[t * p.N + nn] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
         }
     }
-#pragma unroll
-    for (int t = 0; t < 16; ++t)
-        if (t < p.T) p.y[t * p.N + n] = (uint16_t)(pack_bf16x2(y[t], 0.0f) & 0xFFFFu);
 }
 
 int gemv_ks(int64_t T, int64_t K) { return (int)ceil_div(K, T <= 8 ? 4096 : 2048); }
@@ -327,7 +418,14 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, const uint8_t* f
     if (ae != hipSuccess) return ae;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_gemv_finalize, dim3((unsigned)ceil_div(pl.N, 256)), block, 0, s, a);
+    const dim3 fg((unsigned)ceil_div(pl.N, kFinCols));
+    switch (pl.r_pad / 64) {
+        case 0: hipLaunchKernelGGL(k_gemv_finalize<0>, fg, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL(k_gemv_finalize<1>, fg, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL(k_gemv_finalize<2>, fg, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL(k_gemv_finalize<3>, fg, block, 0, s, a); break;
+        default: hipLaunchKernelGGL(k_gemv_finalize<4>, fg, block, 0, s, a); break;
+    }
     return hipGetLastError();
 }
 
