@@ -302,7 +302,7 @@ def main():
         comp[f"decode_T{Td}"] = {"GB/s": round(nbytes / secs / 1e9, 1),
                                  "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
                                  "us_per_layer_set": round(1e6 * secs, 2),
-                                 "note": "7 linears, fused dequant + VALU GEMV incl. LoRA; weights rotated over 6 copies"}
+                                 "note": "7 linears, fused dequant + small-M MFMA (16x16x32) incl. LoRA; weights rotated over 6 copies"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, T, r, s, args.cpu_tokens)
     print(json.dumps(out), flush=True)

@@ -102,6 +102,61 @@ QL_DEV const __attribute__((address_space(3))) T* lds_at(uint32_t a) {
     return reinterpret_cast<const __attribute__((address_space(3))) T*>((uintptr_t)a);
 }
 
+// Byte-pair codebook tables in LDS: the entry of code byte e holds the fp32
+// pair (q[e >> 4], q[e & 15]), i.e. the values of its high (even element) and
+// low (odd element) nibbles.  The table is replicated so that the lanes one
+// LDS cycle serves read distinct banks:
+//   wide:   32 copies, entry e of copy c at e*256 + c*8 (64 KB), copy = lane & 31;
+//   narrow: 16 copies, entry e of copy c at e*128 + c*8 (32 KB), copy = lane & 15.
+// Both builders take a 256-thread workgroup.  Each thread writes entries whose
+// high nibble is a compile-time constant of the unrolled loop and whose low
+// nibble is fixed per thread, so every codebook value is read from the kernel
+// arguments with a constant index (scalar loads once, no per-entry memory
+// round trip).
+constexpr uint32_t kWideTableBytes = 256 * 256;
+constexpr uint32_t kNarrowTableBytes = 256 * 128;
+
+// Codebook value j as a wave-uniform register (keeps selects between values
+// from being folded into a per-lane indexed load)
+QL_DEV float cb_value(const Codebook& cb, int j) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cb.q[j])));
+}
+
+QL_DEV void build_wide_pair_table(lds8_t* tbl, const Codebook& cb) {
+    // thread: copy (tid & 31), entries e = (tid >> 5) + 8 i, i < 32, so
+    // e >> 4 = i >> 1 and e & 15 = (tid >> 5) + 8 (i & 1)
+    const int sub = (int)threadIdx.x >> 5;
+    float lo0 = cb_value(cb, 0), lo1 = cb_value(cb, 8);
+#pragma unroll
+    for (int j = 1; j < 8; ++j)
+        if (sub == j) {
+            lo0 = cb_value(cb, j);
+            lo1 = cb_value(cb, j + 8);
+        }
+    lds8_t* dst = tbl + sub * 256 + (threadIdx.x & 31) * 8;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const f32x2_t v = {cb_value(cb, i >> 1), (i & 1) ? lo1 : lo0};
+        *reinterpret_cast<lds_f32x2_t*>(dst + i * 2048) = v;
+    }
+}
+
+QL_DEV void build_pair_table16(lds8_t* tbl, const Codebook& cb) {
+    // thread: copy (tid & 15), entries e = (tid >> 4) + 16 i, i < 16, so
+    // e >> 4 = i and e & 15 = tid >> 4
+    const int sub = (int)threadIdx.x >> 4;
+    float lo = cb_value(cb, 0);
+#pragma unroll
+    for (int j = 1; j < 16; ++j)
+        if (sub == j) lo = cb_value(cb, j);
+    lds8_t* dst = tbl + sub * 128 + (threadIdx.x & 15) * 8;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const f32x2_t v = {cb_value(cb, i), lo};
+        *reinterpret_cast<lds_f32x2_t*>(dst + i * 2048) = v;
+    }
+}
+
 // LDS tile of [rows][64] bf16: 128 bytes per row in 16-byte chunks, the chunk
 // index XOR-swizzled with bits of the row so that fragment reads (16 or 32
 // consecutive rows at a fixed chunk) and row-wise writes spread over all banks.

@@ -178,21 +178,6 @@ struct FwdArgs {
     int64_t T, K, N, r, r_pad;
 };
 
-// Byte-pair codebook replicated 32 times so that the 32 lanes one LDS cycle
-// serves (64 banks x 4 bytes) always read distinct banks: entry e of copy c
-// sits at e*256 + c*8, and lane l uses copy (l & 31).  With that stride the
-// lookup address is (byte << 8) | (copy * 8), one byte permute of the packed
-// codes.
-constexpr uint32_t kWideTableBytes = 256 * 256;
-
-QL_DEV void build_wide_pair_table(lds8_t* tbl, const Codebook& cb) {
-    for (int i = threadIdx.x; i < 256 * 32; i += kThreads) {
-        const int e = i >> 5;
-        const f32x2_t v = {cb.q[e >> 4], cb.q[e & 15]};
-        *reinterpret_cast<lds_f32x2_t*>(tbl + e * 256 + (i & 31) * 8) = v;
-    }
-}
-
 // Y = X W'^T (+ (s X A) B), tile 256 (n) x 256 (t), waves stacked along n.
 //
 // Wave w owns W rows n0 + 64w .. +63 (two 32-row MFMA A-fragments) against all
@@ -530,16 +515,6 @@ __global__ __launch_bounds__(256) void k_scales_t(const uint8_t* __restrict__ fp
 // written, barrier, then the fragments of tile kt+1's step 0 and the lookups
 // of quarter 0 of tile kt+2 are read during the other half.  W codes and
 // block scales are loaded about a tile and a half ahead, dY one tile ahead.
-constexpr uint32_t kNarrowTableBytes = 256 * 128;
-
-QL_DEV void build_pair_table16(lds8_t* tbl, const Codebook& cb) {
-    for (int i = threadIdx.x; i < 256 * 16; i += kThreads) {
-        const int e = i >> 4;
-        const f32x2_t v = {cb.q[e >> 4], cb.q[e & 15]};
-        *reinterpret_cast<lds_f32x2_t*>(tbl + e * 128 + (i & 15) * 8) = v;
-    }
-}
-
 // LDS offset inside a W^T tile: rows permuted as described above.
 QL_DEV uint32_t lds_off_w(int row, int chunk) { return lds_off(row ^ ((row >> 6) & 1), chunk); }
 

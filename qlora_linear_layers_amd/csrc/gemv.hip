@@ -1,24 +1,28 @@
-// Decode-size forward (T <= 16 tokens): fused NF4 double dequantization +
-// GEMV on the vector ALUs, no MFMA.  The weight stream is the only large
-// operand (0.516 bytes per weight), so the kernel is organised around reading
-// it once with wide coalesced loads and reusing every dequantized weight for
-// all T tokens.
+// Decode-size forward (T <= 16 tokens): fused NF4 double dequantization and
+// a small-M MFMA product, then one small kernel for the split sums and the
+// LoRA up projection.  The weight stream is the only large operand (0.516
+// bytes per weight), so the kernel is organised around issuing all of it at
+// once, with enough waves in flight to cover the memory latency.
 //
 // Layer: Y = X W'^T + s (X A) B with W' = RNE_bf16(fl32(q[code] * c1')) and
 // c1' = fl32(e4m3(f) * s2) ("QLoRA 原理精讲" section 2.2; the layer equation of
-// the Volcengine article section 3.4, read as above).  s X A arrives as the
-// bf16 hi/lo pair the LoRA down-projection writes.
+// the Volcengine article section 3.4, read as above).
 //
-// Mapping: a workgroup of four wave64s owns R consecutive rows of W (R = 16,
-// 8 or 4 as T grows) and one round of the reduction (4096 k, or 2048 at
-// T > 8).  The round of X (T x round bf16) is staged in LDS once; each lane
-// takes 16 consecutive k (8 code bytes per row, one block scale per row),
-// dequantizes them once and multiplies them with all T tokens using
-// v_dot2_f32_bf16 (two products per instruction, fp32 accumulation).  The 64
-// lanes of a wave are summed with DPP row swaps and four lane reads, the four
-// waves in LDS.  The LoRA down projection runs as extra workgroups of the
-// same launch over 256-wide slices; a second small kernel adds all partial
-// sums in a fixed order and applies the LoRA up projection.
+// Product: v_mfma_f32_16x16x32_bf16 with X as the 16-row A operand (tokens,
+// rows past T read as zeros) and the dequantized W as the B operand (16 rows
+// of W per MFMA).  The contraction order inside a 128-wide k step is free, so
+// lane group g (lanes 16g .. 16g+15) takes the 32 consecutive k at 32g for
+// both operands: one 16-byte code load per W row and four 16-byte X loads
+// per lane, and sub-step j of the step uses k 32g + 8j .. +7.  The codes of
+// one byte (two weights) are looked up in the 32-way replicated pair table
+// (one byte permute builds the LDS address), scaled by the block constant,
+// rounded to bf16 and packed: the per-weight work does not grow with T.
+//
+// Workgroup: eight waves, two groups of 64 W rows (four 16-row MFMA tiles per
+// wave) times four 128-wide k steps, so 128 rows x 512 k; the four k waves of a
+// row group are added in LDS in wave order and one fp32 partial per
+// (k split, token, row) is written.  The LoRA down projection runs as extra
+// workgroups of the same launch over 256-wide k slices (VALU, lane = rank).
 #include "common.hpp"
 #include "plan.hpp"
 
@@ -26,31 +30,7 @@ namespace ql {
 
 namespace {
 
-typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) uint8_t g_lds8_t;
-typedef __attribute__((address_space(3))) u32x4_t g_lds_u32x4_t;
-typedef __attribute__((address_space(3))) f32x2_t g_lds_f32x2_t;
-
-
-// Sum over the 64 lanes of a wave, returned in every lane (deterministic
-// order): DPP swaps give every lane its 16-lane row's sum (quad_perm
-// [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror), then the four row sums
-// are read out and added.
-__device__ __forceinline__ float wave_sum(float v) {
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
-    return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
-            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))) +
-           (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
-            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
-}
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, a), __builtin_bit_cast(bf16x2v_t, b), c,
-                                           false);
-}
+typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
 
 }  // namespace
 
@@ -61,7 +41,7 @@ struct GemvArgs {
     const float* sup;
     const uint16_t* lora_a;   // [K][r]
     const uint16_t* lora_b;   // [r][N]
-    float* part;              // [KS][T][N] fp32 base-GEMV partials
+    float* part;              // [KS][T][N] fp32 base partials
     float* lpart;             // [KL][T][r_pad] fp32 LoRA down-projection partials
     uint16_t* y;              // [T][N]
     int64_t T, K, N, r, r_pad;
@@ -69,190 +49,159 @@ struct GemvArgs {
     float scaling;
 };
 
-// Rows per workgroup for a token count: the X reuse (R rows per X read) grows
-// with T while the accumulators (R x TT registers) stay within budget.
-template <int TT>
-constexpr int gemv_rows() { return TT <= 4 ? 16 : (TT <= 8 ? 8 : 4); }
-// k per workgroup (one LDS-staged round of X; four 1024-wide wave chunks)
-template <int TT>
-constexpr int gemv_round() { return TT <= 8 ? 4096 : 2048; }
+constexpr int kDecThreads = 512;  // eight waves: 2 row groups x 4 k steps
+constexpr int kDecRows = 128;     // W rows per workgroup
+constexpr int kDecK = 512;        // k per workgroup
 constexpr int kLoraSlice = 256;   // k per LoRA down-projection workgroup (one 64-k chunk per wave)
+constexpr size_t kDecLds = kWideTableBytes;   // pair table; later reused for the wave sums
 
-// Launch 1.  Blocks [0, gemv_blocks) are GEMV blocks: rows [n0, n0 + R) over
-// the k round ks; the round of X (T x 4096 bf16) is staged in LDS once and
-// each wave takes one 1024-wide chunk of it (16 k per lane), so every load a
-// wave needs (8 code bytes, one FP8 constant and one super-scale per row) is
-// issued up front.  Weights are dequantized once and multiplied with all T
-// tokens by v_dot2_f32_bf16; the four wave sums meet in LDS and one fp32
-// partial per (ks, t, n) is written.  The remaining blocks compute partial
-// sums of X A over 256-wide k slices (lane j, wave-uniform k, so the X values
-// are scalar loads).
+// LoRA down-projection partials of one 256-wide k slice and 64 ranks:
+// lpart[kl][t][j] = sum_{k in slice} X[t][k] A[k][j].  X[0:TT][slice] is
+// staged in LDS; waves 0-3 take a quarter of the slice each: lane j loads
+// its 64 A values in one burst and reads X as LDS broadcasts.  Every thread
+// of the workgroup reaches every barrier.
 template <int TT>
-__global__ __launch_bounds__(256) void k_gemv(GemvArgs p, Codebook cb) {
-    constexpr int R = gemv_rows<TT>();
-    constexpr int KR = gemv_round<TT>();
+__device__ __forceinline__ void lora_down_block(const GemvArgs& p, uint8_t* dyn, int lb) {
     typedef __attribute__((address_space(3))) float g_lds_f32_t;
-    extern __shared__ __align__(16) uint8_t dyn[];
-    g_lds8_t* base = (g_lds8_t*)dyn;
+    lds8_t* xl = (lds8_t*)dyn;                                         // [TT][kLoraSlice] bf16
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-    if ((int)blockIdx.x >= p.gemv_blocks) {
-        // ---- LoRA down-projection partials: lpart[kl][t][j] = sum_{k in slice} X[t][k] A[k][j]
-        // X[0:TT][slice] is staged in LDS; wave g takes its quarter of the slice
-        // in chunks of 64: lane j loads its 64 A values of a chunk in one burst
-        // and reads X as LDS broadcasts.
-        const int lb = (int)blockIdx.x - p.gemv_blocks;
-        const int jc = lb % (int)(p.r_pad / 64), kl = lb / (int)(p.r_pad / 64);
-        const int64_t j = (int64_t)jc * 64 + lane;
-        const int64_t k0 = (int64_t)kl * kLoraSlice;
-        g_lds8_t* xl = base;                                           // [TT][kLoraSlice] bf16
-        for (int ch = threadIdx.x; ch < TT * (kLoraSlice / 8); ch += 256) {
-            const int t = ch / (kLoraSlice / 8);
-            const int64_t kk = k0 + (ch % (kLoraSlice / 8)) * 8;
-            u32x4_t v = {0, 0, 0, 0};
-            if (t < p.T && kk < p.K) v = *reinterpret_cast<const u32x4_t*>(p.x + t * p.K + kk);
-            *reinterpret_cast<g_lds_u32x4_t*>(xl + (t * kLoraSlice + (ch % (kLoraSlice / 8)) * 8) * 2) = v;
-        }
-        __syncthreads();
-        float acc[TT];
+    const int jc = lb % (int)(p.r_pad / 64), kl = lb / (int)(p.r_pad / 64);
+    const int64_t j = (int64_t)jc * 64 + lane;
+    const int64_t k0 = (int64_t)kl * kLoraSlice;
+    const rsrc_t rx = make_rsrc(p.x, p.T * p.K * 2);
+    for (int ch = threadIdx.x; ch < TT * (kLoraSlice / 8); ch += kDecThreads) {
+        const int t = ch / (kLoraSlice / 8);
+        const int64_t kk = k0 + (ch % (kLoraSlice / 8)) * 8;
+        const u32x4_t v = bload16(rx, (t < p.T && kk < p.K) ? (uint32_t)((t * p.K + kk) * 2) : kOOB, 0);
+        *reinterpret_cast<lds_u32x4_t*>(xl + (t * kLoraSlice + (ch % (kLoraSlice / 8)) * 8) * 2) = v;
+    }
+    __syncthreads();
+    float acc[TT];
 #pragma unroll
-        for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+    for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+    if (wave < 4) {
         // A[k][j] by buffer loads: ranks j >= r get an offset past the end, and
         // so do rows k >= K (their offset is at least K r 2 bytes), both read 0
         const rsrc_t ra = make_rsrc(p.lora_a, p.K * p.r * 2);
-        for (int sub = 0; sub < kLoraSlice / 256; ++sub) {
-            const int kw = (kLoraSlice / 4) * wave + 64 * sub;         // chunk start inside the slice
-            const uint32_t vo = j < p.r ? (uint32_t)(((k0 + kw) * p.r + j) * 2) : kOOB;
-            const uint32_t row = (uint32_t)(p.r * 2);
-            float av[64];
+        const int kw = (kLoraSlice / 4) * wave;                         // chunk start inside the slice
+        const uint32_t vo = j < p.r ? (uint32_t)(((k0 + kw) * p.r + j) * 2) : kOOB;
+        const uint32_t row = (uint32_t)(p.r * 2);
+        float av[64];
 #pragma unroll
-            for (int i = 0; i < 64; ++i) av[i] = bf16lo(bload2(ra, vo + i * row, 0));
+        for (int i = 0; i < 64; ++i) av[i] = bf16lo(bload2(ra, vo + i * row, 0));
 #pragma unroll
-            for (int t = 0; t < TT; ++t) {
-                float v = acc[t];
+        for (int t = 0; t < TT; ++t) {
+            float v = acc[t];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const u32x4_t xv = *reinterpret_cast<const g_lds_u32x4_t*>(xl + (t * kLoraSlice + kw + 8 * c) * 2);
+            for (int c = 0; c < 8; ++c) {
+                const u32x4_t xv = *reinterpret_cast<const lds_u32x4_t*>(xl + (t * kLoraSlice + kw + 8 * c) * 2);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        v = fmaf(bf16lo(xv[e]), av[8 * c + 2 * e], v);
-                        v = fmaf(bf16hi(xv[e]), av[8 * c + 2 * e + 1], v);
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    v = fmaf(bf16lo(xv[e]), av[8 * c + 2 * e], v);
+                    v = fmaf(bf16hi(xv[e]), av[8 * c + 2 * e + 1], v);
                 }
-                acc[t] = v;
             }
+            acc[t] = v;
         }
-        __syncthreads();
-        g_lds_f32_t* red = (g_lds_f32_t*)base;                         // [4][TT][64]
+    }
+    __syncthreads();
+    g_lds_f32_t* red = (g_lds_f32_t*)dyn;                              // [4][TT][64]
+    if (wave < 4) {
 #pragma unroll
         for (int t = 0; t < TT; ++t) red[(wave * TT + t) * 64 + lane] = acc[t];
-        __syncthreads();
-        for (int i = threadIdx.x; i < TT * 64; i += 256) {
-            const int t = i >> 6, jj = i & 63;
-            if (t < p.T) {
-                const float v = red[(0 * TT + t) * 64 + jj] + red[(1 * TT + t) * 64 + jj] +
-                                red[(2 * TT + t) * 64 + jj] + red[(3 * TT + t) * 64 + jj];
-                p.lpart[((int64_t)kl * p.T + t) * p.r_pad + jc * 64 + jj] = v;
-            }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < TT * 64; i += kDecThreads) {
+        const int t = i >> 6, jj = i & 63;
+        if (t < p.T) {
+            const float v = red[(0 * TT + t) * 64 + jj] + red[(1 * TT + t) * 64 + jj] +
+                            red[(2 * TT + t) * 64 + jj] + red[(3 * TT + t) * 64 + jj];
+            p.lpart[((int64_t)kl * p.T + t) * p.r_pad + jc * 64 + jj] = v;
         }
+    }
+}
+
+// Launch 1.  Blocks [0, gemv_blocks) are base blocks: rows [n0, n0 + 128) over
+// the k split ks (512 k); the rest are LoRA down-projection blocks.
+template <int TT>
+__global__ __launch_bounds__(kDecThreads) void k_gemv(GemvArgs p, Codebook cb) {
+    extern __shared__ __align__(16) uint8_t dyn[];
+    if ((int)blockIdx.x >= p.gemv_blocks) {
+        lora_down_block<TT>(p, dyn, (int)blockIdx.x - p.gemv_blocks);
         return;
     }
-
-    // ---- base GEMV partials
-    g_lds8_t* tbl = base;                                              // 2 KB byte-pair table
-    g_lds8_t* xs = base + 2048;                                        // [TT][KR] bf16
-    {
-        const f32x2_t v = {cb.q[threadIdx.x >> 4], cb.q[threadIdx.x & 15]};
-        *reinterpret_cast<g_lds_f32x2_t*>(tbl + threadIdx.x * 8) = v;
-    }
-    const int nb = (int)ceil_div(p.N, R);
+    lds8_t* tbl = (lds8_t*)dyn;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = wv & 3, rg = wv >> 2;                             // k step, row group
+    const int nl = lane & 15, g = lane >> 4;
+    const int nb = (int)ceil_div(p.N, kDecRows);
     const int rb = (int)blockIdx.x % nb, ks = (int)blockIdx.x / nb;
-    const int64_t n0 = (int64_t)rb * R;
-    const int64_t kr0 = (int64_t)ks * KR;
+    const int64_t n0 = (int64_t)rb * kDecRows + 64 * rg;
+    const int64_t kk = (int64_t)ks * kDecK + 128 * wave + 32 * g;      // this lane's 32 k
+    const bool kok = kk < p.K;                                         // K % 64 == 0: all 32 or none
     const rsrc_t rc = make_rsrc(p.codes, p.N * p.K / 2);
     const rsrc_t rf = make_rsrc(p.fp8, p.N * p.K / 64);
     const rsrc_t rs = make_rsrc(p.sup, ceil_div(p.N * p.K / 64, 256) * 4);
     const rsrc_t rx = make_rsrc(p.x, p.T * p.K * 2);
 
-    // this wave's loads first: codes, FP8 constants and super-scales of R rows
-    const int64_t k = kr0 + wave * 1024 + lane * 16;
-    const bool kok = k < p.K && k < kr0 + KR;
-    u32x2_t cw[R];
-    uint32_t f8[R];
-    float s2[R];
+    // every load of the wave first: 16 code bytes, the FP8 constant and the
+    // super-scale of four rows, and the lane's 32 k of X (token nl)
+    u32x4_t cw[4], xv[4];
+    uint32_t f8[4], s2[4];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-        const int64_t n = n0 + i;
+    for (int c = 0; c < 4; ++c) {
+        const int64_t n = n0 + 16 * c + nl;
         const bool ok = kok && n < p.N;
-        const int64_t blk = n * (p.K / 64) + k / 64;
-        cw[i] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
-                                                rc, ok ? (uint32_t)(n * (p.K / 2) + k / 2) : kOOB, 0, 0));
-        f8[i] = __builtin_amdgcn_raw_buffer_load_b8(rf, ok ? (uint32_t)blk : kOOB, 0, 0);
-        s2[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, ok ? (uint32_t)(blk >> 8) * 4u : kOOB, 0, 0));
+        const int64_t blk = n * (p.K / 64) + kk / 64;
+        cw[c] = bload16(rc, ok ? (uint32_t)(n * (p.K / 2) + kk / 2) : kOOB, 0);
+        f8[c] = bload1(rf, ok ? (uint32_t)blk : kOOB, 0);
+        s2[c] = bload4(rs, ok ? (uint32_t)(blk >> 8) * 4u : kOOB, 0);
     }
-    // stage X[0:TT][kr0 : kr0 + KR] (zeros past T and K)
+    const bool xok = kok && nl < p.T;
 #pragma unroll
-    for (int c = 0; c < TT * KR / 8 / 256; ++c) {
-        const int ch = threadIdx.x + c * 256;
-        const int t = ch / (KR / 8);
-        const int64_t kk = kr0 + (ch % (KR / 8)) * 8;
-        const uint32_t vo = (t < p.T && kk < p.K) ? (uint32_t)((t * p.K + kk) * 2) : kOOB;
-        const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, vo, 0, 0));
-        *reinterpret_cast<g_lds_u32x4_t*>(xs + (int64_t)t * (KR * 2) + (ch % (KR / 8)) * 16) = v;
-    }
+    for (int j = 0; j < 4; ++j) xv[j] = bload16(rx, xok ? (uint32_t)((nl * p.K + kk + 8 * j) * 2) : kOOB, 0);
+    if (threadIdx.x < 256) build_wide_pair_table(tbl, cb);
     __syncthreads();
 
-    float acc[R][TT];
+    const uint32_t lane8 = lds_addr(tbl) + (uint32_t)(lane & 31) * 8u;   // table at LDS address 0
+    f32x4_t acc[4];
 #pragma unroll
-    for (int i = 0; i < R; ++i)
+    for (int c = 0; c < 4; ++c) {
+        acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        const float c1p = block_scale(f8[c], __uint_as_float(s2[c]));
 #pragma unroll
-        for (int t = 0; t < TT; ++t) acc[i][t] = 0.0f;
-    // A round narrower than the four wave chunks (KR = 2048) leaves waves 2, 3
-    // without k: they read no X (their chunk lies outside the staged rows).
-    if (wave * 1024 < KR) {
-        u32x4_t xv[TT][2];
-        const int xo = (wave * 1024 + lane * 16) * 2;
+        for (int j = 0; j < 4; ++j) {
+            u32x4_t w;
 #pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            xv[t][0] = *reinterpret_cast<const g_lds_u32x4_t*>(xs + t * (KR * 2) + xo);
-            xv[t][1] = *reinterpret_cast<const g_lds_u32x4_t*>(xs + t * (KR * 2) + xo + 16);
-        }
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const float c1p = block_scale(f8[i], s2[i]);
-#pragma unroll
-            for (int d = 0; d < 2; ++d) {
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const uint32_t byte = __builtin_amdgcn_ubfe(cw[i][d], 8 * b, 8);
-                    const f32x2_t qq = *reinterpret_cast<const g_lds_f32x2_t*>(tbl + byte * 8);
-                    const uint32_t wp = pack_bf16x2(__fmul_rn(qq[0], c1p), __fmul_rn(qq[1], c1p));
-                    const int e = d * 4 + b;
-#pragma unroll
-                    for (int t = 0; t < TT; ++t) acc[i][t] = dot2(wp, xv[t][e >> 2][e & 3], acc[i][t]);
-                }
+            for (int b = 0; b < 4; ++b) {
+                // address bytes: [0] lane copy, [1] code byte b, [2..3] table base
+                const uint32_t addr = __builtin_amdgcn_perm(cw[c][j], lane8, 0x03020000u | ((4u + b) << 8));
+                const f32x2_t q = *lds_at<f32x2_t>(addr);
+                w[b] = pack_bf16x2(__fmul_rn(q[0], c1p), __fmul_rn(q[1], c1p));
             }
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v_t, xv[j]),
+                                                             __builtin_bit_cast(bf16x8v_t, w), acc[c], 0, 0, 0);
         }
     }
-    // wave sums, then the four waves meet in LDS (reusing the X area)
+
+    // the four k waves of a row group meet in LDS (over the table), in wave order
     __syncthreads();
-    g_lds_f32_t* red = (g_lds_f32_t*)xs;                               // [4][R][TT]
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(dyn) + rg * 1024;        // [4 waves][4 tiles][64 lanes]
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            const float v = wave_sum(acc[i][t]);
-            if (lane == 0) red[(wave * R + i) * TT + t] = v;
-        }
+    for (int c = 0; c < 4; ++c) red[(wave * 4 + c) * 64 + lane] = acc[c];
     __syncthreads();
-    if (threadIdx.x < R * TT) {
-        const int i = threadIdx.x / TT, t = threadIdx.x % TT;
-        const int64_t n = n0 + i;
-        if (t < p.T && n < p.N) {
-            const float v = red[(0 * R + i) * TT + t] + red[(1 * R + i) * TT + t] + red[(2 * R + i) * TT + t] +
-                            red[(3 * R + i) * TT + t];
-            p.part[((int64_t)ks * p.T + t) * p.N + n] = v;
+    {
+        // thread (rg, c, l): tile c of its row group, accumulator lane l =
+        // row 16c + (l & 15), tokens 4 (l >> 4) .. +3
+        const int c = wave, l = lane;
+        const f32x4_t v = ((red[c * 64 + l] + red[(4 + c) * 64 + l]) + red[(8 + c) * 64 + l]) + red[(12 + c) * 64 + l];
+        const int64_t n = n0 + 16 * c + (l & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 4 * (l >> 4) + e;
+            if (t < p.T && n < p.N) p.part[((int64_t)ks * p.T + t) * p.N + n] = v[e];
         }
     }
 }
@@ -306,7 +255,8 @@ __global__ __launch_bounds__(256) void k_gemv_finalize(GemvArgs p) {
         const int eb = (int)threadIdx.x % W, g = (int)threadIdx.x / W;
         const rsrc_t rl = make_rsrc(p.lpart, (int64_t)p.KL * p.T * p.r_pad * 4);
         const uint32_t slice = (uint32_t)(p.T * p.r_pad * 4);
-        for (int e = eb; e < E4; e += W) {
+        // threads past G groups of W (when W does not divide 256) take no part
+        for (int e = eb; g < G && e < E4; e += W) {
             f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
             for (int kb = g; kb < p.KL; kb += 16 * G) {
                 u32x4_t v[16];
@@ -320,7 +270,7 @@ __global__ __launch_bounds__(256) void k_gemv_finalize(GemvArgs p) {
             }
             if (G == 1) {
                 *reinterpret_cast<f32x4_t*>(ps + 4 * e) = a * p.scaling;
-            } else if (g < G) {
+            } else {
                 *reinterpret_cast<f32x4_t*>(pr + 4 * (g * W + e)) = a;
             }
         }
@@ -385,46 +335,46 @@ __global__ __launch_bounds__(256) void k_gemv_finalize(GemvArgs p) {
     }
 }
 
-int gemv_ks(int64_t T, int64_t K) { return (int)ceil_div(K, T <= 8 ? 4096 : 2048); }
+int gemv_ks(int64_t K) { return (int)ceil_div(K, kDecK); }
 int gemv_kl(int64_t K) { return (int)ceil_div(K, kLoraSlice); }
 size_t gemv_workspace(int64_t T, int64_t K, int64_t N, int64_t r_pad) {
-    return align256((size_t)gemv_ks(T, K) * T * N * 4) + align256((size_t)gemv_kl(K) * T * (r_pad ? r_pad : 64) * 4);
+    // base partials [KS][T][N], LoRA partials [KL][T][r_pad] (none without an adapter)
+    return align256((size_t)gemv_ks(K) * T * N * 4) + align256((size_t)gemv_kl(K) * T * r_pad * 4);
 }
 
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, const uint8_t* fp8, const float* sup,
                        const uint16_t* lora_a, const uint16_t* lora_b, float scaling, const LoraPlan& pl,
                        uint8_t* ws, uint16_t* y, hipStream_t s) {
     GemvArgs a{x, codes, fp8, sup, lora_a, lora_b, nullptr, nullptr, y, pl.T, pl.K, pl.N, pl.r, pl.r_pad,
-               gemv_ks(pl.T, pl.K), pl.r ? gemv_kl(pl.K) : 0, 0, scaling};
+               gemv_ks(pl.K), pl.r ? gemv_kl(pl.K) : 0, 0, scaling};
     a.part = reinterpret_cast<float*>(ws);
     a.lpart = reinterpret_cast<float*>(ws + align256((size_t)a.KS * pl.T * pl.N * 4));
+    a.gemv_blocks = (int)ceil_div(pl.N, kDecRows) * a.KS;
     const Codebook& cb = host_codebook();
-    const dim3 block(256);
     const int lora_blocks = pl.r ? (int)(pl.r_pad / 64) * a.KL : 0;
+    const dim3 grid((unsigned)(a.gemv_blocks + lora_blocks));
     hipError_t ae = hipSuccess;
-    auto go = [&](auto kern, int R, int KR, int TT) {
-        a.gemv_blocks = (int)ceil_div(pl.N, R) * a.KS;
-        const size_t lds = 2048 + (size_t)TT * KR * 2;           // up to 66 KB: above the default limit
+    auto go = [&](auto kern) {
+        // 64 KB of dynamic LDS: above the default limit
         ae = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)lds);
-        if (ae == hipSuccess)
-            hipLaunchKernelGGL(kern, dim3((unsigned)(a.gemv_blocks + lora_blocks)), block, lds, s, a, cb);
+                                 (int)kDecLds);
+        if (ae == hipSuccess) hipLaunchKernelGGL(kern, grid, dim3(kDecThreads), kDecLds, s, a, cb);
     };
-    if (pl.T <= 1) go(k_gemv<1>, gemv_rows<1>(), gemv_round<1>(), 1);
-    else if (pl.T <= 2) go(k_gemv<2>, gemv_rows<2>(), gemv_round<2>(), 2);
-    else if (pl.T <= 4) go(k_gemv<4>, gemv_rows<4>(), gemv_round<4>(), 4);
-    else if (pl.T <= 8) go(k_gemv<8>, gemv_rows<8>(), gemv_round<8>(), 8);
-    else go(k_gemv<16>, gemv_rows<16>(), gemv_round<16>(), 16);
+    if (pl.T <= 1) go(k_gemv<1>);
+    else if (pl.T <= 2) go(k_gemv<2>);
+    else if (pl.T <= 4) go(k_gemv<4>);
+    else if (pl.T <= 8) go(k_gemv<8>);
+    else go(k_gemv<16>);
     if (ae != hipSuccess) return ae;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 fg((unsigned)ceil_div(pl.N, kFinCols));
+    const dim3 fg((unsigned)ceil_div(pl.N, kFinCols)), fb(256);
     switch (pl.r_pad / 64) {
-        case 0: hipLaunchKernelGGL(k_gemv_finalize<0>, fg, block, 0, s, a); break;
-        case 1: hipLaunchKernelGGL(k_gemv_finalize<1>, fg, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(k_gemv_finalize<2>, fg, block, 0, s, a); break;
-        case 3: hipLaunchKernelGGL(k_gemv_finalize<3>, fg, block, 0, s, a); break;
-        default: hipLaunchKernelGGL(k_gemv_finalize<4>, fg, block, 0, s, a); break;
+        case 0: hipLaunchKernelGGL(k_gemv_finalize<0>, fg, fb, 0, s, a); break;
+        case 1: hipLaunchKernelGGL(k_gemv_finalize<1>, fg, fb, 0, s, a); break;
+        case 2: hipLaunchKernelGGL(k_gemv_finalize<2>, fg, fb, 0, s, a); break;
+        case 3: hipLaunchKernelGGL(k_gemv_finalize<3>, fg, fb, 0, s, a); break;
+        default: hipLaunchKernelGGL(k_gemv_finalize<4>, fg, fb, 0, s, a); break;
     }
     return hipGetLastError();
 }

@@ -114,7 +114,10 @@ def test_bwd_validation(L):
 
 
 def test_workspace_bytes(L):
-    assert L.qlora_workspace_bytes(16, 4096, 4096, 0) == (4096 // 64) * 4096 * 4   # backward block scales
+    # the larger of the backward's block scales [K/64][N] fp32 and the decode
+    # path's split partials [K/512][T][N] fp32 (T <= 16, no adapter)
+    assert L.qlora_workspace_bytes(16, 4096, 4096, 0) == max((4096 // 64) * 4096 * 4, (4096 // 512) * 16 * 4096 * 4)
+    assert L.qlora_workspace_bytes(1, 4096, 4096, 0) == (4096 // 64) * 4096 * 4
     assert L.qlora_workspace_bytes(1 << 23, 4096, 4096, 16) == 0                     # T too large
     assert L.qlora_workspace_bytes(16, 100, 4096, 16) == 0
     a = L.qlora_workspace_bytes(4096, 4096, 11008, 64)

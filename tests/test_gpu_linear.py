@@ -77,7 +77,7 @@ def test_zero_weight_lora_only():
 
 
 def test_single_token_and_small_T():
-    for T in (1, 4, 8, 16):
+    for T in (1, 2, 3, 4, 8, 13, 16):
         _run_full(f"T={T}", synth.Linear("t", 384, 512), T=T, r=16, s=0.5)
 
 
