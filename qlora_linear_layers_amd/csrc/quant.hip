@@ -135,7 +135,9 @@ __global__ __launch_bounds__(256) void k_dequantize_dq(const uint32_t* __restric
                                                        const float* __restrict__ superscale,
                                                        int64_t nunits, u32x4_t* __restrict__ out, Codebook cb) {
     __shared__ float s_q[16];
-    if (threadIdx.x < 16) s_q[threadIdx.x] = cb.q[threadIdx.x];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        if (threadIdx.x == j) s_q[j] = cb_value(cb, j);     // constant indexes: no memory round trip
 
     const int64_t u0 = (int64_t)blockIdx.x * (256 * kDeqUnits) + threadIdx.x;
     uint32_t cv[kDeqUnits];
