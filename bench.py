@@ -99,13 +99,17 @@ def decode_bytes(lin, T, r):
     return storage_bytes(lin.N * lin.K) + 2 * T * lin.K + 2 * T * lin.N + 2 * r * (lin.K + lin.N)
 
 
-def measure_decode(api, torch, layers, qws, r, s, tokens=(1, 4, 8), copies=6, reps=10):
-    """Decode-size forward over the seven linears, rotating `copies` copies of the
-    quantized weights (about 100 MB each) so that the 256 MB last-level cache
-    cannot serve repeats.  Returns {T: (seconds per layer set, bytes per layer set)}."""
-    import numpy as np
-    sets = [[api.NF4Weight(q.codes.clone(), q.absmax_fp8.clone(), q.superscale.clone(), q.N, q.K) for q in qws]
+def weight_copies(api, qws, copies=6):
+    """`copies` copies of the quantized weights of the seven linears (about 100 MB
+    each), rotated so that the 256 MB last-level cache cannot serve repeats."""
+    return [[api.NF4Weight(q.codes.clone(), q.absmax_fp8.clone(), q.superscale.clone(), q.N, q.K) for q in qws]
             for _ in range(copies)]
+
+
+def measure_decode(api, torch, layers, sets, r, s, tokens=(1, 4, 8), reps=10):
+    """Decode-size forward over the seven linears, one weight copy per pass.
+    Returns {T: (seconds per layer set, bytes per layer set)}."""
+    copies = len(sets)
     out = {}
     for T in tokens:
         g = torch.Generator(device="cuda").manual_seed(T)
@@ -131,6 +135,35 @@ def measure_decode(api, torch, layers, qws, r, s, tokens=(1, 4, 8), copies=6, re
         secs = ev[0].elapsed_time(ev[1]) / 1e3 / reps
         out[T] = (secs, sum(decode_bytes(l, T, r) for l in layers))
     return out
+
+
+def merge_bytes(lin, r):
+    """Algorithmic bytes of one LoRA merge: the packed weight and the adapters in, bf16 W_m out."""
+    return storage_bytes(lin.N * lin.K) + 2 * lin.N * lin.K + 2 * r * (lin.K + lin.N)
+
+
+def measure_merge(api, torch, layers, sets, r, s, reps=6):
+    """W_m = RNE_bf16(W' + s (A B)^T) for the seven linears, one weight copy per pass
+    (the 405 MB of outputs are written once per pass).  Returns (seconds, bytes) per layer set."""
+    copies = len(sets)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = [torch.randn((l.K, r), generator=g, device="cuda").mul_(0.01).to(torch.bfloat16) for l in layers]
+    b = [torch.randn((r, l.N), generator=g, device="cuda").mul_(0.01).to(torch.bfloat16) for l in layers]
+    outs = [torch.empty((l.N, l.K), dtype=torch.bfloat16, device="cuda") for l in layers]
+
+    def one(c):
+        for i in range(len(layers)):
+            api.qlora_merge_lora(sets[c][i], a[i], b[i], s, out=outs[i])
+    for c in range(copies):
+        one(c)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for k in range(reps):
+        one(k % copies)
+    ev[1].record()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / 1e3 / reps, sum(merge_bytes(l, r) for l in layers)
 
 
 def cpu_baseline(layers, T, r, s, t_sample):
@@ -297,12 +330,18 @@ def main():
         "components": comp,
         "roofline": roofline,
     }
-    dec = measure_decode(api, torch, layers, [b["qw"] for b in bufs], r, s)
+    sets = weight_copies(api, [b["qw"] for b in bufs])
+    dec = measure_decode(api, torch, layers, sets, r, s)
     for Td, (secs, nbytes) in dec.items():
         comp[f"decode_T{Td}"] = {"GB/s": round(nbytes / secs / 1e9, 1),
                                  "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
                                  "us_per_layer_set": round(1e6 * secs, 2),
                                  "note": "7 linears, fused dequant + small-M MFMA (16x16x32) incl. LoRA; weights rotated over 6 copies"}
+    secs, nbytes = measure_merge(api, torch, layers, sets, r, s)
+    comp["merge"] = {"GB/s": round(nbytes / secs / 1e9, 1), "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
+                     "us_per_layer_set": round(1e6 * secs, 2),
+                     "note": "7 linears, W_m = RNE_bf16(W' + s (A B)^T), r=64; weights rotated over 6 copies"}
+    del sets
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, T, r, s, args.cpu_tokens)
     print(json.dumps(out), flush=True)

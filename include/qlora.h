@@ -164,6 +164,27 @@ int qlora_linear_bwd_input(const uint16_t* dy, int64_t T, int64_t K, int64_t N,
                            uint16_t* d_lora_a, uint16_t* d_lora_b,
                            void* workspace, size_t workspace_bytes, unsigned flags, void* stream);
 
+/*
+ * qlora_merge_lora - the adapted layer's weight, merged back into bf16.
+ *   Source: "QLoRA 原理精讲" section 2.5 (after merging, inference runs at the
+ *   base model's speed: the adapter merges back into BF16 weights) and
+ *   section 3, pitfall 3 (deployment from the merged BF16 weights).  Since
+ *   X W'^T + s (X A) B = X (W' + s (A B)^T)^T, the merged weight is
+ *     W_m[n][k] = RNE_bf16(W'[n][k] + scaling * sum_j A[k][j] B[j][n]),
+ *   with W' the double-dequantized bf16 weight (the values nf4_dequantize_dq
+ *   writes), the rank-r sum accumulated in fp32 and added to W' by one fused
+ *   multiply-add before the single rounding.
+ *   codes/absmax_fp8/superscale: W [N, K] quantized as above (device), read;
+ *   lora_a [K, r] bf16 and lora_b [r, N] bf16 (device), read (both NULL iff
+ *   r == 0, which writes W' itself); w_out [N, K] bf16 (device), written.
+ *   K a multiple of 64, N a multiple of 8, r = 0 or a multiple of 8 up to 256,
+ *   K, N <= 2^20, N*K < 2^32.  Needs no workspace.
+ *   Errors: NULL, SHAPE, ALIGN, VALUE (non-finite scaling), DEVICE.
+ */
+int qlora_merge_lora(const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale,
+                     int64_t K, int64_t N, const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
+                     float scaling, uint16_t* w_out, void* stream);
+
 /* qlora_status_string - static, NUL-terminated description of a status code. */
 const char* qlora_status_string(int status);
 

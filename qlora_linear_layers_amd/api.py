@@ -26,6 +26,8 @@ _SIGS = {
     "qlora_linear_bwd_input": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                               ctypes.c_float, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t,
                                               ctypes.c_uint, _c_p]),
+    "qlora_merge_lora": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, ctypes.c_float, _c_p,
+                                        _c_p]),
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 EXPORTS = tuple(_SIGS)
@@ -185,3 +187,17 @@ def qlora_linear_bwd_input(dy, qw, lora_a=None, lora_b=None, scaling=1.0, x=None
         _ptr(d_lora_b) if lora_grads else None, _ptr(workspace), workspace.numel(),
         REUSE_FORWARD if reuse_forward else 0, _stream()))
     return (dx, d_lora_a, d_lora_b) if lora_grads else (dx, None, None)
+
+
+def qlora_merge_lora(qw, lora_a=None, lora_b=None, scaling=1.0, out=None):
+    """W_m = RNE_bf16(W' + scaling (A B)^T) -> bf16 [N, K] (W' itself without an adapter)."""
+    _dev(lora_a, torch.bfloat16, "lora_a")
+    _dev(lora_b, torch.bfloat16, "lora_b")
+    r = 0 if lora_a is None else lora_a.shape[1]
+    if out is None:
+        out = torch.empty((qw.N, qw.K), dtype=torch.bfloat16, device=qw.codes.device)
+    _dev(out, torch.bfloat16, "out")
+    _check("qlora_merge_lora", lib().qlora_merge_lora(
+        _ptr(qw.codes), _ptr(qw.absmax_fp8), _ptr(qw.superscale), qw.K, qw.N, _ptr(lora_a), _ptr(lora_b), r,
+        float(scaling), _ptr(out), _stream()))
+    return out

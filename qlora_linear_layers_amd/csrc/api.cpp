@@ -157,4 +157,20 @@ int qlora_linear_bwd_input(const uint16_t* dy, int64_t T, int64_t K, int64_t N, 
     return QLORA_OK;
 }
 
+int qlora_merge_lora(const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale, int64_t K, int64_t N,
+                     const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling, uint16_t* w_out,
+                     void* stream) {
+    if (!codes || !absmax_fp8 || !superscale || !w_out) return QLORA_ERR_NULL;
+    if (r > 0 && (!lora_a || !lora_b)) return QLORA_ERR_NULL;
+    if (K < 64 || K % 64 || N < 8 || N % 8 || K > (int64_t(1) << 20) || N > (int64_t(1) << 20) || N * K >= (int64_t(1) << 32))
+        return QLORA_ERR_SHAPE;
+    if (r < 0 || r > QLORA_MAX_RANK || r % 8 || (r == 0 && (lora_a || lora_b))) return QLORA_ERR_SHAPE;
+    const void* ptrs[] = {codes, absmax_fp8, superscale, lora_a, lora_b, w_out};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
+    if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
+    return dev(ql::launch_merge(codes, absmax_fp8, superscale, lora_a, lora_b, K, N, r, scaling, w_out,
+                                static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

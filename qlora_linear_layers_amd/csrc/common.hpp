@@ -177,6 +177,9 @@ QL_DEV rsrc_t make_rsrc(const void* base, int64_t bytes) {
 QL_DEV u32x4_t bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+QL_DEV u32x2_t bload8(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
 QL_DEV uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
@@ -198,6 +201,9 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* fp8, const flo
 constexpr int64_t kGemvMaxT = 16;
 struct LoraPlan;
 size_t gemv_workspace(int64_t T, int64_t K, int64_t N, int64_t r_pad);
+hipError_t launch_merge(const uint8_t* codes, const uint8_t* fp8, const float* sup, const uint16_t* lora_a,
+                        const uint16_t* lora_b, int64_t K, int64_t N, int64_t r, float scaling, uint16_t* w_out,
+                        hipStream_t s);
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, const uint8_t* fp8, const float* sup,
                        const uint16_t* lora_a, const uint16_t* lora_b, float scaling, const LoraPlan& pl,
                        uint8_t* ws, uint16_t* y, hipStream_t s);

@@ -1,0 +1,180 @@
+// LoRA merge: W_m[n][k] = RNE_bf16(W'[n][k] + s sum_j A[k][j] B[j][n]), the
+// adapted layer's weight in bf16 ("QLoRA 原理精讲" section 2.5 and section 3,
+// pitfall 3: after training the adapter can be merged back into BF16 weights).
+// W' = RNE_bf16(fl32(q[code] * c1')) with c1' = fl32(e4m3(f) * s2), the same
+// values nf4_dequantize_dq writes.  The rank-r product is accumulated in fp32
+// on MFMA and added to W' with one fused multiply-add before the rounding.
+//
+// HBM-bound: 0.516 bytes of codes and constants in and 2 bytes out per
+// weight; A and B are small and re-read from L2.
+//
+// Workgroup: 64 rows n x 256 k, four waves of 64 k.  B's 64 columns of the
+// workgroup are staged transposed in LDS ([n][j], XOR-swizzled 64-wide j
+// blocks), so both MFMA operands are 16-byte fragment reads.  Each wave runs
+// v_mfma_f32_16x16x32_bf16 with the A operand = rows of A (index k) and the B
+// operand = columns of B^T's transpose (index n), 4 x 4 tiles of 16 k x 16 n.
+// The k of MFMA row m in row tile t is 16 (m / 4) + 4 t + (m % 4): the
+// accumulator rows a lane holds (4 (lane / 16) + v in every tile) then cover
+// 16 consecutive k of one row n, so the epilogue is one 8-byte code load,
+// 16 dequantized weights and two 16-byte stores per (lane, n tile), straight
+// from the accumulators.
+#include "common.hpp"
+#include "plan.hpp"
+
+namespace ql {
+
+namespace {
+
+typedef __bf16 bf16x8m_t __attribute__((ext_vector_type(8)));
+
+struct MergeArgs {
+    const uint8_t* codes;
+    const uint8_t* fp8;
+    const float* sup;
+    const uint16_t* a;    // [K][r]
+    const uint16_t* b;    // [r][N]
+    uint16_t* w;          // [N][K]
+    int64_t K, N, r;
+    float s;
+};
+
+constexpr int kMergeRows = 64;    // n per workgroup
+constexpr int kMergeK = 256;      // k per workgroup (64 per wave)
+
+// RP = r_pad / 64 (1..4): B^T is RP swizzled [64 n][64 j] tiles of 8 KB
+template <int RP>
+__global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
+    __shared__ float s_q[16];
+    __shared__ __align__(16) uint8_t s_bt[RP * 8192];
+    lds8_t* bt = (lds8_t*)s_bt;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nl = lane & 15, q = lane >> 4;
+    const int nb = (int)ceil_div(p.N, kMergeRows);
+    const int rb = (int)blockIdx.x % nb, kb = (int)blockIdx.x / nb;
+    const int64_t n0 = (int64_t)rb * kMergeRows;
+    const int64_t k0 = (int64_t)kb * kMergeK + 64 * wave;             // this wave's 64 k (one block per row)
+    const bool kok = k0 < p.K;                                         // K % 64 == 0: all 64 or none
+    const rsrc_t rc = make_rsrc(p.codes, p.N * p.K / 2);
+    const rsrc_t rf = make_rsrc(p.fp8, p.N * p.K / 64);
+    const rsrc_t rs = make_rsrc(p.sup, ceil_div(p.N * p.K / 64, 256) * 4);
+    const rsrc_t ra = make_rsrc(p.a, p.K * p.r * 2);
+    const rsrc_t rbm = make_rsrc(p.b, p.r * p.N * 2);
+
+    // epilogue loads first: for n tile c, row n0 + 16c + nl, k0 + 16q .. +15
+    u32x2_t cw[4];
+    uint32_t f8[4], s2[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int64_t n = n0 + 16 * c + nl;
+        const bool ok = kok && n < p.N;
+        const int64_t blk = n * (p.K / 64) + k0 / 64;
+        cw[c] = bload8(rc, ok ? (uint32_t)(n * (p.K / 2) + (k0 + 16 * q) / 2) : kOOB, 0);
+        f8[c] = bload1(rf, ok ? (uint32_t)blk : kOOB, 0);
+        s2[c] = bload4(rs, ok ? (uint32_t)(blk >> 8) * 4u : kOOB, 0);
+    }
+
+    // A fragments of the first kPre rank steps, before the barrier (A operand
+    // row of this lane in tile t: m = nl -> k = 16 (m / 4) + 4 t + m % 4)
+    constexpr int kSteps = RP * 2, kPre = kSteps < 4 ? kSteps : 4;
+    auto a_frag = [&](int js, int t) -> u32x4_t {
+        const int j = 32 * js + 8 * q;                                 // this lane's 8 ranks
+        const int64_t k = k0 + 16 * (nl >> 2) + 4 * t + (nl & 3);
+        return bload16(ra, (kok && j < p.r) ? (uint32_t)((k * p.r + j) * 2) : kOOB, 0);
+    };
+    u32x4_t apre[kPre][4];
+#pragma unroll
+    for (int js = 0; js < kPre; ++js)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) apre[js][t] = a_frag(js, t);
+
+    // stage B^T: thread takes 16 bytes of row j of B (8 columns; N % 8 == 0
+    // keeps them inside the row and 16-byte aligned) and writes them down
+    // column j of the transposed tile; ranks j >= r and columns n >= N are zeros
+#pragma unroll
+    for (int i = 0; i < RP * 2; ++i) {
+        const int ch = (int)threadIdx.x + 256 * i;                      // RP * 64 rows j x 8 chunks
+        const int j = ch >> 3, nc = ch & 7;
+        const int64_t n = n0 + 8 * nc;
+        const u32x4_t v = bload16(rbm, (j < p.r && n < p.N) ? (uint32_t)((j * p.N + n) * 2) : kOOB, 0);
+        lds8_t* tile = bt + (j >> 6) * 8192 + ((j & 7) * 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint16_t h = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            *reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(
+                tile + lds_off(8 * nc + e, (j & 63) >> 3)) = h;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        if (threadIdx.x == j) s_q[j] = cb_value(cb, j);
+    __syncthreads();
+
+    // rank-r product: acc[t][c] = 16 k x 16 n tile, 32 ranks per MFMA
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[t][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int js = 0; js < kSteps; ++js) {
+        u32x4_t af[4], bf[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) af[t] = js < kPre ? apre[js < kPre ? js : 0][t] : a_frag(js, t);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            bf[c] = *reinterpret_cast<const lds_u32x4_t*>(bt + (js >> 1) * 8192 +
+                                                          lds_off(16 * c + nl, ((js & 1) << 2) + q));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8m_t, af[t]),
+                                                                    __builtin_bit_cast(bf16x8m_t, bf[c]),
+                                                                    acc[t][c], 0, 0, 0);
+    }
+
+    // epilogue: lane holds k0 + 16q + 4t + v of row n0 + 16c + nl in acc[t][c][v]
+    const float sc = p.s;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int64_t n = n0 + 16 * c + nl;
+        const float c1p = block_scale(f8[c], __uint_as_float(s2[c]));
+        u32x4_t o[2];
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb) {                               // code byte bb: k 2bb (high nibble), 2bb + 1
+            const uint32_t byte = (cw[c][bb >> 2] >> (8 * (bb & 3))) & 0xFFu;
+            const uint32_t wq = pack_bf16x2(__fmul_rn(s_q[byte >> 4], c1p), __fmul_rn(s_q[byte & 15u], c1p));
+            const int e = 2 * bb;                                      // element index 4t + v
+            const float m0 = fmaf(sc, acc[e >> 2][c][e & 3], bf16lo(wq));
+            const float m1 = fmaf(sc, acc[(e + 1) >> 2][c][(e + 1) & 3], bf16hi(wq));
+            o[bb >> 2][bb & 3] = pack_bf16x2(m0, m1);
+        }
+        if (kok && n < p.N) {
+            // streamed once: non-temporal stores keep it from displacing A and B in the caches
+            u32x4_t* dst = reinterpret_cast<u32x4_t*>(p.w + n * p.K + k0 + 16 * q);
+            __builtin_nontemporal_store(o[0], dst);
+            __builtin_nontemporal_store(o[1], dst + 1);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const uint8_t* codes, const uint8_t* fp8, const float* sup, const uint16_t* lora_a,
+                        const uint16_t* lora_b, int64_t K, int64_t N, int64_t r, float scaling, uint16_t* w_out,
+                        hipStream_t s) {
+    if (r == 0) return launch_dequantize(codes, fp8, sup, N * K, w_out, s);
+    const MergeArgs a{codes, fp8, sup, lora_a, lora_b, w_out, K, N, r, scaling};
+    const dim3 grid((unsigned)(ceil_div(N, kMergeRows) * ceil_div(K, kMergeK))), block(256);
+    const Codebook& cb = host_codebook();
+    switch ((int)ceil_div(r, 64)) {
+        case 1: hipLaunchKernelGGL(k_merge<1>, grid, block, 0, s, a, cb); break;
+        case 2: hipLaunchKernelGGL(k_merge<2>, grid, block, 0, s, a, cb); break;
+        case 3: hipLaunchKernelGGL(k_merge<3>, grid, block, 0, s, a, cb); break;
+        default: hipLaunchKernelGGL(k_merge<4>, grid, block, 0, s, a, cb); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ql

@@ -123,3 +123,24 @@ def test_workspace_bytes(L):
     a = L.qlora_workspace_bytes(4096, 4096, 11008, 64)
     b = L.qlora_workspace_bytes(4096, 4096, 11008, 16)
     assert a > 0 and b > 0 and a % 256 == 0
+
+
+def _merge(L, codes=FAKE, f=FAKE, s2=FAKE, K=128, N=64, la=FAKE, lb=FAKE, r=16, s=0.5, w=FAKE):
+    return L.qlora_merge_lora(codes, f, s2, K, N, la, lb, r, s, w, None)
+
+
+def test_merge_validation(L):
+    assert _merge(L, codes=None) == NULL
+    assert _merge(L, w=None) == NULL
+    assert _merge(L, la=None) == NULL              # adapter half missing with r > 0
+    assert _merge(L, K=100) == SHAPE               # K not a multiple of 64
+    assert _merge(L, N=0) == SHAPE
+    assert _merge(L, N=100) == SHAPE             # N not a multiple of 8
+    assert _merge(L, r=12) == SHAPE                # r not a multiple of 8
+    assert _merge(L, r=264) == SHAPE               # above the rank limit
+    assert _merge(L, r=0) == SHAPE                 # adapter pointers given with r = 0
+    assert _merge(L, K=1 << 21) == SHAPE
+    assert _merge(L, K=1 << 20, N=1 << 12) == SHAPE   # N*K = 2^32
+    assert _merge(L, w=MIS) == ALIGN
+    assert _merge(L, lb=MIS) == ALIGN
+    assert _merge(L, s=math.nan) == VALUE
