@@ -35,6 +35,7 @@ from .quant import (
     e4m3fn_values, e4m3fn_encode, e4m3fn_decode,
     double_quantize, double_dequantize_scales,
     quantize_nf4_dq, dequantize_nf4_dq, dequantize_rows, storage_bytes,
+    quantize_nf4_sq, dequantize_nf4_sq, dequantize_rows_sq, storage_bytes_sq,
 )
 from .linear import (
     linear_fwd, linear_bwd, linear_fwd_f64, linear_bwd_f64, linear_fwd_at, linear_bwd_dx_at,

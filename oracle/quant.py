@@ -193,3 +193,45 @@ def dequantize_rows(packed, fp8_codes, supers, N, K, rows):
 def storage_bytes(numel):
     """Bytes of the storage triple: 4-bit codes + one FP8 code per 64 + one fp32 per 64*256."""
     return numel // 2 + numel // BLOCK + 4 * (-(-numel // (BLOCK * GROUP)))
+
+
+# ---------------------------------------------------------------- single quantization
+#
+# The first level alone ("QLoRA 原理精讲", section 2.2, engineering motivation:
+# one fp32 scale per 64 weights, 32/64 = 0.5 bits of overhead per weight):
+# the same codes as above and the exact fp32 block absmax c1 kept as it is;
+# dequantization is w' = RNE_bf16(fl32(q[code] * c1)).
+
+def quantize_nf4_sq(w_bits):
+    """bf16 weight (uint16 bits, numel % 64 == 0) -> (packed codes uint8[numel/2], absmax fp32[numel/64])."""
+    w = bf16_bits_to_f32(np.asarray(w_bits, dtype=np.uint16).reshape(-1))
+    c1 = block_absmax(w)
+    return pack_codes(nf4_encode(w, c1)), c1
+
+
+def dequantize_nf4_sq(packed, absmax):
+    """(packed codes, fp32 absmax) -> bf16 bits (uint16[numel])."""
+    codes = unpack_codes(packed)
+    c1 = np.asarray(absmax, dtype=np.float32).reshape(-1)
+    if c1.size * BLOCK != codes.size:
+        raise ValueError("one absmax per 64 codes is required")
+    w = nf4_codebook()[codes].reshape(-1, BLOCK) * c1[:, None]      # fp32 multiply
+    return round_to_bf16_bits(w.astype(np.float64)).reshape(-1)
+
+
+def dequantize_rows_sq(packed, absmax, N, K, rows):
+    """Rows ``rows`` of the dequantized [N, K] weight (single quantization), bf16 bits [len(rows), K]."""
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 64")
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    bpr = K // BLOCK
+    packed = np.asarray(packed, dtype=np.uint8).reshape(N, K // 2)
+    c1 = np.asarray(absmax, dtype=np.float32).reshape(N, bpr)[rows]
+    codes = unpack_codes(packed[rows].reshape(-1)).reshape(len(rows), bpr, BLOCK)
+    w = nf4_codebook()[codes] * c1[..., None]
+    return round_to_bf16_bits(w.astype(np.float64)).reshape(len(rows), K)
+
+
+def storage_bytes_sq(numel):
+    """Bytes of the single-quantization pair: 4-bit codes + one fp32 per 64."""
+    return numel // 2 + 4 * (numel // BLOCK)

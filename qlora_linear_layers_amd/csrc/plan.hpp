@@ -14,14 +14,15 @@ constexpr int kTileSmall = 64;   // LoRA rank padding
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Token split of an adapter-gradient product over C columns: about 256
-// workgroups (128 columns x 64 ranks each), each wave taking `cpw` chunks of
-// 32 tokens; returns the number of splits (fp32 partials).
+// Token split of an adapter-gradient product over C columns: at most 256
+// workgroups (128 columns x 64 ranks each, one per CU at a time) so that the
+// grid runs in one round, each wave taking `cpw` chunks of 32 tokens; returns
+// the number of splits (fp32 partials).
 inline int grad_splits(int64_t T, int64_t C, int64_t r_pad, int& cpw) {
     const int64_t groups = ceil_div(C, 128) * (r_pad / 64);
-    const int64_t target = ceil_div(256, groups > 0 ? groups : 1);
-    int64_t c = T / (128 * target);
-    cpw = (int)(c < 1 ? 1 : c);
+    int64_t target = 256 / (groups > 0 ? groups : 1);
+    if (target < 1) target = 1;
+    cpw = (int)ceil_div(T, 128 * target);
     return (int)ceil_div(T, 128 * (int64_t)cpw);
 }
 
