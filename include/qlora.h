@@ -185,6 +185,37 @@ int qlora_merge_lora(const uint8_t* codes, const uint8_t* absmax_fp8, const floa
                      int64_t K, int64_t N, const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
                      float scaling, uint16_t* w_out, void* stream);
 
+/*
+ * Single quantization (no double quantization).
+ *   Source: "QLoRA 原理精讲" section 2.2, its engineering motivation: the first
+ *   level alone keeps one fp32 scale per 64 weights (32/64 = 0.5 bit of
+ *   overhead per weight, against about 0.127 bit with the second level).  The
+ *   codes are those of nf4_quantize_dq (same absmax, same nearest-codeword
+ *   rule); the block constant is the exact fp32 absmax c1 itself, and
+ *   dequantization is w' = RNE_bf16(fl32(q[code] * c1)).  Storage of W with
+ *   numel = N*K elements:
+ *       codes   uint8 [numel/2]   as above
+ *       absmax  float [numel/64]  fp32 absmax of each block
+ *   Every _sq entry point takes `absmax` in place of the pair
+ *   (absmax_fp8, superscale) and otherwise has the arguments, sizes, workspace
+ *   and errors of the entry point it is named after.
+ */
+int nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, void* stream);
+int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t numel, uint16_t* w_out, void* stream);
+int qlora_linear_fwd_sq(const uint16_t* x, int64_t T, int64_t K, int64_t N,
+                        const uint8_t* codes, const float* absmax,
+                        const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling,
+                        uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+int qlora_linear_bwd_input_sq(const uint16_t* dy, int64_t T, int64_t K, int64_t N,
+                              const uint8_t* codes, const float* absmax,
+                              const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling,
+                              uint16_t* dx, const uint16_t* x,
+                              uint16_t* d_lora_a, uint16_t* d_lora_b,
+                              void* workspace, size_t workspace_bytes, unsigned flags, void* stream);
+int qlora_merge_lora_sq(const uint8_t* codes, const float* absmax, int64_t K, int64_t N,
+                        const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
+                        float scaling, uint16_t* w_out, void* stream);
+
 /* qlora_status_string - static, NUL-terminated description of a status code. */
 const char* qlora_status_string(int status);
 

@@ -28,6 +28,15 @@ _SIGS = {
                                               ctypes.c_uint, _c_p]),
     "qlora_merge_lora": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, ctypes.c_float, _c_p,
                                         _c_p]),
+    "nf4_quantize": (ctypes.c_int, [_c_p, _c_i64, _c_p, _c_p, _c_p]),
+    "nf4_dequantize": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_p, _c_p]),
+    "qlora_linear_fwd_sq": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                                           ctypes.c_float, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "qlora_linear_bwd_input_sq": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                                                 ctypes.c_float, _c_p, _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t,
+                                                 ctypes.c_uint, _c_p]),
+    "qlora_merge_lora_sq": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, ctypes.c_float, _c_p,
+                                           _c_p]),
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 EXPORTS = tuple(_SIGS)
@@ -99,6 +108,22 @@ class NF4Weight:
         return self.codes.numel() + self.absmax_fp8.numel() + 4 * self.superscale.numel()
 
 
+@dataclass
+class NF4WeightSQ:
+    """Single-quantization pair of an [N, K] weight (device tensors): no second level."""
+    codes: torch.Tensor       # uint8 [N*K/2]
+    absmax: torch.Tensor      # float32 [N*K/64]
+    N: int
+    K: int
+
+    @property
+    def numel(self):
+        return self.N * self.K
+
+    def nbytes(self):
+        return self.codes.numel() + 4 * self.absmax.numel()
+
+
 def nf4_build_codebook():
     out = (ctypes.c_float * 16)()
     _check("nf4_build_codebook", lib().nf4_build_codebook(out))
@@ -134,6 +159,33 @@ def nf4_dequantize_dq(qw, out=None):
     return out
 
 
+def nf4_quantize(w):
+    """bf16 weight [N, K] (or flat) on the GPU -> NF4WeightSQ (single quantization)."""
+    _dev(w, torch.bfloat16, "w")
+    numel = w.numel()
+    N, K = (w.shape[0], w.shape[1]) if w.dim() == 2 else (1, numel)
+    codes = torch.empty(numel // 2, dtype=torch.uint8, device=w.device)
+    absmax = torch.empty(max(numel // 64, 1), dtype=torch.float32, device=w.device)
+    _check("nf4_quantize", lib().nf4_quantize(_ptr(w), numel, _ptr(codes), _ptr(absmax), _stream()))
+    return NF4WeightSQ(codes, absmax, N, K)
+
+
+def nf4_dequantize(qw, out=None):
+    """NF4WeightSQ -> bf16 [N, K] on the GPU."""
+    if out is None:
+        out = torch.empty((qw.N, qw.K), dtype=torch.bfloat16, device=qw.codes.device)
+    _dev(out, torch.bfloat16, "out")
+    _check("nf4_dequantize", lib().nf4_dequantize(_ptr(qw.codes), _ptr(qw.absmax), qw.numel, _ptr(out), _stream()))
+    return out
+
+
+def _scale_args(qw):
+    """(entry-point suffix, block-constant pointers) of either storage format."""
+    if isinstance(qw, NF4WeightSQ):
+        return "_sq", (_ptr(qw.absmax),)
+    return "", (_ptr(qw.absmax_fp8), _ptr(qw.superscale))
+
+
 def qlora_workspace_bytes(T, K, N, r):
     return int(lib().qlora_workspace_bytes(T, K, N, r))
 
@@ -144,7 +196,8 @@ def workspace_for(T, K, N, r, device):
 
 
 def qlora_linear_fwd(x, qw, lora_a=None, lora_b=None, scaling=1.0, workspace=None, out=None):
-    """Y = X W'^T + scaling (X A) B; x [T, K] bf16 -> y [T, N] bf16."""
+    """Y = X W'^T + scaling (X A) B; x [T, K] bf16 -> y [T, N] bf16.  `qw` is an NF4Weight
+    (double quantization) or an NF4WeightSQ (single quantization, the _sq entry point)."""
     _dev(x, torch.bfloat16, "x")
     _dev(lora_a, torch.bfloat16, "lora_a")
     _dev(lora_b, torch.bfloat16, "lora_b")
@@ -154,8 +207,10 @@ def qlora_linear_fwd(x, qw, lora_a=None, lora_b=None, scaling=1.0, workspace=Non
         out = torch.empty((T, qw.N), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
         workspace = workspace_for(T, K, qw.N, r, x.device)
-    _check("qlora_linear_fwd", lib().qlora_linear_fwd(
-        _ptr(x), T, K, qw.N, _ptr(qw.codes), _ptr(qw.absmax_fp8), _ptr(qw.superscale), _ptr(lora_a), _ptr(lora_b),
+    sfx, sc = _scale_args(qw)
+    fn = "qlora_linear_fwd" + sfx
+    _check(fn, getattr(lib(), fn)(
+        _ptr(x), T, K, qw.N, _ptr(qw.codes), *sc, _ptr(lora_a), _ptr(lora_b),
         r, float(scaling), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
     return out
 
@@ -181,8 +236,10 @@ def qlora_linear_bwd_input(dy, qw, lora_a=None, lora_b=None, scaling=1.0, x=None
             d_lora_b = torch.empty((r, N), dtype=torch.bfloat16, device=dy.device)
     if workspace is None:
         workspace = workspace_for(T, K, N, r, dy.device)
-    _check("qlora_linear_bwd_input", lib().qlora_linear_bwd_input(
-        _ptr(dy), T, K, N, _ptr(qw.codes), _ptr(qw.absmax_fp8), _ptr(qw.superscale), _ptr(lora_a), _ptr(lora_b),
+    sfx, sc = _scale_args(qw)
+    fn = "qlora_linear_bwd_input" + sfx
+    _check(fn, getattr(lib(), fn)(
+        _ptr(dy), T, K, N, _ptr(qw.codes), *sc, _ptr(lora_a), _ptr(lora_b),
         r, float(scaling), _ptr(dx), _ptr(x), _ptr(d_lora_a) if lora_grads else None,
         _ptr(d_lora_b) if lora_grads else None, _ptr(workspace), workspace.numel(),
         REUSE_FORWARD if reuse_forward else 0, _stream()))
@@ -197,7 +254,26 @@ def qlora_merge_lora(qw, lora_a=None, lora_b=None, scaling=1.0, out=None):
     if out is None:
         out = torch.empty((qw.N, qw.K), dtype=torch.bfloat16, device=qw.codes.device)
     _dev(out, torch.bfloat16, "out")
-    _check("qlora_merge_lora", lib().qlora_merge_lora(
-        _ptr(qw.codes), _ptr(qw.absmax_fp8), _ptr(qw.superscale), qw.K, qw.N, _ptr(lora_a), _ptr(lora_b), r,
-        float(scaling), _ptr(out), _stream()))
+    sfx, sc = _scale_args(qw)
+    fn = "qlora_merge_lora" + sfx
+    _check(fn, getattr(lib(), fn)(
+        _ptr(qw.codes), *sc, qw.K, qw.N, _ptr(lora_a), _ptr(lora_b), r, float(scaling), _ptr(out), _stream()))
     return out
+
+
+# The _sq entry points under their C names (the wrappers above pick them for an NF4WeightSQ).
+def qlora_linear_fwd_sq(x, qw, lora_a=None, lora_b=None, scaling=1.0, workspace=None, out=None):
+    assert isinstance(qw, NF4WeightSQ)
+    return qlora_linear_fwd(x, qw, lora_a, lora_b, scaling, workspace, out)
+
+
+def qlora_linear_bwd_input_sq(dy, qw, lora_a=None, lora_b=None, scaling=1.0, x=None, lora_grads=False,
+                              workspace=None, dx=None, d_lora_a=None, d_lora_b=None, reuse_forward=False):
+    assert isinstance(qw, NF4WeightSQ)
+    return qlora_linear_bwd_input(dy, qw, lora_a, lora_b, scaling, x, lora_grads, workspace, dx, d_lora_a, d_lora_b,
+                                  reuse_forward)
+
+
+def qlora_merge_lora_sq(qw, lora_a=None, lora_b=None, scaling=1.0, out=None):
+    assert isinstance(qw, NF4WeightSQ)
+    return qlora_merge_lora(qw, lora_a, lora_b, scaling, out)

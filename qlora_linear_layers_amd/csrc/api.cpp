@@ -13,10 +13,10 @@ hipError_t launch_lora_down_x(const uint16_t* x, float scaling, const LoraPlan& 
                               hipStream_t s);
 hipError_t launch_lora_down_dy(const uint16_t* dy, const uint16_t* lora_b, float scaling, const LoraPlan& pl,
                                uint8_t* ws, bool transposed, hipStream_t s);
-hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* fp8, const float* sup,
-                      const uint16_t* lora_b, const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s);
-hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* fp8, const float* sup,
-                     const uint16_t* lora_a, const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s);
+hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, BlockScales sc, const uint16_t* lora_b,
+                      const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s);
+hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
+                     const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s);
 hipError_t launch_lora_grads(const uint16_t* x, const uint16_t* dy, const LoraPlan& pl, uint8_t* ws,
                              uint16_t* d_lora_a, uint16_t* d_lora_b, hipStream_t s);
 }  // namespace ql
@@ -36,6 +36,103 @@ int check_linear_shape(int64_t T, int64_t K, int64_t N, int64_t r) {
     if (T * K > (int64_t(1) << 30) || T * N > (int64_t(1) << 30) || N * K >= (int64_t(1) << 32))
         return QLORA_ERR_SHAPE;
     return QLORA_OK;
+}
+
+// Block constants as the entry points receive them: the double-quantized pair
+// or (for the _sq entry points) one fp32 absmax per block.  A missing array is
+// a NULL error; a present one must be 16-byte aligned like every pointer.
+ql::BlockScales dq_scales(const uint8_t* fp8, const float* sup) { return {fp8, sup, nullptr}; }
+ql::BlockScales sq_scales(const float* absmax) { return {nullptr, nullptr, absmax}; }
+bool scales_present(const ql::BlockScales& sc) { return sc.absmax || (sc.fp8 && sc.sup); }
+bool scales_aligned(const ql::BlockScales& sc) {
+    return (!sc.fp8 || aligned16(sc.fp8)) && (!sc.sup || aligned16(sc.sup)) && (!sc.absmax || aligned16(sc.absmax));
+}
+
+int dequantize_impl(const uint8_t* codes, ql::BlockScales sc, int64_t numel, uint16_t* w_out, void* stream) {
+    if (!codes || !scales_present(sc) || !w_out) return QLORA_ERR_NULL;
+    if (numel <= 0 || numel % 64 || numel > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
+    if (!aligned16(w_out) || !aligned16(codes) || !scales_aligned(sc)) return QLORA_ERR_ALIGN;
+    return dev(ql::launch_dequantize(codes, sc, numel, w_out, static_cast<hipStream_t>(stream)));
+}
+
+int fwd_impl(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* codes, ql::BlockScales sc,
+             const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling, uint16_t* y, void* workspace,
+             size_t workspace_bytes, void* stream) {
+    if (!x || !codes || !scales_present(sc) || !y) return QLORA_ERR_NULL;
+    if (r > 0 && (!lora_a || !lora_b)) return QLORA_ERR_NULL;
+    if (int st = check_linear_shape(T, K, N, r)) return st;
+    if (r == 0 && (lora_a || lora_b)) return QLORA_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(codes) || !scales_aligned(sc) || !aligned16(y) ||
+        (lora_a && !aligned16(lora_a)) || (lora_b && !aligned16(lora_b)) || (workspace && !aligned16(workspace)))
+        return QLORA_ERR_ALIGN;
+    if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
+    const ql::LoraPlan pl(T, K, N, r);
+    const size_t need = T <= ql::kGemvMaxT ? ql::gemv_workspace(T, K, N, pl.r_pad) : pl.fwd_bytes;
+    if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    if (T <= ql::kGemvMaxT)      // decode sizes: small-M MFMA, split-k partials
+        return dev(ql::launch_gemv(x, codes, sc, lora_a, lora_b, scaling, pl, ws, y, s));
+    if (r > 0) {
+        if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
+        // s X A in both layouts: the transposed copy lets a backward with
+        // QLORA_BWD_REUSE_FORWARD take the adapter gradients without recomputing it
+        if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, true, s))) return st;
+    }
+    return dev(ql::launch_fwd(x, codes, sc, lora_b, pl, ws, y, s));
+}
+
+int bwd_impl(const uint16_t* dy, int64_t T, int64_t K, int64_t N, const uint8_t* codes, ql::BlockScales sc,
+             const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling, uint16_t* dx, const uint16_t* x,
+             uint16_t* d_lora_a, uint16_t* d_lora_b, void* workspace, size_t workspace_bytes, unsigned flags,
+             void* stream) {
+    if (!dy || !codes || !scales_present(sc) || !dx) return QLORA_ERR_NULL;
+    if (r > 0 && (!lora_a || !lora_b)) return QLORA_ERR_NULL;
+    const bool grads = d_lora_a || d_lora_b;
+    if (grads && !x) return QLORA_ERR_NULL;
+    if (int st = check_linear_shape(T, K, N, r)) return st;
+    if (r == 0 && (lora_a || lora_b || grads)) return QLORA_ERR_SHAPE;
+    if (!scales_aligned(sc)) return QLORA_ERR_ALIGN;
+    const void* ptrs[] = {dy, codes, dx, x, lora_a, lora_b, d_lora_a, d_lora_b, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
+    if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
+    if (flags & ~(unsigned)QLORA_BWD_REUSE_FORWARD) return QLORA_ERR_VALUE;
+    const ql::LoraPlan pl(T, K, N, r);
+    const size_t need = grads ? pl.bwd_grad_bytes : pl.bwd_bytes;   // > 0: the scale pre-pass needs room
+    // s X A from the forward's workspace (only the MFMA forward, T > 16, leaves it there)
+    const bool reuse = (flags & QLORA_BWD_REUSE_FORWARD) && T > ql::kGemvMaxT;
+    if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    if (r > 0)
+        if (int st = dev(ql::launch_lora_down_dy(dy, lora_b, scaling, pl, ws, grads, s))) return st;
+    if (int st = dev(ql::launch_dx(dy, codes, sc, lora_a, pl, ws, dx, s))) return st;
+    if (grads) {
+        if (!reuse) {
+            if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
+            if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, true, s))) return st;
+        }
+        if (int st = dev(ql::launch_lora_grads(x, dy, pl, ws, d_lora_a, d_lora_b, s))) return st;
+    }
+    return QLORA_OK;
+}
+
+int merge_impl(const uint8_t* codes, ql::BlockScales sc, int64_t K, int64_t N, const uint16_t* lora_a,
+               const uint16_t* lora_b, int64_t r, float scaling, uint16_t* w_out, void* stream) {
+    if (!codes || !scales_present(sc) || !w_out) return QLORA_ERR_NULL;
+    if (r > 0 && (!lora_a || !lora_b)) return QLORA_ERR_NULL;
+    if (K < 64 || K % 64 || N < 8 || N % 8 || K > (int64_t(1) << 20) || N > (int64_t(1) << 20) || N * K >= (int64_t(1) << 32))
+        return QLORA_ERR_SHAPE;
+    if (r < 0 || r > QLORA_MAX_RANK || r % 8 || (r == 0 && (lora_a || lora_b))) return QLORA_ERR_SHAPE;
+    if (!scales_aligned(sc)) return QLORA_ERR_ALIGN;
+    const void* ptrs[] = {codes, lora_a, lora_b, w_out};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
+    if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
+    return dev(ql::launch_merge(codes, sc, lora_a, lora_b, K, N, r, scaling, w_out, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -73,11 +170,18 @@ int nf4_quantize_dq(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* a
 
 int nf4_dequantize_dq(const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale, int64_t numel,
                       uint16_t* w_out, void* stream) {
-    if (!codes || !absmax_fp8 || !superscale || !w_out) return QLORA_ERR_NULL;
+    return dequantize_impl(codes, dq_scales(absmax_fp8, superscale), numel, w_out, stream);
+}
+
+int nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, void* stream) {
+    if (!w || !codes || !absmax) return QLORA_ERR_NULL;
     if (numel <= 0 || numel % 64 || numel > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
-    if (!aligned16(w_out) || !aligned16(codes) || !aligned16(absmax_fp8) || !aligned16(superscale))
-        return QLORA_ERR_ALIGN;
-    return dev(ql::launch_dequantize(codes, absmax_fp8, superscale, numel, w_out, static_cast<hipStream_t>(stream)));
+    if (!aligned16(w) || !aligned16(codes) || !aligned16(absmax)) return QLORA_ERR_ALIGN;
+    return dev(ql::launch_quantize_sq(w, numel, codes, absmax, static_cast<hipStream_t>(stream)));
+}
+
+int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t numel, uint16_t* w_out, void* stream) {
+    return dequantize_impl(codes, sq_scales(absmax), numel, w_out, stream);
 }
 
 size_t qlora_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r) {
@@ -95,29 +199,15 @@ int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N, const u
                      const uint8_t* absmax_fp8, const float* superscale, const uint16_t* lora_a,
                      const uint16_t* lora_b, int64_t r, float scaling, uint16_t* y, void* workspace,
                      size_t workspace_bytes, void* stream) {
-    if (!x || !codes || !absmax_fp8 || !superscale || !y) return QLORA_ERR_NULL;
-    if (r > 0 && (!lora_a || !lora_b)) return QLORA_ERR_NULL;
-    if (int st = check_linear_shape(T, K, N, r)) return st;
-    if (r == 0 && (lora_a || lora_b)) return QLORA_ERR_SHAPE;
-    if (!aligned16(x) || !aligned16(codes) || !aligned16(absmax_fp8) || !aligned16(superscale) || !aligned16(y) ||
-        (lora_a && !aligned16(lora_a)) || (lora_b && !aligned16(lora_b)) || (workspace && !aligned16(workspace)))
-        return QLORA_ERR_ALIGN;
-    if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
-    const ql::LoraPlan pl(T, K, N, r);
-    const size_t need = T <= ql::kGemvMaxT ? ql::gemv_workspace(T, K, N, pl.r_pad) : pl.fwd_bytes;
-    if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
+    return fwd_impl(x, T, K, N, codes, dq_scales(absmax_fp8, superscale), lora_a, lora_b, r, scaling, y, workspace,
+                    workspace_bytes, stream);
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    if (T <= ql::kGemvMaxT)      // decode sizes: VALU GEMV, no MFMA
-        return dev(ql::launch_gemv(x, codes, absmax_fp8, superscale, lora_a, lora_b, scaling, pl, ws, y, s));
-    if (r > 0) {
-        if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
-        // s X A in both layouts: the transposed copy lets a backward with
-        // QLORA_BWD_REUSE_FORWARD take the adapter gradients without recomputing it
-        if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, true, s))) return st;
-    }
-    return dev(ql::launch_fwd(x, codes, absmax_fp8, superscale, lora_b, pl, ws, y, s));
+int qlora_linear_fwd_sq(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* codes,
+                        const float* absmax, const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
+                        float scaling, uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
+    return fwd_impl(x, T, K, N, codes, sq_scales(absmax), lora_a, lora_b, r, scaling, y, workspace,
+                    workspace_bytes, stream);
 }
 
 int qlora_linear_bwd_input(const uint16_t* dy, int64_t T, int64_t K, int64_t N, const uint8_t* codes,
@@ -125,52 +215,28 @@ int qlora_linear_bwd_input(const uint16_t* dy, int64_t T, int64_t K, int64_t N, 
                            const uint16_t* lora_b, int64_t r, float scaling, uint16_t* dx, const uint16_t* x,
                            uint16_t* d_lora_a, uint16_t* d_lora_b, void* workspace, size_t workspace_bytes,
                            unsigned flags, void* stream) {
-    if (!dy || !codes || !absmax_fp8 || !superscale || !dx) return QLORA_ERR_NULL;
-    if (r > 0 && (!lora_a || !lora_b)) return QLORA_ERR_NULL;
-    const bool grads = d_lora_a || d_lora_b;
-    if (grads && !x) return QLORA_ERR_NULL;
-    if (int st = check_linear_shape(T, K, N, r)) return st;
-    if (r == 0 && (lora_a || lora_b || grads)) return QLORA_ERR_SHAPE;
-    const void* ptrs[] = {dy, codes, absmax_fp8, superscale, dx, x, lora_a, lora_b, d_lora_a, d_lora_b, workspace};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
-    if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
-    if (flags & ~(unsigned)QLORA_BWD_REUSE_FORWARD) return QLORA_ERR_VALUE;
-    const ql::LoraPlan pl(T, K, N, r);
-    const size_t need = grads ? pl.bwd_grad_bytes : pl.bwd_bytes;   // > 0: the scale pre-pass needs room
-    // s X A from the forward's workspace (only the MFMA forward, T > 16, leaves it there)
-    const bool reuse = (flags & QLORA_BWD_REUSE_FORWARD) && T > ql::kGemvMaxT;
-    if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
+    return bwd_impl(dy, T, K, N, codes, dq_scales(absmax_fp8, superscale), lora_a, lora_b, r, scaling, dx, x,
+                    d_lora_a, d_lora_b, workspace, workspace_bytes, flags, stream);
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    if (r > 0)
-        if (int st = dev(ql::launch_lora_down_dy(dy, lora_b, scaling, pl, ws, grads, s))) return st;
-    if (int st = dev(ql::launch_dx(dy, codes, absmax_fp8, superscale, lora_a, pl, ws, dx, s))) return st;
-    if (grads) {
-        if (!reuse) {
-            if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
-            if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, true, s))) return st;
-        }
-        if (int st = dev(ql::launch_lora_grads(x, dy, pl, ws, d_lora_a, d_lora_b, s))) return st;
-    }
-    return QLORA_OK;
+int qlora_linear_bwd_input_sq(const uint16_t* dy, int64_t T, int64_t K, int64_t N, const uint8_t* codes,
+                              const float* absmax, const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
+                              float scaling, uint16_t* dx, const uint16_t* x, uint16_t* d_lora_a,
+                              uint16_t* d_lora_b, void* workspace, size_t workspace_bytes, unsigned flags,
+                              void* stream) {
+    return bwd_impl(dy, T, K, N, codes, sq_scales(absmax), lora_a, lora_b, r, scaling, dx, x, d_lora_a, d_lora_b,
+                    workspace, workspace_bytes, flags, stream);
 }
 
 int qlora_merge_lora(const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale, int64_t K, int64_t N,
                      const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling, uint16_t* w_out,
                      void* stream) {
-    if (!codes || !absmax_fp8 || !superscale || !w_out) return QLORA_ERR_NULL;
-    if (r > 0 && (!lora_a || !lora_b)) return QLORA_ERR_NULL;
-    if (K < 64 || K % 64 || N < 8 || N % 8 || K > (int64_t(1) << 20) || N > (int64_t(1) << 20) || N * K >= (int64_t(1) << 32))
-        return QLORA_ERR_SHAPE;
-    if (r < 0 || r > QLORA_MAX_RANK || r % 8 || (r == 0 && (lora_a || lora_b))) return QLORA_ERR_SHAPE;
-    const void* ptrs[] = {codes, absmax_fp8, superscale, lora_a, lora_b, w_out};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
-    if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
-    return dev(ql::launch_merge(codes, absmax_fp8, superscale, lora_a, lora_b, K, N, r, scaling, w_out,
-                                static_cast<hipStream_t>(stream)));
+    return merge_impl(codes, dq_scales(absmax_fp8, superscale), K, N, lora_a, lora_b, r, scaling, w_out, stream);
+}
+
+int qlora_merge_lora_sq(const uint8_t* codes, const float* absmax, int64_t K, int64_t N, const uint16_t* lora_a,
+                        const uint16_t* lora_b, int64_t r, float scaling, uint16_t* w_out, void* stream) {
+    return merge_impl(codes, sq_scales(absmax), K, N, lora_a, lora_b, r, scaling, w_out, stream);
 }
 
 }  // extern "C"

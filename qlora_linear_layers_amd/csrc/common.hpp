@@ -192,20 +192,29 @@ QL_DEV uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
 
 // ------------------------------------------------------------------ launchers
 
+// Block constants of a quantized weight: the double-quantized pair (one FP8
+// code per block, one fp32 super-scale per 256 blocks), or with `absmax` set
+// the fp32 absmax of every block (single quantization, no second level).
+struct BlockScales {
+    const uint8_t* fp8;
+    const float* sup;
+    const float* absmax;
+    bool single() const { return absmax != nullptr; }
+};
+
 hipError_t launch_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* fp8,
                            float* superscale, hipStream_t s);
-hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* fp8, const float* superscale,
-                             int64_t numel, uint16_t* out, hipStream_t s);
+hipError_t launch_quantize_sq(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, hipStream_t s);
+hipError_t launch_dequantize(const uint8_t* codes, BlockScales sc, int64_t numel, uint16_t* out, hipStream_t s);
 
-// Forward calls with at most this many tokens take the VALU GEMV path.
+// Forward calls with at most this many tokens take the decode (small-M MFMA) path.
 constexpr int64_t kGemvMaxT = 16;
 struct LoraPlan;
 size_t gemv_workspace(int64_t T, int64_t K, int64_t N, int64_t r_pad);
-hipError_t launch_merge(const uint8_t* codes, const uint8_t* fp8, const float* sup, const uint16_t* lora_a,
-                        const uint16_t* lora_b, int64_t K, int64_t N, int64_t r, float scaling, uint16_t* w_out,
-                        hipStream_t s);
-hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, const uint8_t* fp8, const float* sup,
-                       const uint16_t* lora_a, const uint16_t* lora_b, float scaling, const LoraPlan& pl,
-                       uint8_t* ws, uint16_t* y, hipStream_t s);
+hipError_t launch_merge(const uint8_t* codes, BlockScales sc, const uint16_t* lora_a, const uint16_t* lora_b,
+                        int64_t K, int64_t N, int64_t r, float scaling, uint16_t* w_out, hipStream_t s);
+hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
+                       const uint16_t* lora_b, float scaling, const LoraPlan& pl, uint8_t* ws, uint16_t* y,
+                       hipStream_t s);
 
 }  // namespace ql

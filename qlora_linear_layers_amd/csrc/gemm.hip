@@ -171,6 +171,7 @@ struct FwdArgs {
     const uint8_t* codes;
     const uint8_t* fp8;
     const float* sup;
+    const float* absmax;      // single quantization: fp32 block absmax (fp8/sup unused)
     const uint16_t* lora_b;   // [r][N]
     const uint16_t* ps_hi;    // [T][r_pad] bf16: s X A = hi + lo
     const uint16_t* ps_lo;
@@ -192,6 +193,10 @@ struct FwdArgs {
 // registers, alternating register sets by tile parity); X is written to the
 // idle LDS buffer one tile ahead, in the middle of the last step of a tile;
 // one barrier per tile.  Within the tile, see fwd_tile.
+//
+// SQ: single quantization, the block constant is the stored fp32 absmax (one
+// 4-byte load per row and tile instead of the FP8 code and the super-scale).
+template <bool SQ>
 struct FwdPipe {
     static constexpr int TT = 256;
     static constexpr uint32_t kTile = TT * 128;   // one [256][64] bf16 LDS tile
@@ -211,10 +216,17 @@ struct FwdPipe {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             wc[par][i] = bload16(rc, cvo[i], (uint32_t)kt * 32u);
-            wf[par][i] = bload1(rf, fvo[i], (uint32_t)kt);
-            ws[par][i] = __uint_as_float(bload4(rs, wok[i] ? ((blk[i] + kt) >> 8) * 4u : kOOB, 0));
+            if constexpr (SQ) {
+                wf[par][i] = 0;
+                ws[par][i] = __uint_as_float(bload4(rf, wok[i] ? (blk[i] + kt) * 4u : kOOB, 0));
+            } else {
+                wf[par][i] = bload1(rf, fvo[i], (uint32_t)kt);
+                ws[par][i] = __uint_as_float(bload4(rs, wok[i] ? ((blk[i] + kt) >> 8) * 4u : kOOB, 0));
+            }
         }
     }
+    // block constant c1' of row i from register set par
+    QL_DEV float c1(int par, int i) const { return SQ ? ws[par][i] : block_scale(wf[par][i], ws[par][i]); }
     QL_DEV void load_x(int kt, int par) {
         kt = kt < KT ? kt : KT - 1;
 #pragma unroll
@@ -290,11 +302,11 @@ QL_DEV void interleave() {
 // the codebook pairs of step s+2 are read, and the A fragments of step s+1
 // are built from pairs read during step s-1.  On entry xa / aa hold step 0 of
 // tile kt and qa the pairs of step 1; on exit the same for tile kt+1.
-template <int P>
-QL_DEV void fwd_tile(FwdPipe& pp, int kt, f32x16_t (&acc)[2][8], lds8_t* lX, int r, int h, XFr& xa, AFr& aa,
+template <int P, bool SQ>
+QL_DEV void fwd_tile(FwdPipe<SQ>& pp, int kt, f32x16_t (&acc)[2][8], lds8_t* lX, int r, int h, XFr& xa, AFr& aa,
                      QPr& qa, float (&c1p)[2]) {
     constexpr int Q = P ^ 1;
-    const lds8_t* xb = lX + P * FwdPipe::kTile;
+    const lds8_t* xb = lX + P * FwdPipe<SQ>::kTile;
     XFr xb_;
     AFr ab;
     QPr qb;
@@ -322,17 +334,17 @@ QL_DEV void fwd_tile(FwdPipe& pp, int kt, f32x16_t (&acc)[2][8], lds8_t* lX, int
     interleave<16, 16, 16>();
     __builtin_amdgcn_sched_barrier(0);
     pp.load_w(kt + 2, P);                     // code set P is no longer read
-    const float n1p[2] = {block_scale(pp.wf[Q][0], pp.ws[Q][0]), block_scale(pp.wf[Q][1], pp.ws[Q][1])};
+    const float n1p[2] = {pp.c1(Q, 0), pp.c1(Q, 1)};
     // step 3: the first half of its MFMAs cover the X store and the barrier
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[0], xb_[j], acc[0][j], 0, 0, 0);
         acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[1], xb_[j], acc[1][j], 0, 0, 0);
     }
-    pp.store_x(Q, lX + Q * FwdPipe::kTile);
+    pp.store_x(Q, lX + Q * FwdPipe<SQ>::kTile);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    read_x(xa, lX + Q * FwdPipe::kTile, 0, r, h);
+    read_x(xa, lX + Q * FwdPipe<SQ>::kTile, 0, r, h);
     read_q(qa, pp.wc[Q], 1, pp.lane8);
     make_a(aa, qb, n1p);
 #pragma unroll
@@ -346,11 +358,12 @@ QL_DEV void fwd_tile(FwdPipe& pp, int kt, f32x16_t (&acc)[2][8], lds8_t* lX, int
     c1p[1] = n1p[1];
 }
 
+template <bool SQ>
 __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     lds8_t* smem = (lds8_t*)(smem_raw);
-    constexpr int TT = FwdPipe::TT;
-    constexpr uint32_t kTile = FwdPipe::kTile;
+    constexpr int TT = FwdPipe<SQ>::TT;
+    constexpr uint32_t kTile = FwdPipe<SQ>::kTile;
     lds8_t* const lX = smem;                  // 2 tiles (the LoRA phase reuses them)
     lds8_t* const lL = smem + kTile;
     lds8_t* const tbl = smem + 2 * kTile;     // wide pair table
@@ -363,10 +376,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 31, h = lane >> 5;
 
-    FwdPipe pp;
+    FwdPipe<SQ> pp;
     pp.rc = make_rsrc(p.codes, p.N * p.K / 2);
-    pp.rf = make_rsrc(p.fp8, p.N * p.K / 64);
-    pp.rs = make_rsrc(p.sup, ceil_div(p.N * p.K / 64, 256) * 4);
+    if constexpr (SQ) {
+        pp.rf = make_rsrc(p.absmax, p.N * p.K / 64 * 4);
+        pp.rs = pp.rf;
+    } else {
+        pp.rf = make_rsrc(p.fp8, p.N * p.K / 64);
+        pp.rs = make_rsrc(p.sup, ceil_div(p.N * p.K / 64, 256) * 4);
+    }
     pp.rx = make_rsrc(p.x, p.T * p.K * 2);
     pp.KT = (int)(p.K / 64);
     pp.lane8 = lds_addr(tbl) + (uint32_t)(lane & 31) * 8u;   // table is 64 KB aligned
@@ -403,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
     XFr xa;
     AFr aa;
     QPr qa;
-    float c1p[2] = {block_scale(pp.wf[0][0], pp.ws[0][0]), block_scale(pp.wf[0][1], pp.ws[0][1])};
+    float c1p[2] = {pp.c1(0, 0), pp.c1(0, 1)};
     {
         QPr q0;
         read_q(q0, pp.wc[0], 0, pp.lane8);
@@ -480,15 +498,18 @@ struct DxArgs {
     int64_t T, K, N, r, r_pad;
 };
 
-// Block scales c1' = fl32(e4m3(f) * s2) of W [N, K], written transposed as
-// [K/64][N] so that eight consecutive rows of one block column are contiguous.
+// Block scales c1' = fl32(e4m3(f) * s2) of W [N, K] (single quantization: the
+// stored fp32 absmax), written transposed as [K/64][N] so that eight
+// consecutive rows of one block column are contiguous.
+template <bool SQ>
 __global__ __launch_bounds__(256) void k_scales_t(const uint8_t* __restrict__ fp8, const float* __restrict__ sup,
-                                                  int64_t N, int64_t KB, float* __restrict__ out) {
+                                                  const float* __restrict__ absmax, int64_t N, int64_t KB,
+                                                  float* __restrict__ out) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;     // over N x KB, n fastest
     if (i >= N * KB) return;
     const int64_t kb = i / N, n = i % N;
     const int64_t b = n * KB + kb;
-    out[i] = block_scale(fp8[b], sup[b >> 8]);
+    out[i] = SQ ? absmax[b] : block_scale(fp8[b], sup[b >> 8]);
 }
 
 // dX = dY W' (+ (s dY B^T) A^T): tile 256 (k) x 256 (t), reduction over n in
@@ -784,28 +805,34 @@ hipError_t set_smem(F* f, size_t bytes) {
 
 }  // namespace
 
-hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, const uint8_t* fp8, const float* sup,
-                      const uint16_t* lora_b, const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s) {
-    FwdArgs a{x, codes, fp8, sup, lora_b, reinterpret_cast<const uint16_t*>(ws + pl.off_ps_hi),
+hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, BlockScales sc, const uint16_t* lora_b,
+                      const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s) {
+    FwdArgs a{x, codes, sc.fp8, sc.sup, sc.absmax, lora_b, reinterpret_cast<const uint16_t*>(ws + pl.off_ps_hi),
               reinterpret_cast<const uint16_t*>(ws + pl.off_ps_lo), y,
               pl.T, pl.K, pl.N, pl.r, pl.r_pad};
     const size_t lds = kFwdSmem;
-    hipError_t e = set_smem(k_fwd, lds);
-    if (e != hipSuccess) return e;
     const int64_t tiles = ceil_div(pl.N, 256) * ceil_div(pl.T, 256);
-    hipLaunchKernelGGL(k_fwd, dim3((unsigned)tiles), dim3(kThreads), lds, s, a, host_codebook());
-    return hipGetLastError();
+    auto go = [&](auto kern) {
+        hipError_t e = set_smem(kern, lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kThreads), lds, s, a, host_codebook());
+        return hipGetLastError();
+    };
+    return sc.single() ? go(k_fwd<true>) : go(k_fwd<false>);
 }
 
-hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* fp8, const float* sup,
-                     const uint16_t* lora_a, const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s) {
+hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
+                     const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s) {
     float* sclt = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + pl.off_scl);
     const int64_t nsc = (pl.K / 64) * pl.N;
-    hipLaunchKernelGGL(k_scales_t, dim3((unsigned)ceil_div(nsc, 256)), dim3(256), 0, s, fp8, sup, pl.N, pl.K / 64,
-                       sclt);
+    const dim3 sg((unsigned)ceil_div(nsc, 256));
+    if (sc.single())
+        hipLaunchKernelGGL(k_scales_t<true>, sg, dim3(256), 0, s, nullptr, nullptr, sc.absmax, pl.N, pl.K / 64, sclt);
+    else
+        hipLaunchKernelGGL(k_scales_t<false>, sg, dim3(256), 0, s, sc.fp8, sc.sup, nullptr, pl.N, pl.K / 64, sclt);
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
-    DxArgs a{dy, codes, fp8, sup, lora_a, reinterpret_cast<const uint16_t*>(ws + pl.off_gs_hi),
+    DxArgs a{dy, codes, sc.fp8, sc.sup, lora_a, reinterpret_cast<const uint16_t*>(ws + pl.off_gs_hi),
              reinterpret_cast<const uint16_t*>(ws + pl.off_gs_lo), sclt, dx,
              pl.T, pl.K, pl.N, pl.r, pl.r_pad};
     const size_t lds = kDxSmem;

@@ -39,6 +39,7 @@ struct GemvArgs {
     const uint8_t* codes;
     const uint8_t* fp8;
     const float* sup;
+    const float* absmax;      // single quantization: fp32 block absmax (fp8/sup unused)
     const uint16_t* lora_a;   // [K][r]
     const uint16_t* lora_b;   // [r][N]
     float* part;              // [KS][T][N] fp32 base partials
@@ -123,8 +124,9 @@ __device__ __forceinline__ void lora_down_block(const GemvArgs& p, uint8_t* dyn,
 }
 
 // Launch 1.  Blocks [0, gemv_blocks) are base blocks: rows [n0, n0 + 128) over
-// the k split ks (512 k); the rest are LoRA down-projection blocks.
-template <int TT>
+// the k split ks (512 k); the rest are LoRA down-projection blocks.  SQ: the
+// block constant is the stored fp32 absmax (single quantization).
+template <int TT, bool SQ>
 __global__ __launch_bounds__(kDecThreads) void k_gemv(GemvArgs p, Codebook cb) {
     extern __shared__ __align__(16) uint8_t dyn[];
     if ((int)blockIdx.x >= p.gemv_blocks) {
@@ -142,8 +144,8 @@ __global__ __launch_bounds__(kDecThreads) void k_gemv(GemvArgs p, Codebook cb) {
     const int64_t kk = (int64_t)ks * kDecK + 128 * wave + 32 * g;      // this lane's 32 k
     const bool kok = kk < p.K;                                         // K % 64 == 0: all 32 or none
     const rsrc_t rc = make_rsrc(p.codes, p.N * p.K / 2);
-    const rsrc_t rf = make_rsrc(p.fp8, p.N * p.K / 64);
-    const rsrc_t rs = make_rsrc(p.sup, ceil_div(p.N * p.K / 64, 256) * 4);
+    const rsrc_t rf = SQ ? make_rsrc(p.absmax, p.N * p.K / 64 * 4) : make_rsrc(p.fp8, p.N * p.K / 64);
+    const rsrc_t rs = SQ ? rf : make_rsrc(p.sup, ceil_div(p.N * p.K / 64, 256) * 4);
     const rsrc_t rx = make_rsrc(p.x, p.T * p.K * 2);
 
     // every load of the wave first: 16 code bytes, the FP8 constant and the
@@ -156,8 +158,13 @@ __global__ __launch_bounds__(kDecThreads) void k_gemv(GemvArgs p, Codebook cb) {
         const bool ok = kok && n < p.N;
         const int64_t blk = n * (p.K / 64) + kk / 64;
         cw[c] = bload16(rc, ok ? (uint32_t)(n * (p.K / 2) + kk / 2) : kOOB, 0);
-        f8[c] = bload1(rf, ok ? (uint32_t)blk : kOOB, 0);
-        s2[c] = bload4(rs, ok ? (uint32_t)(blk >> 8) * 4u : kOOB, 0);
+        if constexpr (SQ) {
+            f8[c] = 0;
+            s2[c] = bload4(rf, ok ? (uint32_t)blk * 4u : kOOB, 0);
+        } else {
+            f8[c] = bload1(rf, ok ? (uint32_t)blk : kOOB, 0);
+            s2[c] = bload4(rs, ok ? (uint32_t)(blk >> 8) * 4u : kOOB, 0);
+        }
     }
     const bool xok = kok && nl < p.T;
 #pragma unroll
@@ -170,7 +177,7 @@ __global__ __launch_bounds__(kDecThreads) void k_gemv(GemvArgs p, Codebook cb) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        const float c1p = block_scale(f8[c], __uint_as_float(s2[c]));
+        const float c1p = SQ ? __uint_as_float(s2[c]) : block_scale(f8[c], __uint_as_float(s2[c]));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             u32x4_t w;
@@ -342,10 +349,10 @@ size_t gemv_workspace(int64_t T, int64_t K, int64_t N, int64_t r_pad) {
     return align256((size_t)gemv_ks(K) * T * N * 4) + align256((size_t)gemv_kl(K) * T * r_pad * 4);
 }
 
-hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, const uint8_t* fp8, const float* sup,
-                       const uint16_t* lora_a, const uint16_t* lora_b, float scaling, const LoraPlan& pl,
-                       uint8_t* ws, uint16_t* y, hipStream_t s) {
-    GemvArgs a{x, codes, fp8, sup, lora_a, lora_b, nullptr, nullptr, y, pl.T, pl.K, pl.N, pl.r, pl.r_pad,
+hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
+                       const uint16_t* lora_b, float scaling, const LoraPlan& pl, uint8_t* ws, uint16_t* y,
+                       hipStream_t s) {
+    GemvArgs a{x, codes, sc.fp8, sc.sup, sc.absmax, lora_a, lora_b, nullptr, nullptr, y, pl.T, pl.K, pl.N, pl.r, pl.r_pad,
                gemv_ks(pl.K), pl.r ? gemv_kl(pl.K) : 0, 0, scaling};
     a.part = reinterpret_cast<float*>(ws);
     a.lpart = reinterpret_cast<float*>(ws + align256((size_t)a.KS * pl.T * pl.N * 4));
@@ -360,11 +367,12 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, const uint8_t* f
                                  (int)kDecLds);
         if (ae == hipSuccess) hipLaunchKernelGGL(kern, grid, dim3(kDecThreads), kDecLds, s, a, cb);
     };
-    if (pl.T <= 1) go(k_gemv<1>);
-    else if (pl.T <= 2) go(k_gemv<2>);
-    else if (pl.T <= 4) go(k_gemv<4>);
-    else if (pl.T <= 8) go(k_gemv<8>);
-    else go(k_gemv<16>);
+    const bool sq = sc.single();
+    if (pl.T <= 1) sq ? go(k_gemv<1, true>) : go(k_gemv<1, false>);
+    else if (pl.T <= 2) sq ? go(k_gemv<2, true>) : go(k_gemv<2, false>);
+    else if (pl.T <= 4) sq ? go(k_gemv<4, true>) : go(k_gemv<4, false>);
+    else if (pl.T <= 8) sq ? go(k_gemv<8, true>) : go(k_gemv<8, false>);
+    else sq ? go(k_gemv<16, true>) : go(k_gemv<16, false>);
     if (ae != hipSuccess) return ae;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

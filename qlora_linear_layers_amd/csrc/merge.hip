@@ -31,6 +31,7 @@ struct MergeArgs {
     const uint8_t* codes;
     const uint8_t* fp8;
     const float* sup;
+    const float* absmax;  // single quantization: fp32 block absmax (fp8/sup unused)
     const uint16_t* a;    // [K][r]
     const uint16_t* b;    // [r][N]
     uint16_t* w;          // [N][K]
@@ -41,8 +42,9 @@ struct MergeArgs {
 constexpr int kMergeRows = 64;    // n per workgroup
 constexpr int kMergeK = 256;      // k per workgroup (64 per wave)
 
-// RP = r_pad / 64 (1..4): B^T is RP swizzled [64 n][64 j] tiles of 8 KB
-template <int RP>
+// RP = r_pad / 64 (1..4): B^T is RP swizzled [64 n][64 j] tiles of 8 KB.
+// SQ: the block constant is the stored fp32 absmax (single quantization).
+template <int RP, bool SQ>
 __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
     __shared__ float s_q[16];
     __shared__ __align__(16) uint8_t s_bt[RP * 8192];
@@ -56,8 +58,8 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
     const int64_t k0 = (int64_t)kb * kMergeK + 64 * wave;             // this wave's 64 k (one block per row)
     const bool kok = k0 < p.K;                                         // K % 64 == 0: all 64 or none
     const rsrc_t rc = make_rsrc(p.codes, p.N * p.K / 2);
-    const rsrc_t rf = make_rsrc(p.fp8, p.N * p.K / 64);
-    const rsrc_t rs = make_rsrc(p.sup, ceil_div(p.N * p.K / 64, 256) * 4);
+    const rsrc_t rf = SQ ? make_rsrc(p.absmax, p.N * p.K / 64 * 4) : make_rsrc(p.fp8, p.N * p.K / 64);
+    const rsrc_t rs = SQ ? rf : make_rsrc(p.sup, ceil_div(p.N * p.K / 64, 256) * 4);
     const rsrc_t ra = make_rsrc(p.a, p.K * p.r * 2);
     const rsrc_t rbm = make_rsrc(p.b, p.r * p.N * 2);
 
@@ -70,8 +72,13 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
         const bool ok = kok && n < p.N;
         const int64_t blk = n * (p.K / 64) + k0 / 64;
         cw[c] = bload8(rc, ok ? (uint32_t)(n * (p.K / 2) + (k0 + 16 * q) / 2) : kOOB, 0);
-        f8[c] = bload1(rf, ok ? (uint32_t)blk : kOOB, 0);
-        s2[c] = bload4(rs, ok ? (uint32_t)(blk >> 8) * 4u : kOOB, 0);
+        if constexpr (SQ) {
+            f8[c] = 0;
+            s2[c] = bload4(rf, ok ? (uint32_t)blk * 4u : kOOB, 0);
+        } else {
+            f8[c] = bload1(rf, ok ? (uint32_t)blk : kOOB, 0);
+            s2[c] = bload4(rs, ok ? (uint32_t)(blk >> 8) * 4u : kOOB, 0);
+        }
     }
 
     // A fragments of the first kPre rank steps, before the barrier (A operand
@@ -139,7 +146,7 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int64_t n = n0 + 16 * c + nl;
-        const float c1p = block_scale(f8[c], __uint_as_float(s2[c]));
+        const float c1p = SQ ? __uint_as_float(s2[c]) : block_scale(f8[c], __uint_as_float(s2[c]));
         u32x4_t o[2];
 #pragma unroll
         for (int bb = 0; bb < 8; ++bb) {                               // code byte bb: k 2bb (high nibble), 2bb + 1
@@ -161,18 +168,19 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
 
 }  // namespace
 
-hipError_t launch_merge(const uint8_t* codes, const uint8_t* fp8, const float* sup, const uint16_t* lora_a,
-                        const uint16_t* lora_b, int64_t K, int64_t N, int64_t r, float scaling, uint16_t* w_out,
-                        hipStream_t s) {
-    if (r == 0) return launch_dequantize(codes, fp8, sup, N * K, w_out, s);
-    const MergeArgs a{codes, fp8, sup, lora_a, lora_b, w_out, K, N, r, scaling};
+hipError_t launch_merge(const uint8_t* codes, BlockScales sc, const uint16_t* lora_a, const uint16_t* lora_b,
+                        int64_t K, int64_t N, int64_t r, float scaling, uint16_t* w_out, hipStream_t s) {
+    if (r == 0) return launch_dequantize(codes, sc, N * K, w_out, s);
+    const MergeArgs a{codes, sc.fp8, sc.sup, sc.absmax, lora_a, lora_b, w_out, K, N, r, scaling};
     const dim3 grid((unsigned)(ceil_div(N, kMergeRows) * ceil_div(K, kMergeK))), block(256);
     const Codebook& cb = host_codebook();
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, a, cb); };
+    const bool sq = sc.single();
     switch ((int)ceil_div(r, 64)) {
-        case 1: hipLaunchKernelGGL(k_merge<1>, grid, block, 0, s, a, cb); break;
-        case 2: hipLaunchKernelGGL(k_merge<2>, grid, block, 0, s, a, cb); break;
-        case 3: hipLaunchKernelGGL(k_merge<3>, grid, block, 0, s, a, cb); break;
-        default: hipLaunchKernelGGL(k_merge<4>, grid, block, 0, s, a, cb); break;
+        case 1: sq ? go(k_merge<1, true>) : go(k_merge<1, false>); break;
+        case 2: sq ? go(k_merge<2, true>) : go(k_merge<2, false>); break;
+        case 3: sq ? go(k_merge<3, true>) : go(k_merge<3, false>); break;
+        default: sq ? go(k_merge<4, true>) : go(k_merge<4, false>); break;
     }
     return hipGetLastError();
 }

@@ -22,10 +22,14 @@ namespace ql {
 // midpoint gives the same code as the exact ratio.  Blocks whose c1 is outside
 // [2^-64, 2^64] (where rcp could over/underflow) take correctly rounded
 // division instead, which is the definition itself.
-__global__ __launch_bounds__(256) void k_quantize_dq(const uint16_t* __restrict__ w, int64_t nblocks,
-                                                     uint8_t* __restrict__ codes,
-                                                     uint8_t* __restrict__ fp8,
-                                                     float* __restrict__ superscale, EncodeTable tab) {
+//
+// SQ: single quantization (the first level alone): each block's fp32 absmax
+// c1 is stored as it is and there is no second level.
+template <bool SQ>
+__global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ w, int64_t nblocks,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ fp8,
+                                                  float* __restrict__ superscale, float* __restrict__ absmax,
+                                                  EncodeTable tab) {
     __shared__ uint2 s_tab[34];
     __shared__ float s_c1[kGroup];
     __shared__ float s_wmax[4];
@@ -89,10 +93,14 @@ __global__ __launch_bounds__(256) void k_quantize_dq(const uint16_t* __restrict_
         }
         if (lb < nb) {
             dst[chunk] = out;
-            if ((tid & 7) == 0) s_c1[lb] = c1;
+            if ((tid & 7) == 0) {
+                if constexpr (SQ) absmax[blk0 + lb] = c1;
+                else s_c1[lb] = c1;
+            }
         }
         gmax = fmaxf(gmax, c1);
     }
+    if constexpr (SQ) return;                                 // uniform: no second level
 
     // Second level: group max -> fp32 super-scale, then one FP8 code per block.
     gmax = fmaxf(gmax, __shfl_xor(gmax, 8));
@@ -114,8 +122,16 @@ hipError_t launch_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uin
                            float* superscale, hipStream_t s) {
     const int64_t nblocks = numel / kBlock;
     const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
-    hipLaunchKernelGGL(k_quantize_dq, dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes, fp8,
-                       superscale, host_encode_table());
+    hipLaunchKernelGGL(k_quantize<false>, dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes, fp8,
+                       superscale, nullptr, host_encode_table());
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_sq(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, hipStream_t s) {
+    const int64_t nblocks = numel / kBlock;
+    const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
+    hipLaunchKernelGGL(k_quantize<true>, dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes, nullptr,
+                       nullptr, absmax, host_encode_table());
     return hipGetLastError();
 }
 
@@ -125,15 +141,18 @@ hipError_t launch_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uin
 // one 16-byte bf16 store, so every wave-wide load and store instruction covers
 // one contiguous span (256 B of codes in, 1 KB of bf16 out).  A thread handles
 // kDeqUnits such units, 256 units apart, to keep several loads in flight.
-// c1' = fl32(e4m3(f) * s2) per unit; w' = RNE_bf16(fl32(q[code] * c1')) per
-// element with the codebook in LDS (16 floats: every lookup hits one of 16
-// distinct banks, so lookups never conflict).
+// c1' = fl32(e4m3(f) * s2) per unit (single quantization: c1' = the stored
+// fp32 absmax); w' = RNE_bf16(fl32(q[code] * c1')) per element with the
+// codebook in LDS (16 floats: every lookup hits one of 16 distinct banks, so
+// lookups never conflict).
 constexpr int kDeqUnits = 4;
 
-__global__ __launch_bounds__(256) void k_dequantize_dq(const uint32_t* __restrict__ codes,
-                                                       const uint8_t* __restrict__ fp8,
-                                                       const float* __restrict__ superscale,
-                                                       int64_t nunits, u32x4_t* __restrict__ out, Codebook cb) {
+template <bool SQ>
+__global__ __launch_bounds__(256) void k_dequantize(const uint32_t* __restrict__ codes,
+                                                    const uint8_t* __restrict__ fp8,
+                                                    const float* __restrict__ superscale,
+                                                    const float* __restrict__ absmax,
+                                                    int64_t nunits, u32x4_t* __restrict__ out, Codebook cb) {
     __shared__ float s_q[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
@@ -149,15 +168,20 @@ __global__ __launch_bounds__(256) void k_dequantize_dq(const uint32_t* __restric
         const int64_t ii = i < nunits ? i : 0;
         cv[u] = __builtin_nontemporal_load(codes + ii);
         const int64_t blk = ii >> 3;                      // 8 units of 8 codes per block
-        f8[u] = fp8[blk];
-        s2[u] = superscale[blk >> 8];
+        if constexpr (SQ) {
+            f8[u] = 0;
+            s2[u] = absmax[blk];
+        } else {
+            f8[u] = fp8[blk];
+            s2[u] = superscale[blk >> 8];
+        }
     }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kDeqUnits; ++u) {
         const int64_t i = u0 + u * 256;
         if (i >= nunits) continue;
-        const float c1p = __fmul_rn(e4m3_decode(f8[u]), s2[u]);
+        const float c1p = SQ ? s2[u] : __fmul_rn(e4m3_decode(f8[u]), s2[u]);
         u32x4_t o;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -168,13 +192,18 @@ __global__ __launch_bounds__(256) void k_dequantize_dq(const uint32_t* __restric
     }
 }
 
-hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* fp8, const float* superscale,
-                             int64_t numel, uint16_t* out, hipStream_t s) {
+hipError_t launch_dequantize(const uint8_t* codes, BlockScales sc, int64_t numel, uint16_t* out, hipStream_t s) {
     const int64_t nunits = numel / 8;
     const int64_t per_wg = 256 * kDeqUnits;
-    hipLaunchKernelGGL(k_dequantize_dq, dim3((unsigned)((nunits + per_wg - 1) / per_wg)), dim3(256), 0, s,
-                       reinterpret_cast<const uint32_t*>(codes), fp8, superscale, nunits,
-                       reinterpret_cast<u32x4_t*>(out), host_codebook());
+    const dim3 grid((unsigned)((nunits + per_wg - 1) / per_wg));
+    const uint32_t* c = reinterpret_cast<const uint32_t*>(codes);
+    u32x4_t* o = reinterpret_cast<u32x4_t*>(out);
+    if (sc.single())
+        hipLaunchKernelGGL(k_dequantize<true>, grid, dim3(256), 0, s, c, nullptr, nullptr, sc.absmax, nunits, o,
+                           host_codebook());
+    else
+        hipLaunchKernelGGL(k_dequantize<false>, grid, dim3(256), 0, s, c, sc.fp8, sc.sup, nullptr, nunits, o,
+                           host_codebook());
     return hipGetLastError();
 }
 

@@ -144,3 +144,30 @@ def test_merge_validation(L):
     assert _merge(L, w=MIS) == ALIGN
     assert _merge(L, lb=MIS) == ALIGN
     assert _merge(L, s=math.nan) == VALUE
+
+
+def test_single_quantization_validation(L):
+    assert L.nf4_quantize(None, 64, FAKE, FAKE, None) == NULL
+    assert L.nf4_quantize(FAKE, 64, FAKE, None, None) == NULL
+    assert L.nf4_quantize(FAKE, 96, FAKE, FAKE, None) == SHAPE
+    assert L.nf4_quantize(FAKE, 64, FAKE, MIS, None) == ALIGN
+    assert L.nf4_dequantize(FAKE, None, 64, FAKE, None) == NULL
+    assert L.nf4_dequantize(FAKE, FAKE, 0, FAKE, None) == SHAPE
+    assert L.nf4_dequantize(FAKE, MIS, 64, FAKE, None) == ALIGN
+    f = L.qlora_linear_fwd_sq
+    assert f(FAKE, 16, 128, 128, FAKE, None, None, None, 0, 1.0, FAKE, FAKE, 1 << 30, None) == NULL
+    assert f(FAKE, 16, 100, 128, FAKE, FAKE, None, None, 0, 1.0, FAKE, FAKE, 1 << 30, None) == SHAPE
+    assert f(FAKE, 16, 128, 128, FAKE, MIS, None, None, 0, 1.0, FAKE, FAKE, 1 << 30, None) == ALIGN
+    assert f(FAKE, 16, 128, 128, FAKE, FAKE, None, None, 0, math.inf, FAKE, FAKE, 1 << 30, None) == VALUE
+    assert f(FAKE, 16, 128, 128, FAKE, FAKE, None, None, 0, 1.0, FAKE, None, 0, None) == WORKSPACE
+    b = L.qlora_linear_bwd_input_sq
+    assert b(FAKE, 64, 128, 128, FAKE, None, FAKE, FAKE, 16, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 0,
+             None) == NULL
+    assert b(FAKE, 64, 128, 128, FAKE, FAKE, FAKE, FAKE, 16, 1.0, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, 0,
+             None) == NULL                                # grads without X
+    assert b(FAKE, 64, 128, 128, FAKE, FAKE, FAKE, FAKE, 16, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 4,
+             None) == VALUE
+    m = L.qlora_merge_lora_sq
+    assert m(FAKE, None, 128, 64, FAKE, FAKE, 16, 0.5, FAKE, None) == NULL
+    assert m(FAKE, FAKE, 128, 60, FAKE, FAKE, 16, 0.5, FAKE, None) == SHAPE
+    assert m(FAKE, MIS, 128, 64, FAKE, FAKE, 16, 0.5, FAKE, None) == ALIGN
