@@ -14,7 +14,9 @@ Output: one JSON line.  `value` is the step's attainment of the MI355X
 roofline: the sum over all phases of their roofline time (algorithmic bytes at
 8 TB/s for quantize / dequantize, algorithmic flops at 2.5 PFLOP/s bf16 dense
 for the GEMM phases) divided by the measured step time.  Per-phase durations
-come from HIP events recorded on the stream the kernels run on.
+come from HIP events recorded on the stream the kernels run on.  Outside the
+step, `components` also carries the decode forward (T = 1 / 4 / 8), the LoRA
+merge and the single-quantization variant measured on the same seven linears.
 """
 import argparse
 import json
@@ -164,6 +166,45 @@ def measure_merge(api, torch, layers, sets, r, s, reps=6):
     ev[1].record()
     torch.cuda.synchronize()
     return ev[0].elapsed_time(ev[1]) / 1e3 / reps, sum(merge_bytes(l, r) for l in layers)
+
+
+def measure_sq(api, torch, bufs, T, r, s, ws, reps=5):
+    """The single-quantization variant (codes + fp32 absmax per block) on the same
+    seven linears: quantize, dequantize, forward and backward, each timed over
+    `reps` passes with HIP events.  Returns {phase: (seconds per layer set, amount)}."""
+    qs = [api.nf4_quantize(b["w"]) for b in bufs]
+    ops = {
+        "quantize_sq": ("hbm", lambda b, q: api.nf4_quantize(b["w"]),
+                        lambda l: 2 * l.N * l.K + storage_bytes_sq(l.N * l.K)),
+        "dequantize_sq": ("hbm", lambda b, q: api.nf4_dequantize(q, out=b["wd"]),
+                          lambda l: 2 * l.N * l.K + storage_bytes_sq(l.N * l.K)),
+        "forward_sq": ("mfma", lambda b, q: api.qlora_linear_fwd(b["x"], q, b["a"], b["b"], s, workspace=ws,
+                                                                  out=b["y"]),
+                       lambda l: phase_work(l, T, r)["forward"][1]),
+        "backward_sq": ("mfma", lambda b, q: api.qlora_linear_bwd_input(b["dy"], q, b["a"], b["b"], s, x=b["x"],
+                                                                         lora_grads=True, workspace=ws, dx=b["dx"],
+                                                                         d_lora_a=b["da"], d_lora_b=b["db"]),
+                        lambda l: phase_work(l, T, r)["backward"][1]),
+    }
+    out = {}
+    for name, (kind, fn, work) in ops.items():
+        for b, q in zip(bufs, qs):
+            fn(b, q)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            for b, q in zip(bufs, qs):
+                fn(b, q)
+        ev[1].record()
+        torch.cuda.synchronize()
+        out[name] = (kind, ev[0].elapsed_time(ev[1]) / 1e3 / reps, sum(work(b["lin"]) for b in bufs))
+    return out
+
+
+def storage_bytes_sq(numel):
+    """Codes + one fp32 absmax per 64 weights."""
+    return numel // 2 + 4 * (numel // 64)
 
 
 def cpu_baseline(layers, T, r, s, t_sample):
@@ -337,6 +378,14 @@ def main():
                                  "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
                                  "us_per_layer_set": round(1e6 * secs, 2),
                                  "note": "7 linears, fused dequant + small-M MFMA (16x16x32) incl. LoRA; weights rotated over 6 copies"}
+    for name, (kind, secs, amt) in measure_sq(api, torch, bufs, T, r, s, ws).items():
+        if kind == "hbm":
+            comp[name] = {"GB/s": round(amt / secs / 1e9, 1), "frac_of_hbm_peak": round(amt / secs / HBM_PEAK, 4),
+                          "ms": round(1e3 * secs, 4), "note": "single quantization (fp32 absmax per 64 weights)"}
+        else:
+            comp[name] = {"TFLOP/s": round(amt / secs / 1e12, 1),
+                          "frac_of_mfma_peak": round(amt / secs / MFMA_BF16_PEAK, 4), "ms": round(1e3 * secs, 4),
+                          "note": "single quantization (fp32 absmax per 64 weights)"}
     secs, nbytes = measure_merge(api, torch, layers, sets, r, s)
     comp["merge"] = {"GB/s": round(nbytes / secs / 1e9, 1), "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
                      "us_per_layer_set": round(1e6 * secs, 2),
