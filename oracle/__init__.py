@@ -16,6 +16,8 @@ Sources (titles of the pages, with the part each function follows):
   * "从LoRA到QLoRA：量化技术如何改变预训练模型的微调方式", sections 2.2-2.3 (quantile
     data type normalised to [-1, 1]) and 3.1 (bf16 compute, only LoRA weights
     receive gradients).
+  * "QLoRA 原理精讲", section 2.1 (why not INT4: the uniform 16-level baseline
+    of the data-type ablation).
   * "QLoRA 原理精讲", section 2.5 and section 3 pitfall 3 (merging the adapter
     back into BF16 weights).
   * The Volcengine article on LoRA / Q-LoRA / PortLLM, sections 3.1, 3.2 and 3.4
@@ -42,5 +44,9 @@ from .linear import (
     lora_grads,
 )
 from .merge import merge_lora, merge_lora_f64, merge_lora_rows
+from .int4 import (
+    int4_levels, int4_levels_f32, int4_midpoints, int4_encode, quantize_int4, dequantize_int4,
+    relative_rms_error,
+)
 
 __all__ = [n for n in dir() if not n.startswith("_")]
