@@ -16,7 +16,8 @@ roofline: the sum over all phases of their roofline time (algorithmic bytes at
 for the GEMM phases) divided by the measured step time.  Per-phase durations
 come from HIP events recorded on the stream the kernels run on.  Outside the
 step, `components` also carries the decode forward (T = 1 / 4 / 8), the LoRA
-merge and the single-quantization variant measured on the same seven linears.
+merge, the single-quantization variant and the NF4-vs-INT4 data-type ablation
+measured on the same seven linears.
 """
 import argparse
 import json
@@ -200,6 +201,44 @@ def measure_sq(api, torch, bufs, T, r, s, ws, reps=5):
         torch.cuda.synchronize()
         out[name] = (kind, ev[0].elapsed_time(ev[1]) / 1e3 / reps, sum(work(b["lin"]) for b in bufs))
     return out
+
+
+def measure_ablation(api, torch, synth, np, bufs, reps=5):
+    """Data-type ablation on the seven 7B weights (N(0, 0.02)) and on a seeded
+    outlier tensor (the 70B stream recipe, k-projection shape 1024 x 8192):
+    relative rms error sqrt(sum (w' - w)^2 / sum w^2) of NF4 and INT4 absmax
+    quantization (both with an fp32 absmax per 64 weights, so only the levels
+    differ), and the INT4 quantize throughput.  The error sums are fp64
+    reductions of the GPU-dequantized weights (measurement, not the path)."""
+    def rel_err(w, wd):
+        d = wd.double() - w.double()
+        return (d * d).sum(), (w.double() * w.double()).sum()
+
+    out = {}
+    for name, ws in (("normal_7b", [b["w"] for b in bufs]),
+                     ("outliers_70b_k", [torch.from_numpy(synth.outlier_weight_bf16(
+                         synth.rng_for(5, 0, 1, synth.ROLE_W), (1024, 8192)).view(np.int16))
+                         .view(torch.bfloat16).cuda()])):
+        acc = {"nf4": [0.0, 0.0], "int4": [0.0, 0.0]}
+        for w in ws:
+            for dt, q, dq in (("nf4", api.nf4_quantize, api.nf4_dequantize),
+                              ("int4", api.int4_quantize, api.int4_dequantize)):
+                e, n = rel_err(w, dq(q(w)))
+                acc[dt][0] += float(e)
+                acc[dt][1] += float(n)
+        out[name] = {dt: (a[0] / a[1]) ** 0.5 for dt, a in acc.items()}
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    qs = [api.int4_quantize(b["w"]) for b in bufs]
+    ev[0].record()
+    for _ in range(reps):
+        for b, q in zip(bufs, qs):
+            api.int4_quantize(b["w"])
+    ev[1].record()
+    torch.cuda.synchronize()
+    secs = ev[0].elapsed_time(ev[1]) / 1e3 / reps
+    nbytes = sum(2 * b["lin"].N * b["lin"].K + storage_bytes_sq(b["lin"].N * b["lin"].K) for b in bufs)
+    return out, secs, nbytes
 
 
 def storage_bytes_sq(numel):
@@ -386,6 +425,11 @@ def main():
             comp[name] = {"TFLOP/s": round(amt / secs / 1e12, 1),
                           "frac_of_mfma_peak": round(amt / secs / MFMA_BF16_PEAK, 4), "ms": round(1e3 * secs, 4),
                           "note": "single quantization (fp32 absmax per 64 weights)"}
+    abl, secs, nbytes = measure_ablation(api, torch, synth, np, bufs)
+    comp["int4_ablation"] = {
+        "relative_rms_error": {k: {dt: round(e, 5) for dt, e in v.items()} for k, v in abl.items()},
+        "int4_quantize_GB/s": round(nbytes / secs / 1e9, 1),
+        "note": "NF4 vs INT4 absmax levels, fp32 absmax per 64 weights for both"}
     secs, nbytes = measure_merge(api, torch, layers, sets, r, s)
     comp["merge"] = {"GB/s": round(nbytes / secs / 1e9, 1), "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
                      "us_per_layer_set": round(1e6 * secs, 2),

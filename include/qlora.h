@@ -216,6 +216,19 @@ int qlora_merge_lora_sq(const uint8_t* codes, const float* absmax, int64_t K, in
                         const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
                         float scaling, uint16_t* w_out, void* stream);
 
+/*
+ * INT4 absmax quantization: the baseline of the data-type ablation.
+ *   Source: "QLoRA 原理精讲" section 2.1 (why not INT4: 16 uniform integer
+ *   levels [-8, 7], against NF4's equal-probability levels).  Same blocks,
+ *   absmax and storage as nf4_quantize / nf4_dequantize, with the levels
+ *   v_i = fl32((i - 8) / 7) in place of the NF4 codewords: code = level
+ *   nearest to fl32(w / c1), exact ties to the lower code, all-zero blocks
+ *   code 8; w' = RNE_bf16(fl32(v[code] * c1)).  Not used by the layer entry
+ *   points; arguments and errors as for nf4_quantize / nf4_dequantize.
+ */
+int int4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, void* stream);
+int int4_dequantize(const uint8_t* codes, const float* absmax, int64_t numel, uint16_t* w_out, void* stream);
+
 /* qlora_status_string - static, NUL-terminated description of a status code. */
 const char* qlora_status_string(int status);
 

@@ -30,6 +30,8 @@ _SIGS = {
                                         _c_p]),
     "nf4_quantize": (ctypes.c_int, [_c_p, _c_i64, _c_p, _c_p, _c_p]),
     "nf4_dequantize": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_p, _c_p]),
+    "int4_quantize": (ctypes.c_int, [_c_p, _c_i64, _c_p, _c_p, _c_p]),
+    "int4_dequantize": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_p, _c_p]),
     "qlora_linear_fwd_sq": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                            ctypes.c_float, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "qlora_linear_bwd_input_sq": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_i64,
@@ -176,6 +178,26 @@ def nf4_dequantize(qw, out=None):
         out = torch.empty((qw.N, qw.K), dtype=torch.bfloat16, device=qw.codes.device)
     _dev(out, torch.bfloat16, "out")
     _check("nf4_dequantize", lib().nf4_dequantize(_ptr(qw.codes), _ptr(qw.absmax), qw.numel, _ptr(out), _stream()))
+    return out
+
+
+def int4_quantize(w):
+    """bf16 weight on the GPU -> NF4WeightSQ-shaped pair holding INT4 absmax codes (ablation baseline)."""
+    _dev(w, torch.bfloat16, "w")
+    numel = w.numel()
+    N, K = (w.shape[0], w.shape[1]) if w.dim() == 2 else (1, numel)
+    codes = torch.empty(numel // 2, dtype=torch.uint8, device=w.device)
+    absmax = torch.empty(max(numel // 64, 1), dtype=torch.float32, device=w.device)
+    _check("int4_quantize", lib().int4_quantize(_ptr(w), numel, _ptr(codes), _ptr(absmax), _stream()))
+    return NF4WeightSQ(codes, absmax, N, K)
+
+
+def int4_dequantize(qw, out=None):
+    if out is None:
+        out = torch.empty((qw.N, qw.K), dtype=torch.bfloat16, device=qw.codes.device)
+    _dev(out, torch.bfloat16, "out")
+    _check("int4_dequantize", lib().int4_dequantize(_ptr(qw.codes), _ptr(qw.absmax), qw.numel, _ptr(out),
+                                                     _stream()))
     return out
 
 

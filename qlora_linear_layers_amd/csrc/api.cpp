@@ -48,11 +48,19 @@ bool scales_aligned(const ql::BlockScales& sc) {
     return (!sc.fp8 || aligned16(sc.fp8)) && (!sc.sup || aligned16(sc.sup)) && (!sc.absmax || aligned16(sc.absmax));
 }
 
-int dequantize_impl(const uint8_t* codes, ql::BlockScales sc, int64_t numel, uint16_t* w_out, void* stream) {
+int dequantize_impl(const uint8_t* codes, ql::BlockScales sc, int64_t numel, uint16_t* w_out, void* stream,
+                    bool int4 = false) {
     if (!codes || !scales_present(sc) || !w_out) return QLORA_ERR_NULL;
     if (numel <= 0 || numel % 64 || numel > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
     if (!aligned16(w_out) || !aligned16(codes) || !scales_aligned(sc)) return QLORA_ERR_ALIGN;
-    return dev(ql::launch_dequantize(codes, sc, numel, w_out, static_cast<hipStream_t>(stream)));
+    return dev(ql::launch_dequantize(codes, sc, numel, w_out, static_cast<hipStream_t>(stream), int4));
+}
+
+int quantize_sq_impl(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, void* stream, bool int4) {
+    if (!w || !codes || !absmax) return QLORA_ERR_NULL;
+    if (numel <= 0 || numel % 64 || numel > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(codes) || !aligned16(absmax)) return QLORA_ERR_ALIGN;
+    return dev(ql::launch_quantize_sq(w, numel, codes, absmax, static_cast<hipStream_t>(stream), int4));
 }
 
 int fwd_impl(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* codes, ql::BlockScales sc,
@@ -174,10 +182,15 @@ int nf4_dequantize_dq(const uint8_t* codes, const uint8_t* absmax_fp8, const flo
 }
 
 int nf4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, void* stream) {
-    if (!w || !codes || !absmax) return QLORA_ERR_NULL;
-    if (numel <= 0 || numel % 64 || numel > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
-    if (!aligned16(w) || !aligned16(codes) || !aligned16(absmax)) return QLORA_ERR_ALIGN;
-    return dev(ql::launch_quantize_sq(w, numel, codes, absmax, static_cast<hipStream_t>(stream)));
+    return quantize_sq_impl(w, numel, codes, absmax, stream, false);
+}
+
+int int4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, void* stream) {
+    return quantize_sq_impl(w, numel, codes, absmax, stream, true);
+}
+
+int int4_dequantize(const uint8_t* codes, const float* absmax, int64_t numel, uint16_t* w_out, void* stream) {
+    return dequantize_impl(codes, sq_scales(absmax), numel, w_out, stream, true);
 }
 
 int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t numel, uint16_t* w_out, void* stream) {

@@ -34,23 +34,17 @@ double inverse_phi(double p) {
     return x;
 }
 
-Codebook g_codebook;
-EncodeTable g_table;
+Codebook g_codebook, g_int4_codebook;
+EncodeTable g_table, g_int4_table;
 std::once_flag g_once;
 
-void build_all() {
-    const double d = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0));
-    const double z = inverse_phi(d);
-    double v[16];
-    for (int j = 1; j <= 7; ++j) v[7 - j] = -inverse_phi(0.5 + j * (d - 0.5) / 7.0) / z;
-    v[7] = 0.0;
-    for (int j = 1; j <= 8; ++j) v[7 + j] = inverse_phi(0.5 + j * (d - 0.5) / 8.0) / z;
-    for (int i = 0; i < 16; ++i) g_codebook.q[i] = (float)v[i];
-
-    // Decision midpoints of neighbouring fp32 codewords (exact in fp64), then
-    // the per-cell (base, threshold) lookup used by the encoder kernels.
+// Decision midpoints of neighbouring fp32 codewords (exact in fp64), then the
+// per-cell (base, threshold) lookup used by the encoder kernels.  Valid for any
+// ascending codebook on [-1, 1] whose neighbouring midpoints are more than 1/16
+// apart (NF4: at least 0.08; INT4: 1/7).
+void build_table(const Codebook& cb, EncodeTable& tab) {
     double mid[15];
-    for (int i = 0; i < 15; ++i) mid[i] = 0.5 * ((double)g_codebook.q[i] + (double)g_codebook.q[i + 1]);
+    for (int i = 0; i < 15; ++i) mid[i] = 0.5 * ((double)cb.q[i] + (double)cb.q[i + 1]);
     for (int c = 0; c < 34; ++c) {
         const double lo = c / 16.0 - 1.0, hi = (c + 1) / 16.0 - 1.0;
         uint32_t base = 0;
@@ -63,9 +57,26 @@ void build_all() {
                 thr = t;
             }
         }
-        g_table.base[c] = base;
-        g_table.thr[c] = thr;
+        tab.base[c] = base;
+        tab.thr[c] = thr;
     }
+}
+
+void build_all() {
+    const double d = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0));
+    const double z = inverse_phi(d);
+    double v[16];
+    for (int j = 1; j <= 7; ++j) v[7 - j] = -inverse_phi(0.5 + j * (d - 0.5) / 7.0) / z;
+    v[7] = 0.0;
+    for (int j = 1; j <= 8; ++j) v[7 + j] = inverse_phi(0.5 + j * (d - 0.5) / 8.0) / z;
+    for (int i = 0; i < 16; ++i) g_codebook.q[i] = (float)v[i];
+
+    build_table(g_codebook, g_table);
+
+    // INT4 absmax levels (i - 8) / 7 ("QLoRA 原理精讲" section 2.1: 16 uniform
+    // integers [-8, 7]; +absmax lands on 7), the baseline of the data-type ablation
+    for (int i = 0; i < 16; ++i) g_int4_codebook.q[i] = (float)((i - 8) / 7.0);
+    build_table(g_int4_codebook, g_int4_table);
 }
 
 }  // namespace
@@ -78,6 +89,16 @@ const Codebook& host_codebook() {
 const EncodeTable& host_encode_table() {
     std::call_once(g_once, build_all);
     return g_table;
+}
+
+const Codebook& host_int4_codebook() {
+    std::call_once(g_once, build_all);
+    return g_int4_codebook;
+}
+
+const EncodeTable& host_int4_encode_table() {
+    std::call_once(g_once, build_all);
+    return g_int4_table;
 }
 
 }  // namespace ql

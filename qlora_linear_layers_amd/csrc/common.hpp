@@ -32,6 +32,9 @@ struct EncodeTable {
 // Host: the library's codebook and encoder table (computed once, thread-safe).
 const Codebook& host_codebook();
 const EncodeTable& host_encode_table();
+// INT4 absmax levels (i - 8) / 7 and their encoder table (data-type ablation)
+const Codebook& host_int4_codebook();
+const EncodeTable& host_int4_encode_table();
 
 // ------------------------------------------------------------------ bf16
 
@@ -204,8 +207,11 @@ struct BlockScales {
 
 hipError_t launch_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* fp8,
                            float* superscale, hipStream_t s);
-hipError_t launch_quantize_sq(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, hipStream_t s);
-hipError_t launch_dequantize(const uint8_t* codes, BlockScales sc, int64_t numel, uint16_t* out, hipStream_t s);
+// int4: the INT4 absmax levels instead of NF4 (single quantization only)
+hipError_t launch_quantize_sq(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, hipStream_t s,
+                              bool int4 = false);
+hipError_t launch_dequantize(const uint8_t* codes, BlockScales sc, int64_t numel, uint16_t* out, hipStream_t s,
+                             bool int4 = false);
 
 // Forward calls with at most this many tokens take the decode (small-M MFMA) path.
 constexpr int64_t kGemvMaxT = 16;

@@ -24,8 +24,11 @@ namespace ql {
 // division instead, which is the definition itself.
 //
 // SQ: single quantization (the first level alone): each block's fp32 absmax
-// c1 is stored as it is and there is no second level.
-template <bool SQ>
+// c1 is stored as it is and there is no second level.  EXACT: every ratio by
+// correctly rounded division (the INT4 levels have exact midpoints such as
+// 1/14 that ratios of bf16 values can reach, so the reciprocal shortcut does
+// not hold for them).
+template <bool SQ, bool EXACT>
 __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ w, int64_t nblocks,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ fp8,
                                                   float* __restrict__ superscale, float* __restrict__ absmax,
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ w
         m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, false));
         const float c1 = __uint_as_float(m << 16);
         const float r = c1 > 0.0f ? __builtin_amdgcn_rcpf(c1) : 0.0f;
-        const bool exact = c1 != 0.0f && (c1 < 0x1p-64f || c1 > 0x1p64f);
+        const bool exact = c1 != 0.0f && (EXACT || c1 < 0x1p-64f || c1 > 0x1p64f);
 
         float n[8];
 #pragma unroll
@@ -122,16 +125,21 @@ hipError_t launch_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uin
                            float* superscale, hipStream_t s) {
     const int64_t nblocks = numel / kBlock;
     const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
-    hipLaunchKernelGGL(k_quantize<false>, dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes, fp8,
+    hipLaunchKernelGGL((k_quantize<false, false>), dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes, fp8,
                        superscale, nullptr, host_encode_table());
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_sq(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, hipStream_t s) {
+hipError_t launch_quantize_sq(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, hipStream_t s,
+                              bool int4) {
     const int64_t nblocks = numel / kBlock;
     const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
-    hipLaunchKernelGGL(k_quantize<true>, dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes, nullptr,
-                       nullptr, absmax, host_encode_table());
+    if (int4)
+        hipLaunchKernelGGL((k_quantize<true, true>), dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes,
+                           nullptr, nullptr, absmax, host_int4_encode_table());
+    else
+        hipLaunchKernelGGL((k_quantize<true, false>), dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes,
+                           nullptr, nullptr, absmax, host_encode_table());
     return hipGetLastError();
 }
 
@@ -192,18 +200,18 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint32_t* __restrict__
     }
 }
 
-hipError_t launch_dequantize(const uint8_t* codes, BlockScales sc, int64_t numel, uint16_t* out, hipStream_t s) {
+hipError_t launch_dequantize(const uint8_t* codes, BlockScales sc, int64_t numel, uint16_t* out, hipStream_t s,
+                             bool int4) {
+    const Codebook& cb = int4 ? host_int4_codebook() : host_codebook();
     const int64_t nunits = numel / 8;
     const int64_t per_wg = 256 * kDeqUnits;
     const dim3 grid((unsigned)((nunits + per_wg - 1) / per_wg));
     const uint32_t* c = reinterpret_cast<const uint32_t*>(codes);
     u32x4_t* o = reinterpret_cast<u32x4_t*>(out);
     if (sc.single())
-        hipLaunchKernelGGL(k_dequantize<true>, grid, dim3(256), 0, s, c, nullptr, nullptr, sc.absmax, nunits, o,
-                           host_codebook());
+        hipLaunchKernelGGL(k_dequantize<true>, grid, dim3(256), 0, s, c, nullptr, nullptr, sc.absmax, nunits, o, cb);
     else
-        hipLaunchKernelGGL(k_dequantize<false>, grid, dim3(256), 0, s, c, sc.fp8, sc.sup, nullptr, nunits, o,
-                           host_codebook());
+        hipLaunchKernelGGL(k_dequantize<false>, grid, dim3(256), 0, s, c, sc.fp8, sc.sup, nullptr, nunits, o, cb);
     return hipGetLastError();
 }
 

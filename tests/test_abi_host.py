@@ -171,3 +171,12 @@ def test_single_quantization_validation(L):
     assert m(FAKE, None, 128, 64, FAKE, FAKE, 16, 0.5, FAKE, None) == NULL
     assert m(FAKE, FAKE, 128, 60, FAKE, FAKE, 16, 0.5, FAKE, None) == SHAPE
     assert m(FAKE, MIS, 128, 64, FAKE, FAKE, 16, 0.5, FAKE, None) == ALIGN
+
+
+def test_int4_validation(L):
+    assert L.int4_quantize(None, 64, FAKE, FAKE, None) == NULL
+    assert L.int4_quantize(FAKE, 65, FAKE, FAKE, None) == SHAPE
+    assert L.int4_quantize(FAKE, 64, MIS, FAKE, None) == ALIGN
+    assert L.int4_dequantize(FAKE, None, 64, FAKE, None) == NULL
+    assert L.int4_dequantize(FAKE, FAKE, -64, FAKE, None) == SHAPE
+    assert L.int4_dequantize(FAKE, FAKE, 64, MIS, None) == ALIGN
