@@ -18,6 +18,7 @@ Sources (titles of the pages, with the part each function follows):
     receive gradients).
   * "QLoRA 原理精讲", section 2.1 (why not INT4: the uniform 16-level baseline
     of the data-type ablation).
+  * "QLoRA 原理精讲", section 3 pitfall 4 (the fp16 compute dtype).
   * "QLoRA 原理精讲", section 2.5 and section 3 pitfall 3 (merging the adapter
     back into BF16 weights).
   * The Volcengine article on LoRA / Q-LoRA / PortLLM, sections 3.1, 3.2 and 3.4
@@ -44,6 +45,10 @@ from .linear import (
     lora_grads,
 )
 from .merge import merge_lora, merge_lora_f64, merge_lora_rows
+from .f16 import (
+    f16_bits_to_f64, round_to_f16_bits, quantize_nf4_dq_f16, dequantize_nf4_dq_f16, dequantize_rows_f16,
+    linear_fwd_f16, linear_fwd_at_f16, linear_bwd_f16, merge_lora_f16,
+)
 from .int4 import (
     int4_levels, int4_levels_f32, int4_midpoints, int4_encode, quantize_int4, dequantize_int4,
     relative_rms_error,
