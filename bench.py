@@ -16,8 +16,8 @@ roofline: the sum over all phases of their roofline time (algorithmic bytes at
 for the GEMM phases) divided by the measured step time.  Per-phase durations
 come from HIP events recorded on the stream the kernels run on.  Outside the
 step, `components` also carries the decode forward (T = 1 / 4 / 8), the LoRA
-merge, the single-quantization variant and the NF4-vs-INT4 data-type ablation
-measured on the same seven linears.
+merge, the single-quantization variant, the fp16 compute type and the
+NF4-vs-INT4 data-type ablation measured on the same seven linears.
 """
 import argparse
 import json
@@ -241,6 +241,48 @@ def measure_ablation(api, torch, synth, np, bufs, reps=5):
     return out, secs, nbytes
 
 
+def measure_f16(api, torch, bufs, T, r, s, ws, reps=5):
+    """The fp16 compute type on the same seven linears (the step's tensors
+    converted to fp16; the storage format is the bf16 path's): quantize from
+    fp16 weights, dequantize to fp16, forward and backward with s X A reused,
+    each over `reps` passes with HIP events.  Returns {phase: (kind, seconds, amount)}."""
+    h = [{k: b[k].to(torch.float16) for k in ("w", "x", "dy", "a", "b")} for b in bufs]
+    for hb, b in zip(h, bufs):
+        hb["qw"] = api.nf4_quantize_dq(hb["w"])
+        for k in ("wd", "y", "dx", "da", "db"):
+            hb[k] = torch.empty_like(b[k], dtype=torch.float16)
+    ops = {
+        "quantize_f16": ("hbm", lambda hb: api.nf4_quantize_dq_into(hb["w"], hb["qw"]),
+                         lambda l: phase_work(l, T, r)["quantize"][1]),
+        "dequantize_f16": ("hbm", lambda hb: api.nf4_dequantize_dq(hb["qw"], out=hb["wd"]),
+                           lambda l: phase_work(l, T, r)["dequantize"][1]),
+        "forward_f16": ("mfma", lambda hb: api.qlora_linear_fwd(hb["x"], hb["qw"], hb["a"], hb["b"], s, workspace=ws,
+                                                                 out=hb["y"]),
+                        lambda l: phase_work(l, T, r)["forward"][1]),
+        "backward_f16": ("mfma", lambda hb: (api.qlora_linear_fwd(hb["x"], hb["qw"], hb["a"], hb["b"], s, workspace=ws,
+                                                                   out=hb["y"]),
+                                             api.qlora_linear_bwd_input(hb["dy"], hb["qw"], hb["a"], hb["b"], s,
+                                                                        x=hb["x"], lora_grads=True, workspace=ws,
+                                                                        dx=hb["dx"], d_lora_a=hb["da"],
+                                                                        d_lora_b=hb["db"], reuse_forward=True)),
+                         lambda l: phase_work(l, T, r)["forward"][1] + phase_work(l, T, r)["backward"][1]),
+    }
+    out = {}
+    for name, (kind, fn, work) in ops.items():
+        for hb in h:
+            fn(hb)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            for hb in h:
+                fn(hb)
+        ev[1].record()
+        torch.cuda.synchronize()
+        out[name] = (kind, ev[0].elapsed_time(ev[1]) / 1e3 / reps, sum(work(b["lin"]) for b in bufs))
+    return out
+
+
 def storage_bytes_sq(numel):
     """Codes + one fp32 absmax per 64 weights."""
     return numel // 2 + 4 * (numel // 64)
@@ -425,6 +467,15 @@ def main():
             comp[name] = {"TFLOP/s": round(amt / secs / 1e12, 1),
                           "frac_of_mfma_peak": round(amt / secs / MFMA_BF16_PEAK, 4), "ms": round(1e3 * secs, 4),
                           "note": "single quantization (fp32 absmax per 64 weights)"}
+    for name, (kind, secs, amt) in measure_f16(api, torch, bufs, T, r, s, ws).items():
+        note = "fp16 compute type" + (" (forward + backward pass, s X A reused)" if name == "backward_f16" else "")
+        if kind == "hbm":
+            comp[name] = {"GB/s": round(amt / secs / 1e9, 1), "frac_of_hbm_peak": round(amt / secs / HBM_PEAK, 4),
+                          "ms": round(1e3 * secs, 4), "note": note}
+        else:
+            comp[name] = {"TFLOP/s": round(amt / secs / 1e12, 1),
+                          "frac_of_mfma_peak": round(amt / secs / MFMA_BF16_PEAK, 4), "ms": round(1e3 * secs, 4),
+                          "note": note}
     abl, secs, nbytes = measure_ablation(api, torch, synth, np, bufs)
     comp["int4_ablation"] = {
         "relative_rms_error": {k: {dt: round(e, 5) for dt, e in v.items()} for k, v in abl.items()},

@@ -229,6 +229,37 @@ int qlora_merge_lora_sq(const uint8_t* codes, const float* absmax, int64_t K, in
 int int4_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, void* stream);
 int int4_dequantize(const uint8_t* codes, const float* absmax, int64_t numel, uint16_t* w_out, void* stream);
 
+/*
+ * fp16 compute type.
+ *   Source: "QLoRA 原理精讲" section 3, pitfall 4 (GPUs without bfloat16 switch
+ *   the compute dtype to FP16).  Each _f16 entry point has the arguments,
+ *   sizes, workspace and errors of the entry point it is named after, with
+ *   every 16-bit tensor in IEEE fp16 instead of bf16: the weight given to
+ *   nf4_quantize_dq_f16, the dequantized weight, x, y, dy, dx, lora_a,
+ *   lora_b and the adapter gradients.  The storage (codes, FP8 constants,
+ *   super-scales) is the same as for bf16.  Every rounding to 16 bits (the
+ *   dequantized weight w' = RNE_fp16(fl32(q[code] * c1')), the outputs) is
+ *   to nearest even in fp16; products accumulate in fp32 on the fp16 MFMA.
+ *   The layer's intermediates s X A and s dY B^T travel as fp16 hi + lo pairs.
+ */
+int nf4_quantize_dq_f16(const uint16_t* w, int64_t numel,
+                        uint8_t* codes, uint8_t* absmax_fp8, float* superscale, void* stream);
+int nf4_dequantize_dq_f16(const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale,
+                          int64_t numel, uint16_t* w_out, void* stream);
+int qlora_linear_fwd_f16(const uint16_t* x, int64_t T, int64_t K, int64_t N,
+                         const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale,
+                         const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling,
+                         uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+int qlora_linear_bwd_input_f16(const uint16_t* dy, int64_t T, int64_t K, int64_t N,
+                               const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale,
+                               const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling,
+                               uint16_t* dx, const uint16_t* x,
+                               uint16_t* d_lora_a, uint16_t* d_lora_b,
+                               void* workspace, size_t workspace_bytes, unsigned flags, void* stream);
+int qlora_merge_lora_f16(const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale,
+                         int64_t K, int64_t N, const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
+                         float scaling, uint16_t* w_out, void* stream);
+
 /* qlora_status_string - static, NUL-terminated description of a status code. */
 const char* qlora_status_string(int status);
 

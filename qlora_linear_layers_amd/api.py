@@ -41,6 +41,9 @@ _SIGS = {
                                            _c_p]),
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
+# fp16 compute type: the same arguments as the bf16 entry point of the same stem
+for _n in ("nf4_quantize_dq", "nf4_dequantize_dq", "qlora_linear_fwd", "qlora_linear_bwd_input", "qlora_merge_lora"):
+    _SIGS[_n + "_f16"] = _SIGS[_n]
 EXPORTS = tuple(_SIGS)
 
 REUSE_FORWARD = 1   # QLORA_BWD_REUSE_FORWARD
@@ -93,6 +96,25 @@ def _dev(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+_HALF = (torch.bfloat16, torch.float16)
+
+
+def _ct(t, name):
+    """Compute type of a 16-bit tensor: '' for bf16, '_f16' for fp16."""
+    if t.dtype not in _HALF:
+        raise TypeError(f"{name} must be bfloat16 or float16, got {t.dtype}")
+    return "_f16" if t.dtype == torch.float16 else ""
+
+
+def _entry(stem, ct, qw):
+    """C entry point for a compute type and a storage format."""
+    if isinstance(qw, NF4WeightSQ):
+        if ct:
+            raise ValueError("single quantization has no fp16 entry points")
+        return stem + "_sq"
+    return stem + ct
+
+
 @dataclass
 class NF4Weight:
     """Storage triple of a quantized [N, K] weight (device tensors)."""
@@ -133,31 +155,35 @@ def nf4_build_codebook():
 
 
 def nf4_quantize_dq(w):
-    """bf16 weight [N, K] (or flat) on the GPU -> NF4Weight."""
-    _dev(w, torch.bfloat16, "w")
+    """bf16 (or fp16) weight [N, K] (or flat) on the GPU -> NF4Weight."""
+    ct = _ct(w, "w")
+    _dev(w, w.dtype, "w")
     numel = w.numel()
     N, K = (w.shape[0], w.shape[1]) if w.dim() == 2 else (1, numel)
     codes = torch.empty(numel // 2, dtype=torch.uint8, device=w.device)
     fp8 = torch.empty(max(numel // 64, 1), dtype=torch.uint8, device=w.device)
     sup = torch.empty(max(-(-numel // 16384), 1), dtype=torch.float32, device=w.device)
-    _check("nf4_quantize_dq", lib().nf4_quantize_dq(_ptr(w), numel, _ptr(codes), _ptr(fp8), _ptr(sup), _stream()))
+    fn = "nf4_quantize_dq" + ct
+    _check(fn, getattr(lib(), fn)(_ptr(w), numel, _ptr(codes), _ptr(fp8), _ptr(sup), _stream()))
     return NF4Weight(codes, fp8, sup, N, K)
 
 
 def nf4_quantize_dq_into(w, qw):
     """Quantize into an existing NF4Weight (no allocation)."""
-    _dev(w, torch.bfloat16, "w")
-    _check("nf4_quantize_dq", lib().nf4_quantize_dq(_ptr(w), w.numel(), _ptr(qw.codes), _ptr(qw.absmax_fp8),
-                                                     _ptr(qw.superscale), _stream()))
+    fn = "nf4_quantize_dq" + _ct(w, "w")
+    _dev(w, w.dtype, "w")
+    _check(fn, getattr(lib(), fn)(_ptr(w), w.numel(), _ptr(qw.codes), _ptr(qw.absmax_fp8), _ptr(qw.superscale),
+                                  _stream()))
 
 
-def nf4_dequantize_dq(qw, out=None):
-    """NF4Weight -> bf16 [N, K] on the GPU."""
+def nf4_dequantize_dq(qw, out=None, dtype=torch.bfloat16):
+    """NF4Weight -> [N, K] on the GPU, bf16 or (dtype / out fp16) fp16."""
     if out is None:
-        out = torch.empty((qw.N, qw.K), dtype=torch.bfloat16, device=qw.codes.device)
-    _dev(out, torch.bfloat16, "out")
-    _check("nf4_dequantize_dq", lib().nf4_dequantize_dq(_ptr(qw.codes), _ptr(qw.absmax_fp8), _ptr(qw.superscale),
-                                                         qw.numel, _ptr(out), _stream()))
+        out = torch.empty((qw.N, qw.K), dtype=dtype, device=qw.codes.device)
+    fn = "nf4_dequantize_dq" + _ct(out, "out")
+    _dev(out, out.dtype, "out")
+    _check(fn, getattr(lib(), fn)(_ptr(qw.codes), _ptr(qw.absmax_fp8), _ptr(qw.superscale), qw.numel, _ptr(out),
+                                  _stream()))
     return out
 
 
@@ -218,19 +244,21 @@ def workspace_for(T, K, N, r, device):
 
 
 def qlora_linear_fwd(x, qw, lora_a=None, lora_b=None, scaling=1.0, workspace=None, out=None):
-    """Y = X W'^T + scaling (X A) B; x [T, K] bf16 -> y [T, N] bf16.  `qw` is an NF4Weight
-    (double quantization) or an NF4WeightSQ (single quantization, the _sq entry point)."""
-    _dev(x, torch.bfloat16, "x")
-    _dev(lora_a, torch.bfloat16, "lora_a")
-    _dev(lora_b, torch.bfloat16, "lora_b")
+    """Y = X W'^T + scaling (X A) B; x [T, K] -> y [T, N], bf16 or fp16 (the _f16 entry point).
+    `qw` is an NF4Weight (double quantization) or an NF4WeightSQ (single quantization, _sq)."""
+    ct = _ct(x, "x")
+    _dev(x, x.dtype, "x")
+    _dev(lora_a, x.dtype, "lora_a")
+    _dev(lora_b, x.dtype, "lora_b")
     T, K = x.shape
     r = 0 if lora_a is None else lora_a.shape[1]
     if out is None:
-        out = torch.empty((T, qw.N), dtype=torch.bfloat16, device=x.device)
+        out = torch.empty((T, qw.N), dtype=x.dtype, device=x.device)
     if workspace is None:
         workspace = workspace_for(T, K, qw.N, r, x.device)
-    sfx, sc = _scale_args(qw)
-    fn = "qlora_linear_fwd" + sfx
+    _dev(out, x.dtype, "out")
+    sc = _scale_args(qw)[1]
+    fn = _entry("qlora_linear_fwd", ct, qw)
     _check(fn, getattr(lib(), fn)(
         _ptr(x), T, K, qw.N, _ptr(qw.codes), *sc, _ptr(lora_a), _ptr(lora_b),
         r, float(scaling), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
@@ -244,22 +272,25 @@ def qlora_linear_bwd_input(dy, qw, lora_a=None, lora_b=None, scaling=1.0, x=None
     just used (s X A is taken from it)."""
     if reuse_forward and workspace is None:
         raise ValueError("reuse_forward needs the forward's workspace")
-    _dev(dy, torch.bfloat16, "dy")
-    _dev(x, torch.bfloat16, "x")
+    ct = _ct(dy, "dy")
+    _dev(dy, dy.dtype, "dy")
+    _dev(x, dy.dtype, "x")
+    _dev(lora_a, dy.dtype, "lora_a")
+    _dev(lora_b, dy.dtype, "lora_b")
     T, N = dy.shape
     K = qw.K
     r = 0 if lora_a is None else lora_a.shape[1]
     if dx is None:
-        dx = torch.empty((T, K), dtype=torch.bfloat16, device=dy.device)
+        dx = torch.empty((T, K), dtype=dy.dtype, device=dy.device)
     if lora_grads:
         if d_lora_a is None:
-            d_lora_a = torch.empty((K, r), dtype=torch.bfloat16, device=dy.device)
+            d_lora_a = torch.empty((K, r), dtype=dy.dtype, device=dy.device)
         if d_lora_b is None:
-            d_lora_b = torch.empty((r, N), dtype=torch.bfloat16, device=dy.device)
+            d_lora_b = torch.empty((r, N), dtype=dy.dtype, device=dy.device)
     if workspace is None:
         workspace = workspace_for(T, K, N, r, dy.device)
-    sfx, sc = _scale_args(qw)
-    fn = "qlora_linear_bwd_input" + sfx
+    sc = _scale_args(qw)[1]
+    fn = _entry("qlora_linear_bwd_input", ct, qw)
     _check(fn, getattr(lib(), fn)(
         _ptr(dy), T, K, N, _ptr(qw.codes), *sc, _ptr(lora_a), _ptr(lora_b),
         r, float(scaling), _ptr(dx), _ptr(x), _ptr(d_lora_a) if lora_grads else None,
@@ -268,16 +299,18 @@ def qlora_linear_bwd_input(dy, qw, lora_a=None, lora_b=None, scaling=1.0, x=None
     return (dx, d_lora_a, d_lora_b) if lora_grads else (dx, None, None)
 
 
-def qlora_merge_lora(qw, lora_a=None, lora_b=None, scaling=1.0, out=None):
-    """W_m = RNE_bf16(W' + scaling (A B)^T) -> bf16 [N, K] (W' itself without an adapter)."""
-    _dev(lora_a, torch.bfloat16, "lora_a")
-    _dev(lora_b, torch.bfloat16, "lora_b")
+def qlora_merge_lora(qw, lora_a=None, lora_b=None, scaling=1.0, out=None, dtype=None):
+    """W_m = RNE_16(W' + scaling (A B)^T) -> [N, K] (W' itself without an adapter), in the
+    dtype of the adapters (else of `out`, else `dtype`, else bf16)."""
+    dt = lora_a.dtype if lora_a is not None else (out.dtype if out is not None else (dtype or torch.bfloat16))
+    _dev(lora_a, dt, "lora_a")
+    _dev(lora_b, dt, "lora_b")
     r = 0 if lora_a is None else lora_a.shape[1]
     if out is None:
-        out = torch.empty((qw.N, qw.K), dtype=torch.bfloat16, device=qw.codes.device)
-    _dev(out, torch.bfloat16, "out")
-    sfx, sc = _scale_args(qw)
-    fn = "qlora_merge_lora" + sfx
+        out = torch.empty((qw.N, qw.K), dtype=dt, device=qw.codes.device)
+    _dev(out, dt, "out")
+    sc = _scale_args(qw)[1]
+    fn = _entry("qlora_merge_lora", _ct(out, "out"), qw)
     _check(fn, getattr(lib(), fn)(
         _ptr(qw.codes), *sc, qw.K, qw.N, _ptr(lora_a), _ptr(lora_b), r, float(scaling), _ptr(out), _stream()))
     return out

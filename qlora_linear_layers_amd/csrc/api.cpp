@@ -10,15 +10,15 @@
 namespace ql {
 hipError_t launch_transpose_a(const uint16_t* lora_a, const LoraPlan& pl, uint8_t* ws, hipStream_t s);
 hipError_t launch_lora_down_x(const uint16_t* x, float scaling, const LoraPlan& pl, uint8_t* ws, bool transposed,
-                              hipStream_t s);
+                              hipStream_t s, bool f16);
 hipError_t launch_lora_down_dy(const uint16_t* dy, const uint16_t* lora_b, float scaling, const LoraPlan& pl,
-                               uint8_t* ws, bool transposed, hipStream_t s);
+                               uint8_t* ws, bool transposed, hipStream_t s, bool f16);
 hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, BlockScales sc, const uint16_t* lora_b,
-                      const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s);
+                      const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s, bool f16);
 hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
-                     const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s);
+                     const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s, bool f16);
 hipError_t launch_lora_grads(const uint16_t* x, const uint16_t* dy, const LoraPlan& pl, uint8_t* ws,
-                             uint16_t* d_lora_a, uint16_t* d_lora_b, hipStream_t s);
+                             uint16_t* d_lora_a, uint16_t* d_lora_b, hipStream_t s, bool f16);
 }  // namespace ql
 
 namespace {
@@ -49,11 +49,11 @@ bool scales_aligned(const ql::BlockScales& sc) {
 }
 
 int dequantize_impl(const uint8_t* codes, ql::BlockScales sc, int64_t numel, uint16_t* w_out, void* stream,
-                    bool int4 = false) {
+                    bool int4 = false, bool f16 = false) {
     if (!codes || !scales_present(sc) || !w_out) return QLORA_ERR_NULL;
     if (numel <= 0 || numel % 64 || numel > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
     if (!aligned16(w_out) || !aligned16(codes) || !scales_aligned(sc)) return QLORA_ERR_ALIGN;
-    return dev(ql::launch_dequantize(codes, sc, numel, w_out, static_cast<hipStream_t>(stream), int4));
+    return dev(ql::launch_dequantize(codes, sc, numel, w_out, static_cast<hipStream_t>(stream), int4, f16));
 }
 
 int quantize_sq_impl(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, void* stream, bool int4) {
@@ -65,7 +65,7 @@ int quantize_sq_impl(const uint16_t* w, int64_t numel, uint8_t* codes, float* ab
 
 int fwd_impl(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* codes, ql::BlockScales sc,
              const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling, uint16_t* y, void* workspace,
-             size_t workspace_bytes, void* stream) {
+             size_t workspace_bytes, void* stream, bool f16 = false) {
     if (!x || !codes || !scales_present(sc) || !y) return QLORA_ERR_NULL;
     if (r > 0 && (!lora_a || !lora_b)) return QLORA_ERR_NULL;
     if (int st = check_linear_shape(T, K, N, r)) return st;
@@ -81,20 +81,20 @@ int fwd_impl(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* 
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (T <= ql::kGemvMaxT)      // decode sizes: small-M MFMA, split-k partials
-        return dev(ql::launch_gemv(x, codes, sc, lora_a, lora_b, scaling, pl, ws, y, s));
+        return dev(ql::launch_gemv(x, codes, sc, lora_a, lora_b, scaling, pl, ws, y, s, f16));
     if (r > 0) {
         if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
         // s X A in both layouts: the transposed copy lets a backward with
         // QLORA_BWD_REUSE_FORWARD take the adapter gradients without recomputing it
-        if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, true, s))) return st;
+        if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, true, s, f16))) return st;
     }
-    return dev(ql::launch_fwd(x, codes, sc, lora_b, pl, ws, y, s));
+    return dev(ql::launch_fwd(x, codes, sc, lora_b, pl, ws, y, s, f16));
 }
 
 int bwd_impl(const uint16_t* dy, int64_t T, int64_t K, int64_t N, const uint8_t* codes, ql::BlockScales sc,
              const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling, uint16_t* dx, const uint16_t* x,
              uint16_t* d_lora_a, uint16_t* d_lora_b, void* workspace, size_t workspace_bytes, unsigned flags,
-             void* stream) {
+             void* stream, bool f16 = false) {
     if (!dy || !codes || !scales_present(sc) || !dx) return QLORA_ERR_NULL;
     if (r > 0 && (!lora_a || !lora_b)) return QLORA_ERR_NULL;
     const bool grads = d_lora_a || d_lora_b;
@@ -116,20 +116,20 @@ int bwd_impl(const uint16_t* dy, int64_t T, int64_t K, int64_t N, const uint8_t*
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (r > 0)
-        if (int st = dev(ql::launch_lora_down_dy(dy, lora_b, scaling, pl, ws, grads, s))) return st;
-    if (int st = dev(ql::launch_dx(dy, codes, sc, lora_a, pl, ws, dx, s))) return st;
+        if (int st = dev(ql::launch_lora_down_dy(dy, lora_b, scaling, pl, ws, grads, s, f16))) return st;
+    if (int st = dev(ql::launch_dx(dy, codes, sc, lora_a, pl, ws, dx, s, f16))) return st;
     if (grads) {
         if (!reuse) {
             if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
-            if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, true, s))) return st;
+            if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, true, s, f16))) return st;
         }
-        if (int st = dev(ql::launch_lora_grads(x, dy, pl, ws, d_lora_a, d_lora_b, s))) return st;
+        if (int st = dev(ql::launch_lora_grads(x, dy, pl, ws, d_lora_a, d_lora_b, s, f16))) return st;
     }
     return QLORA_OK;
 }
 
 int merge_impl(const uint8_t* codes, ql::BlockScales sc, int64_t K, int64_t N, const uint16_t* lora_a,
-               const uint16_t* lora_b, int64_t r, float scaling, uint16_t* w_out, void* stream) {
+               const uint16_t* lora_b, int64_t r, float scaling, uint16_t* w_out, void* stream, bool f16 = false) {
     if (!codes || !scales_present(sc) || !w_out) return QLORA_ERR_NULL;
     if (r > 0 && (!lora_a || !lora_b)) return QLORA_ERR_NULL;
     if (K < 64 || K % 64 || N < 8 || N % 8 || K > (int64_t(1) << 20) || N > (int64_t(1) << 20) || N * K >= (int64_t(1) << 32))
@@ -140,7 +140,17 @@ int merge_impl(const uint8_t* codes, ql::BlockScales sc, int64_t K, int64_t N, c
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
     if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
-    return dev(ql::launch_merge(codes, sc, lora_a, lora_b, K, N, r, scaling, w_out, static_cast<hipStream_t>(stream)));
+    return dev(ql::launch_merge(codes, sc, lora_a, lora_b, K, N, r, scaling, w_out, static_cast<hipStream_t>(stream),
+                                f16));
+}
+
+int quantize_dq_impl(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* absmax_fp8, float* superscale,
+                     void* stream, bool f16) {
+    if (!w || !codes || !absmax_fp8 || !superscale) return QLORA_ERR_NULL;
+    if (numel <= 0 || numel % 64 || numel > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(codes) || !aligned16(absmax_fp8) || !aligned16(superscale))
+        return QLORA_ERR_ALIGN;
+    return dev(ql::launch_quantize(w, numel, codes, absmax_fp8, superscale, static_cast<hipStream_t>(stream), f16));
 }
 
 }  // namespace
@@ -169,11 +179,12 @@ int nf4_build_codebook(float codebook_out[16]) {
 
 int nf4_quantize_dq(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* absmax_fp8, float* superscale,
                     void* stream) {
-    if (!w || !codes || !absmax_fp8 || !superscale) return QLORA_ERR_NULL;
-    if (numel <= 0 || numel % 64 || numel > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
-    if (!aligned16(w) || !aligned16(codes) || !aligned16(absmax_fp8) || !aligned16(superscale))
-        return QLORA_ERR_ALIGN;
-    return dev(ql::launch_quantize(w, numel, codes, absmax_fp8, superscale, static_cast<hipStream_t>(stream)));
+    return quantize_dq_impl(w, numel, codes, absmax_fp8, superscale, stream, false);
+}
+
+int nf4_quantize_dq_f16(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* absmax_fp8, float* superscale,
+                        void* stream) {
+    return quantize_dq_impl(w, numel, codes, absmax_fp8, superscale, stream, true);
 }
 
 int nf4_dequantize_dq(const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale, int64_t numel,
@@ -250,6 +261,35 @@ int qlora_merge_lora(const uint8_t* codes, const uint8_t* absmax_fp8, const floa
 int qlora_merge_lora_sq(const uint8_t* codes, const float* absmax, int64_t K, int64_t N, const uint16_t* lora_a,
                         const uint16_t* lora_b, int64_t r, float scaling, uint16_t* w_out, void* stream) {
     return merge_impl(codes, sq_scales(absmax), K, N, lora_a, lora_b, r, scaling, w_out, stream);
+}
+
+int nf4_dequantize_dq_f16(const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale, int64_t numel,
+                          uint16_t* w_out, void* stream) {
+    return dequantize_impl(codes, dq_scales(absmax_fp8, superscale), numel, w_out, stream, false, true);
+}
+
+int qlora_linear_fwd_f16(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* codes,
+                         const uint8_t* absmax_fp8, const float* superscale, const uint16_t* lora_a,
+                         const uint16_t* lora_b, int64_t r, float scaling, uint16_t* y, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    return fwd_impl(x, T, K, N, codes, dq_scales(absmax_fp8, superscale), lora_a, lora_b, r, scaling, y, workspace,
+                    workspace_bytes, stream, true);
+}
+
+int qlora_linear_bwd_input_f16(const uint16_t* dy, int64_t T, int64_t K, int64_t N, const uint8_t* codes,
+                               const uint8_t* absmax_fp8, const float* superscale, const uint16_t* lora_a,
+                               const uint16_t* lora_b, int64_t r, float scaling, uint16_t* dx, const uint16_t* x,
+                               uint16_t* d_lora_a, uint16_t* d_lora_b, void* workspace, size_t workspace_bytes,
+                               unsigned flags, void* stream) {
+    return bwd_impl(dy, T, K, N, codes, dq_scales(absmax_fp8, superscale), lora_a, lora_b, r, scaling, dx, x,
+                    d_lora_a, d_lora_b, workspace, workspace_bytes, flags, stream, true);
+}
+
+int qlora_merge_lora_f16(const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale, int64_t K,
+                         int64_t N, const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling,
+                         uint16_t* w_out, void* stream) {
+    return merge_impl(codes, dq_scales(absmax_fp8, superscale), K, N, lora_a, lora_b, r, scaling, w_out, stream,
+                      true);
 }
 
 }  // extern "C"

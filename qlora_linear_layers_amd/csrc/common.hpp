@@ -48,12 +48,58 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
 // Round-to-nearest-even of two fp32 values into one packed dword: `a` in the
 // low half (lower address), `b` in the high half (v_cvt_pk_bf16_f32).
 QL_DEV uint32_t pack_bf16x2(float a, float b) {
     f32x2_t v = {a, b};
     bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
     return __builtin_bit_cast(uint32_t, r);
+}
+
+// ------------------------------------------------------------------ 16-bit compute type
+//
+// The layer computes in bf16, or in fp16 when F16 (the compute dtype the pages
+// tell users to switch to on GPUs without bf16, "QLoRA 原理精讲" section 3,
+// pitfall 4).  Only packing, unpacking and the MFMA opcode depend on it; a
+// 16-byte fragment travels as bf16x8_t bits either way.
+template <bool F16>
+QL_DEV uint32_t pack16x2(float a, float b) {     // RNE, `a` in the low half
+    if constexpr (F16) {
+        f32x2_t v = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));   // v_cvt_pk_f16_f32
+    } else {
+        return pack_bf16x2(a, b);
+    }
+}
+template <bool F16>
+QL_DEV float lo16(uint32_t v) {
+    if constexpr (F16) return (float)__builtin_bit_cast(f16x2_t, v)[0];
+    else return bf16lo(v);
+}
+template <bool F16>
+QL_DEV float hi16(uint32_t v) {
+    if constexpr (F16) return (float)__builtin_bit_cast(f16x2_t, v)[1];
+    else return bf16hi(v);
+}
+template <bool F16>
+QL_DEV f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <bool F16>
+QL_DEV f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // ------------------------------------------------------------------ FP8 E4M3FN
@@ -205,22 +251,23 @@ struct BlockScales {
     bool single() const { return absmax != nullptr; }
 };
 
+// f16: the weights (quantize) / the output (dequantize, merge) are fp16
 hipError_t launch_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* fp8,
-                           float* superscale, hipStream_t s);
+                           float* superscale, hipStream_t s, bool f16 = false);
 // int4: the INT4 absmax levels instead of NF4 (single quantization only)
 hipError_t launch_quantize_sq(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, hipStream_t s,
                               bool int4 = false);
 hipError_t launch_dequantize(const uint8_t* codes, BlockScales sc, int64_t numel, uint16_t* out, hipStream_t s,
-                             bool int4 = false);
+                             bool int4 = false, bool f16 = false);
 
 // Forward calls with at most this many tokens take the decode (small-M MFMA) path.
 constexpr int64_t kGemvMaxT = 16;
 struct LoraPlan;
 size_t gemv_workspace(int64_t T, int64_t K, int64_t N, int64_t r_pad);
 hipError_t launch_merge(const uint8_t* codes, BlockScales sc, const uint16_t* lora_a, const uint16_t* lora_b,
-                        int64_t K, int64_t N, int64_t r, float scaling, uint16_t* w_out, hipStream_t s);
+                        int64_t K, int64_t N, int64_t r, float scaling, uint16_t* w_out, hipStream_t s, bool f16);
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
                        const uint16_t* lora_b, float scaling, const LoraPlan& pl, uint8_t* ws, uint16_t* y,
-                       hipStream_t s);
+                       hipStream_t s, bool f16);
 
 }  // namespace ql

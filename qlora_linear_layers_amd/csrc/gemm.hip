@@ -24,7 +24,6 @@
 
 namespace ql {
 
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 
@@ -141,10 +140,11 @@ QL_DEV bf16x8_t lds_frag(const lds8_t* base, int row, int chunk) {
     return *reinterpret_cast<const lds_bf16x8_t*>(base + lds_off(row, chunk));
 }
 
-// C[a][b] to out[b][a] (a contiguous), bf16: four consecutive a of one b per
-// MFMA row group g of a 32 x 32 accumulator, as one 8-byte store.
-QL_DEV void store4_bf16(const f32x16_t& v, int g, uint16_t* out, int64_t ldo, int64_t a, int64_t b) {
-    const u32x2_t o = {pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3])};
+// C[a][b] to out[b][a] (a contiguous), 16-bit: four consecutive a of one b
+// per MFMA row group g of a 32 x 32 accumulator, as one 8-byte store.
+template <bool F16>
+QL_DEV void store4_16(const f32x16_t& v, int g, uint16_t* out, int64_t ldo, int64_t a, int64_t b) {
+    const u32x2_t o = {pack16x2<F16>(v[4 * g], v[4 * g + 1]), pack16x2<F16>(v[4 * g + 2], v[4 * g + 3])};
     *reinterpret_cast<u32x2_t*>(out + b * ldo + a) = o;
 }
 
@@ -264,21 +264,23 @@ QL_DEV void read_q(QPr& q, const u32x4_t (&wc)[2], int s, uint32_t lane8) {
         }
 }
 
+template <bool F16>
 QL_DEV void make_a(AFr& a, const QPr& q, const float (&c1p)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         u32x4_t o;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) o[b] = pack_bf16x2(__fmul_rn(q[i][b][0], c1p[i]), __fmul_rn(q[i][b][1], c1p[i]));
+        for (int b = 0; b < 4; ++b) o[b] = pack16x2<F16>(__fmul_rn(q[i][b][0], c1p[i]), __fmul_rn(q[i][b][1], c1p[i]));
         a[i] = __builtin_bit_cast(bf16x8_t, o);
     }
 }
 
+template <bool F16>
 QL_DEV void mfma16(f32x16_t (&acc)[2][8], const AFr& a, const XFr& x) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], x[j], acc[0][j], 0, 0, 0);
-        acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], x[j], acc[1][j], 0, 0, 0);
+        acc[0][j] = mfma32x32x16<F16>(a[0], x[j], acc[0][j]);
+        acc[1][j] = mfma32x32x16<F16>(a[1], x[j], acc[1][j]);
     }
 }
 
@@ -302,7 +304,7 @@ QL_DEV void interleave() {
 // the codebook pairs of step s+2 are read, and the A fragments of step s+1
 // are built from pairs read during step s-1.  On entry xa / aa hold step 0 of
 // tile kt and qa the pairs of step 1; on exit the same for tile kt+1.
-template <int P, bool SQ>
+template <int P, bool SQ, bool F16>
 QL_DEV void fwd_tile(FwdPipe<SQ>& pp, int kt, f32x16_t (&acc)[2][8], lds8_t* lX, int r, int h, XFr& xa, AFr& aa,
                      QPr& qa, float (&c1p)[2]) {
     constexpr int Q = P ^ 1;
@@ -315,22 +317,22 @@ QL_DEV void fwd_tile(FwdPipe<SQ>& pp, int kt, f32x16_t (&acc)[2][8], lds8_t* lX,
     // step 0
     read_x(xb_, xb, 1, r, h);
     read_q(qb, pp.wc[P], 2, pp.lane8);
-    make_a(ab, qa, c1p);
-    mfma16(acc, aa, xa);
+    make_a<F16>(ab, qa, c1p);
+    mfma16<F16>(acc, aa, xa);
     interleave<16, 16, 16>();
     __builtin_amdgcn_sched_barrier(0);
     // step 1
     read_x(xa, xb, 2, r, h);
     read_q(qa, pp.wc[P], 3, pp.lane8);
-    make_a(aa, qb, c1p);
-    mfma16(acc, ab, xb_);
+    make_a<F16>(aa, qb, c1p);
+    mfma16<F16>(acc, ab, xb_);
     interleave<16, 16, 16>();
     __builtin_amdgcn_sched_barrier(0);
     // step 2: the pairs of the next tile's step 0 come from code set Q
     read_x(xb_, xb, 3, r, h);
     read_q(qb, pp.wc[Q], 0, pp.lane8);
-    make_a(ab, qa, c1p);
-    mfma16(acc, aa, xa);
+    make_a<F16>(ab, qa, c1p);
+    mfma16<F16>(acc, aa, xa);
     interleave<16, 16, 16>();
     __builtin_amdgcn_sched_barrier(0);
     pp.load_w(kt + 2, P);                     // code set P is no longer read
@@ -338,19 +340,19 @@ QL_DEV void fwd_tile(FwdPipe<SQ>& pp, int kt, f32x16_t (&acc)[2][8], lds8_t* lX,
     // step 3: the first half of its MFMAs cover the X store and the barrier
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[0], xb_[j], acc[0][j], 0, 0, 0);
-        acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[1], xb_[j], acc[1][j], 0, 0, 0);
+        acc[0][j] = mfma32x32x16<F16>(ab[0], xb_[j], acc[0][j]);
+        acc[1][j] = mfma32x32x16<F16>(ab[1], xb_[j], acc[1][j]);
     }
     pp.store_x(Q, lX + Q * FwdPipe<SQ>::kTile);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     read_x(xa, lX + Q * FwdPipe<SQ>::kTile, 0, r, h);
     read_q(qa, pp.wc[Q], 1, pp.lane8);
-    make_a(aa, qb, n1p);
+    make_a<F16>(aa, qb, n1p);
 #pragma unroll
     for (int j = 4; j < 8; ++j) {
-        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[0], xb_[j], acc[0][j], 0, 0, 0);
-        acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[1], xb_[j], acc[1][j], 0, 0, 0);
+        acc[0][j] = mfma32x32x16<F16>(ab[0], xb_[j], acc[0][j]);
+        acc[1][j] = mfma32x32x16<F16>(ab[1], xb_[j], acc[1][j]);
     }
     interleave<8, 8, 8>();
     __builtin_amdgcn_sched_barrier(0);
@@ -358,7 +360,7 @@ QL_DEV void fwd_tile(FwdPipe<SQ>& pp, int kt, f32x16_t (&acc)[2][8], lds8_t* lX,
     c1p[1] = n1p[1];
 }
 
-template <bool SQ>
+template <bool SQ, bool F16>
 __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     lds8_t* smem = (lds8_t*)(smem_raw);
@@ -425,17 +427,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
     {
         QPr q0;
         read_q(q0, pp.wc[0], 0, pp.lane8);
-        make_a(aa, q0, c1p);
+        make_a<F16>(aa, q0, c1p);
         read_q(qa, pp.wc[0], 1, pp.lane8);
         read_x(xa, lX, 0, r, h);
     }
     const int KT = pp.KT;
     int kt = 0;
     for (; kt + 1 < KT; kt += 2) {
-        fwd_tile<0>(pp, kt, acc, lX, r, h, xa, aa, qa, c1p);
-        fwd_tile<1>(pp, kt + 1, acc, lX, r, h, xa, aa, qa, c1p);
+        fwd_tile<0, SQ, F16>(pp, kt, acc, lX, r, h, xa, aa, qa, c1p);
+        fwd_tile<1, SQ, F16>(pp, kt + 1, acc, lX, r, h, xa, aa, qa, c1p);
     }
-    if (kt < KT) fwd_tile<0>(pp, kt, acc, lX, r, h, xa, aa, qa, c1p);
+    if (kt < KT) fwd_tile<0, SQ, F16>(pp, kt, acc, lX, r, h, xa, aa, qa, c1p);
 
     if (p.r > 0) {
         // reduction over [hi | lo] of s X A (tokens) against B^T stacked twice (rows n)
@@ -458,8 +460,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const bf16x8_t b = lds_frag(lX, 32 * j + r, 4 * h + s);
-                    acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0][j], 0, 0, 0);
-                    acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1][j], 0, 0, 0);
+                    acc[0][j] = mfma32x32x16<F16>(a0, b, acc[0][j]);
+                    acc[1][j] = mfma32x32x16<F16>(a1, b, acc[1][j]);
                 }
             }
             __syncthreads();
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int64_t n = n0 + 64 * w + 32 * i + 8 * g + 4 * h;
-                if (n < p.N) store4_bf16(acc[i][j], g, p.y, p.N, n, t);
+                if (n < p.N) store4_16<F16>(acc[i][j], g, p.y, p.N, n, t);
             }
         }
 }
@@ -580,8 +582,9 @@ struct DxPipe {
             qv[i] = *lds_at<f32x2_t>(addr);
         }
     }
-    // k columns 2j, 2j+1 of the patch: w' = RNE_bf16(fl32(q * c1')), eight n
+    // k columns 2j, 2j+1 of the patch: w' = RNE_16(fl32(q * c1')), eight n
     // values per column packed into one 16-byte chunk
+    template <bool F16>
     QL_DEV void finish(const DqPairs& qv, int par, int j, lds8_t* l) const {
         const int kc = threadIdx.x & 31, ng = threadIdx.x >> 5;
         float v[8][2];
@@ -595,7 +598,7 @@ struct DxPipe {
         for (int c = 0; c < 2; ++c) {
             u32x4_t o;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) o[p] = pack_bf16x2(v[2 * p][c], v[2 * p + 1][c]);
+            for (int p = 0; p < 4; ++p) o[p] = pack16x2<F16>(v[2 * p][c], v[2 * p + 1][c]);
             *reinterpret_cast<lds_u32x4_t*>(l + lds_off_w(kc * 8 + 2 * j + c, ng)) = o;
         }
     }
@@ -616,25 +619,26 @@ QL_DEV void dx_reads(DxFrags& f, const lds8_t* lw, const lds8_t* ld, int s, int 
     for (int j = 0; j < 4; ++j) f.b[j] = lds_frag(ld, wb * 128 + j * 32 + r, 2 * s + h);
 }
 
+template <bool F16>
 QL_DEV void dx_mfma(f32x16_t (&acc)[4][4], const DxFrags& f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = mfma32x32x16<F16>(f.a[i], f.b[j], acc[i][j]);
 }
 
 // MFMAs of output rows i in [i0, i1) only (used to split a step around the barrier)
-template <int i0, int i1>
+template <int i0, int i1, bool F16>
 QL_DEV void dx_mfma_rows(f32x16_t (&acc)[4][4], const DxFrags& f) {
 #pragma unroll
     for (int i = i0; i < i1; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = mfma32x32x16<F16>(f.a[i], f.b[j], acc[i][j]);
 }
 
-template <int P>
+template <int P, bool F16>
 QL_DEV void dx_tile(DxPipe& pp, int kt, f32x16_t (&acc)[4][4], lds8_t* lW, lds8_t* lD, int wa, int wb, int r,
                     int h, DxFrags& f0, DqPairs& qa) {
     constexpr int Q = P ^ 1;
@@ -647,27 +651,27 @@ QL_DEV void dx_tile(DxPipe& pp, int kt, f32x16_t (&acc)[4][4], lds8_t* lW, lds8_
     // step 0
     dx_reads<true>(f1, cw, cd, 1, wa, wb, r, h);
     pp.lookup(qb, Q, 1);
-    pp.finish(qa, Q, 0, nw);
-    dx_mfma(acc, f0);
+    pp.template finish<F16>(qa, Q, 0, nw);
+    dx_mfma<F16>(acc, f0);
     interleave<16, 16, 16>();
     __builtin_amdgcn_sched_barrier(0);
     // step 1
     dx_reads<true>(f0, cw, cd, 2, wa, wb, r, h);
     pp.lookup(qa, Q, 2);
-    pp.finish(qb, Q, 1, nw);
-    dx_mfma(acc, f1);
+    pp.template finish<F16>(qb, Q, 1, nw);
+    dx_mfma<F16>(acc, f1);
     interleave<16, 16, 16>();
     __builtin_amdgcn_sched_barrier(0);
     // step 2
     dx_reads<true>(f1, cw, cd, 3, wa, wb, r, h);
     pp.lookup(qb, Q, 3);
-    pp.finish(qa, Q, 2, nw);
-    dx_mfma(acc, f0);
+    pp.template finish<F16>(qa, Q, 2, nw);
+    dx_mfma<F16>(acc, f0);
     interleave<16, 16, 16>();
     __builtin_amdgcn_sched_barrier(0);
     // step 3
-    dx_mfma_rows<0, 2>(acc, f1);
-    pp.finish(qb, Q, 3, nw);
+    dx_mfma_rows<0, 2, F16>(acc, f1);
+    pp.template finish<F16>(qb, Q, 3, nw);
     pp.store_dy(nd);
     interleave<8, 0, 8, 8, 4>();
     __builtin_amdgcn_sched_barrier(0);
@@ -675,12 +679,13 @@ QL_DEV void dx_tile(DxPipe& pp, int kt, f32x16_t (&acc)[4][4], lds8_t* lW, lds8_
     __syncthreads();
     dx_reads<true>(f0, nw, nd, 0, wa, wb, r, h);
     pp.lookup(qa, P, 0);                      // tile kt+2's codes (set P, loaded during tile kt-1)
-    dx_mfma_rows<2, 4>(acc, f1);
+    dx_mfma_rows<2, 4, F16>(acc, f1);
     interleave<8, 16, 0>();
     __builtin_amdgcn_sched_barrier(0);
     pp.load_w(kt + 3, Q);                     // set Q (tile kt+1) is no longer read
 }
 
+template <bool F16>
 __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     lds8_t* smem = (lds8_t*)(smem_raw);
@@ -738,7 +743,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         pp.lookup(qa, 0, j);
-        pp.finish(qa, 0, j, lW);
+        pp.template finish<F16>(qa, 0, j, lW);
     }
     pp.store_dy(lD);
     pp.load_dy(1);
@@ -750,10 +755,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
     const int NT = pp.NT;
     int kt = 0;
     for (; kt + 1 < NT; kt += 2) {
-        dx_tile<0>(pp, kt, acc, lW, lD, wa, wb, r, h, f0, qa);
-        dx_tile<1>(pp, kt + 1, acc, lW, lD, wa, wb, r, h, f0, qa);
+        dx_tile<0, F16>(pp, kt, acc, lW, lD, wa, wb, r, h, f0, qa);
+        dx_tile<1, F16>(pp, kt + 1, acc, lW, lD, wa, wb, r, h, f0, qa);
     }
-    if (kt < NT) dx_tile<0>(pp, kt, acc, lW, lD, wa, wb, r, h, f0, qa);
+    if (kt < NT) dx_tile<0, F16>(pp, kt, acc, lW, lD, wa, wb, r, h, f0, qa);
 
     if (p.r > 0) {
         // LoRA term (s dY B^T) A^T: reduction over [hi | lo] of s dY B^T against A stacked twice
@@ -773,7 +778,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
             for (int s = 0; s < 4; ++s) {
                 DxFrags f;
                 dx_reads<false>(f, lW, lD, s, wa, wb, r, h);
-                dx_mfma(acc, f);
+                dx_mfma<F16>(acc, f);
             }
         }
     }
@@ -787,7 +792,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int64_t k = k0 + wa * 128 + i * 32 + g * 8 + h * 4;
-                if (k < p.K) store4_bf16(acc[i][j], g, p.dx, p.K, k, t);
+                if (k < p.K) store4_16<F16>(acc[i][j], g, p.dx, p.K, k, t);
             }
         }
 }
@@ -806,7 +811,7 @@ hipError_t set_smem(F* f, size_t bytes) {
 }  // namespace
 
 hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, BlockScales sc, const uint16_t* lora_b,
-                      const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s) {
+                      const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s, bool f16) {
     FwdArgs a{x, codes, sc.fp8, sc.sup, sc.absmax, lora_b, reinterpret_cast<const uint16_t*>(ws + pl.off_ps_hi),
               reinterpret_cast<const uint16_t*>(ws + pl.off_ps_lo), y,
               pl.T, pl.K, pl.N, pl.r, pl.r_pad};
@@ -818,11 +823,12 @@ hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, BlockScales sc, c
         hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kThreads), lds, s, a, host_codebook());
         return hipGetLastError();
     };
-    return sc.single() ? go(k_fwd<true>) : go(k_fwd<false>);
+    if (f16) return sc.single() ? go(k_fwd<true, true>) : go(k_fwd<false, true>);
+    return sc.single() ? go(k_fwd<true, false>) : go(k_fwd<false, false>);
 }
 
 hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
-                     const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s) {
+                     const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s, bool f16) {
     float* sclt = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + pl.off_scl);
     const int64_t nsc = (pl.K / 64) * pl.N;
     const dim3 sg((unsigned)ceil_div(nsc, 256));
@@ -836,11 +842,14 @@ hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, BlockScales sc, c
              reinterpret_cast<const uint16_t*>(ws + pl.off_gs_lo), sclt, dx,
              pl.T, pl.K, pl.N, pl.r, pl.r_pad};
     const size_t lds = kDxSmem;
-    hipError_t e = set_smem(k_dx, lds);
-    if (e != hipSuccess) return e;
     const int64_t tiles = ceil_div(pl.K, 256) * ceil_div(pl.T, 256);
-    hipLaunchKernelGGL(k_dx, dim3((unsigned)tiles), dim3(kThreads), lds, s, a, host_codebook());
-    return hipGetLastError();
+    auto go = [&](auto kern) {
+        hipError_t e = set_smem(kern, lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kThreads), lds, s, a, host_codebook());
+        return hipGetLastError();
+    };
+    return f16 ? go(k_dx<true>) : go(k_dx<false>);
 }
 
 }  // namespace ql

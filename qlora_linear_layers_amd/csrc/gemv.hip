@@ -23,6 +23,8 @@
 // row group are added in LDS in wave order and one fp32 partial per
 // (k split, token, row) is written.  The LoRA down projection runs as extra
 // workgroups of the same launch over 256-wide k slices (VALU, lane = rank).
+#include <type_traits>
+
 #include "common.hpp"
 #include "plan.hpp"
 
@@ -30,7 +32,6 @@ namespace ql {
 
 namespace {
 
-typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
 
 }  // namespace
 
@@ -61,7 +62,7 @@ constexpr size_t kDecLds = kWideTableBytes;   // pair table; later reused for th
 // staged in LDS; waves 0-3 take a quarter of the slice each: lane j loads
 // its 64 A values in one burst and reads X as LDS broadcasts.  Every thread
 // of the workgroup reaches every barrier.
-template <int TT>
+template <int TT, bool F16>
 __device__ __forceinline__ void lora_down_block(const GemvArgs& p, uint8_t* dyn, int lb) {
     typedef __attribute__((address_space(3))) float g_lds_f32_t;
     lds8_t* xl = (lds8_t*)dyn;                                         // [TT][kLoraSlice] bf16
@@ -90,7 +91,7 @@ __device__ __forceinline__ void lora_down_block(const GemvArgs& p, uint8_t* dyn,
         const uint32_t row = (uint32_t)(p.r * 2);
         float av[64];
 #pragma unroll
-        for (int i = 0; i < 64; ++i) av[i] = bf16lo(bload2(ra, vo + i * row, 0));
+        for (int i = 0; i < 64; ++i) av[i] = lo16<F16>(bload2(ra, vo + i * row, 0));
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
             float v = acc[t];
@@ -99,8 +100,8 @@ __device__ __forceinline__ void lora_down_block(const GemvArgs& p, uint8_t* dyn,
                 const u32x4_t xv = *reinterpret_cast<const lds_u32x4_t*>(xl + (t * kLoraSlice + kw + 8 * c) * 2);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    v = fmaf(bf16lo(xv[e]), av[8 * c + 2 * e], v);
-                    v = fmaf(bf16hi(xv[e]), av[8 * c + 2 * e + 1], v);
+                    v = fmaf(lo16<F16>(xv[e]), av[8 * c + 2 * e], v);
+                    v = fmaf(hi16<F16>(xv[e]), av[8 * c + 2 * e + 1], v);
                 }
             }
             acc[t] = v;
@@ -126,11 +127,11 @@ __device__ __forceinline__ void lora_down_block(const GemvArgs& p, uint8_t* dyn,
 // Launch 1.  Blocks [0, gemv_blocks) are base blocks: rows [n0, n0 + 128) over
 // the k split ks (512 k); the rest are LoRA down-projection blocks.  SQ: the
 // block constant is the stored fp32 absmax (single quantization).
-template <int TT, bool SQ>
+template <int TT, bool SQ, bool F16>
 __global__ __launch_bounds__(kDecThreads) void k_gemv(GemvArgs p, Codebook cb) {
     extern __shared__ __align__(16) uint8_t dyn[];
     if ((int)blockIdx.x >= p.gemv_blocks) {
-        lora_down_block<TT>(p, dyn, (int)blockIdx.x - p.gemv_blocks);
+        lora_down_block<TT, F16>(p, dyn, (int)blockIdx.x - p.gemv_blocks);
         return;
     }
     lds8_t* tbl = (lds8_t*)dyn;
@@ -186,10 +187,9 @@ __global__ __launch_bounds__(kDecThreads) void k_gemv(GemvArgs p, Codebook cb) {
                 // address bytes: [0] lane copy, [1] code byte b, [2..3] table base
                 const uint32_t addr = __builtin_amdgcn_perm(cw[c][j], lane8, 0x03020000u | ((4u + b) << 8));
                 const f32x2_t q = *lds_at<f32x2_t>(addr);
-                w[b] = pack_bf16x2(__fmul_rn(q[0], c1p), __fmul_rn(q[1], c1p));
+                w[b] = pack16x2<F16>(__fmul_rn(q[0], c1p), __fmul_rn(q[1], c1p));
             }
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v_t, xv[j]),
-                                                             __builtin_bit_cast(bf16x8v_t, w), acc[c], 0, 0, 0);
+            acc[c] = mfma16x16x32<F16>(__builtin_bit_cast(bf16x8_t, xv[j]), __builtin_bit_cast(bf16x8_t, w), acc[c]);
         }
     }
 
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kDecThreads) void k_gemv(GemvArgs p, Codebook cb) {
 // G group sums are added in g order.  The four wave sums of each output are
 // added in wave order, so the result does not depend on timing.
 constexpr int kFinCols = 64;
-template <int RP>
+template <int RP, bool F16>
 __global__ __launch_bounds__(256) void k_gemv_finalize(GemvArgs p) {
     constexpr int RQ = 16 * RP;                                        // ranks of B per wave
     __shared__ __align__(16) float pr[4 * 256];                        // group sums [G][W] float4
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256) void k_gemv_finalize(GemvArgs p) {
                 for (int q = 0; q < RQ / 4; ++q) {
                     const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(ps + t * p.r_pad + wave * RQ + 4 * q);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v = fmaf(sv[e], bf16lo(bv[4 * q + e]), v);
+                    for (int e = 0; e < 4; ++e) v = fmaf(sv[e], lo16<F16>(bv[4 * q + e]), v);
                 }
             }
             red[(wave * 16 + t) * kFinCols + lane] = v;
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(256) void k_gemv_finalize(GemvArgs p) {
         if (nn < p.N) {
             const float v = red[(0 * 16 + t) * kFinCols + l] + red[(1 * 16 + t) * kFinCols + l] +
                             red[(2 * 16 + t) * kFinCols + l] + red[(3 * 16 + t) * kFinCols + l];
-            p.y[t * p.N + nn] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+            p.y[t * p.N + nn] = (uint16_t)(pack16x2<F16>(v, 0.0f) & 0xFFFFu);
         }
     }
 }
@@ -351,7 +351,7 @@ size_t gemv_workspace(int64_t T, int64_t K, int64_t N, int64_t r_pad) {
 
 hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
                        const uint16_t* lora_b, float scaling, const LoraPlan& pl, uint8_t* ws, uint16_t* y,
-                       hipStream_t s) {
+                       hipStream_t s, bool f16) {
     GemvArgs a{x, codes, sc.fp8, sc.sup, sc.absmax, lora_a, lora_b, nullptr, nullptr, y, pl.T, pl.K, pl.N, pl.r, pl.r_pad,
                gemv_ks(pl.K), pl.r ? gemv_kl(pl.K) : 0, 0, scaling};
     a.part = reinterpret_cast<float*>(ws);
@@ -368,21 +368,27 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, BlockScales sc, 
         if (ae == hipSuccess) hipLaunchKernelGGL(kern, grid, dim3(kDecThreads), kDecLds, s, a, cb);
     };
     const bool sq = sc.single();
-    if (pl.T <= 1) sq ? go(k_gemv<1, true>) : go(k_gemv<1, false>);
-    else if (pl.T <= 2) sq ? go(k_gemv<2, true>) : go(k_gemv<2, false>);
-    else if (pl.T <= 4) sq ? go(k_gemv<4, true>) : go(k_gemv<4, false>);
-    else if (pl.T <= 8) sq ? go(k_gemv<8, true>) : go(k_gemv<8, false>);
-    else sq ? go(k_gemv<16, true>) : go(k_gemv<16, false>);
+    auto pick = [&](auto tt) {
+        constexpr int TT = decltype(tt)::value;
+        if (sq) f16 ? go(k_gemv<TT, true, true>) : go(k_gemv<TT, true, false>);
+        else f16 ? go(k_gemv<TT, false, true>) : go(k_gemv<TT, false, false>);
+    };
+    if (pl.T <= 1) pick(std::integral_constant<int, 1>{});
+    else if (pl.T <= 2) pick(std::integral_constant<int, 2>{});
+    else if (pl.T <= 4) pick(std::integral_constant<int, 4>{});
+    else if (pl.T <= 8) pick(std::integral_constant<int, 8>{});
+    else pick(std::integral_constant<int, 16>{});
     if (ae != hipSuccess) return ae;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 fg((unsigned)ceil_div(pl.N, kFinCols)), fb(256);
+    auto fin = [&](auto kern) { hipLaunchKernelGGL(kern, fg, fb, 0, s, a); };
     switch (pl.r_pad / 64) {
-        case 0: hipLaunchKernelGGL(k_gemv_finalize<0>, fg, fb, 0, s, a); break;
-        case 1: hipLaunchKernelGGL(k_gemv_finalize<1>, fg, fb, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(k_gemv_finalize<2>, fg, fb, 0, s, a); break;
-        case 3: hipLaunchKernelGGL(k_gemv_finalize<3>, fg, fb, 0, s, a); break;
-        default: hipLaunchKernelGGL(k_gemv_finalize<4>, fg, fb, 0, s, a); break;
+        case 0: f16 ? fin(k_gemv_finalize<0, true>) : fin(k_gemv_finalize<0, false>); break;
+        case 1: f16 ? fin(k_gemv_finalize<1, true>) : fin(k_gemv_finalize<1, false>); break;
+        case 2: f16 ? fin(k_gemv_finalize<2, true>) : fin(k_gemv_finalize<2, false>); break;
+        case 3: f16 ? fin(k_gemv_finalize<3, true>) : fin(k_gemv_finalize<3, false>); break;
+        default: f16 ? fin(k_gemv_finalize<4, true>) : fin(k_gemv_finalize<4, false>); break;
     }
     return hipGetLastError();
 }

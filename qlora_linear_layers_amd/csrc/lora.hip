@@ -36,17 +36,19 @@ namespace {
 
 constexpr int kThreads = 256;
 
+template <bool F16>
 QL_DEV f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    return mfma16x16x32<F16>(a, b, c);
 }
 
 QL_DEV bf16x8_t as_bf16x8(const u32x4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// hi = RNE_bf16(v), lo = RNE_bf16(v - hi) as 16-bit patterns
+// hi = RNE_16(v), lo = RNE_16(v - hi) as 16-bit patterns (bf16, or fp16 when F16)
+template <bool F16>
 QL_DEV void split_hi_lo(float v, uint16_t& hi, uint16_t& lo) {
-    const uint32_t hb = pack_bf16x2(v, 0.0f) & 0xFFFFu;
+    const uint32_t hb = pack16x2<F16>(v, 0.0f) & 0xFFFFu;
     hi = (uint16_t)hb;
-    lo = (uint16_t)(pack_bf16x2(v - bf16lo(hb), 0.0f) & 0xFFFFu);
+    lo = (uint16_t)(pack16x2<F16>(v - lo16<F16>(hb), 0.0f) & 0xFFFFu);
 }
 
 }  // namespace
@@ -100,9 +102,10 @@ struct DownArgs {
 };
 
 // v (already scaled) -> hi/lo at row t, column j of both layouts
+template <bool F16>
 QL_DEV void down_out(const DownArgs& a, int64_t t, int j, float v, bool rowmajor) {
     uint16_t h, lw;
-    split_hi_lo(v, h, lw);
+    split_hi_lo<F16>(v, h, lw);
     if (rowmajor) {
         if (t < a.T) {
             a.hi[t * a.r_pad + j] = h;
@@ -115,16 +118,16 @@ QL_DEV void down_out(const DownArgs& a, int64_t t, int j, float v, bool rowmajor
 }
 
 // sum[ROWS][R] (row stride R + 4) of rows t0 .. t0+ROWS-1 -> both output layouts
-template <int R, int ROWS>
+template <int R, int ROWS, bool F16>
 QL_DEV void down_emit(const DownArgs& a, const float* sum, int64_t t0) {
     for (int e = threadIdx.x; e < ROWS * R; e += kThreads) {      // [T][r_pad], j fastest
         const int tl = e / R, j = e % R;
-        down_out(a, t0 + tl, j, sum[tl * (R + 4) + j] * a.scale, true);
+        down_out<F16>(a, t0 + tl, j, sum[tl * (R + 4) + j] * a.scale, true);
     }
     if (a.hit)
         for (int e = threadIdx.x; e < ROWS * R; e += kThreads) {  // [r_pad][ldt], t fastest
             const int j = e / ROWS, tl = e % ROWS;
-            down_out(a, t0 + tl, j, sum[tl * (R + 4) + j] * a.scale, false);
+            down_out<F16>(a, t0 + tl, j, sum[tl * (R + 4) + j] * a.scale, false);
         }
 }
 
@@ -136,7 +139,7 @@ QL_DEV void down_emit(const DownArgs& a, const float* sum, int64_t t0) {
 // fragments, so every global load fetches whole cache lines and M is read
 // once per 64 rows.  With several splits each workgroup stores an fp32
 // partial (whole rows, through LDS) and k_down_fin adds them in split order.
-template <int RT>
+template <int RT, bool F16>
 __global__ __launch_bounds__(kThreads, 2) void k_down(DownArgs a) {
     constexpr int PD = RT <= 4 ? 4 : 2;
     constexpr int NX = 2;            // 16-byte chunks of the 64 x 64 S tile per thread
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(DownArgs a) {
 #pragma unroll
             for (int jt = 0; jt < RT; ++jt) {
                 const bf16x8_t mv = *reinterpret_cast<const lds_bf16x8_t*>(buf + kXT + lds_off(16 * jt + (l & 15), ch));
-                acc[jt] = mfma16(xv, mv, acc[jt]);
+                acc[jt] = mfma16<F16>(xv, mv, acc[jt]);
             }
         }
     };
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(DownArgs a) {
         for (int v = 0; v < 4; ++v) sum[(16 * w + 4 * (l >> 4) + v) * (R + 4) + 16 * jt + (l & 15)] = acc[jt][v];
     __syncthreads();
     if (a.splits == 1) {
-        down_emit<R, 64>(a, sum, t0);
+        down_emit<R, 64, F16>(a, sum, t0);
         return;
     }
     float* out = a.part + (int64_t)split * a.T * a.r_pad;     // whole rows, 16 bytes per lane
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(DownArgs a) {
 }
 
 // Split-ordered sum of the k_down partials of 16 rows, then both layouts.
-template <int RT>
+template <int RT, bool F16>
 __global__ __launch_bounds__(kThreads) void k_down_fin(DownArgs a) {
     constexpr int R = RT * 16;
     extern __shared__ __align__(16) uint8_t smem_raw[];
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void k_down_fin(DownArgs a) {
         for (int c = 0; c < 4; ++c) sum[tl * (R + 4) + j + c] = s4[c];
     }
     __syncthreads();
-    down_emit<R, 16>(a, sum, t0);
+    down_emit<R, 16, F16>(a, sum, t0);
 }
 
 // ------------------------------------------------------------------ adapter gradients
@@ -283,6 +286,7 @@ struct GradArgs {
 
 // part[split][c][j] = sum over the split's tokens of S[t][c] (V_hi + V_lo)[t][j]
 // for 128 columns c and 64 columns j (blockIdx.y picks the 64) per workgroup.
+template <bool F16>
 __global__ __launch_bounds__(kThreads, 1) void k_grad(GradArgs a) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     float* red = reinterpret_cast<float*>(smem_raw);     // [4 waves][8 i][4 jt][64 lanes][4]
@@ -338,8 +342,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grad(GradArgs a) {
             const bf16x8_t xi = as_bf16x8(o);
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) {
-                acc[i][jt] = mfma16(xi, as_bf16x8(vh[slot][jt]), acc[i][jt]);
-                acc[i][jt] = mfma16(xi, as_bf16x8(vl[slot][jt]), acc[i][jt]);
+                acc[i][jt] = mfma16<F16>(xi, as_bf16x8(vh[slot][jt]), acc[i][jt]);
+                acc[i][jt] = mfma16<F16>(xi, as_bf16x8(vl[slot][jt]), acc[i][jt]);
             }
         }
     };
@@ -391,6 +395,7 @@ struct GradFin {
     int transpose;
 };
 
+template <bool F16>
 __global__ __launch_bounds__(256) void k_grad_finalize(GradFin f0, GradFin f1, int blocks0) {
     __shared__ uint16_t tile[256][16 + 2];              // [j][c] for the transposed output
     const bool second = (int)blockIdx.x >= blocks0;
@@ -414,7 +419,7 @@ __global__ __launch_bounds__(256) void k_grad_finalize(GradFin f0, GradFin f1, i
             }
             for (; s < f.splits; ++s) sum += *reinterpret_cast<const f32x4_t*>(src + (int64_t)s * stride);
         }
-        const uint32_t p01 = pack_bf16x2(sum[0], sum[1]), p23 = pack_bf16x2(sum[2], sum[3]);
+        const uint32_t p01 = pack16x2<F16>(sum[0], sum[1]), p23 = pack16x2<F16>(sum[2], sum[3]);
         if (!f.transpose) {
             if (c < f.C && j < f.r) *reinterpret_cast<u32x2_t*>(f.out + c * f.r + j) = u32x2_t{p01, p23};
         } else {
@@ -443,42 +448,48 @@ hipError_t set_smem(F* f, size_t bytes) {
                                (int)bytes);
 }
 
-template <int RT>
+template <int RT, bool F16>
 hipError_t down_rt(const DownArgs& a, hipStream_t s) {
     constexpr int R = RT * 16;
     const size_t bufs = (size_t)2 * (64 + R) * 128, sums = (size_t)64 * (R + 4) * 4;
     const size_t lds = bufs > sums ? bufs : sums;
-    hipError_t e = set_smem(k_down<RT>, lds);
+    hipError_t e = set_smem(k_down<RT, F16>, lds);
     if (e != hipSuccess) return e;
     const unsigned tiles = (unsigned)ceil_div(a.T, 64);
-    hipLaunchKernelGGL(k_down<RT>, dim3(tiles * (unsigned)a.splits), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((k_down<RT, F16>), dim3(tiles * (unsigned)a.splits), dim3(kThreads), lds, s, a);
     if (a.splits > 1) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         const size_t fl = (size_t)16 * (R + 4) * 4;
-        hipLaunchKernelGGL(k_down_fin<RT>, dim3((unsigned)ceil_div(a.T, 16)), dim3(kThreads), fl, s, a);
+        hipLaunchKernelGGL((k_down_fin<RT, F16>), dim3((unsigned)ceil_div(a.T, 16)), dim3(kThreads), fl, s, a);
     }
     return hipGetLastError();
 }
 
-hipError_t down(const DownArgs& a, hipStream_t s) {
+template <bool F16>
+hipError_t down_t(const DownArgs& a, hipStream_t s) {
     switch (a.r_pad / 16) {
-        case 4: return down_rt<4>(a, s);
-        case 8: return down_rt<8>(a, s);
-        case 12: return down_rt<12>(a, s);
-        case 16: return down_rt<16>(a, s);
+        case 4: return down_rt<4, F16>(a, s);
+        case 8: return down_rt<8, F16>(a, s);
+        case 12: return down_rt<12, F16>(a, s);
+        case 16: return down_rt<16, F16>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
+hipError_t down(const DownArgs& a, hipStream_t s, bool f16) { return f16 ? down_t<true>(a, s) : down_t<false>(a, s); }
+
 constexpr size_t kGradSmem = (size_t)4 * 8 * 4 * 64 * 4 * 4;   // 128 KB
 
-hipError_t grad(const GradArgs& a, int splits, hipStream_t s) {
-    hipError_t e = set_smem(k_grad, kGradSmem);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_grad, dim3((unsigned)(a.cblocks * splits), (unsigned)(a.r_pad / 64)), dim3(kThreads),
-                       kGradSmem, s, a);
-    return hipGetLastError();
+hipError_t grad(const GradArgs& a, int splits, hipStream_t s, bool f16) {
+    auto go = [&](auto kern) {
+        hipError_t e = set_smem(kern, kGradSmem);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)(a.cblocks * splits), (unsigned)(a.r_pad / 64)), dim3(kThreads),
+                           kGradSmem, s, a);
+        return hipGetLastError();
+    };
+    return f16 ? go(k_grad<true>) : go(k_grad<false>);
 }
 
 }  // namespace
@@ -492,30 +503,30 @@ hipError_t launch_transpose_a(const uint16_t* lora_a, const LoraPlan& pl, uint8_
 
 // s X A -> P (hi/lo [T][r_pad]; also transposed when `transposed`).  Needs A^T in ws.
 hipError_t launch_lora_down_x(const uint16_t* x, float scaling, const LoraPlan& pl, uint8_t* ws, bool transposed,
-                              hipStream_t s) {
+                              hipStream_t s, bool f16) {
     DownArgs a{x, reinterpret_cast<const uint16_t*>(ws + pl.off_at), pl.T, pl.K, pl.ld_at, pl.r_pad, pl.r_pad,
                scaling,
                reinterpret_cast<uint16_t*>(ws + pl.off_ps_hi), reinterpret_cast<uint16_t*>(ws + pl.off_ps_lo),
                transposed ? reinterpret_cast<uint16_t*>(ws + pl.off_pst_hi) : nullptr,
                transposed ? reinterpret_cast<uint16_t*>(ws + pl.off_pst_lo) : nullptr, pl.T8, pl.ld_t,
                reinterpret_cast<float*>(ws + pl.off_dpart), pl.s_down_x};
-    return down(a, s);
+    return down(a, s, f16);
 }
 
 // s dY B^T -> G (hi/lo [T][r_pad] and transposed)
 hipError_t launch_lora_down_dy(const uint16_t* dy, const uint16_t* lora_b, float scaling, const LoraPlan& pl,
-                               uint8_t* ws, bool transposed, hipStream_t s) {
+                               uint8_t* ws, bool transposed, hipStream_t s, bool f16) {
     DownArgs a{dy, lora_b, pl.T, pl.N, pl.N, pl.r, pl.r_pad, scaling,
                reinterpret_cast<uint16_t*>(ws + pl.off_gs_hi), reinterpret_cast<uint16_t*>(ws + pl.off_gs_lo),
                transposed ? reinterpret_cast<uint16_t*>(ws + pl.off_gst_hi) : nullptr,
                transposed ? reinterpret_cast<uint16_t*>(ws + pl.off_gst_lo) : nullptr, pl.T8, pl.ld_t,
                reinterpret_cast<float*>(ws + pl.off_dpart), pl.s_down_dy};
-    return down(a, s);
+    return down(a, s, f16);
 }
 
 // dA = X^T G and dB = P^T dY from the transposed intermediates in ws.
 hipError_t launch_lora_grads(const uint16_t* x, const uint16_t* dy, const LoraPlan& pl, uint8_t* ws,
-                             uint16_t* d_lora_a, uint16_t* d_lora_b, hipStream_t s) {
+                             uint16_t* d_lora_a, uint16_t* d_lora_b, hipStream_t s, bool f16) {
     float* pda = reinterpret_cast<float*>(ws + pl.off_pda);
     float* pdb = reinterpret_cast<float*>(ws + pl.off_pdb);
     GradFin fa{pda, pl.s_da, pl.K, pl.r_pad, pl.r, d_lora_a, 0};
@@ -524,20 +535,25 @@ hipError_t launch_lora_grads(const uint16_t* x, const uint16_t* dy, const LoraPl
         GradArgs g{x, reinterpret_cast<const uint16_t*>(ws + pl.off_gst_hi),
                    reinterpret_cast<const uint16_t*>(ws + pl.off_gst_lo), pda, pl.T, pl.T8, pl.ld_t, pl.K, pl.r_pad,
                    (int)ceil_div(pl.K, 128), pl.cpw_da};
-        hipError_t e = grad(g, pl.s_da, s);
+        hipError_t e = grad(g, pl.s_da, s, f16);
         if (e != hipSuccess) return e;
     }
     if (d_lora_b) {
         GradArgs g{dy, reinterpret_cast<const uint16_t*>(ws + pl.off_pst_hi),
                    reinterpret_cast<const uint16_t*>(ws + pl.off_pst_lo), pdb, pl.T, pl.T8, pl.ld_t, pl.N, pl.r_pad,
                    (int)ceil_div(pl.N, 128), pl.cpw_db};
-        hipError_t e = grad(g, pl.s_db, s);
+        hipError_t e = grad(g, pl.s_db, s, f16);
         if (e != hipSuccess) return e;
     }
     const int ba = d_lora_a ? (int)ceil_div(pl.K, 16) : 0;
     const int bb = d_lora_b ? (int)ceil_div(pl.N, 16) : 0;
     if (!d_lora_a) fa = fb;                // a single problem runs as the first one
-    hipLaunchKernelGGL(k_grad_finalize, dim3((unsigned)(ba + bb)), dim3(256), 0, s, fa, fb, d_lora_a ? ba : bb);
+    if (f16)
+        hipLaunchKernelGGL(k_grad_finalize<true>, dim3((unsigned)(ba + bb)), dim3(256), 0, s, fa, fb,
+                           d_lora_a ? ba : bb);
+    else
+        hipLaunchKernelGGL(k_grad_finalize<false>, dim3((unsigned)(ba + bb)), dim3(256), 0, s, fa, fb,
+                           d_lora_a ? ba : bb);
     return hipGetLastError();
 }
 

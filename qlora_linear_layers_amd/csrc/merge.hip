@@ -1,5 +1,5 @@
 // LoRA merge: W_m[n][k] = RNE_bf16(W'[n][k] + s sum_j A[k][j] B[j][n]), the
-// adapted layer's weight in bf16 ("QLoRA 原理精讲" section 2.5 and section 3,
+// adapted layer's weight in bf16 (fp16 with the F16 compute type) ("QLoRA 原理精讲" section 2.5 and section 3,
 // pitfall 3: after training the adapter can be merged back into BF16 weights).
 // W' = RNE_bf16(fl32(q[code] * c1')) with c1' = fl32(e4m3(f) * s2), the same
 // values nf4_dequantize_dq writes.  The rank-r product is accumulated in fp32
@@ -18,6 +18,8 @@
 // 16 consecutive k of one row n, so the epilogue is one 8-byte code load,
 // 16 dequantized weights and two 16-byte stores per (lane, n tile), straight
 // from the accumulators.
+#include <type_traits>
+
 #include "common.hpp"
 #include "plan.hpp"
 
@@ -25,7 +27,6 @@ namespace ql {
 
 namespace {
 
-typedef __bf16 bf16x8m_t __attribute__((ext_vector_type(8)));
 
 struct MergeArgs {
     const uint8_t* codes;
@@ -44,7 +45,7 @@ constexpr int kMergeK = 256;      // k per workgroup (64 per wave)
 
 // RP = r_pad / 64 (1..4): B^T is RP swizzled [64 n][64 j] tiles of 8 KB.
 // SQ: the block constant is the stored fp32 absmax (single quantization).
-template <int RP, bool SQ>
+template <int RP, bool SQ, bool F16>
 __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
     __shared__ float s_q[16];
     __shared__ __align__(16) uint8_t s_bt[RP * 8192];
@@ -136,9 +137,8 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8m_t, af[t]),
-                                                                    __builtin_bit_cast(bf16x8m_t, bf[c]),
-                                                                    acc[t][c], 0, 0, 0);
+                acc[t][c] = mfma16x16x32<F16>(__builtin_bit_cast(bf16x8_t, af[t]), __builtin_bit_cast(bf16x8_t, bf[c]),
+                                              acc[t][c]);
     }
 
     // epilogue: lane holds k0 + 16q + 4t + v of row n0 + 16c + nl in acc[t][c][v]
@@ -151,11 +151,11 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
 #pragma unroll
         for (int bb = 0; bb < 8; ++bb) {                               // code byte bb: k 2bb (high nibble), 2bb + 1
             const uint32_t byte = (cw[c][bb >> 2] >> (8 * (bb & 3))) & 0xFFu;
-            const uint32_t wq = pack_bf16x2(__fmul_rn(s_q[byte >> 4], c1p), __fmul_rn(s_q[byte & 15u], c1p));
+            const uint32_t wq = pack16x2<F16>(__fmul_rn(s_q[byte >> 4], c1p), __fmul_rn(s_q[byte & 15u], c1p));
             const int e = 2 * bb;                                      // element index 4t + v
-            const float m0 = fmaf(sc, acc[e >> 2][c][e & 3], bf16lo(wq));
-            const float m1 = fmaf(sc, acc[(e + 1) >> 2][c][(e + 1) & 3], bf16hi(wq));
-            o[bb >> 2][bb & 3] = pack_bf16x2(m0, m1);
+            const float m0 = fmaf(sc, acc[e >> 2][c][e & 3], lo16<F16>(wq));
+            const float m1 = fmaf(sc, acc[(e + 1) >> 2][c][(e + 1) & 3], hi16<F16>(wq));
+            o[bb >> 2][bb & 3] = pack16x2<F16>(m0, m1);
         }
         if (kok && n < p.N) {
             // streamed once: non-temporal stores keep it from displacing A and B in the caches
@@ -169,18 +169,23 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
 }  // namespace
 
 hipError_t launch_merge(const uint8_t* codes, BlockScales sc, const uint16_t* lora_a, const uint16_t* lora_b,
-                        int64_t K, int64_t N, int64_t r, float scaling, uint16_t* w_out, hipStream_t s) {
-    if (r == 0) return launch_dequantize(codes, sc, N * K, w_out, s);
+                        int64_t K, int64_t N, int64_t r, float scaling, uint16_t* w_out, hipStream_t s, bool f16) {
+    if (r == 0) return launch_dequantize(codes, sc, N * K, w_out, s, false, f16);
     const MergeArgs a{codes, sc.fp8, sc.sup, sc.absmax, lora_a, lora_b, w_out, K, N, r, scaling};
     const dim3 grid((unsigned)(ceil_div(N, kMergeRows) * ceil_div(K, kMergeK))), block(256);
     const Codebook& cb = host_codebook();
     auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, a, cb); };
     const bool sq = sc.single();
+    auto pick = [&](auto rp) {
+        constexpr int RP = decltype(rp)::value;
+        if (sq) f16 ? go(k_merge<RP, true, true>) : go(k_merge<RP, true, false>);
+        else f16 ? go(k_merge<RP, false, true>) : go(k_merge<RP, false, false>);
+    };
     switch ((int)ceil_div(r, 64)) {
-        case 1: sq ? go(k_merge<1, true>) : go(k_merge<1, false>); break;
-        case 2: sq ? go(k_merge<2, true>) : go(k_merge<2, false>); break;
-        case 3: sq ? go(k_merge<3, true>) : go(k_merge<3, false>); break;
-        default: sq ? go(k_merge<4, true>) : go(k_merge<4, false>); break;
+        case 1: pick(std::integral_constant<int, 1>{}); break;
+        case 2: pick(std::integral_constant<int, 2>{}); break;
+        case 3: pick(std::integral_constant<int, 3>{}); break;
+        default: pick(std::integral_constant<int, 4>{}); break;
     }
     return hipGetLastError();
 }

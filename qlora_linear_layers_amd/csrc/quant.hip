@@ -27,8 +27,9 @@ namespace ql {
 // c1 is stored as it is and there is no second level.  EXACT: every ratio by
 // correctly rounded division (the INT4 levels have exact midpoints such as
 // 1/14 that ratios of bf16 values can reach, so the reciprocal shortcut does
-// not hold for them).
-template <bool SQ, bool EXACT>
+// not hold for them).  F16: the weights are fp16 (11-bit significands, for
+// which that argument does not hold either, so they take exact division too).
+template <bool SQ, bool EXACT, bool F16>
 __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ w, int64_t nblocks,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ fp8,
                                                   float* __restrict__ superscale, float* __restrict__ absmax,
@@ -66,21 +67,22 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ w
         m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));
         m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));
         m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, false));
-        const float c1 = __uint_as_float(m << 16);
+        // |w| bit patterns order like the values in both formats (sign-magnitude)
+        const float c1 = F16 ? lo16<true>(m) : __uint_as_float(m << 16);
         const float r = c1 > 0.0f ? __builtin_amdgcn_rcpf(c1) : 0.0f;
-        const bool exact = c1 != 0.0f && (EXACT || c1 < 0x1p-64f || c1 > 0x1p64f);
+        const bool exact = c1 != 0.0f && (EXACT || F16 || c1 < 0x1p-64f || c1 > 0x1p64f);
 
         float n[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float x = (e & 1) ? bf16hi(d[e >> 1]) : bf16lo(d[e >> 1]);
+            const float x = (e & 1) ? hi16<F16>(d[e >> 1]) : lo16<F16>(d[e >> 1]);
             n[e] = __fmul_rn(x, r);
         }
         if (__any(exact)) {
             if (exact) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float x = (e & 1) ? bf16hi(d[e >> 1]) : bf16lo(d[e >> 1]);
+                    const float x = (e & 1) ? hi16<F16>(d[e >> 1]) : lo16<F16>(d[e >> 1]);
                     n[e] = __fdiv_rn(x, c1);
                 }
             }
@@ -122,11 +124,15 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ w
 }
 
 hipError_t launch_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* fp8,
-                           float* superscale, hipStream_t s) {
+                           float* superscale, hipStream_t s, bool f16) {
     const int64_t nblocks = numel / kBlock;
     const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
-    hipLaunchKernelGGL((k_quantize<false, false>), dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes, fp8,
-                       superscale, nullptr, host_encode_table());
+    if (f16)
+        hipLaunchKernelGGL((k_quantize<false, false, true>), dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks,
+                           codes, fp8, superscale, nullptr, host_encode_table());
+    else
+        hipLaunchKernelGGL((k_quantize<false, false, false>), dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks,
+                           codes, fp8, superscale, nullptr, host_encode_table());
     return hipGetLastError();
 }
 
@@ -135,10 +141,10 @@ hipError_t launch_quantize_sq(const uint16_t* w, int64_t numel, uint8_t* codes, 
     const int64_t nblocks = numel / kBlock;
     const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
     if (int4)
-        hipLaunchKernelGGL((k_quantize<true, true>), dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes,
+        hipLaunchKernelGGL((k_quantize<true, true, false>), dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes,
                            nullptr, nullptr, absmax, host_int4_encode_table());
     else
-        hipLaunchKernelGGL((k_quantize<true, false>), dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes,
+        hipLaunchKernelGGL((k_quantize<true, false, false>), dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes,
                            nullptr, nullptr, absmax, host_encode_table());
     return hipGetLastError();
 }
@@ -155,7 +161,7 @@ hipError_t launch_quantize_sq(const uint16_t* w, int64_t numel, uint8_t* codes, 
 // lookups never conflict).
 constexpr int kDeqUnits = 4;
 
-template <bool SQ>
+template <bool SQ, bool F16>
 __global__ __launch_bounds__(256) void k_dequantize(const uint32_t* __restrict__ codes,
                                                     const uint8_t* __restrict__ fp8,
                                                     const float* __restrict__ superscale,
@@ -194,24 +200,25 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint32_t* __restrict__
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const uint32_t byte = (cv[u] >> (8 * b)) & 0xFFu;
-            o[b] = pack_bf16x2(__fmul_rn(s_q[byte >> 4], c1p), __fmul_rn(s_q[byte & 15u], c1p));
+            o[b] = pack16x2<F16>(__fmul_rn(s_q[byte >> 4], c1p), __fmul_rn(s_q[byte & 15u], c1p));
         }
         __builtin_nontemporal_store(o, out + i);
     }
 }
 
 hipError_t launch_dequantize(const uint8_t* codes, BlockScales sc, int64_t numel, uint16_t* out, hipStream_t s,
-                             bool int4) {
+                             bool int4, bool f16) {
     const Codebook& cb = int4 ? host_int4_codebook() : host_codebook();
     const int64_t nunits = numel / 8;
     const int64_t per_wg = 256 * kDeqUnits;
     const dim3 grid((unsigned)((nunits + per_wg - 1) / per_wg));
     const uint32_t* c = reinterpret_cast<const uint32_t*>(codes);
     u32x4_t* o = reinterpret_cast<u32x4_t*>(out);
-    if (sc.single())
-        hipLaunchKernelGGL(k_dequantize<true>, grid, dim3(256), 0, s, c, nullptr, nullptr, sc.absmax, nunits, o, cb);
-    else
-        hipLaunchKernelGGL(k_dequantize<false>, grid, dim3(256), 0, s, c, sc.fp8, sc.sup, nullptr, nunits, o, cb);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, c, sc.fp8, sc.sup, sc.absmax, nunits, o, cb);
+    };
+    if (sc.single()) f16 ? go(k_dequantize<true, true>) : go(k_dequantize<true, false>);
+    else f16 ? go(k_dequantize<false, true>) : go(k_dequantize<false, false>);
     return hipGetLastError();
 }
 

@@ -29,6 +29,25 @@ def to_bf16_bits(f32):
     return t.view(torch.int16).numpy().view(np.uint16).copy()
 
 
+def to_f16_bits(f32):
+    """fp32 draws -> IEEE half bits (nearest even), for the fp16 compute-type workloads."""
+    return np.asarray(f32, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def layer_inputs_f16(config, layer_idx, lin_idx, lin, T, r, with_dy=False):
+    """layer_inputs with every tensor drawn the same way and rounded to fp16 instead of bf16."""
+    g = lambda role: rng_for(config, layer_idx, lin_idx, role)
+    out = dict(w=to_f16_bits(g(ROLE_W).standard_normal((lin.N, lin.K), dtype=np.float32) * np.float32(0.02)))
+    if T:
+        out["x"] = to_f16_bits(g(ROLE_X).standard_normal((T, lin.K), dtype=np.float32))
+    if r:
+        out["a"] = to_f16_bits(g(ROLE_A).standard_normal((lin.K, r), dtype=np.float32) * np.float32(0.01))
+        out["b"] = to_f16_bits(g(ROLE_B).standard_normal((r, lin.N), dtype=np.float32) * np.float32(0.01))
+    if with_dy:
+        out["dy"] = to_f16_bits(g(ROLE_DY).standard_normal((T, lin.N), dtype=np.float32))
+    return out
+
+
 def normal_bf16(rng, shape, std):
     return to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
 
