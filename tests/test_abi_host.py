@@ -180,3 +180,19 @@ def test_int4_validation(L):
     assert L.int4_dequantize(FAKE, None, 64, FAKE, None) == NULL
     assert L.int4_dequantize(FAKE, FAKE, -64, FAKE, None) == SHAPE
     assert L.int4_dequantize(FAKE, FAKE, 64, MIS, None) == ALIGN
+
+
+def test_f16_validation(L):
+    assert L.nf4_quantize_dq_f16(None, 64, FAKE, FAKE, FAKE, None) == NULL
+    assert L.nf4_quantize_dq_f16(FAKE, 63, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.nf4_dequantize_dq_f16(FAKE, FAKE, FAKE, 64, MIS, None) == ALIGN
+    f = L.qlora_linear_fwd_f16
+    assert f(FAKE, 16, 128, 128, FAKE, FAKE, None, None, None, 0, 1.0, FAKE, FAKE, 1 << 30, None) == NULL
+    assert f(FAKE, 16, 128, 100, FAKE, FAKE, FAKE, None, None, 0, 1.0, FAKE, FAKE, 1 << 30, None) == SHAPE
+    assert f(FAKE, 16, 128, 128, FAKE, FAKE, FAKE, None, None, 0, math.nan, FAKE, FAKE, 1 << 30, None) == VALUE
+    b = L.qlora_linear_bwd_input_f16
+    assert b(FAKE, 64, 128, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 1.0, FAKE, FAKE, FAKE, FAKE, None, 0, 0,
+             None) == WORKSPACE
+    m = L.qlora_merge_lora_f16
+    assert m(FAKE, FAKE, FAKE, 128, 64, FAKE, None, 16, 0.5, FAKE, None) == NULL
+    assert m(FAKE, FAKE, FAKE, 96, 64, FAKE, FAKE, 16, 0.5, FAKE, None) == SHAPE
