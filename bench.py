@@ -322,6 +322,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the step and the roofline kernel (for a kernel trace of the step alone)")
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the calibration copy and the k_fwd launches (for counter runs)")
@@ -452,40 +454,41 @@ def main():
         "components": comp,
         "roofline": roofline,
     }
-    sets = weight_copies(api, [b["qw"] for b in bufs])
-    dec = measure_decode(api, torch, layers, sets, r, s)
-    for Td, (secs, nbytes) in dec.items():
-        comp[f"decode_T{Td}"] = {"GB/s": round(nbytes / secs / 1e9, 1),
-                                 "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
-                                 "us_per_layer_set": round(1e6 * secs, 2),
-                                 "note": "7 linears, fused dequant + small-M MFMA (16x16x32) incl. LoRA; weights rotated over 6 copies"}
-    for name, (kind, secs, amt) in measure_sq(api, torch, bufs, T, r, s, ws).items():
-        if kind == "hbm":
-            comp[name] = {"GB/s": round(amt / secs / 1e9, 1), "frac_of_hbm_peak": round(amt / secs / HBM_PEAK, 4),
-                          "ms": round(1e3 * secs, 4), "note": "single quantization (fp32 absmax per 64 weights)"}
-        else:
-            comp[name] = {"TFLOP/s": round(amt / secs / 1e12, 1),
-                          "frac_of_mfma_peak": round(amt / secs / MFMA_BF16_PEAK, 4), "ms": round(1e3 * secs, 4),
-                          "note": "single quantization (fp32 absmax per 64 weights)"}
-    for name, (kind, secs, amt) in measure_f16(api, torch, bufs, T, r, s, ws).items():
-        note = "fp16 compute type" + (" (forward + backward pass, s X A reused)" if name == "backward_f16" else "")
-        if kind == "hbm":
-            comp[name] = {"GB/s": round(amt / secs / 1e9, 1), "frac_of_hbm_peak": round(amt / secs / HBM_PEAK, 4),
-                          "ms": round(1e3 * secs, 4), "note": note}
-        else:
-            comp[name] = {"TFLOP/s": round(amt / secs / 1e12, 1),
-                          "frac_of_mfma_peak": round(amt / secs / MFMA_BF16_PEAK, 4), "ms": round(1e3 * secs, 4),
-                          "note": note}
-    abl, secs, nbytes = measure_ablation(api, torch, synth, np, bufs)
-    comp["int4_ablation"] = {
-        "relative_rms_error": {k: {dt: round(e, 5) for dt, e in v.items()} for k, v in abl.items()},
-        "int4_quantize_GB/s": round(nbytes / secs / 1e9, 1),
-        "note": "NF4 vs INT4 absmax levels, fp32 absmax per 64 weights for both"}
-    secs, nbytes = measure_merge(api, torch, layers, sets, r, s)
-    comp["merge"] = {"GB/s": round(nbytes / secs / 1e9, 1), "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
-                     "us_per_layer_set": round(1e6 * secs, 2),
-                     "note": "7 linears, W_m = RNE_bf16(W' + s (A B)^T), r=64; weights rotated over 6 copies"}
-    del sets
+    if not args.no_extras:      # decode, single quantization, fp16, ablation, merge (outside the step)
+        sets = weight_copies(api, [b["qw"] for b in bufs])
+        dec = measure_decode(api, torch, layers, sets, r, s)
+        for Td, (secs, nbytes) in dec.items():
+            comp[f"decode_T{Td}"] = {"GB/s": round(nbytes / secs / 1e9, 1),
+                                     "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
+                                     "us_per_layer_set": round(1e6 * secs, 2),
+                                     "note": "7 linears, fused dequant + small-M MFMA (16x16x32) incl. LoRA; weights rotated over 6 copies"}
+        for name, (kind, secs, amt) in measure_sq(api, torch, bufs, T, r, s, ws).items():
+            if kind == "hbm":
+                comp[name] = {"GB/s": round(amt / secs / 1e9, 1), "frac_of_hbm_peak": round(amt / secs / HBM_PEAK, 4),
+                              "ms": round(1e3 * secs, 4), "note": "single quantization (fp32 absmax per 64 weights)"}
+            else:
+                comp[name] = {"TFLOP/s": round(amt / secs / 1e12, 1),
+                              "frac_of_mfma_peak": round(amt / secs / MFMA_BF16_PEAK, 4), "ms": round(1e3 * secs, 4),
+                              "note": "single quantization (fp32 absmax per 64 weights)"}
+        for name, (kind, secs, amt) in measure_f16(api, torch, bufs, T, r, s, ws).items():
+            note = "fp16 compute type" + (" (forward + backward pass, s X A reused)" if name == "backward_f16" else "")
+            if kind == "hbm":
+                comp[name] = {"GB/s": round(amt / secs / 1e9, 1), "frac_of_hbm_peak": round(amt / secs / HBM_PEAK, 4),
+                              "ms": round(1e3 * secs, 4), "note": note}
+            else:
+                comp[name] = {"TFLOP/s": round(amt / secs / 1e12, 1),
+                              "frac_of_mfma_peak": round(amt / secs / MFMA_BF16_PEAK, 4), "ms": round(1e3 * secs, 4),
+                              "note": note}
+        abl, secs, nbytes = measure_ablation(api, torch, synth, np, bufs)
+        comp["int4_ablation"] = {
+            "relative_rms_error": {k: {dt: round(e, 5) for dt, e in v.items()} for k, v in abl.items()},
+            "int4_quantize_GB/s": round(nbytes / secs / 1e9, 1),
+            "note": "NF4 vs INT4 absmax levels, fp32 absmax per 64 weights for both"}
+        secs, nbytes = measure_merge(api, torch, layers, sets, r, s)
+        comp["merge"] = {"GB/s": round(nbytes / secs / 1e9, 1), "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
+                         "us_per_layer_set": round(1e6 * secs, 2),
+                         "note": "7 linears, W_m = RNE_bf16(W' + s (A B)^T), r=64; weights rotated over 6 copies"}
+        del sets
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, T, r, s, args.cpu_tokens)
     print(json.dumps(out), flush=True)
