@@ -101,3 +101,61 @@ def layer_inputs(config, layer_idx, lin_idx, lin, T, r, with_dy=False, outliers=
     if with_dy:
         out["dy"] = normal_bf16(g(ROLE_DY), (T, lin.N), 1.0)
     return out
+
+
+# ----------------------------------------------------------------- on-device draws
+#
+# The 65B- and 70B-shaped workloads are too large to draw with numpy on the host
+# in reasonable time (68.5 G values for the 70B stack).  These draw the same
+# distributions with torch's seeded device generator instead; the seed of each
+# tensor still comes from SeedSequence([config, layer, tensor, role]).  Tests
+# that check such tensors against the oracle copy the drawn bf16 bytes back to
+# the host, so both sides still consume the same bytes.
+
+def device_generator(config, layer, tensor, role, device="cuda"):
+    seed = int(np.random.SeedSequence([config, layer, tensor, role]).generate_state(1, np.uint64)[0]) >> 1
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def device_normal_bf16(g, shape, std, device="cuda"):
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return x.mul_(std).to(torch.bfloat16)
+
+
+def device_outlier_weight_bf16(g, shape, std=0.02, frac=0.001, scale=0.1, device="cuda"):
+    """N(0, std) with a fraction `frac` of the entries (mask u < frac) replaced by
+    scale * t3, where t3 = z / sqrt(chi2_3 / 3) is drawn from its definition
+    (z and the three normals of chi2_3 independent standard normals)."""
+    w = torch.randn(shape, generator=g, device=device, dtype=torch.float32).mul_(std)
+    u = torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+    idx = torch.nonzero(u.view(-1) < frac).view(-1)
+    del u
+    z = torch.randn(idx.numel(), generator=g, device=device, dtype=torch.float32)
+    chi2 = torch.randn((idx.numel(), 3), generator=g, device=device, dtype=torch.float32).square_().sum(1)
+    w.view(-1)[idx] = z / torch.sqrt(chi2 / 3.0) * scale
+    return w.to(torch.bfloat16)
+
+
+def device_layer_weights(config, layer, layers, outliers=False, device="cuda"):
+    """bf16 weights [N, K] of every linear of one layer, drawn on the device."""
+    out = []
+    for ti, lin in enumerate(layers):
+        g = device_generator(config, layer, ti, ROLE_W, device)
+        if outliers:
+            out.append(device_outlier_weight_bf16(g, (lin.N, lin.K), device=device))
+        else:
+            out.append(device_normal_bf16(g, (lin.N, lin.K), 0.02, device=device))
+    return out
+
+
+def device_layer_inputs(config, layer, ti, lin, T, r, with_dy=False, device="cuda"):
+    """X [T,K], A [K,r], B [r,N] and optionally dY [T,N] of one linear, drawn on the device."""
+    g = lambda role: device_generator(config, layer, ti, role, device)
+    out = dict(x=device_normal_bf16(g(ROLE_X), (T, lin.K), 1.0, device),
+               a=device_normal_bf16(g(ROLE_A), (lin.K, r), 0.01, device),
+               b=device_normal_bf16(g(ROLE_B), (r, lin.N), 0.01, device))
+    if with_dy:
+        out["dy"] = device_normal_bf16(g(ROLE_DY), (T, lin.N), 1.0, device)
+    return out
