@@ -283,6 +283,79 @@ def measure_f16(api, torch, bufs, T, r, s, ws, reps=5):
     return out
 
 
+def measure_65b(api, torch, synth, reps=3):
+    """The 65B-shaped layer (q/k/v/o 8192x8192, gate/up 22016x8192, down 8192x22016;
+    T = 2048, r = 64, s = 0.25): full-layer quantize and dequantize, the fused
+    forward, and the backward input gradient dX = dY W' + s (dY B^T) A^T, each
+    timed over `reps` passes of the seven linears with HIP events.  Inputs are
+    drawn on the device (809.5 M weights).  Returns {phase: (kind, seconds, amount)}."""
+    cfg = synth.LAYER_65B
+    layers, T, r, s = cfg["layers"], cfg["T"], cfg["r"], cfg["scaling"]
+    ws = torch.empty(max(api.qlora_workspace_bytes(T, l.K, l.N, r) for l in layers), dtype=torch.uint8,
+                     device="cuda")
+    bufs = []
+    for ti, lin in enumerate(layers):
+        g = synth.device_generator(cfg["config"], 0, ti, synth.ROLE_W)
+        b = synth.device_layer_inputs(cfg["config"], 0, ti, lin, T, r, with_dy=True)
+        b["lin"] = lin
+        b["w"] = synth.device_normal_bf16(g, (lin.N, lin.K), 0.02)
+        b["qw"] = api.nf4_quantize_dq(b["w"])
+        b["wd"] = torch.empty((lin.N, lin.K), dtype=torch.bfloat16, device="cuda")
+        b["y"] = torch.empty((T, lin.N), dtype=torch.bfloat16, device="cuda")
+        b["dx"] = torch.empty((T, lin.K), dtype=torch.bfloat16, device="cuda")
+        bufs.append(b)
+
+    def bwd_flops(l):
+        return 2 * T * l.N * l.K + 2 * T * l.N * r + 2 * T * r * l.K
+
+    ops = {
+        "quantize": ("hbm", lambda b: api.nf4_quantize_dq_into(b["w"], b["qw"]),
+                     lambda l: phase_work(l, T, r)["quantize"][1]),
+        "dequantize": ("hbm", lambda b: api.nf4_dequantize_dq(b["qw"], out=b["wd"]),
+                       lambda l: phase_work(l, T, r)["dequantize"][1]),
+        "forward": ("mfma", lambda b: api.qlora_linear_fwd(b["x"], b["qw"], b["a"], b["b"], s, workspace=ws,
+                                                            out=b["y"]),
+                    lambda l: phase_work(l, T, r)["forward"][1]),
+        "backward_input": ("mfma", lambda b: api.qlora_linear_bwd_input(b["dy"], b["qw"], b["a"], b["b"], s,
+                                                                         workspace=ws, dx=b["dx"]),
+                           bwd_flops),
+    }
+    out = {}
+    for name, (kind, fn, work) in ops.items():
+        for b in bufs:
+            fn(b)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            for b in bufs:
+                fn(b)
+        ev[1].record()
+        torch.cuda.synchronize()
+        out[name] = (kind, ev[0].elapsed_time(ev[1]) / 1e3 / reps, sum(work(b["lin"]) for b in bufs))
+    del bufs, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_stream_70b(torch, synth, n_layers=80):
+    """The 70B-shaped streaming workload: 80 layers of {q 8192x8192, k/v 1024x8192,
+    o 8192x8192, gate/up 28672x8192, down 8192x28672}, each drawn on the device
+    as N(0, 0.02) with 0.1% 0.1 * t3 outliers, quantized (NF4 + double
+    quantization) and dequantized tensor by tensor with one layer resident.
+    Returns (kernel seconds, algorithmic bytes moved, packed bytes, parameters)."""
+    from qlora_linear_layers_amd.stream import LayerStream
+    cfg = synth.STREAM_70B
+    layers = cfg["layers"]
+    st = LayerStream([(l.N, l.K) for l in layers])
+    res = st.run(lambda l: synth.device_layer_weights(cfg["config"], l, layers, outliers=True), n_layers)
+    params = n_layers * sum(l.N * l.K for l in layers)
+    moved = n_layers * sum(2 * (2 * l.N * l.K + storage_bytes(l.N * l.K)) for l in layers)
+    del st
+    torch.cuda.empty_cache()
+    return res["seconds"], moved, res["packed_bytes"], params
+
+
 def storage_bytes_sq(numel):
     """Codes + one fp32 absmax per 64 weights."""
     return numel // 2 + 4 * (numel // 64)
@@ -489,6 +562,23 @@ def main():
                          "us_per_layer_set": round(1e6 * secs, 2),
                          "note": "7 linears, W_m = RNE_bf16(W' + s (A B)^T), r=64; weights rotated over 6 copies"}
         del sets
+        for name, (kind, secs, amt) in measure_65b(api, torch, synth).items():
+            key = name + "_65b"
+            if kind == "hbm":
+                comp[key] = {"GB/s": round(amt / secs / 1e9, 1), "frac_of_hbm_peak": round(amt / secs / HBM_PEAK, 4),
+                             "ms": round(1e3 * secs, 4)}
+            else:
+                comp[key] = {"TFLOP/s": round(amt / secs / 1e12, 1),
+                             "frac_of_mfma_peak": round(amt / secs / MFMA_BF16_PEAK, 4), "ms": round(1e3 * secs, 4)}
+            comp[key]["note"] = ("65B-shaped layer (q/k/v/o 8192x8192, gate/up 22016x8192, down 8192x22016), "
+                                 "T=2048, r=64; 7 linears per pass")
+        secs, moved, packed, params = measure_stream_70b(torch, synth)
+        closed = params * (4 + 8 / 64 + 32 / 16384) / 8
+        comp["stream_70b"] = {"GB/s": round(moved / secs / 1e9, 1), "frac_of_hbm_peak": round(moved / secs / HBM_PEAK, 4),
+                              "ms": round(1e3 * secs, 3), "params": params, "packed_bytes": packed,
+                              "closed_form_bytes": int(closed), "bits_per_param": round(8 * packed / params, 9),
+                              "note": "80 layers x 7 tensors (70B shapes, 0.1% t3 outliers), quantize_dq then "
+                                      "dequantize each tensor, one layer resident; kernel time only"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, T, r, s, args.cpu_tokens)
     print(json.dumps(out), flush=True)
