@@ -260,6 +260,47 @@ int qlora_merge_lora_f16(const uint8_t* codes, const uint8_t* absmax_fp8, const 
                          int64_t K, int64_t N, const uint16_t* lora_a, const uint16_t* lora_b, int64_t r,
                          float scaling, uint16_t* w_out, void* stream);
 
+/*
+ * Grouped decode forward: several independent layers in one launch.
+ *   Source: the layer of qlora_linear_fwd (Volcengine article section 3.4,
+ *   read as Y = X W'^T + s (X A) B); grouping changes only how the work is
+ *   launched.  At decode sizes one linear streams too few bytes to cover the
+ *   memory latency of the device, so the linears that a step can run together
+ *   (q/k/v on the same X, gate/up on the same X) go into one launch pair.
+ *   Each problem i computes exactly what qlora_linear_fwd computes for it:
+ *     problems[i].y = problems[i].x W_i'^T + problems[i].scaling (x A_i) B_i
+ *   with the same arithmetic (and so the same bits) as the single call.
+ *   count      1 .. QLORA_MAX_GROUP problems (HOST array, read during the call).
+ *   T          tokens of every problem, 1 .. QLORA_GROUPED_MAX_T.
+ *   r          adapter rank of every problem (0 = no adapter: lora_a and
+ *              lora_b NULL), rules as for qlora_linear_fwd.
+ *   Per problem: x [T, K] bf16, the storage triple of W [N, K], lora_a [K, r],
+ *   lora_b [r, N], y [T, N] bf16 written; K, N and alignment as for
+ *   qlora_linear_fwd.  Outputs must not overlap one another or any input.
+ *   workspace: at least qlora_grouped_workspace_bytes(count, problems, T, r)
+ *   bytes (device); contents on entry do not matter.
+ *   Errors: NULL, SHAPE (count, T, r or a problem's sizes), ALIGN, VALUE,
+ *   WORKSPACE, DEVICE; nothing is launched unless every problem is valid.
+ */
+#define QLORA_MAX_GROUP 8
+#define QLORA_GROUPED_MAX_T 16
+typedef struct qlora_linear_problem {
+    const uint16_t* x;            /* [T, K] bf16 (device)                    */
+    const uint8_t* codes;         /* W [N, K]: packed codes [N*K/2]          */
+    const uint8_t* absmax_fp8;    /* [N*K/64] FP8 E4M3FN block constants     */
+    const float* superscale;      /* [ceil(N*K/16384)] fp32 super-scales     */
+    const uint16_t* lora_a;       /* [K, r] bf16, or NULL when r == 0        */
+    const uint16_t* lora_b;       /* [r, N] bf16, or NULL when r == 0        */
+    uint16_t* y;                  /* [T, N] bf16 (device), written           */
+    int64_t K, N;
+    float scaling;                /* s = alpha / r                           */
+} qlora_linear_problem;
+
+/* Workspace bytes for qlora_linear_fwd_grouped (0 if any size is invalid). */
+size_t qlora_grouped_workspace_bytes(int count, const qlora_linear_problem* problems, int64_t T, int64_t r);
+int qlora_linear_fwd_grouped(int count, const qlora_linear_problem* problems, int64_t T, int64_t r,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* qlora_status_string - static, NUL-terminated description of a status code. */
 const char* qlora_status_string(int status);
 

@@ -41,6 +41,18 @@ _SIGS = {
                                            _c_p]),
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
+
+
+class LinearProblem(ctypes.Structure):
+    """qlora_linear_problem: one layer of a grouped decode forward."""
+    _fields_ = [("x", _c_p), ("codes", _c_p), ("absmax_fp8", _c_p), ("superscale", _c_p), ("lora_a", _c_p),
+                ("lora_b", _c_p), ("y", _c_p), ("K", _c_i64), ("N", _c_i64), ("scaling", ctypes.c_float)]
+
+
+_SIGS["qlora_grouped_workspace_bytes"] = (ctypes.c_size_t, [ctypes.c_int, ctypes.POINTER(LinearProblem), _c_i64,
+                                                            _c_i64])
+_SIGS["qlora_linear_fwd_grouped"] = (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(LinearProblem), _c_i64, _c_i64,
+                                                    _c_p, ctypes.c_size_t, _c_p])
 # fp16 compute type: the same arguments as the bf16 entry point of the same stem
 for _n in ("nf4_quantize_dq", "nf4_dequantize_dq", "qlora_linear_fwd", "qlora_linear_bwd_input", "qlora_merge_lora"):
     _SIGS[_n + "_f16"] = _SIGS[_n]
@@ -263,6 +275,54 @@ def qlora_linear_fwd(x, qw, lora_a=None, lora_b=None, scaling=1.0, workspace=Non
         _ptr(x), T, K, qw.N, _ptr(qw.codes), *sc, _ptr(lora_a), _ptr(lora_b),
         r, float(scaling), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
     return out
+
+
+MAX_GROUP = 8            # QLORA_MAX_GROUP
+GROUPED_MAX_T = 16       # QLORA_GROUPED_MAX_T
+
+
+def _grouped_array(problems, T, r):
+    arr = (LinearProblem * len(problems))()
+    for i, pr in enumerate(problems):
+        x, qw, a, b, scaling, y = pr
+        if isinstance(qw, NF4WeightSQ):
+            raise TypeError("the grouped forward takes double-quantized weights (NF4Weight)")
+        for t, name in ((x, "x"), (a, "lora_a"), (b, "lora_b"), (y, "out")):
+            _dev(t, torch.bfloat16, name)
+        if tuple(x.shape) != (T, qw.K) or tuple(y.shape) != (T, qw.N):
+            raise ValueError(f"problem {i}: x {tuple(x.shape)} / out {tuple(y.shape)} do not match T={T}, "
+                             f"K={qw.K}, N={qw.N}")
+        if (0 if a is None else a.shape[1]) != r:
+            raise ValueError(f"problem {i}: every problem of a group has the same rank")
+        arr[i] = LinearProblem(x.data_ptr(), qw.codes.data_ptr(), qw.absmax_fp8.data_ptr(), qw.superscale.data_ptr(),
+                               None if a is None else a.data_ptr(), None if b is None else b.data_ptr(),
+                               y.data_ptr(), qw.K, qw.N, float(scaling))
+    return arr
+
+
+def qlora_grouped_workspace_bytes(problems):
+    """Workspace bytes of qlora_linear_fwd_grouped for a list of
+    (x, qw, lora_a, lora_b, scaling, out) problems."""
+    T = problems[0][0].shape[0]
+    r = 0 if problems[0][2] is None else problems[0][2].shape[1]
+    arr = _grouped_array(problems, T, r)
+    return int(lib().qlora_grouped_workspace_bytes(len(problems), arr, T, r))
+
+
+def qlora_linear_fwd_grouped(problems, workspace=None):
+    """Decode forward of up to 8 independent layers in one launch pair.  Each
+    problem is (x [T, K] bf16, NF4Weight, lora_a or None, lora_b or None,
+    scaling, out [T, N] bf16); every problem has the same T (<= 16) and rank.
+    Writes each out exactly as qlora_linear_fwd would."""
+    T = problems[0][0].shape[0]
+    r = 0 if problems[0][2] is None else problems[0][2].shape[1]
+    arr = _grouped_array(problems, T, r)
+    if workspace is None:
+        n = int(lib().qlora_grouped_workspace_bytes(len(problems), arr, T, r))
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=problems[0][0].device)
+    _check("qlora_linear_fwd_grouped", lib().qlora_linear_fwd_grouped(
+        len(problems), arr, T, r, _ptr(workspace), workspace.numel(), _stream()))
+    return [pr[5] for pr in problems]
 
 
 def qlora_linear_bwd_input(dy, qw, lora_a=None, lora_b=None, scaling=1.0, x=None, lora_grads=False,

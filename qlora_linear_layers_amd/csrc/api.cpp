@@ -21,6 +21,9 @@ hipError_t launch_lora_grads(const uint16_t* x, const uint16_t* dy, const LoraPl
                              uint16_t* d_lora_a, uint16_t* d_lora_b, hipStream_t s, bool f16);
 }  // namespace ql
 
+static_assert(QLORA_MAX_GROUP == ql::kMaxGroup, "group size of the header and the kernels");
+static_assert(QLORA_GROUPED_MAX_T == ql::kGemvMaxT, "decode token limit of the header and the kernels");
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -142,6 +145,32 @@ int merge_impl(const uint8_t* codes, ql::BlockScales sc, int64_t K, int64_t N, c
     if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
     return dev(ql::launch_merge(codes, sc, lora_a, lora_b, K, N, r, scaling, w_out, static_cast<hipStream_t>(stream),
                                 f16));
+}
+
+// Host checks of one grouped decode problem (the rules of fwd_impl).
+int check_problem(const qlora_linear_problem& q, int64_t T, int64_t r) {
+    if (!q.x || !q.codes || !q.absmax_fp8 || !q.superscale || !q.y) return QLORA_ERR_NULL;
+    if (r > 0 && (!q.lora_a || !q.lora_b)) return QLORA_ERR_NULL;
+    if (int st = check_linear_shape(T, q.K, q.N, r)) return st;
+    if (r == 0 && (q.lora_a || q.lora_b)) return QLORA_ERR_SHAPE;
+    const void* ptrs[] = {q.x, q.codes, q.absmax_fp8, q.superscale, q.lora_a, q.lora_b, q.y};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
+    if (!std::isfinite(q.scaling)) return QLORA_ERR_VALUE;
+    return QLORA_OK;
+}
+
+int grouped_problems(int count, const qlora_linear_problem* problems, int64_t T, int64_t r,
+                     ql::GemvProblem* out) {
+    if (!problems) return QLORA_ERR_NULL;
+    if (count < 1 || count > QLORA_MAX_GROUP || T < 1 || T > QLORA_GROUPED_MAX_T) return QLORA_ERR_SHAPE;
+    for (int i = 0; i < count; ++i) {
+        const qlora_linear_problem& q = problems[i];
+        if (int st = check_problem(q, T, r)) return st;
+        out[i] = ql::GemvProblem{q.x, q.codes, dq_scales(q.absmax_fp8, q.superscale), q.lora_a, q.lora_b, q.scaling,
+                                 q.K, q.N, q.y};
+    }
+    return QLORA_OK;
 }
 
 int quantize_dq_impl(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* absmax_fp8, float* superscale,
@@ -290,6 +319,23 @@ int qlora_merge_lora_f16(const uint8_t* codes, const uint8_t* absmax_fp8, const 
                          uint16_t* w_out, void* stream) {
     return merge_impl(codes, dq_scales(absmax_fp8, superscale), K, N, lora_a, lora_b, r, scaling, w_out, stream,
                       true);
+}
+
+size_t qlora_grouped_workspace_bytes(int count, const qlora_linear_problem* problems, int64_t T, int64_t r) {
+    ql::GemvProblem g[ql::kMaxGroup];
+    if (grouped_problems(count, problems, T, r, g) != QLORA_OK) return 0;
+    return ql::gemv_group_workspace(g, count, T, r > 0 ? ql::ceil_div(r, 64) * 64 : 0);
+}
+
+int qlora_linear_fwd_grouped(int count, const qlora_linear_problem* problems, int64_t T, int64_t r,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    ql::GemvProblem g[ql::kMaxGroup];
+    if (int st = grouped_problems(count, problems, T, r, g)) return st;
+    if (workspace && !aligned16(workspace)) return QLORA_ERR_ALIGN;
+    const size_t need = ql::gemv_group_workspace(g, count, T, r > 0 ? ql::ceil_div(r, 64) * 64 : 0);
+    if (!workspace || workspace_bytes < need) return QLORA_ERR_WORKSPACE;
+    return dev(ql::launch_gemv_group(g, count, T, r, static_cast<uint8_t*>(workspace),
+                                     static_cast<hipStream_t>(stream), false));
 }
 
 }  // extern "C"

@@ -270,4 +270,21 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, BlockScales sc, 
                        const uint16_t* lora_b, float scaling, const LoraPlan& pl, uint8_t* ws, uint16_t* y,
                        hipStream_t s, bool f16);
 
+// Decode forward of up to kMaxGroup independent problems in one launch pair
+// (same token count T and rank r, same storage format).
+constexpr int kMaxGroup = 8;
+struct GemvProblem {
+    const uint16_t* x;
+    const uint8_t* codes;
+    BlockScales sc;
+    const uint16_t* lora_a;
+    const uint16_t* lora_b;
+    float scaling;
+    int64_t K, N;
+    uint16_t* y;
+};
+size_t gemv_group_workspace(const GemvProblem* probs, int count, int64_t T, int64_t r_pad);
+hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int64_t r, uint8_t* ws, hipStream_t s,
+                             bool f16);
+
 }  // namespace ql

@@ -51,6 +51,27 @@ struct GemvArgs {
     float scaling;
 };
 
+// Up to kMaxGroup independent problems (same T, same rank) in one launch.
+// Launch 1 lays out the LoRA down-projection blocks of every problem first
+// (they are short and latency-bound, so they start while the weight stream
+// ramps up), then the base blocks; `lora_end`, `base_end` and `fin_end` hold
+// the cumulative block ends (absolute block ids) of each problem.
+struct GemvGroup {
+    GemvArgs p[kMaxGroup];
+    int lora_end[kMaxGroup];
+    int base_end[kMaxGroup];
+    int fin_end[kMaxGroup];
+    int count;
+};
+
+// Problem that owns block `bid`, given ascending cumulative ends (uniform).
+__device__ __forceinline__ int group_find(const int* ends, int count, int bid) {
+    int i = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxGroup - 1; ++j) i += (j < count - 1 && bid >= ends[j]) ? 1 : 0;
+    return i;
+}
+
 constexpr int kDecThreads = 512;  // eight waves: 2 row groups x 4 k steps
 constexpr int kDecRows = 128;     // W rows per workgroup
 constexpr int kDecK = 512;        // k per workgroup
@@ -128,19 +149,26 @@ __device__ __forceinline__ void lora_down_block(const GemvArgs& p, uint8_t* dyn,
 // the k split ks (512 k); the rest are LoRA down-projection blocks.  SQ: the
 // block constant is the stored fp32 absmax (single quantization).
 template <int TT, bool SQ, bool F16>
-__global__ __launch_bounds__(kDecThreads) void k_gemv(GemvArgs p, Codebook cb) {
+__global__ __launch_bounds__(kDecThreads) void k_gemv(GemvGroup grp, Codebook cb) {
     extern __shared__ __align__(16) uint8_t dyn[];
-    if ((int)blockIdx.x >= p.gemv_blocks) {
-        lora_down_block<TT, F16>(p, dyn, (int)blockIdx.x - p.gemv_blocks);
+    const int bid = (int)blockIdx.x;
+    const int lora_total = grp.lora_end[grp.count - 1];
+    if (bid < lora_total) {
+        const int i = group_find(grp.lora_end, grp.count, bid);
+        const GemvArgs p = grp.p[i];
+        lora_down_block<TT, F16>(p, dyn, bid - (i ? grp.lora_end[i - 1] : 0));
         return;
     }
+    const int gi = group_find(grp.base_end, grp.count, bid);
+    const GemvArgs p = grp.p[gi];
+    const int bx = bid - (gi ? grp.base_end[gi - 1] : lora_total);     // block within the problem
     lds8_t* tbl = (lds8_t*)dyn;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wave = wv & 3, rg = wv >> 2;                             // k step, row group
     const int nl = lane & 15, g = lane >> 4;
     const int nb = (int)ceil_div(p.N, kDecRows);
-    const int rb = (int)blockIdx.x % nb, ks = (int)blockIdx.x / nb;
+    const int rb = bx % nb, ks = bx / nb;
     const int64_t n0 = (int64_t)rb * kDecRows + 64 * rg;
     const int64_t kk = (int64_t)ks * kDecK + 128 * wave + 32 * g;      // this lane's 32 k
     const bool kok = kk < p.K;                                         // K % 64 == 0: all 32 or none
@@ -223,14 +251,17 @@ __global__ __launch_bounds__(kDecThreads) void k_gemv(GemvArgs p, Codebook cb) {
 // added in wave order, so the result does not depend on timing.
 constexpr int kFinCols = 64;
 template <int RP, bool F16>
-__global__ __launch_bounds__(256) void k_gemv_finalize(GemvArgs p) {
+__global__ __launch_bounds__(256) void k_gemv_finalize(GemvGroup grp) {
+    const int gi = group_find(grp.fin_end, grp.count, (int)blockIdx.x);
+    const GemvArgs p = grp.p[gi];
+    const int bx = (int)blockIdx.x - (gi ? grp.fin_end[gi - 1] : 0);
     constexpr int RQ = 16 * RP;                                        // ranks of B per wave
     __shared__ __align__(16) float pr[4 * 256];                        // group sums [G][W] float4
     __shared__ __align__(16) float ps[16 * 256];                       // s X A [T][r_pad]
     __shared__ __align__(16) float red[4 * 16 * kFinCols];             // wave sums [4][T][64]
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t n = (int64_t)blockIdx.x * kFinCols + lane;
+    const int64_t n = (int64_t)bx * kFinCols + lane;
     const bool nok = n < p.N;
 
     // B column n over this wave's ranks, and the first 8 base partials of its tokens
@@ -333,7 +364,7 @@ __global__ __launch_bounds__(256) void k_gemv_finalize(GemvArgs p) {
     __syncthreads();
     for (int i = threadIdx.x; i < T * kFinCols; i += 256) {
         const int t = i / kFinCols, l = i % kFinCols;
-        const int64_t nn = (int64_t)blockIdx.x * kFinCols + l;
+        const int64_t nn = (int64_t)bx * kFinCols + l;
         if (nn < p.N) {
             const float v = red[(0 * 16 + t) * kFinCols + l] + red[(1 * 16 + t) * kFinCols + l] +
                             red[(2 * 16 + t) * kFinCols + l] + red[(3 * 16 + t) * kFinCols + l];
@@ -349,41 +380,62 @@ size_t gemv_workspace(int64_t T, int64_t K, int64_t N, int64_t r_pad) {
     return align256((size_t)gemv_ks(K) * T * N * 4) + align256((size_t)gemv_kl(K) * T * r_pad * 4);
 }
 
-hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
-                       const uint16_t* lora_b, float scaling, const LoraPlan& pl, uint8_t* ws, uint16_t* y,
-                       hipStream_t s, bool f16) {
-    GemvArgs a{x, codes, sc.fp8, sc.sup, sc.absmax, lora_a, lora_b, nullptr, nullptr, y, pl.T, pl.K, pl.N, pl.r, pl.r_pad,
-               gemv_ks(pl.K), pl.r ? gemv_kl(pl.K) : 0, 0, scaling};
-    a.part = reinterpret_cast<float*>(ws);
-    a.lpart = reinterpret_cast<float*>(ws + align256((size_t)a.KS * pl.T * pl.N * 4));
-    a.gemv_blocks = (int)ceil_div(pl.N, kDecRows) * a.KS;
+size_t gemv_group_workspace(const GemvProblem* probs, int count, int64_t T, int64_t r_pad) {
+    size_t n = 0;
+    for (int i = 0; i < count; ++i) n += gemv_workspace(T, probs[i].K, probs[i].N, r_pad);
+    return n;
+}
+
+hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int64_t r, uint8_t* ws, hipStream_t s,
+                             bool f16) {
+    if (count < 1 || count > kMaxGroup) return hipErrorInvalidValue;
+    const int64_t r_pad = r > 0 ? ceil_div(r, 64) * 64 : 0;
+    GemvGroup g{};
+    g.count = count;
+    int nl = 0, nbase = 0, nfin = 0;
+    for (int i = 0; i < count; ++i) {
+        const GemvProblem& q = probs[i];
+        GemvArgs& a = g.p[i];
+        a = GemvArgs{q.x, q.codes, q.sc.fp8, q.sc.sup, q.sc.absmax, q.lora_a, q.lora_b, nullptr, nullptr, q.y,
+                     T, q.K, q.N, r, r_pad, gemv_ks(q.K), r ? gemv_kl(q.K) : 0, 0, q.scaling};
+        a.part = reinterpret_cast<float*>(ws);
+        a.lpart = reinterpret_cast<float*>(ws + align256((size_t)a.KS * T * q.N * 4));
+        ws += gemv_workspace(T, q.K, q.N, r_pad);
+        a.gemv_blocks = (int)ceil_div(q.N, kDecRows) * a.KS;
+        nl += r ? (int)(r_pad / 64) * a.KL : 0;
+        g.lora_end[i] = nl;
+        nbase += a.gemv_blocks;
+        nfin += (int)ceil_div(q.N, kFinCols);
+        g.fin_end[i] = nfin;
+    }
+    for (int i = 0; i < count; ++i) g.base_end[i] = (i ? g.base_end[i - 1] : nl) + g.p[i].gemv_blocks;
+    for (int i = count; i < kMaxGroup; ++i) g.lora_end[i] = g.base_end[i] = g.fin_end[i] = 0x7FFFFFFF;
+    const bool sq = probs[0].sc.single();
     const Codebook& cb = host_codebook();
-    const int lora_blocks = pl.r ? (int)(pl.r_pad / 64) * a.KL : 0;
-    const dim3 grid((unsigned)(a.gemv_blocks + lora_blocks));
+    const dim3 grid((unsigned)(nl + nbase));
     hipError_t ae = hipSuccess;
     auto go = [&](auto kern) {
         // 64 KB of dynamic LDS: above the default limit
         ae = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                  (int)kDecLds);
-        if (ae == hipSuccess) hipLaunchKernelGGL(kern, grid, dim3(kDecThreads), kDecLds, s, a, cb);
+        if (ae == hipSuccess) hipLaunchKernelGGL(kern, grid, dim3(kDecThreads), kDecLds, s, g, cb);
     };
-    const bool sq = sc.single();
     auto pick = [&](auto tt) {
         constexpr int TT = decltype(tt)::value;
         if (sq) f16 ? go(k_gemv<TT, true, true>) : go(k_gemv<TT, true, false>);
         else f16 ? go(k_gemv<TT, false, true>) : go(k_gemv<TT, false, false>);
     };
-    if (pl.T <= 1) pick(std::integral_constant<int, 1>{});
-    else if (pl.T <= 2) pick(std::integral_constant<int, 2>{});
-    else if (pl.T <= 4) pick(std::integral_constant<int, 4>{});
-    else if (pl.T <= 8) pick(std::integral_constant<int, 8>{});
+    if (T <= 1) pick(std::integral_constant<int, 1>{});
+    else if (T <= 2) pick(std::integral_constant<int, 2>{});
+    else if (T <= 4) pick(std::integral_constant<int, 4>{});
+    else if (T <= 8) pick(std::integral_constant<int, 8>{});
     else pick(std::integral_constant<int, 16>{});
     if (ae != hipSuccess) return ae;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 fg((unsigned)ceil_div(pl.N, kFinCols)), fb(256);
-    auto fin = [&](auto kern) { hipLaunchKernelGGL(kern, fg, fb, 0, s, a); };
-    switch (pl.r_pad / 64) {
+    const dim3 fg((unsigned)nfin), fb(256);
+    auto fin = [&](auto kern) { hipLaunchKernelGGL(kern, fg, fb, 0, s, g); };
+    switch (r_pad / 64) {
         case 0: f16 ? fin(k_gemv_finalize<0, true>) : fin(k_gemv_finalize<0, false>); break;
         case 1: f16 ? fin(k_gemv_finalize<1, true>) : fin(k_gemv_finalize<1, false>); break;
         case 2: f16 ? fin(k_gemv_finalize<2, true>) : fin(k_gemv_finalize<2, false>); break;
@@ -391,6 +443,13 @@ hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, BlockScales sc, 
         default: f16 ? fin(k_gemv_finalize<4, true>) : fin(k_gemv_finalize<4, false>); break;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_gemv(const uint16_t* x, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
+                       const uint16_t* lora_b, float scaling, const LoraPlan& pl, uint8_t* ws, uint16_t* y,
+                       hipStream_t s, bool f16) {
+    const GemvProblem q{x, codes, sc, lora_a, lora_b, scaling, pl.K, pl.N, y};
+    return launch_gemv_group(&q, 1, pl.T, pl.r, ws, s, f16);
 }
 
 }  // namespace ql

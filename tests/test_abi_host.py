@@ -196,3 +196,38 @@ def test_f16_validation(L):
     m = L.qlora_merge_lora_f16
     assert m(FAKE, FAKE, FAKE, 128, 64, FAKE, None, 16, 0.5, FAKE, None) == NULL
     assert m(FAKE, FAKE, FAKE, 96, 64, FAKE, FAKE, 16, 0.5, FAKE, None) == SHAPE
+
+
+def _problems(n, over=None):
+    arr = (api.LinearProblem * n)()
+    for i in range(n):
+        d = dict(x=FAKE, codes=FAKE, absmax_fp8=FAKE, superscale=FAKE, lora_a=FAKE, lora_b=FAKE, y=FAKE,
+                 K=256, N=512, scaling=0.25)
+        d.update((over or {}).get(i, {}))
+        arr[i] = api.LinearProblem(**d)
+    return arr
+
+
+def test_grouped_validation(L):
+    f, wb = L.qlora_linear_fwd_grouped, L.qlora_grouped_workspace_bytes
+    big = 1 << 40
+    assert f(3, None, 8, 16, FAKE, big, None) == NULL
+    assert f(0, _problems(1), 8, 16, FAKE, big, None) == SHAPE
+    assert f(9, _problems(9), 8, 16, FAKE, big, None) == SHAPE            # above QLORA_MAX_GROUP
+    assert f(2, _problems(2), 17, 16, FAKE, big, None) == SHAPE           # above QLORA_GROUPED_MAX_T
+    assert f(2, _problems(2), 0, 16, FAKE, big, None) == SHAPE
+    assert f(2, _problems(2), 8, 12, FAKE, big, None) == SHAPE            # rank not a multiple of 8
+    assert f(2, _problems(2, {1: dict(K=100)}), 8, 16, FAKE, big, None) == SHAPE
+    assert f(2, _problems(2, {1: dict(y=None)}), 8, 16, FAKE, big, None) == NULL
+    assert f(2, _problems(2, {1: dict(lora_b=None)}), 8, 16, FAKE, big, None) == NULL
+    assert f(2, _problems(2), 8, 0, FAKE, big, None) == SHAPE             # adapters given with r = 0
+    assert f(2, _problems(2, {0: dict(codes=MIS)}), 8, 16, FAKE, big, None) == ALIGN
+    assert f(2, _problems(2, {1: dict(scaling=math.nan)}), 8, 16, FAKE, big, None) == VALUE
+    assert f(2, _problems(2), 8, 16, MIS, big, None) == ALIGN
+    assert f(2, _problems(2), 8, 16, None, big, None) == WORKSPACE
+    assert f(2, _problems(2), 8, 16, FAKE, 16, None) == WORKSPACE
+    # workspace: each problem's split partials [K/512][T][N] and adapter partials [K/256][T][r_pad], 256-aligned
+    one = (256 // 512 + 1) * 8 * 512 * 4 + (256 // 256) * 8 * 64 * 4
+    assert wb(3, _problems(3), 8, 16) == 3 * one
+    assert wb(9, _problems(9), 8, 16) == 0
+    assert wb(2, _problems(2, {1: dict(N=100)}), 8, 16) == 0

@@ -1,0 +1,83 @@
+"""GPU parity of the grouped decode forward (several independent layers in one
+launch pair): each output must be bit-identical to the single-layer call, which
+the decode tests pin to the oracle, and a ragged group of mixed shapes is also
+checked against the oracle directly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from qlora_linear_layers_amd import api, synth
+from helpers import assert_gemm_close, bits_of, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(cfg, idx, lin, T, r):
+    d = synth.layer_inputs(cfg, 0, idx, lin, T, r)
+    qw = api.nf4_quantize_dq(to_dev(d["w"], (lin.N, lin.K)))
+    x = to_dev(d["x"], (T, lin.K))
+    a = to_dev(d["a"], (lin.K, r)) if r else None
+    b = to_dev(d["b"], (r, lin.N)) if r else None
+    return d, qw, x, a, b
+
+
+def _group_vs_single(cfg, lins, T, r, s):
+    layers = [_layer(cfg, i, lin, T, r) for i, lin in enumerate(lins)]
+    probs = [(x, qw, a, b, s, torch.empty((T, lin.N), dtype=torch.bfloat16, device="cuda"))
+             for lin, (_, qw, x, a, b) in zip(lins, layers)]
+    got = api.qlora_linear_fwd_grouped(probs)
+    torch.cuda.synchronize()
+    for lin, (_, qw, x, a, b), y in zip(lins, layers, got):
+        ref = api.qlora_linear_fwd(x, qw, a, b, s)
+        assert np.array_equal(bits_of(y), bits_of(ref)), f"{lin.name} {lin.N}x{lin.K} T={T}: grouped != single"
+    return layers, got
+
+
+@pytest.mark.parametrize("T", [1, 4, 8, 16])
+def test_7b_layer_set_matches_single_calls(T):
+    say(f"[grouped] LLaMA-7B layer set, T={T}, r=64")
+    _group_vs_single(2, synth.LLAMA7B, T, 64, 0.25)
+
+
+def test_dependency_stages():
+    """The groups a decode step can launch together: q/k/v, gate/up (and o, down alone)."""
+    for stage in ((0, 1, 2), (4, 5), (3,), (6,)):
+        say(f"[grouped] stage {[synth.LLAMA7B[i].name for i in stage]} T=8")
+        _group_vs_single(2, [synth.LLAMA7B[i] for i in stage], 8, 64, 0.25)
+
+
+def test_ragged_mixed_shapes_against_oracle():
+    """Eight problems (the maximum), N not a multiple of 128 and K not a multiple of
+    512 (partial row blocks and k splits), against the oracle and the single calls."""
+    lins = [synth.Linear(f"p{i}", n, k) for i, (n, k) in enumerate(
+        [(320, 448), (64, 64), (1024, 576), (192, 1088), (448, 320), (128, 2048), (576, 704), (64, 1024)])]
+    T, r, s = 5, 24, 0.75
+    say(f"[grouped] ragged group of {len(lins)}, T={T}, r={r}")
+    layers, got = _group_vs_single(9, lins, T, r, s)
+    for lin, (d, _, _, _, _), y in zip(lins, layers, got):
+        rc, rf, rs = oracle.quantize_nf4_dq(d["w"])
+        wd = oracle.dequantize_nf4_dq(rc, rf, rs).reshape(lin.N, lin.K)
+        assert_gemm_close(bits_of(y), oracle.linear_fwd(d["x"], wd, d["a"], d["b"], s), f"{lin.name} Y")
+
+
+def test_no_adapter_group():
+    lins = [synth.Linear("a", 512, 256), synth.Linear("b", 256, 768)]
+    say("[grouped] r=0 group, T=3")
+    layers, got = _group_vs_single(9, lins, 3, 0, 0.0)
+    for lin, (d, _, _, _, _), y in zip(lins, layers, got):
+        rc, rf, rs = oracle.quantize_nf4_dq(d["w"])
+        wd = oracle.dequantize_nf4_dq(rc, rf, rs).reshape(lin.N, lin.K)
+        assert_gemm_close(bits_of(y), oracle.linear_fwd(d["x"], wd, None, None, 0.0), f"{lin.name} Y")
+
+
+def test_repeat_calls_are_identical():
+    lins = synth.LLAMA7B[:3]
+    layers = [_layer(2, i, lin, 4, 64) for i, lin in enumerate(lins)]
+    outs = []
+    for _ in range(2):
+        probs = [(x, qw, a, b, 0.25, torch.empty((4, lin.N), dtype=torch.bfloat16, device="cuda"))
+                 for lin, (_, qw, x, a, b) in zip(lins, layers)]
+        outs.append([bits_of(y) for y in api.qlora_linear_fwd_grouped(probs)])
+    for u, v in zip(*outs):
+        assert np.array_equal(u, v)
