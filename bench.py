@@ -109,8 +109,15 @@ def weight_copies(api, qws, copies=6):
             for _ in range(copies)]
 
 
-def measure_decode(api, torch, layers, sets, r, s, tokens=(1, 4, 8), reps=10):
+DECODE_STAGES = ((0, 1, 2), (3,), (4, 5), (6,))    # q/k/v, o, gate/up, down: what a decode step can group
+
+
+def measure_decode(api, torch, layers, sets, r, s, tokens=(1, 4, 8), reps=10, mode="single"):
     """Decode-size forward over the seven linears, one weight copy per pass.
+    mode "single": one qlora_linear_fwd per linear; "staged": one grouped call
+    per dependency stage (q/k/v, o, gate/up, down); "all": one grouped call for
+    all seven.  A GPU spin ahead of the timed region lets the host enqueue every
+    pass first, so the events see device time only.
     Returns {T: (seconds per layer set, bytes per layer set)}."""
     copies = len(sets)
     out = {}
@@ -120,16 +127,28 @@ def measure_decode(api, torch, layers, sets, r, s, tokens=(1, 4, 8), reps=10):
         a = [torch.randn((l.K, r), generator=g, device="cuda").mul_(0.01).to(torch.bfloat16) for l in layers]
         b = [torch.randn((r, l.N), generator=g, device="cuda").mul_(0.01).to(torch.bfloat16) for l in layers]
         ys = [torch.empty((T, l.N), dtype=torch.bfloat16, device="cuda") for l in layers]
-        ws = torch.empty(max(api.qlora_workspace_bytes(T, l.K, l.N, r) for l in layers), dtype=torch.uint8,
-                         device="cuda")
+        stages = [tuple(range(len(layers)))] if mode == "all" else DECODE_STAGES
+        if mode == "single":
+            ws = torch.empty(max(api.qlora_workspace_bytes(T, l.K, l.N, r) for l in layers), dtype=torch.uint8,
+                             device="cuda")
+        else:
+            ws = torch.empty(max(api.qlora_grouped_workspace_bytes(
+                [(xs[i], sets[0][i], a[i], b[i], s, ys[i]) for i in st]) for st in stages), dtype=torch.uint8,
+                device="cuda")
 
         def one(c):
-            for i, l in enumerate(layers):
-                api.qlora_linear_fwd(xs[i], sets[c][i], a[i], b[i], s, workspace=ws, out=ys[i])
+            if mode == "single":
+                for i, l in enumerate(layers):
+                    api.qlora_linear_fwd(xs[i], sets[c][i], a[i], b[i], s, workspace=ws, out=ys[i])
+            else:
+                for st in stages:
+                    api.qlora_linear_fwd_grouped([(xs[i], sets[c][i], a[i], b[i], s, ys[i]) for i in st],
+                                                 workspace=ws)
         for c in range(copies):
             one(c)
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda._sleep(20_000_000)
         ev[0].record()
         for k in range(reps):
             one(k % copies)
@@ -529,12 +548,16 @@ def main():
     }
     if not args.no_extras:      # decode, single quantization, fp16, ablation, merge (outside the step)
         sets = weight_copies(api, [b["qw"] for b in bufs])
-        dec = measure_decode(api, torch, layers, sets, r, s)
-        for Td, (secs, nbytes) in dec.items():
-            comp[f"decode_T{Td}"] = {"GB/s": round(nbytes / secs / 1e9, 1),
-                                     "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
-                                     "us_per_layer_set": round(1e6 * secs, 2),
-                                     "note": "7 linears, fused dequant + small-M MFMA (16x16x32) incl. LoRA; weights rotated over 6 copies"}
+        notes = {"single": "one launch pair per linear",
+                 "staged": "grouped launches per dependency stage: q/k/v, o, gate/up, down",
+                 "all": "all 7 linears in one grouped launch pair (independent inputs)"}
+        for mode, prefix in (("staged", "decode"), ("single", "decode_single"), ("all", "decode_all7")):
+            for Td, (secs, nbytes) in measure_decode(api, torch, layers, sets, r, s, mode=mode).items():
+                comp[f"{prefix}_T{Td}"] = {
+                    "GB/s": round(nbytes / secs / 1e9, 1), "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
+                    "us_per_layer_set": round(1e6 * secs, 2),
+                    "note": "7 linears, fused dequant + small-M MFMA (16x16x32) incl. LoRA; " + notes[mode]
+                            + "; weights rotated over 6 copies"}
         for name, (kind, secs, amt) in measure_sq(api, torch, bufs, T, r, s, ws).items():
             if kind == "hbm":
                 comp[name] = {"GB/s": round(amt / secs / 1e9, 1), "frac_of_hbm_peak": round(amt / secs / HBM_PEAK, 4),
