@@ -58,6 +58,13 @@ def test_ranks_above_64(r):
     _run_full(f"r={r}", synth.Linear("t", 384, 448), T=100, r=r, s=0.75)
 
 
+@pytest.mark.parametrize("N,K,T,r", [(192, 320, 1000, 24), (128, 64, 512, 0), (448, 448, 1536, 64), (320, 576, 700, 8)])
+def test_several_token_tiles(N, K, T, r):
+    """Several 256-token tiles with a ragged last one, row counts that are not a
+    multiple of the 256-row tile, and one to nine 64-wide k tiles."""
+    _run_full(f"T={T}", synth.Linear("t", N, K), T=T, r=r, s=0.5, check_bwd=False)
+
+
 def test_short_token_tile():
     """T below one 64-row tile with the reduction split 7 ways (K = 448): ragged
     tokens in the split partials and in the transposed intermediates."""
