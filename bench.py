@@ -408,6 +408,27 @@ def cpu_baseline(layers, T, r, s, t_sample):
             "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
 
 
+def only_component(name, api, torch, synth, layers, r, s):
+    """One component alone, on weights drawn on the device (for kernel traces and counter runs)."""
+    if name.startswith("decode"):
+        g = torch.Generator(device="cuda").manual_seed(1)
+        qws = [api.nf4_quantize_dq(torch.randn((l.N, l.K), generator=g, device="cuda").mul_(0.02)
+                                   .to(torch.bfloat16)) for l in layers]
+        mode = {"decode": "staged", "decode_single": "single", "decode_all7": "all"}[name]
+        res = measure_decode(api, torch, layers, weight_copies(api, qws), r, s, mode=mode)
+        return {f"T{Td}": {"GB/s": round(nb / secs / 1e9, 1), "us_per_layer_set": round(1e6 * secs, 2)}
+                for Td, (secs, nb) in res.items()}
+    if name == "layer_65b":
+        out = {}
+        for k, (kind, secs, amt) in measure_65b(api, torch, synth).items():
+            out[k] = ({"GB/s": round(amt / secs / 1e9, 1)} if kind == "hbm" else
+                      {"TFLOP/s": round(amt / secs / 1e12, 1)})
+        return out
+    secs, moved, packed, params = measure_stream_70b(torch, synth)
+    return {"GB/s": round(moved / secs / 1e9, 1), "ms": round(1e3 * secs, 3), "packed_bytes": packed,
+            "params": params}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -417,6 +438,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the step and the roofline kernel (for a kernel trace of the step alone)")
     ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--only", choices=("decode", "decode_single", "decode_all7", "layer_65b", "stream_70b"),
+                    help="run one component alone (no step, roofline loop or CPU baseline), e.g. for a kernel trace")
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the calibration copy and the k_fwd launches (for counter runs)")
     args = ap.parse_args()
@@ -434,6 +457,11 @@ def main():
     api.lib()
     cfg = synth.TRAIN_7B
     layers, T, r, s = cfg["layers"], cfg["T"], cfg["r"], cfg["scaling"]
+
+    if args.only:
+        print(json.dumps({"component": args.only, **only_component(args.only, api, torch, synth, layers, r, s)}),
+              flush=True)
+        return
 
     def dev(bits, shape):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).reshape(shape).cuda()
