@@ -13,11 +13,13 @@
 // blocks), so both MFMA operands are 16-byte fragment reads.  Each wave runs
 // v_mfma_f32_16x16x32_bf16 with the A operand = rows of A (index k) and the B
 // operand = columns of B^T's transpose (index n), 4 x 4 tiles of 16 k x 16 n.
-// The k of MFMA row m in row tile t is 16 (m / 4) + 4 t + (m % 4): the
-// accumulator rows a lane holds (4 (lane / 16) + v in every tile) then cover
-// 16 consecutive k of one row n, so the epilogue is one 8-byte code load,
-// 16 dequantized weights and two 16-byte stores per (lane, n tile), straight
-// from the accumulators.
+// The k of MFMA row m in row tile t is 32 (t / 2) + 8 (m / 4) + 4 (t % 2) +
+// (m % 4): the accumulator rows a lane holds (m = 4 (lane / 16) + v in every
+// tile) then cover k 8q .. 8q+7 in tiles 0-1 and 32 + 8q .. +7 in tiles 2-3
+// (q = lane / 16), so the epilogue is two 4-byte code loads, 16 dequantized
+// weights and two 16-byte stores per (lane, n tile), straight from the
+// accumulators, and the four lanes of a row write 64 contiguous bytes with
+// each store instruction.
 #include <type_traits>
 
 #include "common.hpp"
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
     const rsrc_t ra = make_rsrc(p.a, p.K * p.r * 2);
     const rsrc_t rbm = make_rsrc(p.b, p.r * p.N * 2);
 
-    // epilogue loads first: for n tile c, row n0 + 16c + nl, k0 + 16q .. +15
+    // epilogue loads first: for n tile c, row n0 + 16c + nl, k0 + 8q .. +7 and k0 + 32 + 8q .. +7
     u32x2_t cw[4];
     uint32_t f8[4], s2[4];
 #pragma unroll
@@ -72,7 +74,9 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
         const int64_t n = n0 + 16 * c + nl;
         const bool ok = kok && n < p.N;
         const int64_t blk = n * (p.K / 64) + k0 / 64;
-        cw[c] = bload8(rc, ok ? (uint32_t)(n * (p.K / 2) + (k0 + 16 * q) / 2) : kOOB, 0);
+        const uint32_t cb0 = ok ? (uint32_t)(n * (p.K / 2) + (k0 + 8 * q) / 2) : kOOB;
+        cw[c][0] = bload4(rc, cb0, 0);
+        cw[c][1] = bload4(rc, ok ? cb0 + 16u : kOOB, 0);
         if constexpr (SQ) {
             f8[c] = 0;
             s2[c] = bload4(rf, ok ? (uint32_t)blk * 4u : kOOB, 0);
@@ -83,11 +87,11 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
     }
 
     // A fragments of the first kPre rank steps, before the barrier (A operand
-    // row of this lane in tile t: m = nl -> k = 16 (m / 4) + 4 t + m % 4)
+    // row of this lane in tile t: m = nl -> k = 32 (t / 2) + 8 (m / 4) + 4 (t % 2) + m % 4)
     constexpr int kSteps = RP * 2, kPre = kSteps < 4 ? kSteps : 4;
     auto a_frag = [&](int js, int t) -> u32x4_t {
         const int j = 32 * js + 8 * q;                                 // this lane's 8 ranks
-        const int64_t k = k0 + 16 * (nl >> 2) + 4 * t + (nl & 3);
+        const int64_t k = k0 + 32 * (t >> 1) + 8 * (nl >> 2) + 4 * (t & 1) + (nl & 3);
         return bload16(ra, (kok && j < p.r) ? (uint32_t)((k * p.r + j) * 2) : kOOB, 0);
     };
     u32x4_t apre[kPre][4];
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
                                               acc[t][c]);
     }
 
-    // epilogue: lane holds k0 + 16q + 4t + v of row n0 + 16c + nl in acc[t][c][v]
+    // epilogue: lane holds k0 + 32 (t / 2) + 8q + 4 (t % 2) + v of row n0 + 16c + nl in acc[t][c][v]
     const float sc = p.s;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -149,19 +153,21 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
         const float c1p = SQ ? __uint_as_float(s2[c]) : block_scale(f8[c], __uint_as_float(s2[c]));
         u32x4_t o[2];
 #pragma unroll
-        for (int bb = 0; bb < 8; ++bb) {                               // code byte bb: k 2bb (high nibble), 2bb + 1
+        for (int bb = 0; bb < 8; ++bb) {
+            // code byte bb of half hf = bb / 4: k 8q + 2 (bb % 4) (high nibble) and the next,
+            // plus 32 in half 1; they sit in tile t = 2 hf + (bb % 4) / 2, rows v = 2 (bb % 2) .. +1
             const uint32_t byte = (cw[c][bb >> 2] >> (8 * (bb & 3))) & 0xFFu;
             const uint32_t wq = pack16x2<F16>(__fmul_rn(s_q[byte >> 4], c1p), __fmul_rn(s_q[byte & 15u], c1p));
-            const int e = 2 * bb;                                      // element index 4t + v
-            const float m0 = fmaf(sc, acc[e >> 2][c][e & 3], lo16<F16>(wq));
-            const float m1 = fmaf(sc, acc[(e + 1) >> 2][c][(e + 1) & 3], hi16<F16>(wq));
+            const int t = 2 * (bb >> 2) + ((bb & 3) >> 1), v = 2 * (bb & 1);
+            const float m0 = fmaf(sc, acc[t][c][v], lo16<F16>(wq));
+            const float m1 = fmaf(sc, acc[t][c][v + 1], hi16<F16>(wq));
             o[bb >> 2][bb & 3] = pack16x2<F16>(m0, m1);
         }
         if (kok && n < p.N) {
             // streamed once: non-temporal stores keep it from displacing A and B in the caches
-            u32x4_t* dst = reinterpret_cast<u32x4_t*>(p.w + n * p.K + k0 + 16 * q);
-            __builtin_nontemporal_store(o[0], dst);
-            __builtin_nontemporal_store(o[1], dst + 1);
+            uint16_t* dst = p.w + n * p.K + k0 + 8 * q;
+            __builtin_nontemporal_store(o[0], reinterpret_cast<u32x4_t*>(dst));
+            __builtin_nontemporal_store(o[1], reinterpret_cast<u32x4_t*>(dst + 32));
         }
     }
 }
