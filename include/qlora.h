@@ -82,7 +82,7 @@ int nf4_build_codebook(float codebook_out[16]);
  *   s2 = fl32(max c1 / 448); each c1 becomes the E4M3FN code nearest to
  *   min(fl32(c1 / s2), 448), exact ties to the lower code (s2 = 0 -> codes 0).
  *   w          [numel] bf16 (device), read.
- *   numel      number of elements, > 0 and a multiple of 64.
+ *   numel      number of elements, > 0, a multiple of 64 and at most 2^43.
  *   codes      [numel/2] uint8 (device), written.
  *   absmax_fp8 [numel/64] uint8 (device), written.
  *   superscale [ceil(numel/16384)] float (device), written.
@@ -98,11 +98,40 @@ int nf4_quantize_dq(const uint16_t* w, int64_t numel,
  *   c1' = fl32(e4m3(absmax_fp8[b]) * superscale[g]);
  *   w'  = RNE_bf16(fl32(q[code] * c1')).
  *   codes, absmax_fp8, superscale: the storage triple (device), read.
- *   numel  > 0, multiple of 64.   w_out [numel] bf16 (device), written.
+ *   numel  > 0, multiple of 64, at most 2^43.   w_out [numel] bf16 (device), written.
  *   Errors: NULL, SHAPE, ALIGN, DEVICE.
  */
 int nf4_dequantize_dq(const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale,
                       int64_t numel, uint16_t* w_out, void* stream);
+
+/*
+ * Grouped quantize / dequantize: several tensors in one launch.
+ *   Source: as nf4_quantize_dq / nf4_dequantize_dq ("QLoRA 原理精讲" sections
+ *   2.1-2.2); grouping changes only how the work is launched (for example all
+ *   weights of a transformer layer at once, so that small tensors do not each
+ *   pay a launch's ramp and tail).  Every tensor gets exactly the bytes the
+ *   single-tensor call would give it.
+ *   count    1 .. QLORA_MAX_TENSORS descriptors (HOST array, read during the call).
+ *   Per tensor: w [numel] bf16 (read by nf4_quantize_dq_grouped, written by
+ *   nf4_dequantize_dq_grouped), numel > 0, a multiple of 64 and at most
+ *   2^43, and the
+ *   storage triple codes [numel/2], absmax_fp8 [numel/64],
+ *   superscale [ceil(numel/16384)] (written by the quantizer, read by the
+ *   dequantizer); all device pointers, 16-byte aligned.  The tensors' buffers
+ *   must not overlap one another.
+ *   Errors: NULL, SHAPE (count, a numel, or more than 2^31 - 1 workgroups in
+ *   total), ALIGN, DEVICE; nothing is launched unless every tensor is valid.
+ */
+#define QLORA_MAX_TENSORS 16
+typedef struct nf4_tensor {
+    uint16_t* w;
+    int64_t numel;
+    uint8_t* codes;
+    uint8_t* absmax_fp8;
+    float* superscale;
+} nf4_tensor;
+int nf4_quantize_dq_grouped(int count, const nf4_tensor* tensors, void* stream);
+int nf4_dequantize_dq_grouped(int count, const nf4_tensor* tensors, void* stream);
 
 /* qlora_linear_bwd_input flag: reuse the forward's s X A (see below). */
 #define QLORA_BWD_REUSE_FORWARD 1u

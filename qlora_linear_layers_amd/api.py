@@ -53,6 +53,15 @@ _SIGS["qlora_grouped_workspace_bytes"] = (ctypes.c_size_t, [ctypes.c_int, ctypes
                                                             _c_i64])
 _SIGS["qlora_linear_fwd_grouped"] = (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(LinearProblem), _c_i64, _c_i64,
                                                     _c_p, ctypes.c_size_t, _c_p])
+
+
+class NF4Tensor(ctypes.Structure):
+    """nf4_tensor: one tensor of a grouped quantize / dequantize."""
+    _fields_ = [("w", _c_p), ("numel", _c_i64), ("codes", _c_p), ("absmax_fp8", _c_p), ("superscale", _c_p)]
+
+
+_SIGS["nf4_quantize_dq_grouped"] = (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(NF4Tensor), _c_p])
+_SIGS["nf4_dequantize_dq_grouped"] = (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(NF4Tensor), _c_p])
 # fp16 compute type: the same arguments as the bf16 entry point of the same stem
 for _n in ("nf4_quantize_dq", "nf4_dequantize_dq", "qlora_linear_fwd", "qlora_linear_bwd_input", "qlora_merge_lora"):
     _SIGS[_n + "_f16"] = _SIGS[_n]
@@ -197,6 +206,45 @@ def nf4_dequantize_dq(qw, out=None, dtype=torch.bfloat16):
     _check(fn, getattr(lib(), fn)(_ptr(qw.codes), _ptr(qw.absmax_fp8), _ptr(qw.superscale), qw.numel, _ptr(out),
                                   _stream()))
     return out
+
+
+MAX_TENSORS = 16         # QLORA_MAX_TENSORS
+
+
+def _tensor_array(ws, qws):
+    if len(ws) != len(qws):
+        raise ValueError("one storage triple per weight")
+    arr = (NF4Tensor * len(ws))()
+    for i, (w, qw) in enumerate(zip(ws, qws)):
+        _dev(w, torch.bfloat16, "w")
+        if w.numel() != qw.numel:
+            raise ValueError(f"tensor {i}: {w.numel()} elements, storage for {qw.numel}")
+        arr[i] = NF4Tensor(w.data_ptr(), w.numel(), qw.codes.data_ptr(), qw.absmax_fp8.data_ptr(),
+                           qw.superscale.data_ptr())
+    return arr
+
+
+def nf4_quantize_dq_grouped(ws, qws=None):
+    """Quantize up to 16 bf16 weights in one launch; returns (or fills) one NF4Weight per weight."""
+    if qws is None:
+        qws = []
+        for w in ws:
+            numel = w.numel()
+            N, K = (w.shape[0], w.shape[1]) if w.dim() == 2 else (1, numel)
+            qws.append(NF4Weight(torch.empty(numel // 2, dtype=torch.uint8, device=w.device),
+                                 torch.empty(max(numel // 64, 1), dtype=torch.uint8, device=w.device),
+                                 torch.empty(max(-(-numel // 16384), 1), dtype=torch.float32, device=w.device), N, K))
+    _check("nf4_quantize_dq_grouped", lib().nf4_quantize_dq_grouped(len(ws), _tensor_array(ws, qws), _stream()))
+    return qws
+
+
+def nf4_dequantize_dq_grouped(qws, outs=None):
+    """Dequantize up to 16 NF4Weights to bf16 in one launch; returns (or fills) the [N, K] outputs."""
+    if outs is None:
+        outs = [torch.empty((q.N, q.K), dtype=torch.bfloat16, device=q.codes.device) for q in qws]
+    _check("nf4_dequantize_dq_grouped", lib().nf4_dequantize_dq_grouped(len(qws), _tensor_array(outs, qws),
+                                                                           _stream()))
+    return outs
 
 
 def nf4_quantize(w):

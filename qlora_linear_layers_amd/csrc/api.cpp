@@ -23,8 +23,13 @@ hipError_t launch_lora_grads(const uint16_t* x, const uint16_t* dy, const LoraPl
 
 static_assert(QLORA_MAX_GROUP == ql::kMaxGroup, "group size of the header and the kernels");
 static_assert(QLORA_GROUPED_MAX_T == ql::kGemvMaxT, "decode token limit of the header and the kernels");
+static_assert(QLORA_MAX_TENSORS == ql::kMaxTensors, "tensor group size of the header and the kernels");
 
 namespace {
+
+// Largest element count of one quantized tensor: the dequantizer's grid
+// (one workgroup per 8192 weights) then stays below 2^31 workgroups.
+constexpr int64_t kMaxNumel = int64_t(1) << 43;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -54,14 +59,14 @@ bool scales_aligned(const ql::BlockScales& sc) {
 int dequantize_impl(const uint8_t* codes, ql::BlockScales sc, int64_t numel, uint16_t* w_out, void* stream,
                     bool int4 = false, bool f16 = false) {
     if (!codes || !scales_present(sc) || !w_out) return QLORA_ERR_NULL;
-    if (numel <= 0 || numel % 64 || numel > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
+    if (numel <= 0 || numel % 64 || numel > kMaxNumel) return QLORA_ERR_SHAPE;
     if (!aligned16(w_out) || !aligned16(codes) || !scales_aligned(sc)) return QLORA_ERR_ALIGN;
     return dev(ql::launch_dequantize(codes, sc, numel, w_out, static_cast<hipStream_t>(stream), int4, f16));
 }
 
 int quantize_sq_impl(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, void* stream, bool int4) {
     if (!w || !codes || !absmax) return QLORA_ERR_NULL;
-    if (numel <= 0 || numel % 64 || numel > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
+    if (numel <= 0 || numel % 64 || numel > kMaxNumel) return QLORA_ERR_SHAPE;
     if (!aligned16(w) || !aligned16(codes) || !aligned16(absmax)) return QLORA_ERR_ALIGN;
     return dev(ql::launch_quantize_sq(w, numel, codes, absmax, static_cast<hipStream_t>(stream), int4));
 }
@@ -173,10 +178,30 @@ int grouped_problems(int count, const qlora_linear_problem* problems, int64_t T,
     return QLORA_OK;
 }
 
+// Host checks of a grouped quantize / dequantize (the rules of the single
+// calls, per tensor), filling the kernel descriptors.
+int grouped_tensors(int count, const nf4_tensor* tensors, ql::QuantTensor* out) {
+    if (!tensors) return QLORA_ERR_NULL;
+    if (count < 1 || count > QLORA_MAX_TENSORS) return QLORA_ERR_SHAPE;
+    int64_t wgs = 0;
+    for (int i = 0; i < count; ++i) {
+        const nf4_tensor& t = tensors[i];
+        if (!t.w || !t.codes || !t.absmax_fp8 || !t.superscale) return QLORA_ERR_NULL;
+        if (t.numel <= 0 || t.numel % 64 || t.numel > kMaxNumel) return QLORA_ERR_SHAPE;
+        if (!aligned16(t.w) || !aligned16(t.codes) || !aligned16(t.absmax_fp8) || !aligned16(t.superscale))
+            return QLORA_ERR_ALIGN;
+        // the larger of the two launches' workgroup counts (groups of 256 blocks; 8192 weights)
+        wgs += ql::ceil_div(t.numel, 8192);
+        if (wgs > 0x7FFFFFFF) return QLORA_ERR_SHAPE;
+        out[i] = ql::QuantTensor{t.w, t.numel, t.codes, t.absmax_fp8, t.superscale, nullptr, t.w};
+    }
+    return QLORA_OK;
+}
+
 int quantize_dq_impl(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* absmax_fp8, float* superscale,
                      void* stream, bool f16) {
     if (!w || !codes || !absmax_fp8 || !superscale) return QLORA_ERR_NULL;
-    if (numel <= 0 || numel % 64 || numel > (int64_t(1) << 46)) return QLORA_ERR_SHAPE;
+    if (numel <= 0 || numel % 64 || numel > kMaxNumel) return QLORA_ERR_SHAPE;
     if (!aligned16(w) || !aligned16(codes) || !aligned16(absmax_fp8) || !aligned16(superscale))
         return QLORA_ERR_ALIGN;
     return dev(ql::launch_quantize(w, numel, codes, absmax_fp8, superscale, static_cast<hipStream_t>(stream), f16));
@@ -319,6 +344,18 @@ int qlora_merge_lora_f16(const uint8_t* codes, const uint8_t* absmax_fp8, const 
                          uint16_t* w_out, void* stream) {
     return merge_impl(codes, dq_scales(absmax_fp8, superscale), K, N, lora_a, lora_b, r, scaling, w_out, stream,
                       true);
+}
+
+int nf4_quantize_dq_grouped(int count, const nf4_tensor* tensors, void* stream) {
+    ql::QuantTensor t[ql::kMaxTensors];
+    if (int st = grouped_tensors(count, tensors, t)) return st;
+    return dev(ql::launch_quantize_group(t, count, static_cast<hipStream_t>(stream), false));
+}
+
+int nf4_dequantize_dq_grouped(int count, const nf4_tensor* tensors, void* stream) {
+    ql::QuantTensor t[ql::kMaxTensors];
+    if (int st = grouped_tensors(count, tensors, t)) return st;
+    return dev(ql::launch_dequantize_group(t, count, static_cast<hipStream_t>(stream), false, false));
 }
 
 size_t qlora_grouped_workspace_bytes(int count, const qlora_linear_problem* problems, int64_t T, int64_t r) {

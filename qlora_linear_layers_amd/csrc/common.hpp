@@ -251,6 +251,38 @@ struct BlockScales {
     bool single() const { return absmax != nullptr; }
 };
 
+// One tensor of a grouped quantize or dequantize launch: `w` is read by the
+// quantizer, `out` written by the dequantizer; `absmax` set selects single
+// quantization (fp8/sup unused).
+constexpr int kMaxTensors = 16;
+struct QuantTensor {
+    const uint16_t* w;
+    int64_t numel;
+    uint8_t* codes;
+    uint8_t* fp8;
+    float* sup;
+    float* absmax;
+    uint16_t* out;
+};
+struct QuantGroup {
+    QuantTensor t[kMaxTensors];
+    int end[kMaxTensors];     // cumulative workgroup ends
+    int count;
+};
+
+// Tensor that owns workgroup `bid`, given ascending cumulative ends (uniform).
+template <int MAXG>
+QL_DEV int group_index(const int* ends, int count, int bid) {
+    int i = 0;
+#pragma unroll
+    for (int j = 0; j < MAXG - 1; ++j) i += (j < count - 1 && bid >= ends[j]) ? 1 : 0;
+    return i;
+}
+QL_DEV int tensor_of(const int* ends, int count, int bid) { return group_index<kMaxTensors>(ends, count, bid); }
+
+hipError_t launch_quantize_group(const QuantTensor* ts, int count, hipStream_t s, bool f16);
+hipError_t launch_dequantize_group(const QuantTensor* ts, int count, hipStream_t s, bool int4, bool f16);
+
 // f16: the weights (quantize) / the output (dequantize, merge) are fp16
 hipError_t launch_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* fp8,
                            float* superscale, hipStream_t s, bool f16 = false);

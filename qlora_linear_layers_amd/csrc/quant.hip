@@ -7,6 +7,7 @@
 // quantized to FP8 in groups of 256 under one fp32 super-scale; dequantization
 // in reverse order).
 #include "common.hpp"
+#include "plan.hpp"
 
 namespace ql {
 
@@ -29,17 +30,27 @@ namespace ql {
 // 1/14 that ratios of bf16 values can reach, so the reciprocal shortcut does
 // not hold for them).  F16: the weights are fp16 (11-bit significands, for
 // which that argument does not hold either, so they take exact division too).
+//
+// A launch covers a group of tensors (one for the single-tensor entry points):
+// workgroup ids are dealt to the tensors in order, `end` holding the
+// cumulative workgroup ends.
 template <bool SQ, bool EXACT, bool F16>
-__global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ w, int64_t nblocks,
-                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ fp8,
-                                                  float* __restrict__ superscale, float* __restrict__ absmax,
-                                                  EncodeTable tab) {
+__global__ __launch_bounds__(256) void k_quantize(QuantGroup grp, EncodeTable tab) {
     __shared__ uint2 s_tab[34];
     __shared__ float s_c1[kGroup];
     __shared__ float s_wmax[4];
 
+    const int ti = tensor_of(grp.end, grp.count, (int)blockIdx.x);
+    const int gl = (int)blockIdx.x - (ti ? grp.end[ti - 1] : 0);        // group of 256 blocks within the tensor
+    const uint16_t* __restrict__ w = grp.t[ti].w;
+    const int64_t nblocks = grp.t[ti].numel / kBlock;
+    uint8_t* __restrict__ codes = grp.t[ti].codes;
+    uint8_t* __restrict__ fp8 = grp.t[ti].fp8;
+    float* __restrict__ superscale = grp.t[ti].sup;
+    float* __restrict__ absmax = grp.t[ti].absmax;
+
     const int tid = threadIdx.x;
-    const int64_t blk0 = (int64_t)blockIdx.x * kGroup;
+    const int64_t blk0 = (int64_t)gl * kGroup;
     const int nb = (int)((nblocks - blk0) < kGroup ? (nblocks - blk0) : kGroup);
     if (tid < 34) s_tab[tid] = make_uint2(__float_as_uint(tab.thr[tid]), tab.base[tid]);
 
@@ -115,7 +126,7 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ w
     __syncthreads();
     const float amax = fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
     const float s2 = __fdiv_rn(amax, 448.0f);
-    if (tid == 0) superscale[blockIdx.x] = s2;
+    if (tid == 0) superscale[gl] = s2;
     if (tid < nb) {
         uint32_t code = 0;
         if (s2 > 0.0f) code = e4m3_encode_tie_low(fminf(__fdiv_rn(s_c1[tid], s2), 448.0f));
@@ -123,29 +134,46 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ w
     }
 }
 
+hipError_t launch_quantize_group(const QuantTensor* ts, int count, hipStream_t s, bool f16) {
+    if (count < 1 || count > kMaxTensors) return hipErrorInvalidValue;
+    QuantGroup g{};
+    int64_t wgs = 0;
+    for (int i = 0; i < count; ++i) {
+        g.t[i] = ts[i];
+        wgs += ceil_div(ts[i].numel / kBlock, kGroup);
+        if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+        g.end[i] = (int)wgs;
+    }
+    g.count = count;
+    if (f16)
+        hipLaunchKernelGGL((k_quantize<false, false, true>), dim3((unsigned)wgs), dim3(256), 0, s, g,
+                           host_encode_table());
+    else
+        hipLaunchKernelGGL((k_quantize<false, false, false>), dim3((unsigned)wgs), dim3(256), 0, s, g,
+                           host_encode_table());
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* fp8,
                            float* superscale, hipStream_t s, bool f16) {
-    const int64_t nblocks = numel / kBlock;
-    const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
-    if (f16)
-        hipLaunchKernelGGL((k_quantize<false, false, true>), dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks,
-                           codes, fp8, superscale, nullptr, host_encode_table());
-    else
-        hipLaunchKernelGGL((k_quantize<false, false, false>), dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks,
-                           codes, fp8, superscale, nullptr, host_encode_table());
-    return hipGetLastError();
+    const QuantTensor t{w, numel, codes, fp8, superscale, nullptr, nullptr};
+    return launch_quantize_group(&t, 1, s, f16);
 }
 
 hipError_t launch_quantize_sq(const uint16_t* w, int64_t numel, uint8_t* codes, float* absmax, hipStream_t s,
                               bool int4) {
-    const int64_t nblocks = numel / kBlock;
-    const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
+    QuantGroup g{};
+    g.t[0] = QuantTensor{w, numel, codes, nullptr, nullptr, absmax, nullptr};
+    const int64_t wgs = ceil_div(numel / kBlock, kGroup);
+    if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+    g.end[0] = (int)wgs;
+    g.count = 1;
     if (int4)
-        hipLaunchKernelGGL((k_quantize<true, true, false>), dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes,
-                           nullptr, nullptr, absmax, host_int4_encode_table());
+        hipLaunchKernelGGL((k_quantize<true, true, false>), dim3((unsigned)wgs), dim3(256), 0, s, g,
+                           host_int4_encode_table());
     else
-        hipLaunchKernelGGL((k_quantize<true, false, false>), dim3((unsigned)ngroups), dim3(256), 0, s, w, nblocks, codes,
-                           nullptr, nullptr, absmax, host_encode_table());
+        hipLaunchKernelGGL((k_quantize<true, false, false>), dim3((unsigned)wgs), dim3(256), 0, s, g,
+                           host_encode_table());
     return hipGetLastError();
 }
 
@@ -162,17 +190,21 @@ hipError_t launch_quantize_sq(const uint16_t* w, int64_t numel, uint8_t* codes, 
 constexpr int kDeqUnits = 4;
 
 template <bool SQ, bool F16>
-__global__ __launch_bounds__(256) void k_dequantize(const uint32_t* __restrict__ codes,
-                                                    const uint8_t* __restrict__ fp8,
-                                                    const float* __restrict__ superscale,
-                                                    const float* __restrict__ absmax,
-                                                    int64_t nunits, u32x4_t* __restrict__ out, Codebook cb) {
+__global__ __launch_bounds__(256) void k_dequantize(QuantGroup grp, Codebook cb) {
     __shared__ float s_q[16];
+    const int ti = tensor_of(grp.end, grp.count, (int)blockIdx.x);
+    const int64_t gl = (int)blockIdx.x - (ti ? grp.end[ti - 1] : 0);    // workgroup within the tensor
+    const uint32_t* __restrict__ codes = reinterpret_cast<const uint32_t*>(grp.t[ti].codes);
+    const uint8_t* __restrict__ fp8 = grp.t[ti].fp8;
+    const float* __restrict__ superscale = grp.t[ti].sup;
+    const float* __restrict__ absmax = grp.t[ti].absmax;
+    const int64_t nunits = grp.t[ti].numel / 8;
+    u32x4_t* __restrict__ out = reinterpret_cast<u32x4_t*>(grp.t[ti].out);
 #pragma unroll
     for (int j = 0; j < 16; ++j)
         if (threadIdx.x == j) s_q[j] = cb_value(cb, j);     // constant indexes: no memory round trip
 
-    const int64_t u0 = (int64_t)blockIdx.x * (256 * kDeqUnits) + threadIdx.x;
+    const int64_t u0 = gl * (256 * kDeqUnits) + threadIdx.x;
     uint32_t cv[kDeqUnits];
     uint32_t f8[kDeqUnits];
     float s2[kDeqUnits];
@@ -206,20 +238,31 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint32_t* __restrict__
     }
 }
 
-hipError_t launch_dequantize(const uint8_t* codes, BlockScales sc, int64_t numel, uint16_t* out, hipStream_t s,
-                             bool int4, bool f16) {
+hipError_t launch_dequantize_group(const QuantTensor* ts, int count, hipStream_t s, bool int4, bool f16) {
+    if (count < 1 || count > kMaxTensors) return hipErrorInvalidValue;
     const Codebook& cb = int4 ? host_int4_codebook() : host_codebook();
-    const int64_t nunits = numel / 8;
+    QuantGroup g{};
+    int64_t wgs = 0;
     const int64_t per_wg = 256 * kDeqUnits;
-    const dim3 grid((unsigned)((nunits + per_wg - 1) / per_wg));
-    const uint32_t* c = reinterpret_cast<const uint32_t*>(codes);
-    u32x4_t* o = reinterpret_cast<u32x4_t*>(out);
-    auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, c, sc.fp8, sc.sup, sc.absmax, nunits, o, cb);
-    };
-    if (sc.single()) f16 ? go(k_dequantize<true, true>) : go(k_dequantize<true, false>);
+    for (int i = 0; i < count; ++i) {
+        g.t[i] = ts[i];
+        wgs += ceil_div(ts[i].numel / 8, per_wg);
+        if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+        g.end[i] = (int)wgs;
+    }
+    g.count = count;
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(256), 0, s, g, cb); };
+    const bool sq = ts[0].absmax != nullptr;
+    if (sq) f16 ? go(k_dequantize<true, true>) : go(k_dequantize<true, false>);
     else f16 ? go(k_dequantize<false, true>) : go(k_dequantize<false, false>);
     return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, BlockScales sc, int64_t numel, uint16_t* out, hipStream_t s,
+                             bool int4, bool f16) {
+    const QuantTensor t{nullptr, numel, const_cast<uint8_t*>(codes), const_cast<uint8_t*>(sc.fp8),
+                        const_cast<float*>(sc.sup), const_cast<float*>(sc.absmax), out};
+    return launch_dequantize_group(&t, 1, s, int4, f16);
 }
 
 }  // namespace ql

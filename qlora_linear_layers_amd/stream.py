@@ -5,9 +5,10 @@ figure, and the memory table of section 2.4: about 35 GB of 4-bit weights for
 70B parameters, against about 140 GB in bf16) is about the stored format; the
 bf16 source never needs to be resident as a whole.  This driver walks the
 layers in order: it obtains one layer's bf16
-weights from a caller-supplied function, quantizes every tensor with
-``nf4_quantize_dq`` into storage that is reused for every layer, dequantizes it
-back with ``nf4_dequantize_dq`` into reused bf16 buffers, hands both to an
+weights from a caller-supplied function, quantizes all its tensors with one
+``nf4_quantize_dq_grouped`` launch into storage that is reused for every layer,
+dequantizes them back with one ``nf4_dequantize_dq_grouped`` launch into reused
+bf16 buffers, hands both to an
 optional per-layer callback (to keep, check or copy out what it needs), and then
 drops the layer's weights before the next one is drawn.
 
@@ -59,9 +60,11 @@ class LayerStream:
             ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if timed else None
             if ev:
                 ev[0].record(stream)
-            for w, qw, wd in zip(ws, self.qws, self.wds):
-                api.nf4_quantize_dq_into(w, qw)
-                api.nf4_dequantize_dq(qw, out=wd)
+            # all tensors of the layer in one launch per step (at most 16 per launch)
+            for i in range(0, len(ws), api.MAX_TENSORS):
+                api.nf4_quantize_dq_grouped(ws[i:i + api.MAX_TENSORS], self.qws[i:i + api.MAX_TENSORS])
+            for i in range(0, len(ws), api.MAX_TENSORS):
+                api.nf4_dequantize_dq_grouped(self.qws[i:i + api.MAX_TENSORS], self.wds[i:i + api.MAX_TENSORS])
             if ev:
                 ev[1].record(stream)
                 events.append(ev)

@@ -231,3 +231,28 @@ def test_grouped_validation(L):
     assert wb(3, _problems(3), 8, 16) == 3 * one
     assert wb(9, _problems(9), 8, 16) == 0
     assert wb(2, _problems(2, {1: dict(N=100)}), 8, 16) == 0
+
+
+def _tensors(n, over=None):
+    arr = (api.NF4Tensor * n)()
+    for i in range(n):
+        d = dict(w=FAKE, numel=64 * 300, codes=FAKE, absmax_fp8=FAKE, superscale=FAKE)
+        d.update((over or {}).get(i, {}))
+        arr[i] = api.NF4Tensor(**d)
+    return arr
+
+
+def test_grouped_quantize_validation(L):
+    for f in (L.nf4_quantize_dq_grouped, L.nf4_dequantize_dq_grouped):
+        assert f(2, None, None) == NULL
+        assert f(0, _tensors(1), None) == SHAPE
+        assert f(17, _tensors(17), None) == SHAPE                          # above QLORA_MAX_TENSORS
+        assert f(2, _tensors(2, {1: dict(numel=100)}), None) == SHAPE
+        assert f(2, _tensors(2, {1: dict(numel=0)}), None) == SHAPE
+        assert f(2, _tensors(2, {0: dict(numel=(1 << 43) + 64)}), None) == SHAPE
+        assert f(2, _tensors(2, {1: dict(codes=None)}), None) == NULL
+        assert f(2, _tensors(2, {0: dict(w=MIS)}), None) == ALIGN
+        assert f(2, _tensors(2, {1: dict(superscale=MIS)}), None) == ALIGN
+    # single-tensor calls share the element limit
+    assert L.nf4_quantize_dq(FAKE, (1 << 43) + 64, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.nf4_dequantize_dq(FAKE, FAKE, FAKE, (1 << 43) + 64, FAKE, None) == SHAPE

@@ -120,3 +120,29 @@ def test_dequantize_oracle_storage_and_determinism():
     b = _gpu_quant(w, (1024, 4096))
     for u, v in zip(a[1:], b[1:]):
         assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+def test_grouped_launch_matches_single_calls():
+    """Several tensors in one launch (the maximum of 16): every storage byte and every
+    dequantized value equals the single-tensor call's; the small, ragged tensors
+    (partial groups, a single block) are also checked against the oracle directly."""
+    shapes = [(lin.N, lin.K) for lin in synth.LLAMA7B] + [(300, 64), (1, 64), (5, 4096), (4, 16384 // 4 + 64)]
+    shapes += [(64 * (i + 1), 192) for i in range(16 - len(shapes))]
+    ws = []
+    for i, (N, K) in enumerate(shapes):
+        g = synth.device_generator(10, 0, i, synth.ROLE_W)
+        ws.append(synth.device_normal_bf16(g, (N, K), 0.02))
+    say(f"[quant grouped] {len(ws)} tensors")
+    got = api.nf4_quantize_dq_grouped(ws)
+    ref = [api.nf4_quantize_dq(w) for w in ws]
+    for (N, K), g_, r_ in zip(shapes, got, ref):
+        for name in ("codes", "absmax_fp8", "superscale"):
+            assert torch.equal(getattr(g_, name), getattr(r_, name)), f"{N}x{K} {name}"
+    outs = api.nf4_dequantize_dq_grouped(got)
+    for (N, K), o, r_ in zip(shapes, outs, ref):
+        assert torch.equal(o.view(torch.int16), api.nf4_dequantize_dq(r_).view(torch.int16)), f"{N}x{K} dequantized"
+    for (N, K), w, g_, o in list(zip(shapes, ws, got, outs))[7:11]:
+        rc, rf, rs = oracle.quantize_nf4_dq(bits_of(w).reshape(-1))
+        assert np.array_equal(g_.codes.cpu().numpy(), rc) and np.array_equal(g_.absmax_fp8.cpu().numpy(), rf)
+        assert np.array_equal(g_.superscale.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+        assert np.array_equal(bits_of(o).reshape(-1), oracle.dequantize_nf4_dq(rc, rf, rs)), f"{N}x{K} vs oracle"
