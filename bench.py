@@ -3,11 +3,11 @@
 
 Workload (one "step"): the seven linears of a LLaMA-7B-shaped transformer
 layer (q/k/v/o 4096x4096, gate/up 11008x4096, down 4096x11008) at training
-shape T = 8 x 512 = 4096 tokens, LoRA rank 64, alpha 16 (s = 0.25).  For each
-linear the step runs the whole path: NF4 + double quantization of the bf16
-weight, double dequantization back to bf16, the fused forward
-Y = X W'^T + s (X A) B, and the backward dX = dY W' + s (dY B^T) A^T with the
-LoRA gradients dA, dB.  Inputs are seeded synthetic tensors (W ~ N(0, 0.02),
+shape T = 8 x 512 = 4096 tokens, LoRA rank 64, alpha 16 (s = 0.25).  The step
+runs the whole path: NF4 + double quantization of the seven bf16 weights (one
+grouped launch), their double dequantization back to bf16 (one grouped
+launch), and for each linear the fused forward Y = X W'^T + s (X A) B and the
+backward dX = dY W' + s (dY B^T) A^T with the LoRA gradients dA, dB.  Inputs are seeded synthetic tensors (W ~ N(0, 0.02),
 X, dY ~ N(0, 1), A, B ~ N(0, 0.01)), resident in HBM before timing starts.
 
 Output: one JSON line.  `value` is the step's attainment of the MI355X
@@ -17,7 +17,8 @@ for the GEMM phases) divided by the measured step time.  Per-phase durations
 come from HIP events recorded on the stream the kernels run on.  Outside the
 step, `components` also carries the decode forward (T = 1 / 4 / 8), the LoRA
 merge, the single-quantization variant, the fp16 compute type and the
-NF4-vs-INT4 data-type ablation measured on the same seven linears.
+NF4-vs-INT4 data-type ablation measured on the same seven linears, the
+65B-shaped layer and the 70B-shaped streaming quantization.
 """
 import argparse
 import json
@@ -304,7 +305,8 @@ def measure_f16(api, torch, bufs, T, r, s, ws, reps=5):
 
 def measure_65b(api, torch, synth, reps=3):
     """The 65B-shaped layer (q/k/v/o 8192x8192, gate/up 22016x8192, down 8192x22016;
-    T = 2048, r = 64, s = 0.25): full-layer quantize and dequantize, the fused
+    T = 2048, r = 64, s = 0.25): full-layer quantize and dequantize (one grouped
+    launch each), the fused
     forward, and the backward input gradient dX = dY W' + s (dY B^T) A^T, each
     timed over `reps` passes of the seven linears with HIP events.  Inputs are
     drawn on the device (809.5 M weights).  Returns {phase: (kind, seconds, amount)}."""
@@ -327,10 +329,12 @@ def measure_65b(api, torch, synth, reps=3):
     def bwd_flops(l):
         return 2 * T * l.N * l.K + 2 * T * l.N * r + 2 * T * r * l.K
 
+    wl, ql, dl = [b["w"] for b in bufs], [b["qw"] for b in bufs], [b["wd"] for b in bufs]
+    # quantize / dequantize: the whole layer in one grouped launch (run once per pass)
     ops = {
-        "quantize": ("hbm", lambda b: api.nf4_quantize_dq_into(b["w"], b["qw"]),
+        "quantize": ("hbm", lambda b: b is bufs[0] and api.nf4_quantize_dq_grouped(wl, ql),
                      lambda l: phase_work(l, T, r)["quantize"][1]),
-        "dequantize": ("hbm", lambda b: api.nf4_dequantize_dq(b["qw"], out=b["wd"]),
+        "dequantize": ("hbm", lambda b: b is bufs[0] and api.nf4_dequantize_dq_grouped(ql, dl),
                        lambda l: phase_work(l, T, r)["dequantize"][1]),
         "forward": ("mfma", lambda b: api.qlora_linear_fwd(b["x"], b["qw"], b["a"], b["b"], s, workspace=ws,
                                                             out=b["y"]),
@@ -496,25 +500,29 @@ def main():
     phases = ("quantize", "dequantize", "forward", "backward")
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
+    wlist, qlist, dlist = [b["w"] for b in bufs], [b["qw"] for b in bufs], [b["wd"] for b in bufs]
+
+    def step(ev=None):
+        # ev: [quantize start, quantize end = dequantize start, dequantize end, then per linear
+        # forward end and backward end]
+        if ev: ev[0].record(stream)
+        api.nf4_quantize_dq_grouped(wlist, qlist)          # the seven weights in one launch
+        if ev: ev[1].record(stream)
+        api.nf4_dequantize_dq_grouped(qlist, dlist)
+        if ev: ev[2].record(stream)
         for li, b in enumerate(bufs):
-            ev = events[li] if events is not None else None
-            if ev: ev[0].record(stream)
-            api.nf4_quantize_dq_into(b["w"], b["qw"])
-            if ev: ev[1].record(stream)
-            api.nf4_dequantize_dq(b["qw"], out=b["wd"])
-            if ev: ev[2].record(stream)
             api.qlora_linear_fwd(b["x"], b["qw"], b["a"], b["b"], s, workspace=ws, out=b["y"])
-            if ev: ev[3].record(stream)
+            if ev: ev[3 + 2 * li].record(stream)
             api.qlora_linear_bwd_input(b["dy"], b["qw"], b["a"], b["b"], s, x=b["x"], lora_grads=True,
                                        workspace=ws, dx=b["dx"], d_lora_a=b["da"], d_lora_b=b["db"],
                                        reuse_forward=True)
-            if ev: ev[4].record(stream)
+            if ev: ev[4 + 2 * li].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    all_events = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in bufs] for _ in range(args.steps)]
+    nev = 3 + 2 * len(bufs)
+    all_events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -523,13 +531,15 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
 
-    # per-phase, per-linear average durations (ms) from the events
-    dur = {p: np.zeros(len(bufs)) for p in phases}
-    for k in range(args.steps):
+    # per-phase average durations (ms) from the events: quantize and dequantize of the
+    # seven weights (one launch each), forward and backward per linear
+    dur = {p: 0.0 for p in phases}
+    for ev in all_events:
+        dur["quantize"] += ev[0].elapsed_time(ev[1]) / args.steps
+        dur["dequantize"] += ev[1].elapsed_time(ev[2]) / args.steps
         for li in range(len(bufs)):
-            ev = all_events[k][li]
-            for pi, p in enumerate(phases):
-                dur[p][li] += ev[pi].elapsed_time(ev[pi + 1]) / args.steps
+            dur["forward"] += ev[2 + 2 * li].elapsed_time(ev[3 + 2 * li]) / args.steps
+            dur["backward"] += ev[3 + 2 * li].elapsed_time(ev[4 + 2 * li]) / args.steps
 
     comp = {}
     roof_step = 0.0
@@ -539,7 +549,7 @@ def main():
         for b in bufs:
             kind, a = phase_work(b["lin"], T, r)[p]
             amt += a
-        secs = dur[p].sum() / 1e3
+        secs = dur[p] / 1e3
         rs = roofline_seconds(kind, amt)
         roof_step += rs
         if kind == "hbm":
@@ -568,7 +578,7 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "LLaMA-7B-shaped layer, 7 linears (q/k/v/o 4096x4096, gate/up 11008x4096, "
-                               "down 4096x11008), T=4096 tokens, LoRA r=64 alpha=16; step = quantize + dequantize "
+                               "down 4096x11008), T=4096 tokens, LoRA r=64 alpha=16; step = quantize + dequantize (grouped) "
                                "+ forward + backward (dX, dA, dB; s X A kept from the forward) of every linear",
                    "global_batch": 8, "seq_len": 512, "parallelism": "none (1 GPU)"},
         "components": comp,
@@ -622,14 +632,14 @@ def main():
                 comp[key] = {"TFLOP/s": round(amt / secs / 1e12, 1),
                              "frac_of_mfma_peak": round(amt / secs / MFMA_BF16_PEAK, 4), "ms": round(1e3 * secs, 4)}
             comp[key]["note"] = ("65B-shaped layer (q/k/v/o 8192x8192, gate/up 22016x8192, down 8192x22016), "
-                                 "T=2048, r=64; 7 linears per pass")
+                                 "T=2048, r=64; 7 linears per pass (quantize / dequantize: one grouped launch)")
         secs, moved, packed, params = measure_stream_70b(torch, synth)
         closed = params * (4 + 8 / 64 + 32 / 16384) / 8
         comp["stream_70b"] = {"GB/s": round(moved / secs / 1e9, 1), "frac_of_hbm_peak": round(moved / secs / HBM_PEAK, 4),
                               "ms": round(1e3 * secs, 3), "params": params, "packed_bytes": packed,
                               "closed_form_bytes": int(closed), "bits_per_param": round(8 * packed / params, 9),
-                              "note": "80 layers x 7 tensors (70B shapes, 0.1% t3 outliers), quantize_dq then "
-                                      "dequantize each tensor, one layer resident; kernel time only"}
+                              "note": "80 layers x 7 tensors (70B shapes, 0.1% t3 outliers), grouped quantize_dq then "
+                                      "grouped dequantize per layer, one layer resident; kernel time only"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers, T, r, s, args.cpu_tokens)
     print(json.dumps(out), flush=True)
