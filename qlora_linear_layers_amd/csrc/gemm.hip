@@ -140,12 +140,32 @@ QL_DEV bf16x8_t lds_frag(const lds8_t* base, int row, int chunk) {
     return *reinterpret_cast<const lds_bf16x8_t*>(base + lds_off(row, chunk));
 }
 
-// C[a][b] to out[b][a] (a contiguous), 16-bit: four consecutive a of one b
-// per MFMA row group g of a 32 x 32 accumulator, as one 8-byte store.
+// Output tiles [256 (t)][256 (c)] of 16-bit values staged in LDS (128 KB) so
+// that the global stores are whole rows.  Row t is 512 bytes; its 16-byte
+// chunk c sits at chunk position c ^ (t & 31), which keeps both the
+// accumulator writes (32 rows at one chunk) and the row reads conflict-free.
+QL_DEV uint32_t otile_off(int t, int c) { return (uint32_t)t * 512u + ((uint32_t)(c ^ (t & 31)) << 4); }
+
+// Columns col .. col+3 (col % 4 == 0) of tile row t: the four consecutive
+// accumulator rows of MFMA row group g.
 template <bool F16>
-QL_DEV void store4_16(const f32x16_t& v, int g, uint16_t* out, int64_t ldo, int64_t a, int64_t b) {
+QL_DEV void otile_put4(lds8_t* lo, const f32x16_t& v, int g, int t, int col) {
     const u32x2_t o = {pack16x2<F16>(v[4 * g], v[4 * g + 1]), pack16x2<F16>(v[4 * g + 2], v[4 * g + 3])};
-    *reinterpret_cast<u32x2_t*>(out + b * ldo + a) = o;
+    *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(lo + otile_off(t, col >> 3) + (col & 7) * 2) = o;
+}
+
+// out[t0 + t][c0 + c] = tile[t][c] for t0 + t < T and c0 + c < C (C % 8 == 0):
+// each wave store covers two rows of 512 contiguous bytes.
+QL_DEV void otile_store(const lds8_t* lo, uint16_t* out, int64_t ldo, int64_t t0, int64_t c0, int64_t T, int64_t C) {
+#pragma unroll 8
+    for (int it = 0; it < 256 * 32 / kThreads; ++it) {
+        const int u = threadIdx.x + it * kThreads;
+        const int t = u >> 5, c = u & 31;
+        const int64_t tg = t0 + t, cg = c0 + c * 8;
+        if (tg < T && cg < C)
+            *reinterpret_cast<u32x4_t*>(out + tg * ldo + cg) =
+                *reinterpret_cast<const lds_u32x4_t*>(lo + otile_off(t, c));
+    }
 }
 
 // Map a linear workgroup id to an (a-tile, b-tile) pair.  Workgroups are
@@ -468,19 +488,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
         }
     }
 
-    // C[n][t] -> Y[t][n]
+    // C[n][t] -> Y[t][n] through an LDS tile over the X buffers and the table
+    __syncthreads();                          // every wave is done reading them
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t t = t0 + 32 * j + r;
-            if (t >= p.T) continue;
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t n = n0 + 64 * w + 32 * i + 8 * g + 4 * h;
-                if (n < p.N) store4_16<F16>(acc[i][j], g, p.y, p.N, n, t);
-            }
-        }
+            for (int g = 0; g < 4; ++g) otile_put4<F16>(smem, acc[i][j], g, 32 * j + r, 64 * w + 32 * i + 8 * g + 4 * h);
+    __syncthreads();
+    otile_store(smem, p.y, p.N, t0, n0, p.T, p.N);
 }
 
 constexpr size_t kFwdSmem = 2 * 256 * 128 + kWideTableBytes;
@@ -782,19 +799,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
             }
         }
     }
-    // C[k][t] -> dX[t][k]
+    // C[k][t] -> dX[t][k] through an LDS tile over the W and dY tiles
+    __syncthreads();                          // every wave is done reading them
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t t = t0 + wb * 128 + j * 32 + r;
-            if (t >= p.T) continue;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t k = k0 + wa * 128 + i * 32 + g * 8 + h * 4;
-                if (k < p.K) store4_16<F16>(acc[i][j], g, p.dx, p.K, k, t);
-            }
-        }
+            for (int g = 0; g < 4; ++g)
+                otile_put4<F16>(smem, acc[i][j], g, wb * 128 + j * 32 + r, wa * 128 + i * 32 + g * 8 + h * 4);
+    __syncthreads();
+    otile_store(smem, p.dx, p.K, t0, k0, p.T, p.K);
 }
 
 constexpr size_t kDxSmem = 4 * 256 * 128 + kNarrowTableBytes;
