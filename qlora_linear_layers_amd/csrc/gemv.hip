@@ -18,9 +18,9 @@
 // (one byte permute builds the LDS address), scaled by the block constant,
 // rounded to bf16 and packed: the per-weight work does not grow with T.
 //
-// Workgroup: eight waves, two groups of 64 W rows (four 16-row MFMA tiles per
-// wave) times four 128-wide k steps, so 128 rows x 512 k; the four k waves of a
-// row group are added in LDS in wave order and one fp32 partial per
+// Workgroup (kKW, kRG below): eight waves, two groups of 64 W rows (four
+// 16-row MFMA tiles per wave) times four 128-wide k steps, so 128 rows x 512 k;
+// the k waves of a row group are added in LDS in wave order and one fp32 partial per
 // (k split, token, row) is written.  The LoRA down projection runs as extra
 // workgroups of the same launch over 256-wide k slices (VALU, lane = rank).
 #include <type_traits>
@@ -72,9 +72,12 @@ __device__ __forceinline__ int group_find(const int* ends, int count, int bid) {
     return i;
 }
 
-constexpr int kDecThreads = 512;  // eight waves: 2 row groups x 4 k steps
-constexpr int kDecRows = 128;     // W rows per workgroup
-constexpr int kDecK = 512;        // k per workgroup
+constexpr int kKW = 4;            // k waves per row group, 128 k each
+constexpr int kRG = 2;            // row groups of 64 W rows
+constexpr int kDecThreads = 64 * kKW * kRG;
+constexpr int kDecRows = 64 * kRG;  // W rows per workgroup
+constexpr int kDecK = 128 * kKW;    // k per workgroup
+static_assert(kRG * kKW * 4 * 64 * 16 <= (int)kWideTableBytes, "wave sums must fit over the pair table");
 constexpr int kLoraSlice = 256;   // k per LoRA down-projection workgroup (one 64-k chunk per wave)
 constexpr size_t kDecLds = kWideTableBytes;   // pair table; later reused for the wave sums
 
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(kDecThreads) void k_gemv(GemvGroup grp, Codebook cb
     lds8_t* tbl = (lds8_t*)dyn;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wave = wv & 3, rg = wv >> 2;                             // k step, row group
+    const int wave = wv % kKW, rg = wv / kKW;                          // k step, row group
     const int nl = lane & 15, g = lane >> 4;
     const int nb = (int)ceil_div(p.N, kDecRows);
     const int rb = bx % nb, ks = bx / nb;
@@ -221,17 +224,19 @@ __global__ __launch_bounds__(kDecThreads) void k_gemv(GemvGroup grp, Codebook cb
         }
     }
 
-    // the four k waves of a row group meet in LDS (over the table), in wave order
+    // the k waves of a row group meet in LDS (over the table), in wave order
     __syncthreads();
-    f32x4_t* red = reinterpret_cast<f32x4_t*>(dyn) + rg * 1024;        // [4 waves][4 tiles][64 lanes]
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(dyn) + rg * (kKW * 4 * 64);   // [kKW waves][4 tiles][64 lanes]
 #pragma unroll
     for (int c = 0; c < 4; ++c) red[(wave * 4 + c) * 64 + lane] = acc[c];
     __syncthreads();
-    {
+    if (wave < 4) {
         // thread (rg, c, l): tile c of its row group, accumulator lane l =
         // row 16c + (l & 15), tokens 4 (l >> 4) .. +3
         const int c = wave, l = lane;
-        const f32x4_t v = ((red[c * 64 + l] + red[(4 + c) * 64 + l]) + red[(8 + c) * 64 + l]) + red[(12 + c) * 64 + l];
+        f32x4_t v = red[c * 64 + l];
+#pragma unroll
+        for (int w = 1; w < kKW; ++w) v += red[(w * 4 + c) * 64 + l];
         const int64_t n = n0 + 16 * c + (l & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
