@@ -10,7 +10,8 @@
 //
 // Workgroup: 64 rows n x 256 k, four waves of 64 k.  B's 64 columns of the
 // workgroup are staged transposed in LDS ([n][j], XOR-swizzled 64-wide j
-// blocks), so both MFMA operands are 16-byte fragment reads.  Each wave runs
+// blocks; an 8 x 8 register transpose per lane, so the staging is 16-byte LDS
+// writes), and both MFMA operands are 16-byte fragment reads.  Each wave runs
 // v_mfma_f32_16x16x32_bf16 with the A operand = rows of A (index k) and the B
 // operand = columns of B^T's transpose (index n), 4 x 4 tiles of 16 k x 16 n.
 // The k of MFMA row m in row tile t is 32 (t / 2) + 8 (m / 4) + 4 (t % 2) +
@@ -100,21 +101,28 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs p, Codebook cb) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) apre[js][t] = a_frag(js, t);
 
-    // stage B^T: thread takes 16 bytes of row j of B (8 columns; N % 8 == 0
-    // keeps them inside the row and 16-byte aligned) and writes them down
-    // column j of the transposed tile; ranks j >= r and columns n >= N are zeros
-#pragma unroll
-    for (int i = 0; i < RP * 2; ++i) {
-        const int ch = (int)threadIdx.x + 256 * i;                      // RP * 64 rows j x 8 chunks
-        const int j = ch >> 3, nc = ch & 7;
-        const int64_t n = n0 + 8 * nc;
-        const u32x4_t v = bload16(rbm, (j < p.r && n < p.N) ? (uint32_t)((j * p.N + n) * 2) : kOOB, 0);
-        lds8_t* tile = bt + (j >> 6) * 8192 + ((j & 7) * 2);
+    // stage B^T: thread (jb, nc) of the first RP * 64 loads the 8 x 8 block of
+    // ranks 8 jb .. +7 and columns n0 + 8 nc .. +7 (16 bytes per rank row; N % 8
+    // == 0 keeps them inside the row and 16-byte aligned), transposes it with 32
+    // byte permutes and writes column n's 8 ranks as one 16-byte chunk of the
+    // [n][j] tile; ranks j >= r and columns n >= N are zeros
+    if ((int)threadIdx.x < RP * 64) {
+        const int jb = (int)threadIdx.x >> 3, nc = (int)threadIdx.x & 7;
+        const int64_t nb8 = n0 + 8 * nc;
+        u32x4_t v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const uint16_t h = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-            *reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(
-                tile + lds_off(8 * nc + e, (j & 63) >> 3)) = h;
+            const int j = 8 * jb + e;
+            v[e] = bload16(rbm, (j < p.r && nb8 < p.N) ? (uint32_t)((j * p.N + nb8) * 2) : kOOB, 0);
+        }
+        lds8_t* tile = bt + (jb >> 3) * 8192;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;  // high or low halves: column 8 nc + i
+            u32x4_t o;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) o[pp] = __builtin_amdgcn_perm(v[2 * pp + 1][i >> 1], v[2 * pp][i >> 1], sel);
+            *reinterpret_cast<lds_u32x4_t*>(tile + lds_off(8 * nc + i, jb & 7)) = o;
         }
     }
 #pragma unroll
