@@ -412,6 +412,16 @@ def cpu_baseline(layers, T, r, s, t_sample):
             "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
 
 
+def calibration_copy(torch):
+    """Three device copies of COPY_BYTES: counter runs scale their byte counts by
+    what the same counters read for this copy of known size."""
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    c = torch.empty_like(a)
+    for _ in range(3):
+        c.copy_(a)
+    torch.cuda.synchronize()
+
+
 def only_component(name, api, torch, synth, layers, r, s):
     """One component alone, on weights drawn on the device (for kernel traces and counter runs)."""
     if name.startswith("decode"):
@@ -463,6 +473,7 @@ def main():
     layers, T, r, s = cfg["layers"], cfg["T"], cfg["r"], cfg["scaling"]
 
     if args.only:
+        calibration_copy(torch)
         print(json.dumps({"component": args.only, **only_component(args.only, api, torch, synth, layers, r, s)}),
               flush=True)
         return
@@ -487,10 +498,7 @@ def main():
     torch.cuda.synchronize()
 
     if args.roofline_only:
-        a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
-        c = torch.empty_like(a)
-        for _ in range(3):
-            c.copy_(a)
+        calibration_copy(torch)
         flops, secs = measure_roofline_kernel(api, torch, layers, bufs, args.steps)
         print(json.dumps({"roofline_kernel": "k_fwd", "tflops": flops / secs / 1e12, "us_per_launch": secs * 1e6,
                           "copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES,
