@@ -1,5 +1,5 @@
 // MFMA GEMMs of the QLoRA linear layer on gfx950, with NF4 double
-// dequantization fused into the producers of the weight operand.
+// dequantization fused into the LDS tile producers.
 //
 // Layer (Volcengine article section 3.4, equation lost; reading used):
 //   Y  = X W'^T + s (X A) B
