@@ -1,6 +1,7 @@
 // extern "C" entry points declared in include/qlora.h: host-side validation,
 // workspace carving and kernel sequencing.  No device memory is allocated
 // here; every buffer comes from the caller.
+#include <algorithm>
 #include <cmath>
 
 #include "qlora.h"
@@ -83,13 +84,27 @@ int fwd_impl(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* 
         return QLORA_ERR_ALIGN;
     if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
     const ql::LoraPlan pl(T, K, N, r);
-    const size_t need = T <= ql::kGemvMaxT ? ql::gemv_workspace(T, K, N, pl.r_pad) : pl.fwd_bytes;
+    const bool chunked = T > ql::kGemvMaxT && T <= ql::kChunkMaxT;
+    const size_t need = T <= ql::kGemvMaxT ? ql::gemv_workspace(T, K, N, pl.r_pad)
+                        : chunked      ? ql::gemv_workspace(ql::kGemvMaxT, K, N, pl.r_pad)
+                                       : pl.fwd_bytes;
     if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (T <= ql::kGemvMaxT)      // decode sizes: small-M MFMA, split-k partials
         return dev(ql::launch_gemv(x, codes, sc, lora_a, lora_b, scaling, pl, ws, y, s, f16));
+    if (chunked) {
+        // small prefill: token chunks through the decode kernels, one after the
+        // other on the stream (they share the workspace)
+        for (int64_t t0 = 0; t0 < T; t0 += ql::kGemvMaxT) {
+            const ql::LoraPlan pc(std::min<int64_t>(ql::kGemvMaxT, T - t0), K, N, r);
+            if (int st = dev(ql::launch_gemv(x + t0 * K, codes, sc, lora_a, lora_b, scaling, pc, ws, y + t0 * N, s,
+                                             f16)))
+                return st;
+        }
+        return QLORA_OK;
+    }
     if (r > 0) {
         if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
         // s X A in both layouts: the transposed copy lets a backward with
@@ -117,8 +132,8 @@ int bwd_impl(const uint16_t* dy, int64_t T, int64_t K, int64_t N, const uint8_t*
     if (flags & ~(unsigned)QLORA_BWD_REUSE_FORWARD) return QLORA_ERR_VALUE;
     const ql::LoraPlan pl(T, K, N, r);
     const size_t need = grads ? pl.bwd_grad_bytes : pl.bwd_bytes;   // > 0: the scale pre-pass needs room
-    // s X A from the forward's workspace (only the MFMA forward, T > 16, leaves it there)
-    const bool reuse = (flags & QLORA_BWD_REUSE_FORWARD) && T > ql::kGemvMaxT;
+    // s X A from the forward's workspace (only the MFMA forward, T > kChunkMaxT, leaves it there)
+    const bool reuse = (flags & QLORA_BWD_REUSE_FORWARD) && T > ql::kChunkMaxT;
     if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -266,8 +281,8 @@ size_t qlora_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r) {
     if (check_linear_shape(T, K, N, r) != QLORA_OK) return 0;
     const ql::LoraPlan pl(T, K, N, r);
     size_t n = pl.bwd_grad_bytes;
-    if (T <= ql::kGemvMaxT) {
-        const size_t g = ql::gemv_workspace(T, K, N, pl.r_pad);
+    if (T <= ql::kChunkMaxT) {
+        const size_t g = ql::gemv_workspace(std::min<int64_t>(T, ql::kGemvMaxT), K, N, pl.r_pad);
         if (g > n) n = g;
     }
     return n;

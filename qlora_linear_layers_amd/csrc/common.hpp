@@ -294,6 +294,10 @@ hipError_t launch_dequantize(const uint8_t* codes, BlockScales sc, int64_t numel
 
 // Forward calls with at most this many tokens take the decode (small-M MFMA) path.
 constexpr int64_t kGemvMaxT = 16;
+// Forward sizes T (kGemvMaxT < T <= kChunkMaxT) that run as kGemvMaxT-token
+// chunks through the decode kernels: each chunk streams the weight once, which
+// beats one pass of 256-token MFMA tiles that leave most CUs idle.
+constexpr int64_t kChunkMaxT = 96;
 struct LoraPlan;
 size_t gemv_workspace(int64_t T, int64_t K, int64_t N, int64_t r_pad);
 hipError_t launch_merge(const uint8_t* codes, BlockScales sc, const uint16_t* lora_a, const uint16_t* lora_b,

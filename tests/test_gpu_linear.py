@@ -71,6 +71,14 @@ def test_short_token_tile():
     _run_full("T=40", synth.Linear("t", 320, 448), T=40, r=8, s=1.5)
 
 
+@pytest.mark.parametrize("T", [17, 33, 95, 96, 97])
+def test_chunked_small_prefill(T):
+    """16 < T <= 96 runs 16-token chunks through the decode kernels (a ragged
+    last chunk for 17, 33 and 95); T = 97 takes the 256-token MFMA tiles.
+    Forward and backward against the oracle."""
+    _run_full(f"T={T}", synth.Linear("t", 320, 448), T=T, r=24, s=0.75)
+
+
 def test_decode_rank_256():
     _run_full("decode r=256", synth.Linear("t", 256, 320), T=5, r=256, s=0.25, check_bwd=False)
 
@@ -158,11 +166,14 @@ def test_determinism():
         assert np.array_equal(u, v)
 
 
-def test_backward_reuses_forward_state():
+@pytest.mark.parametrize("T", [333, 64])
+def test_backward_reuses_forward_state(T):
     """QLORA_BWD_REUSE_FORWARD: the backward takes s X A from the forward's
-    workspace; dX, dA and dB are bit-identical to the backward that recomputes it."""
+    workspace; dX, dA and dB are bit-identical to the backward that recomputes it.
+    At T = 64 the forward runs 16-token decode chunks, which keep no s X A, and
+    the flag must be ignored."""
     lin = synth.Linear("t", 640, 448)
-    T, r, s = 333, 24, 0.5
+    r, s = 24, 0.5
     d = _inputs(9, lin, T, r)
     qw = api.nf4_quantize_dq(to_dev(d["w"], (lin.N, lin.K)))
     x, a, b = to_dev(d["x"], (T, lin.K)), to_dev(d["a"], (lin.K, r)), to_dev(d["b"], (r, lin.N))
