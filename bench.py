@@ -165,6 +165,37 @@ def merge_bytes(lin, r):
     return storage_bytes(lin.N * lin.K) + 2 * lin.N * lin.K + 2 * r * (lin.K + lin.N)
 
 
+def measure_prefill(api, torch, layers, sets, r, s, tokens=(32, 64), reps=6):
+    """Small-prefill forward (16 < T <= 96 runs 16-token chunks through the decode
+    kernels) over the seven linears, one weight copy per pass.
+    Returns {T: (seconds per layer set, bytes per layer set, flops per layer set)}."""
+    copies = len(sets)
+    out = {}
+    for T in tokens:
+        g = torch.Generator(device="cuda").manual_seed(100 + T)
+        xs = [torch.randn((T, l.K), generator=g, device="cuda").to(torch.bfloat16) for l in layers]
+        a = [torch.randn((l.K, r), generator=g, device="cuda").mul_(0.01).to(torch.bfloat16) for l in layers]
+        b = [torch.randn((r, l.N), generator=g, device="cuda").mul_(0.01).to(torch.bfloat16) for l in layers]
+        ws = [torch.empty(api.qlora_workspace_bytes(T, l.K, l.N, r), dtype=torch.uint8, device="cuda") for l in layers]
+        ys = [torch.empty((T, l.N), dtype=torch.bfloat16, device="cuda") for l in layers]
+
+        def one(c):
+            for i in range(len(layers)):
+                api.qlora_linear_fwd(xs[i], sets[c][i], a[i], b[i], s, workspace=ws[i], out=ys[i])
+        for c in range(copies):
+            one(c)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for k in range(reps):
+            one(k % copies)
+        ev[1].record()
+        torch.cuda.synchronize()
+        out[T] = (ev[0].elapsed_time(ev[1]) / 1e3 / reps, sum(decode_bytes(l, T, r) for l in layers),
+                  sum(2 * T * l.N * l.K + 2 * T * r * (l.K + l.N) for l in layers))
+    return out
+
+
 def measure_merge(api, torch, layers, sets, r, s, reps=6):
     """W_m = RNE_bf16(W' + s (A B)^T) for the seven linears, one weight copy per pass
     (the 405 MB of outputs are written once per pass).  Returns (seconds, bytes) per layer set."""
@@ -630,6 +661,12 @@ def main():
         comp["merge"] = {"GB/s": round(nbytes / secs / 1e9, 1), "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
                          "us_per_layer_set": round(1e6 * secs, 2),
                          "note": "7 linears, W_m = RNE_bf16(W' + s (A B)^T), r=64; weights rotated over 6 copies"}
+        for Tp, (secs, nbytes, flops) in measure_prefill(api, torch, layers, sets, r, s).items():
+            comp[f"prefill_T{Tp}"] = {"TFLOP/s": round(flops / secs / 1e12, 1), "GB/s": round(nbytes / secs / 1e9, 1),
+                                      "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
+                                      "us_per_layer_set": round(1e6 * secs, 2),
+                                      "note": "7 linears, r=64, forward at a small-prefill T: 16-token chunks through "
+                                              "the decode kernels; weights rotated over 6 copies"}
         del sets
         for name, (kind, secs, amt) in measure_65b(api, torch, synth).items():
             key = name + "_65b"
