@@ -166,8 +166,8 @@ def merge_bytes(lin, r):
 
 
 def measure_prefill(api, torch, layers, sets, r, s, tokens=(32, 64), reps=6):
-    """Small-prefill forward (16 < T <= 96 runs 16-token chunks through the decode
-    kernels) over the seven linears, one weight copy per pass.
+    """Small-prefill forward (16 < T <= 128 runs 16-token windows as one grouped
+    decode launch) over the seven linears, one weight copy per pass.
     Returns {T: (seconds per layer set, bytes per layer set, flops per layer set)}."""
     copies = len(sets)
     out = {}
@@ -665,8 +665,8 @@ def main():
             comp[f"prefill_T{Tp}"] = {"TFLOP/s": round(flops / secs / 1e12, 1), "GB/s": round(nbytes / secs / 1e9, 1),
                                       "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
                                       "us_per_layer_set": round(1e6 * secs, 2),
-                                      "note": "7 linears, r=64, forward at a small-prefill T: 16-token chunks through "
-                                              "the decode kernels; weights rotated over 6 copies"}
+                                      "note": "7 linears, r=64, forward at a small-prefill T: 16-token windows as one "
+                                              "grouped decode launch pair; weights rotated over 6 copies"}
         del sets
         for name, (kind, secs, amt) in measure_65b(api, torch, synth).items():
             key = name + "_65b"

@@ -158,8 +158,8 @@ size_t qlora_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r);
  *   workspace: device scratch of at least qlora_workspace_bytes(T, K, N, r)
  *   bytes (may be NULL if that is 0); its contents on entry do not matter.
  *   Kernels by size: T <= 16 runs the decode kernels (small-M MFMA, weight
- *   stream read once); 16 < T <= 96 runs them on 16-token chunks, one after
- *   the other on the stream; larger T runs the 256 x 256-tile MFMA GEMM.
+ *   stream read once); 16 < T <= 128 runs them on 16-token windows as one
+ *   grouped launch; larger T runs the 256 x 256-tile MFMA GEMM.
  *   Errors: NULL, SHAPE, ALIGN, VALUE (non-finite scaling), WORKSPACE, DEVICE.
  */
 int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N,
@@ -184,7 +184,7 @@ int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N,
  *   flags: 0, or QLORA_BWD_REUSE_FORWARD when `workspace` still holds what a
  *   qlora_linear_fwd with the same x, lora_a, scaling and sizes left there
  *   (nothing else used it since): s X A is then taken from it instead of
- *   being recomputed for dB.  Ignored for T <= 96 (the decode-kernel
+ *   being recomputed for dB.  Ignored for T <= 128 (the decode-kernel
  *   forward keeps nothing).  With a stale workspace the flag gives wrong dB.
  *   Errors: NULL, SHAPE, ALIGN, VALUE (non-finite scaling, unknown flag),
  *   WORKSPACE, DEVICE.

@@ -36,6 +36,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int dev(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_DEVICE; }
 
+// Workspace of a chunked forward (kGemvMaxT < T <= kChunkMaxT): one decode
+// workspace per kGemvMaxT-token window of the grouped launch.
+static_assert(ql::kChunkMaxT / ql::kGemvMaxT <= ql::kMaxGroup, "the windows fit one grouped launch");
+size_t chunked_workspace(int64_t T, int64_t K, int64_t N, int64_t r_pad) {
+    const int64_t windows = (T + ql::kGemvMaxT - 1) / ql::kGemvMaxT;
+    return (size_t)windows * ql::gemv_workspace(ql::kGemvMaxT, K, N, r_pad);
+}
+
 // Shape rules shared by the linear entry points.  The GEMM kernels address
 // each operand with 32-bit buffer offsets, so every operand stays below 2 GiB.
 int check_linear_shape(int64_t T, int64_t K, int64_t N, int64_t r) {
@@ -86,7 +94,7 @@ int fwd_impl(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* 
     const ql::LoraPlan pl(T, K, N, r);
     const bool chunked = T > ql::kGemvMaxT && T <= ql::kChunkMaxT;
     const size_t need = T <= ql::kGemvMaxT ? ql::gemv_workspace(T, K, N, pl.r_pad)
-                        : chunked      ? ql::gemv_workspace(ql::kGemvMaxT, K, N, pl.r_pad)
+                        : chunked      ? chunked_workspace(T, K, N, pl.r_pad)
                                        : pl.fwd_bytes;
     if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
 
@@ -95,15 +103,18 @@ int fwd_impl(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* 
     if (T <= ql::kGemvMaxT)      // decode sizes: small-M MFMA, split-k partials
         return dev(ql::launch_gemv(x, codes, sc, lora_a, lora_b, scaling, pl, ws, y, s, f16));
     if (chunked) {
-        // small prefill: token chunks through the decode kernels, one after the
-        // other on the stream (they share the workspace)
-        for (int64_t t0 = 0; t0 < T; t0 += ql::kGemvMaxT) {
-            const ql::LoraPlan pc(std::min<int64_t>(ql::kGemvMaxT, T - t0), K, N, r);
-            if (int st = dev(ql::launch_gemv(x + t0 * K, codes, sc, lora_a, lora_b, scaling, pc, ws, y + t0 * N, s,
-                                             f16)))
-                return st;
+        // small prefill: kGemvMaxT-token windows as the problems of one grouped
+        // decode launch pair (they share the weight).  Window c starts at token
+        // min(16 c, T - 16), so every window is full; the last one overlaps its
+        // predecessor, computes those rows identically and skips writing them.
+        const int64_t windows = (T + ql::kGemvMaxT - 1) / ql::kGemvMaxT;
+        ql::GemvProblem g[ql::kMaxGroup];
+        for (int64_t c = 0; c < windows; ++c) {
+            const int64_t t0 = std::min<int64_t>(c * ql::kGemvMaxT, T - ql::kGemvMaxT);
+            g[c] = ql::GemvProblem{x + t0 * K, codes, sc, lora_a, lora_b, scaling, K, N, y + t0 * N,
+                                   c * ql::kGemvMaxT - t0};
         }
-        return QLORA_OK;
+        return dev(ql::launch_gemv_group(g, (int)windows, ql::kGemvMaxT, r, ws, s, f16));
     }
     if (r > 0) {
         if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
@@ -282,7 +293,7 @@ size_t qlora_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r) {
     const ql::LoraPlan pl(T, K, N, r);
     size_t n = pl.bwd_grad_bytes;
     if (T <= ql::kChunkMaxT) {
-        const size_t g = ql::gemv_workspace(std::min<int64_t>(T, ql::kGemvMaxT), K, N, pl.r_pad);
+        const size_t g = T <= ql::kGemvMaxT ? ql::gemv_workspace(T, K, N, pl.r_pad) : chunked_workspace(T, K, N, pl.r_pad);
         if (g > n) n = g;
     }
     return n;

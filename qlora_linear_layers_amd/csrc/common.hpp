@@ -295,9 +295,9 @@ hipError_t launch_dequantize(const uint8_t* codes, BlockScales sc, int64_t numel
 // Forward calls with at most this many tokens take the decode (small-M MFMA) path.
 constexpr int64_t kGemvMaxT = 16;
 // Forward sizes T (kGemvMaxT < T <= kChunkMaxT) that run as kGemvMaxT-token
-// chunks through the decode kernels: each chunk streams the weight once, which
-// beats one pass of 256-token MFMA tiles that leave most CUs idle.
-constexpr int64_t kChunkMaxT = 96;
+// windows through one grouped decode launch: each window streams the weight,
+// which beats one pass of 256-token MFMA tiles that leave most CUs idle.
+constexpr int64_t kChunkMaxT = 128;
 struct LoraPlan;
 size_t gemv_workspace(int64_t T, int64_t K, int64_t N, int64_t r_pad);
 hipError_t launch_merge(const uint8_t* codes, BlockScales sc, const uint16_t* lora_a, const uint16_t* lora_b,
@@ -318,6 +318,7 @@ struct GemvProblem {
     float scaling;
     int64_t K, N;
     uint16_t* y;
+    int64_t skip = 0;     // leading token rows computed but not written (another problem writes them)
 };
 size_t gemv_group_workspace(const GemvProblem* probs, int count, int64_t T, int64_t r_pad);
 hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int64_t r, uint8_t* ws, hipStream_t s,

@@ -49,6 +49,7 @@ struct GemvArgs {
     int64_t T, K, N, r, r_pad;
     int KS, KL, gemv_blocks;
     float scaling;
+    int skip;                 // leading token rows not written (see GemvProblem)
 };
 
 // Up to kMaxGroup independent problems (same T, same rank) in one launch.
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(256) void k_gemv_finalize(GemvGroup grp) {
     for (int i = threadIdx.x; i < T * kFinCols; i += 256) {
         const int t = i / kFinCols, l = i % kFinCols;
         const int64_t nn = (int64_t)bx * kFinCols + l;
-        if (nn < p.N) {
+        if (nn < p.N && t >= p.skip) {
             const float v = red[(0 * 16 + t) * kFinCols + l] + red[(1 * 16 + t) * kFinCols + l] +
                             red[(2 * 16 + t) * kFinCols + l] + red[(3 * 16 + t) * kFinCols + l];
             p.y[t * p.N + nn] = (uint16_t)(pack16x2<F16>(v, 0.0f) & 0xFFFFu);
@@ -402,7 +403,7 @@ hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int
         const GemvProblem& q = probs[i];
         GemvArgs& a = g.p[i];
         a = GemvArgs{q.x, q.codes, q.sc.fp8, q.sc.sup, q.sc.absmax, q.lora_a, q.lora_b, nullptr, nullptr, q.y,
-                     T, q.K, q.N, r, r_pad, gemv_ks(q.K), r ? gemv_kl(q.K) : 0, 0, q.scaling};
+                     T, q.K, q.N, r, r_pad, gemv_ks(q.K), r ? gemv_kl(q.K) : 0, 0, q.scaling, (int)q.skip};
         a.part = reinterpret_cast<float*>(ws);
         a.lpart = reinterpret_cast<float*>(ws + align256((size_t)a.KS * T * q.N * 4));
         ws += gemv_workspace(T, q.K, q.N, r_pad);

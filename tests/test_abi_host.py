@@ -118,9 +118,10 @@ def test_workspace_bytes(L):
     # path's split partials [K/512][T][N] fp32 (T <= 16, no adapter)
     assert L.qlora_workspace_bytes(16, 4096, 4096, 0) == max((4096 // 64) * 4096 * 4, (4096 // 512) * 16 * 4096 * 4)
     assert L.qlora_workspace_bytes(1, 4096, 4096, 0) == (4096 // 64) * 4096 * 4
-    # 16 < T <= 96 runs 16-token chunks through the decode kernels: one chunk's partials
-    assert L.qlora_workspace_bytes(64, 4096, 4096, 0) == max((4096 // 64) * 4096 * 4, (4096 // 512) * 16 * 4096 * 4)
-    assert L.qlora_workspace_bytes(97, 4096, 4096, 0) == (4096 // 64) * 4096 * 4
+    # 16 < T <= 128 runs 16-token windows as one grouped decode launch: one window's partials each
+    assert L.qlora_workspace_bytes(64, 4096, 4096, 0) == max((4096 // 64) * 4096 * 4, 4 * (4096 // 512) * 16 * 4096 * 4)
+    assert L.qlora_workspace_bytes(40, 4096, 4096, 0) == max((4096 // 64) * 4096 * 4, 3 * (4096 // 512) * 16 * 4096 * 4)
+    assert L.qlora_workspace_bytes(129, 4096, 4096, 0) == (4096 // 64) * 4096 * 4
     assert L.qlora_workspace_bytes(1 << 23, 4096, 4096, 16) == 0                     # T too large
     assert L.qlora_workspace_bytes(16, 100, 4096, 16) == 0
     a = L.qlora_workspace_bytes(4096, 4096, 11008, 64)

@@ -71,11 +71,12 @@ def test_short_token_tile():
     _run_full("T=40", synth.Linear("t", 320, 448), T=40, r=8, s=1.5)
 
 
-@pytest.mark.parametrize("T", [17, 33, 95, 96, 97])
+@pytest.mark.parametrize("T", [17, 33, 95, 127, 128, 129])
 def test_chunked_small_prefill(T):
-    """16 < T <= 96 runs 16-token chunks through the decode kernels (a ragged
-    last chunk for 17, 33 and 95); T = 97 takes the 256-token MFMA tiles.
-    Forward and backward against the oracle."""
+    """16 < T <= 128 runs 16-token windows as one grouped decode launch (the last
+    window overlaps its predecessor for 17, 33, 95 and 127 and writes only its
+    new rows); T = 129 takes the 256-token MFMA tiles.  Forward and backward
+    against the oracle."""
     _run_full(f"T={T}", synth.Linear("t", 320, 448), T=T, r=24, s=0.75)
 
 
