@@ -26,8 +26,11 @@
  *     on it and the call returns before it completes; a device fault surfaces
  *     at the caller's next synchronisation.
  *   - Every call validates its arguments on the host BEFORE launching anything:
- *     on a non-zero status nothing has been launched and no output was touched.
- *     Functions never throw across the ABI.
+ *     on a status other than QLORA_ERR_DEVICE nothing has been launched and no
+ *     output was touched.  QLORA_ERR_DEVICE means the HIP runtime refused a
+ *     launch; kernels the same call enqueued before that one may still run, so
+ *     its outputs and workspace are then unspecified.  Functions never throw
+ *     across the ABI.
  *   - Blocks are 64 consecutive elements of the flattened weight, groups are 256
  *     consecutive blocks (the last group may be partial).  Both are fixed.
  *   - Inputs must be finite; the result for non-finite inputs is unspecified.
@@ -139,9 +142,21 @@ int nf4_dequantize_dq_grouped(int count, const nf4_tensor* tensors, void* stream
 /*
  * qlora_workspace_bytes - device workspace (bytes) that qlora_linear_fwd and
  *   qlora_linear_bwd_input need for these sizes (the larger of the two).
- *   Returns 0 for sizes the entry points would reject.
+ *   Returns 0 for sizes the entry points would reject.  The size is not
+ *   monotone in T: 16 < T <= 128 keeps one set of split partials per 16-token
+ *   window and can need more than a larger T (for example about 46 MB at
+ *   T = 128 against about 21 MB at T = 4096 on an 11008 x 4096 weight with
+ *   r = 64), so a caller that sizes one workspace for a range of T takes the
+ *   maximum over that range (qlora_workspace_bytes_upto).
  */
 size_t qlora_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r);
+
+/*
+ * qlora_workspace_bytes_upto - the largest qlora_workspace_bytes(T, K, N, r)
+ *   over 1 <= T <= T_max: one workspace of this size serves every call with
+ *   up to T_max tokens.  Returns 0 for sizes the entry points would reject.
+ */
+size_t qlora_workspace_bytes_upto(int64_t T_max, int64_t K, int64_t N, int64_t r);
 
 /*
  * qlora_linear_fwd - fused forward of one QLoRA linear layer.

@@ -21,6 +21,7 @@ _SIGS = {
     "nf4_quantize_dq": (ctypes.c_int, [_c_p, _c_i64, _c_p, _c_p, _c_p, _c_p]),
     "nf4_dequantize_dq": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_p, _c_p]),
     "qlora_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64]),
+    "qlora_workspace_bytes_upto": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64]),
     "qlora_linear_fwd": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                         ctypes.c_float, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "qlora_linear_bwd_input": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
@@ -136,6 +137,40 @@ def _entry(stem, ct, qw):
     return stem + ct
 
 
+def _shape(t, shape, name):
+    """Raise ValueError unless tensor `t` (if given) has exactly `shape`."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_storage(qw):
+    """The storage tensors of a quantized weight must hold exactly what its (N, K) needs:
+    the C ABI trusts the sizes, so a mismatch would read past an allocation."""
+    n = qw.N * qw.K
+    if qw.N < 1 or qw.K < 1 or n % 64:
+        raise ValueError(f"quantized weight [{qw.N}, {qw.K}]: N*K must be a positive multiple of 64")
+    _shape(qw.codes.reshape(-1), (n // 2,), "codes")
+    if isinstance(qw, NF4WeightSQ):
+        _shape(qw.absmax.reshape(-1), (n // 64,), "absmax")
+    else:
+        _shape(qw.absmax_fp8.reshape(-1), (n // 64,), "absmax_fp8")
+        _shape(qw.superscale.reshape(-1), (-(-n // 16384),), "superscale")
+
+
+def _check_adapters(lora_a, lora_b, K, N):
+    """Rank of the adapter pair A [K, r], B [r, N] (0 without an adapter)."""
+    if (lora_a is None) != (lora_b is None):
+        raise ValueError("lora_a and lora_b are given together or not at all")
+    if lora_a is None:
+        return 0
+    if lora_a.dim() != 2:
+        raise ValueError(f"lora_a must be 2-D [K, r], got shape {tuple(lora_a.shape)}")
+    r = lora_a.shape[1]
+    _shape(lora_a, (K, r), "lora_a")
+    _shape(lora_b, (r, N), "lora_b")
+    return r
+
+
 @dataclass
 class NF4Weight:
     """Storage triple of a quantized [N, K] weight (device tensors)."""
@@ -192,6 +227,9 @@ def nf4_quantize_dq(w):
 def nf4_quantize_dq_into(w, qw):
     """Quantize into an existing NF4Weight (no allocation)."""
     fn = "nf4_quantize_dq" + _ct(w, "w")
+    _check_storage(qw)
+    if w.numel() != qw.numel:
+        raise ValueError(f"w has {w.numel()} elements, the storage holds {qw.numel}")
     _dev(w, w.dtype, "w")
     _check(fn, getattr(lib(), fn)(_ptr(w), w.numel(), _ptr(qw.codes), _ptr(qw.absmax_fp8), _ptr(qw.superscale),
                                   _stream()))
@@ -199,6 +237,9 @@ def nf4_quantize_dq_into(w, qw):
 
 def nf4_dequantize_dq(qw, out=None, dtype=torch.bfloat16):
     """NF4Weight -> [N, K] on the GPU, bf16 or (dtype / out fp16) fp16."""
+    _check_storage(qw)
+    if out is not None and out.numel() != qw.numel:
+        raise ValueError(f"out has {out.numel()} elements, the weight has {qw.numel}")
     if out is None:
         out = torch.empty((qw.N, qw.K), dtype=dtype, device=qw.codes.device)
     fn = "nf4_dequantize_dq" + _ct(out, "out")
@@ -215,10 +256,12 @@ def _tensor_array(ws, qws):
     if len(ws) != len(qws):
         raise ValueError("one storage triple per weight")
     arr = (NF4Tensor * len(ws))()
-    for i, (w, qw) in enumerate(zip(ws, qws)):
-        _dev(w, torch.bfloat16, "w")
+    for i, (w, qw) in enumerate(zip(ws, qws)):   # every size first, then the device checks
+        _check_storage(qw)
         if w.numel() != qw.numel:
             raise ValueError(f"tensor {i}: {w.numel()} elements, storage for {qw.numel}")
+    for i, (w, qw) in enumerate(zip(ws, qws)):
+        _dev(w, torch.bfloat16, "w")
         arr[i] = NF4Tensor(w.data_ptr(), w.numel(), qw.codes.data_ptr(), qw.absmax_fp8.data_ptr(),
                            qw.superscale.data_ptr())
     return arr
@@ -260,6 +303,9 @@ def nf4_quantize(w):
 
 def nf4_dequantize(qw, out=None):
     """NF4WeightSQ -> bf16 [N, K] on the GPU."""
+    _check_storage(qw)
+    if out is not None and out.numel() != qw.numel:
+        raise ValueError(f"out has {out.numel()} elements, the weight has {qw.numel}")
     if out is None:
         out = torch.empty((qw.N, qw.K), dtype=torch.bfloat16, device=qw.codes.device)
     _dev(out, torch.bfloat16, "out")
@@ -279,6 +325,9 @@ def int4_quantize(w):
 
 
 def int4_dequantize(qw, out=None):
+    _check_storage(qw)
+    if out is not None and out.numel() != qw.numel:
+        raise ValueError(f"out has {out.numel()} elements, the weight has {qw.numel}")
     if out is None:
         out = torch.empty((qw.N, qw.K), dtype=torch.bfloat16, device=qw.codes.device)
     _dev(out, torch.bfloat16, "out")
@@ -298,6 +347,11 @@ def qlora_workspace_bytes(T, K, N, r):
     return int(lib().qlora_workspace_bytes(T, K, N, r))
 
 
+def qlora_workspace_bytes_upto(T_max, K, N, r):
+    """Workspace bytes that serve every call with 1 <= T <= T_max tokens."""
+    return int(lib().qlora_workspace_bytes_upto(T_max, K, N, r))
+
+
 def workspace_for(T, K, N, r, device):
     n = qlora_workspace_bytes(T, K, N, r)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
@@ -307,11 +361,16 @@ def qlora_linear_fwd(x, qw, lora_a=None, lora_b=None, scaling=1.0, workspace=Non
     """Y = X W'^T + scaling (X A) B; x [T, K] -> y [T, N], bf16 or fp16 (the _f16 entry point).
     `qw` is an NF4Weight (double quantization) or an NF4WeightSQ (single quantization, _sq)."""
     ct = _ct(x, "x")
+    _check_storage(qw)
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D [T, K], got shape {tuple(x.shape)}")
+    T, K = x.shape
+    _shape(x, (T, qw.K), "x")
+    r = _check_adapters(lora_a, lora_b, qw.K, qw.N)
+    _shape(out, (T, qw.N), "out")
     _dev(x, x.dtype, "x")
     _dev(lora_a, x.dtype, "lora_a")
     _dev(lora_b, x.dtype, "lora_b")
-    T, K = x.shape
-    r = 0 if lora_a is None else lora_a.shape[1]
     if out is None:
         out = torch.empty((T, qw.N), dtype=x.dtype, device=x.device)
     if workspace is None:
@@ -331,17 +390,20 @@ GROUPED_MAX_T = 16       # QLORA_GROUPED_MAX_T
 
 def _grouped_array(problems, T, r):
     arr = (LinearProblem * len(problems))()
-    for i, pr in enumerate(problems):
+    for i, pr in enumerate(problems):          # every shape first, then the device checks
         x, qw, a, b, scaling, y = pr
         if isinstance(qw, NF4WeightSQ):
             raise TypeError("the grouped forward takes double-quantized weights (NF4Weight)")
-        for t, name in ((x, "x"), (a, "lora_a"), (b, "lora_b"), (y, "out")):
-            _dev(t, torch.bfloat16, name)
+        _check_storage(qw)
         if tuple(x.shape) != (T, qw.K) or tuple(y.shape) != (T, qw.N):
             raise ValueError(f"problem {i}: x {tuple(x.shape)} / out {tuple(y.shape)} do not match T={T}, "
                              f"K={qw.K}, N={qw.N}")
-        if (0 if a is None else a.shape[1]) != r:
+        if _check_adapters(a, b, qw.K, qw.N) != r:
             raise ValueError(f"problem {i}: every problem of a group has the same rank")
+    for i, pr in enumerate(problems):
+        x, qw, a, b, scaling, y = pr
+        for t, name in ((x, "x"), (a, "lora_a"), (b, "lora_b"), (y, "out")):
+            _dev(t, torch.bfloat16, name)
         arr[i] = LinearProblem(x.data_ptr(), qw.codes.data_ptr(), qw.absmax_fp8.data_ptr(), qw.superscale.data_ptr(),
                                None if a is None else a.data_ptr(), None if b is None else b.data_ptr(),
                                y.data_ptr(), qw.K, qw.N, float(scaling))
@@ -381,13 +443,25 @@ def qlora_linear_bwd_input(dy, qw, lora_a=None, lora_b=None, scaling=1.0, x=None
     if reuse_forward and workspace is None:
         raise ValueError("reuse_forward needs the forward's workspace")
     ct = _ct(dy, "dy")
+    _check_storage(qw)
+    if dy.dim() != 2:
+        raise ValueError(f"dy must be 2-D [T, N], got shape {tuple(dy.shape)}")
+    T, N, K = dy.shape[0], qw.N, qw.K
+    _shape(dy, (T, N), "dy")
+    r = _check_adapters(lora_a, lora_b, K, N)
+    if lora_grads and r == 0:
+        raise ValueError("lora_grads needs the adapters")
+    if lora_grads and x is None:
+        raise ValueError("lora_grads needs x")
+    _shape(x, (T, K), "x")
+    _shape(dx, (T, K), "dx")
+    if lora_grads:
+        _shape(d_lora_a, (K, r), "d_lora_a")
+        _shape(d_lora_b, (r, N), "d_lora_b")
     _dev(dy, dy.dtype, "dy")
     _dev(x, dy.dtype, "x")
     _dev(lora_a, dy.dtype, "lora_a")
     _dev(lora_b, dy.dtype, "lora_b")
-    T, N = dy.shape
-    K = qw.K
-    r = 0 if lora_a is None else lora_a.shape[1]
     if dx is None:
         dx = torch.empty((T, K), dtype=dy.dtype, device=dy.device)
     if lora_grads:
@@ -395,6 +469,10 @@ def qlora_linear_bwd_input(dy, qw, lora_a=None, lora_b=None, scaling=1.0, x=None
             d_lora_a = torch.empty((K, r), dtype=dy.dtype, device=dy.device)
         if d_lora_b is None:
             d_lora_b = torch.empty((r, N), dtype=dy.dtype, device=dy.device)
+    _dev(dx, dy.dtype, "dx")
+    if lora_grads:
+        _dev(d_lora_a, dy.dtype, "d_lora_a")
+        _dev(d_lora_b, dy.dtype, "d_lora_b")
     if workspace is None:
         workspace = workspace_for(T, K, N, r, dy.device)
     sc = _scale_args(qw)[1]
@@ -411,9 +489,11 @@ def qlora_merge_lora(qw, lora_a=None, lora_b=None, scaling=1.0, out=None, dtype=
     """W_m = RNE_16(W' + scaling (A B)^T) -> [N, K] (W' itself without an adapter), in the
     dtype of the adapters (else of `out`, else `dtype`, else bf16)."""
     dt = lora_a.dtype if lora_a is not None else (out.dtype if out is not None else (dtype or torch.bfloat16))
+    _check_storage(qw)
+    r = _check_adapters(lora_a, lora_b, qw.K, qw.N)
+    _shape(out, (qw.N, qw.K), "out")
     _dev(lora_a, dt, "lora_a")
     _dev(lora_b, dt, "lora_b")
-    r = 0 if lora_a is None else lora_a.shape[1]
     if out is None:
         out = torch.empty((qw.N, qw.K), dtype=dt, device=qw.codes.device)
     _dev(out, dt, "out")

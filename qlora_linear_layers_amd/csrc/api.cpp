@@ -299,6 +299,18 @@ size_t qlora_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r) {
     return n;
 }
 
+size_t qlora_workspace_bytes_upto(int64_t T_max, int64_t K, int64_t N, int64_t r) {
+    if (check_linear_shape(T_max, K, N, r) != QLORA_OK) return 0;
+    // below T_max the size peaks somewhere in the decode and window range
+    // (T <= kChunkMaxT); above it the MFMA-path size grows with T
+    size_t n = qlora_workspace_bytes(T_max, K, N, r);
+    for (int64_t T = 1; T <= std::min<int64_t>(T_max, ql::kChunkMaxT); ++T) {
+        const size_t m = qlora_workspace_bytes(T, K, N, r);
+        if (m > n) n = m;
+    }
+    return n;
+}
+
 int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* codes,
                      const uint8_t* absmax_fp8, const float* superscale, const uint16_t* lora_a,
                      const uint16_t* lora_b, int64_t r, float scaling, uint16_t* y, void* workspace,

@@ -30,11 +30,6 @@
 
 namespace ql {
 
-namespace {
-
-
-}  // namespace
-
 struct GemvArgs {
     const uint16_t* x;        // [T][K]
     const uint8_t* codes;

@@ -47,6 +47,17 @@ def test_codebook_bit_exact(L):
     assert L.nf4_build_codebook(None) == NULL
 
 
+def test_workspace_upto_covers_every_token_count(L):
+    """qlora_workspace_bytes is not monotone in T (16 < T <= 128 keeps one set of
+    split partials per 16-token window); the _upto size is the maximum over T."""
+    for K, N, r in ((4096, 11008, 64), (11008, 4096, 64), (448, 320, 24), (256, 256, 0)):
+        sizes = [L.qlora_workspace_bytes(T, K, N, r) for T in range(1, 301)]
+        for T_max in (1, 16, 17, 100, 128, 129, 300):
+            assert L.qlora_workspace_bytes_upto(T_max, K, N, r) == max(sizes[:T_max])
+    assert L.qlora_workspace_bytes(128, 4096, 11008, 64) > L.qlora_workspace_bytes(4096, 4096, 11008, 64)
+    assert L.qlora_workspace_bytes_upto(0, 4096, 4096, 64) == 0
+
+
 def test_status_strings(L):
     for s in range(7):
         assert L.qlora_status_string(s)

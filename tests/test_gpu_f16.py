@@ -84,6 +84,8 @@ def test_linear_prefill_shapes():
     _linear("multi-tile", synth.Linear("t", 768, 1024), T=520, r=64, s=0.25)
     _linear("r=0", synth.Linear("t", 512, 256), T=64, r=0, s=0.0)
     _linear("r=136", synth.Linear("t", 384, 448), T=100, r=136, s=0.75)
+    _linear("r=136 T=300", synth.Linear("t", 384, 448), T=300, r=136, s=0.75)
+    _linear("r=256 T=129", synth.Linear("t", 384, 448), T=129, r=256, s=0.75)
 
 
 def test_linear_decode_shapes():

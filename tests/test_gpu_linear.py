@@ -51,11 +51,14 @@ def test_multi_tile_rank64():
     _run_full("multi-tile", synth.Linear("t", 768, 1024), T=520, r=64, s=0.25)
 
 
-@pytest.mark.parametrize("r", [72, 136, 256])
-def test_ranks_above_64(r):
+@pytest.mark.parametrize("T,r", [(300, 72), (300, 136), (300, 256), (129, 136), (100, 136)])
+def test_ranks_above_64(T, r):
     """Padded ranks (r_pad = 128, 192, 256): the wide down-projection variants,
-    several 64-rank groups in the adapter gradients, zero rank padding."""
-    _run_full(f"r={r}", synth.Linear("t", 384, 448), T=100, r=r, s=0.75)
+    the forward GEMM's LoRA reduction over several 64-rank groups, several
+    64-rank groups in the adapter gradients, zero rank padding.  T = 300 and
+    the boundary T = 129 run the 256-token MFMA tiles; T = 100 the 16-token
+    decode windows."""
+    _run_full(f"T={T} r={r}", synth.Linear("t", 384, 448), T=T, r=r, s=0.75)
 
 
 @pytest.mark.parametrize("N,K,T,r", [(192, 320, 1000, 24), (128, 64, 512, 0), (448, 448, 1536, 64), (320, 576, 700, 8)])
@@ -118,8 +121,19 @@ def test_one_hot_rows_give_columns():
     assert np.array_equal(bits_of(dx), wd)
 
 
-def _sampled(cfg, lin, T, r, s, nsamp=192):
-    say(f"[linear sampled] config {cfg} {lin.name}: T={T} N={lin.N} K={lin.K} r={r}")
+def _tile_rows(T, rng, per_tile=2):
+    """`per_tile` random token rows from every 256-token tile (and the last row):
+    a full output row crosses every column tile, so these rows put at least one
+    compared element in every output tile of the grid."""
+    rows = [int(t) for t0 in range(0, T, 256) for t in rng.integers(t0, min(t0 + 256, T), per_tile)]
+    return np.unique(np.array(rows + [T - 1]))
+
+
+def _sampled(cfg, lin, T, r, s, nsamp=192, full=False):
+    """Forward and backward at a full-size shape: Y and dX compared on whole rows
+    (per_tile rows of every 256-token tile, see _tile_rows) plus `nsamp` random
+    single outputs, or in full with `full`; dA and dB always in full."""
+    say(f"[linear {'full' if full else 'sampled'}] config {cfg} {lin.name}: T={T} N={lin.N} K={lin.K} r={r}")
     d = _inputs(cfg, lin, T, r)
     qw = api.nf4_quantize_dq(to_dev(d["w"], (lin.N, lin.K)))
     rc, rf, rs = oracle.quantize_nf4_dq(d["w"])
@@ -128,15 +142,26 @@ def _sampled(cfg, lin, T, r, s, nsamp=192):
     y = bits_of(api.qlora_linear_fwd(x, qw, a, b, s))
     dx, da, db = api.qlora_linear_bwd_input(dy, qw, a, b, s, x=x, lora_grads=True)
     dx, da, db = bits_of(dx), bits_of(da), bits_of(db)
+    wd = oracle.dequantize_nf4_dq(rc, rf, rs).reshape(lin.N, lin.K)
+    if full:
+        assert_gemm_close(y, oracle.linear_fwd(d["x"], wd, d["a"], d["b"], s), "Y (full)")
+        rdx, rda, rdb = oracle.linear_bwd(d["dy"], d["x"], wd, d["a"], d["b"], s)
+        assert_gemm_close(dx, rdx, "dX (full)")
+        assert_gemm_close(da, rda, "dA (full)")
+        assert_gemm_close(db, rdb, "dB (full)")
+        return
     rng = np.random.default_rng(cfg * 100 + lin.N)
+    rows = _tile_rows(T, rng)
+    assert_gemm_close(y[rows], oracle.linear_fwd(d["x"][rows], wd, d["a"], d["b"], s), f"Y rows ({len(rows)})")
+    rdx_rows = oracle.linear_bwd(d["dy"][rows], None, wd, d["a"], d["b"], s)[0]
+    assert_gemm_close(dx[rows], rdx_rows, f"dX rows ({len(rows)})")
     t = rng.integers(0, T, nsamp)
     n = rng.integers(0, lin.N, nsamp)
     k = rng.integers(0, lin.K, nsamp)
     wrows = oracle.dequantize_rows(rc, rf, rs, lin.N, lin.K, n)
     ref = oracle.linear_fwd_at(d["x"], wrows, d["a"], d["b"], s, t, n)
     assert_gemm_close(y[t, n], ref, "Y samples")
-    wfull_cols = oracle.dequantize_nf4_dq(rc, rf, rs).reshape(lin.N, lin.K)[:, k].T
-    ref = oracle.linear_bwd_dx_at(d["dy"], wfull_cols, d["a"], d["b"], s, t, k)
+    ref = oracle.linear_bwd_dx_at(d["dy"], wd[:, k].T, d["a"], d["b"], s, t, k)
     assert_gemm_close(dx[t, k], ref, "dX samples")
     rda, rdb = oracle.lora_grads(d["x"], d["dy"], d["a"], d["b"], s)
     assert_gemm_close(da, rda, "dA (full)")
@@ -148,8 +173,14 @@ def test_train_7b_shapes_sampled(idx):
     _sampled(3, synth.LLAMA7B[idx], 4096, 64, 16.0 / 64)
 
 
-@pytest.mark.parametrize("idx", [0, 6])
+def test_train_7b_q_full():
+    """The 7B q projection at T = 4096 compared in full: every Y, dX, dA and dB element."""
+    _sampled(3, synth.LLAMA7B[0], 4096, 64, 16.0 / 64, full=True)
+
+
+@pytest.mark.parametrize("idx", [0, 4, 6])
 def test_65b_shapes_sampled(idx):
+    """The 65B-shaped q (8192 x 8192), gate (22016 x 8192) and down (8192 x 22016) at T = 2048."""
     _sampled(4, synth.LLAMA65B[idx], 2048, 64, 16.0 / 64)
 
 
@@ -190,7 +221,7 @@ def test_backward_reuses_forward_state(T):
 
 @pytest.mark.parametrize("idx", [0, 4, 6])
 def test_decode_7b_shapes_full(idx):
-    """Decode-size forward (VALU GEMV path) on the 7B layer shapes, r = 64, s = 0.25,
+    """Decode-size forward (small-M MFMA path) on the 7B layer shapes, r = 64, s = 0.25,
     T = 1, 4, 8: every output against the oracle."""
     lin = synth.LLAMA7B[idx]
     d = synth.layer_inputs(2, 0, idx, lin, 8, 64)

@@ -58,8 +58,8 @@ def test_layer_and_merge_closed_forms():
     rng = np.random.default_rng(3)
     T, K, N, r = 3, 64, 5, 2
     f = lambda *sh: rng.standard_normal(sh).astype(np.float16).view(np.uint16)
-    x, w, a, b, dy = f(T, K), f(N, K), f(K, r), f(r, N), f(T, N)
-    X, W, A, B, DY = (oracle.f16_bits_to_f64(v) for v in (x, w, a, b, dy))
+    x, w, a, b = f(T, K), f(N, K), f(K, r), f(r, N)
+    X, W, A, B = (oracle.f16_bits_to_f64(v) for v in (x, w, a, b))
     s = 0.5
     # brute-force loops against the matrix forms
     y = np.array([[sum(X[t, k] * W[n, k] for k in range(K)) + s * sum(sum(X[t, k] * A[k, j] for k in range(K)) * B[j, n]
@@ -67,11 +67,96 @@ def test_layer_and_merge_closed_forms():
     assert np.array_equal(oracle.linear_fwd_f16(x, w, a, b, s), oracle.round_to_f16_bits(y))
     assert np.array_equal(oracle.linear_fwd_at_f16(x, w[[1, 4]], a, b, s, [0, 2], [1, 4]),
                           oracle.round_to_f16_bits(y[[0, 2], [1, 4]]))
-    dx, da, db = oracle.linear_bwd_f16(dy, x, w, a, b, s)
-    g = DY @ B.T
-    assert np.array_equal(dx, oracle.round_to_f16_bits(DY @ W + s * g @ A.T))
-    assert np.array_equal(da, oracle.round_to_f16_bits(s * np.einsum("tk,tj->kj", X, g)))
-    assert np.array_equal(db, oracle.round_to_f16_bits(s * np.einsum("tj,tn->jn", X @ A, DY)))
+    # the backward is pinned below (exact rational sums, adjoint identity, directional derivatives)
     wm = oracle.merge_lora_f16(w, a, b, s)
     assert np.array_equal(wm, oracle.round_to_f16_bits(W + s * np.multiply.outer(B[0], A[:, 0])
                                                        + s * np.multiply.outer(B[1], A[:, 1])))
+
+
+def _small_f16(T, K, N, r, seed, lora_std=0.01):
+    rng = np.random.default_rng(seed)
+    f = lambda sh, std: synth.to_f16_bits(rng.standard_normal(sh).astype(np.float32) * np.float32(std))
+    x, w, a, b, dy = f((T, K), 1.0), f((N, K), 0.02), f((K, r), lora_std), f((r, N), lora_std), f((T, N), 1.0)
+    p, fq, sq = oracle.quantize_nf4_dq_f16(w)
+    wd = oracle.dequantize_nf4_dq_f16(p, fq, sq).reshape(N, K)
+    return x, wd, a, b, dy
+
+
+def test_backward_brute_force_exact_sums():
+    """dX, dA, dB of the fp16 oracle against exact rational sums over the loop
+    definitions, each rounded once to fp16 (an independent computation: no BLAS,
+    no fp64 accumulation)."""
+    from fractions import Fraction
+    x, wd, a, b, dy = _small_f16(T=4, K=64, N=3, r=3, seed=11)
+    s = 0.25
+    F = lambda bits: [[Fraction(float(v)) for v in row] for row in oracle.f16_bits_to_f64(bits)]
+    X, W, A, B, D = F(x), F(wd), F(a), F(b), F(dy)
+    T, K, N, r = len(X), len(X[0]), len(W), len(B)
+    S = Fraction(s)
+    G = [[sum(D[t][n] * B[j][n] for n in range(N)) for j in range(r)] for t in range(T)]
+    XA = [[sum(X[t][k] * A[k][j] for k in range(K)) for j in range(r)] for t in range(T)]
+    dx = [[float(sum(D[t][n] * W[n][k] for n in range(N)) + S * sum(G[t][j] * A[k][j] for j in range(r)))
+           for k in range(K)] for t in range(T)]
+    da = [[float(S * sum(X[t][k] * G[t][j] for t in range(T))) for j in range(r)] for k in range(K)]
+    db = [[float(S * sum(XA[t][j] * D[t][n] for t in range(T))) for n in range(N)] for j in range(r)]
+    gdx, gda, gdb = oracle.linear_bwd_f16(dy, x, wd, a, b, s)
+    # Fraction -> float is correctly rounded, and the fp16 rounding of a double that
+    # is itself the nearest double to the exact value is the nearest fp16 unless the
+    # exact value sits within 2^-53 relative of an fp16 midpoint (none does here)
+    assert np.array_equal(gdx, oracle.round_to_f16_bits(np.array(dx)))
+    assert np.array_equal(gda, oracle.round_to_f16_bits(np.array(da)))
+    assert np.array_equal(gdb, oracle.round_to_f16_bits(np.array(db)))
+
+
+def _fwd_f64_f16(x, wd, a, b, s):
+    """The forward in fp64 from fp16 operands, by explicit loops over numpy rows
+    (the matrix algebra of the oracle's backward is what this pins)."""
+    X, W, A, B = (oracle.f16_bits_to_f64(v) for v in (x, wd, a, b))
+    T, N = X.shape[0], W.shape[0]
+    y = np.empty((T, N))
+    for t in range(T):
+        xa = np.array([np.dot(X[t], A[:, j]) for j in range(A.shape[1])])
+        for n in range(N):
+            y[t, n] = np.dot(X[t], W[n]) + float(np.float32(s)) * np.dot(xa, B[:, n])
+    return y
+
+
+def test_backward_adjoint_identity():
+    """The forward is linear in X, so its input gradient is the adjoint map:
+    <Y(X), dY> = <X, dX(dY)>.  Y is the fp64 loop forward; dX is the fp16
+    oracle's, so the identity holds up to one fp16 rounding per element.  The
+    adapters are scaled up so that the LoRA term of dX is far above that."""
+    x, wd, a, b, dy = _small_f16(T=6, K=192, N=9, r=4, seed=12, lora_std=0.25)
+    s = 2.0
+    y = _fwd_f64_f16(x, wd, a, b, s)
+    # the oracle rounds dX to fp16; compare against the rounded adjoint, and check
+    # the rounded value brackets the exact inner product within fp16 resolution
+    dx16 = oracle.f16_bits_to_f64(oracle.linear_bwd_f16(dy, x, wd, a, b, s)[0])
+    DY, X = oracle.f16_bits_to_f64(dy), oracle.f16_bits_to_f64(x)
+    lhs = float(np.sum(y * DY))
+    rhs = float(np.sum(X * dx16))
+    # |rhs - <X, dX_exact>| <= sum |X| |dX| 2^-11 (one fp16 rounding per element)
+    bound = float(np.sum(np.abs(X) * np.abs(dx16))) * 2.0 ** -11 + 1e-12
+    assert abs(lhs - rhs) <= bound
+
+
+def test_lora_grads_directional_derivative():
+    """L(A, B) = <Y, dY> is linear in A for fixed B (and in B for fixed A), so
+    L(A + U) - L(A) = <dA, U> exactly; dA, dB of the fp16 oracle must agree with
+    these directional derivatives to their fp16 rounding."""
+    x, wd, a, b, dy = _small_f16(T=5, K=128, N=6, r=3, seed=13)
+    s = 0.25
+    _, da16, db16 = oracle.linear_bwd_f16(dy, x, wd, a, b, s)
+    rng = np.random.default_rng(14)
+    DY = oracle.f16_bits_to_f64(dy)
+    l0 = np.sum(_fwd_f64_f16(x, wd, a, b, s) * DY)
+    for which, g16 in (("a", da16), ("b", db16)):
+        base = a if which == "a" else b
+        u = synth.to_f16_bits(rng.standard_normal(base.shape).astype(np.float32))
+        pert = oracle.round_to_f16_bits(oracle.f16_bits_to_f64(base) + oracle.f16_bits_to_f64(u))
+        delta = oracle.f16_bits_to_f64(pert) - oracle.f16_bits_to_f64(base)
+        args = (x, wd, pert, b, s) if which == "a" else (x, wd, a, pert, s)
+        l1 = np.sum(_fwd_f64_f16(*args) * DY)
+        g = oracle.f16_bits_to_f64(g16)
+        bound = float(np.sum(np.abs(g) * np.abs(delta))) * 2.0 ** -11 + 1e-9 * max(1.0, abs(l1))
+        assert abs((l1 - l0) - np.sum(g * delta)) <= bound, which

@@ -58,6 +58,62 @@ def test_fp32_division_equals_exact_ratio_for_all_bf16_pairs():
                 assert np.array_equal(code_fl, code_ex), (qs, dexp, sign)
 
 
+# Error of the GPU encoder's n = fl32(w * rcp(c1)) relative to w / c1: the
+# hardware reciprocal is within 1 ulp (2^-23 relative; 2^-22 taken here), the
+# product adds one rounding (2^-24).
+RCP_MUL_REL_ERR = 2.0 ** -22 + 2.0 ** -24
+
+
+def _all_bf16_ratios_le_one():
+    """Every ratio w / c1 of two bf16 values with 0 < |w| <= c1 that can reach an
+    NF4 decision midpoint, as exact (numerator, denominator) pairs.  A bf16 value
+    is s * 2^e with s in 1..255 (normal significands 128..255, subnormals
+    1..127, and every s * 2^k that fits); so every such ratio is
+    (s_w * 2^-d) / s_c with d >= 0 (a larger exponent on w is absorbed into s_w),
+    and d <= 13 reaches below half the smallest midpoint magnitude (0.0398)."""
+    sig = np.arange(1, 256, dtype=np.float64)
+    for d in range(0, 14):
+        num = (sig * 2.0 ** -d)[:, None]                  # exact
+        den = sig[None, :]
+        keep = num <= den
+        yield np.broadcast_to(num, keep.shape)[keep], np.broadcast_to(den, keep.shape)[keep]
+
+
+def test_reciprocal_encoding_margin_over_all_bf16_pairs():
+    """k_quantize encodes with n = w * rcp(c1) and compares n with the round-down
+    fp32 midpoints, instead of dividing.  That gives the exact-ratio code iff no
+    ratio of two bf16 values lies within the product's error of a midpoint:
+    enumerate every (w, c1) significand pair and exponent gap and check that the
+    smallest relative distance |w/c1 - m| / |m| to any of the 15 midpoints m
+    exceeds RCP_MUL_REL_ERR (it is about 2^-19.4)."""
+    mids = oracle.nf4_midpoints().astype(np.float64)     # exact fp64 midpoints of fp32 codewords
+    best = np.inf
+    for num, den in _all_bf16_ratios_le_one():
+        for sign in (1.0, -1.0):
+            # |s*num/den - m| / |m| = |s*num - den*m| / (den*|m|); den*m has <= 34 bits
+            # and the difference of two nearby fp64 values is exact
+            diff = np.abs(sign * num[:, None] - den[:, None] * mids[None, :])
+            rel = diff / (den[:, None] * np.abs(mids)[None, :])
+            best = min(best, float(rel.min()))
+    assert best > RCP_MUL_REL_ERR
+    assert best > 2.0 ** -20                              # the figure the kernel comment quotes (2^-19.4)
+
+
+def test_encoder_cells_hold_one_midpoint_away_from_their_edges():
+    """The encoder's lookup: cell = trunc(16 n + 16) in [0, 32], code = base[cell]
+    + (n > thr[cell]).  It is exact if (1) every 1/16-wide cell holds at most one
+    midpoint and (2) no midpoint lies within the cell computation's error
+    (n's own 2^-22 plus the fma's rounding of 16 n + 16) of a cell edge k / 16,
+    so that a value landing in the neighbouring cell has no midpoint between it
+    and the edge."""
+    mids = oracle.nf4_midpoints().astype(np.float64)
+    assert np.min(np.diff(mids)) > 1.0 / 16
+    edge_dist = np.abs(mids * 16 - np.rint(mids * 16)) / 16
+    assert np.min(edge_dist) > 2.0 ** -20
+    cells = np.floor(mids * 16 + 16).astype(int)
+    assert np.unique(cells).size == mids.size
+
+
 def test_zero_block_and_absmax_element():
     w = np.zeros(128, np.float32)
     w[64 + 5] = -0.5
