@@ -1,24 +1,29 @@
 #!/usr/bin/env python
 """Benchmark of the QLoRA frozen-base linear layer hot path on one MI355X.
 
-Workload (one "step"): the seven linears of a LLaMA-7B-shaped transformer
-layer (q/k/v/o 4096x4096, gate/up 11008x4096, down 4096x11008) at training
-shape T = 8 x 512 = 4096 tokens, LoRA rank 64, alpha 16 (s = 0.25).  The step
-runs the whole path: NF4 + double quantization of the seven bf16 weights (one
-grouped launch), their double dequantization back to bf16 (one grouped
-launch), and for each linear the fused forward Y = X W'^T + s (X A) B and the
-backward dX = dY W' + s (dY B^T) A^T with the LoRA gradients dA, dB.  Inputs are seeded synthetic tensors (W ~ N(0, 0.02),
-X, dY ~ N(0, 1), A, B ~ N(0, 0.01)), resident in HBM before timing starts.
+Headline workload (one "step"): the seven linears of a LLaMA-65B-shaped
+transformer layer (q/k/v/o 8192x8192, gate/up 22016x8192, down 8192x22016;
+809.5 M weights) at T = 2048 tokens, LoRA rank 64, s = alpha / r = 0.25.  A
+step runs NF4 + double quantization of the seven bf16 weights (one grouped
+launch), their double dequantization back to bf16 (one grouped launch), and
+for each linear the fused forward Y = X W'^T + s (X A) B and the backward
+input gradient dX = dY W' + s (dY B^T) A^T.  Inputs are seeded synthetic
+tensors drawn on the device (W ~ N(0, 0.02), X, dY ~ N(0, 1), A, B ~ N(0,
+0.01)), resident in HBM before timing starts.
 
 Output: one JSON line.  `value` is the step's attainment of the MI355X
-roofline: the sum over all phases of their roofline time (algorithmic bytes at
+roofline: the sum over its phases of their roofline time (algorithmic bytes at
 8 TB/s for quantize / dequantize, algorithmic flops at 2.5 PFLOP/s bf16 dense
 for the GEMM phases) divided by the measured step time.  Per-phase durations
-come from HIP events recorded on the stream the kernels run on.  Outside the
-step, `components` also carries the decode forward (T = 1 / 4 / 8), the LoRA
-merge, the single-quantization variant, the fp16 compute type and the
-NF4-vs-INT4 data-type ablation measured on the same seven linears, the
-65B-shaped layer and the 70B-shaped streaming quantization.
+come from HIP events recorded on the stream the kernels run on.  `roofline`
+is the fused NF4-dequant MFMA GEMM (k_fwd) at the same shapes, timed alone.
+`components` carries the other workloads measured on the same device: the
+single 4096 x 4096 layer (T = 16, r = 16), the decode forward of the 7B layer
+set (T = 1 / 4 / 8), the 7B training step (T = 4096, forward + backward with
+the LoRA gradients), the 70B-shaped streaming quantization, the LoRA merge,
+the single-quantization and fp16 variants, the NF4-vs-INT4 ablation, and the
+calibration legs (a 128-bit streaming copy, an MFMA-only loop, and torch.matmul
+on the dequantized weight as the unfused context).
 """
 import argparse
 import json
@@ -29,10 +34,10 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK = 8.0e12          # bytes/s
-MFMA_BF16_PEAK = 2.5e15    # flop/s, dense
+HBM_PEAK = 8.0e12          # bytes/s, published
+MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16, published
 GEMM_SOURCE = os.path.join(ROOT, "qlora_linear_layers_amd", "csrc", "gemm.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fwd_llama7b_T4096_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fwd_llama65b_T2048_traffic.txt")
 COPY_BYTES = 256 << 20     # calibration copy for the HBM byte counters
 
 
@@ -54,20 +59,74 @@ def stored_traffic():
     return float(kv["hbm_bytes_per_launch"])
 
 
-def measure_roofline_kernel(api, torch, layers, bufs, reps):
+def storage_bytes(numel):
+    return numel // 2 + numel // 64 + 4 * (-(-numel // 16384))
+
+
+def phase_work(lin, T, r):
+    """Algorithmic (kind, amount, bytes) of each phase of one linear: bytes for the
+    HBM phases, flops for the GEMM phases (with the algorithmic bytes they move,
+    for the arithmetic intensity).  The backward with the LoRA gradients takes
+    s X A from the forward (saved activation), so it has no X A recompute."""
+    N, K = lin.N, lin.K
+    nk = N * K
+    st = storage_bytes(nk)
+    ad = 2 * r * (K + N)
+    return {
+        "quantize": ("hbm", 2 * nk + st, 2 * nk + st),
+        "dequantize": ("hbm", st + 2 * nk, st + 2 * nk),
+        "forward": ("mfma", 2 * T * N * K + 2 * T * K * r + 2 * T * r * N, st + 2 * T * K + 2 * T * N + ad),
+        # dX = dY W' + (s dY B^T) A^T
+        "backward_input": ("mfma", 2 * T * N * K + 2 * T * N * r + 2 * T * r * K, st + 2 * T * N + 2 * T * K + ad),
+        # dX as above, dA = X^T G and dB = P^T dY (P = s X A saved by the forward)
+        "backward": ("mfma", 2 * T * N * K + 2 * T * N * r + 2 * T * r * K + 2 * T * K * r + 2 * T * r * N,
+                     st + 2 * T * N + 4 * T * K + 2 * ad),
+    }
+
+
+def roofline_seconds(kind, amount):
+    return amount / (HBM_PEAK if kind == "hbm" else MFMA_BF16_PEAK)
+
+
+def attainable(kind, amount, nbytes):
+    """min(P_MFMA, BW x AI_alg) for a GEMM phase (flop/s), BW for an HBM phase (B/s)."""
+    if kind == "hbm":
+        return HBM_PEAK
+    return min(MFMA_BF16_PEAK, HBM_PEAK * amount / nbytes)
+
+
+def phase_entry(kind, amount, nbytes, secs, calib=None):
+    """One component entry: rate, fraction of the published peak, of the attainable
+    roofline and (when measured) of the device's measured peak."""
+    rate = amount / secs
+    e = ({"GB/s": round(rate / 1e9, 1), "frac_of_hbm_peak": round(rate / HBM_PEAK, 4)} if kind == "hbm" else
+         {"TFLOP/s": round(rate / 1e12, 1), "frac_of_mfma_peak": round(rate / MFMA_BF16_PEAK, 4)})
+    if nbytes:
+        e["frac_of_attainable"] = round(rate / attainable(kind, amount, nbytes), 4)
+    if calib:
+        meas = calib.get("copy_B/s") if kind == "hbm" else calib.get("mfma_flop/s")
+        if meas:
+            e["frac_of_measured_peak"] = round(rate / meas, 4)
+    e["ms"] = round(1e3 * secs, 4)
+    return e
+
+
+def measure_roofline_kernel(api, torch, bufs, reps):
     """k_fwd alone: the forward with r = 0 is exactly one launch of the fused
-    NF4-dequant MFMA GEMM.  Returns (flops per launch, seconds per launch)."""
+    NF4-dequant MFMA GEMM.  HIP events on the launch stream around every launch.
+    Returns (flops per launch, seconds per launch)."""
     ys = [torch.empty((b["x"].shape[0], b["lin"].N), dtype=torch.bfloat16, device="cuda") for b in bufs]
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")          # r = 0 needs none
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps * len(bufs))]
     for i, b in enumerate(bufs):
-        api.qlora_linear_fwd(b["x"], b["qw"], out=ys[i])
+        api.qlora_linear_fwd(b["x"], b["qw"], workspace=ws, out=ys[i])
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     for k in range(reps):
         for i, b in enumerate(bufs):
             e = ev[k * len(bufs) + i]
             e[0].record(stream)
-            api.qlora_linear_fwd(b["x"], b["qw"], out=ys[i])
+            api.qlora_linear_fwd(b["x"], b["qw"], workspace=ws, out=ys[i])
             e[1].record(stream)
     torch.cuda.synchronize()
     secs = sum(e[0].elapsed_time(e[1]) for e in ev) / 1e3 / len(ev)
@@ -75,27 +134,252 @@ def measure_roofline_kernel(api, torch, layers, bufs, reps):
     return flops, secs
 
 
-def storage_bytes(numel):
-    return numel // 2 + numel // 64 + 4 * (-(-numel // 16384))
+def layer_65b_buffers(api, torch, synth):
+    """The 65B-shaped layer's tensors, drawn on the device (809.5 M weights)."""
+    cfg = synth.LAYER_65B
+    layers, T, r = cfg["layers"], cfg["T"], cfg["r"]
+    bufs = []
+    for ti, lin in enumerate(layers):
+        g = synth.device_generator(cfg["config"], 0, ti, synth.ROLE_W)
+        b = synth.device_layer_inputs(cfg["config"], 0, ti, lin, T, r, with_dy=True)
+        b["lin"] = lin
+        b["w"] = synth.device_normal_bf16(g, (lin.N, lin.K), 0.02)
+        b["qw"] = api.nf4_quantize_dq(b["w"])
+        b["wd"] = torch.empty((lin.N, lin.K), dtype=torch.bfloat16, device="cuda")
+        b["y"] = torch.empty((T, lin.N), dtype=torch.bfloat16, device="cuda")
+        b["dx"] = torch.empty((T, lin.K), dtype=torch.bfloat16, device="cuda")
+        bufs.append(b)
+    torch.cuda.synchronize()
+    return bufs
 
 
-def phase_work(lin, T, r):
-    """Algorithmic bytes (HBM phases) and flops (GEMM phases) of one linear."""
-    N, K = lin.N, lin.K
-    nk = N * K
-    st = storage_bytes(nk)
-    return {
-        "quantize": ("hbm", 2 * nk + st),
-        "dequantize": ("hbm", st + 2 * nk),
-        "forward": ("mfma", 2 * T * N * K + 2 * T * K * r + 2 * T * r * N),
-        # dX (base + LoRA), dY B^T, X A recompute, dA, dB
-        "backward": ("mfma", 2 * T * N * K + 2 * T * N * r + 2 * T * r * K + 2 * T * K * r + 2 * T * K * r
-                     + 2 * T * r * N),
+def run_step(torch, step, nev, steps, warmup):
+    """`warmup` untimed steps, then `steps` timed ones; returns (wall seconds of the
+    timed region, per-step event lists)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    all_events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(all_events[k])
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, all_events
+
+
+def layer_step(api, bufs, T, r, s, ws, stream, with_grads):
+    """One step over the seven linears: grouped quantize, grouped dequantize, then
+    per linear the forward and the backward (input gradient only, or with the LoRA
+    gradients and s X A reused from the forward).  Event layout: [quantize start,
+    quantize end = dequantize start, dequantize end, per linear forward end and
+    backward end]."""
+    wl, ql, dl = [b["w"] for b in bufs], [b["qw"] for b in bufs], [b["wd"] for b in bufs]
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        api.nf4_quantize_dq_grouped(wl, ql)
+        if ev: ev[1].record(stream)
+        api.nf4_dequantize_dq_grouped(ql, dl)
+        if ev: ev[2].record(stream)
+        for li, b in enumerate(bufs):
+            api.qlora_linear_fwd(b["x"], b["qw"], b["a"], b["b"], s, workspace=ws, out=b["y"])
+            if ev: ev[3 + 2 * li].record(stream)
+            if with_grads:
+                api.qlora_linear_bwd_input(b["dy"], b["qw"], b["a"], b["b"], s, x=b["x"], lora_grads=True,
+                                           workspace=ws, dx=b["dx"], d_lora_a=b["da"], d_lora_b=b["db"],
+                                           reuse_forward=True)
+            else:
+                api.qlora_linear_bwd_input(b["dy"], b["qw"], b["a"], b["b"], s, workspace=ws, dx=b["dx"])
+            if ev: ev[4 + 2 * li].record(stream)
+    return step, 3 + 2 * len(bufs)
+
+
+def step_phases(bufs, all_events, steps, T, r, bwd_name, calib=None):
+    """Per-phase durations from the step events, their components entries and the
+    step's total roofline time."""
+    dur = {"quantize": 0.0, "dequantize": 0.0, "forward": 0.0, bwd_name: 0.0}
+    for ev in all_events:
+        dur["quantize"] += ev[0].elapsed_time(ev[1]) / steps
+        dur["dequantize"] += ev[1].elapsed_time(ev[2]) / steps
+        for li in range(len(bufs)):
+            dur["forward"] += ev[2 + 2 * li].elapsed_time(ev[3 + 2 * li]) / steps
+            dur[bwd_name] += ev[3 + 2 * li].elapsed_time(ev[4 + 2 * li]) / steps
+    comp, roof = {}, 0.0
+    for p, ms in dur.items():
+        kind, amt, nb = None, 0, 0
+        for b in bufs:
+            kind, a, n = phase_work(b["lin"], T, r)[p]
+            amt += a
+            nb += n
+        roof += roofline_seconds(kind, amt)
+        comp[p] = phase_entry(kind, amt, nb, ms / 1e3, calib)
+    return comp, roof
+
+
+def measure_train_7b(api, torch, synth, np, steps, calib):
+    """The 7B training-shaped step (T = 4096, r = 64, alpha = 16): grouped quantize and
+    dequantize, then forward and backward with dX, dA, dB (s X A kept from the forward)
+    for each of the seven linears.  Inputs from the host generators (the oracle's
+    bytes).  Returns (components of the phases, ms per step, step attainment)."""
+    cfg = synth.TRAIN_7B
+    layers, T, r, s = cfg["layers"], cfg["T"], cfg["r"], cfg["scaling"]
+
+    def dev(bits, shape):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).reshape(shape).cuda()
+
+    ws = torch.empty(max(api.qlora_workspace_bytes(T, l.K, l.N, r) for l in layers), dtype=torch.uint8,
+                     device="cuda")
+    bufs = []
+    for li, lin in enumerate(layers):
+        d = synth.layer_inputs(cfg["config"], 0, li, lin, T, r, with_dy=True)
+        b = dict(lin=lin, w=dev(d["w"], (lin.N, lin.K)), x=dev(d["x"], (T, lin.K)), dy=dev(d["dy"], (T, lin.N)),
+                 a=dev(d["a"], (lin.K, r)), b=dev(d["b"], (r, lin.N)))
+        b["qw"] = api.nf4_quantize_dq(b["w"])
+        b["wd"] = torch.empty((lin.N, lin.K), dtype=torch.bfloat16, device="cuda")
+        b["y"] = torch.empty((T, lin.N), dtype=torch.bfloat16, device="cuda")
+        b["dx"] = torch.empty((T, lin.K), dtype=torch.bfloat16, device="cuda")
+        b["da"] = torch.empty((lin.K, r), dtype=torch.bfloat16, device="cuda")
+        b["db"] = torch.empty((r, lin.N), dtype=torch.bfloat16, device="cuda")
+        bufs.append(b)
+    torch.cuda.synchronize()
+    step, nev = layer_step(api, bufs, T, r, s, ws, torch.cuda.current_stream(), with_grads=True)
+    wall, evs = run_step(torch, step, nev, steps, 3)
+    comp, roof = step_phases(bufs, evs, steps, T, r, "backward", calib)
+    return comp, 1e3 * wall / steps, roof / (wall / steps), bufs, ws
+
+
+def measure_single_layer(api, torch, synth, launches=100, rotate_bytes=512 << 20):
+    """The single 4096 x 4096 layer (T = 16, r = 16, s = 1): quantize, dequantize and
+    forward, each as `launches` back-to-back launches over input/output sets that
+    together exceed `rotate_bytes` (so the 256 MB memory-side cache cannot serve
+    repeats), behind a GPU spin so that the events see device time only.
+    Returns {phase: (kind, seconds per launch, amount, algorithmic bytes)}."""
+    cfg = synth.SINGLE_LAYER
+    lin, T, r, s = cfg["layers"][0], cfg["T"], cfg["r"], cfg["scaling"]
+    g = synth.device_generator(cfg["config"], 0, 0, synth.ROLE_W)
+    w = synth.device_normal_bf16(g, (lin.N, lin.K), 0.02)
+    inp = synth.device_layer_inputs(cfg["config"], 0, 0, lin, T, r)
+    work = phase_work(lin, T, r)
+    qset = -(-rotate_bytes // work["quantize"][2])
+    fset = -(-rotate_bytes // work["forward"][2])
+    ws_in = [w.clone() for _ in range(qset)]
+    q_out = [api.nf4_quantize_dq(w) for _ in range(max(qset, fset))]
+    d_out = [torch.empty_like(w) for _ in range(qset)]
+    ys = torch.empty((T, lin.N), dtype=torch.bfloat16, device="cuda")
+    wsp = torch.empty(max(api.qlora_workspace_bytes(T, lin.K, lin.N, r), 256), dtype=torch.uint8, device="cuda")
+    ops = {
+        "quantize": (qset, lambda i: api.nf4_quantize_dq_into(ws_in[i], q_out[i])),
+        "dequantize": (qset, lambda i: api.nf4_dequantize_dq(q_out[i], out=d_out[i])),
+        "forward": (fset, lambda i: api.qlora_linear_fwd(inp["x"], q_out[i], inp["a"], inp["b"], s, workspace=wsp,
+                                                        out=ys)),
     }
+    out = {}
+    for name, (nset, fn) in ops.items():
+        for i in range(nset):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda._sleep(50_000_000)
+        ev[0].record()
+        for k in range(launches):
+            fn(k % nset)
+        ev[1].record()
+        torch.cuda.synchronize()
+        kind, amt, nb = work[name]
+        out[name] = (kind, ev[0].elapsed_time(ev[1]) / 1e3 / launches, amt, nb, nset)
+    return out
 
 
-def roofline_seconds(kind, amount):
-    return amount / (HBM_PEAK if kind == "hbm" else MFMA_BF16_PEAK)
+def measure_calibration(torch, calib, bufs=None, reps=10):
+    """The device's achievable peaks: the 128-bit streaming copy of 1 GiB (read +
+    write bytes over time), the MFMA-only loop (4 rounds of one 4-wave workgroup per
+    CU), and, as the unfused context, torch.matmul (hipBLASLt) of X by the
+    dequantized bf16 W' on the 65B layer's shapes."""
+    res = {}
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    calib.stream_copy(src, dst)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        calib.stream_copy(src, dst)
+    ev[1].record()
+    torch.cuda.synchronize()
+    secs = ev[0].elapsed_time(ev[1]) / 1e3 / reps
+    res["copy_B/s"] = 2 * n / secs
+    del src, dst
+    seed = torch.randint(-2 ** 30, 2 ** 30, (128,), dtype=torch.int32, device="cuda") & 0x3F803F80
+    wgs, iters = 256 * 4, 4096
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    flops = calib.mfma_loop(seed, out, wgs, iters)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(3):
+        calib.mfma_loop(seed, out, wgs, iters)
+    ev[1].record()
+    torch.cuda.synchronize()
+    res["mfma_flop/s"] = flops / (ev[0].elapsed_time(ev[1]) / 1e3 / 3)
+    if bufs is not None:
+        flops = 0
+        for b in bufs:
+            torch.matmul(b["x"], b["wd"].t())
+            flops += 2 * b["x"].shape[0] * b["lin"].N * b["lin"].K
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(3):
+            for b in bufs:
+                torch.matmul(b["x"], b["wd"].t())
+        ev[1].record()
+        torch.cuda.synchronize()
+        res["torch_matmul_flop/s"] = flops / (ev[0].elapsed_time(ev[1]) / 1e3 / 3)
+    return res
+
+
+def calibration_copy(torch, calib):
+    """Three streaming copies of COPY_BYTES: counter runs scale their byte counts by
+    what the same counters read for this copy of known size."""
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    c = torch.empty_like(a)
+    for _ in range(3):
+        calib.stream_copy(a, c)
+    torch.cuda.synchronize()
+
+
+def cpu_baseline(layers, T, r, s, row_frac=8, t_sample=32):
+    """The oracle, as it stands, on a bounded sample of the headline workload: NF4 +
+    double quantization and double dequantization of the first 1/row_frac of the
+    rows of each of the seven 65B-shaped weights, and the forward and backward-input
+    GEMMs of those rows on t_sample of the T tokens (inputs from the host generators
+    in the same distributions).  Scaled to the same unit as `value`."""
+    import numpy as np
+    import oracle
+    from qlora_linear_layers_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    roof = 0.0
+    t0 = time.perf_counter()
+    for li, lin in enumerate(layers):
+        sub = synth.Linear(lin.name, lin.N // row_frac, lin.K)
+        d = synth.layer_inputs(4, 0, li, sub, t_sample, r, with_dy=True)
+        rc, rf, rs = oracle.quantize_nf4_dq(d["w"])
+        wd = oracle.dequantize_nf4_dq(rc, rf, rs).reshape(sub.N, sub.K)
+        oracle.linear_fwd(d["x"], wd, d["a"], d["b"], s)
+        oracle.linear_bwd(d["dy"], None, wd, d["a"], d["b"], s)
+        for p in ("quantize", "dequantize", "forward", "backward_input"):
+            kind, amt, _ = phase_work(sub, t_sample, r)[p]
+            roof += roofline_seconds(kind, amt)
+    dt = time.perf_counter() - t0
+    return {"value": 100.0 * roof / dt, "unit": "% of MI355X roofline", "cores": int(threads), "kind": "oracle",
+            "sample": f"65B layer: quantize + dequantize of 1/{row_frac} of the rows of each of the 7 weights, "
+                      f"forward and backward-input of those rows on {t_sample} of {T} tokens",
+            "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
 
 
 def decode_bytes(lin, T, r):
@@ -108,6 +392,7 @@ def weight_copies(api, qws, copies=6):
     each), rotated so that the 256 MB last-level cache cannot serve repeats."""
     return [[api.NF4Weight(q.codes.clone(), q.absmax_fp8.clone(), q.superscale.clone(), q.N, q.K) for q in qws]
             for _ in range(copies)]
+
 
 
 DECODE_STAGES = ((0, 1, 2), (3,), (4, 5), (6,))    # q/k/v, o, gate/up, down: what a decode step can group
@@ -160,9 +445,11 @@ def measure_decode(api, torch, layers, sets, r, s, tokens=(1, 4, 8), reps=10, mo
     return out
 
 
+
 def merge_bytes(lin, r):
     """Algorithmic bytes of one LoRA merge: the packed weight and the adapters in, bf16 W_m out."""
     return storage_bytes(lin.N * lin.K) + 2 * lin.N * lin.K + 2 * r * (lin.K + lin.N)
+
 
 
 def measure_prefill(api, torch, layers, sets, r, s, tokens=(32, 64), reps=6):
@@ -196,6 +483,7 @@ def measure_prefill(api, torch, layers, sets, r, s, tokens=(32, 64), reps=6):
     return out
 
 
+
 def measure_merge(api, torch, layers, sets, r, s, reps=6):
     """W_m = RNE_bf16(W' + s (A B)^T) for the seven linears, one weight copy per pass
     (the 405 MB of outputs are written once per pass).  Returns (seconds, bytes) per layer set."""
@@ -218,6 +506,7 @@ def measure_merge(api, torch, layers, sets, r, s, reps=6):
     ev[1].record()
     torch.cuda.synchronize()
     return ev[0].elapsed_time(ev[1]) / 1e3 / reps, sum(merge_bytes(l, r) for l in layers)
+
 
 
 def measure_sq(api, torch, bufs, T, r, s, ws, reps=5):
@@ -252,6 +541,7 @@ def measure_sq(api, torch, bufs, T, r, s, ws, reps=5):
         torch.cuda.synchronize()
         out[name] = (kind, ev[0].elapsed_time(ev[1]) / 1e3 / reps, sum(work(b["lin"]) for b in bufs))
     return out
+
 
 
 def measure_ablation(api, torch, synth, np, bufs, reps=5):
@@ -290,6 +580,7 @@ def measure_ablation(api, torch, synth, np, bufs, reps=5):
     secs = ev[0].elapsed_time(ev[1]) / 1e3 / reps
     nbytes = sum(2 * b["lin"].N * b["lin"].K + storage_bytes_sq(b["lin"].N * b["lin"].K) for b in bufs)
     return out, secs, nbytes
+
 
 
 def measure_f16(api, torch, bufs, T, r, s, ws, reps=5):
@@ -334,63 +625,6 @@ def measure_f16(api, torch, bufs, T, r, s, ws, reps=5):
     return out
 
 
-def measure_65b(api, torch, synth, reps=3):
-    """The 65B-shaped layer (q/k/v/o 8192x8192, gate/up 22016x8192, down 8192x22016;
-    T = 2048, r = 64, s = 0.25): full-layer quantize and dequantize (one grouped
-    launch each), the fused
-    forward, and the backward input gradient dX = dY W' + s (dY B^T) A^T, each
-    timed over `reps` passes of the seven linears with HIP events.  Inputs are
-    drawn on the device (809.5 M weights).  Returns {phase: (kind, seconds, amount)}."""
-    cfg = synth.LAYER_65B
-    layers, T, r, s = cfg["layers"], cfg["T"], cfg["r"], cfg["scaling"]
-    ws = torch.empty(max(api.qlora_workspace_bytes(T, l.K, l.N, r) for l in layers), dtype=torch.uint8,
-                     device="cuda")
-    bufs = []
-    for ti, lin in enumerate(layers):
-        g = synth.device_generator(cfg["config"], 0, ti, synth.ROLE_W)
-        b = synth.device_layer_inputs(cfg["config"], 0, ti, lin, T, r, with_dy=True)
-        b["lin"] = lin
-        b["w"] = synth.device_normal_bf16(g, (lin.N, lin.K), 0.02)
-        b["qw"] = api.nf4_quantize_dq(b["w"])
-        b["wd"] = torch.empty((lin.N, lin.K), dtype=torch.bfloat16, device="cuda")
-        b["y"] = torch.empty((T, lin.N), dtype=torch.bfloat16, device="cuda")
-        b["dx"] = torch.empty((T, lin.K), dtype=torch.bfloat16, device="cuda")
-        bufs.append(b)
-
-    def bwd_flops(l):
-        return 2 * T * l.N * l.K + 2 * T * l.N * r + 2 * T * r * l.K
-
-    wl, ql, dl = [b["w"] for b in bufs], [b["qw"] for b in bufs], [b["wd"] for b in bufs]
-    # quantize / dequantize: the whole layer in one grouped launch (run once per pass)
-    ops = {
-        "quantize": ("hbm", lambda b: b is bufs[0] and api.nf4_quantize_dq_grouped(wl, ql),
-                     lambda l: phase_work(l, T, r)["quantize"][1]),
-        "dequantize": ("hbm", lambda b: b is bufs[0] and api.nf4_dequantize_dq_grouped(ql, dl),
-                       lambda l: phase_work(l, T, r)["dequantize"][1]),
-        "forward": ("mfma", lambda b: api.qlora_linear_fwd(b["x"], b["qw"], b["a"], b["b"], s, workspace=ws,
-                                                            out=b["y"]),
-                    lambda l: phase_work(l, T, r)["forward"][1]),
-        "backward_input": ("mfma", lambda b: api.qlora_linear_bwd_input(b["dy"], b["qw"], b["a"], b["b"], s,
-                                                                         workspace=ws, dx=b["dx"]),
-                           bwd_flops),
-    }
-    out = {}
-    for name, (kind, fn, work) in ops.items():
-        for b in bufs:
-            fn(b)
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record()
-        for _ in range(reps):
-            for b in bufs:
-                fn(b)
-        ev[1].record()
-        torch.cuda.synchronize()
-        out[name] = (kind, ev[0].elapsed_time(ev[1]) / 1e3 / reps, sum(work(b["lin"]) for b in bufs))
-    del bufs, ws
-    torch.cuda.empty_cache()
-    return out
-
 
 def measure_stream_70b(torch, synth, n_layers=80):
     """The 70B-shaped streaming workload: 80 layers of {q 8192x8192, k/v 1024x8192,
@@ -410,65 +644,38 @@ def measure_stream_70b(torch, synth, n_layers=80):
     return res["seconds"], moved, res["packed_bytes"], params
 
 
+
 def storage_bytes_sq(numel):
     """Codes + one fp32 absmax per 64 weights."""
     return numel // 2 + 4 * (numel // 64)
 
 
-def cpu_baseline(layers, T, r, s, t_sample):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
-    import numpy as np
-    import oracle
-    from qlora_linear_layers_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    roof = 0.0
-    t0 = time.perf_counter()
-    for li, lin in enumerate(layers):
-        d = synth.layer_inputs(3, 0, li, lin, T, r, with_dy=True)
-        x, dy = d["x"][:t_sample], d["dy"][:t_sample]
-        rc, rf, rs = oracle.quantize_nf4_dq(d["w"])
-        wd = oracle.dequantize_nf4_dq(rc, rf, rs).reshape(lin.N, lin.K)
-        oracle.linear_fwd(x, wd, d["a"], d["b"], s)
-        oracle.linear_bwd(dy, x, wd, d["a"], d["b"], s)
-        for name, (kind, amt) in phase_work(lin, t_sample, r).items():
-            roof += roofline_seconds(kind, amt)
-    dt = time.perf_counter() - t0
-    # generation of the synthetic inputs is inside dt; it is small next to the oracle
-    return {"value": 100.0 * roof / dt, "unit": "% of MI355X roofline", "cores": int(threads), "kind": "oracle",
-            "sample": f"all 7 linears: full quantize + dequantize, forward and backward on {t_sample} of {T} tokens",
-            "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
-
-
-def calibration_copy(torch):
-    """Three device copies of COPY_BYTES: counter runs scale their byte counts by
-    what the same counters read for this copy of known size."""
-    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
-    c = torch.empty_like(a)
-    for _ in range(3):
-        c.copy_(a)
-    torch.cuda.synchronize()
-
-
-def only_component(name, api, torch, synth, layers, r, s):
-    """One component alone, on weights drawn on the device (for kernel traces and counter runs)."""
+def only_component(name, api, torch, synth, calib, args):
+    """One component alone (for kernel traces and counter runs)."""
+    layers7, r, s = synth.TRAIN_7B["layers"], synth.TRAIN_7B["r"], synth.TRAIN_7B["scaling"]
     if name.startswith("decode"):
         g = torch.Generator(device="cuda").manual_seed(1)
         qws = [api.nf4_quantize_dq(torch.randn((l.N, l.K), generator=g, device="cuda").mul_(0.02)
-                                   .to(torch.bfloat16)) for l in layers]
+                                   .to(torch.bfloat16)) for l in layers7]
         mode = {"decode": "staged", "decode_single": "single", "decode_all7": "all"}[name]
-        res = measure_decode(api, torch, layers, weight_copies(api, qws), r, s, mode=mode)
+        res = measure_decode(api, torch, layers7, weight_copies(api, qws), r, s, mode=mode)
         return {f"T{Td}": {"GB/s": round(nb / secs / 1e9, 1), "us_per_layer_set": round(1e6 * secs, 2)}
                 for Td, (secs, nb) in res.items()}
-    if name == "layer_65b":
-        out = {}
-        for k, (kind, secs, amt) in measure_65b(api, torch, synth).items():
-            out[k] = ({"GB/s": round(amt / secs / 1e9, 1)} if kind == "hbm" else
-                      {"TFLOP/s": round(amt / secs / 1e12, 1)})
-        return out
+    if name == "single_layer":
+        return {k: {"GB/s": round(nb / secs / 1e9, 1), "us_per_launch": round(1e6 * secs, 3)}
+                for k, (kind, secs, amt, nb, _) in measure_single_layer(api, torch, synth).items()}
+    if name == "train_7b":
+        import numpy as np
+        comp, ms, att, _, _ = measure_train_7b(api, torch, synth, np, args.steps, None)
+        return {"ms_per_step": round(ms, 4), "attainment": round(att, 4), "phases": comp}
+    if name == "merge":
+        g = torch.Generator(device="cuda").manual_seed(1)
+        qws = [api.nf4_quantize_dq(torch.randn((l.N, l.K), generator=g, device="cuda").mul_(0.02)
+                                   .to(torch.bfloat16)) for l in layers7]
+        secs, nbytes = measure_merge(api, torch, layers7, weight_copies(api, qws), r, s)
+        return {"GB/s": round(nbytes / secs / 1e9, 1), "us_per_layer_set": round(1e6 * secs, 2)}
+    if name == "calibration":
+        return {k: round(v / 1e9, 1) for k, v in measure_calibration(torch, calib).items()}
     secs, moved, packed, params = measure_stream_70b(torch, synth)
     return {"GB/s": round(moved / secs / 1e9, 1), "ms": round(1e3 * secs, 3), "packed_bytes": packed,
             "params": params}
@@ -481,12 +688,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="only the step and the roofline kernel (for a kernel trace of the step alone)")
-    ap.add_argument("--cpu-tokens", type=int, default=256)
-    ap.add_argument("--only", choices=("decode", "decode_single", "decode_all7", "layer_65b", "stream_70b"),
+                    help="only the headline step and the roofline kernel (for a kernel trace of the step alone)")
+    ap.add_argument("--only", choices=("decode", "decode_single", "decode_all7", "single_layer", "train_7b",
+                                       "merge", "calibration", "stream_70b"),
                     help="run one component alone (no step, roofline loop or CPU baseline), e.g. for a kernel trace")
     ap.add_argument("--roofline-only", action="store_true",
-                    help="only the calibration copy and the k_fwd launches (for counter runs)")
+                    help="only the calibration copy and the k_fwd launches at the 65B shapes (for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path is single-GPU by design); --gpus {args.gpus} is not "
@@ -495,120 +702,53 @@ def main():
 
     import numpy as np
     import torch
-    from qlora_linear_layers_amd import api, synth
+    from qlora_linear_layers_amd import api, calib, synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     api.lib()
-    cfg = synth.TRAIN_7B
-    layers, T, r, s = cfg["layers"], cfg["T"], cfg["r"], cfg["scaling"]
 
     if args.only:
-        calibration_copy(torch)
-        print(json.dumps({"component": args.only, **only_component(args.only, api, torch, synth, layers, r, s)}),
+        calibration_copy(torch, calib)
+        print(json.dumps({"component": args.only, **only_component(args.only, api, torch, synth, calib, args)}),
               flush=True)
         return
 
-    def dev(bits, shape):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).reshape(shape).cuda()
-
-    bufs = []
-    ws_bytes = max(api.qlora_workspace_bytes(T, l.K, l.N, r) for l in layers)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    for li, lin in enumerate(layers):
-        d = synth.layer_inputs(3, 0, li, lin, T, r, with_dy=True)
-        b = dict(lin=lin, w=dev(d["w"], (lin.N, lin.K)), x=dev(d["x"], (T, lin.K)), dy=dev(d["dy"], (T, lin.N)),
-                 a=dev(d["a"], (lin.K, r)), b=dev(d["b"], (r, lin.N)))
-        b["qw"] = api.nf4_quantize_dq(b["w"])
-        b["wd"] = torch.empty((lin.N, lin.K), dtype=torch.bfloat16, device="cuda")
-        b["y"] = torch.empty((T, lin.N), dtype=torch.bfloat16, device="cuda")
-        b["dx"] = torch.empty((T, lin.K), dtype=torch.bfloat16, device="cuda")
-        b["da"] = torch.empty((lin.K, r), dtype=torch.bfloat16, device="cuda")
-        b["db"] = torch.empty((r, lin.N), dtype=torch.bfloat16, device="cuda")
-        bufs.append(b)
-    torch.cuda.synchronize()
+    cfg = synth.LAYER_65B
+    layers, T, r, s = cfg["layers"], cfg["T"], cfg["r"], cfg["scaling"]
+    bufs = layer_65b_buffers(api, torch, synth)
 
     if args.roofline_only:
-        calibration_copy(torch)
-        flops, secs = measure_roofline_kernel(api, torch, layers, bufs, args.steps)
+        calibration_copy(torch, calib)
+        flops, secs = measure_roofline_kernel(api, torch, bufs, args.steps)
         print(json.dumps({"roofline_kernel": "k_fwd", "tflops": flops / secs / 1e12, "us_per_launch": secs * 1e6,
                           "copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES,
                           "gemm_source_sha256_16": source_hash()}), flush=True)
         return
 
-    phases = ("quantize", "dequantize", "forward", "backward")
+    # headline: the 65B-shaped layer step
+    ws = torch.empty(max(api.qlora_workspace_bytes(T, l.K, l.N, r) for l in layers), dtype=torch.uint8,
+                     device="cuda")
     stream = torch.cuda.current_stream()
-
-    wlist, qlist, dlist = [b["w"] for b in bufs], [b["qw"] for b in bufs], [b["wd"] for b in bufs]
-
-    def step(ev=None):
-        # ev: [quantize start, quantize end = dequantize start, dequantize end, then per linear
-        # forward end and backward end]
-        if ev: ev[0].record(stream)
-        api.nf4_quantize_dq_grouped(wlist, qlist)          # the seven weights in one launch
-        if ev: ev[1].record(stream)
-        api.nf4_dequantize_dq_grouped(qlist, dlist)
-        if ev: ev[2].record(stream)
-        for li, b in enumerate(bufs):
-            api.qlora_linear_fwd(b["x"], b["qw"], b["a"], b["b"], s, workspace=ws, out=b["y"])
-            if ev: ev[3 + 2 * li].record(stream)
-            api.qlora_linear_bwd_input(b["dy"], b["qw"], b["a"], b["b"], s, x=b["x"], lora_grads=True,
-                                       workspace=ws, dx=b["dx"], d_lora_a=b["da"], d_lora_b=b["db"],
-                                       reuse_forward=True)
-            if ev: ev[4 + 2 * li].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    nev = 3 + 2 * len(bufs)
-    all_events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(all_events[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    step, nev = layer_step(api, bufs, T, r, s, ws, stream, with_grads=False)
+    wall, evs = run_step(torch, step, nev, args.steps, args.warmup)
     ms_per_step = 1e3 * wall / args.steps
+    calib_res = None if args.no_extras else measure_calibration(torch, calib, bufs)
+    comp, roof_step = step_phases(bufs, evs, args.steps, T, r, "backward_input", calib_res)
 
-    # per-phase average durations (ms) from the events: quantize and dequantize of the
-    # seven weights (one launch each), forward and backward per linear
-    dur = {p: 0.0 for p in phases}
-    for ev in all_events:
-        dur["quantize"] += ev[0].elapsed_time(ev[1]) / args.steps
-        dur["dequantize"] += ev[1].elapsed_time(ev[2]) / args.steps
-        for li in range(len(bufs)):
-            dur["forward"] += ev[2 + 2 * li].elapsed_time(ev[3 + 2 * li]) / args.steps
-            dur["backward"] += ev[3 + 2 * li].elapsed_time(ev[4 + 2 * li]) / args.steps
-
-    comp = {}
-    roof_step = 0.0
-    for p in phases:
-        kind = None
-        amt = 0
-        for b in bufs:
-            kind, a = phase_work(b["lin"], T, r)[p]
-            amt += a
-        secs = dur[p] / 1e3
-        rs = roofline_seconds(kind, amt)
-        roof_step += rs
-        if kind == "hbm":
-            comp[p] = {"GB/s": round(amt / secs / 1e9, 1), "frac_of_hbm_peak": round(rs / secs, 4),
-                       "ms": round(1e3 * secs, 4)}
-        else:
-            comp[p] = {"TFLOP/s": round(amt / secs / 1e12, 1), "frac_of_mfma_peak": round(rs / secs, 4),
-                       "ms": round(1e3 * secs, 4)}
-
-    # roofline of the dominant kernel: k_fwd, timed alone (r = 0 forward = one launch)
-    rf_flops, rf_secs = measure_roofline_kernel(api, torch, layers, bufs, max(args.steps // 2, 3))
+    # roofline of the dominant kernel: k_fwd at the same shapes, timed alone (r = 0 forward = one launch)
+    rf_flops, rf_secs = measure_roofline_kernel(api, torch, bufs, max(args.steps // 2, 3))
     achieved = rf_flops / rf_secs / 1e12
     traffic = stored_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": 2500.0, "unit": "TFLOP/s",
                 "frac": round(achieved / 2500.0, 4),
                 "traffic": None if traffic is None else round(traffic),
-                "kernel": "k_fwd: fused NF4 double-dequant + MFMA bf16 GEMM, 7B layer shapes at T=4096 "
+                "kernel": "k_fwd: fused NF4 double-dequant + MFMA bf16 GEMM, 65B layer shapes at T=2048 "
                           "(per-launch average over the 7 linears)",
                 "us_per_launch": round(1e6 * rf_secs, 2),
                 "flops_per_launch": rf_flops}
+    if calib_res:
+        roofline["frac_of_measured_mfma_peak"] = round(achieved * 1e12 / calib_res["mfma_flop/s"], 4)
 
     out = {
         "metric": "QLoRA linear fwd TFLOP/s + NF4 quant/dequant GB/s, as % of MI355X roofline",
@@ -616,77 +756,92 @@ def main():
         "unit": "% of MI355X roofline",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "LLaMA-7B-shaped layer, 7 linears (q/k/v/o 4096x4096, gate/up 11008x4096, "
-                               "down 4096x11008), T=4096 tokens, LoRA r=64 alpha=16; step = quantize + dequantize (grouped) "
-                               "+ forward + backward (dX, dA, dB; s X A kept from the forward) of every linear",
-                   "global_batch": 8, "seq_len": 512, "parallelism": "none (1 GPU)"},
+        "config": {"workload": "LLaMA-65B-shaped layer, 7 linears (q/k/v/o 8192x8192, gate/up 22016x8192, "
+                               "down 8192x22016), T=2048 tokens, LoRA r=64 alpha=16; step = quantize + dequantize "
+                               "(grouped) + forward + backward input (dX) of every linear",
+                   "tokens": T, "rank": r, "parallelism": "none (1 GPU)"},
         "components": comp,
         "roofline": roofline,
     }
-    if not args.no_extras:      # decode, single quantization, fp16, ablation, merge (outside the step)
-        sets = weight_copies(api, [b["qw"] for b in bufs])
+    if not args.no_extras:
+        comp["calibration"] = {
+            "stream_copy_GB/s": round(calib_res["copy_B/s"] / 1e9, 1),
+            "stream_copy_frac_of_hbm_peak": round(calib_res["copy_B/s"] / HBM_PEAK, 4),
+            "mfma_loop_TFLOP/s": round(calib_res["mfma_flop/s"] / 1e12, 1),
+            "mfma_loop_frac_of_mfma_peak": round(calib_res["mfma_flop/s"] / MFMA_BF16_PEAK, 4),
+            "torch_matmul_on_dequantized_W_TFLOP/s": round(calib_res["torch_matmul_flop/s"] / 1e12, 1),
+            "note": "128-bit streaming copy of 1 GiB (read + write bytes); MFMA-only loop (v_mfma_f32_32x32x16_bf16, "
+                    "16 independent chains per wave, one wave per SIMD); torch.matmul (hipBLASLt) of X by the "
+                    "dequantized bf16 W' on the 65B shapes, T=2048 (unfused context, no LoRA term)"}
+        for b in bufs:
+            b.pop("w", None)
+        del bufs, ws
+        torch.cuda.empty_cache()
+        # config 1: the single 4096 x 4096 layer
+        for name, (kind, secs, amt, nb, nset) in measure_single_layer(api, torch, synth).items():
+            e = phase_entry(kind, amt, nb, secs, calib_res)
+            e.pop("ms")
+            e["us_per_launch"] = round(1e6 * secs, 3)
+            if kind == "mfma":
+                e["GB/s"] = round(nb / secs / 1e9, 1)
+                e["frac_of_hbm_peak"] = round(nb / secs / HBM_PEAK, 4)
+            e["note"] = (f"4096x4096, T=16, r=16, s=1; 100 back-to-back launches over {nset} buffer sets "
+                         f"(>= 512 MB rotated)")
+            comp[f"single_layer_{name}"] = e
+        # config 3: the 7B training step (forward + backward with dA, dB)
+        c7, ms7, att7, bufs7, ws7 = measure_train_7b(api, torch, synth, np, args.steps, calib_res)
+        comp["train_7b"] = {"ms_per_step": round(ms7, 4), "attainment": round(att7, 4), "phases": c7,
+                            "note": "LLaMA-7B-shaped layer, T=4096, r=64 alpha=16: quantize + dequantize (grouped) "
+                                    "+ forward + backward (dX, dA, dB; s X A kept from the forward)"}
+        # config 2: decode, three launch patterns
+        sets = weight_copies(api, [b["qw"] for b in bufs7])
+        layers7, r7, s7 = synth.TRAIN_7B["layers"], synth.TRAIN_7B["r"], synth.TRAIN_7B["scaling"]
         notes = {"single": "one launch pair per linear",
                  "staged": "grouped launches per dependency stage: q/k/v, o, gate/up, down",
                  "all": "all 7 linears in one grouped launch pair (independent inputs)"}
         for mode, prefix in (("staged", "decode"), ("single", "decode_single"), ("all", "decode_all7")):
-            for Td, (secs, nbytes) in measure_decode(api, torch, layers, sets, r, s, mode=mode).items():
+            for Td, (secs, nbytes) in measure_decode(api, torch, layers7, sets, r7, s7, mode=mode).items():
                 comp[f"{prefix}_T{Td}"] = {
                     "GB/s": round(nbytes / secs / 1e9, 1), "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
+                    "frac_of_measured_peak": round(nbytes / secs / calib_res["copy_B/s"], 4),
                     "us_per_layer_set": round(1e6 * secs, 2),
                     "note": "7 linears, fused dequant + small-M MFMA (16x16x32) incl. LoRA; " + notes[mode]
                             + "; weights rotated over 6 copies"}
-        for name, (kind, secs, amt) in measure_sq(api, torch, bufs, T, r, s, ws).items():
-            if kind == "hbm":
-                comp[name] = {"GB/s": round(amt / secs / 1e9, 1), "frac_of_hbm_peak": round(amt / secs / HBM_PEAK, 4),
-                              "ms": round(1e3 * secs, 4), "note": "single quantization (fp32 absmax per 64 weights)"}
-            else:
-                comp[name] = {"TFLOP/s": round(amt / secs / 1e12, 1),
-                              "frac_of_mfma_peak": round(amt / secs / MFMA_BF16_PEAK, 4), "ms": round(1e3 * secs, 4),
-                              "note": "single quantization (fp32 absmax per 64 weights)"}
-        for name, (kind, secs, amt) in measure_f16(api, torch, bufs, T, r, s, ws).items():
-            note = "fp16 compute type" + (" (forward + backward pass, s X A reused)" if name == "backward_f16" else "")
-            if kind == "hbm":
-                comp[name] = {"GB/s": round(amt / secs / 1e9, 1), "frac_of_hbm_peak": round(amt / secs / HBM_PEAK, 4),
-                              "ms": round(1e3 * secs, 4), "note": note}
-            else:
-                comp[name] = {"TFLOP/s": round(amt / secs / 1e12, 1),
-                              "frac_of_mfma_peak": round(amt / secs / MFMA_BF16_PEAK, 4), "ms": round(1e3 * secs, 4),
-                              "note": note}
-        abl, secs, nbytes = measure_ablation(api, torch, synth, np, bufs)
+        for name, (kind, secs, amt) in measure_sq(api, torch, bufs7, synth.TRAIN_7B["T"], r7, s7, ws7).items():
+            comp[name] = phase_entry(kind, amt, None, secs)
+            comp[name]["note"] = "single quantization (fp32 absmax per 64 weights), 7B layer set, T=4096"
+        for name, (kind, secs, amt) in measure_f16(api, torch, bufs7, synth.TRAIN_7B["T"], r7, s7, ws7).items():
+            comp[name] = phase_entry(kind, amt, None, secs)
+            comp[name]["note"] = "fp16 compute type, 7B layer set, T=4096" + (
+                " (forward + backward pass, s X A reused)" if name == "backward_f16" else "")
+        abl, secs, nbytes = measure_ablation(api, torch, synth, np, bufs7)
         comp["int4_ablation"] = {
             "relative_rms_error": {k: {dt: round(e, 5) for dt, e in v.items()} for k, v in abl.items()},
             "int4_quantize_GB/s": round(nbytes / secs / 1e9, 1),
             "note": "NF4 vs INT4 absmax levels, fp32 absmax per 64 weights for both"}
-        secs, nbytes = measure_merge(api, torch, layers, sets, r, s)
+        secs, nbytes = measure_merge(api, torch, layers7, sets, r7, s7)
         comp["merge"] = {"GB/s": round(nbytes / secs / 1e9, 1), "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
                          "us_per_layer_set": round(1e6 * secs, 2),
                          "note": "7 linears, W_m = RNE_bf16(W' + s (A B)^T), r=64; weights rotated over 6 copies"}
-        for Tp, (secs, nbytes, flops) in measure_prefill(api, torch, layers, sets, r, s).items():
+        for Tp, (secs, nbytes, flops) in measure_prefill(api, torch, layers7, sets, r7, s7).items():
             comp[f"prefill_T{Tp}"] = {"TFLOP/s": round(flops / secs / 1e12, 1), "GB/s": round(nbytes / secs / 1e9, 1),
                                       "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
                                       "us_per_layer_set": round(1e6 * secs, 2),
                                       "note": "7 linears, r=64, forward at a small-prefill T: 16-token windows as one "
                                               "grouped decode launch pair; weights rotated over 6 copies"}
-        del sets
-        for name, (kind, secs, amt) in measure_65b(api, torch, synth).items():
-            key = name + "_65b"
-            if kind == "hbm":
-                comp[key] = {"GB/s": round(amt / secs / 1e9, 1), "frac_of_hbm_peak": round(amt / secs / HBM_PEAK, 4),
-                             "ms": round(1e3 * secs, 4)}
-            else:
-                comp[key] = {"TFLOP/s": round(amt / secs / 1e12, 1),
-                             "frac_of_mfma_peak": round(amt / secs / MFMA_BF16_PEAK, 4), "ms": round(1e3 * secs, 4)}
-            comp[key]["note"] = ("65B-shaped layer (q/k/v/o 8192x8192, gate/up 22016x8192, down 8192x22016), "
-                                 "T=2048, r=64; 7 linears per pass (quantize / dequantize: one grouped launch)")
+        del sets, bufs7, ws7
+        torch.cuda.empty_cache()
+        # config 5: the 70B-shaped stream
         secs, moved, packed, params = measure_stream_70b(torch, synth)
         closed = params * (4 + 8 / 64 + 32 / 16384) / 8
         comp["stream_70b"] = {"GB/s": round(moved / secs / 1e9, 1), "frac_of_hbm_peak": round(moved / secs / HBM_PEAK, 4),
+                              "frac_of_measured_peak": round(moved / secs / calib_res["copy_B/s"], 4),
                               "ms": round(1e3 * secs, 3), "params": params, "packed_bytes": packed,
                               "closed_form_bytes": int(closed), "bits_per_param": round(8 * packed / params, 9),
                               "note": "80 layers x 7 tensors (70B shapes, 0.1% t3 outliers), grouped quantize_dq then "
                                       "grouped dequantize per layer, one layer resident; kernel time only"}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(layers, T, r, s, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(layers, T, r, s)
     print(json.dumps(out), flush=True)
 
 

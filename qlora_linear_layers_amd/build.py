@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libqlora_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ("codebook.cpp", "quant.hip", "gemm.hip", "lora.hip", "gemv.hip", "merge.hip", "api.cpp")
+SOURCES = ("codebook.cpp", "quant.hip", "gemm.hip", "lora.hip", "gemv.hip", "merge.hip", "api.cpp", "calib.hip")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -14,7 +14,8 @@ import oracle
 from qlora_linear_layers_amd import api
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "qlora.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 OK, NULL, SHAPE, ALIGN, VALUE, WORKSPACE = 0, 1, 2, 3, 4, 5
 FAKE = 1 << 20           # a 16-byte aligned non-NULL address; never dereferenced on these paths
@@ -29,16 +30,29 @@ def L():
 
 
 def _declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M))
+    return sorted(names)
 
 
 def test_exports_match_header(L):
+    from qlora_linear_layers_amd import calib
     names = _declared()
-    assert set(names) == set(api.EXPORTS), names
+    assert set(names) == set(api.EXPORTS) | set(calib.EXPORTS), names
     for n in names:
         assert hasattr(L, n)
+
+
+def test_calibration_validation(L):
+    from qlora_linear_layers_amd import calib
+    c = calib._lib()
+    assert c.qlora_calib_copy(None, FAKE, 16, None) == 1
+    assert c.qlora_calib_copy(FAKE, FAKE, 24, None) == 1
+    assert c.qlora_calib_copy(MIS, FAKE, 16, None) == 1
+    assert c.qlora_calib_mfma(FAKE, FAKE, 0, 10, None) == 1
+    assert c.qlora_calib_mfma_flops(256, 10) == 256 * 4 * 10 * 16 * 32 * 32 * 16 * 2
 
 
 def test_codebook_bit_exact(L):
