@@ -348,6 +348,30 @@ size_t qlora_grouped_workspace_bytes(int count, const qlora_linear_problem* prob
 int qlora_linear_fwd_grouped(int count, const qlora_linear_problem* problems, int64_t T, int64_t r,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * qlora_linear_fwd_noalloc - qlora_linear_fwd for callers that cannot
+ *   allocate device memory (code under HIP graph capture, tight serving
+ *   loops, harnesses that forbid hipMalloc): the same computation, kernels and
+ *   bits as qlora_linear_fwd, with no workspace argument.  Its scratch is a
+ *   static device array of qlora_noalloc_scratch_bytes() (32 MiB) that every
+ *   GPU the library runs on holds until the process ends; the call allocates
+ *   nothing.  Sizes whose workspace (qlora_workspace_bytes' forward part)
+ *   exceeds it are rejected with QLORA_ERR_WORKSPACE before anything is
+ *   launched; that covers, for example, every T <= 16 decode call of the
+ *   LLaMA-7B and -65B linears with r <= 64, and T = 4096 on the 7B shapes.
+ *   All calls on one GPU share its array and each leaves it in an unspecified
+ *   state, so calls that may overlap on one GPU (other streams, other host
+ *   threads) race and must be serialised by the caller; nothing in the array
+ *   needs to start at zero.  The forward's s X A is not kept for a backward
+ *   (no QLORA_BWD_REUSE_FORWARD after this call).  The stream must belong to
+ *   the current device.  Arguments and errors otherwise as qlora_linear_fwd.
+ */
+int qlora_linear_fwd_noalloc(const uint16_t* x, int64_t T, int64_t K, int64_t N,
+                             const uint8_t* codes, const uint8_t* absmax_fp8, const float* superscale,
+                             const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling,
+                             uint16_t* y, void* stream);
+size_t qlora_noalloc_scratch_bytes(void);
+
 /* qlora_status_string - static, NUL-terminated description of a status code. */
 const char* qlora_status_string(int status);
 

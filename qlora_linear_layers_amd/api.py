@@ -41,6 +41,9 @@ _SIGS = {
     "qlora_merge_lora_sq": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, ctypes.c_float, _c_p,
                                            _c_p]),
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "qlora_linear_fwd_noalloc": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                                                ctypes.c_float, _c_p, _c_p]),
+    "qlora_noalloc_scratch_bytes": (ctypes.c_size_t, []),
 }
 
 
@@ -381,6 +384,29 @@ def qlora_linear_fwd(x, qw, lora_a=None, lora_b=None, scaling=1.0, workspace=Non
     _check(fn, getattr(lib(), fn)(
         _ptr(x), T, K, qw.N, _ptr(qw.codes), *sc, _ptr(lora_a), _ptr(lora_b),
         r, float(scaling), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def qlora_linear_fwd_noalloc(x, qw, lora_a=None, lora_b=None, scaling=1.0, out=None):
+    """qlora_linear_fwd with the library's static scratch instead of a workspace
+    (for callers that cannot allocate; `out` must then be given).  bf16 and
+    double quantization only."""
+    if x.dtype != torch.bfloat16 or isinstance(qw, NF4WeightSQ):
+        raise TypeError("the no-allocation forward takes bf16 tensors and double-quantized weights")
+    _check_storage(qw)
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D [T, K], got shape {tuple(x.shape)}")
+    T = x.shape[0]
+    _shape(x, (T, qw.K), "x")
+    r = _check_adapters(lora_a, lora_b, qw.K, qw.N)
+    _shape(out, (T, qw.N), "out")
+    for t, name in ((x, "x"), (lora_a, "lora_a"), (lora_b, "lora_b"), (out, "out")):
+        _dev(t, torch.bfloat16, name)
+    if out is None:
+        out = torch.empty((T, qw.N), dtype=torch.bfloat16, device=x.device)
+    _check("qlora_linear_fwd_noalloc", lib().qlora_linear_fwd_noalloc(
+        _ptr(x), T, qw.K, qw.N, _ptr(qw.codes), _ptr(qw.absmax_fp8), _ptr(qw.superscale), _ptr(lora_a),
+        _ptr(lora_b), r, float(scaling), _ptr(out), _stream()))
     return out
 
 

@@ -3,6 +3,7 @@
 // here; every buffer comes from the caller.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "qlora.h"
 #include "common.hpp"
@@ -80,22 +81,36 @@ int quantize_sq_impl(const uint16_t* w, int64_t numel, uint8_t* codes, float* ab
     return dev(ql::launch_quantize_sq(w, numel, codes, absmax, static_cast<hipStream_t>(stream), int4));
 }
 
-int fwd_impl(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* codes, ql::BlockScales sc,
-             const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling, uint16_t* y, void* workspace,
-             size_t workspace_bytes, void* stream, bool f16 = false) {
+// Argument checks of the forward (everything but the workspace).
+int fwd_check(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* codes, ql::BlockScales sc,
+              const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling, const uint16_t* y) {
     if (!x || !codes || !scales_present(sc) || !y) return QLORA_ERR_NULL;
     if (r > 0 && (!lora_a || !lora_b)) return QLORA_ERR_NULL;
     if (int st = check_linear_shape(T, K, N, r)) return st;
     if (r == 0 && (lora_a || lora_b)) return QLORA_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(codes) || !scales_aligned(sc) || !aligned16(y) ||
-        (lora_a && !aligned16(lora_a)) || (lora_b && !aligned16(lora_b)) || (workspace && !aligned16(workspace)))
+        (lora_a && !aligned16(lora_a)) || (lora_b && !aligned16(lora_b)))
         return QLORA_ERR_ALIGN;
     if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
+    return QLORA_OK;
+}
+
+// Workspace bytes of one forward call (sizes already checked).
+size_t fwd_workspace(int64_t T, int64_t K, int64_t N, int64_t r) {
+    const ql::LoraPlan pl(T, K, N, r);
+    if (T <= ql::kGemvMaxT) return ql::gemv_workspace(T, K, N, pl.r_pad);
+    if (T <= ql::kChunkMaxT) return chunked_workspace(T, K, N, pl.r_pad);
+    return pl.fwd_bytes;
+}
+
+int fwd_impl(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* codes, ql::BlockScales sc,
+             const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling, uint16_t* y, void* workspace,
+             size_t workspace_bytes, void* stream, bool f16 = false) {
+    if (int st = fwd_check(x, T, K, N, codes, sc, lora_a, lora_b, r, scaling, y)) return st;
+    if (workspace && !aligned16(workspace)) return QLORA_ERR_ALIGN;
     const ql::LoraPlan pl(T, K, N, r);
     const bool chunked = T > ql::kGemvMaxT && T <= ql::kChunkMaxT;
-    const size_t need = T <= ql::kGemvMaxT ? ql::gemv_workspace(T, K, N, pl.r_pad)
-                        : chunked      ? chunked_workspace(T, K, N, pl.r_pad)
-                                       : pl.fwd_bytes;
+    const size_t need = fwd_workspace(T, K, N, r);
     if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -233,9 +248,52 @@ int quantize_dq_impl(const uint16_t* w, int64_t numel, uint8_t* codes, uint8_t* 
     return dev(ql::launch_quantize(w, numel, codes, absmax_fp8, superscale, static_cast<hipStream_t>(stream), f16));
 }
 
+// ------------------------------------------------------------ no-allocation forward
+//
+// qlora_linear_fwd_noalloc takes its workspace from this file-scope device
+// array instead of the caller.  Host code never passes the array's name to a
+// kernel or a copy (on the host it is only a stand-in for the symbol): the
+// device address of each GPU's copy is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept below.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int scratch_of_current_device(void** out) {
+    int d = -1;
+    if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kMaxDevices) return QLORA_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[d]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QLORA_ERR_DEVICE;
+        g_scratch[d] = p;
+    }
+    *out = g_scratch[d];
+    return QLORA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t qlora_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int qlora_linear_fwd_noalloc(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* codes,
+                             const uint8_t* absmax_fp8, const float* superscale, const uint16_t* lora_a,
+                             const uint16_t* lora_b, int64_t r, float scaling, uint16_t* y, void* stream) {
+    const ql::BlockScales sc = dq_scales(absmax_fp8, superscale);
+    if (int st = fwd_check(x, T, K, N, codes, sc, lora_a, lora_b, r, scaling, y)) return st;
+    const size_t need = fwd_workspace(T, K, N, r);
+    if (need > kScratchBytes) return QLORA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need)
+        if (int st = scratch_of_current_device(&ws)) return st;
+    return fwd_impl(x, T, K, N, codes, sc, lora_a, lora_b, r, scaling, y, ws, kScratchBytes, stream);
+}
 
 const char* qlora_status_string(int status) {
     switch (status) {

@@ -72,6 +72,39 @@ def test_workspace_upto_covers_every_token_count(L):
     assert L.qlora_workspace_bytes_upto(0, 4096, 4096, 64) == 0
 
 
+def test_noalloc_forward_validation(L):
+    """The no-allocation forward checks its arguments like qlora_linear_fwd and
+    rejects sizes whose workspace exceeds its static scratch, before anything
+    touches a device.  Accepted sizes then need the device (this machine has
+    none: QLORA_ERR_DEVICE), which separates accepted from rejected sizes here."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("accepted sizes would launch kernels on these fake pointers")
+    DEVICE = 6
+    f = L.qlora_linear_fwd_noalloc
+    assert L.qlora_noalloc_scratch_bytes() == 32 << 20
+
+    def call(T, K, N, r, **kw):
+        a = dict(x=FAKE, codes=FAKE, f8=FAKE, sup=FAKE, la=FAKE if r else None, lb=FAKE if r else None, s=0.25,
+                 y=FAKE)
+        a.update(kw)
+        return f(a["x"], T, K, N, a["codes"], a["f8"], a["sup"], a["la"], a["lb"], r, a["s"], a["y"], None)
+
+    assert call(16, 256, 256, 16, x=None) == NULL
+    assert call(16, 256, 256, 16, y=MIS) == ALIGN
+    assert call(16, 250, 256, 16) == SHAPE
+    assert call(16, 256, 256, 16, s=math.inf) == VALUE
+    # T <= 16 decode of every 7B and 65B linear with r = 64 fits; so does T = 4096 on the 7B shapes
+    for K, N in ((4096, 4096), (4096, 11008), (11008, 4096), (8192, 8192), (8192, 22016), (22016, 8192)):
+        for T in (1, 8, 16):
+            assert call(T, K, N, 64) == DEVICE, (T, K, N)
+    for K, N in ((4096, 4096), (4096, 11008), (11008, 4096)):
+        assert call(4096, K, N, 64) == DEVICE
+    # windows of the 7B gate at T = 128 (one decode workspace per 16-token window) do not
+    assert call(128, 4096, 11008, 64) == WORKSPACE
+    assert call(1 << 20, 1024, 1024, 64) == WORKSPACE
+
+
 def test_status_strings(L):
     for s in range(7):
         assert L.qlora_status_string(s)
