@@ -14,11 +14,12 @@ hipError_t launch_transpose_a(const uint16_t* lora_a, const LoraPlan& pl, uint8_
 hipError_t launch_lora_down_x(const uint16_t* x, float scaling, const LoraPlan& pl, uint8_t* ws, bool transposed,
                               hipStream_t s, bool f16);
 hipError_t launch_lora_down_dy(const uint16_t* dy, const uint16_t* lora_b, float scaling, const LoraPlan& pl,
-                               uint8_t* ws, bool transposed, hipStream_t s, bool f16);
+                               uint8_t* ws, bool transposed, hipStream_t s, bool f16, const ScalesJob* scales);
 hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, BlockScales sc, const uint16_t* lora_b,
                       const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s, bool f16);
 hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
-                     const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s, bool f16);
+                     const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s, bool f16,
+                     bool scales_ready);
 hipError_t launch_lora_grads(const uint16_t* x, const uint16_t* dy, const LoraPlan& pl, uint8_t* ws,
                              uint16_t* d_lora_a, uint16_t* d_lora_b, hipStream_t s, bool f16);
 }  // namespace ql
@@ -164,9 +165,12 @@ int bwd_impl(const uint16_t* dy, int64_t T, int64_t K, int64_t N, const uint8_t*
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    if (r > 0)
-        if (int st = dev(ql::launch_lora_down_dy(dy, lora_b, scaling, pl, ws, grads, s, f16))) return st;
-    if (int st = dev(ql::launch_dx(dy, codes, sc, lora_a, pl, ws, dx, s, f16))) return st;
+    if (r > 0) {
+        // s dY B^T, with the dX kernel's block scales as extra workgroups of the same launch
+        const ql::ScalesJob sj = ql::scales_job_for(sc, pl, ws);
+        if (int st = dev(ql::launch_lora_down_dy(dy, lora_b, scaling, pl, ws, grads, s, f16, &sj))) return st;
+    }
+    if (int st = dev(ql::launch_dx(dy, codes, sc, lora_a, pl, ws, dx, s, f16, r > 0))) return st;
     if (grads) {
         if (!reuse) {
             if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;

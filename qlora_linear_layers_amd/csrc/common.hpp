@@ -251,6 +251,28 @@ struct BlockScales {
     bool single() const { return absmax != nullptr; }
 };
 
+// The transposed block scales c1' of a quantized W [N, K] that the dX kernel
+// reads: out[kb][n] = c1' of block kb of row n, i.e. fl32(e4m3(f) * s2) (the
+// stored fp32 absmax with single quantization), [K/64][N] so that eight
+// consecutive rows of one block column are contiguous.  It runs as extra
+// workgroups of another launch (or alone): workgroup `b` of `blocks` writes
+// entries 256 b .. 256 b + 255 (n fastest).
+struct ScalesJob {
+    const uint8_t* fp8;
+    const float* sup;
+    const float* absmax;      // single quantization (fp8, sup unused)
+    int64_t N, KB;
+    float* out;
+    int blocks;               // ceil(N * KB / 256), 0 = no job
+};
+QL_DEV void scales_job(const ScalesJob& j, int b) {
+    const int64_t i = (int64_t)b * 256 + threadIdx.x;
+    if (i >= j.N * j.KB) return;
+    const int64_t kb = i / j.N, n = i % j.N;
+    const int64_t blk = n * j.KB + kb;
+    j.out[i] = j.absmax ? j.absmax[blk] : block_scale(j.fp8[blk], j.sup[blk >> 8]);
+}
+
 // One tensor of a grouped quantize or dequantize launch: `w` is read by the
 // quantizer, `out` written by the dequantizer; `absmax` set selects single
 // quantization (fp8/sup unused).
@@ -299,6 +321,7 @@ constexpr int64_t kGemvMaxT = 16;
 // which beats one pass of 256-token MFMA tiles that leave most CUs idle.
 constexpr int64_t kChunkMaxT = 128;
 struct LoraPlan;
+ScalesJob scales_job_for(BlockScales sc, const LoraPlan& pl, uint8_t* ws);
 size_t gemv_workspace(int64_t T, int64_t K, int64_t N, int64_t r_pad);
 hipError_t launch_merge(const uint8_t* codes, BlockScales sc, const uint16_t* lora_a, const uint16_t* lora_b,
                         int64_t K, int64_t N, int64_t r, float scaling, uint16_t* w_out, hipStream_t s, bool f16);

@@ -517,19 +517,9 @@ struct DxArgs {
     int64_t T, K, N, r, r_pad;
 };
 
-// Block scales c1' = fl32(e4m3(f) * s2) of W [N, K] (single quantization: the
-// stored fp32 absmax), written transposed as [K/64][N] so that eight
-// consecutive rows of one block column are contiguous.
-template <bool SQ>
-__global__ __launch_bounds__(256) void k_scales_t(const uint8_t* __restrict__ fp8, const float* __restrict__ sup,
-                                                  const float* __restrict__ absmax, int64_t N, int64_t KB,
-                                                  float* __restrict__ out) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;     // over N x KB, n fastest
-    if (i >= N * KB) return;
-    const int64_t kb = i / N, n = i % N;
-    const int64_t b = n * KB + kb;
-    out[i] = SQ ? absmax[b] : block_scale(fp8[b], sup[b >> 8]);
-}
+// The transposed block scales alone (when no other launch of the backward
+// carries them).
+__global__ __launch_bounds__(256) void k_scales_t(ScalesJob j) { scales_job(j, (int)blockIdx.x); }
 
 // dX = dY W' (+ (s dY B^T) A^T): tile 256 (k) x 256 (t), reduction over n in
 // tiles of 64, waves 2 x 2 (wave (wa, wb) owns k rows wa*128.. and t rows
@@ -842,17 +832,21 @@ hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, BlockScales sc, c
     return sc.single() ? go(k_fwd<true, false>) : go(k_fwd<false, false>);
 }
 
+ScalesJob scales_job_for(BlockScales sc, const LoraPlan& pl, uint8_t* ws) {
+    return ScalesJob{sc.fp8, sc.sup, sc.absmax, pl.N, pl.K / 64, reinterpret_cast<float*>(ws + pl.off_scl),
+                     (int)ceil_div((pl.K / 64) * pl.N, 256)};
+}
+
 hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
-                     const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s, bool f16) {
-    float* sclt = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + pl.off_scl);
-    const int64_t nsc = (pl.K / 64) * pl.N;
-    const dim3 sg((unsigned)ceil_div(nsc, 256));
-    if (sc.single())
-        hipLaunchKernelGGL(k_scales_t<true>, sg, dim3(256), 0, s, nullptr, nullptr, sc.absmax, pl.N, pl.K / 64, sclt);
-    else
-        hipLaunchKernelGGL(k_scales_t<false>, sg, dim3(256), 0, s, sc.fp8, sc.sup, nullptr, pl.N, pl.K / 64, sclt);
-    hipError_t e0 = hipGetLastError();
-    if (e0 != hipSuccess) return e0;
+                     const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s, bool f16,
+                     bool scales_ready) {
+    const float* sclt = reinterpret_cast<const float*>(ws + pl.off_scl);
+    if (!scales_ready) {
+        const ScalesJob j = scales_job_for(sc, pl, const_cast<uint8_t*>(ws));
+        hipLaunchKernelGGL(k_scales_t, dim3((unsigned)j.blocks), dim3(256), 0, s, j);
+        hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) return e0;
+    }
     DxArgs a{dy, codes, sc.fp8, sc.sup, lora_a, reinterpret_cast<const uint16_t*>(ws + pl.off_gs_hi),
              reinterpret_cast<const uint16_t*>(ws + pl.off_gs_lo), sclt, dx,
              pl.T, pl.K, pl.N, pl.r, pl.r_pad};

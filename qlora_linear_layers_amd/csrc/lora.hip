@@ -99,6 +99,7 @@ struct DownArgs {
     int64_t T8, ldt;
     float* part;          // [splits][T][r_pad] fp32 partial sums (splits > 1)
     int splits;
+    ScalesJob sj;         // the dX kernel's transposed block scales, as extra workgroups (sj.blocks may be 0)
 };
 
 // v (already scaled) -> hi/lo at row t, column j of both layouts
@@ -148,9 +149,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(DownArgs a) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     lds8_t* smem = (lds8_t*)(smem_raw);
     constexpr uint32_t kXT = 64 * 128, kMT = R * 128, kBuf = kXT + kMT;
+    if ((int)blockIdx.x < a.sj.blocks) {        // block-scale workgroups of the same launch
+        scales_job(a.sj, (int)blockIdx.x);
+        return;
+    }
+    const int bid = (int)blockIdx.x - a.sj.blocks;
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int tiles = (int)ceil_div(a.T, 64);
-    const int tile = (int)blockIdx.x % tiles, split = (int)blockIdx.x / tiles;
+    const int tile = bid % tiles, split = bid / tiles;
     const int64_t t0 = (int64_t)tile * 64;
     const int nr_all = (int)(a.L / 64);
     const int r0 = split * nr_all / a.splits, r1 = (split + 1) * nr_all / a.splits;
@@ -286,12 +292,17 @@ struct GradArgs {
 
 // part[split][c][j] = sum over the split's tokens of S[t][c] (V_hi + V_lo)[t][j]
 // for 128 columns c and 64 columns j (blockIdx.y picks the 64) per workgroup.
+// One launch serves both adapter gradients: workgroups [0, blocks0) take
+// problem a0 (dA = X^T G), the rest problem a1 (dB = P^T dY).
 template <bool F16>
-__global__ __launch_bounds__(kThreads, 1) void k_grad(GradArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void k_grad(GradArgs a0, GradArgs a1, int blocks0) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     float* red = reinterpret_cast<float*>(smem_raw);     // [4 waves][8 i][4 jt][64 lanes][4]
+    const bool second = (int)blockIdx.x >= blocks0;
+    const GradArgs& a = second ? a1 : a0;
+    const int bx = second ? (int)blockIdx.x - blocks0 : (int)blockIdx.x;
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int cb = (int)(blockIdx.x % a.cblocks), split = (int)(blockIdx.x / a.cblocks);
+    const int cb = bx % a.cblocks, split = bx / a.cblocks;
     const int64_t j0 = (int64_t)blockIdx.y * 64;
     const int64_t c0 = (int64_t)cb * 128 + 8 * (l & 15);          // this lane's 8 columns
     const int64_t tw = ((int64_t)split * 4 + w) * 32 * a.cpw;      // first token of this wave
@@ -456,7 +467,8 @@ hipError_t down_rt(const DownArgs& a, hipStream_t s) {
     hipError_t e = set_smem(k_down<RT, F16>, lds);
     if (e != hipSuccess) return e;
     const unsigned tiles = (unsigned)ceil_div(a.T, 64);
-    hipLaunchKernelGGL((k_down<RT, F16>), dim3(tiles * (unsigned)a.splits), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((k_down<RT, F16>), dim3(tiles * (unsigned)a.splits + (unsigned)a.sj.blocks), dim3(kThreads),
+                       lds, s, a);
     if (a.splits > 1) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -481,12 +493,13 @@ hipError_t down(const DownArgs& a, hipStream_t s, bool f16) { return f16 ? down_
 
 constexpr size_t kGradSmem = (size_t)4 * 8 * 4 * 64 * 4 * 4;   // 128 KB
 
-hipError_t grad(const GradArgs& a, int splits, hipStream_t s, bool f16) {
+// One k_grad launch over up to two problems (`n1` = 0: a0 alone).
+hipError_t grad(const GradArgs& a0, int n0, const GradArgs& a1, int n1, int64_t r_pad, hipStream_t s, bool f16) {
     auto go = [&](auto kern) {
         hipError_t e = set_smem(kern, kGradSmem);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3((unsigned)(a.cblocks * splits), (unsigned)(a.r_pad / 64)), dim3(kThreads),
-                           kGradSmem, s, a);
+        hipLaunchKernelGGL(kern, dim3((unsigned)(n0 + n1), (unsigned)(r_pad / 64)), dim3(kThreads), kGradSmem, s,
+                           a0, a1, n0);
         return hipGetLastError();
     };
     return f16 ? go(k_grad<true>) : go(k_grad<false>);
@@ -509,18 +522,19 @@ hipError_t launch_lora_down_x(const uint16_t* x, float scaling, const LoraPlan& 
                reinterpret_cast<uint16_t*>(ws + pl.off_ps_hi), reinterpret_cast<uint16_t*>(ws + pl.off_ps_lo),
                transposed ? reinterpret_cast<uint16_t*>(ws + pl.off_pst_hi) : nullptr,
                transposed ? reinterpret_cast<uint16_t*>(ws + pl.off_pst_lo) : nullptr, pl.T8, pl.ld_t,
-               reinterpret_cast<float*>(ws + pl.off_dpart), pl.s_down_x};
+               reinterpret_cast<float*>(ws + pl.off_dpart), pl.s_down_x, ScalesJob{}};
     return down(a, s, f16);
 }
 
-// s dY B^T -> G (hi/lo [T][r_pad] and transposed)
+// s dY B^T -> G (hi/lo [T][r_pad] and transposed); `scales` (if not NULL) runs
+// as extra workgroups of the same launch.
 hipError_t launch_lora_down_dy(const uint16_t* dy, const uint16_t* lora_b, float scaling, const LoraPlan& pl,
-                               uint8_t* ws, bool transposed, hipStream_t s, bool f16) {
+                               uint8_t* ws, bool transposed, hipStream_t s, bool f16, const ScalesJob* scales) {
     DownArgs a{dy, lora_b, pl.T, pl.N, pl.N, pl.r, pl.r_pad, scaling,
                reinterpret_cast<uint16_t*>(ws + pl.off_gs_hi), reinterpret_cast<uint16_t*>(ws + pl.off_gs_lo),
                transposed ? reinterpret_cast<uint16_t*>(ws + pl.off_gst_hi) : nullptr,
                transposed ? reinterpret_cast<uint16_t*>(ws + pl.off_gst_lo) : nullptr, pl.T8, pl.ld_t,
-               reinterpret_cast<float*>(ws + pl.off_dpart), pl.s_down_dy};
+               reinterpret_cast<float*>(ws + pl.off_dpart), pl.s_down_dy, scales ? *scales : ScalesJob{}};
     return down(a, s, f16);
 }
 
@@ -531,18 +545,16 @@ hipError_t launch_lora_grads(const uint16_t* x, const uint16_t* dy, const LoraPl
     float* pdb = reinterpret_cast<float*>(ws + pl.off_pdb);
     GradFin fa{pda, pl.s_da, pl.K, pl.r_pad, pl.r, d_lora_a, 0};
     GradFin fb{pdb, pl.s_db, pl.N, pl.r_pad, pl.r, d_lora_b, 1};
-    if (d_lora_a) {
-        GradArgs g{x, reinterpret_cast<const uint16_t*>(ws + pl.off_gst_hi),
-                   reinterpret_cast<const uint16_t*>(ws + pl.off_gst_lo), pda, pl.T, pl.T8, pl.ld_t, pl.K, pl.r_pad,
-                   (int)ceil_div(pl.K, 128), pl.cpw_da};
-        hipError_t e = grad(g, pl.s_da, s, f16);
-        if (e != hipSuccess) return e;
-    }
-    if (d_lora_b) {
-        GradArgs g{dy, reinterpret_cast<const uint16_t*>(ws + pl.off_pst_hi),
-                   reinterpret_cast<const uint16_t*>(ws + pl.off_pst_lo), pdb, pl.T, pl.T8, pl.ld_t, pl.N, pl.r_pad,
-                   (int)ceil_div(pl.N, 128), pl.cpw_db};
-        hipError_t e = grad(g, pl.s_db, s, f16);
+    // dA and dB in one launch (either may be absent)
+    const GradArgs ga{x, reinterpret_cast<const uint16_t*>(ws + pl.off_gst_hi),
+                      reinterpret_cast<const uint16_t*>(ws + pl.off_gst_lo), pda, pl.T, pl.T8, pl.ld_t, pl.K,
+                      pl.r_pad, (int)ceil_div(pl.K, 128), pl.cpw_da};
+    const GradArgs gb{dy, reinterpret_cast<const uint16_t*>(ws + pl.off_pst_hi),
+                      reinterpret_cast<const uint16_t*>(ws + pl.off_pst_lo), pdb, pl.T, pl.T8, pl.ld_t, pl.N,
+                      pl.r_pad, (int)ceil_div(pl.N, 128), pl.cpw_db};
+    const int na = d_lora_a ? ga.cblocks * pl.s_da : 0, nb = d_lora_b ? gb.cblocks * pl.s_db : 0;
+    {
+        hipError_t e = na ? grad(ga, na, gb, nb, pl.r_pad, s, f16) : grad(gb, nb, gb, 0, pl.r_pad, s, f16);
         if (e != hipSuccess) return e;
     }
     const int ba = d_lora_a ? (int)ceil_div(pl.K, 16) : 0;
