@@ -39,14 +39,15 @@ EncodeTable g_table, g_int4_table;
 std::once_flag g_once;
 
 // Decision midpoints of neighbouring fp32 codewords (exact in fp64), then the
-// per-cell (base, threshold) lookup used by the encoder kernels.  Valid for any
-// ascending codebook on [-1, 1] whose neighbouring midpoints are more than 1/16
-// apart (NF4: at least 0.08; INT4: 1/7).
+// per-cell (base, threshold) lookup used by the encoder kernels.  Cell c is
+// [(c - 1/2)/16 - 1, (c + 1/2)/16 - 1), the values that round(16 n + 16)
+// sends to c.  Valid for any ascending codebook on [-1, 1] whose neighbouring
+// midpoints are more than 1/16 apart (NF4: at least 0.08; INT4: 1/7).
 void build_table(const Codebook& cb, EncodeTable& tab) {
     double mid[15];
     for (int i = 0; i < 15; ++i) mid[i] = 0.5 * ((double)cb.q[i] + (double)cb.q[i + 1]);
     for (int c = 0; c < 34; ++c) {
-        const double lo = c / 16.0 - 1.0, hi = (c + 1) / 16.0 - 1.0;
+        const double lo = (c - 0.5) / 16.0 - 1.0, hi = (c + 0.5) / 16.0 - 1.0;
         uint32_t base = 0;
         float thr = 2.0f;
         for (int i = 0; i < 15; ++i) {

@@ -20,10 +20,13 @@ struct Codebook {
     float q[16];
 };
 
-// Encoder lookup over n in [-1, 1]: cell = trunc(16 n + 16) in [0, 32]; the
-// code is base[cell] + (n > thr[cell]).  Each cell of width 1/16 holds at most
-// one decision midpoint (neighbouring midpoints are >= 0.08 apart), whose
-// round-down fp32 value is thr[cell] (cells without one carry thr = 2).
+// Encoder lookup over n in [-1, 1]: cell = round(16 n + 16) in [0, 32]; the
+// code is base[cell] + (n > thr[cell]), base[cell] counting the midpoints
+// below the cell.  Each cell of width 1/16 holds at most one decision midpoint
+// (neighbouring midpoints are >= 0.08 apart), whose round-down fp32 value is
+// thr[cell] (cells without one carry thr = 2).  A value exactly on a cell's
+// lower edge may be sent to the cell below (ties to even); the lookup there
+// gives the same code.
 struct EncodeTable {
     float thr[34];
     uint32_t base[34];

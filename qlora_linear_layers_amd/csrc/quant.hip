@@ -53,6 +53,7 @@ __global__ __launch_bounds__(256) void k_quantize(QuantGroup grp, EncodeTable ta
     const int64_t blk0 = (int64_t)gl * kGroup;
     const int nb = (int)((nblocks - blk0) < kGroup ? (nblocks - blk0) : kGroup);
     if (tid < 34) s_tab[tid] = make_uint2(__float_as_uint(tab.thr[tid]), tab.base[tid]);
+    const uint32_t tab_adj = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint2*)s_tab - 0x4B400000u * 8u;
 
     const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w + blk0 * kBlock);
     u32x4_t v[8];
@@ -101,10 +102,14 @@ __global__ __launch_bounds__(256) void k_quantize(QuantGroup grp, EncodeTable ta
         uint32_t out = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            int cell = (int)fmaf(n[e], 16.0f, 16.0f);
-            cell = min(max(cell, 0), 32);
-            const uint2 t = s_tab[cell];
-            const uint32_t code = t.y + (n[e] > __uint_as_float(t.x) ? 1u : 0u);
+            // cell = round(16 n + 16): one fma against 1.5 * 2^23, whose ulp is 1,
+            // leaves the rounded integer in the low mantissa bits; the table
+            // entry's LDS address is 8 * (bits - bits(1.5 * 2^23)) + the table's
+            // (|n| <= 1 + 2^-22 keeps the cell in [0, 32])
+            const uint32_t vb = __float_as_uint(fmaf(n[e], 16.0f, 12582928.0f));
+            const u32x2_t t = *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>(
+                (uintptr_t)(vb * 8u + tab_adj));
+            const uint32_t code = t[1] + (n[e] > __uint_as_float(t[0]) ? 1u : 0u);
             out |= code << ((e >> 1) * 8 + ((e & 1) ? 0 : 4));   // even element -> high nibble
         }
         if (lb < nb) {

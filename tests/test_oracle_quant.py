@@ -100,17 +100,18 @@ def test_reciprocal_encoding_margin_over_all_bf16_pairs():
 
 
 def test_encoder_cells_hold_one_midpoint_away_from_their_edges():
-    """The encoder's lookup: cell = trunc(16 n + 16) in [0, 32], code = base[cell]
-    + (n > thr[cell]).  It is exact if (1) every 1/16-wide cell holds at most one
-    midpoint and (2) no midpoint lies within the cell computation's error
-    (n's own 2^-22 plus the fma's rounding of 16 n + 16) of a cell edge k / 16,
-    so that a value landing in the neighbouring cell has no midpoint between it
-    and the edge."""
+    """The encoder's lookup: cell = round(16 n + 16) in [0, 32] (one fma against
+    1.5 * 2^23), code = base[cell] + (n > thr[cell]).  Cell c covers
+    [(c - 1/2)/16 - 1, (c + 1/2)/16 - 1).  The lookup is exact if every cell
+    holds at most one midpoint; the margin below (no midpoint within 2^-20 of a
+    cell edge) additionally keeps every code away from the edges, where a tie
+    may send a value to the cell below."""
     mids = oracle.nf4_midpoints().astype(np.float64)
     assert np.min(np.diff(mids)) > 1.0 / 16
-    edge_dist = np.abs(mids * 16 - np.rint(mids * 16)) / 16
+    pos = (mids + 1) * 16 - 0.5                      # edges sit at integer positions
+    edge_dist = np.abs(pos - np.rint(pos)) / 16
     assert np.min(edge_dist) > 2.0 ** -20
-    cells = np.floor(mids * 16 + 16).astype(int)
+    cells = np.floor((mids + 1) * 16 + 0.5).astype(int)
     assert np.unique(cells).size == mids.size
 
 
