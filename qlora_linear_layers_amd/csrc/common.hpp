@@ -259,21 +259,27 @@ struct BlockScales {
 // stored fp32 absmax with single quantization), [K/64][N] so that eight
 // consecutive rows of one block column are contiguous.  It runs as extra
 // workgroups of another launch (or alone): workgroup `b` of `blocks` writes
-// entries 256 b .. 256 b + 255 (n fastest).
+// entries kScalesPerBlock b .. + kScalesPerBlock - 1 (n fastest), eight per
+// thread, so that it adds few workgroups to the launch it rides on.
 struct ScalesJob {
     const uint8_t* fp8;
     const float* sup;
     const float* absmax;      // single quantization (fp8, sup unused)
     int64_t N, KB;
     float* out;
-    int blocks;               // ceil(N * KB / 256), 0 = no job
+    int blocks;               // ceil(N * KB / kScalesPerBlock), 0 = no job
 };
+constexpr int kScalesPerBlock = 8 * 256;
 QL_DEV void scales_job(const ScalesJob& j, int b) {
-    const int64_t i = (int64_t)b * 256 + threadIdx.x;
-    if (i >= j.N * j.KB) return;
-    const int64_t kb = i / j.N, n = i % j.N;
-    const int64_t blk = n * j.KB + kb;
-    j.out[i] = j.absmax ? j.absmax[blk] : block_scale(j.fp8[blk], j.sup[blk >> 8]);
+#pragma unroll
+    for (int e = 0; e < kScalesPerBlock / 256; ++e) {
+        const int64_t i = (int64_t)b * kScalesPerBlock + e * 256 + threadIdx.x;
+        if (i < j.N * j.KB) {
+            const int64_t kb = i / j.N, n = i % j.N;
+            const int64_t blk = n * j.KB + kb;
+            j.out[i] = j.absmax ? j.absmax[blk] : block_scale(j.fp8[blk], j.sup[blk >> 8]);
+        }
+    }
 }
 
 // One tensor of a grouped quantize or dequantize launch: `w` is read by the

@@ -834,7 +834,7 @@ hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, BlockScales sc, c
 
 ScalesJob scales_job_for(BlockScales sc, const LoraPlan& pl, uint8_t* ws) {
     return ScalesJob{sc.fp8, sc.sup, sc.absmax, pl.N, pl.K / 64, reinterpret_cast<float*>(ws + pl.off_scl),
-                     (int)ceil_div((pl.K / 64) * pl.N, 256)};
+                     (int)ceil_div((pl.K / 64) * pl.N, kScalesPerBlock)};
 }
 
 hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
