@@ -398,12 +398,13 @@ def weight_copies(api, qws, copies=6):
 DECODE_STAGES = ((0, 1, 2), (3,), (4, 5), (6,))    # q/k/v, o, gate/up, down: what a decode step can group
 
 
-def measure_decode(api, torch, layers, sets, r, s, tokens=(1, 4, 8), reps=10, mode="single"):
+def measure_decode(api, torch, layers, sets, r, s, tokens=(1, 4, 8), reps=10, mode="single", product=None):
     """Decode-size forward over the seven linears, one weight copy per pass.
     mode "single": one qlora_linear_fwd per linear; "staged": one grouped call
     per dependency stage (q/k/v, o, gate/up, down); "all": one grouped call for
-    all seven.  A GPU spin ahead of the timed region lets the host enqueue every
-    pass first, so the events see device time only.
+    all seven.  `product` ("mfma", "valu" or None for the library's choice)
+    applies to the grouped modes.  A GPU spin ahead of the timed region lets the
+    host enqueue every pass first, so the events see device time only.
     Returns {T: (seconds per layer set, bytes per layer set)}."""
     copies = len(sets)
     out = {}
@@ -429,7 +430,7 @@ def measure_decode(api, torch, layers, sets, r, s, tokens=(1, 4, 8), reps=10, mo
             else:
                 for st in stages:
                     api.qlora_linear_fwd_grouped([(xs[i], sets[c][i], a[i], b[i], s, ys[i]) for i in st],
-                                                 workspace=ws)
+                                                 workspace=ws, product=product)
         for c in range(copies):
             one(c)
         torch.cuda.synchronize()
@@ -657,8 +658,10 @@ def only_component(name, api, torch, synth, calib, args):
         g = torch.Generator(device="cuda").manual_seed(1)
         qws = [api.nf4_quantize_dq(torch.randn((l.N, l.K), generator=g, device="cuda").mul_(0.02)
                                    .to(torch.bfloat16)) for l in layers7]
-        mode = {"decode": "staged", "decode_single": "single", "decode_all7": "all"}[name]
-        res = measure_decode(api, torch, layers7, weight_copies(api, qws), r, s, mode=mode)
+        mode = {"decode": "staged", "decode_single": "single", "decode_all7": "all", "decode_valu": "staged",
+                "decode_all7_valu": "all", "decode_mfma": "staged", "decode_all7_mfma": "all"}[name]
+        product = "valu" if name.endswith("_valu") else "mfma" if name.endswith("_mfma") else None
+        res = measure_decode(api, torch, layers7, weight_copies(api, qws), r, s, mode=mode, product=product)
         return {f"T{Td}": {"GB/s": round(nb / secs / 1e9, 1), "us_per_layer_set": round(1e6 * secs, 2)}
                 for Td, (secs, nb) in res.items()}
     if name == "single_layer":
@@ -689,7 +692,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline step and the roofline kernel (for a kernel trace of the step alone)")
-    ap.add_argument("--only", choices=("decode", "decode_single", "decode_all7", "single_layer", "train_7b",
+    ap.add_argument("--only", choices=("decode", "decode_single", "decode_all7", "decode_valu", "decode_all7_valu",
+                                       "decode_mfma", "decode_all7_mfma", "single_layer", "train_7b",
                                        "merge", "calibration", "stream_70b"),
                     help="run one component alone (no step, roofline loop or CPU baseline), e.g. for a kernel trace")
     ap.add_argument("--roofline-only", action="store_true",
@@ -799,14 +803,20 @@ def main():
         notes = {"single": "one launch pair per linear",
                  "staged": "grouped launches per dependency stage: q/k/v, o, gate/up, down",
                  "all": "all 7 linears in one grouped launch pair (independent inputs)"}
-        for mode, prefix in (("staged", "decode"), ("single", "decode_single"), ("all", "decode_all7")):
-            for Td, (secs, nbytes) in measure_decode(api, torch, layers7, sets, r7, s7, mode=mode).items():
+        products = {None: "the library's decode product for T", "mfma": "small-M MFMA (16x16x32) product",
+                    "valu": "VALU dot-product form (v_dot2, no MFMA)"}
+        for mode, prefix, product in (("staged", "decode", None), ("single", "decode_single", None),
+                                      ("all", "decode_all7", None), ("staged", "decode_mfma", "mfma"),
+                                      ("all", "decode_all7_mfma", "mfma"), ("staged", "decode_valu", "valu"),
+                                      ("all", "decode_all7_valu", "valu")):
+            for Td, (secs, nbytes) in measure_decode(api, torch, layers7, sets, r7, s7, mode=mode,
+                                                     product=product).items():
                 comp[f"{prefix}_T{Td}"] = {
                     "GB/s": round(nbytes / secs / 1e9, 1), "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
                     "frac_of_measured_peak": round(nbytes / secs / calib_res["copy_B/s"], 4),
                     "us_per_layer_set": round(1e6 * secs, 2),
-                    "note": "7 linears, fused dequant + small-M MFMA (16x16x32) incl. LoRA; " + notes[mode]
-                            + "; weights rotated over 6 copies"}
+                    "note": "7 linears, fused NF4 double dequant + " + products[product] + " incl. LoRA; "
+                            + notes[mode] + "; weights rotated over 6 copies"}
         for name, (kind, secs, amt) in measure_sq(api, torch, bufs7, synth.TRAIN_7B["T"], r7, s7, ws7).items():
             comp[name] = phase_entry(kind, amt, None, secs)
             comp[name]["note"] = "single quantization (fp32 absmax per 64 weights), 7B layer set, T=4096"

@@ -349,6 +349,27 @@ int qlora_linear_fwd_grouped(int count, const qlora_linear_problem* problems, in
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qlora_linear_fwd_grouped_ex - qlora_linear_fwd_grouped with the decode
+ *   product chosen by the caller.  The layer and its dequantized weights are
+ *   those above ("QLoRA 原理精讲" section 2.2; Volcengine article section 3.4);
+ *   the weight stream, blocks and dequantization are the same in both forms,
+ *   only the multiply-add of the dequantized bf16 weights with X differs:
+ *     QLORA_DECODE_MFMA  matrix cores, X padded to 16 token rows;
+ *     QLORA_DECODE_VALU  vector dot products (v_dot2 of two bf16 pairs into
+ *                        fp32), no matrix-core instruction; T <= 8;
+ *     0                  the library's choice for T (what
+ *                        qlora_linear_fwd_grouped and qlora_linear_fwd use).
+ *   The two forms sum in different orders, so their outputs may differ in the
+ *   last bits; each is deterministic.
+ *   Errors: those of qlora_linear_fwd_grouped, and QLORA_ERR_VALUE for any
+ *   other flags value or QLORA_DECODE_VALU with T > 8.
+ */
+#define QLORA_DECODE_MFMA 1u
+#define QLORA_DECODE_VALU 2u
+int qlora_linear_fwd_grouped_ex(int count, const qlora_linear_problem* problems, int64_t T, int64_t r,
+                                unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * qlora_linear_fwd_noalloc - qlora_linear_fwd for callers that cannot
  *   allocate device memory (code under HIP graph capture, tight serving
  *   loops, harnesses that forbid hipMalloc): the same computation, kernels and

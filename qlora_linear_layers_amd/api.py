@@ -57,6 +57,10 @@ _SIGS["qlora_grouped_workspace_bytes"] = (ctypes.c_size_t, [ctypes.c_int, ctypes
                                                             _c_i64])
 _SIGS["qlora_linear_fwd_grouped"] = (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(LinearProblem), _c_i64, _c_i64,
                                                     _c_p, ctypes.c_size_t, _c_p])
+_SIGS["qlora_linear_fwd_grouped_ex"] = (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(LinearProblem), _c_i64, _c_i64,
+                                                       ctypes.c_uint, _c_p, ctypes.c_size_t, _c_p])
+QLORA_DECODE_MFMA = 1
+QLORA_DECODE_VALU = 2
 
 
 class NF4Tensor(ctypes.Structure):
@@ -445,19 +449,28 @@ def qlora_grouped_workspace_bytes(problems):
     return int(lib().qlora_grouped_workspace_bytes(len(problems), arr, T, r))
 
 
-def qlora_linear_fwd_grouped(problems, workspace=None):
+def qlora_linear_fwd_grouped(problems, workspace=None, product=None):
     """Decode forward of up to 8 independent layers in one launch pair.  Each
     problem is (x [T, K] bf16, NF4Weight, lora_a or None, lora_b or None,
     scaling, out [T, N] bf16); every problem has the same T (<= 16) and rank.
-    Writes each out exactly as qlora_linear_fwd would."""
+    Writes each out exactly as qlora_linear_fwd would.  `product` None keeps
+    the library's choice; "mfma" or "valu" (T <= 8) picks the decode product
+    (qlora_linear_fwd_grouped_ex)."""
+    flags = {None: 0, "mfma": QLORA_DECODE_MFMA, "valu": QLORA_DECODE_VALU}.get(product)
+    if flags is None:
+        raise ValueError(f"product must be None, 'mfma' or 'valu', not {product!r}")
     T = problems[0][0].shape[0]
     r = 0 if problems[0][2] is None else problems[0][2].shape[1]
     arr = _grouped_array(problems, T, r)
     if workspace is None:
         n = int(lib().qlora_grouped_workspace_bytes(len(problems), arr, T, r))
         workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=problems[0][0].device)
-    _check("qlora_linear_fwd_grouped", lib().qlora_linear_fwd_grouped(
-        len(problems), arr, T, r, _ptr(workspace), workspace.numel(), _stream()))
+    if flags:
+        _check("qlora_linear_fwd_grouped_ex", lib().qlora_linear_fwd_grouped_ex(
+            len(problems), arr, T, r, flags, _ptr(workspace), workspace.numel(), _stream()))
+    else:
+        _check("qlora_linear_fwd_grouped", lib().qlora_linear_fwd_grouped(
+            len(problems), arr, T, r, _ptr(workspace), workspace.numel(), _stream()))
     return [pr[5] for pr in problems]
 
 

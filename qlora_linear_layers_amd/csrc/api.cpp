@@ -464,15 +464,25 @@ size_t qlora_grouped_workspace_bytes(int count, const qlora_linear_problem* prob
     return ql::gemv_group_workspace(g, count, T, r > 0 ? ql::ceil_div(r, 64) * 64 : 0);
 }
 
-int qlora_linear_fwd_grouped(int count, const qlora_linear_problem* problems, int64_t T, int64_t r,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+int qlora_linear_fwd_grouped_ex(int count, const qlora_linear_problem* problems, int64_t T, int64_t r,
+                                unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
     ql::GemvProblem g[ql::kMaxGroup];
     if (int st = grouped_problems(count, problems, T, r, g)) return st;
+    ql::DecodeProduct prod = ql::DecodeProduct::Auto;
+    if (flags == QLORA_DECODE_MFMA) prod = ql::DecodeProduct::Mfma;
+    else if (flags == QLORA_DECODE_VALU) prod = ql::DecodeProduct::Valu;
+    else if (flags != 0) return QLORA_ERR_VALUE;
+    if (prod == ql::DecodeProduct::Valu && T > ql::kGemvValuMaxT) return QLORA_ERR_VALUE;
     if (workspace && !aligned16(workspace)) return QLORA_ERR_ALIGN;
     const size_t need = ql::gemv_group_workspace(g, count, T, r > 0 ? ql::ceil_div(r, 64) * 64 : 0);
     if (!workspace || workspace_bytes < need) return QLORA_ERR_WORKSPACE;
     return dev(ql::launch_gemv_group(g, count, T, r, static_cast<uint8_t*>(workspace),
-                                     static_cast<hipStream_t>(stream), false));
+                                     static_cast<hipStream_t>(stream), false, prod));
+}
+
+int qlora_linear_fwd_grouped(int count, const qlora_linear_problem* problems, int64_t T, int64_t r,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    return qlora_linear_fwd_grouped_ex(count, problems, T, r, 0u, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -67,7 +67,7 @@ QL_DEV uint32_t pack_bf16x2(float a, float b) {
 //
 // The layer computes in bf16, or in fp16 when F16 (the compute dtype the pages
 // tell users to switch to on GPUs without bf16, "QLoRA 原理精讲" section 3,
-// pitfall 4).  Only packing, unpacking and the MFMA opcode depend on it; a
+// pitfall 4).  Only packing, unpacking and the MFMA and dot opcodes depend on it; a
 // 16-byte fragment travels as bf16x8_t bits either way.
 template <bool F16>
 QL_DEV uint32_t pack16x2(float a, float b) {     // RNE, `a` in the low half
@@ -87,6 +87,15 @@ template <bool F16>
 QL_DEV float hi16(uint32_t v) {
     if constexpr (F16) return (float)__builtin_bit_cast(f16x2_t, v)[1];
     else return bf16hi(v);
+}
+// c + a.lo * b.lo + a.hi * b.hi on the VALU (v_dot2c_f32_bf16 / _f16), fp32 accumulate
+template <bool F16>
+QL_DEV float dot16x2(uint32_t a, uint32_t b, float c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+    else
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                               false);
 }
 template <bool F16>
 QL_DEV f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -353,7 +362,11 @@ struct GemvProblem {
     int64_t skip = 0;     // leading token rows computed but not written (another problem writes them)
 };
 size_t gemv_group_workspace(const GemvProblem* probs, int count, int64_t T, int64_t r_pad);
+// The decode product: on the matrix cores (16 token rows, padded) or as VALU
+// dot products (T <= kGemvValuMaxT); Auto is the library's choice per T.
+enum class DecodeProduct { Auto, Mfma, Valu };
+constexpr int64_t kGemvValuMaxT = 8;
 hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int64_t r, uint8_t* ws, hipStream_t s,
-                             bool f16);
+                             bool f16, DecodeProduct prod = DecodeProduct::Auto);
 
 }  // namespace ql

@@ -74,6 +74,7 @@ constexpr int kDecThreads = 64 * kKW * kRG;
 constexpr int kDecRows = 64 * kRG;  // W rows per workgroup
 constexpr int kDecK = 128 * kKW;    // k per workgroup
 static_assert(kRG * kKW * 4 * 64 * 16 <= (int)kWideTableBytes, "wave sums must fit over the pair table");
+static_assert(kRG * kKW * 4 * 8 * 64 * 4 <= (int)kWideTableBytes, "VALU wave sums (8 tokens) must fit too");
 constexpr int kLoraSlice = 256;   // k per LoRA down-projection workgroup (one 64-k chunk per wave)
 constexpr size_t kDecLds = kWideTableBytes;   // pair table; later reused for the wave sums
 
@@ -147,8 +148,22 @@ __device__ __forceinline__ void lora_down_block(const GemvArgs& p, uint8_t* dyn,
 // Launch 1.  Blocks [0, gemv_blocks) are base blocks: rows [n0, n0 + 128) over
 // the k split ks (512 k); the rest are LoRA down-projection blocks.  SQ: the
 // block constant is the stored fp32 absmax (single quantization).
-template <int TT, bool SQ, bool F16>
+//
+// DOT: the same blocks, loads and dequantization with the product on the VALU
+// instead of the matrix cores (TT <= 8).  Per code byte and token one
+// v_dot2c_f32_bf16 adds the two dequantized weights times the two X values to
+// an fp32 sum per (W row, token); the four lane groups of a row (k 32g .. +31)
+// and the k waves are added in LDS, lane group inside wave, in that order.
+// Up to 4 tokens a lane holds the X of every token for its 32 k in registers
+// (TT x 16); above that the workgroup's X [TT][512] is staged in LDS behind
+// the pair table and read per 8-k sub-step (TT x 4 registers), which keeps the
+// occupancy of the MFMA form.  Per weight this adds T/2 VALU instructions to
+// the two of the dequantization, where the MFMA form adds a quarter of an
+// MFMA whatever T is.
+template <int TT, bool SQ, bool F16, bool DOT>
 __global__ __launch_bounds__(kDecThreads) void k_gemv(GemvGroup grp, Codebook cb) {
+    static_assert(!DOT || TT <= kGemvValuMaxT, "VALU product: up to 8 tokens");
+    constexpr bool LX = DOT && TT > 4;                                 // X staged in LDS
     extern __shared__ __align__(16) uint8_t dyn[];
     const int bid = (int)blockIdx.x;
     const int lora_total = grp.lora_end[grp.count - 1];
@@ -177,8 +192,10 @@ __global__ __launch_bounds__(kDecThreads) void k_gemv(GemvGroup grp, Codebook cb
     const rsrc_t rx = make_rsrc(p.x, p.T * p.K * 2);
 
     // every load of the wave first: 16 code bytes, the FP8 constant and the
-    // super-scale of four rows, and the lane's 32 k of X (token nl)
-    u32x4_t cw[4], xv[4];
+    // super-scale of four rows, and the lane's 32 k of X (MFMA: token nl;
+    // VALU: every token)
+    constexpr int XT = DOT && !LX ? TT : 1;
+    u32x4_t cw[4], xv[XT][4];
     uint32_t f8[4], s2[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -194,34 +211,110 @@ __global__ __launch_bounds__(kDecThreads) void k_gemv(GemvGroup grp, Codebook cb
             s2[c] = bload4(rs, ok ? (uint32_t)(blk >> 8) * 4u : kOOB, 0);
         }
     }
-    const bool xok = kok && nl < p.T;
+    lds8_t* xl = tbl + kWideTableBytes;                                // LX: X [TT][kDecK] bf16
+    if constexpr (LX) {
+        // one 16-byte piece of X [TT][512] per thread (TT * 64 pieces <= 512 threads)
+        const int t = (int)threadIdx.x / (kDecK / 8), pc = (int)threadIdx.x % (kDecK / 8);
+        const int64_t kx = (int64_t)ks * kDecK + 8 * pc;
+        if (t < TT) {
+            const u32x4_t v = bload16(rx, (t < p.T && kx < p.K) ? (uint32_t)((t * p.K + kx) * 2) : kOOB, 0);
+            *reinterpret_cast<lds_u32x4_t*>(xl + (t * kDecK + 8 * pc) * 2) = v;
+        }
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xv[j] = bload16(rx, xok ? (uint32_t)((nl * p.K + kk + 8 * j) * 2) : kOOB, 0);
+        for (int t = 0; t < XT; ++t) {
+            const int tx = DOT ? t : nl;
+            const bool xok = kok && tx < p.T;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                xv[t][j] = bload16(rx, xok ? (uint32_t)((tx * p.K + kk + 8 * j) * 2) : kOOB, 0);
+        }
+    }
     if (threadIdx.x < 256) build_wide_pair_table(tbl, cb);
     __syncthreads();
 
     const uint32_t lane8 = lds_addr(tbl) + (uint32_t)(lane & 31) * 8u;   // table at LDS address 0
-    f32x4_t acc[4];
+    // address bytes of a pair lookup: [0] lane copy, [1] code byte b, [2..3] table base
+    auto dequant4 = [&](uint32_t codes4, float c1p) {
+        u32x4_t w;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        const float c1p = SQ ? __uint_as_float(s2[c]) : block_scale(f8[c], __uint_as_float(s2[c]));
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t addr = __builtin_amdgcn_perm(codes4, lane8, 0x03020000u | ((4u + b) << 8));
+            const f32x2_t q = *lds_at<f32x2_t>(addr);
+            w[b] = pack16x2<F16>(__fmul_rn(q[0], c1p), __fmul_rn(q[1], c1p));
+        }
+        return w;
+    };
+    f32x4_t acc[4];
+    float dacc[4][DOT ? TT : 1];
+    if constexpr (DOT) {
+        float c1p[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            c1p[c] = SQ ? __uint_as_float(s2[c]) : block_scale(f8[c], __uint_as_float(s2[c]));
+#pragma unroll
+            for (int t = 0; t < TT; ++t) dacc[c][t] = 0.0f;
+        }
+        // sub-step j (k kk + 8j .. +7) of every row tile: X of every token, then
+        // per tile the four code bytes' weights and their dot products
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            u32x4_t w;
+            u32x4_t xj[TT];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                // address bytes: [0] lane copy, [1] code byte b, [2..3] table base
-                const uint32_t addr = __builtin_amdgcn_perm(cw[c][j], lane8, 0x03020000u | ((4u + b) << 8));
-                const f32x2_t q = *lds_at<f32x2_t>(addr);
-                w[b] = pack16x2<F16>(__fmul_rn(q[0], c1p), __fmul_rn(q[1], c1p));
+            for (int t = 0; t < TT; ++t) {
+                if constexpr (LX)
+                    xj[t] = *reinterpret_cast<const lds_u32x4_t*>(xl + (t * kDecK + 128 * wave + 32 * g + 8 * j) * 2);
+                else
+                    xj[t] = xv[t < XT ? t : 0][j];
             }
-            acc[c] = mfma16x16x32<F16>(__builtin_bit_cast(bf16x8_t, xv[j]), __builtin_bit_cast(bf16x8_t, w), acc[c]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const u32x4_t w = dequant4(cw[c][j], c1p[c]);
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) dacc[c][t] = dot16x2<F16>(w[b], xj[t][b], dacc[c][t]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            const float c1p = SQ ? __uint_as_float(s2[c]) : block_scale(f8[c], __uint_as_float(s2[c]));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[c] = mfma16x16x32<F16>(__builtin_bit_cast(bf16x8_t, xv[0][j]),
+                                           __builtin_bit_cast(bf16x8_t, dequant4(cw[c][j], c1p)), acc[c]);
         }
     }
 
     // the k waves of a row group meet in LDS (over the table), in wave order
     __syncthreads();
+    if constexpr (DOT) {
+        // [kRG][kKW waves][4 tiles][TT tokens][64 lanes]; lane 16g + i holds
+        // row 16c + i over k 32g .. 32g + 31
+        float* redf = reinterpret_cast<float*>(dyn) + rg * (kKW * 4 * TT * 64);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int t = 0; t < TT; ++t) redf[((wave * 4 + c) * TT + t) * 64 + lane] = dacc[c][t];
+        __syncthreads();
+        if (wave < 4) {
+            // thread (rg, c, l): row 16c + (l & 15) of tile c, tokens l / 16, l / 16 + 4
+            const int c = wave, i = lane & 15;
+            const int64_t n = n0 + 16 * c + i;
+#pragma unroll
+            for (int t = lane >> 4; t < TT; t += 4) {
+                float v = redf[(c * TT + t) * 64 + i];
+#pragma unroll
+                for (int w = 0; w < kKW; ++w)
+#pragma unroll
+                    for (int g2 = (w == 0 ? 1 : 0); g2 < 4; ++g2) v += redf[((w * 4 + c) * TT + t) * 64 + 16 * g2 + i];
+                if (t < p.T && n < p.N) p.part[((int64_t)ks * p.T + t) * p.N + n] = v;
+            }
+        }
+        return;
+    }
     f32x4_t* red = reinterpret_cast<f32x4_t*>(dyn) + rg * (kKW * 4 * 64);   // [kKW waves][4 tiles][64 lanes]
 #pragma unroll
     for (int c = 0; c < 4; ++c) red[(wave * 4 + c) * 64 + lane] = acc[c];
@@ -388,8 +481,10 @@ size_t gemv_group_workspace(const GemvProblem* probs, int count, int64_t T, int6
 }
 
 hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int64_t r, uint8_t* ws, hipStream_t s,
-                             bool f16) {
+                             bool f16, DecodeProduct prod) {
     if (count < 1 || count > kMaxGroup) return hipErrorInvalidValue;
+    if (prod == DecodeProduct::Valu && T > kGemvValuMaxT) return hipErrorInvalidValue;
+    const bool dot = prod == DecodeProduct::Valu;
     const int64_t r_pad = r > 0 ? ceil_div(r, 64) * 64 : 0;
     GemvGroup g{};
     g.count = count;
@@ -415,16 +510,25 @@ hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int
     const Codebook& cb = host_codebook();
     const dim3 grid((unsigned)(nl + nbase));
     hipError_t ae = hipSuccess;
+    size_t lds = kDecLds;
     auto go = [&](auto kern) {
-        // 64 KB of dynamic LDS: above the default limit
+        // 64 KB (and more) of dynamic LDS: above the default limit
         ae = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)kDecLds);
-        if (ae == hipSuccess) hipLaunchKernelGGL(kern, grid, dim3(kDecThreads), kDecLds, s, g, cb);
+                                 (int)lds);
+        if (ae == hipSuccess) hipLaunchKernelGGL(kern, grid, dim3(kDecThreads), lds, s, g, cb);
     };
     auto pick = [&](auto tt) {
         constexpr int TT = decltype(tt)::value;
-        if (sq) f16 ? go(k_gemv<TT, true, true>) : go(k_gemv<TT, true, false>);
-        else f16 ? go(k_gemv<TT, false, true>) : go(k_gemv<TT, false, false>);
+        if constexpr (TT <= kGemvValuMaxT) {
+            if (dot) {
+                if (TT > 4) lds += (size_t)TT * kDecK * 2;             // X staged behind the table
+                if (sq) f16 ? go(k_gemv<TT, true, true, true>) : go(k_gemv<TT, true, false, true>);
+                else f16 ? go(k_gemv<TT, false, true, true>) : go(k_gemv<TT, false, false, true>);
+                return;
+            }
+        }
+        if (sq) f16 ? go(k_gemv<TT, true, true, false>) : go(k_gemv<TT, true, false, false>);
+        else f16 ? go(k_gemv<TT, false, true, false>) : go(k_gemv<TT, false, false, false>);
     };
     if (T <= 1) pick(std::integral_constant<int, 1>{});
     else if (T <= 2) pick(std::integral_constant<int, 2>{});

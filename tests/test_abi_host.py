@@ -295,6 +295,18 @@ def test_grouped_validation(L):
     assert wb(2, _problems(2, {1: dict(N=100)}), 8, 16) == 0
 
 
+def test_grouped_product_validation(L):
+    f = L.qlora_linear_fwd_grouped_ex
+    big = 1 << 40
+    assert f(2, _problems(2), 8, 16, 3, FAKE, big, None) == VALUE          # unknown decode product
+    assert f(2, _problems(2), 8, 16, 1 << 31, FAKE, big, None) == VALUE
+    assert f(2, _problems(2), 9, 16, api.QLORA_DECODE_VALU, FAKE, big, None) == VALUE   # VALU product: T <= 8
+    assert f(2, _problems(2), 17, 16, api.QLORA_DECODE_MFMA, FAKE, big, None) == SHAPE
+    assert f(2, _problems(2, {1: dict(K=100)}), 8, 16, api.QLORA_DECODE_VALU, FAKE, big, None) == SHAPE
+    assert f(2, _problems(2), 8, 16, api.QLORA_DECODE_VALU, FAKE, 16, None) == WORKSPACE
+    assert f(2, _problems(2), 8, 16, api.QLORA_DECODE_MFMA, None, big, None) == WORKSPACE
+
+
 def _tensors(n, over=None):
     arr = (api.NF4Tensor * n)()
     for i in range(n):
