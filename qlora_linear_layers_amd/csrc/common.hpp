@@ -363,7 +363,8 @@ struct GemvProblem {
 };
 size_t gemv_group_workspace(const GemvProblem* probs, int count, int64_t T, int64_t r_pad);
 // The decode product: on the matrix cores (16 token rows, padded) or as VALU
-// dot products (T <= kGemvValuMaxT); Auto is the library's choice per T.
+// dot products (T <= kGemvValuMaxT; bf16 with double quantization); Auto is the
+// library's choice per T.
 enum class DecodeProduct { Auto, Mfma, Valu };
 constexpr int64_t kGemvValuMaxT = 8;
 hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int64_t r, uint8_t* ws, hipStream_t s,

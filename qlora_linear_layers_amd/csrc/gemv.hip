@@ -507,6 +507,7 @@ hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int
     for (int i = 0; i < count; ++i) g.base_end[i] = (i ? g.base_end[i - 1] : nl) + g.p[i].gemv_blocks;
     for (int i = count; i < kMaxGroup; ++i) g.lora_end[i] = g.base_end[i] = g.fin_end[i] = 0x7FFFFFFF;
     const bool sq = probs[0].sc.single();
+    if (dot && (sq || f16)) return hipErrorInvalidValue;             // the VALU form serves the bf16 DQ path
     const Codebook& cb = host_codebook();
     const dim3 grid((unsigned)(nl + nbase));
     hipError_t ae = hipSuccess;
@@ -520,10 +521,9 @@ hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int
     auto pick = [&](auto tt) {
         constexpr int TT = decltype(tt)::value;
         if constexpr (TT <= kGemvValuMaxT) {
-            if (dot) {
+            if (dot) {                                                 // double quantization, bf16 only
                 if (TT > 4) lds += (size_t)TT * kDecK * 2;             // X staged behind the table
-                if (sq) f16 ? go(k_gemv<TT, true, true, true>) : go(k_gemv<TT, true, false, true>);
-                else f16 ? go(k_gemv<TT, false, true, true>) : go(k_gemv<TT, false, false, true>);
+                go(k_gemv<TT, false, false, true>);
                 return;
             }
         }
