@@ -184,6 +184,12 @@ def test_65b_shapes_sampled(idx):
     _sampled(4, synth.LLAMA65B[idx], 2048, 64, 16.0 / 64)
 
 
+def test_65b_q_full():
+    """The 65B-shaped q projection (8192 x 8192, 32 x 8 output tiles in the XCD-remapped
+    order) at T = 2048 compared in full: every Y, dX, dA and dB element."""
+    _sampled(4, synth.LLAMA65B[0], 2048, 64, 16.0 / 64, full=True)
+
+
 def test_determinism():
     lin = synth.Linear("t", 512, 768)
     d = _inputs(9, lin, 300, 16)
