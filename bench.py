@@ -168,7 +168,7 @@ def run_step(torch, step, nev, steps, warmup):
     return time.perf_counter() - t0, all_events
 
 
-def layer_step(api, bufs, T, r, s, ws, stream, with_grads):
+def layer_step(api, bufs, T, r, s, ws, stream, with_grads, fused=False):
     """One step over the seven linears: grouped quantize, grouped dequantize, then
     per linear the forward and the backward (input gradient only, or with the LoRA
     gradients and s X A reused from the forward).  Event layout: [quantize start,
@@ -188,7 +188,7 @@ def layer_step(api, bufs, T, r, s, ws, stream, with_grads):
             if with_grads:
                 api.qlora_linear_bwd_input(b["dy"], b["qw"], b["a"], b["b"], s, x=b["x"], lora_grads=True,
                                            workspace=ws, dx=b["dx"], d_lora_a=b["da"], d_lora_b=b["db"],
-                                           reuse_forward=True)
+                                           reuse_forward=True, fused_grads=fused)
             else:
                 api.qlora_linear_bwd_input(b["dy"], b["qw"], b["a"], b["b"], s, workspace=ws, dx=b["dx"])
             if ev: ev[4 + 2 * li].record(stream)
@@ -217,19 +217,21 @@ def step_phases(bufs, all_events, steps, T, r, bwd_name, calib=None):
     return comp, roof
 
 
-def measure_train_7b(api, torch, synth, np, steps, calib):
+def measure_train_7b(api, torch, synth, np, steps, calib, fused=False):
     """The 7B training-shaped step (T = 4096, r = 64, alpha = 16): grouped quantize and
     dequantize, then forward and backward with dX, dA, dB (s X A kept from the forward)
-    for each of the seven linears.  Inputs from the host generators (the oracle's
-    bytes).  Returns (components of the phases, ms per step, step attainment)."""
+    for each of the seven linears; with `fused`, the backward forms dA and dB inside
+    the dX kernel (QLORA_BWD_FUSED_GRADS).  Inputs from the host generators (the
+    oracle's bytes).  Returns (components of the phases, ms per step, step attainment)."""
     cfg = synth.TRAIN_7B
     layers, T, r, s = cfg["layers"], cfg["T"], cfg["r"], cfg["scaling"]
 
     def dev(bits, shape):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).reshape(shape).cuda()
 
-    ws = torch.empty(max(api.qlora_workspace_bytes(T, l.K, l.N, r) for l in layers), dtype=torch.uint8,
-                     device="cuda")
+    flags = api.REUSE_FORWARD | (api.FUSED_GRADS if fused else 0)
+    ws = torch.empty(max(max(api.qlora_workspace_bytes(T, l.K, l.N, r), api.qlora_workspace_bytes_bwd(
+        T, l.K, l.N, r, flags)) for l in layers), dtype=torch.uint8, device="cuda")
     bufs = []
     for li, lin in enumerate(layers):
         d = synth.layer_inputs(cfg["config"], 0, li, lin, T, r, with_dy=True)
@@ -243,7 +245,7 @@ def measure_train_7b(api, torch, synth, np, steps, calib):
         b["db"] = torch.empty((r, lin.N), dtype=torch.bfloat16, device="cuda")
         bufs.append(b)
     torch.cuda.synchronize()
-    step, nev = layer_step(api, bufs, T, r, s, ws, torch.cuda.current_stream(), with_grads=True)
+    step, nev = layer_step(api, bufs, T, r, s, ws, torch.cuda.current_stream(), with_grads=True, fused=fused)
     wall, evs = run_step(torch, step, nev, steps, 3)
     comp, roof = step_phases(bufs, evs, steps, T, r, "backward", calib)
     return comp, 1e3 * wall / steps, roof / (wall / steps), bufs, ws
@@ -667,9 +669,9 @@ def only_component(name, api, torch, synth, calib, args):
     if name == "single_layer":
         return {k: {"GB/s": round(nb / secs / 1e9, 1), "us_per_launch": round(1e6 * secs, 3)}
                 for k, (kind, secs, amt, nb, _) in measure_single_layer(api, torch, synth).items()}
-    if name == "train_7b":
+    if name in ("train_7b", "train_7b_fused"):
         import numpy as np
-        comp, ms, att, _, _ = measure_train_7b(api, torch, synth, np, args.steps, None)
+        comp, ms, att, _, _ = measure_train_7b(api, torch, synth, np, args.steps, None, fused=name.endswith("fused"))
         return {"ms_per_step": round(ms, 4), "attainment": round(att, 4), "phases": comp}
     if name == "merge":
         g = torch.Generator(device="cuda").manual_seed(1)
@@ -693,7 +695,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline step and the roofline kernel (for a kernel trace of the step alone)")
     ap.add_argument("--only", choices=("decode", "decode_single", "decode_all7", "decode_valu", "decode_all7_valu",
-                                       "decode_mfma", "decode_all7_mfma", "single_layer", "train_7b",
+                                       "decode_mfma", "decode_all7_mfma", "single_layer", "train_7b", "train_7b_fused",
                                        "merge", "calibration", "stream_70b"),
                     help="run one component alone (no step, roofline loop or CPU baseline), e.g. for a kernel trace")
     ap.add_argument("--roofline-only", action="store_true",
@@ -797,6 +799,11 @@ def main():
         comp["train_7b"] = {"ms_per_step": round(ms7, 4), "attainment": round(att7, 4), "phases": c7,
                             "note": "LLaMA-7B-shaped layer, T=4096, r=64 alpha=16: quantize + dequantize (grouped) "
                                     "+ forward + backward (dX, dA, dB; s X A kept from the forward)"}
+        c7f, ms7f, att7f, bf, wsf = measure_train_7b(api, torch, synth, np, args.steps, calib_res, fused=True)
+        comp["train_7b_fused"] = {"ms_per_step": round(ms7f, 4), "attainment": round(att7f, 4), "phases": c7f,
+                                  "note": "the same step with the fused backward: dA and dB formed inside the dX "
+                                          "kernel (QLORA_BWD_FUSED_GRADS), 4 launches per linear instead of 5"}
+        del bf, wsf
         # config 2: decode, three launch patterns
         sets = weight_copies(api, [b["qw"] for b in bufs7])
         layers7, r7, s7 = synth.TRAIN_7B["layers"], synth.TRAIN_7B["r"], synth.TRAIN_7B["scaling"]

@@ -136,8 +136,10 @@ typedef struct nf4_tensor {
 int nf4_quantize_dq_grouped(int count, const nf4_tensor* tensors, void* stream);
 int nf4_dequantize_dq_grouped(int count, const nf4_tensor* tensors, void* stream);
 
-/* qlora_linear_bwd_input flag: reuse the forward's s X A (see below). */
+/* qlora_linear_bwd_input flags: reuse the forward's s X A; compute the
+ * adapter gradients in the dX kernel (see below). */
 #define QLORA_BWD_REUSE_FORWARD 1u
+#define QLORA_BWD_FUSED_GRADS 2u
 
 /*
  * qlora_workspace_bytes - device workspace (bytes) that qlora_linear_fwd and
@@ -157,6 +159,16 @@ size_t qlora_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r);
  *   up to T_max tokens.  Returns 0 for sizes the entry points would reject.
  */
 size_t qlora_workspace_bytes_upto(int64_t T_max, int64_t K, int64_t N, int64_t r);
+
+/*
+ * qlora_workspace_bytes_bwd - device workspace (bytes) that a
+ *   qlora_linear_bwd_input call with these flags needs when it computes the
+ *   adapter gradients (at least the forward's part, so the forward can use the
+ *   same workspace).  With QLORA_BWD_FUSED_GRADS this holds fp32 gradient
+ *   partials for every 256-token tile and can exceed qlora_workspace_bytes.
+ *   Returns 0 for sizes the entry points would reject or an unknown flag.
+ */
+size_t qlora_workspace_bytes_bwd(int64_t T, int64_t K, int64_t N, int64_t r, unsigned flags);
 
 /*
  * qlora_linear_fwd - fused forward of one QLoRA linear layer.
@@ -196,11 +208,21 @@ int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N,
  *   d_lora_a [K, r] and d_lora_b [r, N] bf16, written when non-NULL
  *   (must be NULL when r == 0).  Sizes as for qlora_linear_fwd.  The
  *   workspace is needed even when r == 0 (block scales are staged there).
- *   flags: 0, or QLORA_BWD_REUSE_FORWARD when `workspace` still holds what a
- *   qlora_linear_fwd with the same x, lora_a, scaling and sizes left there
- *   (nothing else used it since): s X A is then taken from it instead of
- *   being recomputed for dB.  Ignored for T <= 128 (the decode-kernel
- *   forward keeps nothing).  With a stale workspace the flag gives wrong dB.
+ *   flags: an OR of
+ *     QLORA_BWD_REUSE_FORWARD when `workspace` still holds what a
+ *       qlora_linear_fwd with the same x, lora_a, scaling and sizes left there
+ *       (nothing else used it since): s X A is then taken from it instead of
+ *       being recomputed for dB.  Ignored for T <= 128 (the decode-kernel
+ *       forward keeps nothing).  With a stale workspace the flag gives wrong
+ *       dB.
+ *     QLORA_BWD_FUSED_GRADS: dA and dB come from the dX kernel itself, each
+ *       of its workgroups adding the gradients of its 256-token tile after
+ *       its dX tile (dA over its own k columns, dB over an even share of N),
+ *       and one launch sums the tiles' fp32 partials in tile order; the
+ *       separate gradient pass over X and dY is gone.  dX is the same bits as
+ *       without the flag; dA and dB sum in another order (same tolerance).
+ *       The workspace must hold qlora_workspace_bytes_bwd(T, K, N, r, flags)
+ *       bytes.  Without d_lora_a and d_lora_b the flag changes nothing.
  *   Errors: NULL, SHAPE, ALIGN, VALUE (non-finite scaling, unknown flag),
  *   WORKSPACE, DEVICE.
  */

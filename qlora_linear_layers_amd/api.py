@@ -22,6 +22,7 @@ _SIGS = {
     "nf4_dequantize_dq": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_i64, _c_p, _c_p]),
     "qlora_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64]),
     "qlora_workspace_bytes_upto": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64]),
+    "qlora_workspace_bytes_bwd": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_uint]),
     "qlora_linear_fwd": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                         ctypes.c_float, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "qlora_linear_bwd_input": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
@@ -76,6 +77,7 @@ for _n in ("nf4_quantize_dq", "nf4_dequantize_dq", "qlora_linear_fwd", "qlora_li
 EXPORTS = tuple(_SIGS)
 
 REUSE_FORWARD = 1   # QLORA_BWD_REUSE_FORWARD
+FUSED_GRADS = 2     # QLORA_BWD_FUSED_GRADS
 
 _lib = None
 
@@ -359,6 +361,10 @@ def qlora_workspace_bytes_upto(T_max, K, N, r):
     return int(lib().qlora_workspace_bytes_upto(T_max, K, N, r))
 
 
+def qlora_workspace_bytes_bwd(T, K, N, r, flags):
+    return int(lib().qlora_workspace_bytes_bwd(T, K, N, r, flags))
+
+
 def workspace_for(T, K, N, r, device):
     n = qlora_workspace_bytes(T, K, N, r)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
@@ -475,10 +481,13 @@ def qlora_linear_fwd_grouped(problems, workspace=None, product=None):
 
 
 def qlora_linear_bwd_input(dy, qw, lora_a=None, lora_b=None, scaling=1.0, x=None, lora_grads=False,
-                           workspace=None, dx=None, d_lora_a=None, d_lora_b=None, reuse_forward=False):
+                           workspace=None, dx=None, d_lora_a=None, d_lora_b=None, reuse_forward=False,
+                           fused_grads=False):
     """dX (and dA, dB when lora_grads) for upstream gradient dy [T, N] bf16.  With
     reuse_forward, `workspace` must be the one the forward of the same x, A, scaling
-    just used (s X A is taken from it)."""
+    just used (s X A is taken from it).  With fused_grads the dX kernel also forms
+    dA and dB (QLORA_BWD_FUSED_GRADS); the workspace must then hold
+    qlora_workspace_bytes_bwd(T, K, N, r, flags) bytes."""
     if reuse_forward and workspace is None:
         raise ValueError("reuse_forward needs the forward's workspace")
     ct = _ct(dy, "dy")
@@ -512,15 +521,16 @@ def qlora_linear_bwd_input(dy, qw, lora_a=None, lora_b=None, scaling=1.0, x=None
     if lora_grads:
         _dev(d_lora_a, dy.dtype, "d_lora_a")
         _dev(d_lora_b, dy.dtype, "d_lora_b")
+    flags = (REUSE_FORWARD if reuse_forward else 0) | (FUSED_GRADS if fused_grads else 0)
     if workspace is None:
-        workspace = workspace_for(T, K, N, r, dy.device)
+        n = qlora_workspace_bytes_bwd(T, K, N, r, flags) if fused_grads else qlora_workspace_bytes(T, K, N, r)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dy.device)
     sc = _scale_args(qw)[1]
     fn = _entry("qlora_linear_bwd_input", ct, qw)
     _check(fn, getattr(lib(), fn)(
         _ptr(dy), T, K, N, _ptr(qw.codes), *sc, _ptr(lora_a), _ptr(lora_b),
         r, float(scaling), _ptr(dx), _ptr(x), _ptr(d_lora_a) if lora_grads else None,
-        _ptr(d_lora_b) if lora_grads else None, _ptr(workspace), workspace.numel(),
-        REUSE_FORWARD if reuse_forward else 0, _stream()))
+        _ptr(d_lora_b) if lora_grads else None, _ptr(workspace), workspace.numel(), flags, _stream()))
     return (dx, d_lora_a, d_lora_b) if lora_grads else (dx, None, None)
 
 
@@ -550,10 +560,11 @@ def qlora_linear_fwd_sq(x, qw, lora_a=None, lora_b=None, scaling=1.0, workspace=
 
 
 def qlora_linear_bwd_input_sq(dy, qw, lora_a=None, lora_b=None, scaling=1.0, x=None, lora_grads=False,
-                              workspace=None, dx=None, d_lora_a=None, d_lora_b=None, reuse_forward=False):
+                              workspace=None, dx=None, d_lora_a=None, d_lora_b=None, reuse_forward=False,
+                              fused_grads=False):
     assert isinstance(qw, NF4WeightSQ)
     return qlora_linear_bwd_input(dy, qw, lora_a, lora_b, scaling, x, lora_grads, workspace, dx, d_lora_a, d_lora_b,
-                                  reuse_forward)
+                                  reuse_forward, fused_grads)
 
 
 def qlora_merge_lora_sq(qw, lora_a=None, lora_b=None, scaling=1.0, out=None):

@@ -7,6 +7,7 @@
 
 #include "qlora.h"
 #include "common.hpp"
+#include "grad.hpp"
 #include "plan.hpp"
 
 namespace ql {
@@ -19,9 +20,13 @@ hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, BlockScales sc, c
                       const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s, bool f16);
 hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
                      const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s, bool f16,
-                     bool scales_ready);
+                     bool scales_ready, const FusedGrads* fused);
 hipError_t launch_lora_grads(const uint16_t* x, const uint16_t* dy, const LoraPlan& pl, uint8_t* ws,
                              uint16_t* d_lora_a, uint16_t* d_lora_b, hipStream_t s, bool f16);
+FusedGrads fused_grads_for(const uint16_t* x, const uint16_t* dy, const LoraPlan& pl, uint8_t* ws, bool da,
+                           bool db);
+hipError_t launch_fused_grads_finalize(const LoraPlan& pl, uint8_t* ws, uint16_t* d_lora_a, uint16_t* d_lora_b,
+                                       hipStream_t s, bool f16);
 }  // namespace ql
 
 static_assert(QLORA_MAX_GROUP == ql::kMaxGroup, "group size of the header and the kernels");
@@ -156,9 +161,11 @@ int bwd_impl(const uint16_t* dy, int64_t T, int64_t K, int64_t N, const uint8_t*
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return QLORA_ERR_ALIGN;
     if (!std::isfinite(scaling)) return QLORA_ERR_VALUE;
-    if (flags & ~(unsigned)QLORA_BWD_REUSE_FORWARD) return QLORA_ERR_VALUE;
+    if (flags & ~(unsigned)(QLORA_BWD_REUSE_FORWARD | QLORA_BWD_FUSED_GRADS)) return QLORA_ERR_VALUE;
     const ql::LoraPlan pl(T, K, N, r);
-    const size_t need = grads ? pl.bwd_grad_bytes : pl.bwd_bytes;   // > 0: the scale pre-pass needs room
+    const bool fused = grads && (flags & QLORA_BWD_FUSED_GRADS);
+    // > 0 in every case: the scale pre-pass needs room
+    const size_t need = grads ? (fused ? pl.bwd_fused_bytes : pl.bwd_grad_bytes) : pl.bwd_bytes;
     // s X A from the forward's workspace (only the MFMA forward, T > kChunkMaxT, leaves it there)
     const bool reuse = (flags & QLORA_BWD_REUSE_FORWARD) && T > ql::kChunkMaxT;
     if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
@@ -170,12 +177,23 @@ int bwd_impl(const uint16_t* dy, int64_t T, int64_t K, int64_t N, const uint8_t*
         const ql::ScalesJob sj = ql::scales_job_for(sc, pl, ws);
         if (int st = dev(ql::launch_lora_down_dy(dy, lora_b, scaling, pl, ws, grads, s, f16, &sj))) return st;
     }
-    if (int st = dev(ql::launch_dx(dy, codes, sc, lora_a, pl, ws, dx, s, f16, r > 0))) return st;
+    // s X A (both layouts) for dB when the forward's is not reused
+    auto recompute_p = [&]() -> int {
+        if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
+        return dev(ql::launch_lora_down_x(x, scaling, pl, ws, true, s, f16));
+    };
+    if (fused) {
+        // dX, and the gradient partials of each 256-token tile, from one k_dx launch
+        if (!reuse)
+            if (int st = recompute_p()) return st;
+        const ql::FusedGrads fz = ql::fused_grads_for(x, dy, pl, ws, d_lora_a != nullptr, d_lora_b != nullptr);
+        if (int st = dev(ql::launch_dx(dy, codes, sc, lora_a, pl, ws, dx, s, f16, true, &fz))) return st;
+        return dev(ql::launch_fused_grads_finalize(pl, ws, d_lora_a, d_lora_b, s, f16));
+    }
+    if (int st = dev(ql::launch_dx(dy, codes, sc, lora_a, pl, ws, dx, s, f16, r > 0, nullptr))) return st;
     if (grads) {
-        if (!reuse) {
-            if (int st = dev(ql::launch_transpose_a(lora_a, pl, ws, s))) return st;
-            if (int st = dev(ql::launch_lora_down_x(x, scaling, pl, ws, true, s, f16))) return st;
-        }
+        if (!reuse)
+            if (int st = recompute_p()) return st;
         if (int st = dev(ql::launch_lora_grads(x, dy, pl, ws, d_lora_a, d_lora_b, s, f16))) return st;
     }
     return QLORA_OK;
@@ -359,6 +377,13 @@ size_t qlora_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r) {
         if (g > n) n = g;
     }
     return n;
+}
+
+size_t qlora_workspace_bytes_bwd(int64_t T, int64_t K, int64_t N, int64_t r, unsigned flags) {
+    if (check_linear_shape(T, K, N, r) != QLORA_OK) return 0;
+    if (flags & ~(unsigned)(QLORA_BWD_REUSE_FORWARD | QLORA_BWD_FUSED_GRADS)) return 0;
+    const ql::LoraPlan pl(T, K, N, r);
+    return (flags & QLORA_BWD_FUSED_GRADS) ? pl.bwd_fused_bytes : pl.bwd_grad_bytes;
 }
 
 size_t qlora_workspace_bytes_upto(int64_t T_max, int64_t K, int64_t N, int64_t r) {

@@ -20,6 +20,7 @@
 // PlainRows (bf16 rows contiguous along the reduction) or TransRows (bf16
 // stored with the reduction as the row index).  Outputs leave as bf16 rows.
 #include "common.hpp"
+#include "grad.hpp"
 #include "plan.hpp"
 
 namespace ql {
@@ -692,8 +693,8 @@ QL_DEV void dx_tile(DxPipe& pp, int kt, f32x16_t (&acc)[4][4], lds8_t* lW, lds8_
     pp.load_w(kt + 3, Q);                     // set Q (tile kt+1) is no longer read
 }
 
-template <bool F16>
-__global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
+template <bool F16, bool FUSED>
+__global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb, FusedGrads fz) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     lds8_t* smem = (lds8_t*)(smem_raw);
     constexpr uint32_t kTile = DxPipe::kTile;
@@ -800,6 +801,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb) {
                 otile_put4<F16>(smem, acc[i][j], g, wb * 128 + j * 32 + r, wa * 128 + i * 32 + g * 8 + h * 4);
     __syncthreads();
     otile_store(smem, p.dx, p.K, t0, k0, p.T, p.K);
+
+    if constexpr (FUSED) {
+        // the adapter gradients of this token tile: the blocks (column block x
+        // 64 ranks) of dA, then of dB, dealt to the four waves in turn; each
+        // wave sums its blocks over all 256 tokens and writes them itself
+        const int RB = (int)(p.r_pad / 64);
+        const int w = (int)(threadIdx.x >> 6);
+        const int na = fz.ga.part ? 2 * RB : 0;
+        int nb = 0;
+        if (fz.gb.part)
+            for (int cbn = ta; cbn < fz.gb.cblocks; cbn += fz.ktiles) nb += RB;
+#pragma unroll 1
+        for (int q = w; q < na + nb; q += 4) {
+            const bool first = q < na;
+            const int qq = first ? q : q - na;
+            const int cbx = first ? 2 * ta + qq / RB : ta + (qq / RB) * fz.ktiles;
+            const GradArgs g = first ? fz.ga : fz.gb;
+            if (cbx < g.cblocks) grad_wave<F16>(g, cbx, tb, (int64_t)(qq % RB) * 64);
+        }
+    }
 }
 
 constexpr size_t kDxSmem = 4 * 256 * 128 + kNarrowTableBytes;
@@ -839,7 +860,7 @@ ScalesJob scales_job_for(BlockScales sc, const LoraPlan& pl, uint8_t* ws) {
 
 hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,
                      const LoraPlan& pl, const uint8_t* ws, uint16_t* dx, hipStream_t s, bool f16,
-                     bool scales_ready) {
+                     bool scales_ready, const FusedGrads* fused) {
     const float* sclt = reinterpret_cast<const float*>(ws + pl.off_scl);
     if (!scales_ready) {
         const ScalesJob j = scales_job_for(sc, pl, const_cast<uint8_t*>(ws));
@@ -855,10 +876,12 @@ hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, BlockScales sc, c
     auto go = [&](auto kern) {
         hipError_t e = set_smem(kern, lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kThreads), lds, s, a, host_codebook());
+        hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kThreads), lds, s, a, host_codebook(),
+                           fused ? *fused : FusedGrads{});
         return hipGetLastError();
     };
-    return f16 ? go(k_dx<true>) : go(k_dx<false>);
+    if (fused) return f16 ? go(k_dx<true, true>) : go(k_dx<false, true>);
+    return f16 ? go(k_dx<true, false>) : go(k_dx<false, false>);
 }
 
 }  // namespace ql

@@ -19,15 +19,12 @@
 // transposed for k_grad.  A is transposed once per call by k_transpose so that
 // both down projections read the r-wide operand as rows.
 //
-// k_grad: the reduction runs over tokens, which index the rows of X and dY,
-// so their fragments need eight consecutive rows per lane: a lane loads an
-// 8 (t) x 8 (c) bf16 block with eight 16-byte loads and transposes it with 32
-// byte permutes into eight MFMA operands, one per column c.  A wave covers
-// 128 columns x 32 tokens per block; the workgroup's four waves take quarters
-// of its token range and are added in LDS in a fixed order; token ranges of
-// different workgroups produce fp32 partials that k_grad_finalize sums in
-// split order.  Every result is deterministic.
+// k_grad: the adapter-gradient block product of grad.hpp, one 128-column x
+// 64-rank block per workgroup; token ranges of different workgroups produce
+// fp32 partials that k_grad_finalize sums in split order.  Every result is
+// deterministic.
 #include "common.hpp"
+#include "grad.hpp"
 #include "plan.hpp"
 
 namespace ql {
@@ -280,116 +277,16 @@ __global__ __launch_bounds__(kThreads) void k_down_fin(DownArgs a) {
 
 // ------------------------------------------------------------------ adapter gradients
 
-struct GradArgs {
-    const uint16_t* s;       // [T][C] bf16 (X or dY)
-    const uint16_t* vt_hi;   // [r_pad][ldt] bf16 (G^T or P^T, hi and lo; tokens [0, T8))
-    const uint16_t* vt_lo;
-    float* part;             // [splits][C][r_pad] fp32
-    int64_t T, T8, ldt, C, r_pad;
-    int cblocks;             // ceil(C / 128)
-    int cpw;                 // 32-token chunks per wave
-};
-
-// part[split][c][j] = sum over the split's tokens of S[t][c] (V_hi + V_lo)[t][j]
-// for 128 columns c and 64 columns j (blockIdx.y picks the 64) per workgroup.
 // One launch serves both adapter gradients: workgroups [0, blocks0) take
-// problem a0 (dA = X^T G), the rest problem a1 (dB = P^T dY).
+// problem a0 (dA = X^T G), the rest problem a1 (dB = P^T dY); blockIdx.y
+// picks the 64 ranks.
 template <bool F16>
 __global__ __launch_bounds__(kThreads, 1) void k_grad(GradArgs a0, GradArgs a1, int blocks0) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
-    float* red = reinterpret_cast<float*>(smem_raw);     // [4 waves][8 i][4 jt][64 lanes][4]
     const bool second = (int)blockIdx.x >= blocks0;
     const GradArgs& a = second ? a1 : a0;
     const int bx = second ? (int)blockIdx.x - blocks0 : (int)blockIdx.x;
-    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int cb = bx % a.cblocks, split = bx / a.cblocks;
-    const int64_t j0 = (int64_t)blockIdx.y * 64;
-    const int64_t c0 = (int64_t)cb * 128 + 8 * (l & 15);          // this lane's 8 columns
-    const int64_t tw = ((int64_t)split * 4 + w) * 32 * a.cpw;      // first token of this wave
-    const int tl8 = 8 * (l >> 4);                                 // lane's token group in a chunk
-
-    const rsrc_t rs = make_rsrc(a.s, a.T * a.C * 2);
-    const rsrc_t rh = make_rsrc(a.vt_hi, a.r_pad * a.ldt * 2);
-    const rsrc_t rl = make_rsrc(a.vt_lo, a.r_pad * a.ldt * 2);
-    // workgroups of one split read the same V columns; each column block walks
-    // its chunks from its own starting point
-    const int rot = (int)(cb % a.cpw);
-    const bool cok = c0 < a.C;
-
-    f32x4_t acc[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) acc[i][jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-    u32x4_t xr[2][8], vh[2][4], vl[2][4];
-    auto load = [&](int ch, int slot) {
-        const bool live = ch < a.cpw;
-        int cr = live ? ch + rot : 0;
-        cr = cr >= a.cpw ? cr - a.cpw : cr;
-        const int64_t tc = tw + (int64_t)cr * 32 + tl8;           // first of the lane's 8 tokens
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int64_t t = tc + s;
-            xr[slot][s] = bload16(rs, (live && cok && t < a.T) ? (uint32_t)((t * a.C + c0) * 2) : kOOB, 0);
-        }
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            const int64_t j = j0 + jt * 16 + (l & 15);
-            const uint32_t vo = (live && tc < a.T8) ? (uint32_t)((j * a.ldt + tc) * 2) : kOOB;
-            vh[slot][jt] = bload16(rh, vo, 0);
-            vl[slot][jt] = bload16(rl, vo, 0);
-        }
-    };
-    auto compute = [&](int slot) {
-        // transpose the 8 x 8 block: operand i holds column c0 + i over the 8 tokens
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-            u32x4_t o;
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-                o[p] = __builtin_amdgcn_perm(xr[slot][2 * p + 1][i >> 1], xr[slot][2 * p][i >> 1], sel);
-            const bf16x8_t xi = as_bf16x8(o);
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                acc[i][jt] = mfma16<F16>(xi, as_bf16x8(vh[slot][jt]), acc[i][jt]);
-                acc[i][jt] = mfma16<F16>(xi, as_bf16x8(vl[slot][jt]), acc[i][jt]);
-            }
-        }
-    };
-    load(0, 0);
-    load(1, 1);
-    for (int ch = 0; ch < a.cpw; ch += 2) {
-        compute(0);
-        load(ch + 2, 0);
-        if (ch + 1 < a.cpw) compute(1);
-        load(ch + 3, 1);
-    }
-
-    // fixed-order sum of the four waves, then one fp32 partial per split
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-            *reinterpret_cast<f32x4_t*>(red + (((w * 8 + i) * 4 + jt) * 64 + l) * 4) = acc[i][jt];
-    __syncthreads();
-    // thread: one (operand i, rank tile jt, lane) slot, the four waves' float4s
-    // added in wave order; the float4 holds rows c = 8 (4 (lane / 16) + v) + i
-    float* out = a.part + (int64_t)split * a.C * a.r_pad;
-    const f32x4_t* red4 = reinterpret_cast<const f32x4_t*>(red);
-    for (int e = threadIdx.x; e < 8 * 4 * 64; e += kThreads) {
-        const int ll = e & 63, jt = (e >> 6) & 3, i = e >> 8;
-        f32x4_t s4 = red4[(i * 4 + jt) * 64 + ll];
-#pragma unroll
-        for (int ww = 1; ww < 4; ++ww) s4 += red4[((ww * 8 + i) * 4 + jt) * 64 + ll];
-        const int64_t j = j0 + jt * 16 + (ll & 15);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t c = (int64_t)cb * 128 + 8 * (4 * (ll >> 4) + v) + i;
-            if (c < a.C) out[c * a.r_pad + j] = s4[v];
-        }
-    }
+    grad_block<F16>(a, bx % a.cblocks, bx / a.cblocks, (int64_t)blockIdx.y * 64, reinterpret_cast<float*>(smem_raw));
 }
 
 // dA[k][j] (transpose = 0) or dB[j][n] (transpose = 1): RNE_bf16 of the
@@ -491,8 +388,6 @@ hipError_t down_t(const DownArgs& a, hipStream_t s) {
 
 hipError_t down(const DownArgs& a, hipStream_t s, bool f16) { return f16 ? down_t<true>(a, s) : down_t<false>(a, s); }
 
-constexpr size_t kGradSmem = (size_t)4 * 8 * 4 * 64 * 4 * 4;   // 128 KB
-
 // One k_grad launch over up to two problems (`n1` = 0: a0 alone).
 hipError_t grad(const GradArgs& a0, int n0, const GradArgs& a1, int n1, int64_t r_pad, hipStream_t s, bool f16) {
     auto go = [&](auto kern) {
@@ -503,6 +398,21 @@ hipError_t grad(const GradArgs& a0, int n0, const GradArgs& a1, int n1, int64_t 
         return hipGetLastError();
     };
     return f16 ? go(k_grad<true>) : go(k_grad<false>);
+}
+
+// One k_grad_finalize launch for dA (fa, when has_a) and dB (fb, when has_b).
+hipError_t grad_finalize(GradFin fa, bool has_a, const GradFin& fb, bool has_b, const LoraPlan& pl, hipStream_t s,
+                         bool f16) {
+    const int ba = has_a ? (int)ceil_div(pl.K, 16) : 0;
+    const int bb = has_b ? (int)ceil_div(pl.N, 16) : 0;
+    if (!has_a) fa = fb;                   // a single problem runs as the first one
+    if (f16)
+        hipLaunchKernelGGL(k_grad_finalize<true>, dim3((unsigned)(ba + bb)), dim3(256), 0, s, fa, fb,
+                           has_a ? ba : bb);
+    else
+        hipLaunchKernelGGL(k_grad_finalize<false>, dim3((unsigned)(ba + bb)), dim3(256), 0, s, fa, fb,
+                           has_a ? ba : bb);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -557,16 +467,33 @@ hipError_t launch_lora_grads(const uint16_t* x, const uint16_t* dy, const LoraPl
         hipError_t e = na ? grad(ga, na, gb, nb, pl.r_pad, s, f16) : grad(gb, nb, gb, 0, pl.r_pad, s, f16);
         if (e != hipSuccess) return e;
     }
-    const int ba = d_lora_a ? (int)ceil_div(pl.K, 16) : 0;
-    const int bb = d_lora_b ? (int)ceil_div(pl.N, 16) : 0;
-    if (!d_lora_a) fa = fb;                // a single problem runs as the first one
-    if (f16)
-        hipLaunchKernelGGL(k_grad_finalize<true>, dim3((unsigned)(ba + bb)), dim3(256), 0, s, fa, fb,
-                           d_lora_a ? ba : bb);
-    else
-        hipLaunchKernelGGL(k_grad_finalize<false>, dim3((unsigned)(ba + bb)), dim3(256), 0, s, fa, fb,
-                           d_lora_a ? ba : bb);
-    return hipGetLastError();
+    return grad_finalize(fa, d_lora_a != nullptr, fb, d_lora_b != nullptr, pl, s, f16);
+}
+
+// The fused backward's gradient problems: S = X against G^T for dA and S = dY
+// against P^T for dB, one 256-token tile (eight 32-token chunks of one wave)
+// per split, partials in the fused region of ws.
+FusedGrads fused_grads_for(const uint16_t* x, const uint16_t* dy, const LoraPlan& pl, uint8_t* ws, bool da,
+                           bool db) {
+    FusedGrads f{};
+    f.ktiles = (int)ceil_div(pl.K, 256);
+    if (da)
+        f.ga = GradArgs{x, reinterpret_cast<const uint16_t*>(ws + pl.off_gst_hi),
+                        reinterpret_cast<const uint16_t*>(ws + pl.off_gst_lo), reinterpret_cast<float*>(ws + pl.off_fza),
+                        pl.T, pl.T8, pl.ld_t, pl.K, pl.r_pad, (int)ceil_div(pl.K, 128), 8};
+    if (db)
+        f.gb = GradArgs{dy, reinterpret_cast<const uint16_t*>(ws + pl.off_pst_hi),
+                        reinterpret_cast<const uint16_t*>(ws + pl.off_pst_lo), reinterpret_cast<float*>(ws + pl.off_fzb),
+                        pl.T, pl.T8, pl.ld_t, pl.N, pl.r_pad, (int)ceil_div(pl.N, 128), 8};
+    return f;
+}
+
+// dA and dB from the fused backward's partials (one per 256-token tile).
+hipError_t launch_fused_grads_finalize(const LoraPlan& pl, uint8_t* ws, uint16_t* d_lora_a, uint16_t* d_lora_b,
+                                       hipStream_t s, bool f16) {
+    const GradFin fa{reinterpret_cast<const float*>(ws + pl.off_fza), pl.s_fz, pl.K, pl.r_pad, pl.r, d_lora_a, 0};
+    const GradFin fb{reinterpret_cast<const float*>(ws + pl.off_fzb), pl.s_fz, pl.N, pl.r_pad, pl.r, d_lora_b, 1};
+    return grad_finalize(fa, d_lora_a != nullptr, fb, d_lora_b != nullptr, pl, s, f16);
 }
 
 }  // namespace ql

@@ -52,7 +52,11 @@ struct LoraPlan {
     size_t off_gst_hi, off_gst_lo;      // G^T hi/lo, [r_pad][ld_t] each
     size_t off_pda, off_pdb;            // fp32 partials [s_da][K][r_pad], [s_db][N][r_pad]
     size_t off_dpart;                   // fp32 partials of a down projection [splits][T][r_pad]
-    size_t fwd_bytes, bwd_bytes, bwd_grad_bytes;
+    // fused backward (QLORA_BWD_FUSED_GRADS): the gradient partials of k_dx's
+    // epilogue, one per 256-token tile, in place of the k_grad partials
+    int s_fz;
+    size_t off_fza, off_fzb;            // fp32 [s_fz][K][r_pad], [s_fz][N][r_pad]
+    size_t fwd_bytes, bwd_bytes, bwd_grad_bytes, bwd_fused_bytes;
 
     LoraPlan(int64_t T_, int64_t K_, int64_t N_, int64_t r_) : T(T_), K(K_), N(N_), r(r_) {
         r_pad = r > 0 ? ceil_div(r, kTileSmall) * kTileSmall : 0;
@@ -72,8 +76,10 @@ struct LoraPlan {
             off_pst_hi = off_pst_lo = off_gst_hi = off_gst_lo = off_pda = off_pdb = 0;
             off_dpart = 0;
             off_scl = 0;
+            s_fz = 0;
+            off_fza = off_fzb = 0;
             fwd_bytes = 0;
-            bwd_bytes = bwd_grad_bytes = scl;
+            bwd_bytes = bwd_grad_bytes = bwd_fused_bytes = scl;
             return;
         }
         const size_t tr2 = (size_t)T * r_pad * 2, rt2 = (size_t)r_pad * ld_t * 2;
@@ -98,9 +104,15 @@ struct LoraPlan {
         // adapter gradients
         off_gst_hi = o; o = align256(o + rt2);
         off_gst_lo = o; o = align256(o + rt2);
+        const size_t grad_start = o;
         off_pda = o;    o = align256(o + (size_t)s_da * K * r_pad * 4);
         off_pdb = o;    o = align256(o + (size_t)s_db * N * r_pad * 4);
         bwd_grad_bytes = o;
+        s_fz = (int)ceil_div(T, 256);
+        o = grad_start;
+        off_fza = o;    o = align256(o + (size_t)s_fz * K * r_pad * 4);
+        off_fzb = o;    o = align256(o + (size_t)s_fz * N * r_pad * 4);
+        bwd_fused_bytes = o;
     }
 };
 

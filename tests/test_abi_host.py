@@ -167,8 +167,37 @@ def test_bwd_validation(L):
     assert _bwd(L, r=0, la=None, lb=None) == SHAPE   # grads requested with r = 0
     assert _bwd(L, da=MIS) == ALIGN
     assert _bwd(L, s=math.inf) == VALUE
-    assert _bwd(L, flags=2) == VALUE          # unknown flag bit
+    assert _bwd(L, flags=4) == VALUE          # unknown flag bit
+    assert _bwd(L, flags=1 << 31) == VALUE
     assert _bwd(L, wsb=0) == WORKSPACE
+    # the fused gradients need their own, larger workspace (one fp32 partial per 256-token tile)
+    T, K, N, r = 300, 256, 320, 16
+    plain = L.qlora_workspace_bytes_bwd(T, K, N, r, 0)
+    fused = L.qlora_workspace_bytes_bwd(T, K, N, r, api.FUSED_GRADS)
+    assert fused > 0 and plain > 0
+    assert _bwd(L, T=T, K=K, N=N, r=r, wsb=fused - 1, flags=api.FUSED_GRADS) == WORKSPACE
+    assert _bwd(L, T=T, K=K, N=N, r=r, wsb=fused - 1, flags=api.FUSED_GRADS | api.REUSE_FORWARD) == WORKSPACE
+    assert _bwd(L, T=T, K=K, N=N, r=r, wsb=fused - 1, flags=api.FUSED_GRADS | 4) == VALUE
+
+
+def test_workspace_bytes_bwd(L):
+    f = L.qlora_workspace_bytes_bwd
+    for T, K, N, r in ((300, 256, 320, 16), (4096, 4096, 11008, 64), (2048, 22016, 8192, 64), (17, 64, 64, 256)):
+        plain, fused = f(T, K, N, r, 0), f(T, K, N, r, api.FUSED_GRADS)
+        assert f(T, K, N, r, api.REUSE_FORWARD) == plain
+        assert f(T, K, N, r, api.REUSE_FORWARD | api.FUSED_GRADS) == fused
+        # the two layouts share everything up to the gradient partials: plain holds the k_grad
+        # partials, fused one [K + N][r_pad] fp32 block per 256-token tile instead
+        r_pad = -(-r // 64) * 64
+        tiles = -(-T // 256)
+        ceil256 = lambda v: -(-v // 256) * 256
+        assert fused - ceil256(tiles * K * r_pad * 4) - ceil256(tiles * N * r_pad * 4) < plain
+        assert fused >= ceil256(tiles * K * r_pad * 4) + ceil256(tiles * N * r_pad * 4)
+        assert plain >= L.qlora_workspace_bytes(T, K, N, r) or T <= 128
+    assert f(16, 100, 64, 16, 0) == 0                      # rejected sizes
+    assert f(300, 256, 320, 16, 4) == 0                    # unknown flag
+    # without an adapter there are no gradients: the scale table alone
+    assert f(300, 256, 320, 0, api.FUSED_GRADS) == f(300, 256, 320, 0, 0) == (256 // 64) * 320 * 4
 
 
 def test_workspace_bytes(L):
