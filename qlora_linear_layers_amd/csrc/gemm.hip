@@ -803,22 +803,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb, Fused
     otile_store(smem, p.dx, p.K, t0, k0, p.T, p.K);
 
     if constexpr (FUSED) {
-        // the adapter gradients of this token tile: the blocks (column block x
-        // 64 ranks) of dA, then of dB, dealt to the four waves in turn; each
-        // wave sums its blocks over all 256 tokens and writes them itself
+        // this wave's blocks of the adapter gradients (see FusedGrads): every
+        // wave of the grid takes every waves-th block and writes its partial
         const int RB = (int)(p.r_pad / 64);
-        const int w = (int)(threadIdx.x >> 6);
-        const int na = fz.ga.part ? 2 * RB : 0;
-        int nb = 0;
-        if (fz.gb.part)
-            for (int cbn = ta; cbn < fz.gb.cblocks; cbn += fz.ktiles) nb += RB;
+        const int na = fz.ga.part ? fz.groups * fz.ga.cblocks * RB : 0;
+        const int nb = fz.gb.part ? fz.groups * fz.gb.cblocks * RB : 0;
 #pragma unroll 1
-        for (int q = w; q < na + nb; q += 4) {
+        for (int q = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6); q < na + nb; q += fz.waves) {
             const bool first = q < na;
-            const int qq = first ? q : q - na;
-            const int cbx = first ? 2 * ta + qq / RB : ta + (qq / RB) * fz.ktiles;
             const GradArgs g = first ? fz.ga : fz.gb;
-            if (cbx < g.cblocks) grad_wave<F16>(g, cbx, tb, (int64_t)(qq % RB) * 64);
+            const int qq = first ? q : q - na;
+            const int jb = qq % RB, cbx = (qq / RB) % g.cblocks, grp = qq / (RB * g.cblocks);
+            grad_wave<F16>(g, cbx, grp, fz.tpg, (int64_t)jb * 64);
         }
     }
 }
@@ -880,7 +876,12 @@ hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, BlockScales sc, c
                            fused ? *fused : FusedGrads{});
         return hipGetLastError();
     };
-    if (fused) return f16 ? go(k_dx<true, true>) : go(k_dx<false, true>);
+    if (fused) {
+        FusedGrads f = *fused;
+        f.waves = (int)tiles * 4;
+        fused = &f;
+        return f16 ? go(k_dx<true, true>) : go(k_dx<false, true>);
+    }
     return f16 ? go(k_dx<true, false>) : go(k_dx<false, false>);
 }
 

@@ -30,16 +30,17 @@ struct GradArgs {
 };
 
 // The adapter gradients computed by the fused backward's k_dx after its dX
-// tile (a problem with part == nullptr is not asked for).  Workgroup (k tile
-// ta, token tile tb) adds, over the 256 tokens of tb (split tb), the blocks
-// of 128 columns x 64 ranks
-//   dA: of the two column blocks 2 ta, 2 ta + 1 of its own k tile (S = X);
-//   dB: of the column blocks ta, ta + ktiles, ta + 2 ktiles, ... of N
-//       (S = dY), so the k tiles of one token tile share N evenly;
-// one wave per block (grad_wave below).
+// tile (a problem with part == nullptr is not asked for).  The work is split
+// into blocks of 128 columns x 64 ranks x `tpg` 256-token tiles (one fp32
+// partial per tile group); block q goes to wave q mod waves of the grid (wave
+// w of workgroup b is 4 b + w).  Blocks are numbered token group first, then
+// column block, then rank block, dA's before dB's, so that the neighbouring
+// waves of a group read the same rows of V.
 struct FusedGrads {
     GradArgs ga, gb;
-    int ktiles;
+    int tpg;             // 256-token tiles per token group (= per partial)
+    int groups;          // token groups: ceil(ceil(T / 256) / tpg)
+    int waves;           // waves of the k_dx grid
 };
 
 constexpr int kGradThreads = 256;
@@ -153,14 +154,14 @@ QL_DEV void grad_block(const GradArgs& a, int cb, int split, int64_t j0, float* 
 }
 
 // One wave alone: part[split][c][j] for column block cb and ranks j0 .. j0 + 63
-// over the 256 tokens of `split` (eight chunks), written straight from the
-// wave's sums: no partner waves, no LDS, no barrier, so the four waves of a
-// workgroup can each take their own blocks.
+// over the 256 tpg tokens of token group `split` (8 tpg chunks), written
+// straight from the wave's sums: no partner waves, no LDS, no barrier, so the
+// waves of a workgroup can each take their own blocks.
 template <bool F16>
-QL_DEV void grad_wave(const GradArgs& a, int cb, int split, int64_t j0) {
+QL_DEV void grad_wave(const GradArgs& a, int cb, int split, int tpg, int64_t j0) {
     const int l = threadIdx.x & 63;
     f32x4_t acc[8][4];
-    grad_accumulate<F16>(a, cb, (int64_t)split * 256, 8, 0, j0, acc);
+    grad_accumulate<F16>(a, cb, (int64_t)split * 256 * tpg, 8 * tpg, 0, j0, acc);
     float* out = a.part + (int64_t)split * a.C * a.r_pad;
 #pragma unroll
     for (int i = 0; i < 8; ++i)

@@ -471,12 +471,14 @@ hipError_t launch_lora_grads(const uint16_t* x, const uint16_t* dy, const LoraPl
 }
 
 // The fused backward's gradient problems: S = X against G^T for dA and S = dY
-// against P^T for dB, one 256-token tile (eight 32-token chunks of one wave)
-// per split, partials in the fused region of ws.
+// against P^T for dB, one group of fz_tpg 256-token tiles per split, partials
+// in the fused region of ws.
 FusedGrads fused_grads_for(const uint16_t* x, const uint16_t* dy, const LoraPlan& pl, uint8_t* ws, bool da,
                            bool db) {
     FusedGrads f{};
-    f.ktiles = (int)ceil_div(pl.K, 256);
+    f.tpg = pl.fz_tpg;
+    f.groups = pl.s_fz;
+    f.waves = 0;                                   // set by the dX launcher from its grid
     if (da)
         f.ga = GradArgs{x, reinterpret_cast<const uint16_t*>(ws + pl.off_gst_hi),
                         reinterpret_cast<const uint16_t*>(ws + pl.off_gst_lo), reinterpret_cast<float*>(ws + pl.off_fza),

@@ -53,8 +53,9 @@ struct LoraPlan {
     size_t off_pda, off_pdb;            // fp32 partials [s_da][K][r_pad], [s_db][N][r_pad]
     size_t off_dpart;                   // fp32 partials of a down projection [splits][T][r_pad]
     // fused backward (QLORA_BWD_FUSED_GRADS): the gradient partials of k_dx's
-    // epilogue, one per 256-token tile, in place of the k_grad partials
-    int s_fz;
+    // epilogue, one per group of fz_tpg 256-token tiles, in place of the
+    // k_grad partials
+    int s_fz, fz_tpg;
     size_t off_fza, off_fzb;            // fp32 [s_fz][K][r_pad], [s_fz][N][r_pad]
     size_t fwd_bytes, bwd_bytes, bwd_grad_bytes, bwd_fused_bytes;
 
@@ -76,7 +77,7 @@ struct LoraPlan {
             off_pst_hi = off_pst_lo = off_gst_hi = off_gst_lo = off_pda = off_pdb = 0;
             off_dpart = 0;
             off_scl = 0;
-            s_fz = 0;
+            s_fz = fz_tpg = 0;
             off_fza = off_fzb = 0;
             fwd_bytes = 0;
             bwd_bytes = bwd_grad_bytes = bwd_fused_bytes = scl;
@@ -108,7 +109,11 @@ struct LoraPlan {
         off_pda = o;    o = align256(o + (size_t)s_da * K * r_pad * 4);
         off_pdb = o;    o = align256(o + (size_t)s_db * N * r_pad * 4);
         bwd_grad_bytes = o;
-        s_fz = (int)ceil_div(T, 256);
+        {
+            const int64_t tiles = ceil_div(T, 256);
+            fz_tpg = tiles >= 4 ? 2 : 1;      // two tiles per partial halve the partials' bytes
+            s_fz = (int)ceil_div(tiles, fz_tpg);
+        }
         o = grad_start;
         off_fza = o;    o = align256(o + (size_t)s_fz * K * r_pad * 4);
         off_fzb = o;    o = align256(o + (size_t)s_fz * N * r_pad * 4);

@@ -187,9 +187,11 @@ def test_workspace_bytes_bwd(L):
         assert f(T, K, N, r, api.REUSE_FORWARD) == plain
         assert f(T, K, N, r, api.REUSE_FORWARD | api.FUSED_GRADS) == fused
         # the two layouts share everything up to the gradient partials: plain holds the k_grad
-        # partials, fused one [K + N][r_pad] fp32 block per 256-token tile instead
+        # partials, fused one [K + N][r_pad] fp32 block per group of 256-token tiles instead
+        # (two tiles per group from four tiles on)
         r_pad = -(-r // 64) * 64
         tiles = -(-T // 256)
+        tiles = -(-tiles // 2) if tiles >= 4 else tiles
         ceil256 = lambda v: -(-v // 256) * 256
         assert fused - ceil256(tiles * K * r_pad * 4) - ceil256(tiles * N * r_pad * 4) < plain
         assert fused >= ceil256(tiles * K * r_pad * 4) + ceil256(tiles * N * r_pad * 4)

@@ -28,8 +28,9 @@ def _case(lin, T, r, cfg=9):
 
 
 # (name, weight [N, K], T, r, s): ragged tiles in every dimension, padded ranks,
-# a single k tile that owns every dB column block, more k tiles than dB column
-# blocks (idle dB shares), and a T <= 128 backward (its forward runs decode windows)
+# more gradient blocks than waves and fewer, one-tile token groups (T < 1024)
+# and two-tile groups with a ragged last group (T = 1100: five tiles), and a
+# T <= 128 backward (its forward runs decode windows)
 CASES = [
     ("ragged", synth.Linear("t", 448, 320), 300, 16, 1.0),
     ("multi-tile", synth.Linear("t", 768, 1024), 520, 64, 0.25),
@@ -37,6 +38,8 @@ CASES = [
     ("rank 256 at T = 129", synth.Linear("t", 1088, 576), 129, 256, 0.25),
     ("one k tile", synth.Linear("t", 2112, 256), 260, 64, 0.25),
     ("many k tiles", synth.Linear("t", 192, 2560), 300, 16, 1.0),
+    ("five token tiles", synth.Linear("t", 704, 384), 1100, 24, 0.5),
+    ("four token tiles, rank 192", synth.Linear("t", 320, 448), 1024, 136, 0.25),
     ("T = 40", synth.Linear("t", 640, 448), 40, 24, 0.5),
 ]
 
