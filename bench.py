@@ -455,6 +455,39 @@ def merge_bytes(lin, r):
 
 
 
+def measure_forward_midt(api, torch, layers, sets, r, s, tokens=(256, 512, 1024, 2048), reps=6):
+    """Forward of the seven linears at token counts whose 256 x 256 tiles fill part of
+    the chip (the split-k forward), one weight copy per pass.
+    Returns {T: (seconds per layer set, flops per layer set)}."""
+    copies = len(sets)
+    out = {}
+    for T in tokens:
+        g = torch.Generator(device="cuda").manual_seed(200 + T)
+        xs = [torch.randn((T, l.K), generator=g, device="cuda").to(torch.bfloat16) for l in layers]
+        a = [torch.randn((l.K, r), generator=g, device="cuda").mul_(0.01).to(torch.bfloat16) for l in layers]
+        b = [torch.randn((r, l.N), generator=g, device="cuda").mul_(0.01).to(torch.bfloat16) for l in layers]
+        ws = torch.empty(max(api.qlora_workspace_bytes(T, l.K, l.N, r) for l in layers), dtype=torch.uint8,
+                         device="cuda")
+        ys = [torch.empty((T, l.N), dtype=torch.bfloat16, device="cuda") for l in layers]
+
+        def one(c):
+            for i in range(len(layers)):
+                api.qlora_linear_fwd(xs[i], sets[c][i], a[i], b[i], s, workspace=ws, out=ys[i])
+        for c in range(copies):
+            one(c)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for k in range(reps):
+            one(k % copies)
+        ev[1].record()
+        torch.cuda.synchronize()
+        secs = ev[0].elapsed_time(ev[1]) / 1e3 / reps
+        out[T] = (secs, sum(2 * T * l.N * l.K + 4 * T * r * (l.K + l.N) for l in layers))
+        del xs, a, b, ws, ys
+    return out
+
+
 def measure_prefill(api, torch, layers, sets, r, s, tokens=(32, 64), reps=6):
     """Small-prefill forward (16 < T <= 128 runs 16-token windows as one grouped
     decode launch) over the seven linears, one weight copy per pass.
@@ -666,6 +699,13 @@ def only_component(name, api, torch, synth, calib, args):
         res = measure_decode(api, torch, layers7, weight_copies(api, qws), r, s, mode=mode, product=product)
         return {f"T{Td}": {"GB/s": round(nb / secs / 1e9, 1), "us_per_layer_set": round(1e6 * secs, 2)}
                 for Td, (secs, nb) in res.items()}
+    if name == "forward_midt":
+        g = torch.Generator(device="cuda").manual_seed(1)
+        qws = [api.nf4_quantize_dq(torch.randn((l.N, l.K), generator=g, device="cuda").mul_(0.02)
+                                   .to(torch.bfloat16)) for l in layers7]
+        res = measure_forward_midt(api, torch, layers7, weight_copies(api, qws), r, s)
+        return {f"T{Tm}": {"TFLOP/s": round(fl / secs / 1e12, 1), "us_per_layer_set": round(1e6 * secs, 2)}
+                for Tm, (secs, fl) in res.items()}
     if name == "single_layer":
         return {k: {"GB/s": round(nb / secs / 1e9, 1), "us_per_launch": round(1e6 * secs, 3)}
                 for k, (kind, secs, amt, nb, _) in measure_single_layer(api, torch, synth).items()}
@@ -695,7 +735,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline step and the roofline kernel (for a kernel trace of the step alone)")
     ap.add_argument("--only", choices=("decode", "decode_single", "decode_all7", "decode_valu", "decode_all7_valu",
-                                       "decode_mfma", "decode_all7_mfma", "single_layer", "train_7b", "train_7b_fused",
+                                       "decode_mfma", "decode_all7_mfma", "single_layer", "train_7b", "train_7b_fused", "forward_midt",
                                        "merge", "calibration", "stream_70b"),
                     help="run one component alone (no step, roofline loop or CPU baseline), e.g. for a kernel trace")
     ap.add_argument("--roofline-only", action="store_true",
@@ -840,6 +880,12 @@ def main():
         comp["merge"] = {"GB/s": round(nbytes / secs / 1e9, 1), "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
                          "us_per_layer_set": round(1e6 * secs, 2),
                          "note": "7 linears, W_m = RNE_bf16(W' + s (A B)^T), r=64; weights rotated over 6 copies"}
+        for Tm, (secs, flops) in measure_forward_midt(api, torch, layers7, sets, r7, s7).items():
+            comp[f"forward_T{Tm}"] = {"TFLOP/s": round(flops / secs / 1e12, 1),
+                                      "frac_of_mfma_peak": round(flops / secs / MFMA_BF16_PEAK, 4),
+                                      "us_per_layer_set": round(1e6 * secs, 2),
+                                      "note": "7 linears, r=64, forward at a token count whose 256x256 tiles fill "
+                                              "part of the chip (split-k where it pays); weights rotated over 6 copies"}
         for Tp, (secs, nbytes, flops) in measure_prefill(api, torch, layers7, sets, r7, s7).items():
             comp[f"prefill_T{Tp}"] = {"TFLOP/s": round(flops / secs / 1e12, 1), "GB/s": round(nbytes / secs / 1e9, 1),
                                       "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),

@@ -371,27 +371,26 @@ int nf4_dequantize(const uint8_t* codes, const float* absmax, int64_t numel, uin
 size_t qlora_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r) {
     if (check_linear_shape(T, K, N, r) != QLORA_OK) return 0;
     const ql::LoraPlan pl(T, K, N, r);
-    size_t n = pl.bwd_grad_bytes;
-    if (T <= ql::kChunkMaxT) {
-        const size_t g = T <= ql::kGemvMaxT ? ql::gemv_workspace(T, K, N, pl.r_pad) : chunked_workspace(T, K, N, pl.r_pad);
-        if (g > n) n = g;
-    }
-    return n;
+    const size_t f = fwd_workspace(T, K, N, r);
+    return f > pl.bwd_grad_bytes ? f : pl.bwd_grad_bytes;
 }
 
 size_t qlora_workspace_bytes_bwd(int64_t T, int64_t K, int64_t N, int64_t r, unsigned flags) {
     if (check_linear_shape(T, K, N, r) != QLORA_OK) return 0;
     if (flags & ~(unsigned)(QLORA_BWD_REUSE_FORWARD | QLORA_BWD_FUSED_GRADS)) return 0;
     const ql::LoraPlan pl(T, K, N, r);
-    return (flags & QLORA_BWD_FUSED_GRADS) ? pl.bwd_fused_bytes : pl.bwd_grad_bytes;
+    const size_t b = (flags & QLORA_BWD_FUSED_GRADS) ? pl.bwd_fused_bytes : pl.bwd_grad_bytes;
+    const size_t f = fwd_workspace(T, K, N, r);
+    return b > f ? b : f;
 }
 
 size_t qlora_workspace_bytes_upto(int64_t T_max, int64_t K, int64_t N, int64_t r) {
     if (check_linear_shape(T_max, K, N, r) != QLORA_OK) return 0;
-    // below T_max the size peaks somewhere in the decode and window range
-    // (T <= kChunkMaxT); above it the MFMA-path size grows with T
+    // the size peaks in the decode and window range (T <= kChunkMaxT) and
+    // wherever a split-k forward keeps partial tiles (a grid of fewer than
+    // 256 tiles: T < 65536); beyond that it grows with T
     size_t n = qlora_workspace_bytes(T_max, K, N, r);
-    for (int64_t T = 1; T <= std::min<int64_t>(T_max, ql::kChunkMaxT); ++T) {
+    for (int64_t T = 1; T <= std::min<int64_t>(T_max, 65536); ++T) {
         const size_t m = qlora_workspace_bytes(T, K, N, r);
         if (m > n) n = m;
     }

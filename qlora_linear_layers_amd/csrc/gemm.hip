@@ -198,6 +198,8 @@ struct FwdArgs {
     const uint16_t* ps_lo;
     uint16_t* y;
     int64_t T, K, N, r, r_pad;
+    float* part;              // split-k: fp32 partial tiles [splits][N][T]
+    int splits;
 };
 
 // Y = X W'^T (+ (s X A) B), tile 256 (n) x 256 (t), waves stacked along n.
@@ -381,7 +383,11 @@ QL_DEV void fwd_tile(FwdPipe<SQ>& pp, int kt, f32x16_t (&acc)[2][8], lds8_t* lX,
     c1p[1] = n1p[1];
 }
 
-template <bool SQ, bool F16>
+// SPLIT: the grid holds `splits` workgroups per tile; workgroup (tile,
+// split) takes k tiles [split KT / splits, (split + 1) KT / splits) (split 0
+// also the LoRA term) and stores its fp32 tile in part[split][n][t], which
+// k_split_sum adds in split order.
+template <bool SQ, bool F16, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     lds8_t* smem = (lds8_t*)(smem_raw);
@@ -393,8 +399,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
     build_wide_pair_table(tbl, cb);
 
     const int ga = (int)ceil_div(p.N, 256), gb = (int)ceil_div(p.T, TT);
-    int ta, tb;
-    tile_of(blockIdx.x, ga, gb, ta, tb);
+    const int KT_all = (int)(p.K / 64);
+    int ta, tb, split = 0, kt0 = 0, kt1 = KT_all;
+    if constexpr (SPLIT) {
+        split = (int)blockIdx.x / (ga * gb);
+        tile_of((int)blockIdx.x % (ga * gb), ga, gb, ta, tb);
+        kt0 = split * KT_all / p.splits;
+        kt1 = (split + 1) * KT_all / p.splits;
+    } else {
+        tile_of(blockIdx.x, ga, gb, ta, tb);
+    }
     const int64_t n0 = (int64_t)ta * 256, t0 = (int64_t)tb * TT;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 31, h = lane >> 5;
@@ -409,21 +423,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
         pp.rs = make_rsrc(p.sup, ceil_div(p.N * p.K / 64, 256) * 4);
     }
     pp.rx = make_rsrc(p.x, p.T * p.K * 2);
-    pp.KT = (int)(p.K / 64);
+    pp.KT = kt1 - kt0;                        // k tiles of this workgroup, counted from kt0
     pp.lane8 = lds_addr(tbl) + (uint32_t)(lane & 31) * 8u;   // table is 64 KB aligned
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int64_t n = n0 + 64 * w + 32 * i + r;
         pp.wok[i] = n < p.N;
-        pp.cvo[i] = pp.wok[i] ? (uint32_t)(n * (p.K / 2) + 16 * h) : kOOB;
-        pp.fvo[i] = pp.wok[i] ? (uint32_t)(n * (p.K / 64)) : kOOB;
-        pp.blk[i] = pp.wok[i] ? (uint32_t)(n * (p.K / 64)) : 0u;
+        pp.cvo[i] = pp.wok[i] ? (uint32_t)(n * (p.K / 2) + 16 * h + 32 * kt0) : kOOB;
+        pp.fvo[i] = pp.wok[i] ? (uint32_t)(n * (p.K / 64) + kt0) : kOOB;
+        pp.blk[i] = pp.wok[i] ? (uint32_t)(n * (p.K / 64) + kt0) : 0u;
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const int ch = threadIdx.x + c * kThreads;
         const int64_t t = t0 + (ch >> 3);
-        pp.xvo[c] = t < p.T ? (uint32_t)((t * p.K + (ch & 7) * 8) * 2) : kOOB;
+        pp.xvo[c] = t < p.T ? (uint32_t)((t * p.K + (int64_t)kt0 * 64 + (ch & 7) * 8) * 2) : kOOB;
     }
 
     f32x16_t acc[2][8];
@@ -460,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
     }
     if (kt < KT) fwd_tile<0, SQ, F16>(pp, kt, acc, lX, r, h, xa, aa, qa, c1p);
 
-    if (p.r > 0) {
+    if (p.r > 0 && split == 0) {
         // reduction over [hi | lo] of s X A (tokens) against B^T stacked twice (rows n)
         TransRows<256> pl;
         pl.init(p.lora_b, p.lora_b, p.N, p.N, p.r_pad, p.r, n0);
@@ -489,6 +503,43 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
         }
     }
 
+    if constexpr (SPLIT) {
+        // fp32 partial tile part[split][n][t], through LDS in two halves of 128
+        // rows (A fragment i of every wave): LDS row 32 w + q holds tile row
+        // 64 w + 32 i + q; the 16-byte chunks of rows with bit 2 set sit 128
+        // bytes over, so the two rows of one accumulator store use distinct
+        // banks; whole 1 KB rows then go out with 16-byte stores
+        float* out = p.part + (int64_t)split * p.N * p.T;
+        float* lt = reinterpret_cast<float*>(smem_raw);                  // [128][256] fp32
+        auto loff = [](int row, int t) { return row * 256 + (t ^ (((row >> 2) & 1) << 5)); };
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {                                    // unrolled: acc indices stay static
+            __syncthreads();                                             // LDS readers are done
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        lt[loff(32 * w + 8 * g + 4 * h + v, 32 * j + r)] = acc[i][j][4 * g + v];
+            __syncthreads();
+#pragma unroll 4
+            for (int e = threadIdx.x; e < 128 * 64; e += kThreads) {     // 64 float4 per row
+                const int row = e >> 6, c4 = e & 63;
+                const int64_t n = n0 + 64 * (row >> 5) + 32 * i + (row & 31);
+                const int64_t t = t0 + 4 * c4;
+                if (n < p.N && t < p.T) {
+                    const float* src = lt + loff(row, 4 * c4);
+                    if ((p.T & 3) == 0) {                                // rows stay 16-byte aligned
+                        *reinterpret_cast<f32x4_t*>(out + n * p.T + t) = f32x4_t{src[0], src[1], src[2], src[3]};
+                    } else {
+                        for (int u = 0; u < 4 && t + u < p.T; ++u) out[n * p.T + t + u] = src[u];
+                    }
+                }
+            }
+        }
+        return;
+    }
     // C[n][t] -> Y[t][n] through an LDS tile over the X buffers and the table
     __syncthreads();                          // every wave is done reading them
 #pragma unroll
@@ -499,6 +550,60 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
             for (int g = 0; g < 4; ++g) otile_put4<F16>(smem, acc[i][j], g, 32 * j + r, 64 * w + 32 * i + 8 * g + 4 * h);
     __syncthreads();
     otile_store(smem, p.y, p.N, t0, n0, p.T, p.N);
+}
+
+// out[t][c] = RNE_16(sum_s part[s][c][t]) for the split-k GEMMs: a workgroup
+// adds a 64 (c) x 64 (t) block over the splits in split order (a thread four
+// consecutive t, its split loads issued four at a time), turns it in LDS and
+// stores whole 128-byte rows of out.
+template <bool F16>
+__global__ __launch_bounds__(256) void k_split_sum(const float* part, int splits, int64_t C, int64_t T,
+                                                  uint16_t* out) {
+    __shared__ uint16_t tile[64][64 + 8];             // [t][c]
+    const int64_t c0 = (int64_t)blockIdx.x * 64, t0 = (int64_t)blockIdx.y * 64;
+    const int64_t plane = C * T;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int e = (int)threadIdx.x + 256 * k;     // 64 rows c x 16 float4 of t
+        const int cl = e >> 4, tl = 4 * (e & 15);
+        const int64_t c = c0 + cl, t = t0 + tl;
+        f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (c < C && t < T) {                         // T % 4 == 0 is not assumed: tail by element
+            const float* src = part + c * T + t;
+            if (t + 4 <= T && ((c * T + t) & 3) == 0) {
+                v = *reinterpret_cast<const f32x4_t*>(src);
+                for (int sp = 1; sp < splits; sp += 4) {
+                    f32x4_t w[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        w[q] = sp + q < splits ? *reinterpret_cast<const f32x4_t*>(src + (sp + q) * plane)
+                                               : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (sp + q < splits) v += w[q];
+                }
+            } else {
+                for (int u = 0; u < 4 && t + u < T; ++u) {
+                    float a = src[u];
+                    for (int sp = 1; sp < splits; ++sp) a += src[sp * plane + u];
+                    v[u] = a;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) tile[tl + u][cl] = (uint16_t)(pack16x2<F16>(v[u], 0.0f) & 0xFFFFu);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+        const int tl = e >> 3, ch = e & 7;
+        const int64_t t = t0 + tl, c = c0 + ch * 8;
+        if (t < T && c < C) {
+            u32x4_t v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = (uint32_t)tile[tl][ch * 8 + 2 * q] | ((uint32_t)tile[tl][ch * 8 + 2 * q + 1] << 16);
+            *reinterpret_cast<u32x4_t*>(out + t * C + c) = v;
+        }
+    }
 }
 
 constexpr size_t kFwdSmem = 2 * 256 * 128 + kWideTableBytes;
@@ -834,19 +939,31 @@ hipError_t set_smem(F* f, size_t bytes) {
 
 hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, BlockScales sc, const uint16_t* lora_b,
                       const LoraPlan& pl, const uint8_t* ws, uint16_t* y, hipStream_t s, bool f16) {
+    const bool split = pl.s_fwd > 1;
     FwdArgs a{x, codes, sc.fp8, sc.sup, sc.absmax, lora_b, reinterpret_cast<const uint16_t*>(ws + pl.off_ps_hi),
               reinterpret_cast<const uint16_t*>(ws + pl.off_ps_lo), y,
-              pl.T, pl.K, pl.N, pl.r, pl.r_pad};
+              pl.T, pl.K, pl.N, pl.r, pl.r_pad,
+              split ? reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + pl.off_fsp) : nullptr, pl.s_fwd};
     const size_t lds = kFwdSmem;
-    const int64_t tiles = ceil_div(pl.N, 256) * ceil_div(pl.T, 256);
+    const int64_t tiles = ceil_div(pl.N, 256) * ceil_div(pl.T, 256) * (split ? pl.s_fwd : 1);
     auto go = [&](auto kern) {
         hipError_t e = set_smem(kern, lds);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kThreads), lds, s, a, host_codebook());
         return hipGetLastError();
     };
-    if (f16) return sc.single() ? go(k_fwd<true, true>) : go(k_fwd<false, true>);
-    return sc.single() ? go(k_fwd<true, false>) : go(k_fwd<false, false>);
+    if (split) {
+        hipError_t e;
+        if (sc.single()) e = f16 ? go(k_fwd<true, true, true>) : go(k_fwd<true, false, true>);
+        else e = f16 ? go(k_fwd<false, true, true>) : go(k_fwd<false, false, true>);
+        if (e != hipSuccess) return e;
+        const dim3 g((unsigned)ceil_div(pl.N, 64), (unsigned)ceil_div(pl.T, 64));
+        if (f16) hipLaunchKernelGGL(k_split_sum<true>, g, dim3(256), 0, s, a.part, pl.s_fwd, pl.N, pl.T, y);
+        else hipLaunchKernelGGL(k_split_sum<false>, g, dim3(256), 0, s, a.part, pl.s_fwd, pl.N, pl.T, y);
+        return hipGetLastError();
+    }
+    if (f16) return sc.single() ? go(k_fwd<true, true, false>) : go(k_fwd<false, true, false>);
+    return sc.single() ? go(k_fwd<true, false, false>) : go(k_fwd<false, false, false>);
 }
 
 ScalesJob scales_job_for(BlockScales sc, const LoraPlan& pl, uint8_t* ws) {

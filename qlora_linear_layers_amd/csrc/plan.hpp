@@ -36,6 +36,36 @@ inline int down_splits(int64_t T, int64_t L) {
     return (int)(s < 1 ? 1 : s);
 }
 
+// Split of the reduction of a 256 x 256-tile GEMM (out [T][C], reduction L)
+// over several workgroups when its tiles fill too little of the chip: S
+// workgroups per tile each take L/S of the reduction and leave an fp32
+// partial tile [S][C][T] that one small launch adds.  S minimises a time
+// model fitted to kernel timings of the LLaMA-7B shapes at T = 256 .. 2048:
+// rounds of ceil(L / 64 / S) k tiles at 1.2 + 0.5 W / 256 us each (W
+// workgroups in flight of 256), plus 0.2 us per MB of partials (written and
+// read back) and 10 us for the partial tile stores and the summing launch;
+// at least 4 k tiles per split, at most 16 splits and 64 MiB of partials.
+inline int gemm_splits(int64_t T, int64_t L, int64_t C) {
+    const int64_t tiles = ceil_div(C, 256) * ceil_div(T, 256);
+    const int64_t kt = L / 64;
+    auto cost = [&](int64_t S) {
+        const int64_t wgs = tiles * S;
+        const double w = (double)(wgs < 256 ? wgs : 256) / 256.0;
+        double t = (double)ceil_div(wgs, 256) * (double)ceil_div(kt, S) * (1.2 + 0.5 * w);
+        if (S > 1) t += 0.2e-6 * (double)S * (double)C * (double)T * 4.0 + 10.0;
+        return t;
+    };
+    double best = cost(1);
+    int bs = 1;
+    for (int S = 2; S <= 16; ++S) {
+        if (kt / S < 4) break;
+        if ((double)S * (double)C * (double)T * 4.0 > 64.0 * 1024 * 1024) break;
+        const double t = cost(S);
+        if (t < best) { best = t; bs = S; }
+    }
+    return bs;
+}
+
 struct LoraPlan {
     int64_t T, K, N, r, r_pad, T8;
     int s_down_x, s_down_dy;   // reduction splits of s X A and s dY B^T
@@ -57,6 +87,10 @@ struct LoraPlan {
     // k_grad partials
     int s_fz, fz_tpg;
     size_t off_fza, off_fzb;            // fp32 [s_fz][K][r_pad], [s_fz][N][r_pad]
+    // split-k forward (s_fwd > 1): fp32 partial tiles [s_fwd][N][T] after the
+    // forward's state; the backward's regions start at the end of that state
+    int s_fwd;
+    size_t off_fsp;
     size_t fwd_bytes, bwd_bytes, bwd_grad_bytes, bwd_fused_bytes;
 
     LoraPlan(int64_t T_, int64_t K_, int64_t N_, int64_t r_) : T(T_), K(K_), N(N_), r(r_) {
@@ -72,6 +106,8 @@ struct LoraPlan {
         s_da = r > 0 ? grad_splits(T, K, r_pad, cpw_da) : 0;
         s_db = r > 0 ? grad_splits(T, N, r_pad, cpw_db) : 0;
         const size_t scl = align256((size_t)(K / 64) * N * 4);
+        s_fwd = gemm_splits(T, K, N);
+        const size_t fsp = s_fwd > 1 ? align256((size_t)s_fwd * N * T * 4) : 0;
         if (r == 0) {
             off_at = off_ps_hi = off_ps_lo = off_gs_hi = off_gs_lo = 0;
             off_pst_hi = off_pst_lo = off_gst_hi = off_gst_lo = off_pda = off_pdb = 0;
@@ -79,7 +115,8 @@ struct LoraPlan {
             off_scl = 0;
             s_fz = fz_tpg = 0;
             off_fza = off_fzb = 0;
-            fwd_bytes = 0;
+            off_fsp = 0;
+            fwd_bytes = fsp;
             bwd_bytes = bwd_grad_bytes = bwd_fused_bytes = scl;
             return;
         }
@@ -96,8 +133,10 @@ struct LoraPlan {
             const int sd = s_down_x > s_down_dy ? s_down_x : s_down_dy;
             o = align256(o + (sd > 1 ? (size_t)sd * T * r_pad * 4 : 0));
         }
-        fwd_bytes = o;
-        // backward (dX): s dY B^T, block scales
+        off_fsp = o;
+        fwd_bytes = o + fsp;
+        // backward (dX): s dY B^T, block scales (over the forward's split
+        // partials, which are dead once the forward has finished)
         off_gs_hi = o;  o = align256(o + tr2);
         off_gs_lo = o;  o = align256(o + tr2);
         off_scl = o;    o = align256(o + scl);

@@ -210,7 +210,15 @@ def test_workspace_bytes(L):
     # 16 < T <= 128 runs 16-token windows as one grouped decode launch: one window's partials each
     assert L.qlora_workspace_bytes(64, 4096, 4096, 0) == max((4096 // 64) * 4096 * 4, 4 * (4096 // 512) * 16 * 4096 * 4)
     assert L.qlora_workspace_bytes(40, 4096, 4096, 0) == max((4096 // 64) * 4096 * 4, 3 * (4096 // 512) * 16 * 4096 * 4)
-    assert L.qlora_workspace_bytes(129, 4096, 4096, 0) == (4096 // 64) * 4096 * 4
+    # T > 128 runs 256 x 256 MFMA tiles: with 256 or more tiles only the scale table ...
+    assert L.qlora_workspace_bytes(4096, 4096, 4096, 0) == (4096 // 64) * 4096 * 4
+    # ... with fewer, the forward splits the reduction and keeps S fp32 partial
+    # tiles [S][N][T] (2 <= S <= 16, at most 64 MiB, at least 4 k tiles per split)
+    for T in (129, 300, 700, 2048):
+        n = L.qlora_workspace_bytes(T, 4096, 4096, 0)
+        split = n // (4096 * T * 4)
+        assert n > (4096 // 64) * 4096 * 4 and n % 256 == 0
+        assert 2 <= split <= 16 and n <= -(-16 * 4096 * T * 4 // 256) * 256 and n <= 64 << 20
     assert L.qlora_workspace_bytes(1 << 23, 4096, 4096, 16) == 0                     # T too large
     assert L.qlora_workspace_bytes(16, 100, 4096, 16) == 0
     a = L.qlora_workspace_bytes(4096, 4096, 11008, 64)

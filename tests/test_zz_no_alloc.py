@@ -2,7 +2,8 @@
 allocate device memory) against qlora_linear_fwd: the same kernels, so the
 outputs must be identical bit for bit.  Two calls in a row on each path, the
 second smaller than the first (the shared static scratch keeps the first
-call's contents), over the decode, 16-token-window and MFMA-tile routes."""
+call's contents), over the decode, 16-token-window and MFMA-tile routes (split-k
+and not)."""
 import numpy as np
 import pytest
 import torch
@@ -25,8 +26,9 @@ def _case(lin, T, r, s, seed):
 @pytest.mark.parametrize("first,second", [
     ((synth.Linear("t", 4096, 4096), 8, 64), (synth.Linear("t", 1024, 2048), 3, 16)),       # decode
     ((synth.Linear("t", 2048, 1024), 100, 64), (synth.Linear("t", 512, 768), 40, 24)),      # windows
-    ((synth.Linear("t", 1024, 2048), 700, 64), (synth.Linear("t", 640, 448), 333, 0)),      # MFMA tiles
-    ((synth.Linear("t", 4096, 4096), 520, 136), (synth.Linear("t", 384, 256), 5, 8)),       # across routes
+    ((synth.Linear("t", 1024, 2048), 700, 64), (synth.Linear("t", 640, 448), 333, 0)),      # split-k MFMA tiles
+    ((synth.Linear("t", 2048, 1024), 520, 136), (synth.Linear("t", 384, 256), 5, 8)),       # across routes
+    ((synth.Linear("t", 4096, 4096), 4096, 16), (synth.Linear("t", 512, 256), 200, 16)),    # one round of tiles
 ])
 def test_noalloc_matches_workspace_forward(first, second):
     for i, (lin, T, r) in enumerate((first, second)):
