@@ -148,7 +148,10 @@ int nf4_dequantize_dq_grouped(int count, const nf4_tensor* tensors, void* stream
  *   monotone in T: 16 < T <= 128 keeps one set of split partials per 16-token
  *   window and can need more than a larger T (for example about 46 MB at
  *   T = 128 against about 21 MB at T = 4096 on an 11008 x 4096 weight with
- *   r = 64), so a caller that sizes one workspace for a range of T takes the
+ *   r = 64), and a mid-size T whose 256 x 256 output tiles are too few to
+ *   fill the chip splits the reduction over several workgroups with fp32
+ *   partial tiles (at most 64 MiB; 64 MiB for a 4096 x 4096 weight at
+ *   T = 512), so a caller that sizes one workspace for a range of T takes the
  *   maximum over that range (qlora_workspace_bytes_upto).
  */
 size_t qlora_workspace_bytes(int64_t T, int64_t K, int64_t N, int64_t r);
@@ -186,7 +189,10 @@ size_t qlora_workspace_bytes_bwd(int64_t T, int64_t K, int64_t N, int64_t r, uns
  *   bytes (may be NULL if that is 0); its contents on entry do not matter.
  *   Kernels by size: T <= 16 runs the decode kernels (small-M MFMA, weight
  *   stream read once); 16 < T <= 128 runs them on 16-token windows as one
- *   grouped launch; larger T runs the 256 x 256-tile MFMA GEMM.
+ *   grouped launch; larger T runs the 256 x 256-tile MFMA GEMM, whose
+ *   reduction over K is split over up to 16 workgroups per tile (fp32
+ *   partials in the workspace, added in split order by one more launch) when
+ *   the tiles alone are too few for the chip.  Results are deterministic.
  *   Errors: NULL, SHAPE, ALIGN, VALUE (non-finite scaling), WORKSPACE, DEVICE.
  */
 int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N,
@@ -394,14 +400,19 @@ int qlora_linear_fwd_grouped_ex(int count, const qlora_linear_problem* problems,
 /*
  * qlora_linear_fwd_noalloc - qlora_linear_fwd for callers that cannot
  *   allocate device memory (code under HIP graph capture, tight serving
- *   loops, harnesses that forbid hipMalloc): the same computation, kernels and
- *   bits as qlora_linear_fwd, with no workspace argument.  Its scratch is a
- *   static device array of qlora_noalloc_scratch_bytes() (32 MiB) that every
- *   GPU the library runs on holds until the process ends; the call allocates
- *   nothing.  Sizes whose workspace (qlora_workspace_bytes' forward part)
- *   exceeds it are rejected with QLORA_ERR_WORKSPACE before anything is
- *   launched; that covers, for example, every T <= 16 decode call of the
- *   LLaMA-7B and -65B linears with r <= 64, and T = 4096 on the 7B shapes.
+ *   loops, harnesses that forbid hipMalloc): the same computation and kernels
+ *   as qlora_linear_fwd, with no workspace argument.  Its scratch is a static
+ *   device array of qlora_noalloc_scratch_bytes() (32 MiB) that every GPU the
+ *   library runs on holds until the process ends; the call allocates nothing.
+ *   The output is bit-identical to qlora_linear_fwd's whenever the latter's
+ *   forward workspace fits the scratch.  Where the tile GEMM's split-k
+ *   partials (mid-size T) would not fit, the reduction is split over fewer
+ *   workgroups (down to one), so the fp32 sums run in another order and the
+ *   bf16 results can differ in the last bit.  Sizes whose remaining workspace
+ *   still exceeds the scratch are rejected with QLORA_ERR_WORKSPACE before
+ *   anything is launched; every T <= 16 decode call of the LLaMA-7B and -65B
+ *   linears with r <= 64 fits, and so does every T from 129 to 4096 on the
+ *   7B shapes.
  *   All calls on one GPU share its array and each leaves it in an unspecified
  *   state, so calls that may overlap on one GPU (other streams, other host
  *   threads) race and must be serialised by the caller; nothing in the array

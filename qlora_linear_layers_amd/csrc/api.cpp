@@ -101,9 +101,10 @@ int fwd_check(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t*
     return QLORA_OK;
 }
 
-// Workspace bytes of one forward call (sizes already checked).
-size_t fwd_workspace(int64_t T, int64_t K, int64_t N, int64_t r) {
-    const ql::LoraPlan pl(T, K, N, r);
+// Workspace bytes of one forward call (sizes already checked); `cap` limits
+// the split-k partials of the tile GEMM as in LoraPlan.
+size_t fwd_workspace(int64_t T, int64_t K, int64_t N, int64_t r, size_t cap = SIZE_MAX) {
+    const ql::LoraPlan pl(T, K, N, r, cap);
     if (T <= ql::kGemvMaxT) return ql::gemv_workspace(T, K, N, pl.r_pad);
     if (T <= ql::kChunkMaxT) return chunked_workspace(T, K, N, pl.r_pad);
     return pl.fwd_bytes;
@@ -111,12 +112,12 @@ size_t fwd_workspace(int64_t T, int64_t K, int64_t N, int64_t r) {
 
 int fwd_impl(const uint16_t* x, int64_t T, int64_t K, int64_t N, const uint8_t* codes, ql::BlockScales sc,
              const uint16_t* lora_a, const uint16_t* lora_b, int64_t r, float scaling, uint16_t* y, void* workspace,
-             size_t workspace_bytes, void* stream, bool f16 = false) {
+             size_t workspace_bytes, void* stream, bool f16 = false, size_t cap = SIZE_MAX) {
     if (int st = fwd_check(x, T, K, N, codes, sc, lora_a, lora_b, r, scaling, y)) return st;
     if (workspace && !aligned16(workspace)) return QLORA_ERR_ALIGN;
-    const ql::LoraPlan pl(T, K, N, r);
+    const ql::LoraPlan pl(T, K, N, r, cap);
     const bool chunked = T > ql::kGemvMaxT && T <= ql::kChunkMaxT;
-    const size_t need = fwd_workspace(T, K, N, r);
+    const size_t need = fwd_workspace(T, K, N, r, cap);
     if (need && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -309,12 +310,14 @@ int qlora_linear_fwd_noalloc(const uint16_t* x, int64_t T, int64_t K, int64_t N,
                              const uint16_t* lora_b, int64_t r, float scaling, uint16_t* y, void* stream) {
     const ql::BlockScales sc = dq_scales(absmax_fp8, superscale);
     if (int st = fwd_check(x, T, K, N, codes, sc, lora_a, lora_b, r, scaling, y)) return st;
-    const size_t need = fwd_workspace(T, K, N, r);
+    // the tile GEMM's split-k partials are held to what the scratch leaves
+    const size_t need = fwd_workspace(T, K, N, r, kScratchBytes);
     if (need > kScratchBytes) return QLORA_ERR_WORKSPACE;
     void* ws = nullptr;
     if (need)
         if (int st = scratch_of_current_device(&ws)) return st;
-    return fwd_impl(x, T, K, N, codes, sc, lora_a, lora_b, r, scaling, y, ws, kScratchBytes, stream);
+    return fwd_impl(x, T, K, N, codes, sc, lora_a, lora_b, r, scaling, y, ws, kScratchBytes, stream, false,
+                    kScratchBytes);
 }
 
 const char* qlora_status_string(int status) {

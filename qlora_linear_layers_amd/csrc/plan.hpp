@@ -44,8 +44,9 @@ inline int down_splits(int64_t T, int64_t L) {
 // rounds of ceil(L / 64 / S) k tiles at 1.2 + 0.5 W / 256 us each (W
 // workgroups in flight of 256), plus 0.2 us per MB of partials (written and
 // read back) and 10 us for the partial tile stores and the summing launch;
-// at least 4 k tiles per split, at most 16 splits and 64 MiB of partials.
-inline int gemm_splits(int64_t T, int64_t L, int64_t C) {
+// at least 4 k tiles per split, at most 16 splits, and partials of at most
+// `max_bytes` (aligned to 256).
+inline int gemm_splits(int64_t T, int64_t L, int64_t C, size_t max_bytes) {
     const int64_t tiles = ceil_div(C, 256) * ceil_div(T, 256);
     const int64_t kt = L / 64;
     auto cost = [&](int64_t S) {
@@ -59,12 +60,14 @@ inline int gemm_splits(int64_t T, int64_t L, int64_t C) {
     int bs = 1;
     for (int S = 2; S <= 16; ++S) {
         if (kt / S < 4) break;
-        if ((double)S * (double)C * (double)T * 4.0 > 64.0 * 1024 * 1024) break;
+        if (align256((size_t)S * C * T * 4) > max_bytes) break;
         const double t = cost(S);
         if (t < best) { best = t; bs = S; }
     }
     return bs;
 }
+
+constexpr size_t kSplitPartialMax = size_t(64) << 20;
 
 struct LoraPlan {
     int64_t T, K, N, r, r_pad, T8;
@@ -93,7 +96,10 @@ struct LoraPlan {
     size_t off_fsp;
     size_t fwd_bytes, bwd_bytes, bwd_grad_bytes, bwd_fused_bytes;
 
-    LoraPlan(int64_t T_, int64_t K_, int64_t N_, int64_t r_) : T(T_), K(K_), N(N_), r(r_) {
+    // fwd_cap: the most workspace the forward may take; the split-k partials
+    // get at most what the forward's state leaves of it (and at most 64 MiB)
+    LoraPlan(int64_t T_, int64_t K_, int64_t N_, int64_t r_, size_t fwd_cap = SIZE_MAX)
+        : T(T_), K(K_), N(N_), r(r_) {
         r_pad = r > 0 ? ceil_div(r, kTileSmall) * kTileSmall : 0;
         T8 = ceil_div(T, 8) * 8;
         // a 128-byte shift per row keeps the same column of consecutive rows off
@@ -106,9 +112,13 @@ struct LoraPlan {
         s_da = r > 0 ? grad_splits(T, K, r_pad, cpw_da) : 0;
         s_db = r > 0 ? grad_splits(T, N, r_pad, cpw_db) : 0;
         const size_t scl = align256((size_t)(K / 64) * N * 4);
-        s_fwd = gemm_splits(T, K, N);
-        const size_t fsp = s_fwd > 1 ? align256((size_t)s_fwd * N * T * 4) : 0;
+        auto splits_within = [&](size_t state) {
+            const size_t room = fwd_cap > state ? fwd_cap - state : 0;
+            s_fwd = gemm_splits(T, K, N, room < kSplitPartialMax ? room : kSplitPartialMax);
+            return s_fwd > 1 ? align256((size_t)s_fwd * N * T * 4) : 0;
+        };
         if (r == 0) {
+            const size_t fsp = splits_within(0);
             off_at = off_ps_hi = off_ps_lo = off_gs_hi = off_gs_lo = 0;
             off_pst_hi = off_pst_lo = off_gst_hi = off_gst_lo = off_pda = off_pdb = 0;
             off_dpart = 0;
@@ -134,7 +144,7 @@ struct LoraPlan {
             o = align256(o + (sd > 1 ? (size_t)sd * T * r_pad * 4 : 0));
         }
         off_fsp = o;
-        fwd_bytes = o + fsp;
+        fwd_bytes = o + splits_within(o);
         // backward (dX): s dY B^T, block scales (over the forward's split
         // partials, which are dead once the forward has finished)
         off_gs_hi = o;  o = align256(o + tr2);

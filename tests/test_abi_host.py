@@ -100,6 +100,11 @@ def test_noalloc_forward_validation(L):
             assert call(T, K, N, 64) == DEVICE, (T, K, N)
     for K, N in ((4096, 4096), (4096, 11008), (11008, 4096)):
         assert call(4096, K, N, 64) == DEVICE
+        # mid-size T on the 7B shapes: the split-k partials are held to the scratch
+        for T in (256, 512, 1024, 2048):
+            assert L.qlora_workspace_bytes(T, K, N, 64) > 0
+            assert call(T, K, N, 64) == DEVICE, (T, K, N)
+            assert call(T, K, N, 0) == DEVICE, (T, K, N)
     # windows of the 7B gate at T = 128 (one decode workspace per 16-token window) do not
     assert call(128, 4096, 11008, 64) == WORKSPACE
     assert call(1 << 20, 1024, 1024, 64) == WORKSPACE

@@ -1,15 +1,19 @@
 """The no-allocation forward (qlora_linear_fwd_noalloc, for callers that cannot
 allocate device memory) against qlora_linear_fwd: the same kernels, so the
-outputs must be identical bit for bit.  Two calls in a row on each path, the
-second smaller than the first (the shared static scratch keeps the first
-call's contents), over the decode, 16-token-window and MFMA-tile routes (split-k
-and not)."""
+outputs must be identical bit for bit wherever qlora_linear_fwd's workspace fits
+the static scratch.  Where its split-k partials would not, the no-allocation
+call splits the reduction over fewer workgroups, and the two outputs, each
+rounded once from an fp32 sum in another order, are held to the GEMM tolerance
+(max relative error <= 1e-2 with the rms floor, mean absolute error <= 1e-3
+rms).  Two calls in a row on each path, the second smaller than the first (the
+shared static scratch keeps the first call's contents), over the decode,
+16-token-window and MFMA-tile routes (split-k and not)."""
 import numpy as np
 import pytest
 import torch
 
 from qlora_linear_layers_amd import api, synth
-from helpers import bits_of, say, to_dev
+from helpers import assert_gemm_close, bits_of, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -29,16 +33,22 @@ def _case(lin, T, r, s, seed):
     ((synth.Linear("t", 1024, 2048), 700, 64), (synth.Linear("t", 640, 448), 333, 0)),      # split-k MFMA tiles
     ((synth.Linear("t", 2048, 1024), 520, 136), (synth.Linear("t", 384, 256), 5, 8)),       # across routes
     ((synth.Linear("t", 4096, 4096), 4096, 16), (synth.Linear("t", 512, 256), 200, 16)),    # one round of tiles
+    ((synth.Linear("t", 4096, 4096), 512, 16), (synth.Linear("t", 1024, 2048), 700, 64)),   # fewer splits, then all
 ])
 def test_noalloc_matches_workspace_forward(first, second):
     for i, (lin, T, r) in enumerate((first, second)):
-        say(f"[noalloc] call {i}: N={lin.N} K={lin.K} T={T} r={r}")
+        # bit-equal unless qlora_linear_fwd's own workspace exceeds the scratch
+        exact = api.qlora_workspace_bytes(T, lin.K, lin.N, r) <= api.lib().qlora_noalloc_scratch_bytes()
+        say(f"[noalloc] call {i}: N={lin.N} K={lin.K} T={T} r={r} exact={exact}")
         qw, x, a, b = _case(lin, T, r, 0.5, i)
         ref = bits_of(api.qlora_linear_fwd(x, qw, a, b, 0.5))
         y = torch.full((T, lin.N), float("nan"), dtype=torch.bfloat16, device="cuda")
         got = bits_of(api.qlora_linear_fwd_noalloc(x, qw, a, b, 0.5, out=y))
         torch.cuda.synchronize()
-        assert np.array_equal(got, ref), (i, lin, T, r)
+        if exact:
+            assert np.array_equal(got, ref), (i, lin, T, r)
+        else:
+            assert_gemm_close(got, ref, f"call {i} against qlora_linear_fwd")
 
 
 def test_noalloc_rejects_oversized_without_touching_outputs():
