@@ -488,6 +488,48 @@ def measure_forward_midt(api, torch, layers, sets, r, s, tokens=(256, 512, 1024,
     return out
 
 
+def measure_step_midt(api, torch, layers, sets, r, s, tokens=(256, 512, 1024, 2048), reps=4):
+    """Training step of the seven linears (forward, then dX, dA and dB with the
+    forward's s X A reused) at token counts whose tiles fill part of the chip
+    (split-k forward and dX), one weight copy per pass.
+    Returns {T: (seconds per layer set, flops per layer set)}."""
+    copies = len(sets)
+    out = {}
+    for T in tokens:
+        g = torch.Generator(device="cuda").manual_seed(300 + T)
+        xs = [torch.randn((T, l.K), generator=g, device="cuda").to(torch.bfloat16) for l in layers]
+        dys = [torch.randn((T, l.N), generator=g, device="cuda").to(torch.bfloat16) for l in layers]
+        a = [torch.randn((l.K, r), generator=g, device="cuda").mul_(0.01).to(torch.bfloat16) for l in layers]
+        b = [torch.randn((r, l.N), generator=g, device="cuda").mul_(0.01).to(torch.bfloat16) for l in layers]
+        ws = [torch.empty(api.qlora_workspace_bytes_bwd(T, l.K, l.N, r, api.REUSE_FORWARD), dtype=torch.uint8,
+                          device="cuda") for l in layers]
+        ys = [torch.empty((T, l.N), dtype=torch.bfloat16, device="cuda") for l in layers]
+        dxs = [torch.empty((T, l.K), dtype=torch.bfloat16, device="cuda") for l in layers]
+        das = [torch.empty((l.K, r), dtype=torch.bfloat16, device="cuda") for l in layers]
+        dbs = [torch.empty((r, l.N), dtype=torch.bfloat16, device="cuda") for l in layers]
+
+        def one(c):
+            for i in range(len(layers)):
+                api.qlora_linear_fwd(xs[i], sets[c][i], a[i], b[i], s, workspace=ws[i], out=ys[i])
+            for i in reversed(range(len(layers))):
+                api.qlora_linear_bwd_input(dys[i], sets[c][i], a[i], b[i], s, x=xs[i], lora_grads=True,
+                                           workspace=ws[i], reuse_forward=True, dx=dxs[i], d_lora_a=das[i],
+                                           d_lora_b=dbs[i])
+        for c in range(copies):
+            one(c)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for k in range(reps):
+            one(k % copies)
+        ev[1].record()
+        torch.cuda.synchronize()
+        secs = ev[0].elapsed_time(ev[1]) / 1e3 / reps
+        out[T] = (secs, sum(3 * 2 * T * l.N * l.K + 3 * 4 * T * r * (l.K + l.N) for l in layers))
+        del xs, dys, a, b, ws, ys, dxs, das, dbs
+    return out
+
+
 def measure_prefill(api, torch, layers, sets, r, s, tokens=(32, 64), reps=6):
     """Small-prefill forward (16 < T <= 128 runs 16-token windows as one grouped
     decode launch) over the seven linears, one weight copy per pass.
@@ -706,6 +748,13 @@ def only_component(name, api, torch, synth, calib, args):
         res = measure_forward_midt(api, torch, layers7, weight_copies(api, qws), r, s)
         return {f"T{Tm}": {"TFLOP/s": round(fl / secs / 1e12, 1), "us_per_layer_set": round(1e6 * secs, 2)}
                 for Tm, (secs, fl) in res.items()}
+    if name == "train_midt":
+        g = torch.Generator(device="cuda").manual_seed(1)
+        qws = [api.nf4_quantize_dq(torch.randn((l.N, l.K), generator=g, device="cuda").mul_(0.02)
+                                   .to(torch.bfloat16)) for l in layers7]
+        res = measure_step_midt(api, torch, layers7, weight_copies(api, qws), r, s)
+        return {f"T{Tm}": {"TFLOP/s": round(fl / secs / 1e12, 1), "us_per_layer_set": round(1e6 * secs, 2)}
+                for Tm, (secs, fl) in res.items()}
     if name == "single_layer":
         return {k: {"GB/s": round(nb / secs / 1e9, 1), "us_per_launch": round(1e6 * secs, 3)}
                 for k, (kind, secs, amt, nb, _) in measure_single_layer(api, torch, synth).items()}
@@ -735,7 +784,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline step and the roofline kernel (for a kernel trace of the step alone)")
     ap.add_argument("--only", choices=("decode", "decode_single", "decode_all7", "decode_valu", "decode_all7_valu",
-                                       "decode_mfma", "decode_all7_mfma", "single_layer", "train_7b", "train_7b_fused", "forward_midt",
+                                       "decode_mfma", "decode_all7_mfma", "single_layer", "train_7b", "train_7b_fused", "forward_midt", "train_midt",
                                        "merge", "calibration", "stream_70b"),
                     help="run one component alone (no step, roofline loop or CPU baseline), e.g. for a kernel trace")
     ap.add_argument("--roofline-only", action="store_true",

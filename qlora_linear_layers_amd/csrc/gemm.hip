@@ -386,7 +386,9 @@ QL_DEV void fwd_tile(FwdPipe<SQ>& pp, int kt, f32x16_t (&acc)[2][8], lds8_t* lX,
 // SPLIT: the grid holds `splits` workgroups per tile; workgroup (tile,
 // split) takes k tiles [split KT / splits, (split + 1) KT / splits) (split 0
 // also the LoRA term) and stores its fp32 tile in part[split][n][t], which
-// k_split_sum adds in split order.
+// k_split_sum adds in split order.  Partial rows are padded to a multiple of
+// four tokens (ldp), so every row starts 16-byte aligned and both kernels
+// move whole float4s; the padding holds the tile's zero columns.
 template <bool SQ, bool F16, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
@@ -509,7 +511,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
         // 64 w + 32 i + q; the 16-byte chunks of rows with bit 2 set sit 128
         // bytes over, so the two rows of one accumulator store use distinct
         // banks; whole 1 KB rows then go out with 16-byte stores
-        float* out = p.part + (int64_t)split * p.N * p.T;
+        const int64_t ldp = (p.T + 3) & ~int64_t(3);
+        float* out = p.part + (int64_t)split * p.N * ldp;
         float* lt = reinterpret_cast<float*>(smem_raw);                  // [128][256] fp32
         auto loff = [](int row, int t) { return row * 256 + (t ^ (((row >> 2) & 1) << 5)); };
 #pragma unroll
@@ -528,13 +531,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_fwd(FwdArgs p, Codebook cb) {
                 const int row = e >> 6, c4 = e & 63;
                 const int64_t n = n0 + 64 * (row >> 5) + 32 * i + (row & 31);
                 const int64_t t = t0 + 4 * c4;
-                if (n < p.N && t < p.T) {
+                if (n < p.N && t < p.T) {                                 // t + 3 < ldp
                     const float* src = lt + loff(row, 4 * c4);
-                    if ((p.T & 3) == 0) {                                // rows stay 16-byte aligned
-                        *reinterpret_cast<f32x4_t*>(out + n * p.T + t) = f32x4_t{src[0], src[1], src[2], src[3]};
-                    } else {
-                        for (int u = 0; u < 4 && t + u < p.T; ++u) out[n * p.T + t + u] = src[u];
-                    }
+                    *reinterpret_cast<f32x4_t*>(out + n * ldp + t) = f32x4_t{src[0], src[1], src[2], src[3]};
                 }
             }
         }
@@ -561,33 +560,26 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* part, int splits
                                                   uint16_t* out) {
     __shared__ uint16_t tile[64][64 + 8];             // [t][c]
     const int64_t c0 = (int64_t)blockIdx.x * 64, t0 = (int64_t)blockIdx.y * 64;
-    const int64_t plane = C * T;
+    const int64_t ldp = (T + 3) & ~int64_t(3);       // partial row stride (see k_fwd)
+    const int64_t plane = C * ldp;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int e = (int)threadIdx.x + 256 * k;     // 64 rows c x 16 float4 of t
         const int cl = e >> 4, tl = 4 * (e & 15);
         const int64_t c = c0 + cl, t = t0 + tl;
         f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (c < C && t < T) {                         // T % 4 == 0 is not assumed: tail by element
-            const float* src = part + c * T + t;
-            if (t + 4 <= T && ((c * T + t) & 3) == 0) {
-                v = *reinterpret_cast<const f32x4_t*>(src);
-                for (int sp = 1; sp < splits; sp += 4) {
-                    f32x4_t w[4];
+        if (c < C && t < T) {                         // t + 3 < ldp: whole float4s
+            const float* src = part + c * ldp + t;
+            v = *reinterpret_cast<const f32x4_t*>(src);
+            for (int sp = 1; sp < splits; sp += 4) {
+                f32x4_t w[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        w[q] = sp + q < splits ? *reinterpret_cast<const f32x4_t*>(src + (sp + q) * plane)
-                                               : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                for (int q = 0; q < 4; ++q)
+                    w[q] = sp + q < splits ? *reinterpret_cast<const f32x4_t*>(src + (sp + q) * plane)
+                                           : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (sp + q < splits) v += w[q];
-                }
-            } else {
-                for (int u = 0; u < 4 && t + u < T; ++u) {
-                    float a = src[u];
-                    for (int sp = 1; sp < splits; ++sp) a += src[sp * plane + u];
-                    v[u] = a;
-                }
+                for (int q = 0; q < 4; ++q)
+                    if (sp + q < splits) v += w[q];
             }
         }
 #pragma unroll
@@ -621,6 +613,8 @@ struct DxArgs {
     const float* sclt;        // [K/64][N] block scales c1'
     uint16_t* dx;
     int64_t T, K, N, r, r_pad;
+    float* part;              // split-k: fp32 partial tiles [splits][K][T rounded up to 4]
+    int splits;
 };
 
 // The transposed block scales alone (when no other launch of the backward
@@ -798,7 +792,10 @@ QL_DEV void dx_tile(DxPipe& pp, int kt, f32x16_t (&acc)[4][4], lds8_t* lW, lds8_
     pp.load_w(kt + 3, Q);                     // set Q (tile kt+1) is no longer read
 }
 
-template <bool F16, bool FUSED>
+// SPLIT: as in k_fwd, `splits` workgroups per tile, each over a range of the
+// reduction's n tiles (split 0 also adds the LoRA term), writing fp32
+// partial tiles that k_split_sum adds in split order.
+template <bool F16, bool FUSED, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb, FusedGrads fz) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     lds8_t* smem = (lds8_t*)(smem_raw);
@@ -808,8 +805,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb, Fused
     lds8_t* const tbl = smem + 4 * kTile;     // 16-copy pair table
     build_pair_table16(tbl, cb);
     const int ga = (int)ceil_div(p.K, 256), gb = (int)ceil_div(p.T, 256);
-    int ta, tb;
-    tile_of(blockIdx.x, ga, gb, ta, tb);
+    int ta, tb, split = 0;
+    const int NT_all = (int)(p.N / 64);
+    int nt0 = 0, nt1 = NT_all;
+    if constexpr (SPLIT) {
+        split = (int)blockIdx.x / (ga * gb);
+        tile_of((int)blockIdx.x % (ga * gb), ga, gb, ta, tb);
+        nt0 = split * NT_all / p.splits;
+        nt1 = (split + 1) * NT_all / p.splits;
+    } else {
+        tile_of(blockIdx.x, ga, gb, ta, tb);
+    }
     const int64_t k0 = (int64_t)ta * 256, t0 = (int64_t)tb * 256;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wa = wave >> 1, wb = wave & 1;
@@ -818,7 +824,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb, Fused
     DxPipe pp;
     pp.K = p.K;
     pp.N = p.N;
-    pp.NT = (int)(p.N / 64);
+    pp.NT = nt1 - nt0;
     pp.rc = make_rsrc(p.codes, p.N * p.K / 2);
     pp.rs = make_rsrc(p.sclt, (p.K / 64) * p.N * 4);
     pp.rd = make_rsrc(p.dy, p.T * p.N * 2);
@@ -827,14 +833,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb, Fused
         const int64_t k = k0 + (threadIdx.x & 31) * 8;
         const int64_t n = (threadIdx.x >> 5) * 8;
         const bool ok = k < p.K;
-        pp.cvo = ok ? (uint32_t)(n * (p.K / 2) + k / 2) : kOOB;
-        pp.svo = ok ? (uint32_t)(((k / 64) * p.N + n) * 4) : kOOB;
+        const int64_t nb = n + (int64_t)nt0 * 64;                    // first n of this split
+        pp.cvo = ok ? (uint32_t)(nb * (p.K / 2) + k / 2) : kOOB;
+        pp.svo = ok ? (uint32_t)(((k / 64) * p.N + nb) * 4) : kOOB;
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const int ch = threadIdx.x + c * kThreads;
         const int64_t t = t0 + (ch >> 3);
-        pp.dvo[c] = t < p.T ? (uint32_t)((t * p.N + (ch & 7) * 8) * 2) : kOOB;
+        pp.dvo[c] = t < p.T ? (uint32_t)((t * p.N + (int64_t)nt0 * 64 + (ch & 7) * 8) * 2) : kOOB;
     }
 
     f32x16_t acc[4][4];
@@ -873,7 +880,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb, Fused
     }
     if (kt < NT) dx_tile<0, F16>(pp, kt, acc, lW, lD, wa, wb, r, h, f0, qa);
 
-    if (p.r > 0) {
+    if (p.r > 0 && split == 0) {
         // LoRA term (s dY B^T) A^T: reduction over [hi | lo] of s dY B^T against A stacked twice
         const int half = (int)(p.r_pad / 64);
         PlainRows<256, true> pa;
@@ -895,17 +902,54 @@ __global__ __launch_bounds__(kThreads, 1) void k_dx(DxArgs p, Codebook cb, Fused
             }
         }
     }
-    // C[k][t] -> dX[t][k] through an LDS tile over the W and dY tiles
-    __syncthreads();                          // every wave is done reading them
+    if constexpr (SPLIT) {
+        // fp32 partial tile part[split][k][t] through LDS in two halves: half hf
+        // holds accumulators i = 2 hf, 2 hf + 1 of every wave, LDS row
+        // 64 wa + 32 (i & 1) + q = tile row 128 wa + 32 i + q (q = 8 g + 4 h + v);
+        // the chunks of rows with bit 2 set sit 128 bytes over (distinct banks
+        // for the two halves of a wave's store); whole 1 KB rows go out as float4s
+        const int64_t ldp = (p.T + 3) & ~int64_t(3);
+        float* out = p.part + (int64_t)split * p.K * ldp;
+        float* lt = reinterpret_cast<float*>(smem_raw);                  // [128][256] fp32
+        auto loff = [](int row, int t) { return row * 256 + (t ^ (((row >> 2) & 1) << 5)); };
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int hf = 0; hf < 2; ++hf) {                                 // unrolled: acc indices stay static
+            __syncthreads();                                             // LDS readers are done
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                otile_put4<F16>(smem, acc[i][j], g, wb * 128 + j * 32 + r, wa * 128 + i * 32 + g * 8 + h * 4);
-    __syncthreads();
-    otile_store(smem, p.dx, p.K, t0, k0, p.T, p.K);
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            lt[loff(64 * wa + 32 * ii + 8 * g + 4 * h + v, wb * 128 + 32 * j + r)] =
+                                acc[2 * hf + ii][j][4 * g + v];
+            __syncthreads();
+#pragma unroll 4
+            for (int e = threadIdx.x; e < 128 * 64; e += kThreads) {     // 64 float4 per row
+                const int row = e >> 6, c4 = e & 63;
+                const int64_t k = k0 + 128 * (row >> 6) + 64 * hf + (row & 63);
+                const int64_t t = t0 + 4 * c4;
+                if (k < p.K && t < p.T) {                                 // t + 3 < ldp
+                    const float* src = lt + loff(row, 4 * c4);
+                    *reinterpret_cast<f32x4_t*>(out + k * ldp + t) = f32x4_t{src[0], src[1], src[2], src[3]};
+                }
+            }
+        }
+    } else {
+        // C[k][t] -> dX[t][k] through an LDS tile over the W and dY tiles
+        __syncthreads();                          // every wave is done reading them
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    otile_put4<F16>(smem, acc[i][j], g, wb * 128 + j * 32 + r, wa * 128 + i * 32 + g * 8 + h * 4);
+        __syncthreads();
+        otile_store(smem, p.dx, p.K, t0, k0, p.T, p.K);
+    }
 
     if constexpr (FUSED) {
         // this wave's blocks of the adapter gradients (see FusedGrads): every
@@ -981,25 +1025,34 @@ hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, BlockScales sc, c
         hipError_t e0 = hipGetLastError();
         if (e0 != hipSuccess) return e0;
     }
+    const bool split = pl.s_dx > 1;
+    float* part = split ? reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + (fused ? pl.off_dxp_fused : pl.off_dxp))
+                        : nullptr;
     DxArgs a{dy, codes, sc.fp8, sc.sup, lora_a, reinterpret_cast<const uint16_t*>(ws + pl.off_gs_hi),
              reinterpret_cast<const uint16_t*>(ws + pl.off_gs_lo), sclt, dx,
-             pl.T, pl.K, pl.N, pl.r, pl.r_pad};
+             pl.T, pl.K, pl.N, pl.r, pl.r_pad, part, pl.s_dx};
     const size_t lds = kDxSmem;
-    const int64_t tiles = ceil_div(pl.K, 256) * ceil_div(pl.T, 256);
+    const int64_t tiles = ceil_div(pl.K, 256) * ceil_div(pl.T, 256) * (split ? pl.s_dx : 1);
+    FusedGrads f = fused ? *fused : FusedGrads{};
+    f.waves = (int)tiles * 4;                         // the grid's waves share the gradient blocks
     auto go = [&](auto kern) {
         hipError_t e = set_smem(kern, lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kThreads), lds, s, a, host_codebook(),
-                           fused ? *fused : FusedGrads{});
+        hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kThreads), lds, s, a, host_codebook(), f);
         return hipGetLastError();
     };
-    if (fused) {
-        FusedGrads f = *fused;
-        f.waves = (int)tiles * 4;
-        fused = &f;
-        return f16 ? go(k_dx<true, true>) : go(k_dx<false, true>);
+    hipError_t e;
+    if (split) {
+        if (fused) e = f16 ? go(k_dx<true, true, true>) : go(k_dx<false, true, true>);
+        else e = f16 ? go(k_dx<true, false, true>) : go(k_dx<false, false, true>);
+        if (e != hipSuccess) return e;
+        const dim3 g((unsigned)ceil_div(pl.K, 64), (unsigned)ceil_div(pl.T, 64));
+        if (f16) hipLaunchKernelGGL(k_split_sum<true>, g, dim3(256), 0, s, part, pl.s_dx, pl.K, pl.T, dx);
+        else hipLaunchKernelGGL(k_split_sum<false>, g, dim3(256), 0, s, part, pl.s_dx, pl.K, pl.T, dx);
+        return hipGetLastError();
     }
-    return f16 ? go(k_dx<true, false>) : go(k_dx<false, false>);
+    if (fused) return f16 ? go(k_dx<true, true, false>) : go(k_dx<false, true, false>);
+    return f16 ? go(k_dx<true, false, false>) : go(k_dx<false, false, false>);
 }
 
 }  // namespace ql

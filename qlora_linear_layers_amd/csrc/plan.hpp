@@ -45,7 +45,8 @@ inline int down_splits(int64_t T, int64_t L) {
 // workgroups in flight of 256), plus 0.2 us per MB of partials (written and
 // read back) and 10 us for the partial tile stores and the summing launch;
 // at least 4 k tiles per split, at most 16 splits, and partials of at most
-// `max_bytes` (aligned to 256).
+// `max_bytes` (aligned to 256).  Partial rows hold T rounded up to 4 floats.
+inline int64_t split_row(int64_t T) { return (T + 3) & ~int64_t(3); }
 inline int gemm_splits(int64_t T, int64_t L, int64_t C, size_t max_bytes) {
     const int64_t tiles = ceil_div(C, 256) * ceil_div(T, 256);
     const int64_t kt = L / 64;
@@ -53,14 +54,14 @@ inline int gemm_splits(int64_t T, int64_t L, int64_t C, size_t max_bytes) {
         const int64_t wgs = tiles * S;
         const double w = (double)(wgs < 256 ? wgs : 256) / 256.0;
         double t = (double)ceil_div(wgs, 256) * (double)ceil_div(kt, S) * (1.2 + 0.5 * w);
-        if (S > 1) t += 0.2e-6 * (double)S * (double)C * (double)T * 4.0 + 10.0;
+        if (S > 1) t += 0.2e-6 * (double)S * (double)C * (double)split_row(T) * 4.0 + 10.0;
         return t;
     };
     double best = cost(1);
     int bs = 1;
     for (int S = 2; S <= 16; ++S) {
         if (kt / S < 4) break;
-        if (align256((size_t)S * C * T * 4) > max_bytes) break;
+        if (align256((size_t)S * C * split_row(T) * 4) > max_bytes) break;
         const double t = cost(S);
         if (t < best) { best = t; bs = S; }
     }
@@ -90,10 +91,15 @@ struct LoraPlan {
     // k_grad partials
     int s_fz, fz_tpg;
     size_t off_fza, off_fzb;            // fp32 [s_fz][K][r_pad], [s_fz][N][r_pad]
-    // split-k forward (s_fwd > 1): fp32 partial tiles [s_fwd][N][T] after the
+    // split-k forward (s_fwd > 1): fp32 partial tiles [s_fwd][N][T rounded up to 4] after the
     // forward's state; the backward's regions start at the end of that state
     int s_fwd;
     size_t off_fsp;
+    // split-k dX (s_dx > 1): fp32 partial tiles [s_dx][K][T rounded up to 4],
+    // over the k_grad partials (written only after dX is summed), or after
+    // the fused backward's partials (written while dX runs)
+    int s_dx;
+    size_t off_dxp, off_dxp_fused;
     size_t fwd_bytes, bwd_bytes, bwd_grad_bytes, bwd_fused_bytes;
 
     // fwd_cap: the most workspace the forward may take; the split-k partials
@@ -115,8 +121,10 @@ struct LoraPlan {
         auto splits_within = [&](size_t state) {
             const size_t room = fwd_cap > state ? fwd_cap - state : 0;
             s_fwd = gemm_splits(T, K, N, room < kSplitPartialMax ? room : kSplitPartialMax);
-            return s_fwd > 1 ? align256((size_t)s_fwd * N * T * 4) : 0;
+            return s_fwd > 1 ? align256((size_t)s_fwd * N * split_row(T) * 4) : 0;
         };
+        s_dx = gemm_splits(T, N, K, kSplitPartialMax);
+        const size_t dxp = s_dx > 1 ? align256((size_t)s_dx * K * split_row(T) * 4) : 0;
         if (r == 0) {
             const size_t fsp = splits_within(0);
             off_at = off_ps_hi = off_ps_lo = off_gs_hi = off_gs_lo = 0;
@@ -127,7 +135,8 @@ struct LoraPlan {
             off_fza = off_fzb = 0;
             off_fsp = 0;
             fwd_bytes = fsp;
-            bwd_bytes = bwd_grad_bytes = bwd_fused_bytes = scl;
+            off_dxp = off_dxp_fused = scl;
+            bwd_bytes = bwd_grad_bytes = bwd_fused_bytes = scl + dxp;
             return;
         }
         const size_t tr2 = (size_t)T * r_pad * 2, rt2 = (size_t)r_pad * ld_t * 2;
@@ -158,6 +167,9 @@ struct LoraPlan {
         off_pda = o;    o = align256(o + (size_t)s_da * K * r_pad * 4);
         off_pdb = o;    o = align256(o + (size_t)s_db * N * r_pad * 4);
         bwd_grad_bytes = o;
+        off_dxp = grad_start;
+        if (grad_start + dxp > bwd_grad_bytes) bwd_grad_bytes = grad_start + dxp;
+        if (grad_start + dxp > bwd_bytes) bwd_bytes = grad_start + dxp;
         {
             const int64_t tiles = ceil_div(T, 256);
             fz_tpg = tiles >= 4 ? 2 : 1;      // two tiles per partial halve the partials' bytes
@@ -166,7 +178,8 @@ struct LoraPlan {
         o = grad_start;
         off_fza = o;    o = align256(o + (size_t)s_fz * K * r_pad * 4);
         off_fzb = o;    o = align256(o + (size_t)s_fz * N * r_pad * 4);
-        bwd_fused_bytes = o;
+        off_dxp_fused = o;
+        bwd_fused_bytes = o + dxp;
     }
 };
 

@@ -208,22 +208,33 @@ def test_workspace_bytes_bwd(L):
 
 
 def test_workspace_bytes(L):
-    # the larger of the backward's block scales [K/64][N] fp32 and the decode
-    # path's split partials [K/512][T][N] fp32 (T <= 16, no adapter)
-    assert L.qlora_workspace_bytes(16, 4096, 4096, 0) == max((4096 // 64) * 4096 * 4, (4096 // 512) * 16 * 4096 * 4)
-    assert L.qlora_workspace_bytes(1, 4096, 4096, 0) == (4096 // 64) * 4096 * 4
-    # 16 < T <= 128 runs 16-token windows as one grouped decode launch: one window's partials each
-    assert L.qlora_workspace_bytes(64, 4096, 4096, 0) == max((4096 // 64) * 4096 * 4, 4 * (4096 // 512) * 16 * 4096 * 4)
-    assert L.qlora_workspace_bytes(40, 4096, 4096, 0) == max((4096 // 64) * 4096 * 4, 3 * (4096 // 512) * 16 * 4096 * 4)
-    # T > 128 runs 256 x 256 MFMA tiles: with 256 or more tiles only the scale table ...
-    assert L.qlora_workspace_bytes(4096, 4096, 4096, 0) == (4096 // 64) * 4096 * 4
-    # ... with fewer, the forward splits the reduction and keeps S fp32 partial
-    # tiles [S][N][T] (2 <= S <= 16, at most 64 MiB, at least 4 k tiles per split)
-    for T in (129, 300, 700, 2048):
+    # no adapter: the larger of the forward's and the backward's needs.  The
+    # forward at T <= 16 keeps the decode path's split partials [K/512][T][N]
+    # fp32, at 16 < T <= 128 one such set per 16-token window; the backward
+    # keeps the dX kernel's block scales [K/64][N] fp32 and, while dX has too
+    # few 256 x 256 tiles for the chip, S (2..16) fp32 partial tiles [S][K][T
+    # rounded up to 4]
+    scl = (4096 // 64) * 4096 * 4
+
+    def dx_splits(T, n):
+        ldp = -(-T // 4) * 4
+        S, rest = divmod(n - scl, 4096 * ldp * 4)
+        return S if rest == 0 else -1
+
+    for T, fwd in ((16, (4096 // 512) * 16 * 4096 * 4), (1, (4096 // 512) * 1 * 4096 * 4),
+                   (64, 4 * (4096 // 512) * 16 * 4096 * 4), (40, 3 * (4096 // 512) * 16 * 4096 * 4)):
         n = L.qlora_workspace_bytes(T, 4096, 4096, 0)
-        split = n // (4096 * T * 4)
-        assert n > (4096 // 64) * 4096 * 4 and n % 256 == 0
-        assert 2 <= split <= 16 and n <= -(-16 * 4096 * T * 4 // 256) * 256 and n <= 64 << 20
+        assert n >= fwd and n >= scl
+        assert n == fwd or 2 <= dx_splits(T, n) <= 16, (T, n)
+    # T > 128 runs 256 x 256 MFMA tiles: with 256 or more tiles only the scale table ...
+    assert L.qlora_workspace_bytes(4096, 4096, 4096, 0) == scl
+    # ... with fewer, the forward and dX split their reductions and keep S fp32
+    # partial tiles [S][N or K][T rounded up to 4] (2 <= S <= 16, at most
+    # 64 MiB, at least 4 k tiles per split); on a square weight both take the
+    # same S, so the backward's scale table plus its partials is the larger
+    for T in (129, 300, 333, 700, 2048):
+        n = L.qlora_workspace_bytes(T, 4096, 4096, 0)
+        assert n % 256 == 0 and 2 <= dx_splits(T, n) <= 16 and n <= scl + (64 << 20), (T, n)
     assert L.qlora_workspace_bytes(1 << 23, 4096, 4096, 16) == 0                     # T too large
     assert L.qlora_workspace_bytes(16, 100, 4096, 16) == 0
     a = L.qlora_workspace_bytes(4096, 4096, 11008, 64)

@@ -1,7 +1,8 @@
-"""GPU parity of the split-k forward: when a weight's 256 x 256 output tiles fill
-too little of the chip (T from 129 to a few thousand on the 7B shapes), several
-workgroups share each tile's reduction over K and one launch adds their fp32
-partial tiles in split order.  Y against the fp64 oracle rounded once (max
+"""GPU parity of the split-k GEMMs: when a product's 256 x 256 output tiles fill
+too little of the chip (the forward at T from 129 to a few thousand on the 7B
+shapes, dX = dY W' at any T up to that), several workgroups share each tile's
+reduction (over K for Y, over N for dX) and one launch adds their fp32 partial
+tiles in split order.  Outputs against the fp64 oracle rounded once (max
 relative error <= 1e-2 with the rms floor, mean absolute error <= 1e-3 rms), in
 full; the LoRA term rides on the first split."""
 import numpy as np
@@ -88,3 +89,70 @@ def test_split_forward_fp16_and_single_quantization():
     y = api.qlora_linear_fwd(to_dev(d["x"], (T, lin.K)), qw, to_dev(d["a"], (lin.K, r)), to_dev(d["b"], (r, lin.N)), s)
     torch.cuda.synchronize()
     assert_gemm_close(bits_of(y), oracle.linear_fwd(d["x"], wd, d["a"], d["b"], s), "single-quantization Y")
+
+
+# (name, weight [N, K], T, r, s): dX [T, K] with its reduction over N split;
+# ragged K, T (not a multiple of 4) and N tails, padded ranks, no adapter, a
+# decode-size backward, and the 7B q and down shapes
+BWD_CASES = [
+    ("ragged", synth.Linear("t", 1088, 2560), 301, 72, 0.5),
+    ("no adapter", synth.Linear("t", 2048, 1024), 520, 0, 0.0),
+    ("T = 16", synth.Linear("t", 1024, 2048), 16, 16, 1.0),
+    ("7B q at T = 512", synth.LLAMA7B[0], 512, 64, 0.25),
+    ("7B down at T = 258", synth.LLAMA7B[6], 258, 64, 0.25),
+]
+
+
+@pytest.mark.parametrize("name,lin,T,r,s", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_split_backward_against_oracle(name, lin, T, r, s):
+    """dX, dA and dB against the oracle; the fused backward gives the same dX bits."""
+    say(f"[split-k bwd] {name}: T={T} N={lin.N} K={lin.K} r={r}")
+    d = synth.layer_inputs(9, 0, 0, lin, T, r, with_dy=True)
+    qw = api.nf4_quantize_dq(to_dev(d["w"], (lin.N, lin.K)))
+    rc, rf, rs = oracle.quantize_nf4_dq(d["w"])
+    wd = oracle.dequantize_nf4_dq(rc, rf, rs).reshape(lin.N, lin.K)
+    x = to_dev(d["x"], (T, lin.K))
+    dy = to_dev(d["dy"], (T, lin.N))
+    a = to_dev(d["a"], (lin.K, r)) if r else None
+    b = to_dev(d["b"], (r, lin.N)) if r else None
+    dx, da, db = api.qlora_linear_bwd_input(dy, qw, a, b, s, x=x if r else None, lora_grads=bool(r))
+    torch.cuda.synchronize()
+    rdx, rda, rdb = oracle.linear_bwd(d["dy"], d["x"], wd, d["a"] if r else None, d["b"] if r else None, s)
+    assert_gemm_close(bits_of(dx), rdx, f"{name} dX")
+    if r:
+        assert_gemm_close(bits_of(da), rda, f"{name} dA")
+        assert_gemm_close(bits_of(db), rdb, f"{name} dB")
+        fdx, fda, fdb = api.qlora_linear_bwd_input(dy, qw, a, b, s, x=x, lora_grads=True, fused_grads=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(fdx), bits_of(dx)), f"{name}: fused dX differs"
+        assert_gemm_close(bits_of(fda), rda, f"{name} fused dA")
+        assert_gemm_close(bits_of(fdb), rdb, f"{name} fused dB")
+
+
+def test_split_backward_fp16_and_single_quantization():
+    lin, T, r, s = synth.Linear("t", 2048, 1024), 262, 16, 1.0
+    say(f"[split-k bwd] fp16 and single quantization: T={T} N={lin.N} K={lin.K} r={r}")
+    d = synth.layer_inputs_f16(9, 0, 0, lin, T, r, with_dy=True)
+    h = lambda bits, shape: torch.from_numpy(np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+                                             .view(np.int16)).view(torch.float16).reshape(shape).cuda()
+    qw = api.nf4_quantize_dq(h(d["w"], (lin.N, lin.K)))
+    rc, rf, rs = oracle.quantize_nf4_dq_f16(d["w"])
+    wd = oracle.dequantize_nf4_dq_f16(rc, rf, rs).reshape(lin.N, lin.K)
+    dx, _, _ = api.qlora_linear_bwd_input(h(d["dy"], (T, lin.N)), qw, h(d["a"], (lin.K, r)), h(d["b"], (r, lin.N)), s,
+                                          x=h(d["x"], (T, lin.K)), lora_grads=True)
+    torch.cuda.synchronize()
+    rdx, _, _ = oracle.linear_bwd_f16(d["dy"], d["x"], wd, d["a"], d["b"], s)
+    g = oracle.f16_bits_to_f64(bits_of(dx)).reshape(-1)
+    rr = oracle.f16_bits_to_f64(rdx).reshape(-1)
+    rms = np.sqrt(np.mean(rr * rr))
+    err = np.abs(g - rr)
+    assert float(np.max(err / np.maximum(np.abs(rr), rms))) <= 1e-2 and float(np.mean(err) / rms) <= 1e-3
+    d = synth.layer_inputs(9, 0, 0, lin, T, r, with_dy=True)
+    qw = api.nf4_quantize(to_dev(d["w"], (lin.N, lin.K)))
+    rc, ra = oracle.quantize_nf4_sq(d["w"])
+    wd = oracle.dequantize_nf4_sq(rc, ra).reshape(lin.N, lin.K)
+    dx, _, _ = api.qlora_linear_bwd_input(to_dev(d["dy"], (T, lin.N)), qw, to_dev(d["a"], (lin.K, r)),
+                                          to_dev(d["b"], (r, lin.N)), s, x=to_dev(d["x"], (T, lin.K)), lora_grads=True)
+    torch.cuda.synchronize()
+    rdx, _, _ = oracle.linear_bwd(d["dy"], d["x"], wd, d["a"], d["b"], s)
+    assert_gemm_close(bits_of(dx), rdx, "single-quantization dX")
