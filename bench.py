@@ -531,7 +531,7 @@ def measure_step_midt(api, torch, layers, sets, r, s, tokens=(256, 512, 1024, 20
 
 
 def measure_prefill(api, torch, layers, sets, r, s, tokens=(32, 64), reps=6):
-    """Small-prefill forward (16 < T <= 128 runs 16-token windows as one grouped
+    """Small-prefill forward (16 < T <= 96 runs 16-token windows as one grouped
     decode launch) over the seven linears, one weight copy per pass.
     Returns {T: (seconds per layer set, bytes per layer set, flops per layer set)}."""
     copies = len(sets)

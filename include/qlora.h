@@ -145,9 +145,9 @@ int nf4_dequantize_dq_grouped(int count, const nf4_tensor* tensors, void* stream
  * qlora_workspace_bytes - device workspace (bytes) that qlora_linear_fwd and
  *   qlora_linear_bwd_input need for these sizes (the larger of the two).
  *   Returns 0 for sizes the entry points would reject.  The size is not
- *   monotone in T: 16 < T <= 128 keeps one set of split partials per 16-token
- *   window and can need more than a larger T (for example about 46 MB at
- *   T = 128 against about 21 MB at T = 4096 on an 11008 x 4096 weight with
+ *   monotone in T: 16 < T <= 96 keeps one set of split partials per 16-token
+ *   window and can need more than a larger T (for example about 34 MB at
+ *   T = 96 against about 26 MB at T = 4096 on an 11008 x 4096 weight with
  *   r = 64), and a mid-size T whose 256 x 256 output tiles are too few to
  *   fill the chip splits the reduction over several workgroups with fp32
  *   partial tiles (at most 64 MiB; 64 MiB for a 4096 x 4096 weight at
@@ -188,7 +188,7 @@ size_t qlora_workspace_bytes_bwd(int64_t T, int64_t K, int64_t N, int64_t r, uns
  *   workspace: device scratch of at least qlora_workspace_bytes(T, K, N, r)
  *   bytes (may be NULL if that is 0); its contents on entry do not matter.
  *   Kernels by size: T <= 16 runs the decode kernels (small-M MFMA, weight
- *   stream read once); 16 < T <= 128 runs them on 16-token windows as one
+ *   stream read once); 16 < T <= 96 runs them on 16-token windows as one
  *   grouped launch; larger T runs the 256 x 256-tile MFMA GEMM, whose
  *   reduction over K is split over up to 16 workgroups per tile (fp32
  *   partials in the workspace, added in split order by one more launch) when
@@ -218,7 +218,7 @@ int qlora_linear_fwd(const uint16_t* x, int64_t T, int64_t K, int64_t N,
  *     QLORA_BWD_REUSE_FORWARD when `workspace` still holds what a
  *       qlora_linear_fwd with the same x, lora_a, scaling and sizes left there
  *       (nothing else used it since): s X A is then taken from it instead of
- *       being recomputed for dB.  Ignored for T <= 128 (the decode-kernel
+ *       being recomputed for dB.  Ignored for T <= 96 (the decode-kernel
  *       forward keeps nothing).  With a stale workspace the flag gives wrong
  *       dB.
  *     QLORA_BWD_FUSED_GRADS: dA and dB come from the dX kernel itself, each

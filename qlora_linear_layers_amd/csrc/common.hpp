@@ -335,9 +335,11 @@ hipError_t launch_dequantize(const uint8_t* codes, BlockScales sc, int64_t numel
 // Forward calls with at most this many tokens take the decode (small-M MFMA) path.
 constexpr int64_t kGemvMaxT = 16;
 // Forward sizes T (kGemvMaxT < T <= kChunkMaxT) that run as kGemvMaxT-token
-// windows through one grouped decode launch: each window streams the weight,
-// which beats one pass of 256-token MFMA tiles that leave most CUs idle.
-constexpr int64_t kChunkMaxT = 128;
+// windows through one grouped decode launch: each window streams the weight.
+// Up to 96 tokens that beats the split-k MFMA tiles (the LLaMA-7B projections:
+// 371 against 397 us at T = 96); from about 100 tokens the tiles win (395
+// against 456 us at T = 128).
+constexpr int64_t kChunkMaxT = 96;
 struct LoraPlan;
 ScalesJob scales_job_for(BlockScales sc, const LoraPlan& pl, uint8_t* ws);
 size_t gemv_workspace(int64_t T, int64_t K, int64_t N, int64_t r_pad);

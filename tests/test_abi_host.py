@@ -62,13 +62,13 @@ def test_codebook_bit_exact(L):
 
 
 def test_workspace_upto_covers_every_token_count(L):
-    """qlora_workspace_bytes is not monotone in T (16 < T <= 128 keeps one set of
+    """qlora_workspace_bytes is not monotone in T (16 < T <= 96 keeps one set of
     split partials per 16-token window); the _upto size is the maximum over T."""
     for K, N, r in ((4096, 11008, 64), (11008, 4096, 64), (448, 320, 24), (256, 256, 0)):
         sizes = [L.qlora_workspace_bytes(T, K, N, r) for T in range(1, 301)]
         for T_max in (1, 16, 17, 100, 128, 129, 300):
             assert L.qlora_workspace_bytes_upto(T_max, K, N, r) == max(sizes[:T_max])
-    assert L.qlora_workspace_bytes(128, 4096, 11008, 64) > L.qlora_workspace_bytes(4096, 4096, 11008, 64)
+    assert L.qlora_workspace_bytes(96, 4096, 11008, 64) > L.qlora_workspace_bytes(4096, 4096, 11008, 64)
     assert L.qlora_workspace_bytes_upto(0, 4096, 4096, 64) == 0
 
 
@@ -105,8 +105,8 @@ def test_noalloc_forward_validation(L):
             assert L.qlora_workspace_bytes(T, K, N, 64) > 0
             assert call(T, K, N, 64) == DEVICE, (T, K, N)
             assert call(T, K, N, 0) == DEVICE, (T, K, N)
-    # windows of the 7B gate at T = 128 (one decode workspace per 16-token window) do not
-    assert call(128, 4096, 11008, 64) == WORKSPACE
+    # windows of the 7B gate at T = 96 (one decode workspace per 16-token window) do not
+    assert call(96, 4096, 11008, 64) == WORKSPACE
     assert call(1 << 20, 1024, 1024, 64) == WORKSPACE
 
 
@@ -200,7 +200,7 @@ def test_workspace_bytes_bwd(L):
         ceil256 = lambda v: -(-v // 256) * 256
         assert fused - ceil256(tiles * K * r_pad * 4) - ceil256(tiles * N * r_pad * 4) < plain
         assert fused >= ceil256(tiles * K * r_pad * 4) + ceil256(tiles * N * r_pad * 4)
-        assert plain >= L.qlora_workspace_bytes(T, K, N, r) or T <= 128
+        assert plain >= L.qlora_workspace_bytes(T, K, N, r) or T <= 96
     assert f(16, 100, 64, 16, 0) == 0                      # rejected sizes
     assert f(300, 256, 320, 16, 4) == 0                    # unknown flag
     # without an adapter there are no gradients: the scale table alone
@@ -210,7 +210,7 @@ def test_workspace_bytes_bwd(L):
 def test_workspace_bytes(L):
     # no adapter: the larger of the forward's and the backward's needs.  The
     # forward at T <= 16 keeps the decode path's split partials [K/512][T][N]
-    # fp32, at 16 < T <= 128 one such set per 16-token window; the backward
+    # fp32, at 16 < T <= 96 one such set per 16-token window; the backward
     # keeps the dX kernel's block scales [K/64][N] fp32 and, while dX has too
     # few 256 x 256 tiles for the chip, S (2..16) fp32 partial tiles [S][K][T
     # rounded up to 4]
@@ -226,7 +226,7 @@ def test_workspace_bytes(L):
         n = L.qlora_workspace_bytes(T, 4096, 4096, 0)
         assert n >= fwd and n >= scl
         assert n == fwd or 2 <= dx_splits(T, n) <= 16, (T, n)
-    # T > 128 runs 256 x 256 MFMA tiles: with 256 or more tiles only the scale table ...
+    # T > 96 runs 256 x 256 MFMA tiles: with 256 or more tiles only the scale table ...
     assert L.qlora_workspace_bytes(4096, 4096, 4096, 0) == scl
     # ... with fewer, the forward and dX split their reductions and keep S fp32
     # partial tiles [S][N or K][T rounded up to 4] (2 <= S <= 16, at most

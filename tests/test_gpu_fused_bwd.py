@@ -30,7 +30,7 @@ def _case(lin, T, r, cfg=9):
 # (name, weight [N, K], T, r, s): ragged tiles in every dimension, padded ranks,
 # more gradient blocks than waves and fewer, one-tile token groups (T < 1024)
 # and two-tile groups with a ragged last group (T = 1100: five tiles), and a
-# T <= 128 backward (its forward runs decode windows)
+# T <= 96 backward (its forward runs decode windows)
 CASES = [
     ("ragged", synth.Linear("t", 448, 320), 300, 16, 1.0),
     ("multi-tile", synth.Linear("t", 768, 1024), 520, 64, 0.25),

@@ -51,12 +51,12 @@ def test_multi_tile_rank64():
     _run_full("multi-tile", synth.Linear("t", 768, 1024), T=520, r=64, s=0.25)
 
 
-@pytest.mark.parametrize("T,r", [(300, 72), (300, 136), (300, 256), (129, 136), (100, 136)])
+@pytest.mark.parametrize("T,r", [(300, 72), (300, 136), (300, 256), (97, 136), (90, 136)])
 def test_ranks_above_64(T, r):
     """Padded ranks (r_pad = 128, 192, 256): the wide down-projection variants,
     the forward GEMM's LoRA reduction over several 64-rank groups, several
     64-rank groups in the adapter gradients, zero rank padding.  T = 300 and
-    the boundary T = 129 run the 256-token MFMA tiles; T = 100 the 16-token
+    the boundary T = 97 run the 256-token MFMA tiles; T = 90 the 16-token
     decode windows."""
     _run_full(f"T={T} r={r}", synth.Linear("t", 384, 448), T=T, r=r, s=0.75)
 
@@ -74,12 +74,12 @@ def test_short_token_tile():
     _run_full("T=40", synth.Linear("t", 320, 448), T=40, r=8, s=1.5)
 
 
-@pytest.mark.parametrize("T", [17, 33, 95, 127, 128, 129])
+@pytest.mark.parametrize("T", [17, 33, 95, 96, 97, 128, 129])
 def test_chunked_small_prefill(T):
-    """16 < T <= 128 runs 16-token windows as one grouped decode launch (the last
-    window overlaps its predecessor for 17, 33, 95 and 127 and writes only its
-    new rows); T = 129 takes the 256-token MFMA tiles.  Forward and backward
-    against the oracle."""
+    """16 < T <= 96 runs 16-token windows as one grouped decode launch (the last
+    window overlaps its predecessor for 17, 33 and 95 and writes only its new
+    rows); T = 97, 128 and 129 take the 256-token MFMA tiles.  Forward and
+    backward against the oracle."""
     _run_full(f"T={T}", synth.Linear("t", 320, 448), T=T, r=24, s=0.75)
 
 
