@@ -935,6 +935,13 @@ def main():
                                       "us_per_layer_set": round(1e6 * secs, 2),
                                       "note": "7 linears, r=64, forward at a token count whose 256x256 tiles fill "
                                               "part of the chip (split-k where it pays); weights rotated over 6 copies"}
+        for Tm, (secs, flops) in measure_step_midt(api, torch, layers7, sets, r7, s7).items():
+            comp[f"train_step_T{Tm}"] = {"TFLOP/s": round(flops / secs / 1e12, 1),
+                                         "frac_of_mfma_peak": round(flops / secs / MFMA_BF16_PEAK, 4),
+                                         "us_per_layer_set": round(1e6 * secs, 2),
+                                         "note": "7 linears, r=64: forward, then dX, dA, dB with s X A reused, at a "
+                                                 "token count whose tiles fill part of the chip (split-k forward and "
+                                                 "dX); weights rotated over 6 copies"}
         for Tp, (secs, nbytes, flops) in measure_prefill(api, torch, layers7, sets, r7, s7).items():
             comp[f"prefill_T{Tp}"] = {"TFLOP/s": round(flops / secs / 1e12, 1), "GB/s": round(nbytes / secs / 1e9, 1),
                                       "frac_of_hbm_peak": round(nbytes / secs / HBM_PEAK, 4),
