@@ -198,7 +198,7 @@ struct FwdArgs {
     const uint16_t* ps_lo;
     uint16_t* y;
     int64_t T, K, N, r, r_pad;
-    float* part;              // split-k: fp32 partial tiles [splits][N][T]
+    float* part;              // split-k: fp32 partial tiles [splits][N][T rounded up to 4]
     int splits;
 };
 
