@@ -154,18 +154,24 @@ def layer_65b_buffers(api, torch, synth):
 
 
 def run_step(torch, step, nev, steps, warmup):
-    """`warmup` untimed steps, then `steps` timed ones; returns (wall seconds of the
-    timed region, per-step event lists)."""
+    """`warmup` untimed steps, then `steps` timed ones with nothing but the step's
+    own launches on the stream, then `steps` more with an event after every phase
+    for the per-phase breakdown (each event record costs the stream a few
+    microseconds, so the timed steps carry none); returns (wall seconds of the
+    timed region, per-step event lists of the instrumented steps)."""
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
     all_events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     for k in range(steps):
         step(all_events[k])
     torch.cuda.synchronize()
-    return time.perf_counter() - t0, all_events
+    return wall, all_events
 
 
 def layer_step(api, bufs, T, r, s, ws, stream, with_grads, fused=False):
