@@ -41,6 +41,7 @@ CASES = [
     ("7B q at T = 512", synth.LLAMA7B[0], 512, 64, 0.25),
     ("7B gate at T = 2048", synth.LLAMA7B[4], 2048, 64, 0.25),
     ("7B down at T = 1024", synth.LLAMA7B[6], 1024, 64, 0.25),
+    ("7B down at T = 256 (16 splits)", synth.LLAMA7B[6], 256, 64, 0.25),
 ]
 
 
