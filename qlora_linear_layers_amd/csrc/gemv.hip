@@ -14,15 +14,20 @@
 // lane group g (lanes 16g .. 16g+15) takes the 32 consecutive k at 32g for
 // both operands: one 16-byte code load per W row and four 16-byte X loads
 // per lane, and sub-step j of the step uses k 32g + 8j .. +7.  The codes of
-// one byte (two weights) are looked up in the 32-way replicated pair table
-// (one byte permute builds the LDS address), scaled by the block constant,
-// rounded to bf16 and packed: the per-weight work does not grow with T.
+// one byte (two weights) are looked up in the 16-way replicated pair table
+// (32 KB; a bit-field extract and a shift-or build the LDS address), scaled
+// by the block constant, rounded to bf16 and packed: the per-weight work does
+// not grow with T.
 //
 // Workgroup (kKW, kRG below): eight waves, two groups of 64 W rows (four
 // 16-row MFMA tiles per wave) times four 128-wide k steps, so 128 rows x 512 k;
 // the k waves of a row group are added in LDS in wave order and one fp32 partial per
 // (k split, token, row) is written.  The LoRA down projection runs as extra
-// workgroups of the same launch over 256-wide k slices (VALU, lane = rank).
+// workgroups of the same launch over 256-wide k slices (VALU).  With the
+// 32 KB table and at most 80 registers, three workgroups share a CU: the
+// kernel's time is set by how many units' latencies overlap, not by any one
+// unit's work, and the third workgroup per CU (over the 64 KB table's two)
+// pays for the extra address instruction per code byte.
 #include <type_traits>
 
 #include "common.hpp"
@@ -73,16 +78,20 @@ constexpr int kRG = 2;            // row groups of 64 W rows
 constexpr int kDecThreads = 64 * kKW * kRG;
 constexpr int kDecRows = 64 * kRG;  // W rows per workgroup
 constexpr int kDecK = 128 * kKW;    // k per workgroup
-static_assert(kRG * kKW * 4 * 64 * 16 <= (int)kWideTableBytes, "wave sums must fit over the pair table");
+static_assert(kRG * kKW * 4 * 64 * 16 <= (int)kNarrowTableBytes, "wave sums must fit over the pair table");
+static_assert(4 * 2 * kGemvMaxT * 64 * 4 <= (int)kNarrowTableBytes, "LoRA block sums must fit in the table's space");
 static_assert(kRG * kKW * 4 * 8 * 64 * 4 <= (int)kWideTableBytes, "VALU wave sums (8 tokens) must fit too");
 constexpr int kLoraSlice = 256;   // k per LoRA down-projection workgroup (one 64-k chunk per wave)
-constexpr size_t kDecLds = kWideTableBytes;   // pair table; later reused for the wave sums
+constexpr size_t kDecLds = kWideTableBytes;   // VALU form: pair table; later reused for the wave sums
 
 // LoRA down-projection partials of one 256-wide k slice and 64 ranks:
 // lpart[kl][t][j] = sum_{k in slice} X[t][k] A[k][j].  X[0:TT][slice] is
-// staged in LDS; waves 0-3 take a quarter of the slice each: lane j loads
-// its 64 A values in one burst and reads X as LDS broadcasts.  Every thread
-// of the workgroup reaches every barrier.
+// staged in LDS; waves 0-3 take a quarter of the slice (64 rows of A) each.
+// Lane (h, q) of a wave holds ranks 2q, 2q + 1 of rows 32h .. 32h + 31 of its
+// quarter, one 4-byte load per row issued in one burst (32 registers), and
+// reads X as LDS broadcasts; the eight (wave, half) sums of every output are
+// then added in LDS in that order.  Every thread of the workgroup reaches
+// every barrier.
 template <int TT, bool F16>
 __device__ __forceinline__ void lora_down_block(const GemvArgs& p, uint8_t* dyn, int lb) {
     typedef __attribute__((address_space(3))) float g_lds_f32_t;
@@ -90,7 +99,8 @@ __device__ __forceinline__ void lora_down_block(const GemvArgs& p, uint8_t* dyn,
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int jc = lb % (int)(p.r_pad / 64), kl = lb / (int)(p.r_pad / 64);
-    const int64_t j = (int64_t)jc * 64 + lane;
+    const int h = lane >> 5, q = lane & 31;
+    const int64_t j0 = (int64_t)jc * 64 + 2 * q;                       // this lane's two ranks
     const int64_t k0 = (int64_t)kl * kLoraSlice;
     const rsrc_t rx = make_rsrc(p.x, p.T * p.K * 2);
     for (int ch = threadIdx.x; ch < TT * (kLoraSlice / 8); ch += kDecThreads) {
@@ -100,46 +110,59 @@ __device__ __forceinline__ void lora_down_block(const GemvArgs& p, uint8_t* dyn,
         *reinterpret_cast<lds_u32x4_t*>(xl + (t * kLoraSlice + (ch % (kLoraSlice / 8)) * 8) * 2) = v;
     }
     __syncthreads();
-    float acc[TT];
+    float acc[TT][2];
 #pragma unroll
-    for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
+    for (int t = 0; t < TT; ++t) acc[t][0] = acc[t][1] = 0.0f;
     if (wave < 4) {
-        // A[k][j] by buffer loads: ranks j >= r get an offset past the end, and
-        // so do rows k >= K (their offset is at least K r 2 bytes), both read 0
+        // A[k][j0], A[k][j0 + 1] as one dword (r is a multiple of 8, so both
+        // ranks exist or neither): ranks j0 >= r get an offset past the end,
+        // and so do rows k >= K (their offset is at least K r 2 bytes), both
+        // read 0
         const rsrc_t ra = make_rsrc(p.lora_a, p.K * p.r * 2);
-        const int kw = (kLoraSlice / 4) * wave;                         // chunk start inside the slice
-        const uint32_t vo = j < p.r ? (uint32_t)(((k0 + kw) * p.r + j) * 2) : kOOB;
+        const int kw = (kLoraSlice / 4) * wave + 32 * h;               // first row of this lane's 32
+        const uint32_t vo = j0 < p.r ? (uint32_t)(((k0 + kw) * p.r + j0) * 2) : kOOB;
         const uint32_t row = (uint32_t)(p.r * 2);
-        float av[64];
+        uint32_t av[32];
 #pragma unroll
-        for (int i = 0; i < 64; ++i) av[i] = lo16<F16>(bload2(ra, vo + i * row, 0));
+        for (int i = 0; i < 32; ++i) av[i] = bload4(ra, vo + i * row, 0);
+        // rows in order for every token (8 rows per step, every token per step)
 #pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            float v = acc[t];
+        for (int c = 0; c < 4; ++c) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
+            for (int t = 0; t < TT; ++t) {
                 const u32x4_t xv = *reinterpret_cast<const lds_u32x4_t*>(xl + (t * kLoraSlice + kw + 8 * c) * 2);
+                float v0 = acc[t][0], v1 = acc[t][1];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    v = fmaf(lo16<F16>(xv[e]), av[8 * c + 2 * e], v);
-                    v = fmaf(hi16<F16>(xv[e]), av[8 * c + 2 * e + 1], v);
+                    const float xa = lo16<F16>(xv[e]), xb = hi16<F16>(xv[e]);
+                    const uint32_t ra0 = av[8 * c + 2 * e], ra1 = av[8 * c + 2 * e + 1];
+                    v0 = fmaf(xa, lo16<F16>(ra0), v0);
+                    v1 = fmaf(xa, hi16<F16>(ra0), v1);
+                    v0 = fmaf(xb, lo16<F16>(ra1), v0);
+                    v1 = fmaf(xb, hi16<F16>(ra1), v1);
                 }
+                acc[t][0] = v0;
+                acc[t][1] = v1;
             }
-            acc[t] = v;
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     __syncthreads();
-    g_lds_f32_t* red = (g_lds_f32_t*)dyn;                              // [4][TT][64]
+    g_lds_f32_t* red = (g_lds_f32_t*)dyn;                              // [4 waves][2 halves][TT][64]
     if (wave < 4) {
 #pragma unroll
-        for (int t = 0; t < TT; ++t) red[(wave * TT + t) * 64 + lane] = acc[t];
+        for (int t = 0; t < TT; ++t) {
+            red[((wave * 2 + h) * TT + t) * 64 + 2 * q] = acc[t][0];
+            red[((wave * 2 + h) * TT + t) * 64 + 2 * q + 1] = acc[t][1];
+        }
     }
     __syncthreads();
     for (int i = threadIdx.x; i < TT * 64; i += kDecThreads) {
         const int t = i >> 6, jj = i & 63;
         if (t < p.T) {
-            const float v = red[(0 * TT + t) * 64 + jj] + red[(1 * TT + t) * 64 + jj] +
-                            red[(2 * TT + t) * 64 + jj] + red[(3 * TT + t) * 64 + jj];
+            float v = red[t * 64 + jj];
+#pragma unroll
+            for (int u = 1; u < 8; ++u) v += red[(u * TT + t) * 64 + jj];
             p.lpart[((int64_t)kl * p.T + t) * p.r_pad + jc * 64 + jj] = v;
         }
     }
@@ -161,7 +184,7 @@ __device__ __forceinline__ void lora_down_block(const GemvArgs& p, uint8_t* dyn,
 // the two of the dequantization, where the MFMA form adds a quarter of an
 // MFMA whatever T is.
 template <int TT, bool SQ, bool F16, bool DOT>
-__global__ __launch_bounds__(kDecThreads) void k_gemv(GemvGroup grp, Codebook cb) {
+__global__ __launch_bounds__(kDecThreads, (DOT || (F16 && TT > 8)) ? 4 : 6) void k_gemv(GemvGroup grp, Codebook cb) {
     static_assert(!DOT || TT <= kGemvValuMaxT, "VALU product: up to 8 tokens");
     constexpr bool LX = DOT && TT > 4;                                 // X staged in LDS
     extern __shared__ __align__(16) uint8_t dyn[];
@@ -230,16 +253,20 @@ __global__ __launch_bounds__(kDecThreads) void k_gemv(GemvGroup grp, Codebook cb
                 xv[t][j] = bload16(rx, xok ? (uint32_t)((tx * p.K + kk + 8 * j) * 2) : kOOB, 0);
         }
     }
-    if (threadIdx.x < 256) build_wide_pair_table(tbl, cb);
+    if (threadIdx.x < 256) {
+        if constexpr (DOT) build_wide_pair_table(tbl, cb);
+        else build_pair_table16(tbl, cb);
+    }
     __syncthreads();
 
-    const uint32_t lane8 = lds_addr(tbl) + (uint32_t)(lane & 31) * 8u;   // table at LDS address 0
+    const uint32_t lane8 = lds_addr(tbl) + (uint32_t)(lane & (DOT ? 31 : 15)) * 8u;   // table at LDS address 0
     // address bytes of a pair lookup: [0] lane copy, [1] code byte b, [2..3] table base
     auto dequant4 = [&](uint32_t codes4, float c1p) {
         u32x4_t w;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const uint32_t addr = __builtin_amdgcn_perm(codes4, lane8, 0x03020000u | ((4u + b) << 8));
+            const uint32_t addr = DOT ? __builtin_amdgcn_perm(codes4, lane8, 0x03020000u | ((4u + b) << 8))
+                                      : ((__builtin_amdgcn_ubfe(codes4, 8 * b, 8) << 7) | lane8);
             const f32x2_t q = *lds_at<f32x2_t>(addr);
             w[b] = pack16x2<F16>(__fmul_rn(q[0], c1p), __fmul_rn(q[1], c1p));
         }
@@ -511,7 +538,7 @@ hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int
     const Codebook& cb = host_codebook();
     const dim3 grid((unsigned)(nl + nbase));
     hipError_t ae = hipSuccess;
-    size_t lds = kDecLds;
+    size_t lds = dot ? kDecLds : (size_t)kNarrowTableBytes;
     auto go = [&](auto kern) {
         // 64 KB (and more) of dynamic LDS: above the default limit
         ae = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
