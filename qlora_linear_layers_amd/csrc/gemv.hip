@@ -24,10 +24,10 @@
 // the k waves of a row group are added in LDS in wave order and one fp32 partial per
 // (k split, token, row) is written.  The LoRA down projection runs as extra
 // workgroups of the same launch over 256-wide k slices (VALU).  With the
-// 32 KB table and at most 80 registers, three workgroups share a CU: the
-// kernel's time is set by how many units' latencies overlap, not by any one
-// unit's work, and the third workgroup per CU (over the 64 KB table's two)
-// pays for the extra address instruction per code byte.
+// 32 KB table and at most 80 registers, at least three workgroups share a CU:
+// the kernel's time is set by how many units' latencies overlap, not by any
+// one unit's work, and the third workgroup per CU (over the 64 KB table's
+// two) pays for the extra address instruction per code byte.
 #include <type_traits>
 
 #include "common.hpp"

@@ -92,6 +92,20 @@ def test_merge_7b_q_full():
     _assert_merge_close(got, oracle.merge_lora(wd, d["a"], d["b"], s), wd, d["a"], d["b"], s, "q 4096x4096")
 
 
+def test_merge_several_tiles_per_workgroup():
+    """N = 8192, K = 2880, r = 64, in full: a workgroup walks three 256-wide k
+    tiles of its 64-row block (an odd count, so the pair after the third is
+    empty), and the last tile of every row holds only 64 valid k."""
+    lin = synth.Linear("t", 8192, 2880)
+    say(f"[merge] {lin.N}x{lin.K} r=64 (full, three k tiles per workgroup)")
+    d, qw, (rc, rf, rs) = _setup(lin, 64, cfg=5)
+    wd = oracle.dequantize_nf4_dq(rc, rf, rs).reshape(lin.N, lin.K)
+    a, b = to_dev(d["a"], (lin.K, 64)), to_dev(d["b"], (64, lin.N))
+    got = bits_of(api.qlora_merge_lora(qw, a, b, 0.75))
+    torch.cuda.synchronize()
+    _assert_merge_close(got, oracle.merge_lora(wd, d["a"], d["b"], 0.75), wd, d["a"], d["b"], 0.75, "8192x2880")
+
+
 @pytest.mark.parametrize("idx", [4, 6])
 def test_merge_7b_sampled_rows(idx):
     lin = synth.LLAMA7B[idx]
