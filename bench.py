@@ -36,15 +36,22 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # bytes/s, published
 MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16, published
-GEMM_SOURCE = os.path.join(ROOT, "qlora_linear_layers_amd", "csrc", "gemm.hip")
+# k_fwd's source: the kernel file and the headers it includes
+GEMM_SOURCES = [os.path.join(ROOT, "qlora_linear_layers_amd", "csrc", f)
+                for f in ("gemm.hip", "common.hpp", "grad.hpp", "plan.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fwd_llama65b_T2048_traffic.txt")
 COPY_BYTES = 256 << 20     # calibration copy for the HBM byte counters
 
 
 def source_hash():
+    """sha256[:16] over k_fwd's source files in order: the stored HBM traffic is used
+    only while it was measured on exactly this code."""
     import hashlib
-    with open(GEMM_SOURCE, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in GEMM_SOURCES:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic():

@@ -117,12 +117,13 @@ QL_DEV f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 // ------------------------------------------------------------------ FP8 E4M3FN
 
 // Exact value of a non-negative E4M3FN code (0x00..0x7E): bias 7, 3 fraction
-// bits, subnormal spacing 2^-9.
+// bits, subnormal spacing 2^-9.  The code's exponent and fraction fields moved
+// into an fp32's (bits 23.. and 20..) read as 2^(e-127) (1 + m/8) for e > 0
+// and as the fp32 subnormal m 2^-129 for e = 0; one exact multiply by 2^120
+// turns both into the E4M3 value (fp32 subnormals are kept, not flushed, in
+// these kernels).
 QL_DEV float e4m3_decode(uint32_t code) {
-    const uint32_t e = (code >> 3) & 0xF, m = code & 7;
-    const float sub = (float)m * 0.001953125f;                   // m * 2^-9, exact
-    const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
-    return e ? nrm : sub;
+    return __uint_as_float((code & 0x7Fu) << 20) * 0x1p120f;
 }
 
 // Nearest E4M3FN code to y in [0, 448]; an exact tie goes to the lower code.

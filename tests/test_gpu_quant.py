@@ -59,6 +59,24 @@ def test_edge_magnitudes_and_zero_blocks():
     _check_full(w, x.shape, "edge magnitudes")
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_random_sizes_and_magnitudes(seed):
+    """Seeded random cases: a random number of blocks (1 to 2,000, so the last
+    group's length varies), Student-t(3) values under a per-group scale drawn
+    log-uniformly from 2^-120 to 2^100 (subnormal bf16 values, constants on
+    both sides of the reciprocal path's range) times a per-block factor from
+    2^-20 to 1 (FP8 block codes normal and subnormal), and 3% all-zero blocks;
+    bit-exact against the oracle."""
+    rng = np.random.default_rng(100 + seed)
+    nblk = int(rng.integers(1, 2001))
+    x = rng.standard_t(3, (nblk, 64)).astype(np.float32)
+    group = np.exp2(rng.uniform(-120.0, 100.0, -(-nblk // 256)))
+    x *= (np.repeat(group, 256)[:nblk] * np.exp2(rng.uniform(-20.0, 0.0, nblk)))[:, None].astype(np.float32)
+    x[rng.random(nblk) < 0.03] = 0.0
+    assert np.isfinite(x).all()
+    _check_full(synth.to_bf16_bits(x), x.shape, f"random case {seed}: {nblk} blocks")
+
+
 def test_fp8_exact_ties():
     """Groups whose super-scale is exact (amax = 1.75 * 2^e) and whose block
     constants sit exactly on E4M3 midpoints: ties must go to the lower code."""

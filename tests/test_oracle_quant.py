@@ -153,6 +153,18 @@ def test_e4m3_values_match_torch_decode():
     assert np.array_equal(vals, ref)
 
 
+def test_e4m3_decode_by_field_shift_is_exact():
+    """The kernels decode a block's FP8 code by moving its exponent and fraction
+    fields into an fp32 (code << 20, so a zero exponent reads as the fp32
+    subnormal m 2^-129) and multiplying by 2^120 in fp32 with subnormals kept.
+    Exhaustively over the codes: that equals the E4M3FN value for all of them."""
+    codes = np.arange(0x7F, dtype=np.uint32)
+    got = (codes << 20).view(np.float32) * np.float32(2.0 ** 120)
+    assert got.dtype == np.float32
+    assert np.array_equal(got.astype(np.float64), oracle.e4m3fn_values())
+    assert got[1] == 2.0 ** -9 and got[8] == 2.0 ** -6 and got[0x7E] == 448.0
+
+
 def test_e4m3_encode_matches_torch_off_ties():
     rng = np.random.default_rng(3)
     y = np.concatenate([rng.uniform(0, 448, 100_000), np.exp(rng.uniform(-14, 6.1, 100_000))])
