@@ -268,27 +268,48 @@ struct BlockScales {
 // reads: out[kb][n] = c1' of block kb of row n, i.e. fl32(e4m3(f) * s2) (the
 // stored fp32 absmax with single quantization), [K/64][N] so that eight
 // consecutive rows of one block column are contiguous.  It runs as extra
-// workgroups of another launch (or alone): workgroup `b` of `blocks` writes
-// entries kScalesPerBlock b .. + kScalesPerBlock - 1 (n fastest), eight per
-// thread, so that it adds few workgroups to the launch it rides on.
+// workgroups of another launch (or alone), 2,048 constants per workgroup so
+// that it adds few workgroups to the launch it rides on.
 struct ScalesJob {
     const uint8_t* fp8;
     const float* sup;
     const float* absmax;      // single quantization (fp8, sup unused)
     int64_t N, KB;
     float* out;
-    int blocks;               // ceil(N * KB / kScalesPerBlock), 0 = no job
+    int blocks;               // scales_job_blocks(N, KB), 0 = no job
 };
-constexpr int kScalesPerBlock = 8 * 256;
-QL_DEV void scales_job(const ScalesJob& j, int b) {
+// A workgroup takes a tile of 32 rows n x 64 blocks kb: it reads the
+// FP8 codes (or fp32 absmax) of each row as 64 consecutive elements, decodes
+// them into an LDS tile, and writes each kb row's 32 values as 128 contiguous
+// bytes.  Workgroup b takes n tile b % ceil(N / 32) of kb tile b / ceil(N / 32).
+// `lds` holds kScalesLds bytes; every thread of the workgroup calls this.
+constexpr int kScalesTileN = 32, kScalesTileKB = 64;
+constexpr int kScalesLds = kScalesTileN * (kScalesTileKB + 1) * 4;
+inline int scales_job_blocks(int64_t N, int64_t KB) {
+    return (int)(((N + kScalesTileN - 1) / kScalesTileN) * ((KB + kScalesTileKB - 1) / kScalesTileKB));
+}
+QL_DEV void scales_job(const ScalesJob& j, int b, lds8_t* lds) {
+    typedef __attribute__((address_space(3))) float lds_f32_t;
+    lds_f32_t* tile = reinterpret_cast<lds_f32_t*>(lds);                 // [32][65]
+    const int ntn = (int)((j.N + kScalesTileN - 1) / kScalesTileN);
+    const int64_t n0 = (int64_t)(b % ntn) * kScalesTileN, kb0 = (int64_t)(b / ntn) * kScalesTileKB;
 #pragma unroll
-    for (int e = 0; e < kScalesPerBlock / 256; ++e) {
-        const int64_t i = (int64_t)b * kScalesPerBlock + e * 256 + threadIdx.x;
-        if (i < j.N * j.KB) {
-            const int64_t kb = i / j.N, n = i % j.N;
+    for (int u = 0; u < kScalesTileN * kScalesTileKB / 256; ++u) {
+        const int e = (int)threadIdx.x + 256 * u;
+        const int nl = e >> 6, kl = e & 63;                             // a wave reads 64 kb of one row
+        const int64_t n = n0 + nl, kb = kb0 + kl;
+        if (n < j.N && kb < j.KB) {
             const int64_t blk = n * j.KB + kb;
-            j.out[i] = j.absmax ? j.absmax[blk] : block_scale(j.fp8[blk], j.sup[blk >> 8]);
+            tile[nl * (kScalesTileKB + 1) + kl] = j.absmax ? j.absmax[blk] : block_scale(j.fp8[blk], j.sup[blk >> 8]);
         }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kScalesTileN * kScalesTileKB / 256; ++u) {
+        const int e = (int)threadIdx.x + 256 * u;
+        const int nl = e & 31, kl = e >> 5;                             // 32 n of one kb row per half-wave
+        const int64_t n = n0 + nl, kb = kb0 + kl;
+        if (n < j.N && kb < j.KB) j.out[kb * j.N + n] = tile[nl * (kScalesTileKB + 1) + kl];
     }
 }
 

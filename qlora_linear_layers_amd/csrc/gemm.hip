@@ -619,7 +619,10 @@ struct DxArgs {
 
 // The transposed block scales alone (when no other launch of the backward
 // carries them).
-__global__ __launch_bounds__(256) void k_scales_t(ScalesJob j) { scales_job(j, (int)blockIdx.x); }
+__global__ __launch_bounds__(256) void k_scales_t(ScalesJob j) {
+    __shared__ __align__(16) uint8_t lds[kScalesLds];
+    scales_job(j, (int)blockIdx.x, (lds8_t*)lds);
+}
 
 // dX = dY W' (+ (s dY B^T) A^T): tile 256 (k) x 256 (t), reduction over n in
 // tiles of 64, waves 2 x 2 (wave (wa, wb) owns k rows wa*128.. and t rows
@@ -1012,7 +1015,7 @@ hipError_t launch_fwd(const uint16_t* x, const uint8_t* codes, BlockScales sc, c
 
 ScalesJob scales_job_for(BlockScales sc, const LoraPlan& pl, uint8_t* ws) {
     return ScalesJob{sc.fp8, sc.sup, sc.absmax, pl.N, pl.K / 64, reinterpret_cast<float*>(ws + pl.off_scl),
-                     (int)ceil_div((pl.K / 64) * pl.N, kScalesPerBlock)};
+                     scales_job_blocks(pl.N, pl.K / 64)};
 }
 
 hipError_t launch_dx(const uint16_t* dy, const uint8_t* codes, BlockScales sc, const uint16_t* lora_a,

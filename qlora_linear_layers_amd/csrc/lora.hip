@@ -146,13 +146,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(DownArgs a) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     lds8_t* smem = (lds8_t*)(smem_raw);
     constexpr uint32_t kXT = 64 * 128, kMT = R * 128, kBuf = kXT + kMT;
-    if ((int)blockIdx.x < a.sj.blocks) {        // block-scale workgroups of the same launch
-        scales_job(a.sj, (int)blockIdx.x);
+    const int tiles = (int)ceil_div(a.T, 64);
+    const int bid = (int)blockIdx.x;
+    if (bid >= tiles * a.splits) {              // block-scale workgroups of the same launch, dispatched
+        scales_job(a.sj, bid - tiles * a.splits, smem);   // after the longer projection workgroups
         return;
     }
-    const int bid = (int)blockIdx.x - a.sj.blocks;
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int tiles = (int)ceil_div(a.T, 64);
     const int tile = bid % tiles, split = bid / tiles;
     const int64_t t0 = (int64_t)tile * 64;
     const int nr_all = (int)(a.L / 64);
