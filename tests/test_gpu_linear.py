@@ -51,6 +51,15 @@ def test_multi_tile_rank64():
     _run_full("multi-tile", synth.Linear("t", 768, 1024), T=520, r=64, s=0.25)
 
 
+@pytest.mark.parametrize("r", [16, 0])
+def test_block_scales_over_two_tiles(r):
+    """K = 4480 (70 blocks per row): the dX kernel's transposed block scales are
+    written in tiles of 32 rows x 64 blocks, the second of them holding 6
+    blocks (with an adapter as extra workgroups of the s dY B^T launch, without
+    one as a launch of their own)."""
+    _run_full(f"K=4480 r={r}", synth.Linear("t", 192, 4480), T=300, r=r, s=0.5 if r else 0.0)
+
+
 @pytest.mark.parametrize("T,r", [(300, 72), (300, 136), (300, 256), (97, 136), (90, 136)])
 def test_ranks_above_64(T, r):
     """Padded ranks (r_pad = 128, 192, 256): the wide down-projection variants,
