@@ -362,135 +362,180 @@ __global__ __launch_bounds__(kDecThreads, (DOT || (F16 && TT > 8)) ? 4 : 6) void
     }
 }
 
-// Launch 2.  Y[t][n] = sum_ks part[ks][t][n] + sum_j (s X A)[t][j] B[j][n],
-// rounded to bf16.  A workgroup owns 64 columns n (one per lane); wave w takes
-// ranks [w r_pad/4, (w+1) r_pad/4) of B and the base partials of the tokens
-// t = w mod 4, and issues those loads first.  Meanwhile the whole workgroup
-// rebuilds s X A from its slice partials: thread (e, g) adds slices
-// g, g + G, g + 2G, ... of the float4 entry e, all loads independent, and the
-// G group sums are added in g order.  The four wave sums of each output are
-// added in wave order, so the result does not depend on timing.
+// Launch 2.  Y[t][n] = sum_ks part[ks][t][n] + sum_j u[t][j] B[j][n] with
+// u = s X A rebuilt from its slice partials, rounded to the 16-bit type.  A
+// workgroup owns 64 columns n (one per lane) and its four waves work alone:
+// wave w takes the tokens t = w, w + 4, ... (TW of them), adds their base
+// partials in ks order, rebuilds each 64-rank chunk of u from the slice
+// partials (lane (g, i) adds ranks 4i .. 4i + 3 over the slices g, g + 4, ...
+// in order, then the four lane groups are added pairwise), and forms the rank
+// dot with u read lane by lane (v_readlane) against the column of B it holds
+// in registers.  No LDS and no barrier: the B column, the base partials and
+// the first slice partials are all issued before the first sum, so for the
+// decode shapes the kernel waits for one round of loads.
 constexpr int kFinCols = 64;
-template <int RP, bool F16>
+template <int TW, bool LORA, bool F16>
 __global__ __launch_bounds__(256) void k_gemv_finalize(GemvGroup grp) {
     const int gi = group_find(grp.fin_end, grp.count, (int)blockIdx.x);
     const GemvArgs p = grp.p[gi];
     const int bx = (int)blockIdx.x - (gi ? grp.fin_end[gi - 1] : 0);
-    constexpr int RQ = 16 * RP;                                        // ranks of B per wave
-    __shared__ __align__(16) float pr[4 * 256];                        // group sums [G][W] float4
-    __shared__ __align__(16) float ps[16 * 256];                       // s X A [T][r_pad]
-    __shared__ __align__(16) float red[4 * 16 * kFinCols];             // wave sums [4][T][64]
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int T = (int)p.T;
+    if (wave >= T) return;                                             // no token for this wave
     const int64_t n = (int64_t)bx * kFinCols + lane;
     const bool nok = n < p.N;
+    constexpr int kC = 16 / TW;                                        // loads per token and round
+    const int KS = p.KS, KL = p.KL, RP = (int)(p.r_pad / 64);
 
-    // B column n over this wave's ranks, and the first 8 base partials of its tokens
-    uint32_t bv[RQ > 0 ? RQ : 1];
-    if constexpr (RP > 0) {
-        const rsrc_t rb = make_rsrc(p.lora_b, p.r * p.N * 2);
-#pragma unroll
-        for (int u = 0; u < RQ; ++u) {
-            const int64_t j = (int64_t)wave * RQ + u;
-            bv[u] = bload2(rb, (nok && j < p.r) ? (uint32_t)((j * p.N + n) * 2) : kOOB, 0);
-        }
-    }
-    const rsrc_t rp = make_rsrc(p.part, (int64_t)p.KS * p.T * p.N * 4);
-    const uint32_t n4 = (uint32_t)n * 4u;
-    auto part_at = [&](int ks, int t) -> uint32_t {
-        const uint32_t row = (uint32_t)(((int64_t)ks * p.T + t) * p.N * 4);   // wave-uniform
-        return (nok && t < p.T && ks < p.KS) ? row + n4 : kOOB;
+    // Every load takes its lane part as the vector offset and the uniform
+    // part (row of the partials, rank of B) as the scalar offset; a lane past
+    // N, or a partial past KS / KL or a token past T, gets an offset past the
+    // buffer's end and reads 0.
+    const uint32_t vn = nok ? (uint32_t)n : 0u;
+    const uint32_t v4 = nok ? vn * 4u : kOOB;
+    const rsrc_t rp = make_rsrc(p.part, (int64_t)KS * T * p.N * 4);
+    auto part_at = [&](int ks, int tw, uint32_t& soff) -> uint32_t {
+        const int t = wave + 4 * tw;
+        soff = (uint32_t)(((int64_t)ks * T + t) * p.N * 4);
+        return (ks < KS && t < T) ? v4 : kOOB;
     };
-    uint32_t pv[8][4];
+    [[maybe_unused]] const rsrc_t rl = make_rsrc(p.lpart, (int64_t)KL * T * p.r_pad * 4);
+    // slice partials as float4s: lane (g, i) = (lane / 16, lane % 16) takes
+    // ranks 4i .. 4i + 3 of the chunk from the slices kl = g mod 4
+    const int sg = lane >> 4, si = lane & 15;
+    [[maybe_unused]] auto lpart_at = [&](int kl0, int tw, int c, uint32_t& soff) -> uint32_t {
+        const int t = wave + 4 * tw;
+        soff = (uint32_t)((((int64_t)kl0 * T + t) * p.r_pad + 64 * c) * 4);
+        return (kl0 + sg < KL && t < T) ? (uint32_t)(sg * T * p.r_pad * 4 + si * 16) : kOOB;
+    };
+    // ranks past r (padding up to the 64-rank chunk) read row r - 1: their
+    // slice partials are exact zeros, so they add nothing
+    [[maybe_unused]] const rsrc_t rb = make_rsrc(p.lora_b, p.r * p.N * 2);
+    [[maybe_unused]] const uint32_t v2 = nok ? vn * 2u : kOOB;
+    [[maybe_unused]] auto load_b = [&](uint32_t (&bv)[64], int c) {
+        const uint32_t row = (uint32_t)(p.N * 2);
+        const int jv = (int)(p.r - 64 * c);                            // ranks of this chunk below r
+        const uint32_t last = v2 + (uint32_t)(jv - 1) * row;
+        uint32_t vo = v2 + (uint32_t)(64 * c) * row;
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pv[c][i] = bload4(rp, part_at(c, wave + 4 * i), 0);
+        for (int j = 0; j < 64; ++j, vo += row) bv[j] = bload2(rb, j < jv ? vo : last, 0);
+    };
 
-    if constexpr (RP > 0) {
-        const int E4 = (int)(p.T * p.r_pad / 4);                       // float4 entries of s X A
-        const int W = E4 < 256 ? E4 : 256;
-        const int G = 256 / W;                                         // slice groups
-        const int eb = (int)threadIdx.x % W, g = (int)threadIdx.x / W;
-        const rsrc_t rl = make_rsrc(p.lpart, (int64_t)p.KL * p.T * p.r_pad * 4);
-        const uint32_t slice = (uint32_t)(p.T * p.r_pad * 4);
-        // threads past G groups of W (when W does not divide 256) take no part
-        for (int e = eb; g < G && e < E4; e += W) {
-            f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
-            for (int kb = g; kb < p.KL; kb += 16 * G) {
-                u32x4_t v[16];
+    // Partials are added kC per token and round (a load past KS or KL reads
+    // 0 and adds nothing); the next round is issued before the current one
+    // is added.  The first round of base partials and slice partials and the
+    // B column of rank chunk 0 are all issued before the first addition.
+    typedef uint32_t round_t[TW][kC];
+    auto load_base = [&](round_t& v, int ks0) {
 #pragma unroll
-                for (int c = 0; c < 16; ++c) {
-                    const int kl = kb + c * G;
-                    v[c] = bload16(rl, kl < p.KL ? kl * slice + (uint32_t)e * 16u : kOOB, 0);
+        for (int c = 0; c < kC; ++c)
+#pragma unroll
+            for (int tw = 0; tw < TW; ++tw) {
+                uint32_t so;
+                const uint32_t vo = part_at(ks0 + c, tw, so);
+                v[tw][c] = bload4(rp, vo, so);
+            }
+    };
+    constexpr int kCU = 8 / TW;                                        // float4 slice loads per token and round
+    typedef u32x4_t uround_t[TW][kCU];
+    [[maybe_unused]] auto load_slices = [&](uround_t& v, int kl0, int c) {
+#pragma unroll
+        for (int cc = 0; cc < kCU; ++cc)
+#pragma unroll
+            for (int tw = 0; tw < TW; ++tw) {
+                uint32_t so;
+                const uint32_t vo = lpart_at(kl0 + 4 * cc, tw, c, so);
+                v[tw][cc] = bload16(rl, vo, so);
+            }
+    };
+    auto add = [&](float (&acc)[TW], const round_t& v) {
+#pragma unroll
+        for (int c = 0; c < kC; ++c)
+#pragma unroll
+            for (int tw = 0; tw < TW; ++tw) acc[tw] += __uint_as_float(v[tw][c]);
+    };
+    // sum of `count` partials in order, the first round already in `r0`
+    auto add_rounds = [&](float (&acc)[TW], round_t& r0, round_t& r1, int count, auto load) {
+        for (int i = 0;; i += 2 * kC) {
+            if (i + kC < count) load(r1, i + kC);
+            add(acc, r0);
+            if (i + kC >= count) break;
+            if (i + 2 * kC < count) load(r0, i + 2 * kC);
+            add(acc, r1);
+            if (i + 2 * kC >= count) break;
+        }
+    };
+
+    uint32_t bv[LORA ? 64 : 1];
+    round_t pb0, pb1;
+    [[maybe_unused]] uround_t pu0, pu1;
+    if constexpr (LORA) load_b(bv, 0);
+    load_base(pb0, 0);
+    if constexpr (LORA) load_slices(pu0, 0, 0);
+
+    // base partials in ks order (-0 is the identity of fp32 addition)
+    float y[TW];
+#pragma unroll
+    for (int tw = 0; tw < TW; ++tw) y[tw] = -0.0f;
+    add_rounds(y, pb0, pb1, KS, load_base);
+
+    if constexpr (LORA) {
+#pragma unroll 1
+        for (int c = 0; c < RP; ++c) {
+            if (c > 0) {
+                load_b(bv, c);
+                load_slices(pu0, 0, c);
+            }
+            // u of this rank chunk: each lane adds its slices in kl order, the
+            // four slice groups are then added pairwise across lanes
+            f32x4_t u[TW];
+#pragma unroll
+            for (int tw = 0; tw < TW; ++tw) u[tw] = f32x4_t{-0.0f, -0.0f, -0.0f, -0.0f};
+            auto addu = [&](const uround_t& v) {
+#pragma unroll
+                for (int cc = 0; cc < kCU; ++cc)
+#pragma unroll
+                    for (int tw = 0; tw < TW; ++tw) u[tw] += __builtin_bit_cast(f32x4_t, v[tw][cc]);
+            };
+            constexpr int kR = 4 * kCU;                                // slices per round
+            for (int i = 0;; i += 2 * kR) {
+                if (i + kR < KL) load_slices(pu1, i + kR, c);
+                addu(pu0);
+                if (i + kR >= KL) break;
+                if (i + 2 * kR < KL) load_slices(pu0, i + 2 * kR, c);
+                addu(pu1);
+                if (i + 2 * kR >= KL) break;
+            }
+#pragma unroll
+            for (int tw = 0; tw < TW; ++tw) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float v = u[tw][e];
+                    v += __shfl_xor(v, 16);
+                    v += __shfl_xor(v, 32);
+                    u[tw][e] = v * p.scaling;
                 }
-#pragma unroll
-                for (int c = 0; c < 16; ++c) a += __builtin_bit_cast(f32x4_t, v[c]);
             }
-            if (G == 1) {
-                *reinterpret_cast<f32x4_t*>(ps + 4 * e) = a * p.scaling;
-            } else {
-                *reinterpret_cast<f32x4_t*>(pr + 4 * (g * W + e)) = a;
-            }
-        }
-        if (G > 1) {
-            __syncthreads();
-            if ((int)threadIdx.x < E4) {
-                f32x4_t a = *reinterpret_cast<const f32x4_t*>(pr + 4 * threadIdx.x);
-                for (int gg = 1; gg < G; ++gg)
-                    a += *reinterpret_cast<const f32x4_t*>(pr + 4 * (gg * W + threadIdx.x));
-                *reinterpret_cast<f32x4_t*>(ps + 4 * threadIdx.x) = a * p.scaling;
-            }
-        }
-        __syncthreads();
-    }
-
-    // base partials of this wave's tokens, in ks order
-    float yb[4];
+            // rank dot in rank order: u[t][64c + j] sits in lane j / 4, component j % 4
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float v = __uint_as_float(pv[0][i]);
+            for (int tw = 0; tw < TW; ++tw) {
+                float v = y[tw];
 #pragma unroll
-        for (int c = 1; c < 8; ++c) v += __uint_as_float(pv[c][i]);
-        yb[i] = v;
-    }
-    for (int ks0 = 8; ks0 < p.KS; ks0 += 8) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pv[c][i] = bload4(rp, part_at(ks0 + c, wave + 4 * i), 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) yb[i] += __uint_as_float(pv[c][i]);
-    }
-
-    // this wave's share of every output column: base partials (own tokens) + its ranks of B
-    const int T = (int)p.T;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        if (t < T) {
-            float v = (t & 3) == wave ? yb[t >> 2] : 0.0f;
-            if constexpr (RP > 0) {
-#pragma unroll
-                for (int q = 0; q < RQ / 4; ++q) {
-                    const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(ps + t * p.r_pad + wave * RQ + 4 * q);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v = fmaf(sv[e], lo16<F16>(bv[4 * q + e]), v);
+                for (int j = 0; j < 64; ++j) {
+                    const float uj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u[tw][j & 3]), j >> 2));
+                    v = fmaf(uj, lo16<F16>(bv[j]), v);
+                    if (j % 16 == 15) __builtin_amdgcn_sched_barrier(0);   // bounds the live scalar registers
                 }
+                y[tw] = v;
             }
-            red[(wave * 16 + t) * kFinCols + lane] = v;
         }
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < T * kFinCols; i += 256) {
-        const int t = i / kFinCols, l = i % kFinCols;
-        const int64_t nn = (int64_t)bx * kFinCols + l;
-        if (nn < p.N && t >= p.skip) {
-            const float v = red[(0 * 16 + t) * kFinCols + l] + red[(1 * 16 + t) * kFinCols + l] +
-                            red[(2 * 16 + t) * kFinCols + l] + red[(3 * 16 + t) * kFinCols + l];
-            p.y[t * p.N + nn] = (uint16_t)(pack16x2<F16>(v, 0.0f) & 0xFFFFu);
-        }
+
+#pragma unroll
+    for (int tw = 0; tw < TW; ++tw) {
+        const int t = wave + 4 * tw;
+        if (nok && t < T && t >= p.skip) p.y[(int64_t)t * p.N + n] = (uint16_t)(pack16x2<F16>(y[tw], 0.0f) & 0xFFFFu);
     }
 }
 
@@ -567,13 +612,14 @@ hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int
     if (e != hipSuccess) return e;
     const dim3 fg((unsigned)nfin), fb(256);
     auto fin = [&](auto kern) { hipLaunchKernelGGL(kern, fg, fb, 0, s, g); };
-    switch (r_pad / 64) {
-        case 0: f16 ? fin(k_gemv_finalize<0, true>) : fin(k_gemv_finalize<0, false>); break;
-        case 1: f16 ? fin(k_gemv_finalize<1, true>) : fin(k_gemv_finalize<1, false>); break;
-        case 2: f16 ? fin(k_gemv_finalize<2, true>) : fin(k_gemv_finalize<2, false>); break;
-        case 3: f16 ? fin(k_gemv_finalize<3, true>) : fin(k_gemv_finalize<3, false>); break;
-        default: f16 ? fin(k_gemv_finalize<4, true>) : fin(k_gemv_finalize<4, false>); break;
-    }
+    auto fin_tw = [&](auto tw) {
+        constexpr int TW = decltype(tw)::value;
+        if (r_pad > 0) f16 ? fin(k_gemv_finalize<TW, true, true>) : fin(k_gemv_finalize<TW, true, false>);
+        else f16 ? fin(k_gemv_finalize<TW, false, true>) : fin(k_gemv_finalize<TW, false, false>);
+    };
+    if (T <= 4) fin_tw(std::integral_constant<int, 1>{});
+    else if (T <= 8) fin_tw(std::integral_constant<int, 2>{});
+    else fin_tw(std::integral_constant<int, 4>{});
     return hipGetLastError();
 }
 
