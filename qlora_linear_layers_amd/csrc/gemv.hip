@@ -364,9 +364,10 @@ __global__ __launch_bounds__(kDecThreads, (DOT || (F16 && TT > 8)) ? 4 : 6) void
 
 // Launch 2.  Y[t][n] = sum_ks part[ks][t][n] + sum_j u[t][j] B[j][n] with
 // u = s X A rebuilt from its slice partials, rounded to the 16-bit type.  A
-// workgroup owns 64 columns n (one per lane) and its four waves work alone:
-// wave w takes the tokens t = w, w + 4, ... (TW of them), adds their base
-// partials in ks order, rebuilds each 64-rank chunk of u from the slice
+// workgroup owns 64 columns n (one per lane) and has W waves (T of them up to
+// T = 4, then 4, and 8 for T > 8) that work alone: wave w takes the tokens
+// t = w and, for T > 4, t = w + W (TW of them), adds their base partials in ks
+// order, rebuilds each 64-rank chunk of u from the slice
 // partials (lane (g, i) adds ranks 4i .. 4i + 3 over the slices g, g + 4, ...
 // in order, then the four lane groups are added pairwise), and forms the rank
 // dot with u read lane by lane (v_readlane) against the column of B it holds
@@ -375,13 +376,14 @@ __global__ __launch_bounds__(kDecThreads, (DOT || (F16 && TT > 8)) ? 4 : 6) void
 // decode shapes the kernel waits for one round of loads.
 constexpr int kFinCols = 64;
 template <int TW, bool LORA, bool F16>
-__global__ __launch_bounds__(256) void k_gemv_finalize(GemvGroup grp) {
+__global__ __launch_bounds__(512) void k_gemv_finalize(GemvGroup grp) {
     const int gi = group_find(grp.fin_end, grp.count, (int)blockIdx.x);
     const GemvArgs p = grp.p[gi];
     const int bx = (int)blockIdx.x - (gi ? grp.fin_end[gi - 1] : 0);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int T = (int)p.T;
+    const int W = (int)(blockDim.x >> 6);                              // waves (tokens w, w + W)
     if (wave >= T) return;                                             // no token for this wave
     const int64_t n = (int64_t)bx * kFinCols + lane;
     const bool nok = n < p.N;
@@ -396,7 +398,7 @@ __global__ __launch_bounds__(256) void k_gemv_finalize(GemvGroup grp) {
     const uint32_t v4 = nok ? vn * 4u : kOOB;
     const rsrc_t rp = make_rsrc(p.part, (int64_t)KS * T * p.N * 4);
     auto part_at = [&](int ks, int tw, uint32_t& soff) -> uint32_t {
-        const int t = wave + 4 * tw;
+        const int t = wave + W * tw;
         soff = (uint32_t)(((int64_t)ks * T + t) * p.N * 4);
         return (ks < KS && t < T) ? v4 : kOOB;
     };
@@ -405,7 +407,7 @@ __global__ __launch_bounds__(256) void k_gemv_finalize(GemvGroup grp) {
     // ranks 4i .. 4i + 3 of the chunk from the slices kl = g mod 4
     const int sg = lane >> 4, si = lane & 15;
     [[maybe_unused]] auto lpart_at = [&](int kl0, int tw, int c, uint32_t& soff) -> uint32_t {
-        const int t = wave + 4 * tw;
+        const int t = wave + W * tw;
         soff = (uint32_t)((((int64_t)kl0 * T + t) * p.r_pad + 64 * c) * 4);
         return (kl0 + sg < KL && t < T) ? (uint32_t)(sg * T * p.r_pad * 4 + si * 16) : kOOB;
     };
@@ -534,7 +536,7 @@ __global__ __launch_bounds__(256) void k_gemv_finalize(GemvGroup grp) {
 
 #pragma unroll
     for (int tw = 0; tw < TW; ++tw) {
-        const int t = wave + 4 * tw;
+        const int t = wave + W * tw;
         if (nok && t < T && t >= p.skip) p.y[(int64_t)t * p.N + n] = (uint16_t)(pack16x2<F16>(y[tw], 0.0f) & 0xFFFFu);
     }
 }
@@ -610,7 +612,10 @@ hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int
     if (ae != hipSuccess) return ae;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 fg((unsigned)nfin), fb(256);
+    // waves: one per token up to 4, four for T <= 8 (two tokens each), eight
+    // for T > 8 (two tokens each); every wave loads the B column itself
+    const int fw = T <= 4 ? (int)T : T <= 8 ? 4 : 8;
+    const dim3 fg((unsigned)nfin), fb((unsigned)(64 * fw));
     auto fin = [&](auto kern) { hipLaunchKernelGGL(kern, fg, fb, 0, s, g); };
     auto fin_tw = [&](auto tw) {
         constexpr int TW = decltype(tw)::value;
@@ -618,8 +623,7 @@ hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int
         else f16 ? fin(k_gemv_finalize<TW, false, true>) : fin(k_gemv_finalize<TW, false, false>);
     };
     if (T <= 4) fin_tw(std::integral_constant<int, 1>{});
-    else if (T <= 8) fin_tw(std::integral_constant<int, 2>{});
-    else fin_tw(std::integral_constant<int, 4>{});
+    else fin_tw(std::integral_constant<int, 2>{});
     return hipGetLastError();
 }
 
