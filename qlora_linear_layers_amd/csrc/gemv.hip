@@ -364,18 +364,22 @@ __global__ __launch_bounds__(kDecThreads, (DOT || (F16 && TT > 8)) ? 4 : 6) void
 
 // Launch 2.  Y[t][n] = sum_ks part[ks][t][n] + sum_j u[t][j] B[j][n] with
 // u = s X A rebuilt from its slice partials, rounded to the 16-bit type.  A
-// workgroup owns 64 columns n (one per lane) and has W waves (T of them up to
+// workgroup owns 128 columns up to T = 8 (two adjacent ones per lane: N is a
+// multiple of 64, so B is read as dwords, the base partials as float2s and Y
+// written as dwords) and 64 above, and has W waves (T of them up to
 // T = 4, then 4, and 8 for T > 8) that work alone: wave w takes the tokens
 // t = w and, for T > 4, t = w + W (TW of them), adds their base partials in ks
 // order, rebuilds each 64-rank chunk of u from the slice
 // partials (lane (g, i) adds ranks 4i .. 4i + 3 over the slices g, g + 4, ...
 // in order, then the four lane groups are added pairwise), and forms the rank
-// dot with u read lane by lane (v_readlane) against the column of B it holds
+// dot with u read lane by lane (v_readlane) against the columns of B it holds
 // in registers.  No LDS and no barrier: the B column, the base partials and
 // the first slice partials are all issued before the first sum, so for the
 // decode shapes the kernel waits for one round of loads.
-constexpr int kFinCols = 64;
-template <int TW, bool LORA, bool F16>
+// CPL columns per lane: 2 up to T = 8, 1 above (more workgroups for the
+// 8-wave, 16-token case)
+constexpr int fin_cols(int64_t T) { return T <= 8 ? 128 : 64; }
+template <int TW, int CPL, bool LORA, bool F16>
 __global__ __launch_bounds__(512) void k_gemv_finalize(GemvGroup grp) {
     const int gi = group_find(grp.fin_end, grp.count, (int)blockIdx.x);
     const GemvArgs p = grp.p[gi];
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(512) void k_gemv_finalize(GemvGroup grp) {
     const int T = (int)p.T;
     const int W = (int)(blockDim.x >> 6);                              // waves (tokens w, w + W)
     if (wave >= T) return;                                             // no token for this wave
-    const int64_t n = (int64_t)bx * kFinCols + lane;
+    const int64_t n = (int64_t)bx * (64 * CPL) + CPL * lane;           // columns n .. n + CPL - 1 (N is even)
     const bool nok = n < p.N;
     constexpr int kC = 16 / TW;                                        // loads per token and round
     const int KS = p.KS, KL = p.KL, RP = (int)(p.r_pad / 64);
@@ -421,14 +425,15 @@ __global__ __launch_bounds__(512) void k_gemv_finalize(GemvGroup grp) {
         const uint32_t last = v2 + (uint32_t)(jv - 1) * row;
         uint32_t vo = v2 + (uint32_t)(64 * c) * row;
 #pragma unroll
-        for (int j = 0; j < 64; ++j, vo += row) bv[j] = bload2(rb, j < jv ? vo : last, 0);
+        for (int j = 0; j < 64; ++j, vo += row)                        // B[j][n] (and B[j][n + 1])
+            bv[j] = CPL == 2 ? bload4(rb, j < jv ? vo : last, 0) : bload2(rb, j < jv ? vo : last, 0);
     };
 
     // Partials are added kC per token and round (a load past KS or KL reads
     // 0 and adds nothing); the next round is issued before the current one
     // is added.  The first round of base partials and slice partials and the
     // B column of rank chunk 0 are all issued before the first addition.
-    typedef uint32_t round_t[TW][kC];
+    typedef u32x2_t round_t[TW][kC];                                   // .y unused with one column
     auto load_base = [&](round_t& v, int ks0) {
 #pragma unroll
         for (int c = 0; c < kC; ++c)
@@ -436,7 +441,8 @@ __global__ __launch_bounds__(512) void k_gemv_finalize(GemvGroup grp) {
             for (int tw = 0; tw < TW; ++tw) {
                 uint32_t so;
                 const uint32_t vo = part_at(ks0 + c, tw, so);
-                v[tw][c] = bload4(rp, vo, so);
+                if constexpr (CPL == 2) v[tw][c] = bload8(rp, vo, so);
+                else v[tw][c][0] = bload4(rp, vo, so);
             }
     };
     constexpr int kCU = 8 / TW;                                        // float4 slice loads per token and round
@@ -451,14 +457,17 @@ __global__ __launch_bounds__(512) void k_gemv_finalize(GemvGroup grp) {
                 v[tw][cc] = bload16(rl, vo, so);
             }
     };
-    auto add = [&](float (&acc)[TW], const round_t& v) {
+    auto add = [&](f32x2_t (&acc)[TW], const round_t& v) {
 #pragma unroll
         for (int c = 0; c < kC; ++c)
 #pragma unroll
-            for (int tw = 0; tw < TW; ++tw) acc[tw] += __uint_as_float(v[tw][c]);
+            for (int tw = 0; tw < TW; ++tw) {
+                acc[tw][0] += __uint_as_float(v[tw][c][0]);
+                if constexpr (CPL == 2) acc[tw][1] += __uint_as_float(v[tw][c][1]);
+            }
     };
     // sum of `count` partials in order, the first round already in `r0`
-    auto add_rounds = [&](float (&acc)[TW], round_t& r0, round_t& r1, int count, auto load) {
+    auto add_rounds = [&](f32x2_t (&acc)[TW], round_t& r0, round_t& r1, int count, auto load) {
         for (int i = 0;; i += 2 * kC) {
             if (i + kC < count) load(r1, i + kC);
             add(acc, r0);
@@ -477,9 +486,9 @@ __global__ __launch_bounds__(512) void k_gemv_finalize(GemvGroup grp) {
     if constexpr (LORA) load_slices(pu0, 0, 0);
 
     // base partials in ks order (-0 is the identity of fp32 addition)
-    float y[TW];
+    f32x2_t y[TW];
 #pragma unroll
-    for (int tw = 0; tw < TW; ++tw) y[tw] = -0.0f;
+    for (int tw = 0; tw < TW; ++tw) y[tw] = f32x2_t{-0.0f, -0.0f};
     add_rounds(y, pb0, pb1, KS, load_base);
 
     if constexpr (LORA) {
@@ -521,15 +530,15 @@ __global__ __launch_bounds__(512) void k_gemv_finalize(GemvGroup grp) {
             }
             // rank dot in rank order: u[t][64c + j] sits in lane j / 4, component j % 4
 #pragma unroll
-            for (int tw = 0; tw < TW; ++tw) {
-                float v = y[tw];
+            for (int j = 0; j < 64; ++j) {
+                const float b0 = lo16<F16>(bv[j]), b1 = hi16<F16>(bv[j]);
 #pragma unroll
-                for (int j = 0; j < 64; ++j) {
+                for (int tw = 0; tw < TW; ++tw) {
                     const float uj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u[tw][j & 3]), j >> 2));
-                    v = fmaf(uj, lo16<F16>(bv[j]), v);
-                    if (j % 16 == 15) __builtin_amdgcn_sched_barrier(0);   // bounds the live scalar registers
+                    y[tw][0] = fmaf(uj, b0, y[tw][0]);
+                    if constexpr (CPL == 2) y[tw][1] = fmaf(uj, b1, y[tw][1]);
                 }
-                y[tw] = v;
+                if (j % 16 == 15) __builtin_amdgcn_sched_barrier(0);       // bounds the live scalar registers
             }
         }
     }
@@ -537,7 +546,12 @@ __global__ __launch_bounds__(512) void k_gemv_finalize(GemvGroup grp) {
 #pragma unroll
     for (int tw = 0; tw < TW; ++tw) {
         const int t = wave + W * tw;
-        if (nok && t < T && t >= p.skip) p.y[(int64_t)t * p.N + n] = (uint16_t)(pack16x2<F16>(y[tw], 0.0f) & 0xFFFFu);
+        if (nok && t < T && t >= p.skip) {
+            if constexpr (CPL == 2)
+                *reinterpret_cast<uint32_t*>(p.y + (int64_t)t * p.N + n) = pack16x2<F16>(y[tw][0], y[tw][1]);
+            else
+                p.y[(int64_t)t * p.N + n] = (uint16_t)(pack16x2<F16>(y[tw][0], 0.0f) & 0xFFFFu);
+        }
     }
 }
 
@@ -575,7 +589,7 @@ hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int
         nl += r ? (int)(r_pad / 64) * a.KL : 0;
         g.lora_end[i] = nl;
         nbase += a.gemv_blocks;
-        nfin += (int)ceil_div(q.N, kFinCols);
+        nfin += (int)ceil_div(q.N, fin_cols(T));
         g.fin_end[i] = nfin;
     }
     for (int i = 0; i < count; ++i) g.base_end[i] = (i ? g.base_end[i - 1] : nl) + g.p[i].gemv_blocks;
@@ -617,13 +631,16 @@ hipError_t launch_gemv_group(const GemvProblem* probs, int count, int64_t T, int
     const int fw = T <= 4 ? (int)T : T <= 8 ? 4 : 8;
     const dim3 fg((unsigned)nfin), fb((unsigned)(64 * fw));
     auto fin = [&](auto kern) { hipLaunchKernelGGL(kern, fg, fb, 0, s, g); };
-    auto fin_tw = [&](auto tw) {
-        constexpr int TW = decltype(tw)::value;
-        if (r_pad > 0) f16 ? fin(k_gemv_finalize<TW, true, true>) : fin(k_gemv_finalize<TW, true, false>);
-        else f16 ? fin(k_gemv_finalize<TW, false, true>) : fin(k_gemv_finalize<TW, false, false>);
+    auto fin_tw = [&](auto tw, auto cpl) {
+        constexpr int TW = decltype(tw)::value, CPL = decltype(cpl)::value;
+        if (r_pad > 0) f16 ? fin(k_gemv_finalize<TW, CPL, true, true>) : fin(k_gemv_finalize<TW, CPL, true, false>);
+        else f16 ? fin(k_gemv_finalize<TW, CPL, false, true>) : fin(k_gemv_finalize<TW, CPL, false, false>);
     };
-    if (T <= 4) fin_tw(std::integral_constant<int, 1>{});
-    else fin_tw(std::integral_constant<int, 2>{});
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    if (T <= 4) fin_tw(I1{}, I2{});
+    else if (T <= 8) fin_tw(I2{}, I2{});
+    else fin_tw(I2{}, I1{});
     return hipGetLastError();
 }
 
