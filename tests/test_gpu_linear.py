@@ -96,6 +96,17 @@ def test_decode_rank_256():
     _run_full("decode r=256", synth.Linear("t", 256, 320), T=5, r=256, s=0.25, check_bwd=False)
 
 
+@pytest.mark.parametrize("N,K,T,r", [
+    (192, 448, 7, 72),     # two columns per lane, two tokens per wave, the second workgroup half past N, 2 rank chunks
+    (128, 2048, 3, 200),   # two columns per lane, one token per wave, 4 rank chunks (ranks padded to 256), 8 slices
+    (320, 1088, 12, 136),  # one column per lane (T > 8), eight waves of two tokens, 3 rank chunks, 3 k splits
+    (64, 11008, 16, 64),   # 22 k splits and 43 slices: several rounds of base and slice partials
+])
+def test_decode_finalize_layouts(N, K, T, r):
+    """The decode finalize's token and column layouts against the oracle."""
+    _run_full(f"finalize layout T={T} r={r}", synth.Linear("t", N, K), T=T, r=r, s=0.5, check_bwd=False)
+
+
 def test_no_lora():
     _run_full("r=0", synth.Linear("t", 512, 256), T=64, r=0, s=0.0)
 
