@@ -193,6 +193,7 @@ hipError_t launch_quantize_sq(const uint16_t* w, int64_t numel, uint8_t* codes, 
 // codebook in LDS (16 floats: every lookup hits one of 16 distinct banks, so
 // lookups never conflict).
 constexpr int kDeqUnits = 4;
+constexpr unsigned kDeqEarlyTableWgs = 4096;   // two rounds of 8 workgroups on each of 256 CUs
 
 template <bool SQ, bool F16>
 __global__ __launch_bounds__(256) void k_dequantize(QuantGroup grp, Codebook cb) {
@@ -205,9 +206,21 @@ __global__ __launch_bounds__(256) void k_dequantize(QuantGroup grp, Codebook cb)
     const float* __restrict__ absmax = grp.t[ti].absmax;
     const int64_t nunits = grp.t[ti].numel / 8;
     u32x4_t* __restrict__ out = reinterpret_cast<u32x4_t*>(grp.t[ti].out);
+    auto fill_table = [&] {
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-        if (threadIdx.x == j) s_q[j] = cb_value(cb, j);     // constant indexes: no memory round trip
+        for (int j = 0; j < 16; ++j)
+            if (threadIdx.x == j) s_q[j] = cb_value(cb, j);  // constant indexes: no memory round trip
+    };
+    // The barrier's fence waits for the loads issued before it.  A launch of
+    // several rounds of workgroups fills the table and passes the barrier
+    // first, so that unit 0 is expanded while the other loads are in flight;
+    // a one-round launch issues its loads first, since there the barrier would
+    // delay every load of the launch (uniform over the grid).
+    const bool early = gridDim.x >= kDeqEarlyTableWgs;
+    if (early) {
+        fill_table();
+        __syncthreads();
+    }
 
     const int64_t u0 = gl * (256 * kDeqUnits) + threadIdx.x;
     uint32_t cv[kDeqUnits];
@@ -227,7 +240,10 @@ __global__ __launch_bounds__(256) void k_dequantize(QuantGroup grp, Codebook cb)
             s2[u] = superscale[blk >> 8];
         }
     }
-    __syncthreads();
+    if (!early) {
+        fill_table();
+        __syncthreads();
+    }
 #pragma unroll
     for (int u = 0; u < kDeqUnits; ++u) {
         const int64_t i = u0 + u * 256;
